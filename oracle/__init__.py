@@ -1,0 +1,497 @@
+"""Plain FP64 CPU oracle for learned-indexer routed sparse attention.
+
+TEST INFRASTRUCTURE.  Nothing on the product path may import, call or execute
+this package: only the tests, the smoke check and the CPU-baseline leg of the
+benchmark use it.  It shares no code with the HIP library or its Python
+binding and imports neither.
+
+Every function evaluates the plain definition of one step of the method in
+float64 NumPy, with no blocking, fusion or reordering beyond what the
+definition states.  Sources, cited by page title and documented symbol:
+
+* QSA page   -- nemo_automodel.components.models.qwen3_8_flash_next.qsa
+* CSA page   -- nemo_automodel.components.models.step5.sparse
+* FA4 page   -- nemo_automodel.components.models.step5.fa4
+* layers page-- nemo_automodel.components.models.step5.layers
+* latent page-- nemo_automodel.components.models.common.cudnn_sparse_attention
+
+Readings taken where the pages are silent or disagree (each is listed with
+its reason in the design notes):
+
+* scores are ``scale * sum_h w[t,h] * relu(q[t,h] . k[j])`` -- the QSA page's
+  unweighted sum with the CSA page's signed FP32 head weights; ``w == 1``
+  and ``scale = 1/sqrt(D_idx)`` give the QSA formula exactly;
+* ties in top-k go to the lower block ID; -0.0 equals +0.0;
+* a window of ``W`` tokens ends at and includes the query itself;
+* RMSNorm gain is multiplicative; RoPE pairs dimension ``i`` with
+  ``i + D_rope/2`` (half split), dimensions >= D_rope pass through;
+* padding queries get all -1 routes and zero attention output, lse = -inf;
+  a query with an empty route likewise;
+* latent attention uses the first ``Dv`` channels of the shared latent row
+  as the value, and its key/value gradients land in the same buffer.
+
+Parity status: every function here is pinned by the CPU tests (hand-derived
+fixtures, brute force, library special cases, invariants); none is
+"parity unpinned" with respect to these readings.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ---------------------------------------------------------------------------
+# layout
+# ---------------------------------------------------------------------------
+
+def documents(B: int, S: int, cu_seqlens: Optional[np.ndarray] = None,
+              row_lens: Optional[np.ndarray] = None):
+    """Documents of every batch row as lists of (start, stop).
+
+    Packed layout (QSA page, ``_forward_packed``): one row, documents given
+    by strictly increasing ``cu_seqlens`` starting at 0; tokens at or beyond
+    the last boundary are padding.  Right-padded layout (QSA page,
+    ``right_padded_sequence_lengths``): row ``b`` is one document of length
+    ``row_lens[b]`` followed by padding.  Neither: each row one document.
+    """
+    if cu_seqlens is not None:
+        cu = [int(x) for x in np.asarray(cu_seqlens)]
+        if B != 1:
+            raise ValueError("packed layout needs B == 1")
+        if cu[0] != 0 or any(b <= a for a, b in zip(cu, cu[1:])) or cu[-1] > S:
+            raise ValueError("cu_seqlens must start at 0, increase strictly and end <= S")
+        return [[(cu[d], cu[d + 1]) for d in range(len(cu) - 1)]]
+    rows = []
+    for b in range(B):
+        n = S if row_lens is None else int(row_lens[b])
+        if not 0 <= n <= S:
+            raise ValueError("row length out of range")
+        rows.append([(0, n)] if n > 0 else [])
+    return rows
+
+
+def block_bases(docs, c: int):
+    """Global block ID of the first complete block of every document.
+
+    Packed rows number blocks consecutively over documents (the CSA page's
+    global region IDs); each document contributes ``floor(len / c)`` blocks
+    (QSA page, indexer class: only complete groups are compressed).
+    """
+    out = []
+    for row in docs:
+        base, bases = 0, []
+        for (a, e) in row:
+            bases.append(base)
+            base += (e - a) // c
+        out.append(bases)
+    return out
+
+
+def token_info(docs, S: int, c: int):
+    """Per token: (valid, doc_start, block_base, nb) with nb = floor((pos+1)/c).
+
+    ``nb`` is the number of complete blocks visible to the query at
+    document-relative position ``pos`` (QSA page, ``select_qsa_token_ids``).
+    """
+    B = len(docs)
+    valid = np.zeros((B, S), dtype=bool)
+    start = np.zeros((B, S), dtype=np.int64)
+    base = np.zeros((B, S), dtype=np.int64)
+    nb = np.zeros((B, S), dtype=np.int64)
+    bases = block_bases(docs, c)
+    for b, row in enumerate(docs):
+        for d, (a, e) in enumerate(row):
+            valid[b, a:e] = True
+            start[b, a:e] = a
+            base[b, a:e] = bases[b][d]
+            nb[b, a:e] = (np.arange(e - a) + 1) // c
+    return valid, start, base, nb
+
+
+# ---------------------------------------------------------------------------
+# a1: key compression
+# ---------------------------------------------------------------------------
+
+def compress_keys(kI, gamma, eps, freqs, c, cu_seqlens=None, row_lens=None, d_rope=None):
+    """Compressed index keys [B, S//c, D] (float64) and block bases.
+
+    QSA page, indexer class: complete consecutive groups of ``c`` raw index
+    keys are averaged, then RMS-normalised (gain ``gamma``, variance epsilon
+    ``eps``) and rotated at the group's first token.  ``apply_qsa_rope``:
+    the table row is ``cat(cos, sin)`` of width ``D_rope``; dimensions from
+    ``D_rope`` on pass through.  ``_forward_packed``: groups restart at each
+    document start.  Unused block slots are zero.
+    """
+    kI = np.asarray(kI, dtype=np.float64)
+    B, S, D = kI.shape
+    freqs = np.asarray(freqs, dtype=np.float64)
+    R = freqs.shape[-1] if d_rope is None else d_rope
+    half = R // 2
+    g = np.asarray(gamma, dtype=np.float64)
+    docs = documents(B, S, cu_seqlens, row_lens)
+    bases = block_bases(docs, c)
+    kc = np.zeros((B, S // c, D), dtype=np.float64)
+    for b, row in enumerate(docs):
+        for d, (a, e) in enumerate(row):
+            n = (e - a) // c
+            if n == 0:
+                continue
+            groups = kI[b, a:a + n * c].reshape(n, c, D)
+            m = groups.mean(axis=1)
+            u = m / np.sqrt(np.mean(m * m, axis=1, keepdims=True) + eps) * g
+            first = a + c * np.arange(n)
+            cos = freqs[b, first, :half]
+            sin = freqs[b, first, half:2 * half]
+            x1 = u[:, :half].copy()
+            x2 = u[:, half:2 * half].copy()
+            u[:, :half] = x1 * cos - x2 * sin
+            u[:, half:2 * half] = x2 * cos + x1 * sin
+            kc[b, bases[b][d]:bases[b][d] + n] = u
+    cu_blocks = None
+    if cu_seqlens is not None:
+        total = sum((e - a) // c for (a, e) in docs[0])
+        cu_blocks = np.array(bases[0] + [total], dtype=np.int32)
+    return kc, cu_blocks
+
+
+# ---------------------------------------------------------------------------
+# a2: indexer scores
+# ---------------------------------------------------------------------------
+
+def indexer_scores(qI, w, kc, c, scale=None, cu_seqlens=None, row_lens=None, q0=0, q1=None,
+                   row_chunk=256):
+    """Scores [B, q1-q0, NB] (float64); invisible entries are -inf.
+
+    ``s[t, j] = scale * sum_h w[t, h] * max(0, qI[t, h] . kc[j])`` over the
+    blocks ``j`` of the query's own document with local index below
+    ``nb(t) = floor((pos+1)/c)`` (QSA page, ``select_qsa_token_ids``: ReLU
+    head sum over complete visible blocks, divided by sqrt(D); CSA page,
+    ``indexer_score_tile``: signed FP32 head weights).  ``scale`` defaults
+    to 1/sqrt(D_idx).  Padding queries score -inf everywhere.
+    """
+    qI = np.asarray(qI, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    kc = np.asarray(kc, dtype=np.float64)
+    B, S, H, D = qI.shape
+    q1 = S if q1 is None else q1
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    NB = kc.shape[1]
+    docs = documents(B, S, cu_seqlens, row_lens)
+    valid, start, base, nb = token_info(docs, S, c)
+    out = np.full((B, q1 - q0, NB), NEG_INF, dtype=np.float64)
+    for b in range(B):
+        for r0 in range(q0, q1, row_chunk):
+            r1 = min(q1, r0 + row_chunk)
+            dots = np.einsum("thd,jd->thj", qI[b, r0:r1], kc[b])
+            s = scale * np.einsum("th,thj->tj", w[b, r0:r1], np.maximum(dots, 0.0))
+            j = np.arange(NB)[None, :]
+            lo = base[b, r0:r1, None]
+            vis = valid[b, r0:r1, None] & (j >= lo) & (j < lo + nb[b, r0:r1, None])
+            out[b, r0 - q0:r1 - q0] = np.where(vis, s, NEG_INF)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a3: top-k block selection
+# ---------------------------------------------------------------------------
+
+def select_topk(scores, c, topk, cu_seqlens=None, row_lens=None, q0=0, S=None):
+    """Selected global block IDs [B, rows, topk] (ascending, -1 suffix) and counts.
+
+    The ``k_eff = min(topk, nb(t))`` highest visible scores win (QSA page,
+    ``select_qsa_token_ids``: best ``budget / c`` blocks; CSA page,
+    ``RegionMetadata.dense_region_ids``: with no more than ``topk`` visible
+    regions all of them are taken).  Ties go to the lower block ID; -0.0 and
+    +0.0 compare equal.  The chosen IDs are written in ascending order (CSA
+    page, ``RegionSelection.region_ids`` is sorted) and the rest is -1.
+    """
+    scores = np.asarray(scores)
+    B, rows, NB = scores.shape
+    S = q0 + rows if S is None else S
+    docs = documents(B, S, cu_seqlens, row_lens)
+    valid, start, base, nb = token_info(docs, S, c)
+    sel = np.full((B, rows, topk), -1, dtype=np.int32)
+    cnt = np.zeros((B, rows), dtype=np.int32)
+    for b in range(B):
+        for r in range(rows):
+            t = q0 + r
+            if not valid[b, t] or nb[b, t] == 0:
+                continue
+            n, lo = int(nb[b, t]), int(base[b, t])
+            k = min(topk, n)
+            vis = scores[b, r, lo:lo + n]
+            ids = np.arange(n)
+            order = np.lexsort((ids, -vis))[:k]   # score descending, then ID ascending
+            chosen = np.sort(order) + lo
+            sel[b, r, :k] = chosen
+            cnt[b, r] = k
+    return sel, cnt
+
+
+def near_tie_rows(scores, c, topk, cu_seqlens=None, row_lens=None, q0=0, S=None, rel=1e-4):
+    """Rows whose k-th and (k+1)-th visible scores are within ``rel`` relative.
+
+    Only sparse rows (``nb > topk``) can be near-ties.  Such rows are
+    excluded from bit-exact route comparison and counted instead.
+    """
+    scores = np.asarray(scores)
+    B, rows, NB = scores.shape
+    S = q0 + rows if S is None else S
+    docs = documents(B, S, cu_seqlens, row_lens)
+    valid, start, base, nb = token_info(docs, S, c)
+    out = np.zeros((B, rows), dtype=bool)
+    for b in range(B):
+        for r in range(rows):
+            t = q0 + r
+            n = int(nb[b, t])
+            if not valid[b, t] or n <= topk:
+                continue
+            lo = int(base[b, t])
+            v = np.sort(scores[b, r, lo:lo + n])[::-1]
+            a, z = v[topk - 1], v[topk]
+            out[b, r] = bool(a == z) or abs(a - z) <= rel * max(abs(a), abs(z))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a4: route expansion and compaction
+# ---------------------------------------------------------------------------
+
+def route_width(topk, c, window):
+    """Fixed route width ``topk*c + max(window, c-1)``.
+
+    With no window this is the QSA page's ``budget + c - 1`` (indexer
+    ``forward`` return shape); a window of W tokens can replace the tail.
+    """
+    return topk * c + max(window, c - 1)
+
+
+def expand_routes(sel, cnt, c, window, topk, cu_seqlens=None, row_lens=None, L=None):
+    """Token routes [B, S, L] (ascending, unique, -1 suffix) and lengths [B, S].
+
+    ``R(t)`` = tokens of the selected blocks, plus the tokens of the current
+    incomplete group ``[doc_start + nb*c, t]`` (QSA page,
+    ``select_qsa_token_ids``: 0..c-1 tail tokens), plus the window
+    ``[max(doc_start, t-W+1), t]`` (CSA page, ``RegionMetadata.window_layout``:
+    the window holds the query and at most W-1 earlier keys); duplicates
+    removed (QSA page, ``qsa_gqa_attention``: duplicates collapse), sorted,
+    padded with -1 (QSA page, ``QSARouteSelection.selected_token_ids``).
+    """
+    sel = np.asarray(sel)
+    B, S, _ = sel.shape
+    L = route_width(topk, c, window) if L is None else L
+    docs = documents(B, S, cu_seqlens, row_lens)
+    valid, start, base, nb = token_info(docs, S, c)
+    routes = np.full((B, S, L), -1, dtype=np.int32)
+    lens = np.zeros((B, S), dtype=np.int32)
+    for b in range(B):
+        for t in range(S):
+            if not valid[b, t]:
+                continue
+            a = int(start[b, t])
+            k = int(cnt[b, t])
+            local = sel[b, t, :k].astype(np.int64) - int(base[b, t])
+            parts = [(a + local[:, None] * c + np.arange(c)[None, :]).ravel()]
+            parts.append(np.arange(a + int(nb[b, t]) * c, t + 1))
+            if window > 0:
+                parts.append(np.arange(max(a, t - window + 1), t + 1))
+            r = np.unique(np.concatenate(parts))
+            if len(r) > L:
+                raise ValueError("route longer than its width")
+            routes[b, t, :len(r)] = r
+            lens[b, t] = len(r)
+    return routes, lens
+
+
+def compact_routes(ids, key_count):
+    """Ascending unique valid prefix of arbitrary signed ID rows.
+
+    Latent page, ``_compact_and_sort_indices``: negative entries are invalid;
+    the result is an ascending valid prefix plus its length.  Entries at or
+    beyond ``key_count`` are also dropped and counted (``n_out_of_range``).
+    Input [..., W] -> (out [..., W] int32 with -1 suffix, len [...], n_out_of_range).
+    """
+    ids = np.asarray(ids)
+    shape = ids.shape
+    flat = ids.reshape(-1, shape[-1]).astype(np.int64)
+    out = np.full(flat.shape, -1, dtype=np.int32)
+    lens = np.zeros(flat.shape[0], dtype=np.int32)
+    bad = 0
+    for r in range(flat.shape[0]):
+        row = flat[r]
+        bad += int(np.count_nonzero(row >= key_count))
+        u = np.unique(row[(row >= 0) & (row < key_count)])
+        out[r, :len(u)] = u
+        lens[r] = len(u)
+    return out.reshape(shape), lens.reshape(shape[:-1]), bad
+
+
+# ---------------------------------------------------------------------------
+# a5: forward / reverse block lists
+# ---------------------------------------------------------------------------
+
+def block_lists(routes, lens, S_k, block_q, block_k, reverse=False):
+    """Block-sparse lists from token routes.
+
+    Forward (FA4 page, ``_selected_block_lists``, ``_block_lists``): for
+    every tile of ``block_q`` queries, the ascending key tiles of
+    ``block_k`` keys holding at least one routed key of one of its queries.
+    Reverse (``reverse=True``, used by backward): for every key tile, the
+    ascending query tiles that reach it.  Returns counts [B, rows] and
+    indices [B, rows, width] with -1 after the count; width is the number of
+    tiles on the other axis.
+    """
+    routes = np.asarray(routes)
+    lens = np.asarray(lens)
+    B, S_q, _ = routes.shape
+    nqt = -(-S_q // block_q)
+    nkt = -(-S_k // block_k)
+    rows, width = (nkt, nqt) if reverse else (nqt, nkt)
+    counts = np.zeros((B, rows), dtype=np.int32)
+    indices = np.full((B, rows, width), -1, dtype=np.int32)
+    for b in range(B):
+        grid = np.zeros((nqt, nkt), dtype=bool)
+        for t in range(S_q):
+            n = int(lens[b, t])
+            if n:
+                grid[t // block_q, routes[b, t, :n] // block_k] = True
+        if reverse:
+            grid = grid.T
+        for r in range(rows):
+            nz = np.nonzero(grid[r])[0]
+            counts[b, r] = len(nz)
+            indices[b, r, :len(nz)] = nz
+    return counts, indices
+
+
+# ---------------------------------------------------------------------------
+# a6 / a7: sparse GQA attention over gathered keys
+# ---------------------------------------------------------------------------
+
+def _route_set(row, S_k):
+    row = np.asarray(row, dtype=np.int64)
+    return np.unique(row[(row >= 0) & (row < S_k)])
+
+
+def attention_fwd(q, k, v, routes, scale=None, rows=None):
+    """Sparse GQA forward: output [B, S_q, Hq, Dv] and lse [B, Hq, S_q] (float64).
+
+    QSA page, ``gathered_qsa_gqa_attention``: each query attends only to the
+    keys and values at its route IDs; query head ``h`` uses KV group
+    ``h // (Hq/Hkv)`` (grouped query layout [B, Q, Hkv, G, D]); -1 and
+    out-of-range slots are ignored and repeated IDs count once; the score
+    multiplier defaults to 1/sqrt(D).  ``o = softmax(scale q K_R^T) V_R``.
+    A query with an empty route gets o = 0 and lse = -inf.  ``rows``
+    optionally restricts the evaluation to a list of (b, t) pairs.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S_q, Hq, D = q.shape
+    S_k, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = np.zeros((B, S_q, Hq, Dv), dtype=np.float64)
+    lse = np.full((B, Hq, S_q), NEG_INF, dtype=np.float64)
+    todo = [(b, t) for b in range(B) for t in range(S_q)] if rows is None else rows
+    for b, t in todo:
+        ids = _route_set(routes[b, t], S_k)
+        if len(ids) == 0:
+            continue
+        kg = k[b, ids]                                  # [n, Hkv, D]
+        vg = v[b, ids]                                  # [n, Hkv, Dv]
+        qg = q[b, t].reshape(Hkv, G, D)
+        x = scale * np.einsum("agd,nad->agn", qg, kg)  # [Hkv, G, n]
+        m = x.max(axis=-1, keepdims=True)
+        ls = m + np.log(np.exp(x - m).sum(axis=-1, keepdims=True))
+        p = np.exp(x - ls)
+        o[b, t] = np.einsum("agn,nae->age", p, vg).reshape(Hq, Dv)
+        lse[b, :, t] = ls.reshape(Hq)
+    return o, lse
+
+
+def attention_bwd(q, k, v, routes, dO, scale=None):
+    """Sparse GQA backward: dq, dk, dv (float64) for dO.
+
+    Gradients of the forward above with respect to q, k and v (QSA page,
+    ``gathered_qsa_gqa_attention`` is differentiable; the indexer is frozen,
+    so routes carry no gradient).  Per query and head:
+    ``P = softmax(x)``, ``dP = dO V_R^T``, ``dS = P (dP - rowsum(dO * o))``,
+    ``dq = scale dS K_R``, ``dK_R += scale dS^T q``, ``dV_R += P^T dO``;
+    the key/value sums run over every query that routes to that key.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, S_q, Hq, D = q.shape
+    S_k, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for t in range(S_q):
+            ids = _route_set(routes[b, t], S_k)
+            if len(ids) == 0:
+                continue
+            kg, vg = k[b, ids], v[b, ids]
+            qg = q[b, t].reshape(Hkv, G, D)
+            dog = dO[b, t].reshape(Hkv, G, Dv)
+            x = scale * np.einsum("agd,nad->agn", qg, kg)
+            m = x.max(axis=-1, keepdims=True)
+            p = np.exp(x - m)
+            p /= p.sum(axis=-1, keepdims=True)
+            og = np.einsum("agn,nae->age", p, vg)
+            delta = np.sum(dog * og, axis=-1, keepdims=True)
+            dp = np.einsum("age,nae->agn", dog, vg)
+            ds = p * (dp - delta)
+            dq[b, t] = (scale * np.einsum("agn,nad->agd", ds, kg)).reshape(Hq, D)
+            dk[b, ids] += scale * np.einsum("agn,agd->nad", ds, qg)
+            dv[b, ids] += np.einsum("agn,age->nae", p, dog)
+    return dq, dk, dv
+
+
+def latent_attention_fwd(q, kv, idx, scale, dv=512):
+    """Latent single-KV-head sparse attention forward (latent page, ``cudnn_sparse_attention``).
+
+    q [T, H, Dqk], shared latent kv [T, 1, Dqk], index lists [T, 1, W]
+    (-1 invalid); keys are the full latent rows, values their first ``dv``
+    channels.  Returns o [T, H, dv] and lse [H, T].
+    """
+    k = np.asarray(kv, dtype=np.float64)[None]
+    o, lse = attention_fwd(np.asarray(q)[None], k, k[..., :dv], np.asarray(idx)[None, :, 0, :], scale)
+    return o[0], lse[0]
+
+
+def latent_attention_bwd(q, kv, idx, dO, scale, dv=512):
+    """Latent backward: dq [T, H, Dqk] and the merged latent gradient dkv [T, 1, Dqk].
+
+    Keys and values are views of one latent tensor, so its gradient is
+    ``dK + [dV, 0]`` (the value part covers the first ``dv`` channels).
+    """
+    k = np.asarray(kv, dtype=np.float64)[None]
+    dq, dk, dvv = attention_bwd(np.asarray(q)[None], k, k[..., :dv], np.asarray(idx)[None, :, 0, :],
+                                np.asarray(dO)[None], scale)
+    dkv = dk[0].copy()
+    dkv[..., :dv] += dvv[0]
+    return dq[0], dkv
+
+
+# ---------------------------------------------------------------------------
+# whole route pipeline
+# ---------------------------------------------------------------------------
+
+def route_pipeline(kI, qI, w, gamma, freqs, c, topk, window, eps=1e-5, scale=None,
+                   cu_seqlens=None, row_lens=None):
+    """compress -> score -> select -> expand, as the QSA indexer composes them."""
+    kc, cu_blocks = compress_keys(kI, gamma, eps, freqs, c, cu_seqlens, row_lens)
+    s = indexer_scores(qI, w, kc, c, scale, cu_seqlens, row_lens)
+    sel, cnt = select_topk(s, c, topk, cu_seqlens, row_lens)
+    routes, lens = expand_routes(sel, cnt, c, window, topk, cu_seqlens, row_lens)
+    return dict(kc=kc, cu_blocks=cu_blocks, scores=s, sel=sel, cnt=cnt, routes=routes, lens=lens)
