@@ -1,0 +1,284 @@
+/*
+ * irb.h -- C ABI of libirb: learned-indexer routed sparse attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Pipeline (one call per step):
+ *   irb_compress_keys            raw index keys -> compressed block keys
+ *   irb_indexer_score_tile       weighted-ReLU block scores for a query x block tile
+ *   irb_select_topk_regions      top-k blocks per query (ascending, -1 suffix)
+ *   irb_route_topk_fused         the two above without materialising scores
+ *   irb_expand_and_compact_routes blocks + tail + window -> ascending token routes
+ *   irb_compact_routes           arbitrary signed ID lists -> ascending valid prefix
+ *   irb_build_block_lists        forward (query->key) / reverse (key->query) tile lists
+ *   irb_sparse_gqa_attention_fwd GQA attention over the routed keys only
+ *   irb_sparse_gqa_attention_bwd its gradients; key/value side over reverse lists
+ *
+ * Sources (API reference pages, cited by title and documented symbol):
+ *   [QSA]    nemo_automodel.components.models.qwen3_8_flash_next.qsa
+ *   [CSA]    nemo_automodel.components.models.step5.sparse
+ *   [FA4]    nemo_automodel.components.models.step5.fa4
+ *   [LATENT] nemo_automodel.components.models.common.cudnn_sparse_attention
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     never allocates, frees or keeps a pointer after the call returns.
+ *     Host-side arguments (scalars, the layout struct, stride arrays) are
+ *     read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     on it and the call returns without waiting; the library never reads
+ *     device memory from the host, so sizes come from host scalars.
+ *   - All IDs and counts are int32.  Padding slots of ID lists hold -1
+ *     ([QSA] QSARouteSelection.selected_token_ids).
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     non-zero status is returned with nothing enqueued and a message
+ *     available from irb_last_error() (thread-local).  Status codes mirror
+ *     the error classes of [LATENT] cudnn_sparse_attention:
+ *       IRB_ERR_UNAVAILABLE  no usable gfx950 device / code object (RuntimeError)
+ *       IRB_ERR_DTYPE        unsupported dtype (TypeError)
+ *       IRB_ERR_INVALID      bad shape, size, stride, scale or layout (ValueError)
+ *       IRB_ERR_HIP          a HIP launch or runtime call failed
+ *     There is no fallback: an unsupported request is an error.
+ *   - Contents of device inputs (IDs in range, cu_seqlens increasing) cannot
+ *     be checked without a device->host read; kernels treat out-of-range IDs
+ *     as padding where stated, and otherwise require the stated contract.
+ */
+#ifndef IRB_H_
+#define IRB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum irb_status_code {
+  IRB_OK = 0,
+  IRB_ERR_UNAVAILABLE = 1,
+  IRB_ERR_DTYPE = 2,
+  IRB_ERR_INVALID = 3,
+  IRB_ERR_HIP = 4
+};
+
+/* Element type of activation tensors.  bf16 is stored as raw 16-bit words. */
+enum irb_dtype { IRB_F32 = 0, IRB_BF16 = 1 };
+
+/*
+ * Token layout of B rows of S physical tokens ([QSA] indexer forward,
+ * _forward_packed, right_padded_sequence_lengths).  Exactly one of:
+ *   cu_seqlens != NULL : packed documents, B must be 1; device int32
+ *                        [num_docs+1], 0 = cu[0] < cu[1] < ... <= S.
+ *                        Tokens at or past cu[num_docs] are padding.
+ *   row_lens   != NULL : device int32 [B]; row b is one document of
+ *                        row_lens[b] tokens (0..S) followed by padding.
+ *   both NULL          : every row is one document of S tokens.
+ * Compression groups, visibility and routes never cross a document
+ * boundary; IDs are token indices within the row (packed: within the packed
+ * row), block IDs are consecutive over a row's documents.
+ */
+typedef struct irb_layout {
+  int32_t B;
+  int32_t S;
+  const int32_t* cu_seqlens;
+  int32_t num_docs;
+  const int32_t* row_lens;
+} irb_layout;
+
+/* 1 when a gfx950 device is present and the code objects load, else 0. */
+int irb_is_available(void);
+/* Message of the last failed call on this thread ("" if none). */
+const char* irb_last_error(void);
+const char* irb_version(void);
+
+/*
+ * a1 -- [QSA] Qwen3_8_FlashNextQSAIndexer (class docstring): every complete
+ * group of c consecutive raw index keys of a document is averaged in FP32,
+ * RMS-normalised (u = m * rsqrt(mean(m^2) + eps) * gamma) and rotated with
+ * the rotary row of the group's FIRST token ([QSA] apply_qsa_rope: row =
+ * cat(cos[D_rope/2], sin[D_rope/2]); dimension i < D_rope/2 pairs with
+ * i + D_rope/2; dimensions >= D_rope pass through).  An incomplete trailing
+ * group is not compressed.
+ *
+ *   k_idx     [B, S, D_idx] dtype, element strides (stride_b, stride_t), last dim contiguous
+ *   gamma     [D_idx] fp32 gain
+ *   freqs     [B, S, D_rope] fp32 contiguous, per-token document-relative rotary rows
+ *   kc        OUT [B, S/c, D_idx] fp32 contiguous; block j of a row at kc[b, j];
+ *             slots past the row's block count are zero
+ *   cu_blocks OUT device int32 [num_docs+1] block prefix of a packed layout
+ *             (cu_blocks[d] = sum_{d'<d} floor(len_d'/c)); required when
+ *             packed, ignored (may be NULL) otherwise.
+ * Requires 1 <= c <= 64, D_idx in {32,64,...,512} (multiple of 32),
+ * D_rope even, 0 <= D_rope <= D_idx.
+ */
+int irb_compress_keys(const irb_layout* layout, int c, const void* k_idx, int dtype,
+                      int64_t stride_b, int64_t stride_t, int D_idx, const float* gamma,
+                      float eps, const float* freqs, int D_rope, float* kc, int32_t* cu_blocks,
+                      void* stream);
+
+/*
+ * a2 -- [CSA] indexer_score_tile (weighted-ReLU scoring into one bounded FP32
+ * tile, signed FP32 head weights) with the visibility rule of [QSA]
+ * select_qsa_token_ids (query at document position p sees the first
+ * floor((p+1)/c) complete blocks of its own document):
+ *     out[b, t-q0, j-j0] = score_scale * sum_h w[b,t,h] * max(0, q[b,t,h,:] . kc[b,j,:])
+ * for visible j, and -inf otherwise (padding queries: all -inf).
+ * The products use bf16 MFMA with kc split into bf16 high+low parts and FP32
+ * accumulation (fp32 queries are split the same way).
+ *
+ *   q_idx  [B, S, H_idx, D_idx] dtype contiguous
+ *   w      [B, S, H_idx] fp32 contiguous
+ *   kc     [B, S/c, D_idx] fp32 (as written by irb_compress_keys)
+ *   cu_blocks as written by irb_compress_keys (packed layouts), else NULL
+ *   out    OUT fp32, element (b, t-q0, j-j0) at out[(b*(q1-q0) + t-q0)*out_row_stride + j-j0]
+ * Requires 0 <= q0 < q1 <= S, 0 <= j0 < j1 <= S/c, out_row_stride >= j1-j0,
+ * H_idx in {4, 8, 16, 32, 48, 64}, D_idx in {32, 64, 128}, score_scale > 0.
+ */
+int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtype, int H_idx,
+                           int D_idx, const float* w, const float* kc, const int32_t* cu_blocks,
+                           int c, float score_scale, int q0, int q1, int j0, int j1, float* out,
+                           int64_t out_row_stride, void* stream);
+
+/*
+ * a3 -- [QSA] select_qsa_token_ids (the best budget/c blocks) and [CSA]
+ * RegionMetadata.dense_region_ids / RegionSelection.region_ids: each valid
+ * query t in [q0, q1) takes k_eff = min(topk, nb(t)) of its visible blocks
+ * with the largest scores; equal scores go to the lower block ID, -0.0 and
+ * +0.0 are equal, NaN ranks below -inf.  IDs are written ascending, then -1.
+ * Padding queries: cnt = 0, all -1.
+ *
+ *   scores  fp32 rows for queries q0..q1-1; row r at scores + (b*(q1-q0)+r)*score_row_stride,
+ *           column j = block ID j (the tile must start at block 0 and cover
+ *           every block visible to its rows)
+ *   sel     OUT [B, S, topk] int32 (rows q0..q1-1 written)
+ *   cnt     OUT [B, S] int32 (rows q0..q1-1 written)
+ * Requires 1 <= topk <= 4096, 1 <= c.
+ */
+int irb_select_topk_regions(const irb_layout* layout, const float* scores, int64_t score_row_stride,
+                            int q0, int q1, const int32_t* cu_blocks, int c, int topk, int32_t* sel,
+                            int32_t* cnt, void* stream);
+
+/*
+ * a2+a3 in one call: the same sel/cnt as irb_indexer_score_tile followed by
+ * irb_select_topk_regions over [q0, q1), with the FP32 scores of at most a
+ * bounded number of query rows alive at a time ([QSA] select_qsa_token_ids:
+ * chunking bounds the score temporary without changing top-k semantics).
+ * workspace: device scratch; irb_route_topk_fused_workspace_size() gives a
+ * 256 MiB-budget size, any size holding at least one score row works (rows
+ * per chunk = ws_bytes / (B * (S/c) * 4)).
+ */
+size_t irb_route_topk_fused_workspace_size(int B, int S, int c, int topk, int q0, int q1);
+int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype, int H_idx,
+                         int D_idx, const float* w, const float* kc, const int32_t* cu_blocks,
+                         int c, float score_scale, int topk, int q0, int q1, int32_t* sel,
+                         int32_t* cnt, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * a4 -- [QSA] select_qsa_token_ids: selected blocks expand to their c token
+ * IDs, then the tokens of the current incomplete group [doc_start + nb*c, t]
+ * are appended; plus the window [max(doc_start, t-window+1), t] ([CSA]
+ * RegionMetadata.window_layout: the query and at most window-1 earlier keys).
+ * The union is written ascending without duplicates ([QSA] qsa_gqa_attention:
+ * duplicates collapse), then -1 up to width L; lens[t] = its size.
+ *
+ *   sel, cnt  [B, S, topk] / [B, S] as written by irb_select_topk_regions
+ *   routes    OUT [B, S, L] int32;  lens OUT [B, S] int32
+ * Requires L >= topk*c + max(window, c-1) (the [QSA] width budget + c - 1 when
+ * window == 0), window >= 0.
+ */
+int irb_expand_and_compact_routes(const irb_layout* layout, const int32_t* sel, const int32_t* cnt,
+                                  int topk, int c, int window, const int32_t* cu_blocks, int L,
+                                  int32_t* routes, int32_t* lens, void* stream);
+
+/*
+ * a4 (compaction) -- [LATENT] _compact_and_sort_indices: each row of `width`
+ * signed IDs becomes its ascending, duplicate-free valid prefix (valid =
+ * 0 <= id < key_count) followed by -1; lens[r] = prefix length.  IDs at or
+ * past key_count are dropped and counted into *out_of_range (device int32,
+ * nullable; incremented, so zero it first).
+ *
+ *   ids_in [n_rows, width] int32, ids_out OUT [n_rows, width], lens OUT [n_rows]
+ * Requires 1 <= width <= 8192, 1 <= key_count < 2^31.  ids_in == ids_out is allowed.
+ */
+int irb_compact_routes(const int32_t* ids_in, int64_t n_rows, int width, int64_t key_count,
+                       int32_t* ids_out, int32_t* lens, int32_t* out_of_range, void* stream);
+
+/*
+ * a5 -- [FA4] _block_lists / _selected_block_lists / _BackwardBlockPartition:
+ * block lists from token routes without a dense grid in HBM.
+ *   reverse == 0: rows = ceil(S_q/block_q) query tiles; row i lists, ascending,
+ *                 the key tiles floor(k/block_k) holding a routed key of one
+ *                 of its queries.
+ *   reverse == 1: rows = ceil(S_k/block_k) key tiles; row j lists, ascending,
+ *                 the query tiles that route to it (key-to-query lists used
+ *                 by the backward pass).
+ *   routes [B, S_q, L], lens [B, S_q] (ascending valid prefixes)
+ *   counts OUT [B, rows] int32; indices OUT [B, rows, width] int32, -1 after the count
+ *   workspace: irb_build_block_lists_workspace_size() bytes of device scratch
+ * Requires width >= number of tiles on the other axis, block_q, block_k >= 1.
+ */
+size_t irb_build_block_lists_workspace_size(int B, int S_q, int S_k, int block_q, int block_k);
+int irb_build_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L,
+                          int block_q, int block_k, int reverse, int32_t* counts, int32_t* indices,
+                          int width, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * a6 -- [QSA] gathered_qsa_gqa_attention / qsa_gqa_attention and [LATENT]
+ * cudnn_sparse_attention: every valid query attends only to the keys at
+ * routes[b, t, 0:lens[b,t]]; query head h uses KV head h / (Hq/Hkv)
+ * (consecutive heads share a group):
+ *     o = softmax(softmax_scale * q K_R^T) V_R,  lse = logsumexp(scale * q K_R^T)
+ * A query with lens = 0 gets o = 0 and lse = -inf.  Softmax and both
+ * products accumulate in FP32; o is rounded once to the input dtype.
+ *
+ *   q [B, S_q, Hq, Dqk], k [B, S_k, Hkv, Dqk], v [B, S_k, Hkv, Dv]: dtype,
+ *     element strides strides[0..2] = q (batch, token, head), [3..5] = k,
+ *     [6..8] = v; the last dimension is contiguous.  A latent layout passes
+ *     v = k (the value is the first Dv channels of each key row).
+ *   routes [B, S_q, L] int32: routes[b,t,0:lens] ascending, unique, in [0, S_k)
+ *   out OUT [B, S_q, Hq, Dv] dtype contiguous; lse OUT [B, Hq, S_q] fp32
+ * Requires Hq % Hkv == 0, Hq/Hkv <= 64, (Dqk, Dv) in {(64,64), (128,128)} or,
+ * for bf16, (576,512); strides and q/k/v addresses 16-byte aligned;
+ * softmax_scale > 0.
+ */
+int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype,
+                                 const int64_t* strides, const int32_t* routes, const int32_t* lens,
+                                 int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
+                                 float softmax_scale, void* out, float* lse, void* stream);
+
+/*
+ * a7 -- gradients of irb_sparse_gqa_attention_fwd ([QSA]
+ * gathered_qsa_gqa_attention is the differentiable reference; the indexer is
+ * frozen, so only q, k and v receive gradients):
+ *     P = exp(scale q K_R^T - lse), dP = dO V_R^T, Delta = rowsum(dO * o),
+ *     dS = P (dP - Delta), dq = scale dS K_R, dK += scale dS^T q, dV += P^T dO.
+ * dq is computed per query over its route; dK and dV per key tile over the
+ * reverse lists ([FA4] _selected_block_lists, reverse): rev_counts /
+ * rev_indices from irb_build_block_lists(reverse=1) with the same
+ * rev_block_q, rev_block_k.  No atomics: results are deterministic.
+ *
+ *   out        the forward's output (accepted for interface symmetry, not read:
+ *              Delta is recomputed with o in FP32 so that the rounding of the
+ *              stored output does not enter dS)
+ *   lse        the forward's lse; dout [B, S_q, Hq, Dv] dtype contiguous
+ *   dq OUT [B, S_q, Hq, Dqk] dtype contiguous
+ *   dk OUT [B, S_k, Hkv, Dqk] dtype contiguous, dv OUT [B, S_k, Hkv, Dv]
+ *     dtype contiguous.  dk == dv (latent: v aliases k) writes the merged
+ *     gradient dK + [dV, 0] into dk.
+ *   workspace: irb_sparse_gqa_attention_bwd_workspace_size() bytes of device scratch
+ * Requirements as for the forward, plus rev_block_k in {16, 32, 64}.
+ */
+size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int Hq, int Hkv, int Dqk, int Dv);
+int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, int dtype,
+                                 const int64_t* strides, const void* out, const void* dout,
+                                 const float* lse, const int32_t* routes, const int32_t* lens,
+                                 const int32_t* rev_counts, const int32_t* rev_indices,
+                                 int rev_block_q, int rev_block_k, int rev_width, int B, int S_q,
+                                 int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
+                                 float softmax_scale, void* dq, void* dk, void* dv, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IRB_H_ */

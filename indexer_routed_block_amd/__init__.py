@@ -1,0 +1,339 @@
+"""Python binding of libirb (learned-indexer routed sparse attention, MI355X).
+
+Argument marshalling only: every function below checks nothing that the C
+library does not check itself, allocates its outputs with torch on the
+tensors' device, and calls the same-named ``irb_*`` entry point on the
+current HIP stream.  All arithmetic runs in the library's HIP kernels.
+There is no fallback: if ``libirb.so`` is missing or no gfx950 device is
+current, calls raise ``RuntimeError``.
+
+Status codes map to exceptions as in the latent page's
+``cudnn_sparse_attention``: unavailable -> RuntimeError, dtype -> TypeError,
+invalid argument -> ValueError, HIP failure -> RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libirb.so")
+
+IRB_F32, IRB_BF16 = 0, 1
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+
+class IrbLayout(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("cu_seqlens", _P),
+                ("num_docs", ctypes.c_int32), ("row_lens", _P)]
+
+
+_SIGS = {
+    "irb_is_available": ([], _I),
+    "irb_last_error": ([], ctypes.c_char_p),
+    "irb_version": ([], ctypes.c_char_p),
+    "irb_compress_keys": ([_P, _I, _P, _I, _I64, _I64, _I, _P, _F, _P, _I, _P, _P, _P], _I),
+    "irb_indexer_score_tile": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _I, _P, _I64, _P], _I),
+    "irb_select_topk_regions": ([_P, _P, _I64, _I, _I, _P, _I, _I, _P, _P, _P], _I),
+    "irb_route_topk_fused_workspace_size": ([_I, _I, _I, _I, _I, _I], _SZ),
+    "irb_route_topk_fused": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "irb_expand_and_compact_routes": ([_P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P], _I),
+    "irb_compact_routes": ([_P, _I64, _I, _I64, _P, _P, _P, _P], _I),
+    "irb_build_block_lists_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
+    "irb_build_block_lists": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _SZ, _P], _I),
+    "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "irb_sparse_gqa_attention_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _SZ),
+    "irb_sparse_gqa_attention_bwd": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                      _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libirb.so (once) and declare every entry point's signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libirb.so not found at {path}; build it with indexer_routed_block_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def is_available() -> bool:
+    return bool(load_library().irb_is_available())
+
+
+def _check(status: int) -> None:
+    if status == 0:
+        return
+    msg = load_library().irb_last_error().decode()
+    if status == 2:
+        raise TypeError(msg)
+    if status == 3:
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _gpu(*tensors) -> torch.device:
+    """Device shared by every given tensor; it must be a GPU (no CPU path exists)."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise RuntimeError(f"libirb runs on the GPU only; got a tensor on {t.device}")
+        if dev is not None and t.device != dev:
+            raise RuntimeError("all tensors must be on one device")
+        dev = t.device
+    return dev
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return IRB_BF16
+    if t.dtype == torch.float32:
+        return IRB_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_layout(B: int, S: int, cu_seqlens: Optional[torch.Tensor] = None,
+                row_lens: Optional[torch.Tensor] = None) -> IrbLayout:
+    """Layout struct; ``num_docs`` comes from the host-side shape of cu_seqlens."""
+    nd = 0 if cu_seqlens is None else int(cu_seqlens.numel()) - 1
+    return IrbLayout(B, S, None if cu_seqlens is None else cu_seqlens.data_ptr(), nd,
+                     None if row_lens is None else row_lens.data_ptr())
+
+
+def route_width(topk: int, c: int, window: int) -> int:
+    """Fixed route width topk*c + max(window, c-1) (shape bookkeeping only)."""
+    return topk * c + max(window, c - 1)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def compress_keys(k_idx, gamma, freqs, c, eps=1e-5, cu_seqlens=None, row_lens=None):
+    """irb_compress_keys: returns (kc [B, S//c, D] fp32, cu_blocks or None)."""
+    _gpu(k_idx, gamma, freqs, cu_seqlens, row_lens)
+    lib = load_library()
+    B, S, D = k_idx.shape
+    dev = k_idx.device
+    kc = torch.empty((B, S // c, D), dtype=torch.float32, device=dev)
+    cu_blocks = None if cu_seqlens is None else torch.empty(cu_seqlens.numel(), dtype=torch.int32, device=dev)
+    lay = make_layout(B, S, cu_seqlens, row_lens)
+    _check(lib.irb_compress_keys(ctypes.byref(lay), c, _ptr(k_idx), _dtype_code(k_idx), k_idx.stride(0),
+                                 k_idx.stride(1), D, _ptr(gamma), eps, _ptr(freqs), freqs.shape[-1], _ptr(kc),
+                                 _ptr(cu_blocks), _stream(dev)))
+    return kc, cu_blocks
+
+
+def indexer_score_tile(q_idx, w, kc, c, q0=0, q1=None, j0=0, j1=None, score_scale=None, cu_blocks=None,
+                       cu_seqlens=None, row_lens=None, out=None):
+    """irb_indexer_score_tile: FP32 scores [B, q1-q0, j1-j0] (-inf where not visible)."""
+    _gpu(q_idx, w, kc, cu_blocks, cu_seqlens, row_lens, out)
+    lib = load_library()
+    B, S, H, D = q_idx.shape
+    q1 = S if q1 is None else q1
+    j1 = S // c if j1 is None else j1
+    scale = 1.0 / math.sqrt(D) if score_scale is None else score_scale
+    if out is None:
+        out = torch.empty((B, q1 - q0, j1 - j0), dtype=torch.float32, device=q_idx.device)
+    lay = make_layout(B, S, cu_seqlens, row_lens)
+    _check(lib.irb_indexer_score_tile(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), H, D, _ptr(w), _ptr(kc),
+                                      _ptr(cu_blocks), c, scale, q0, q1, j0, j1, _ptr(out), out.stride(1),
+                                      _stream(q_idx.device)))
+    return out
+
+
+def select_topk_regions(scores, c, topk, S, q0=0, cu_blocks=None, cu_seqlens=None, row_lens=None, sel=None,
+                        cnt=None):
+    """irb_select_topk_regions over score rows q0..q0+rows: (sel [B,S,topk], cnt [B,S])."""
+    _gpu(scores, cu_blocks, cu_seqlens, row_lens, sel, cnt)
+    lib = load_library()
+    B, rows, _ = scores.shape
+    dev = scores.device
+    if sel is None:
+        sel = torch.full((B, S, topk), -1, dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.zeros((B, S), dtype=torch.int32, device=dev)
+    lay = make_layout(B, S, cu_seqlens, row_lens)
+    _check(lib.irb_select_topk_regions(ctypes.byref(lay), _ptr(scores), scores.stride(1), q0, q0 + rows,
+                                       _ptr(cu_blocks), c, topk, _ptr(sel), _ptr(cnt), _stream(dev)))
+    return sel, cnt
+
+
+def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_blocks=None, cu_seqlens=None,
+                     row_lens=None, workspace=None, sel=None, cnt=None):
+    """irb_route_topk_fused: scores and selection over bounded score chunks."""
+    _gpu(q_idx, w, kc, cu_blocks, cu_seqlens, row_lens, workspace, sel, cnt)
+    lib = load_library()
+    B, S, H, D = q_idx.shape
+    dev = q_idx.device
+    q1 = S if q1 is None else q1
+    scale = 1.0 / math.sqrt(D) if score_scale is None else score_scale
+    if workspace is None:
+        n = lib.irb_route_topk_fused_workspace_size(B, S, c, topk, q0, q1)
+        workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
+    if sel is None:
+        sel = torch.full((B, S, topk), -1, dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.zeros((B, S), dtype=torch.int32, device=dev)
+    lay = make_layout(B, S, cu_seqlens, row_lens)
+    _check(lib.irb_route_topk_fused(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), H, D, _ptr(w), _ptr(kc),
+                                    _ptr(cu_blocks), c, scale, topk, q0, q1, _ptr(sel), _ptr(cnt), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(dev)))
+    return sel, cnt
+
+
+def expand_and_compact_routes(sel, cnt, c, window, topk, L=None, cu_blocks=None, cu_seqlens=None, row_lens=None):
+    """irb_expand_and_compact_routes: (routes [B,S,L] int32, lens [B,S] int32)."""
+    _gpu(sel, cnt, cu_blocks, cu_seqlens, row_lens)
+    lib = load_library()
+    B, S = cnt.shape
+    dev = cnt.device
+    L = route_width(topk, c, window) if L is None else L
+    routes = torch.empty((B, S, L), dtype=torch.int32, device=dev)
+    lens = torch.empty((B, S), dtype=torch.int32, device=dev)
+    lay = make_layout(B, S, cu_seqlens, row_lens)
+    _check(lib.irb_expand_and_compact_routes(ctypes.byref(lay), _ptr(sel), _ptr(cnt), topk, c, window,
+                                             _ptr(cu_blocks), L, _ptr(routes), _ptr(lens), _stream(dev)))
+    return routes, lens
+
+
+def compact_routes(ids, key_count, out=None, count_out_of_range=True):
+    """irb_compact_routes over the last axis: (ids_out, lens, out_of_range counter or None)."""
+    _gpu(ids, out)
+    lib = load_library()
+    width = ids.shape[-1]
+    rows = ids.numel() // width
+    dev = ids.device
+    out = torch.empty_like(ids) if out is None else out
+    lens = torch.empty(ids.shape[:-1], dtype=torch.int32, device=dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev) if count_out_of_range else None
+    _check(lib.irb_compact_routes(_ptr(ids), rows, width, key_count, _ptr(out), _ptr(lens), _ptr(bad), _stream(dev)))
+    return out, lens, bad
+
+
+def build_block_lists(routes, lens, S_k, block_q, block_k, reverse, width=None, workspace=None):
+    """irb_build_block_lists: (counts [B, rows], indices [B, rows, width])."""
+    _gpu(routes, lens, workspace)
+    lib = load_library()
+    B, S_q, L = routes.shape
+    dev = routes.device
+    nqt, nkt = -(-S_q // block_q), -(-S_k // block_k)
+    rows, other = (nkt, nqt) if reverse else (nqt, nkt)
+    width = other if width is None else width
+    if workspace is None:
+        n = lib.irb_build_block_lists_workspace_size(B, S_q, S_k, block_q, block_k)
+        workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
+    counts = torch.empty((B, rows), dtype=torch.int32, device=dev)
+    indices = torch.empty((B, rows, width), dtype=torch.int32, device=dev)
+    _check(lib.irb_build_block_lists(_ptr(routes), _ptr(lens), B, S_q, S_k, L, block_q, block_k, int(bool(reverse)),
+                                     _ptr(counts), _ptr(indices), width, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(dev)))
+    return counts, indices
+
+
+def _strides9(q, k, v):
+    return (ctypes.c_int64 * 9)(q.stride(0), q.stride(1), q.stride(2), k.stride(0), k.stride(1), k.stride(2),
+                                v.stride(0), v.stride(1), v.stride(2))
+
+
+def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None, lse=None):
+    """irb_sparse_gqa_attention_fwd: (o [B,S_q,Hq,Dv] in q's dtype, lse [B,Hq,S_q] fp32)."""
+    _gpu(q, k, v, routes, lens, out, lse)
+    lib = load_library()
+    B, S_q, Hq, Dqk = q.shape
+    S_k, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    dev = q.device
+    scale = 1.0 / math.sqrt(Dqk) if softmax_scale is None else softmax_scale
+    if out is None:
+        out = torch.empty((B, S_q, Hq, Dv), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev)
+    _check(lib.irb_sparse_gqa_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v),
+                                            _ptr(routes), _ptr(lens), B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv,
+                                            scale, _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, rev_indices, rev_block_q,
+                             rev_block_k=16, softmax_scale=None, merged_kv=False, workspace=None):
+    """irb_sparse_gqa_attention_bwd: (dq, dk, dv); with merged_kv (v aliases k) dk holds dK + [dV, 0], dv is dk."""
+    _gpu(q, k, v, out, dout, lse, routes, lens, rev_counts, rev_indices, workspace)
+    lib = load_library()
+    B, S_q, Hq, Dqk = q.shape
+    S_k, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    dev = q.device
+    scale = 1.0 / math.sqrt(Dqk) if softmax_scale is None else softmax_scale
+    dq = torch.empty((B, S_q, Hq, Dqk), dtype=q.dtype, device=dev)
+    dk = torch.empty((B, S_k, Hkv, Dqk), dtype=q.dtype, device=dev)
+    dv = dk if merged_kv else torch.empty((B, S_k, Hkv, Dv), dtype=q.dtype, device=dev)
+    if workspace is None:
+        n = lib.irb_sparse_gqa_attention_bwd_workspace_size(B, S_q, Hq, Hkv, Dqk, Dv)
+        workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
+    _check(lib.irb_sparse_gqa_attention_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v), _ptr(out), _ptr(dout), _ptr(lse),
+        _ptr(routes), _ptr(lens), _ptr(rev_counts), _ptr(rev_indices), rev_block_q, rev_block_k,
+        rev_indices.shape[-1], B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv, scale, _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# composition of the entry points (host scalars only; no device reads)
+# ---------------------------------------------------------------------------
+
+def first_sparse_query(c: int, topk: int) -> int:
+    """First document position whose query sees more than topk complete blocks."""
+    return (topk + 1) * c - 1
+
+
+def route(k_idx, q_idx, w, gamma, freqs, c, topk, window, eps=1e-5, score_scale=None, cu_seqlens=None,
+          row_lens=None, workspace=None):
+    """compress -> fused score/select -> expand, all in the library.
+
+    Returns dict(kc, cu_blocks, sel, cnt, routes, lens).  With a single
+    document per row, query rows before the first sparse position take every
+    visible block and are not scored.
+    """
+    B, S = q_idx.shape[:2]
+    kc, cu_blocks = compress_keys(k_idx, gamma, freqs, c, eps, cu_seqlens, row_lens)
+    q0 = 0 if cu_seqlens is not None else min(first_sparse_query(c, topk), S - 1)
+    sel = torch.empty((B, S, topk), dtype=torch.int32, device=q_idx.device)
+    cnt = torch.empty((B, S), dtype=torch.int32, device=q_idx.device)
+    if q0 > 0:
+        # rows that see at most topk blocks: selection needs no scores
+        dummy = torch.empty((B, q0, 1), dtype=torch.float32, device=q_idx.device)
+        select_topk_regions(dummy, c, topk, S, q0=0, cu_blocks=cu_blocks, cu_seqlens=cu_seqlens,
+                            row_lens=row_lens, sel=sel, cnt=cnt)
+    route_topk_fused(q_idx, w, kc, c, topk, q0=q0, q1=S, score_scale=score_scale, cu_blocks=cu_blocks,
+                     cu_seqlens=cu_seqlens, row_lens=row_lens, workspace=workspace, sel=sel, cnt=cnt)
+    routes, lens = expand_and_compact_routes(sel, cnt, c, window, topk, cu_blocks=cu_blocks, cu_seqlens=cu_seqlens,
+                                             row_lens=row_lens)
+    return dict(kc=kc, cu_blocks=cu_blocks, sel=sel, cnt=cnt, routes=routes, lens=lens)

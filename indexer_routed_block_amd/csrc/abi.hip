@@ -1,0 +1,308 @@
+// C ABI of libirb: argument validation, error reporting and dispatch.
+// Every entry point validates on the host, enqueues on the caller's stream and
+// returns without synchronising.  See include/irb.h for the contract.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "irb_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return IRB_OK;
+}
+
+// 1 if the current device is a gfx950, cached per device
+int device_ok() {
+  static int cache[64];   // 0 unknown, 1 yes, 2 no
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    cache[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  return cache[dev] == 1;
+}
+
+#define IRB_REQUIRE_DEVICE()                                                                  \
+  do {                                                                                        \
+    if (!device_ok()) return fail(IRB_ERR_UNAVAILABLE, "%s: no gfx950 device is current", __func__); \
+  } while (0)
+
+int launched(const char* fn, int rc) {
+  hipError_t e = rc ? static_cast<hipError_t>(rc) : hipGetLastError();
+  if (e != hipSuccess) return fail(IRB_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+int check_layout(const char* fn, const irb_layout* L, irb::Layout& out) {
+  if (!L) return fail(IRB_ERR_INVALID, "%s: layout is NULL", fn);
+  if (L->B < 1 || L->S < 1) return fail(IRB_ERR_INVALID, "%s: layout needs B >= 1 and S >= 1 (got %d, %d)", fn, L->B, L->S);
+  if (L->cu_seqlens && L->row_lens) return fail(IRB_ERR_INVALID, "%s: give cu_seqlens or row_lens, not both", fn);
+  if (L->cu_seqlens && L->B != 1) return fail(IRB_ERR_INVALID, "%s: packed documents need B == 1", fn);
+  if (L->cu_seqlens && L->num_docs < 1) return fail(IRB_ERR_INVALID, "%s: packed layout needs num_docs >= 1", fn);
+  out.B = L->B;
+  out.S = L->S;
+  out.cu_seqlens = L->cu_seqlens;
+  out.num_docs = L->cu_seqlens ? L->num_docs : 0;
+  out.row_lens = L->row_lens;
+  return 0;
+}
+
+int check_dtype(const char* fn, int dtype) {
+  if (dtype != IRB_F32 && dtype != IRB_BF16) return fail(IRB_ERR_DTYPE, "%s: dtype must be IRB_F32 or IRB_BF16 (got %d)", fn, dtype);
+  return 0;
+}
+
+bool score_heads_ok(int H) { return H >= 4 && H <= 64 && H % 4 == 0 && (16 % H == 0 || H % 16 == 0); }
+
+}  // namespace
+
+extern "C" {
+
+int irb_is_available(void) { return device_ok(); }
+
+const char* irb_last_error(void) { return g_err.c_str(); }
+
+const char* irb_version(void) { return "irb 0.1.0 gfx950"; }
+
+int irb_compress_keys(const irb_layout* layout, int c, const void* k_idx, int dtype, int64_t stride_b,
+                      int64_t stride_t, int D_idx, const float* gamma, float eps, const float* freqs, int D_rope,
+                      float* kc, int32_t* cu_blocks, void* stream) {
+  const char* fn = "irb_compress_keys";
+  irb::Layout L;
+  if (int r = check_layout(fn, layout, L)) return r;
+  if (int r = check_dtype(fn, dtype)) return r;
+  if (c < 1 || c > 64) return fail(IRB_ERR_INVALID, "%s: c must be in 1..64 (got %d)", fn, c);
+  if (D_idx < 32 || D_idx > 512 || D_idx % 32) return fail(IRB_ERR_INVALID, "%s: D_idx must be a multiple of 32 in 32..512", fn);
+  if (D_rope < 0 || D_rope > D_idx || D_rope % 2) return fail(IRB_ERR_INVALID, "%s: D_rope must be even and <= D_idx", fn);
+  if (stride_t < D_idx || stride_b < 0) return fail(IRB_ERR_INVALID, "%s: bad k_idx strides", fn);
+  if (!k_idx || !gamma || !kc || (D_rope > 0 && !freqs)) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks output", fn);
+  if (!(eps >= 0.f)) return fail(IRB_ERR_INVALID, "%s: eps must be >= 0", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_compress(L, c, k_idx, dtype, stride_b, stride_t, D_idx, gamma, eps, freqs, D_rope, kc,
+                                           cu_blocks, static_cast<hipStream_t>(stream)));
+}
+
+int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx,
+                           const float* w, const float* kc, const int32_t* cu_blocks, int c, float score_scale,
+                           int q0, int q1, int j0, int j1, float* out, int64_t out_row_stride, void* stream) {
+  const char* fn = "irb_indexer_score_tile";
+  irb::Layout L;
+  if (int r = check_layout(fn, layout, L)) return r;
+  if (int r = check_dtype(fn, dtype)) return r;
+  if (!score_heads_ok(H_idx)) return fail(IRB_ERR_INVALID, "%s: H_idx must be 4, 8, 16 or a multiple of 16 up to 64 (got %d)", fn, H_idx);
+  if (D_idx != 32 && D_idx != 64 && D_idx != 128) return fail(IRB_ERR_INVALID, "%s: D_idx must be 32, 64 or 128 (got %d)", fn, D_idx);
+  if (c < 1) return fail(IRB_ERR_INVALID, "%s: c must be >= 1", fn);
+  if (!(score_scale > 0.f)) return fail(IRB_ERR_INVALID, "%s: score_scale must be > 0", fn);
+  if (q0 < 0 || q1 <= q0 || q1 > L.S) return fail(IRB_ERR_INVALID, "%s: need 0 <= q0 < q1 <= S", fn);
+  if (j0 < 0 || j1 <= j0 || j1 > L.S / c) return fail(IRB_ERR_INVALID, "%s: need 0 <= j0 < j1 <= S/c", fn);
+  if (out_row_stride < j1 - j0) return fail(IRB_ERR_INVALID, "%s: out_row_stride < j1 - j0", fn);
+  if (!q_idx || !w || !kc || !out) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, cu_blocks, c, score_scale, q0, q1, j0, j1,
+                                             out, out_row_stride, static_cast<hipStream_t>(stream)));
+}
+
+int irb_select_topk_regions(const irb_layout* layout, const float* scores, int64_t score_row_stride, int q0, int q1,
+                            const int32_t* cu_blocks, int c, int topk, int32_t* sel, int32_t* cnt, void* stream) {
+  const char* fn = "irb_select_topk_regions";
+  irb::Layout L;
+  if (int r = check_layout(fn, layout, L)) return r;
+  if (c < 1) return fail(IRB_ERR_INVALID, "%s: c must be >= 1", fn);
+  if (topk < 1 || topk > 4096) return fail(IRB_ERR_INVALID, "%s: topk must be in 1..4096 (got %d)", fn, topk);
+  if (q0 < 0 || q1 <= q0 || q1 > L.S) return fail(IRB_ERR_INVALID, "%s: need 0 <= q0 < q1 <= S", fn);
+  if (score_row_stride < 1) return fail(IRB_ERR_INVALID, "%s: score_row_stride must be >= 1", fn);
+  if (!scores || !sel || !cnt) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_select(L, scores, score_row_stride, q0, q1, cu_blocks, c, topk, sel, cnt,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t irb_route_topk_fused_workspace_size(int B, int S, int c, int topk, int q0, int q1) {
+  (void)topk;
+  if (B < 1 || S < 1 || c < 1 || q1 <= q0) return 0;
+  const int64_t nb = S / c;
+  const int64_t rows_budget = nb > 0 ? ((static_cast<int64_t>(256) << 20) / (4 * nb)) : 1;
+  const int64_t rows = std::min<int64_t>(std::max<int64_t>(rows_budget / B, 512), q1 - q0);
+  return static_cast<size_t>(rows * B * std::max<int64_t>(nb, 1) * 4);
+}
+
+int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx, const float* w,
+                         const float* kc, const int32_t* cu_blocks, int c, float score_scale, int topk, int q0, int q1,
+                         int32_t* sel, int32_t* cnt, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "irb_route_topk_fused";
+  irb::Layout L;
+  if (int r = check_layout(fn, layout, L)) return r;
+  if (int r = check_dtype(fn, dtype)) return r;
+  if (!score_heads_ok(H_idx)) return fail(IRB_ERR_INVALID, "%s: unsupported H_idx %d", fn, H_idx);
+  if (D_idx != 32 && D_idx != 64 && D_idx != 128) return fail(IRB_ERR_INVALID, "%s: D_idx must be 32, 64 or 128", fn);
+  if (c < 1 || topk < 1 || topk > 4096) return fail(IRB_ERR_INVALID, "%s: bad c or topk", fn);
+  if (!(score_scale > 0.f)) return fail(IRB_ERR_INVALID, "%s: score_scale must be > 0", fn);
+  if (q0 < 0 || q1 <= q0 || q1 > L.S) return fail(IRB_ERR_INVALID, "%s: need 0 <= q0 < q1 <= S", fn);
+  if (!q_idx || !w || !kc || !sel || !cnt || !workspace) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
+  const int nb = L.S / c;
+  if (nb < 1) return fail(IRB_ERR_INVALID, "%s: S/c must be >= 1", fn);
+  const int64_t per_row = static_cast<int64_t>(L.B) * nb * 4;
+  const int64_t rows = static_cast<int64_t>(ws_bytes) / per_row;
+  if (rows < 1) return fail(IRB_ERR_INVALID, "%s: workspace too small (%zu bytes)", fn, ws_bytes);
+  IRB_REQUIRE_DEVICE();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* scores = static_cast<float*>(workspace);
+  for (int a = q0; a < q1; a += static_cast<int>(std::min<int64_t>(rows, q1 - a))) {
+    const int e = a + static_cast<int>(std::min<int64_t>(rows, q1 - a));
+    int rc = irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, cu_blocks, c, score_scale, a, e, 0, nb, scores, nb, st);
+    if (!rc) rc = irb::launch_select(L, scores, nb, a, e, cu_blocks, c, topk, sel, cnt, st);
+    if (rc) return launched(fn, rc);
+  }
+  return launched(fn, 0);
+}
+
+int irb_expand_and_compact_routes(const irb_layout* layout, const int32_t* sel, const int32_t* cnt, int topk, int c,
+                                  int window, const int32_t* cu_blocks, int L_width, int32_t* routes, int32_t* lens,
+                                  void* stream) {
+  const char* fn = "irb_expand_and_compact_routes";
+  irb::Layout L;
+  if (int r = check_layout(fn, layout, L)) return r;
+  if (c < 1 || topk < 0 || window < 0) return fail(IRB_ERR_INVALID, "%s: need c >= 1, topk >= 0, window >= 0", fn);
+  const int64_t need = static_cast<int64_t>(topk) * c + std::max(window, c - 1);
+  if (L_width < need) return fail(IRB_ERR_INVALID, "%s: width %d < topk*c + max(window, c-1) = %lld", fn, L_width, (long long)need);
+  if ((topk > 0 && (!sel || !cnt)) || !routes || !lens) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_expand(L, sel, cnt, topk, c, window, cu_blocks, L_width, routes, lens,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int irb_compact_routes(const int32_t* ids_in, int64_t n_rows, int width, int64_t key_count, int32_t* ids_out,
+                       int32_t* lens, int32_t* out_of_range, void* stream) {
+  const char* fn = "irb_compact_routes";
+  if (n_rows < 0 || n_rows > 0x7fffffff) return fail(IRB_ERR_INVALID, "%s: n_rows out of range", fn);
+  if (width < 1 || width > 8192) return fail(IRB_ERR_INVALID, "%s: width must be in 1..8192 (got %d)", fn, width);
+  if (key_count < 1 || key_count > 0x7fffffff) return fail(IRB_ERR_INVALID, "%s: key_count must be in 1..2^31-1", fn);
+  if (!ids_in || !ids_out || !lens) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_compact(ids_in, n_rows, width, key_count, ids_out, lens, out_of_range,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t irb_build_block_lists_workspace_size(int B, int S_q, int S_k, int block_q, int block_k) {
+  if (B < 1 || S_q < 1 || S_k < 1 || block_q < 1 || block_k < 1) return 0;
+  const int64_t nqt = (S_q + block_q - 1) / block_q, nkt = (S_k + block_k - 1) / block_k;
+  const int64_t fwd = nqt * ((nkt + 31) / 32), rev = nkt * ((nqt + 31) / 32);
+  return static_cast<size_t>(B) * static_cast<size_t>(std::max(fwd, rev)) * 4;
+}
+
+int irb_build_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L_width,
+                          int block_q, int block_k, int reverse, int32_t* counts, int32_t* indices, int width,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "irb_build_block_lists";
+  if (B < 1 || S_q < 1 || S_k < 1 || L_width < 1) return fail(IRB_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (block_q < 1 || block_k < 1) return fail(IRB_ERR_INVALID, "%s: block sizes must be >= 1", fn);
+  const int nqt = (S_q + block_q - 1) / block_q, nkt = (S_k + block_k - 1) / block_k;
+  const int other = reverse ? nqt : nkt;
+  if (width < other) return fail(IRB_ERR_INVALID, "%s: width %d < %d tiles", fn, width, other);
+  if (ws_bytes < irb_build_block_lists_workspace_size(B, S_q, S_k, block_q, block_k))
+    return fail(IRB_ERR_INVALID, "%s: workspace too small", fn);
+  if (!routes || !lens || !counts || !indices || !workspace) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_block_lists(routes, lens, B, S_q, S_k, L_width, block_q, block_k, reverse ? 1 : 0, counts,
+                                              indices, width, static_cast<uint32_t*>(workspace),
+                                              static_cast<hipStream_t>(stream)));
+}
+
+static int check_attn(const char* fn, const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
+                      const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L_width, int Hq,
+                      int Hkv, int Dqk, int Dv, float scale, irb::AttnArgs& a) {
+  if (int r = check_dtype(fn, dtype)) return r;
+  if (B < 1 || S_q < 1 || S_k < 1 || L_width < 1) return fail(IRB_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(IRB_ERR_INVALID, "%s: Hq must be a multiple of Hkv", fn);
+  if (Hq / Hkv > 64) return fail(IRB_ERR_INVALID, "%s: Hq/Hkv must be <= 64", fn);
+  const bool dims_ok = dtype == IRB_BF16 ? ((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128) || (Dqk == 576 && Dv == 512))
+                                         : ((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128));
+  if (!dims_ok) return fail(IRB_ERR_INVALID, "%s: unsupported head dims (%d, %d)", fn, Dqk, Dv);
+  if (!(scale > 0.f)) return fail(IRB_ERR_INVALID, "%s: softmax_scale must be > 0", fn);
+  if (!q || !k || !v || !strides || !routes || !lens) return fail(IRB_ERR_INVALID, "%s: NULL argument", fn);
+  for (int i = 0; i < 9; ++i)
+    if (strides[i] < 0) return fail(IRB_ERR_INVALID, "%s: negative stride", fn);
+  if (strides[2] < Dqk || strides[5] < Dqk || strides[8] < Dv) return fail(IRB_ERR_INVALID, "%s: head stride below head dim", fn);
+  // 16-byte vector loads of rows need 16-byte aligned rows
+  const int esz = dtype == IRB_BF16 ? 2 : 4;
+  for (int i = 0; i < 9; ++i)
+    if ((strides[i] * esz) % 16) return fail(IRB_ERR_INVALID, "%s: strides must be multiples of 16 bytes", fn);
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) % 16)
+    return fail(IRB_ERR_INVALID, "%s: q, k, v must be 16-byte aligned", fn);
+  a.q = q; a.k = k; a.v = v;
+  a.sq_b = strides[0]; a.sq_t = strides[1]; a.sq_h = strides[2];
+  a.sk_b = strides[3]; a.sk_t = strides[4]; a.sk_h = strides[5];
+  a.sv_b = strides[6]; a.sv_t = strides[7]; a.sv_h = strides[8];
+  a.routes = routes; a.lens = lens;
+  a.B = B; a.S_q = S_q; a.S_k = S_k; a.L = L_width; a.Hq = Hq; a.Hkv = Hkv; a.Dqk = Dqk; a.Dv = Dv;
+  a.scale = scale; a.dtype = dtype;
+  return 0;
+}
+
+int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
+                                 const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L_width,
+                                 int Hq, int Hkv, int Dqk, int Dv, float softmax_scale, void* out, float* lse,
+                                 void* stream) {
+  const char* fn = "irb_sparse_gqa_attention_fwd";
+  irb::AttnArgs a;
+  if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv, softmax_scale, a))
+    return r;
+  if (!out || !lse) return fail(IRB_ERR_INVALID, "%s: NULL output", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_attn_fwd(a, out, lse, static_cast<hipStream_t>(stream)));
+}
+
+size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int Hq, int Hkv, int Dqk, int Dv) {
+  if (B < 1 || S_q < 1 || Hq < 1 || Hkv < 1) return 0;
+  return irb::attn_bwd_workspace_bytes(B, S_q, Hq, Hkv, Dqk, Dv);
+}
+
+int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
+                                 const void* out, const void* dout, const float* lse, const int32_t* routes,
+                                 const int32_t* lens, const int32_t* rev_counts, const int32_t* rev_indices,
+                                 int rev_block_q, int rev_block_k, int rev_width, int B, int S_q, int S_k, int L_width,
+                                 int Hq, int Hkv, int Dqk, int Dv, float softmax_scale, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "irb_sparse_gqa_attention_bwd";
+  irb::AttnBwdArgs a;
+  if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv, softmax_scale, a.f))
+    return r;
+  if (!out || !dout || !lse || !rev_counts || !rev_indices || !dq || !dk || !dv) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (rev_block_k != 16) return fail(IRB_ERR_INVALID, "%s: rev_block_k must be 16 (got %d)", fn, rev_block_k);
+  if (rev_block_q < 1) return fail(IRB_ERR_INVALID, "%s: rev_block_q must be >= 1", fn);
+  if (rev_width < (S_q + rev_block_q - 1) / rev_block_q) return fail(IRB_ERR_INVALID, "%s: rev_width below the query tile count", fn);
+  if (dk == dv && Dv > Dqk) return fail(IRB_ERR_INVALID, "%s: merged dk/dv needs Dv <= Dqk", fn);
+  if (ws_bytes < irb::attn_bwd_workspace_bytes(B, S_q, Hq, Hkv, Dqk, Dv)) return fail(IRB_ERR_INVALID, "%s: workspace too small", fn);
+  if (!workspace) return fail(IRB_ERR_INVALID, "%s: NULL workspace", fn);
+  a.out = out; a.dout = dout; a.lse = lse;
+  a.rev_counts = rev_counts; a.rev_indices = rev_indices;
+  a.rev_bq = rev_block_q; a.rev_bk = rev_block_k; a.rev_width = rev_width;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.ws = workspace; a.ws_bytes = ws_bytes;
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_attn_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,605 @@
+// a7: sparse GQA attention backward.
+//
+// Gradients of the routed attention of the QSA page (nemo_automodel...
+// qwen3_8_flash_next.qsa, gathered_qsa_gqa_attention: differentiable, indexer
+// frozen) for q, k, v; the key side runs over reverse key-to-query lists as
+// in the FA4 page (step5.fa4, _selected_block_lists with reverse=True,
+// _BackwardBlockPartition).  Latent shared KV (common.cudnn_sparse_attention):
+// the merged gradient dK + [dV, 0] lands in one buffer.
+//
+// Four launches, no atomics (deterministic):
+//  prep  copies of q and dO with the heads of a KV group innermost
+//        ([b, t, kvh, dim, Gp]) so that the key-side MFMAs can read
+//        (rows x dims)^T operands with 8/16-byte loads.
+//  delta Delta[b,h,t] = rowsum(dO * o) from the forward kernel run again with
+//        o kept in FP32 (the stored bf16 output would put its rounding into
+//        every dS of the row, and dK sums those coherently).
+//  dq    per (query, KV head): like the forward, S^T = K Q^T and
+//        dP^T = V dO^T on gathered rows, dS^T = P^T (dP^T - Delta),
+//        dQ^T += K^T dS^T with K^T read transposed from LDS.
+//  dkdv  per (16-key tile, KV head), one wavefront: walks the reverse list,
+//        finds each listed query's keys inside the tile by binary search in
+//        its ascending route, packs hitting queries 32 (query, head) rows at
+//        a time and accumulates dV^T += dO^T P and dK^T += q^T dS in
+//        registers.  The P and dS accumulators are already laid out as the B
+//        operand of those products, so nothing moves between lanes; they
+//        enter as bf16 high + low halves so the long key-side sums keep FP32
+//        accuracy.
+#include "irb_internal.hpp"
+
+namespace irb {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+
+IRB_DEV void bld8(const uint16_t* p, bf16x8& hi, bf16x8& lo) {
+  hi = *reinterpret_cast<const bf16x8*>(p);
+  (void)lo;
+}
+IRB_DEV void bld8(const float* p, bf16x8& hi, bf16x8& lo) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint16_t h, l;
+    split_bf16(f[e], h, l);
+    hi[e] = static_cast<short>(h);
+    lo[e] = static_cast<short>(l);
+  }
+}
+// 4 consecutive elements into operand slots [o, o+4)
+IRB_DEV void bld4(const uint16_t* p, bf16x8& hi, bf16x8& lo, int o) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  hi[o + 0] = static_cast<short>(u.x & 0xffffu);
+  hi[o + 1] = static_cast<short>(u.x >> 16);
+  hi[o + 2] = static_cast<short>(u.y & 0xffffu);
+  hi[o + 3] = static_cast<short>(u.y >> 16);
+  (void)lo;
+}
+IRB_DEV void bld4(const float* p, bf16x8& hi, bf16x8& lo, int o) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float f[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint16_t h, l;
+    split_bf16(f[e], h, l);
+    hi[o + e] = static_cast<short>(h);
+    lo[o + e] = static_cast<short>(l);
+  }
+}
+IRB_DEV void bzero8(bf16x8& x) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0;
+}
+IRB_DEV void bput(bf16x8& hi, bf16x8& lo, int e, uint16_t v) { hi[e] = static_cast<short>(v); (void)lo; }
+IRB_DEV void bput(bf16x8& hi, bf16x8& lo, int e, float v) {
+  uint16_t h, l;
+  split_bf16(v, h, l);
+  hi[e] = static_cast<short>(h);
+  lo[e] = static_cast<short>(l);
+}
+IRB_DEV void bput_f(bf16x8& hi, bf16x8& lo, int e, float v, bool split) {
+  if (split) {
+    uint16_t h, l;
+    split_bf16(v, h, l);
+    hi[e] = static_cast<short>(h);
+    lo[e] = static_cast<short>(l);
+  } else {
+    hi[e] = static_cast<short>(f32_to_bf16(v));
+  }
+}
+template <bool kSplit>
+IRB_DEV f32x4 bmma(const bf16x8& ah, const bf16x8& al, const bf16x8& bh, const bf16x8& bl, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  if (kSplit) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+  }
+  return acc;
+}
+// acc += a * (b_hi + b_lo), plus a_lo * b_hi when a is itself split (FP32 inputs)
+template <bool kSplitA>
+IRB_DEV f32x4 bmma_split_b(const bf16x8& ah, const bf16x8& al, const bf16x8& bh, const bf16x8& bl, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+  if (kSplitA) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+  return acc;
+}
+IRB_DEV void bstore4(uint16_t* p, const float* v) {
+  uint2 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+IRB_DEV void bstore4(float* p, const float* v) { *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]); }
+IRB_DEV void bcopy16(void* dst, const void* src, bool ok) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) v = *reinterpret_cast<const uint4*>(src);
+  *reinterpret_cast<uint4*>(dst) = v;
+}
+
+// heads of a KV group padded so that 4 consecutive rows are 4 heads of one
+// query and 32 rows hold whole queries (or a query holds whole 32-row blocks)
+static int padded_group(int G) {
+  if (G <= 4) return 4;
+  if (G <= 8) return 8;
+  if (G <= 16) return 16;
+  if (G <= 32) return 32;
+  return (G + 31) / 32 * 32;
+}
+
+struct BwdWs {
+  float* delta;   // [B, Hq, S_q]
+  void* qt;       // [B, S_q, Hkv, Dqk, Gp]
+  void* dot;      // [B, S_q, Hkv, Dv, Gp]
+};
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t attn_bwd_workspace_bytes(int B, int S_q, int Hq, int Hkv, int Dqk, int Dv) {
+  const int G = Hq / (Hkv > 0 ? Hkv : 1);
+  const size_t Gp = static_cast<size_t>(padded_group(G));
+  const size_t rows = static_cast<size_t>(B) * S_q;
+  const size_t esz = 4;   // sized for the widest dtype
+  return align256(rows * Hq * 4) + align256(rows * Hkv * Dqk * Gp * esz) + align256(rows * Hkv * Dv * Gp * esz);
+}
+
+static BwdWs carve(void* ws, int B, int S_q, int Hq, int Hkv, int Dqk, int Dv) {
+  const int G = Hq / Hkv;
+  const size_t Gp = static_cast<size_t>(padded_group(G));
+  const size_t rows = static_cast<size_t>(B) * S_q;
+  char* p = static_cast<char*>(ws);
+  BwdWs w;
+  w.delta = reinterpret_cast<float*>(p);
+  p += align256(rows * Hq * 4);
+  w.qt = p;
+  p += align256(rows * Hkv * Dqk * Gp * 4);
+  w.dot = p;
+  return w;
+}
+
+// ---------------------------------------------------------------- prep
+template <typename T>
+__global__ void __launch_bounds__(256)
+bwd_prep_kernel(AttnArgs a, const T* __restrict__ dout, T* __restrict__ qt, T* __restrict__ dot, int G, int Gp) {
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;             // b * S_q + t
+  const int b = static_cast<int>(row / a.S_q), t = static_cast<int>(row % a.S_q);
+  // transposed copies: [kvh][dim][hp]
+  const T* qrow = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(t) * a.sq_t;
+  T* qdst = qt + row * a.Hkv * a.Dqk * Gp;
+  for (int i = tid; i < a.Hkv * a.Dqk * Gp; i += 256) {
+    const int hp = i % Gp, d = (i / Gp) % a.Dqk, g = i / (Gp * a.Dqk);
+    qdst[i] = (hp < G) ? qrow[static_cast<int64_t>(g * G + hp) * a.sq_h + d] : T(0);
+  }
+  const T* drow = dout + row * a.Hq * a.Dv;
+  T* ddst = dot + row * a.Hkv * a.Dv * Gp;
+  for (int i = tid; i < a.Hkv * a.Dv * Gp; i += 256) {
+    const int hp = i % Gp, d = (i / Gp) % a.Dv, g = i / (Gp * a.Dv);
+    ddst[i] = (hp < G) ? drow[static_cast<int64_t>(g * G + hp) * a.Dv + d] : T(0);
+  }
+}
+
+// ---------------------------------------------------------------- dq
+template <typename T, int D, int DV, bool kShared>
+__global__ void __launch_bounds__(256)
+bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+              T* __restrict__ dq, int G, int n_items, int latent) {
+  constexpr bool kSplit = sizeof(T) == 4;
+  constexpr int KS = D / 32, VS = DV / 32, NDQ = D / 16;
+  constexpr int PAD = sizeof(T) == 2 ? 8 : 4;
+  constexpr int LDK = D + PAD, LDV = DV + PAD;
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g16 = lane >> 4, l16 = lane & 15;
+  int item, slice;
+  if (kShared) { item = blockIdx.x; slice = wid; }
+  else { item = blockIdx.x * 4 + wid; slice = 0; if (item >= n_items) return; }
+  const int kvh = item % a.Hkv;
+  const int t = (item / a.Hkv) % a.S_q;
+  const int b = item / (a.Hkv * a.S_q);
+  const int h0 = kvh * G + 16 * slice;
+  const int nh = min(16, G - 16 * slice);
+  const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
+  const int n = max(0, min(a.lens[row], a.L));
+  const int32_t* route = a.routes + row * a.L;
+  const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
+  const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
+  const bool hok = l16 < nh;
+  const int hh = h0 + (hok ? l16 : 0);
+
+  bf16x8 qh[KS], ql[KS], dh[VS], dl[VS];
+  {
+    const T* qp = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(t) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) { bld8(qp + 32 * s, qh[s], ql[s]); if (!hok) { bzero8(qh[s]); bzero8(ql[s]); } }
+    const T* dp = dout + (row * a.Hq + hh) * DV + 8 * g16;
+#pragma unroll
+    for (int s = 0; s < VS; ++s) { bld8(dp + 32 * s, dh[s], dl[s]); if (!hok) { bzero8(dh[s]); bzero8(dl[s]); } }
+  }
+  const float lse2 = hok ? lse[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] * kLog2eB : 0.f;
+  const float dlt = hok ? delta[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] : 0.f;
+  const float sc2 = a.scale * kLog2eB;
+  f32x4 acc[NDQ];
+#pragma unroll
+  for (int i = 0; i < NDQ; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  T* kl = kShared ? reinterpret_cast<T*>(smem) : reinterpret_cast<T*>(smem) + wid * 32 * LDK;
+  T* vl = kl + 32 * LDK;   // shared, non-latent only
+  for (int e0 = 0; e0 < n; e0 += 32) {
+    if (kShared) {
+      __syncthreads();
+      constexpr int K16 = D * static_cast<int>(sizeof(T)) / 16;
+      for (int i = threadIdx.x; i < 32 * K16; i += blockDim.x) {
+        const int kk = i / K16, c16 = i % K16;
+        const int e = e0 + kk;
+        const int id = e < n ? route[e] : -1;
+        const bool ok = id >= 0 && id < a.S_k;
+        bcopy16(reinterpret_cast<char*>(kl + kk * LDK) + 16 * c16,
+                reinterpret_cast<const char*>(kbase + static_cast<int64_t>(ok ? id : 0) * a.sk_t) + 16 * c16, ok);
+      }
+      if (!latent) {
+        constexpr int V16 = DV * static_cast<int>(sizeof(T)) / 16;
+        for (int i = threadIdx.x; i < 32 * V16; i += blockDim.x) {
+          const int kk = i / V16, c16 = i % V16;
+          const int e = e0 + kk;
+          const int id = e < n ? route[e] : -1;
+          const bool ok = id >= 0 && id < a.S_k;
+          bcopy16(reinterpret_cast<char*>(vl + kk * LDV) + 16 * c16,
+                  reinterpret_cast<const char*>(vbase + static_cast<int64_t>(ok ? id : 0) * a.sv_t) + 16 * c16, ok);
+        }
+      }
+      __syncthreads();
+    } else {
+      constexpr int K16 = D * static_cast<int>(sizeof(T)) / 16;
+      const int kk = lane >> 1, hf = lane & 1;
+      const int e = e0 + kk;
+      const int id = e < n ? route[e] : -1;
+      const bool ok = id >= 0 && id < a.S_k;
+      const char* src = reinterpret_cast<const char*>(kbase + static_cast<int64_t>(ok ? id : 0) * a.sk_t);
+      char* dst = reinterpret_cast<char*>(kl + kk * LDK);
+      for (int c16 = hf; c16 < K16; c16 += 2) bcopy16(dst + 16 * c16, src + 16 * c16, ok);
+      wave_lds_sync();
+    }
+    f32x4 st[2], dpt[2];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      st[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dpt[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const T* kr = kl + (16 * ti + l16) * LDK + 8 * g16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        bf16x8 xh, xl;
+        bld8(kr + 32 * s, xh, xl);
+        st[ti] = bmma<kSplit>(xh, xl, qh[s], ql[s], st[ti]);
+      }
+      const T* vr;
+      bool vok = true;
+      if (kShared) {
+        vr = (latent ? kl + (16 * ti + l16) * LDK : vl + (16 * ti + l16) * LDV) + 8 * g16;
+      } else {
+        const int e = e0 + 16 * ti + l16;
+        const int id = e < n ? route[e] : -1;
+        vok = id >= 0 && id < a.S_k;
+        vr = vbase + static_cast<int64_t>(vok ? id : 0) * a.sv_t + 8 * g16;
+      }
+#pragma unroll
+      for (int s = 0; s < VS; ++s) {
+        bf16x8 xh, xl;
+        bld8(vr + 32 * s, xh, xl);
+        if (!vok) { bzero8(xh); bzero8(xl); }
+        dpt[ti] = bmma<kSplit>(xh, xl, dh[s], dl[s], dpt[ti]);
+      }
+    }
+    float ds[2][4];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + 16 * ti + 4 * g16 + i;
+        const float p = (e < n && hok) ? exp2f(st[ti][i] * sc2 - lse2) : 0.f;
+        ds[ti][i] = p * (dpt[ti][i] - dlt);
+      }
+    bf16x8 sh, sl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bput_f(sh, sl, j, ds[0][j], kSplit);
+      bput_f(sh, sl, 4 + j, ds[1][j], kSplit);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDQ; ++dt) {
+      bf16x8 xh, xl;
+      const T* kc = kl + dt * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = (j < 4) ? 4 * g16 + j : 16 + 4 * g16 + (j - 4);
+        bput(xh, xl, j, kc[kk * LDK]);
+      }
+      acc[dt] = bmma<kSplit>(xh, xl, sh, sl, acc[dt]);
+    }
+    if (!kShared) {
+      wave_lds_sync();
+    }
+  }
+  if (hok) {
+    T* op = dq + (row * a.Hq + h0 + l16) * D + 4 * g16;
+#pragma unroll
+    for (int dt = 0; dt < NDQ; ++dt) {
+      const float v[4] = {acc[dt][0] * a.scale, acc[dt][1] * a.scale, acc[dt][2] * a.scale, acc[dt][3] * a.scale};
+      bstore4(op + dt * 16, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dk / dv
+constexpr int kListCap = 128;
+
+template <typename T, int D, int DV>
+__global__ void __launch_bounds__(256)
+bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __restrict__ qt, const T* __restrict__ dot,
+                int G, int Gp, int nkt, int n_items, int merged) {
+  constexpr bool kSplit = sizeof(T) == 4;
+  constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
+  __shared__ int s_t[4][kListCap];
+  __shared__ uint32_t s_m[4][kListCap];
+  const AttnArgs& a = args.f;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int item = blockIdx.x * 4 + wid;
+  if (item >= n_items) return;
+  const int kvh = item % a.Hkv;
+  const int jt = (item / a.Hkv) % nkt;
+  const int b = item / (a.Hkv * nkt);
+  const int k0 = 16 * jt;
+  const int kid = k0 + l16;
+  const bool kok = kid < a.S_k;
+  const T* kr = static_cast<const T*>(a.k) + b * a.sk_b + static_cast<int64_t>(kok ? kid : 0) * a.sk_t + kvh * a.sk_h + 8 * g16;
+  const T* vr = static_cast<const T*>(a.v) + b * a.sv_b + static_cast<int64_t>(kok ? kid : 0) * a.sv_t + kvh * a.sv_h + 8 * g16;
+  const T* dout = static_cast<const T*>(args.dout);
+
+  f32x4 adk[NDK], adv[NDV];
+#pragma unroll
+  for (int i = 0; i < NDK; ++i) adk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NDV; ++i) adv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sc2 = a.scale * kLog2eB;
+  const int qpb = Gp <= 32 ? 32 / Gp : 1;       // queries per 32-row batch
+  const int bpq = Gp <= 32 ? 1 : Gp / 32;       // batches per query
+
+  // one 32-row batch over list slots [s0, s0 + qpb) of this wave's LDS list
+  // (slots at or past nv are empty), head block hb when a query spans batches
+  auto batch = [&](int s0, int nv, int hb) {
+    auto tq = [&](int slot) -> int { return slot < nv ? s_t[wid][s0 + slot] : -1; };
+    auto mq = [&](int slot) -> uint32_t { return slot < nv ? s_m[wid][s0 + slot] : 0u; };
+    f32x4 sacc[2], pacc[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r = 16 * rt + l16;
+      const int slot = Gp <= 32 ? r / Gp : 0;
+      const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
+      const int tr = tq(slot);
+      const bool ok = tr >= 0 && h < G;      // this lane's A row is a (query, head) row
+      const int hh = kvh * G + (h < G ? h : 0);
+      const int tt = tr >= 0 ? tr : 0;
+      const T* qp = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(tt) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
+      const T* dp = dout + ((static_cast<int64_t>(b) * a.S_q + tt) * a.Hq + hh) * DV + 8 * g16;
+      sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        bf16x8 xh, xl, yh, yl;
+        bld8(qp + 32 * s, xh, xl);
+        bld8(kr + 32 * s, yh, yl);
+        if (!ok) { bzero8(xh); bzero8(xl); }
+        sacc[rt] = bmma<kSplit>(xh, xl, yh, yl, sacc[rt]);
+      }
+#pragma unroll
+      for (int s = 0; s < VS; ++s) {
+        bf16x8 xh, xl, yh, yl;
+        bld8(dp + 32 * s, xh, xl);
+        bld8(vr + 32 * s, yh, yl);
+        if (!ok) { bzero8(xh); bzero8(xl); }
+        pacc[rt] = bmma<kSplit>(xh, xl, yh, yl, pacc[rt]);
+      }
+    }
+    // P and dS for rows 16rt + 4g16 + i, key l16
+    float p[2][4], ds[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g16 + i;
+        const int slot = Gp <= 32 ? r / Gp : 0;
+        const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
+        const int tr = tq(slot);
+        float pv = 0.f, dv = 0.f;
+        if (tr >= 0 && h < G && ((mq(slot) >> l16) & 1u)) {
+          const int64_t li = (static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + tr;
+          pv = exp2f(sacc[rt][i] * sc2 - args.lse[li] * kLog2eB);
+          dv = pv * (pacc[rt][i] - delta[li]);
+        }
+        p[rt][i] = pv;
+        ds[rt][i] = dv;
+      }
+    // P and dS always go in as bf16 high + low halves: dK and dV sum these
+    // products over every query routed to the key, so operand rounding would
+    // accumulate; with the split the sums are FP32-accurate.
+    bf16x8 ph, pl, sh, sl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bput_f(ph, pl, j, p[0][j], true);
+      bput_f(ph, pl, 4 + j, p[1][j], true);
+      bput_f(sh, sl, j, ds[0][j], true);
+      bput_f(sh, sl, 4 + j, ds[1][j], true);
+    }
+    // A operands: rows rho(g16, j) = 4g16 + j (j < 4) and 16 + 4g16 + (j - 4)
+    const int rA = 4 * g16, rB = 16 + 4 * g16;
+    const int sA = Gp <= 32 ? rA / Gp : 0, sB = Gp <= 32 ? rB / Gp : 0;
+    const int hA = Gp <= 32 ? rA % Gp : hb * 32 + rA, hB = Gp <= 32 ? rB % Gp : hb * 32 + rB;
+    const int tA = tq(sA), tB = tq(sB);
+    const int64_t baseA = (static_cast<int64_t>(b) * a.S_q + (tA >= 0 ? tA : 0)) * a.Hkv + kvh;
+    const int64_t baseB = (static_cast<int64_t>(b) * a.S_q + (tB >= 0 ? tB : 0)) * a.Hkv + kvh;
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt) {
+      const int d = dt * 16 + l16;
+      bf16x8 xh, xl;
+      bzero8(xh); bzero8(xl);
+      if (tA >= 0) bld4(dot + baseA * DV * Gp + static_cast<int64_t>(d) * Gp + hA, xh, xl, 0);
+      if (tB >= 0) bld4(dot + baseB * DV * Gp + static_cast<int64_t>(d) * Gp + hB, xh, xl, 4);
+      adv[dt] = bmma_split_b<kSplit>(xh, xl, ph, pl, adv[dt]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+      const int d = dt * 16 + l16;
+      bf16x8 xh, xl;
+      bzero8(xh); bzero8(xl);
+      if (tA >= 0) bld4(qt + baseA * D * Gp + static_cast<int64_t>(d) * Gp + hA, xh, xl, 0);
+      if (tB >= 0) bld4(qt + baseB * D * Gp + static_cast<int64_t>(d) * Gp + hB, xh, xl, 4);
+      adk[dt] = bmma_split_b<kSplit>(xh, xl, sh, sl, adk[dt]);
+    }
+  };
+
+  // walk the reverse list: listed query tiles, every query inside them
+  const int64_t lrow = static_cast<int64_t>(b) * nkt + jt;
+  const int cnt = args.rev_counts[lrow];
+  const int32_t* qtiles = args.rev_indices + lrow * args.rev_width;
+  const int bq = args.rev_bq;
+  const int64_t ncand = static_cast<int64_t>(cnt) * bq;
+  int listed = 0;   // entries in s_t/s_m waiting for a batch
+  for (int64_t c0 = 0; c0 < ncand; c0 += 64) {
+    const int64_t cidx = c0 + lane;
+    int t = -1;
+    uint32_t mask = 0u;
+    if (cidx < ncand) {
+      const int qtile = qtiles[cidx / bq];
+      t = qtile * bq + static_cast<int>(cidx % bq);
+      if (qtile < 0 || t >= a.S_q) t = -1;
+    }
+    if (t >= 0) {
+      const int64_t qrow = static_cast<int64_t>(b) * a.S_q + t;
+      const int n = max(0, min(a.lens[qrow], a.L));
+      const int32_t* r = a.routes + qrow * a.L;
+      int lo = 0, hi = n;                 // first entry >= k0
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (r[mid] < k0) lo = mid + 1; else hi = mid;
+      }
+      for (int e = lo; e < n; ++e) {
+        const int id = r[e];
+        if (id >= k0 + 16) break;
+        if (id >= k0) mask |= 1u << (id - k0);
+      }
+    }
+    const bool hit = mask != 0u;
+    const uint64_t bal = __ballot(hit);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (hit) {
+      s_t[wid][listed + before] = t;
+      s_m[wid][listed + before] = mask;
+    }
+    listed += __popcll(bal);
+    wave_lds_sync();
+    // drain full batches
+    int used = 0;
+    while (listed - used >= qpb) {
+      for (int hb = 0; hb < bpq; ++hb) batch(used, qpb, hb);
+      used += qpb;
+    }
+    // keep the remainder at the front
+    const int rem = listed - used;
+    int keep_t = -1;
+    uint32_t keep_m = 0u;
+    if (lane < rem) { keep_t = s_t[wid][used + lane]; keep_m = s_m[wid][used + lane]; }
+    wave_lds_sync();
+    if (lane < rem) { s_t[wid][lane] = keep_t; s_m[wid][lane] = keep_m; }
+    listed = rem;
+    wave_lds_sync();
+  }
+  if (listed > 0) {
+    for (int hb = 0; hb < bpq; ++hb) batch(0, listed, hb);
+  }
+
+  if (!kok) return;
+  T* dkp = static_cast<T*>(args.dk) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * D + 4 * g16;
+  if (merged) {
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = adk[dt][i] * a.scale + (dt < NDV ? adv[dt < NDV ? dt : 0][i] : 0.f);
+      bstore4(dkp + dt * 16, v);
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+      const float v[4] = {adk[dt][0] * a.scale, adk[dt][1] * a.scale, adk[dt][2] * a.scale, adk[dt][3] * a.scale};
+      bstore4(dkp + dt * 16, v);
+    }
+    T* dvp = static_cast<T*>(args.dv) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * DV + 4 * g16;
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt) {
+      const float v[4] = {adv[dt][0], adv[dt][1], adv[dt][2], adv[dt][3]};
+      bstore4(dvp + dt * 16, v);
+    }
+  }
+}
+
+template <typename T, int D, int DV>
+static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
+  const AttnArgs& a = args.f;
+  const int G = a.Hq / a.Hkv;
+  const int Gp = padded_group(G);
+  BwdWs ws = carve(args.ws, a.B, a.S_q, a.Hq, a.Hkv, a.Dqk, a.Dv);
+  const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
+  const int64_t rows = static_cast<int64_t>(a.B) * a.S_q;
+  hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, a,
+                     static_cast<const T*>(args.dout), static_cast<T*>(ws.qt), static_cast<T*>(ws.dot), G, Gp);
+  if (int rc = launch_attn_delta(a, args.dout, ws.delta, stream)) return rc;
+  const int PAD = sizeof(T) == 2 ? 8 : 4;
+  const int64_t items = rows * a.Hkv;
+  if (G <= 16) {
+    const size_t lds = static_cast<size_t>(4) * 32 * (D + PAD) * sizeof(T);
+    auto kern = bwd_dq_kernel<T, D, DV, false>;
+    if (lds > 48 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+      if (e != hipSuccess) return static_cast<int>(e);
+    }
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), lds, stream, a,
+                       static_cast<const T*>(args.dout), args.lse, ws.delta, static_cast<T*>(args.dq), G,
+                       static_cast<int>(items), latent);
+  } else {
+    const int slices = (G + 15) / 16;
+    const size_t lds = static_cast<size_t>(32) * ((D + PAD) + (latent ? 0 : (DV + PAD))) * sizeof(T);
+    auto kern = bwd_dq_kernel<T, D, DV, true>;
+    if (lds > 48 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+      if (e != hipSuccess) return static_cast<int>(e);
+    }
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(items)), dim3(64 * slices), lds, stream, a,
+                       static_cast<const T*>(args.dout), args.lse, ws.delta, static_cast<T*>(args.dq), G,
+                       static_cast<int>(items), latent);
+  }
+  const int nkt = (a.S_k + 15) / 16;
+  const int64_t kitems = static_cast<int64_t>(a.B) * nkt * a.Hkv;
+  const int merged = args.dk == args.dv ? 1 : 0;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0, stream, args,
+                     ws.delta, static_cast<const T*>(ws.qt), static_cast<const T*>(ws.dot), G, Gp, nkt,
+                     static_cast<int>(kitems), merged);
+  return 0;
+}
+
+int launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
+  if (a.f.dtype == IRB_BF16) {
+    if (a.f.Dqk == 64 && a.f.Dv == 64) return launch_bwd_t<uint16_t, 64, 64>(a, stream);
+    if (a.f.Dqk == 128 && a.f.Dv == 128) return launch_bwd_t<uint16_t, 128, 128>(a, stream);
+    if (a.f.Dqk == 576 && a.f.Dv == 512) return launch_bwd_t<uint16_t, 576, 512>(a, stream);
+  } else {
+    if (a.f.Dqk == 64 && a.f.Dv == 64) return launch_bwd_t<float, 64, 64>(a, stream);
+    if (a.f.Dqk == 128 && a.f.Dv == 128) return launch_bwd_t<float, 128, 128>(a, stream);
+  }
+  return static_cast<int>(hipErrorInvalidValue);
+}
+
+}  // namespace irb

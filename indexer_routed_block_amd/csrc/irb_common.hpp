@@ -1,0 +1,126 @@
+// Internal device/host helpers of libirb (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <limits>
+
+#define IRB_DEV __device__ __forceinline__
+
+namespace irb {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;   // MFMA A/B operand
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;    // 16x16 accumulator
+
+// ---------------------------------------------------------------- bf16 <-> f32
+IRB_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+// round-to-nearest-even; NaN kept quiet
+IRB_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// high part = f rounded to bf16; low part = bf16 of the remainder.  hi + lo
+// carries ~16 significant bits of f, so a bf16 MFMA against both halves
+// reproduces an FP32 product to ~2^-17 relative.
+IRB_DEV void split_bf16(float f, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(f);
+  lo = f32_to_bf16(f - bf16_to_f32(hi));
+}
+
+template <typename T> IRB_DEV float load_as_f32(const T* p);
+template <> IRB_DEV float load_as_f32<float>(const float* p) { return *p; }
+template <> IRB_DEV float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// ---------------------------------------------------------------- wave helpers
+IRB_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+IRB_DEV int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+IRB_DEV int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// inclusive prefix sum over the 64 lanes
+IRB_DEV int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Order LDS traffic between the lanes of ONE wavefront (no cross-wave barrier):
+// wait until this wave's LDS operations have completed and stop the compiler
+// from moving memory accesses across this point.
+IRB_DEV void wave_lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------- layout
+struct Layout {
+  int B, S;
+  const int32_t* cu_seqlens;   // packed (B == 1) or nullptr
+  int num_docs;
+  const int32_t* row_lens;     // right-padded rows or nullptr
+};
+
+struct Doc {
+  int start;   // first token of the document
+  int end;     // one past its last token
+  int index;   // document index (packed) or 0
+  bool valid;  // false for padding tokens
+};
+
+IRB_DEV Doc doc_of(const Layout& L, int b, int t) {
+  Doc d;
+  if (L.cu_seqlens) {
+    const int last = L.cu_seqlens[L.num_docs];
+    if (t >= last) { d.start = last; d.end = last; d.index = L.num_docs; d.valid = false; return d; }
+    int lo = 0, hi = L.num_docs - 1;       // largest i with cu[i] <= t
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (L.cu_seqlens[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    d.start = L.cu_seqlens[lo]; d.end = L.cu_seqlens[lo + 1]; d.index = lo; d.valid = true;
+    return d;
+  }
+  const int n = L.row_lens ? L.row_lens[b] : L.S;
+  d.start = 0; d.end = n; d.index = 0; d.valid = t < n;
+  return d;
+}
+
+// first global block ID of the query's document
+IRB_DEV int block_base(const Layout& L, const int32_t* cu_blocks, const Doc& d) {
+  return (L.cu_seqlens && cu_blocks) ? cu_blocks[d.index] : 0;
+}
+
+// order-preserving uint32 key of a float: larger float -> larger key;
+// -0.0 folds onto +0.0; NaN maps below -inf.
+IRB_DEV uint32_t score_key(float f) {
+  if (f != f) return 0u;
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace irb

@@ -1,0 +1,60 @@
+// Launcher prototypes shared by the kernel translation units and the C ABI.
+// Launchers assume validated arguments (see abi.hip) and return 0 or a HIP error code.
+#pragma once
+
+#include "../../include/irb.h"
+#include "irb_common.hpp"
+
+namespace irb {
+
+int launch_compress(const Layout& L, int c, const void* k, int dtype, int64_t sb, int64_t st, int D,
+                    const float* gamma, float eps, const float* freqs, int R, float* kc,
+                    int32_t* cu_blocks, hipStream_t stream);
+
+int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
+                      const float* kc, const int32_t* cu_blocks, int c, float scale, int q0, int q1,
+                      int j0, int j1, float* out, int64_t out_stride, hipStream_t stream);
+
+int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, int q1,
+                  const int32_t* cu_blocks, int c, int topk, int32_t* sel, int32_t* cnt,
+                  hipStream_t stream);
+
+int launch_expand(const Layout& L, const int32_t* sel, const int32_t* cnt, int topk, int c, int window,
+                  const int32_t* cu_blocks, int Lw, int32_t* routes, int32_t* lens, hipStream_t stream);
+
+int launch_compact(const int32_t* in, int64_t rows, int width, int64_t key_count, int32_t* out,
+                   int32_t* lens, int32_t* bad, hipStream_t stream);
+
+int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int Lw,
+                       int bq, int bk, int reverse, int32_t* counts, int32_t* indices, int width,
+                       uint32_t* bitmap, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q; const void* k; const void* v;
+  int64_t sq_b, sq_t, sq_h, sk_b, sk_t, sk_h, sv_b, sv_t, sv_h;
+  const int32_t* routes; const int32_t* lens;
+  int B, S_q, S_k, L, Hq, Hkv, Dqk, Dv;
+  float scale;
+  int dtype;
+};
+
+int launch_attn_fwd(const AttnArgs& a, void* out, float* lse, hipStream_t stream);
+// backward row statistic Delta[b,h,t] = rowsum(dO * o) with o recomputed in FP32
+int launch_attn_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t stream);
+
+struct AttnBwdArgs {
+  AttnArgs f;
+  const void* out; const void* dout; const float* lse;
+  const int32_t* rev_counts; const int32_t* rev_indices;
+  int rev_bq, rev_bk, rev_width;
+  void* dq; void* dk; void* dv;
+  void* ws; size_t ws_bytes;
+};
+
+size_t attn_bwd_workspace_bytes(int B, int S_q, int Hq, int Hkv, int Dqk, int Dv);
+int launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
+
+// fill a device int32 range with a value (a kernel, so callers may capture it in graphs)
+int launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
+
+}  // namespace irb

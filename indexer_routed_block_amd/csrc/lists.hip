@@ -1,0 +1,116 @@
+// a5: forward (query tile -> key tiles) and reverse (key tile -> query tiles)
+// block lists from token routes.
+//
+// FA4 page (nemo_automodel...step5.fa4): _block_lists (no dense grid),
+// _selected_block_lists (route-derived forward/reverse lists with bounded
+// scratch), _BackwardBlockPartition (counts + ascending padded indices).
+//
+// Two passes over a bit matrix in caller-provided scratch (1 bit per
+// (row tile, other-axis tile) pair): a mark pass where each wavefront reads
+// 64 consecutive route entries of a query (coalesced) and sets the bit of
+// every new tile with one atomic OR per run of equal tiles, and an emit pass
+// where a workgroup scans one row of the matrix with popcount prefix sums
+// and writes the ascending tile list.
+#include "irb_internal.hpp"
+
+namespace irb {
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+int launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream) {
+  if (n <= 0) return 0;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p, n, v);
+  return 0;
+}
+
+constexpr int kMarkWaves = 4;
+
+// one wavefront per query row (b, t)
+__global__ void __launch_bounds__(kMarkWaves * 64)
+mark_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int B, int S_q, int S_k, int Lw,
+            int bq, int bk, int reverse, int n_rows, int words, uint32_t* __restrict__ bits) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kMarkWaves + wid;
+  if (row >= static_cast<int64_t>(B) * S_q) return;
+  const int b = static_cast<int>(row / S_q), t = static_cast<int>(row % S_q);
+  const int n = min(lens[row], Lw);
+  const int32_t* r = routes + row * Lw;
+  const int qt = t / bq;
+  uint32_t* mat = bits + static_cast<int64_t>(b) * n_rows * words;
+  int prev_last = -1;
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int e = e0 + lane;
+    const int id = (e < n) ? r[e] : -1;
+    const bool ok = id >= 0 && id < S_k;            // out-of-range IDs are ignored
+    const int kt = ok ? id / bk : -1;
+    int before = __shfl_up(kt, 1, 64);
+    if (lane == 0) before = prev_last;
+    if (ok && kt != before) {
+      if (reverse) atomicOr(&mat[static_cast<int64_t>(kt) * words + (qt >> 5)], 1u << (qt & 31));
+      else atomicOr(&mat[static_cast<int64_t>(qt) * words + (kt >> 5)], 1u << (kt & 31));
+    }
+    prev_last = __shfl(kt, 63, 64);
+  }
+}
+
+// one workgroup per bit-matrix row
+__global__ void __launch_bounds__(256)
+emit_kernel(const uint32_t* __restrict__ bits, int n_rows, int words, int n_other, int32_t* __restrict__ counts,
+            int32_t* __restrict__ indices, int width) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int b = blockIdx.y, row = blockIdx.x;
+  const uint32_t* w = bits + (static_cast<int64_t>(b) * n_rows + row) * words;
+  int32_t* out = indices + (static_cast<int64_t>(b) * n_rows + row) * width;
+  int base = 0;
+  for (int w0 = 0; w0 < words; w0 += 256) {
+    const int i = w0 + tid;
+    const uint32_t x = (i < words) ? w[i] : 0u;
+    const int pc = __popc(x);
+    const int incl = wave_incl_scan(pc);
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int k = 0; k < 4; ++k) { if (k < wid) off += wsum[k]; tot += wsum[k]; }
+    int o = base + off + incl - pc;
+    uint32_t y = x;
+    while (y) {
+      const int bit = __ffs(y) - 1;
+      y &= y - 1;
+      out[o++] = i * 32 + bit;
+    }
+    base += tot;
+    __syncthreads();
+  }
+  for (int i = base + tid; i < width; i += 256) out[i] = -1;
+  if (tid == 0) counts[static_cast<int64_t>(b) * n_rows + row] = base;
+  (void)n_other;
+}
+
+int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int Lw, int bq, int bk,
+                       int reverse, int32_t* counts, int32_t* indices, int width, uint32_t* bitmap,
+                       hipStream_t stream) {
+  const int nqt = (S_q + bq - 1) / bq, nkt = (S_k + bk - 1) / bk;
+  const int n_rows = reverse ? nkt : nqt;
+  const int n_other = reverse ? nqt : nkt;
+  const int words = (n_other + 31) / 32;
+  int rc = launch_fill_i32(reinterpret_cast<int32_t*>(bitmap), static_cast<int64_t>(B) * n_rows * words, 0, stream);
+  if (rc) return rc;
+  const int64_t qrows = static_cast<int64_t>(B) * S_q;
+  if (qrows > 0)
+    hipLaunchKernelGGL(mark_kernel, dim3(static_cast<unsigned>((qrows + kMarkWaves - 1) / kMarkWaves)),
+                       dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw, bq, bk, reverse, n_rows, words,
+                       bitmap);
+  if (n_rows > 0 && B > 0)
+    hipLaunchKernelGGL(emit_kernel, dim3(static_cast<unsigned>(n_rows), static_cast<unsigned>(B)), dim3(256), 0,
+                       stream, bitmap, n_rows, words, n_other, counts, indices, width);
+  return 0;
+}
+
+}  // namespace irb

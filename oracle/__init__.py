@@ -270,7 +270,7 @@ def route_width(topk, c, window):
     return topk * c + max(window, c - 1)
 
 
-def expand_routes(sel, cnt, c, window, topk, cu_seqlens=None, row_lens=None, L=None):
+def expand_routes(sel, cnt, c, window, topk, cu_seqlens=None, row_lens=None, L=None, rows=None):
     """Token routes [B, S, L] (ascending, unique, -1 suffix) and lengths [B, S].
 
     ``R(t)`` = tokens of the selected blocks, plus the tokens of the current
@@ -280,6 +280,7 @@ def expand_routes(sel, cnt, c, window, topk, cu_seqlens=None, row_lens=None, L=N
     the window holds the query and at most W-1 earlier keys); duplicates
     removed (QSA page, ``qsa_gqa_attention``: duplicates collapse), sorted,
     padded with -1 (QSA page, ``QSARouteSelection.selected_token_ids``).
+    ``rows`` optionally restricts the evaluation to a list of (b, t) pairs.
     """
     sel = np.asarray(sel)
     B, S, _ = sel.shape
@@ -288,8 +289,8 @@ def expand_routes(sel, cnt, c, window, topk, cu_seqlens=None, row_lens=None, L=N
     valid, start, base, nb = token_info(docs, S, c)
     routes = np.full((B, S, L), -1, dtype=np.int32)
     lens = np.zeros((B, S), dtype=np.int32)
-    for b in range(B):
-        for t in range(S):
+    todo = [(b, t) for b in range(B) for t in range(S)] if rows is None else rows
+    for b, t in todo:
             if not valid[b, t]:
                 continue
             a = int(start[b, t])

@@ -1,0 +1,138 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments on the host (no GPU needed: validation runs before any
+device call, and nothing here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import indexer_routed_block_amd as irb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "irb.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(irb.LIB_PATH), reason="libirb.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(irb_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = irb.load_library()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(irb.EXPORTED) == names
+
+
+def test_version_and_availability_without_gpu():
+    lib = irb.load_library()
+    assert b"gfx950" in lib.irb_version()
+    assert lib.irb_is_available() in (0, 1)
+
+
+def _layout(B=1, S=64, cu=None, nd=0, rl=None):
+    return irb.IrbLayout(B, S, cu, nd, rl)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _err(status):
+    return status, irb.load_library().irb_last_error().decode()
+
+
+def test_compress_keys_validation():
+    lib = irb.load_library()
+    lay = _layout()
+    s, m = _err(lib.irb_compress_keys(None, 4, FAKE, 1, 0, 64, 64, FAKE, 1e-5, FAKE, 64, FAKE, None, None))
+    assert s == 3 and "layout" in m
+    s, m = _err(lib.irb_compress_keys(ctypes.byref(lay), 4, FAKE, 7, 0, 64, 64, FAKE, 1e-5, FAKE, 64, FAKE, None, None))
+    assert s == 2
+    s, m = _err(lib.irb_compress_keys(ctypes.byref(lay), 0, FAKE, 1, 0, 64, 64, FAKE, 1e-5, FAKE, 64, FAKE, None, None))
+    assert s == 3 and "c must" in m
+    s, m = _err(lib.irb_compress_keys(ctypes.byref(lay), 4, FAKE, 1, 0, 64, 48, FAKE, 1e-5, FAKE, 48, FAKE, None, None))
+    assert s == 3 and "D_idx" in m
+    s, m = _err(lib.irb_compress_keys(ctypes.byref(lay), 4, FAKE, 1, 0, 64, 64, FAKE, 1e-5, FAKE, 63, FAKE, None, None))
+    assert s == 3 and "D_rope" in m
+    packed = _layout(cu=0x2000, nd=3)
+    s, m = _err(lib.irb_compress_keys(ctypes.byref(packed), 4, FAKE, 1, 0, 64, 64, FAKE, 1e-5, FAKE, 64, FAKE, None, None))
+    assert s == 3 and "cu_blocks" in m
+    both = _layout(cu=0x2000, nd=3, rl=0x3000)
+    s, m = _err(lib.irb_compress_keys(ctypes.byref(both), 4, FAKE, 1, 0, 64, 64, FAKE, 1e-5, FAKE, 64, FAKE, FAKE, None))
+    assert s == 3 and "not both" in m
+    batched_packed = _layout(B=2, cu=0x2000, nd=3)
+    s, m = _err(lib.irb_compress_keys(ctypes.byref(batched_packed), 4, FAKE, 1, 0, 64, 64, FAKE, 1e-5, FAKE, 64, FAKE, FAKE, None))
+    assert s == 3 and "B == 1" in m
+
+
+def test_score_and_select_validation():
+    lib = irb.load_library()
+    lay = _layout(S=64)
+    args = lambda H=16, D=128, sc=0.1, q0=0, q1=64, j0=0, j1=16, st=16: lib.irb_indexer_score_tile(
+        ctypes.byref(lay), FAKE, 1, H, D, FAKE, FAKE, None, 4, sc, q0, q1, j0, j1, FAKE, st, None)
+    assert _err(args(H=12))[0] == 3
+    assert _err(args(D=96))[0] == 3
+    assert _err(args(sc=0.0))[0] == 3
+    assert _err(args(q0=10, q1=10))[0] == 3
+    assert _err(args(j1=17))[0] == 3
+    assert _err(args(st=8))[0] == 3
+    s = lib.irb_select_topk_regions(ctypes.byref(lay), FAKE, 16, 0, 64, None, 4, 0, FAKE, FAKE, None)
+    assert _err(s)[0] == 3
+    s = lib.irb_select_topk_regions(ctypes.byref(lay), FAKE, 16, 0, 65, None, 4, 4, FAKE, FAKE, None)
+    assert _err(s)[0] == 3
+
+
+def test_routes_lists_validation():
+    lib = irb.load_library()
+    lay = _layout(S=64)
+    # width below topk*c + max(window, c-1)
+    s, m = _err(lib.irb_expand_and_compact_routes(ctypes.byref(lay), FAKE, FAKE, 4, 4, 8, None, 23, FAKE, FAKE, None))
+    assert s == 3 and "width" in m
+    s, m = _err(lib.irb_compact_routes(FAKE, 4, 0, 10, FAKE, FAKE, None, None))
+    assert s == 3
+    s, m = _err(lib.irb_compact_routes(FAKE, 4, 8, 0, FAKE, FAKE, None, None))
+    assert s == 3
+    need = lib.irb_build_block_lists_workspace_size(1, 64, 64, 16, 16)
+    assert need == 4 * 4
+    s, m = _err(lib.irb_build_block_lists(FAKE, FAKE, 1, 64, 64, 8, 16, 16, 0, FAKE, FAKE, 3, FAKE, need, None))
+    assert s == 3 and "width" in m
+    s, m = _err(lib.irb_build_block_lists(FAKE, FAKE, 1, 64, 64, 8, 16, 16, 0, FAKE, FAKE, 4, FAKE, need - 1, None))
+    assert s == 3 and "workspace" in m
+
+
+def test_attention_validation():
+    lib = irb.load_library()
+    st = (ctypes.c_int64 * 9)(64 * 4 * 128, 4 * 128, 128, 64 * 128, 128, 128, 64 * 128, 128, 128)
+    call = lambda Hq=4, Hkv=1, D=128, Dv=128, sc=0.1, dt=1, strides=st: lib.irb_sparse_gqa_attention_fwd(
+        FAKE, FAKE, FAKE, dt, strides, FAKE, FAKE, 1, 64, 64, 16, Hq, Hkv, D, Dv, sc, FAKE, FAKE, None)
+    assert _err(call(Hq=6, Hkv=4))[0] == 3
+    assert _err(call(Hq=128, Hkv=1))[0] == 3
+    assert _err(call(D=96, Dv=96))[0] == 3
+    assert _err(call(D=576, Dv=512, dt=0))[0] == 3      # latent dims are bf16 only
+    assert _err(call(sc=-1.0))[0] == 3
+    assert _err(call(dt=5))[0] == 2
+    odd = (ctypes.c_int64 * 9)(*list(st)[:8], 129)
+    assert _err(call(strides=odd))[0] == 3
+    # backward: key tile must be 16, merged dk/dv needs Dv <= Dqk
+    bwd = lambda bk=16, width=64: lib.irb_sparse_gqa_attention_bwd(
+        FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, bk, width, 1, 64, 64, 16, 4, 1, 128, 128,
+        0.1, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert _err(bwd(bk=32))[0] == 3
+    assert _err(bwd(width=63))[0] == 3
+
+
+def test_python_binding_has_no_cpu_path():
+    import torch
+    x = torch.zeros(1, 64, 64)
+    with pytest.raises(RuntimeError, match="GPU only"):
+        irb.compress_keys(x, torch.ones(64), torch.zeros(1, 64, 64), 4)
+    q = torch.zeros(1, 8, 2, 64)
+    r = torch.zeros(1, 8, 4, dtype=torch.int32)
+    with pytest.raises(RuntimeError, match="GPU only"):
+        irb.sparse_gqa_attention_fwd(q, q[:, :, :1], q[:, :, :1], r, r[..., 0])

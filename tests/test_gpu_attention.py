@@ -1,0 +1,146 @@
+"""GPU parity of sparse GQA attention forward/backward against the FP64 oracle, through the C ABI.
+
+Tolerances: bf16 outputs and gradients mean-abs <= 5e-3 and per element
+|err| <= 2e-2 + 2^-7 |ref| (see gpu_util.attn_tol_check; FP32 accumulation);
+fp32 inputs max-abs <= 1e-4; lse within 1e-3 (bf16) / 1e-4 (fp32) absolute.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_routed_block_amd as irb
+import oracle
+import synth
+from gpu_util import DEV, act_dtype, attn_tol_check, banner, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_routes(seed, B, S, width, empty_rows=()):
+    rng = np.random.default_rng(seed)
+    ids = synth.random_routes(rng, B, S, width, causal=True, frac_invalid=0.25)
+    routes, lens, _ = oracle.compact_routes(ids, S)
+    for (b, t) in empty_rows:
+        routes[b, t] = -1
+        lens[b, t] = 0
+    return routes, lens
+
+
+def _pipeline_routes(wl_name, S):
+    wl = synth.WORKLOADS[wl_name]
+    x = synth.make_inputs(wl, parts=("route",), S=S)
+    topk = min(wl.topk, max(4, S // wl.c // 4))
+    r = oracle.route_pipeline(x["kI"], x["qI"], x["w"], x["gamma"], x["freqs"], wl.c, topk, wl.window)
+    return r["routes"], r["lens"]
+
+
+def _qkv(wl_name, S, B=1, seed=None):
+    wl = synth.WORKLOADS[wl_name]
+    x = synth.make_inputs(wl, parts=("attn", "bwd"), S=S, B=B, seed=seed)
+    return wl, x
+
+
+def _check_lse(got, want, dtype):
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isneginf(got), np.isneginf(want))
+    tol = 1e-3 if dtype == torch.bfloat16 else 1e-4
+    assert np.max(np.abs(got[fin] - want[fin]), initial=0.0) <= tol
+
+
+def _run_fwd_bwd(wl, x, routes, lens, scale, do_bwd, q_view=None):
+    dt = act_dtype(wl.dtype)
+    q = to_dev(x["q"], dt) if q_view is None else q_view
+    k = to_dev(x["k"], dt)
+    v = to_dev(x["v"], dt)
+    r_d, l_d = to_dev(routes), to_dev(lens)
+    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, scale)
+    ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], routes, scale)
+    attn_tol_check(host(o), ro, dt, "o")
+    _check_lse(host(lse), rlse, dt)
+    if not do_bwd:
+        return
+    S = x["q"].shape[1]
+    rc, ri = irb.build_block_lists(r_d, l_d, S, 1, 16, reverse=True)
+    dO = to_dev(x["dO"], dt)
+    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, 1, 16, scale)
+    rdq, rdk, rdv = oracle.attention_bwd(x["q"], x["k"], x["v"], routes, x["dO"], scale)
+    attn_tol_check(host(dq), rdq, dt, "dq")
+    attn_tol_check(host(dk), rdk, dt, "dk")
+    attn_tol_check(host(dv), rdv, dt, "dv")
+
+
+def test_tiny_fp32_pipeline_routes_fwd_bwd():
+    banner("attn tiny fp32 S=512")
+    wl, x = _qkv("tiny", 512)
+    routes, lens = _pipeline_routes("tiny", 512)
+    _run_fwd_bwd(wl, x, routes, lens, 1.0 / math.sqrt(wl.D), True)
+
+
+@pytest.mark.parametrize("S,width", [(1024, 160), (333, 70)])
+def test_gqa_bf16_random_routes_fwd_bwd(S, width):
+    banner(f"attn gqa bf16 S={S} width={width}")
+    wl, x = _qkv("varlen", S)
+    routes, lens = _random_routes(S, 1, S, width, empty_rows=[(0, 5), (0, S - 1)])
+    _run_fwd_bwd(wl, x, routes, lens, 1.0 / math.sqrt(wl.D), True)
+
+
+def test_gqa_bf16_window_routes_fwd():
+    banner("attn s8192-recipe bf16 S=2048 pipeline routes")
+    wl, x = _qkv("s8192", 2048)
+    routes, lens = _pipeline_routes("s8192", 2048)
+    _run_fwd_bwd(wl, x, routes, lens, 1.0 / math.sqrt(wl.D), False)
+
+
+def test_gqa_bf16_batched_and_strided_q():
+    banner("attn bf16 B=2 strided q")
+    wl, x = _qkv("varlen", 256, B=2)
+    routes, lens = _random_routes(7, 2, 256, 48, empty_rows=[(1, 0)])
+    big = torch.zeros((2, 256, wl.Hq + 3, wl.D), dtype=torch.bfloat16, device=DEV)
+    big[:, :, 1:1 + wl.Hq] = to_dev(x["q"], torch.bfloat16)
+    qv = big[:, :, 1:1 + wl.Hq]
+    assert not qv.is_contiguous()
+    _run_fwd_bwd(wl, x, routes, lens, 0.11, True, q_view=qv)
+
+
+@pytest.mark.parametrize("T,width", [(512, 256), (300, 64)])
+def test_latent_shared_kv_fwd_bwd(T, width):
+    banner(f"attn latent T={T} width={width}")
+    wl = synth.WORKLOADS["latent"]
+    x = synth.make_inputs(wl, parts=("attn", "bwd"), S=T)
+    rng = np.random.default_rng(T)
+    idx = synth.latent_indices(rng, T, width)
+    routes, lens, _ = oracle.compact_routes(idx[:, 0, :], T)
+    kv_d = to_dev(x["kv"], torch.bfloat16)[None]                      # [1, T, 1, 576]
+    q_d = to_dev(x["q"], torch.bfloat16)[None]
+    k_d, v_d = kv_d, kv_d[..., :wl.Dv]
+    r_d, l_d = to_dev(routes)[None], to_dev(lens)[None]
+    o, lse = irb.sparse_gqa_attention_fwd(q_d, k_d, v_d, r_d, l_d, wl.softmax_scale)
+    ro, rlse = oracle.latent_attention_fwd(x["q"], x["kv"], idx, wl.softmax_scale, dv=wl.Dv)
+    attn_tol_check(host(o)[0], ro, torch.bfloat16, "latent o")
+    _check_lse(host(lse)[0], rlse, torch.bfloat16)
+    rc, ri = irb.build_block_lists(r_d, l_d, T, 1, 16, reverse=True)
+    dO = to_dev(x["dO"], torch.bfloat16)[None]
+    dq, dkv, dv_alias = irb.sparse_gqa_attention_bwd(q_d, k_d, v_d, o, dO, lse, r_d, l_d, rc, ri, 1, 16,
+                                                     wl.softmax_scale, merged_kv=True)
+    assert dv_alias.data_ptr() == dkv.data_ptr()
+    rdq, rdkv = oracle.latent_attention_bwd(x["q"], x["kv"], idx, x["dO"], wl.softmax_scale, dv=wl.Dv)
+    attn_tol_check(host(dq)[0], rdq, torch.bfloat16, "latent dq")
+    attn_tol_check(host(dkv)[0], rdkv, torch.bfloat16, "latent dkv")
+
+
+def test_backward_with_coarse_reverse_tiles():
+    """Reverse lists at 16-query granularity give the same gradients as per-query lists."""
+    banner("attn bwd coarse reverse lists")
+    wl, x = _qkv("varlen", 400)
+    routes, lens = _random_routes(11, 1, 400, 64)
+    dt = torch.bfloat16
+    q, k, v = (to_dev(x[n], dt) for n in ("q", "k", "v"))
+    r_d, l_d = to_dev(routes), to_dev(lens)
+    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d)
+    dO = to_dev(x["dO"], dt)
+    a = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, *irb.build_block_lists(r_d, l_d, 400, 1, 16, True), 1)
+    b = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, *irb.build_block_lists(r_d, l_d, 400, 16, 16, True), 16)
+    for u, w_ in zip(a, b):
+        assert torch.equal(u, w_)

@@ -1,0 +1,213 @@
+"""GPU parity of the route pipeline (compress, score, select, expand, compact, block lists)
+against the FP64 oracle, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_routed_block_amd as irb
+import oracle
+import synth
+from gpu_util import DEV, act_dtype, banner, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _layout_case(name, S):
+    """(cu_seqlens, row_lens, B) for a named layout at length S."""
+    if name == "single":
+        return None, None, 1
+    if name == "rows":
+        return None, np.array([S, S // 3 + 5, 0], dtype=np.int32), 3
+    if name == "packed":
+        rng = np.random.default_rng(S)
+        cu, pad = synth.varlen_documents(rng, S, min_len=16, max_len=max(32, S // 3), max_pad=min(511, S // 8))
+        return cu, None, 1
+    raise ValueError(name)
+
+
+def _inputs(wl_name, S, layout):
+    wl = synth.WORKLOADS[wl_name]
+    cu, rl, B = _layout_case(layout, S)
+    x = synth.make_inputs(wl, parts=("route",), S=S, B=B, cu_seqlens=cu, row_lens=rl)
+    return wl, x
+
+
+def _dev_inputs(wl, x):
+    dt = act_dtype(wl.dtype)
+    return dict(kI=to_dev(x["kI"], dt), qI=to_dev(x["qI"], dt), w=to_dev(x["w"]), gamma=to_dev(x["gamma"]),
+                freqs=to_dev(x["freqs"]), cu=to_dev(x["cu_seqlens"]), rl=to_dev(x["row_lens"]))
+
+
+CASES = [("tiny", 512, "single"), ("tiny", 200, "rows"), ("s8192", 2048, "single"), ("varlen", 4096, "packed"),
+         ("long", 2048, "single"), ("s8192", 1500, "rows")]
+
+
+@pytest.mark.parametrize("wl_name,S,layout", CASES)
+def test_compress_keys(wl_name, S, layout):
+    banner(f"compress {wl_name} S={S} {layout}")
+    wl, x = _inputs(wl_name, S, layout)
+    d = _dev_inputs(wl, x)
+    kc, cu_blocks = irb.compress_keys(d["kI"], d["gamma"], d["freqs"], wl.c, 1e-5, d["cu"], d["rl"])
+    ref, ref_cub = oracle.compress_keys(x["kI"], x["gamma"], 1e-5, x["freqs"], wl.c, x["cu_seqlens"], x["row_lens"])
+    got = host(kc)
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+    if ref_cub is not None:
+        np.testing.assert_array_equal(host(cu_blocks), ref_cub)
+
+
+def _score_bound(qI, w, kc, scale):
+    """M[t, j] = scale * sum_h |w[t,h]| * sum_d |q[t,h,d] k[j,d]|.
+
+    The "1e-3 relative" score tolerance is taken against this magnitude: it
+    bounds the cancellation inside each dot product as well as across the
+    signed head weights, so it is the scale FP32-class rounding error lives
+    on.  (relu(q.k) alone is not: a dot product that cancels to ~0 still
+    carries rounding error of order sum_d |q_d k_d| * 2^-17.)
+    """
+    dots = np.einsum("bthd,bjd->bthj", np.abs(qI.astype(np.float64)), np.abs(kc))
+    return scale * np.einsum("bth,bthj->btj", np.abs(w.astype(np.float64)), dots)
+
+
+@pytest.mark.parametrize("wl_name,S,layout", CASES)
+def test_indexer_score_tile(wl_name, S, layout):
+    banner(f"score {wl_name} S={S} {layout}")
+    wl, x = _inputs(wl_name, S, layout)
+    d = _dev_inputs(wl, x)
+    kc, cu_blocks = irb.compress_keys(d["kI"], d["gamma"], d["freqs"], wl.c, 1e-5, d["cu"], d["rl"])
+    kc_h = host(kc).astype(np.float64)
+    scale = 1.0 / math.sqrt(wl.D_idx)
+    nb = S // wl.c
+    # full tile plus an unaligned sub-tile
+    for (q0, q1, j0, j1) in [(0, S, 0, nb), (S // 3 + 1, S - 7, nb // 5 + 3, nb - 2)]:
+        out = irb.indexer_score_tile(d["qI"], d["w"], kc, wl.c, q0, q1, j0, j1, scale, cu_blocks, d["cu"], d["rl"])
+        got = host(out)
+        ref = oracle.indexer_scores(x["qI"], x["w"], kc_h, wl.c, scale, x["cu_seqlens"], x["row_lens"], q0, q1)[:, :, j0:j1]
+        assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+        M = _score_bound(x["qI"][:, q0:q1], x["w"][:, q0:q1], kc_h[:, j0:j1], scale)
+        fin = np.isfinite(ref)
+        err = np.abs(got[fin] - ref[fin])
+        assert np.all(err <= 1e-3 * M[fin] + 1e-30), f"max rel-to-M {np.max(err / np.maximum(M[fin], 1e-30)):.2e}"
+
+
+def _quantised_scores(rng, B, S, nb, ties):
+    s = rng.standard_normal((B, S, nb))
+    if ties:
+        s = np.round(s * 2) / 2          # many exact ties, including 0.0
+        s[rng.random(s.shape) < 0.1] = -0.0
+    return s.astype(np.float32)
+
+
+@pytest.mark.parametrize("layout,topk,c,S,ties", [
+    ("single", 16, 4, 512, True), ("single", 512, 4, 8192, False), ("rows", 7, 2, 300, True),
+    ("packed", 32, 4, 4096, True), ("single", 256, 8, 4096, True)])
+def test_select_bit_exact_on_fixed_scores(layout, topk, c, S, ties):
+    banner(f"select {layout} topk={topk} c={c} S={S} ties={ties}")
+    rng = np.random.default_rng(topk + S)
+    cu, rl, B = _layout_case(layout, S)
+    nb = S // c
+    scores = _quantised_scores(rng, B, S, nb, ties)
+    sel, cnt = irb.select_topk_regions(to_dev(scores), c, topk, S, cu_blocks=_cu_blocks_dev(cu, c),
+                                       cu_seqlens=to_dev(cu), row_lens=to_dev(rl))
+    rsel, rcnt = oracle.select_topk(scores.astype(np.float64), c, topk, cu, rl)
+    np.testing.assert_array_equal(host(cnt), rcnt)
+    np.testing.assert_array_equal(host(sel), rsel)
+
+
+def _cu_blocks_dev(cu, c):
+    if cu is None:
+        return None
+    lens = np.diff(cu) // c
+    return to_dev(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+
+
+@pytest.mark.parametrize("wl_name,S,layout", [("tiny", 512, "single"), ("s8192", 2048, "single"),
+                                              ("varlen", 4096, "packed"), ("long", 4096, "single"),
+                                              ("s8192", 1500, "rows")])
+def test_route_pipeline_matches_oracle(wl_name, S, layout):
+    """compress -> fused score/select -> expand; routes bit-exact except near-tie rows."""
+    banner(f"pipeline {wl_name} S={S} {layout}")
+    wl, x = _inputs(wl_name, S, layout)
+    d = _dev_inputs(wl, x)
+    topk = min(wl.topk, max(4, S // wl.c // 4))     # keep selection sparse at reduced S
+    r = irb.route(d["kI"], d["qI"], d["w"], d["gamma"], d["freqs"], wl.c, topk, wl.window, cu_seqlens=d["cu"],
+                  row_lens=d["rl"])
+    ref = oracle.route_pipeline(x["kI"], x["qI"], x["w"], x["gamma"], x["freqs"], wl.c, topk, wl.window,
+                                cu_seqlens=x["cu_seqlens"], row_lens=x["row_lens"])
+    ties = oracle.near_tie_rows(ref["scores"], wl.c, topk, x["cu_seqlens"], x["row_lens"])
+    got_sel, got_routes, got_lens = host(r["sel"]), host(r["routes"]), host(r["lens"])
+    same = np.all(got_sel == ref["sel"], axis=-1)
+    bad = ~same & ~ties
+    print(f"near-tie rows {int(ties.sum())} of {ties.size}; differing rows {int((~same).sum())}")
+    assert not bad.any(), f"{int(bad.sum())} non-tie rows differ, e.g. {np.argwhere(bad)[:3].tolist()}"
+    keep = ~ties
+    np.testing.assert_array_equal(got_routes[keep], ref["routes"][keep])
+    np.testing.assert_array_equal(got_lens[keep], ref["lens"][keep])
+    np.testing.assert_array_equal(host(r["cnt"]), ref["cnt"])
+
+
+@pytest.mark.parametrize("c,topk,window,layout,S", [(4, 16, 0, "single", 512), (4, 512, 128, "single", 8192),
+                                                   (4, 8, 5, "packed", 3000), (8, 256, 512, "single", 8192),
+                                                   (3, 5, 7, "rows", 400), (1, 6, 0, "rows", 300)])
+def test_expand_bit_exact_on_fixed_selection(c, topk, window, layout, S):
+    banner(f"expand c={c} topk={topk} W={window} {layout} S={S}")
+    rng = np.random.default_rng(S + c)
+    cu, rl, B = _layout_case(layout, S)
+    docs = oracle.documents(B, S, cu, rl)
+    valid, start, base, nb = oracle.token_info(docs, S, c)
+    sel = np.full((B, S, topk), -1, dtype=np.int32)
+    cnt = np.zeros((B, S), dtype=np.int32)
+    for b in range(B):
+        for t in range(S):
+            if valid[b, t] and nb[b, t]:
+                k = min(topk, int(nb[b, t]))
+                sel[b, t, :k] = np.sort(rng.choice(int(nb[b, t]), k, replace=False)) + base[b, t]
+                cnt[b, t] = k
+    routes, lens = irb.expand_and_compact_routes(to_dev(sel), to_dev(cnt), c, window, topk,
+                                                 cu_blocks=_cu_blocks_dev(cu, c), cu_seqlens=to_dev(cu),
+                                                 row_lens=to_dev(rl))
+    rr, rl_ = oracle.expand_routes(sel, cnt, c, window, topk, cu, rl)
+    np.testing.assert_array_equal(host(lens), rl_)
+    np.testing.assert_array_equal(host(routes), rr)
+
+
+@pytest.mark.parametrize("rows,width,key_count", [(300, 67, 300), (64, 2048, 5000), (17, 1, 3), (40, 1000, 10)])
+def test_compact_bit_exact(rows, width, key_count):
+    banner(f"compact rows={rows} width={width} keys={key_count}")
+    rng = np.random.default_rng(rows * width)
+    ids = rng.integers(-3, key_count + 3, size=(rows, width)).astype(np.int32)
+    out, lens, bad = irb.compact_routes(to_dev(ids), key_count)
+    ro, rl, rbad = oracle.compact_routes(ids, key_count)
+    np.testing.assert_array_equal(host(out), ro)
+    np.testing.assert_array_equal(host(lens), rl)
+    assert int(host(bad)[0]) == rbad
+    # in place
+    t = to_dev(ids)
+    irb.compact_routes(t, key_count, out=t)
+    np.testing.assert_array_equal(host(t), ro)
+
+
+def test_compact_latent_indices():
+    wl = synth.WORKLOADS["latent"]
+    x = synth.make_inputs(wl, parts=("idx",), S=1024)
+    banner("compact latent T=1024")
+    out, lens, bad = irb.compact_routes(to_dev(x["idx"]), 1024)
+    ro, rl, rbad = oracle.compact_routes(x["idx"], 1024)
+    np.testing.assert_array_equal(host(out), ro)
+    np.testing.assert_array_equal(host(lens), rl)
+    assert rbad == 0 and int(host(bad)[0]) == 0
+
+
+@pytest.mark.parametrize("bq,bk,reverse", [(1, 16, True), (16, 64, False), (16, 64, True), (3, 5, False),
+                                           (3, 5, True), (128, 16, True), (1, 1, False)])
+def test_block_lists_bit_exact(bq, bk, reverse):
+    banner(f"lists bq={bq} bk={bk} reverse={reverse}")
+    rng = np.random.default_rng(bq * 100 + bk)
+    B, S = 2, 700
+    ids = synth.random_routes(rng, B, S, 40, causal=True, frac_invalid=0.2)
+    routes, lens, _ = oracle.compact_routes(ids, S)
+    counts, indices = irb.build_block_lists(to_dev(routes), to_dev(lens), S, bq, bk, reverse)
+    rc, ri = oracle.block_lists(routes, lens, S, bq, bk, reverse)
+    np.testing.assert_array_equal(host(counts), rc)
+    np.testing.assert_array_equal(host(indices), ri)
