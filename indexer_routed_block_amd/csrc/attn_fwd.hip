@@ -18,6 +18,8 @@
 // G > 16:  one workgroup per item, one wavefront per 16 heads; K and V chunks
 //          staged once in LDS and shared (for latent KV a single slab).
 // FP32 inputs are split into bf16 high/low parts (three MFMAs per product).
+#include <cstdlib>
+
 #include "irb_internal.hpp"
 
 namespace irb {
@@ -94,32 +96,21 @@ IRB_DEV void copy16(void* dst, const void* src, bool ok) {
 // kDelta: instead of o and lse, write Delta[b, h, t] = sum_d dO[t,h,d] * o[t,h,d]
 // with o held in FP32 (the backward's row statistic, free of the rounding of
 // the stored bf16 output).
+// One (batch, query, KV head) item over its route.  kShared: called by every
+// wave of the workgroup (wave = 16-head slice), K/V chunks staged in `smem`
+// shared by all waves; otherwise called by one wave with `smem` its own slab.
 template <typename T, int D, int DV, bool kShared, bool kDelta>
-__global__ void __launch_bounds__(256)
-attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G, int n_items, int latent,
-                const T* __restrict__ dout, float* __restrict__ delta) {
+IRB_DEV void fwd_item(const AttnArgs& a, T* __restrict__ out, float* __restrict__ lse, int G, int latent,
+                      const T* __restrict__ dout, float* __restrict__ delta, int b, int t, int kvh, int slice,
+                      char* smem) {
   constexpr bool kSplit = sizeof(T) == 4;
   constexpr int KS = D / 32;
   constexpr int NDT = DV / 16;
   constexpr int PAD = sizeof(T) == 2 ? 8 : 4;
   constexpr int LDK = D + PAD;
   constexpr int LDV = DV + PAD;
-  extern __shared__ __align__(16) char smem[];
-
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int g16 = lane >> 4, l16 = lane & 15;
-  int item, slice;
-  if (kShared) {
-    item = blockIdx.x;
-    slice = wid;
-  } else {
-    item = blockIdx.x * 4 + wid;
-    slice = 0;
-    if (item >= n_items) return;
-  }
-  const int kvh = item % a.Hkv;
-  const int t = (item / a.Hkv) % a.S_q;
-  const int b = item / (a.Hkv * a.S_q);
   const int h0 = kvh * G + 16 * slice;
   const int nh = min(16, G - 16 * slice);
   const T* qbase = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(t) * a.sq_t;
@@ -152,7 +143,7 @@ attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G,
     vl = latent ? kl : kl + 32 * LDK;
     ldv = latent ? LDK : LDV;
   } else {
-    vl = reinterpret_cast<T*>(smem) + wid * 32 * LDV;
+    vl = reinterpret_cast<T*>(smem);
     ldv = LDV;
   }
 
@@ -235,38 +226,34 @@ attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G,
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
     const float mnew = fmaxf(m2, cmax);
-    float alpha = 1.f;
+    const float mref = (mnew == -INFINITY) ? 0.f : mnew;   // nothing visible yet: every p is 0
     float p[2][4];
-    if (mnew == -INFINITY) {
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[ti][i] = 0.f;
-    } else {
-      alpha = exp2f(m2 - mnew);
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[ti][i] = exp2f(x[ti][i] - mnew);
-    }
-    m2 = mnew;
     float ps = 0.f;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ps += p[ti][i];
+      for (int i = 0; i < 4; ++i) { p[ti][i] = fast_exp2(x[ti][i] - mref); ps += p[ti][i]; }
+    const float alpha = fast_exp2(m2 - mref);
+    m2 = mnew;
     lsum = lsum * alpha + ps;
+    if (__ballot(alpha != 1.f)) {           // rescale only when some head's max moved
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha;
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha;
+    }
 
     // P^T operand: k positions 8*g16 + j <-> keys {4g..4g+3} of tile 0, then of tile 1
     bf16x8 ph, pl;
+    if (kSplit) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      put_p(ph, pl, j, p[0][j], kSplit);
-      put_p(ph, pl, 4 + j, p[1][j], kSplit);
+      for (int j = 0; j < 4; ++j) {
+        put_p(ph, pl, j, p[0][j], true);
+        put_p(ph, pl, 4 + j, p[1][j], true);
+      }
+    } else {
+      const float pf[8] = {p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
+      ph = pack_bf16x8(pf);
     }
     // ---- O^T += V^T P^T; A operand read transposed from LDS
 #pragma unroll
@@ -314,6 +301,375 @@ attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Query-tile kernel for dense-ish routes (G <= 16, bf16).
+//
+// Work item = (batch, tile of BQ = 128/G consecutive queries, KV head): 128
+// (query, head) columns, 32 per wave.  The key tiles (32 keys) any query of
+// the tile routes to are streamed through double-buffered LDS as contiguous
+// rows, K as [key][dim] and V transposed to [dim][key] on the way in, both
+// shared by all 128 columns:
+//   S^T[key, col] = K_tile . Q^T       A = K from LDS, B = resident Q
+//   O^T[dim, col] += V_tile^T . P^T    A = V^T from LDS (two 8-byte reads),
+//                                      B = P^T straight from S^T
+// Route membership enters as one 32-bit mask word per (query, key tile),
+// built in LDS per segment of 8192 keys from each query's sorted route (one
+// binary search per query and segment, then independent coalesced reads with
+// equal words OR-combined across lanes before one atomic per word).  The tile's cost is (key tiles touched) x
+// 128 columns of MFMA work, so a tile is taken here only when its route
+// entries fill at least thr/1000 of (valid queries x key span); the gather
+// kernel handles the other tiles (both kernels evaluate the same integer test).
+constexpr int kSegTiles = 256;   // 32-key tiles per mask segment (8192 keys)
+
+struct TileStats {
+  bool dense;
+  int kmin, kmax;
+};
+
+// Evaluated by a whole wavefront (uniform result).  BQ <= 64.
+IRB_DEV TileStats tile_stats_wave(const AttnArgs& a, int b, int qa, int BQ, int thr_milli) {
+  const int lane = threadIdx.x & 63;
+  int kmin = 0x7fffffff, kmax = -1, total = 0, valid = 0;
+  const int t = qa + lane;
+  if (lane < BQ && t < a.S_q) {
+    const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
+    const int n = max(0, min(a.lens[row], a.L));
+    valid = 1;
+    if (n > 0) {
+      const int32_t* r = a.routes + row * a.L;
+      kmin = r[0];
+      kmax = r[n - 1];
+      total = n;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, __shfl_xor(kmin, o, 64));
+    kmax = max(kmax, __shfl_xor(kmax, o, 64));
+    total += __shfl_xor(total, o, 64);
+    valid += __shfl_xor(valid, o, 64);
+  }
+  TileStats st;
+  st.kmin = max(kmin, 0);
+  st.kmax = min(kmax, a.S_k - 1);
+  const int64_t span = st.kmax >= st.kmin ? static_cast<int64_t>(st.kmax - st.kmin + 1) : 0;
+  st.dense = total > 0 && span > 0 && static_cast<int64_t>(total) * 1000 >= static_cast<int64_t>(thr_milli) * valid * span;
+  return st;
+}
+
+template <typename T, int D, int DV, bool kShared, bool kDelta>
+__global__ void __launch_bounds__(256)
+attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G, int n_items, int latent,
+                const T* __restrict__ dout, float* __restrict__ delta, int tile_bq, int thr_milli) {
+  constexpr int PAD = sizeof(T) == 2 ? 8 : 4;
+  extern __shared__ __align__(16) char smem[];
+  const int wid = threadIdx.x >> 6;
+  int item, slice;
+  char* slab = smem;
+  if (kShared) {
+    item = blockIdx.x;
+    slice = wid;
+  } else {
+    item = blockIdx.x * 4 + wid;
+    slice = 0;
+    if (item >= n_items) return;
+    slab = smem + static_cast<size_t>(wid) * 32 * (DV + PAD) * sizeof(T);
+  }
+  const int kvh = item % a.Hkv;
+  const int t = (item / a.Hkv) % a.S_q;
+  const int b = item / (a.Hkv * a.S_q);
+  if (!kShared && tile_bq > 0 && tile_stats_wave(a, b, (t / tile_bq) * tile_bq, tile_bq, thr_milli).dense) return;
+  fwd_item<T, D, DV, kShared, kDelta>(a, out, lse, G, latent, dout, delta, b, t, kvh, slice, slab);
+}
+
+template <int D, int DV, int G, bool kDelta>
+__global__ void __launch_bounds__(256, 2)
+attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__ lse, const uint16_t* __restrict__ dout,
+                     float* __restrict__ delta, int n_qt, int thr_milli) {
+  using T = uint16_t;
+  constexpr int BQ = 128 / G;
+  constexpr int KS = D / 32, NDT = DV / 16;
+  constexpr int LDK = D + 8;      // K tile row: one key, D dims (+pad)
+  constexpr int LDT = 32 + 4;     // V^T tile row: one dim, 32 keys (+pad): 18 dwords, so the
+                                  // dword-pair stores of a wave hit 64 distinct banks
+  constexpr int KBYTES = 32 * LDK * 2, VBYTES = DV * LDT * 2;
+  constexpr int BUF = KBYTES + VBYTES;
+  __shared__ __align__(16) char raw[2 * BUF];
+  __shared__ uint32_t mask[BQ][kSegTiles];
+  __shared__ int tiles[kSegTiles];
+  __shared__ int s_ntiles;
+  __shared__ int cursor[BQ];
+  __shared__ int s_lo[BQ], s_hi[BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int bid = blockIdx.x;
+  const int kvh = bid % a.Hkv;
+  const int qt = (bid / a.Hkv) % n_qt;
+  const int b = bid / (a.Hkv * n_qt);
+  const int qa = qt * BQ;
+  const TileStats ts = tile_stats_wave(a, b, qa, BQ, thr_milli);
+  if (!ts.dense) return;
+
+  const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
+  const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
+  bf16x8 qop[2][KS];
+  int colq[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int c = 32 * wid + 16 * ct + l16;
+    const int qi = c / G, h = c % G;
+    const int t = qa + qi;
+    colq[ct] = qi;
+    const bool ok = t < a.S_q;
+    const T* qp = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(ok ? t : 0) * a.sq_t +
+                  static_cast<int64_t>(kvh * G + h) * a.sq_h + 8 * g16;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      qop[ct][s2] = *reinterpret_cast<const bf16x8*>(qp + 32 * s2);
+      if (!ok) zero8(qop[ct][s2]);
+    }
+  }
+  f32x4 oacc[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) { oacc[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f}; oacc[dt][1] = oacc[dt][0]; }
+  float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  const float sc2 = a.scale * kLog2e;
+
+  // tile loader: 32 keys of K (16-byte chunks per thread) and V (one thread =
+  // two adjacent keys x 8 dims, so V^T can be written as dword pairs)
+  constexpr int KC = D / 8, VG = DV / 8;
+  constexpr int KPER = (32 * KC + 255) / 256;
+  uint4 kreg[KPER], vreg[2];
+  const int vkp = tid % 16, vdg = tid / 16;           // key pair, dim group
+  const bool vown = vdg < VG;
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+      const int chunk = tid + 256 * u;
+      const int key = kt * 32 + chunk / KC;
+      kreg[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (chunk < 32 * KC && key < a.S_k)
+        kreg[u] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(key) * a.sk_t + 8 * (chunk % KC));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = kt * 32 + 2 * vkp + h;
+      vreg[h] = make_uint4(0u, 0u, 0u, 0u);
+      if (vown && key < a.S_k)
+        vreg[h] = *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(key) * a.sv_t + 8 * vdg);
+    }
+  };
+  auto lstore = [&](int buf) {
+    T* kb = reinterpret_cast<T*>(raw + buf * BUF);
+    uint32_t* vt32 = reinterpret_cast<uint32_t*>(raw + buf * BUF + KBYTES);
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+      const int chunk = tid + 256 * u;
+      if (chunk < 32 * KC) *reinterpret_cast<uint4*>(kb + (chunk / KC) * LDK + 8 * (chunk % KC)) = kreg[u];
+    }
+    if (vown) {
+      const uint32_t a0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+      const uint32_t a1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // dims 8*vdg + 2e and + 2e + 1; each dword = (key 2*vkp, key 2*vkp + 1)
+        vt32[(8 * vdg + 2 * e) * (LDT / 2) + vkp] = (a0[e] & 0xffffu) | (a1[e] << 16);
+        vt32[(8 * vdg + 2 * e + 1) * (LDT / 2) + vkp] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+      }
+    }
+  };
+
+  if (tid < BQ) cursor[tid] = 0;
+  const int kt_first = ts.kmin >> 5, kt_last = ts.kmax >> 5;
+  for (int seg0 = kt_first; seg0 <= kt_last; seg0 += kSegTiles) {
+    const int nseg = min(kSegTiles, kt_last - seg0 + 1);
+    const int key0 = seg0 * 32, key1 = key0 + kSegTiles * 32;
+    __syncthreads();
+    for (int i = tid; i < BQ * kSegTiles; i += 256) (&mask[0][0])[i] = 0u;
+    __syncthreads();
+    // route masks of this segment.  Entry ranges [lo, hi) per query: lo is the
+    // cursor left by the previous segment, hi a binary search (one lane per
+    // query, in parallel); then all 256 threads read consecutive entries with
+    // independent loads, each wavefront OR-combines runs of equal mask words
+    // (entries are sorted) and one lane per run does the LDS atomic.
+    if (wid == 0 && lane < BQ) {
+      const int t = qa + lane;
+      int lo = cursor[lane], hi = lo;
+      if (t < a.S_q) {
+        const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
+        const int n = max(0, min(a.lens[row], a.L));
+        const int32_t* r = a.routes + row * a.L;
+        int l1 = lo, h1 = n;
+        while (l1 < h1) { const int m = (l1 + h1) >> 1; if (r[m] < key1) l1 = m + 1; else h1 = m; }
+        hi = l1;
+      }
+      s_lo[lane] = lo;
+      s_hi[lane] = hi;
+      cursor[lane] = hi;
+    }
+    __syncthreads();
+    for (int qi = 0; qi < BQ; ++qi) {
+      const int lo = s_lo[qi], hi = s_hi[qi];
+      const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + qi) * a.L;
+      for (int e0 = lo; e0 < hi; e0 += 256) {
+        const int e = e0 + tid;
+        const int id = (e < hi) ? r[e] : -1;
+        const bool ok = id >= key0 && id < key1 && id < a.S_k;
+        const int word = ok ? ((id - key0) >> 5) : -1 - lane;   // unique dummy keys for idle lanes
+        uint32_t bits = ok ? (1u << ((id - key0) & 31)) : 0u;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t ob = __shfl_down(bits, o, 64);
+          const int ow = __shfl_down(word, o, 64);
+          if (lane + o < 64 && ow == word) bits |= ob;
+        }
+        const int prev = __shfl_up(word, 1, 64);
+        if (ok && (lane == 0 || prev != word)) atomicOr(&mask[qi][word], bits);
+      }
+    }
+    __syncthreads();
+    // compact list of the key tiles any query routes to
+    if (wid == 0) {
+      int base = 0;
+      for (int j0 = 0; j0 < kSegTiles; j0 += 64) {
+        const int j = j0 + lane;
+        uint32_t any = 0u;
+        if (j < nseg)
+          for (int qi = 0; qi < BQ; ++qi) any |= mask[qi][j];
+        const uint64_t bal = __ballot(any != 0u);
+        if (any) tiles[base + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+        base += __popcll(bal);
+      }
+      if (lane == 0) s_ntiles = base;
+    }
+    __syncthreads();
+    const int ntiles = s_ntiles;
+    if (ntiles == 0) continue;
+    gload(seg0 + tiles[0]);
+    lstore(0);
+    __syncthreads();
+    int buf = 0;
+    for (int it = 0; it < ntiles; ++it) {
+      const int ktl = tiles[it];
+      const bool more = it + 1 < ntiles;
+      if (more) gload(seg0 + tiles[it + 1]);
+      const T* kb = reinterpret_cast<const T*>(raw + buf * BUF);
+      const T* vt = reinterpret_cast<const T*>(raw + buf * BUF + KBYTES);
+      f32x4 st[2][2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) { st[kk][0] = f32x4{0.f, 0.f, 0.f, 0.f}; st[kk][1] = st[kk][0]; }
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + (16 * kk + l16) * LDK + 32 * s2 + 8 * g16);
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+            st[kk][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ct][s2], st[kk][ct], 0, 0, 0);
+        }
+      }
+      bf16x8 pop[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const uint32_t mw = mask[colq[ct]][ktl] >> (4 * g16);
+        float x[8];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[4 * kk + i] = ((mw >> (16 * kk + i)) & 1u) ? st[kk][ct][i] * sc2 : -INFINITY;
+            cmax = fmaxf(cmax, x[4 * kk + i]);
+          }
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+        const float mnew = fmaxf(m2[ct], cmax);
+        float p[8], ps = 0.f;
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;   // all masked so far: every p is 0
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { p[i] = fast_exp2(x[i] - mref); ps += p[i]; }
+        const float alpha = fast_exp2(m2[ct] - mref);
+        m2[ct] = mnew;
+        lsum[ct] = lsum[ct] * alpha + ps;
+        if (__ballot(alpha != 1.f)) {          // rescale only when some column's max moved
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[dt][ct][i] *= alpha;
+        }
+        pop[ct] = pack_bf16x8(p);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const T* vr = vt + (dt * 16 + l16) * LDT + 4 * g16;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          oacc[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], oacc[dt][ct], 0, 0, 0);
+      }
+      if (more) lstore(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int c = 32 * wid + 16 * ct + l16;
+    const int qi = c / G, h = c % G;
+    const int t = qa + qi;
+    float ltot = lsum[ct] + __shfl_xor(lsum[ct], 16, 64);
+    ltot += __shfl_xor(ltot, 32, 64);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (kDelta) {
+      float part = 0.f;
+      if (t < a.S_q) {
+        const T* dp = dout + ((static_cast<int64_t>(b) * a.S_q + t) * a.Hq + kvh * G + h) * DV + 4 * g16;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part += oacc[dt][ct][i] * inv * bf16_to_f32(dp[dt * 16 + i]);
+      }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (t < a.S_q && g16 == 0) delta[(static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + t] = part;
+    } else if (t < a.S_q) {
+      const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
+      T* op = out + (row * a.Hq + kvh * G + h) * DV + 4 * g16;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const float v[4] = {oacc[dt][ct][0] * inv, oacc[dt][ct][1] * inv, oacc[dt][ct][2] * inv, oacc[dt][ct][3] * inv};
+        store4(op + dt * 16, v);
+      }
+      if (g16 == 0)
+        lse[(static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + t] = ltot > 0.f ? (m2[ct] + log2f(ltot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// route-density threshold (per mille) above which a query tile runs on the tile kernel
+static int tile_thr_milli() {
+  static int v = [] {
+    const char* e = getenv("IRB_TILE_MIN_DENSITY");
+    return e ? static_cast<int>(atof(e) * 1000.0) : 120;
+  }();
+  return v;
+}
+
+template <int D, int DV, int G, bool kDelta>
+static void launch_tile(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, hipStream_t stream) {
+  constexpr int BQ = 128 / G;
+  const int n_qt = (a.S_q + BQ - 1) / BQ;
+  const unsigned grid = static_cast<unsigned>(a.B) * n_qt * a.Hkv;
+  hipLaunchKernelGGL((attn_fwd_tile_kernel<D, DV, G, kDelta>), dim3(grid), dim3(256), 0, stream, a,
+                     static_cast<uint16_t*>(out), lse, static_cast<const uint16_t*>(dout), delta, n_qt,
+                     tile_thr_milli());
+}
+
 template <typename T, int D, int DV, bool kDelta>
 static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
@@ -321,6 +677,15 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
   if (items == 0) return 0;
   const int PAD = sizeof(T) == 2 ? 8 : 4;
   const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
+  int tile_bq = 0;    // > 0: the gather kernel skips the query tiles the tile kernel takes
+  if constexpr (sizeof(T) == 2 && (D == 64 || D == 128) && D == DV) {
+    if (tile_thr_milli() <= 1000 && (G == 4 || G == 8 || G == 16)) {
+      if (G == 4) launch_tile<D, DV, 4, kDelta>(a, out, lse, dout, delta, stream);
+      if (G == 8) launch_tile<D, DV, 8, kDelta>(a, out, lse, dout, delta, stream);
+      if (G == 16) launch_tile<D, DV, 16, kDelta>(a, out, lse, dout, delta, stream);
+      tile_bq = 128 / G;
+    }
+  }
   if (G <= 16) {
     const size_t lds = static_cast<size_t>(4) * 32 * (DV + PAD) * sizeof(T);
     auto kern = attn_fwd_kernel<T, D, DV, false, kDelta>;
@@ -330,7 +695,8 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
       if (e != hipSuccess) return static_cast<int>(e);
     }
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), lds, stream, a,
-                       static_cast<T*>(out), lse, G, static_cast<int>(items), latent, static_cast<const T*>(dout), delta);
+                       static_cast<T*>(out), lse, G, static_cast<int>(items), latent, static_cast<const T*>(dout), delta,
+                       tile_bq, tile_thr_milli());
   } else {
     const int slices = (G + 15) / 16;
     const size_t lds = static_cast<size_t>(32) * ((D + PAD) + (latent ? 0 : (DV + PAD))) * sizeof(T);
@@ -341,7 +707,8 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
       if (e != hipSuccess) return static_cast<int>(e);
     }
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(items)), dim3(64 * slices), lds, stream, a,
-                       static_cast<T*>(out), lse, G, static_cast<int>(items), latent, static_cast<const T*>(dout), delta);
+                       static_cast<T*>(out), lse, G, static_cast<int>(items), latent, static_cast<const T*>(dout), delta,
+                       0, 0);
   }
   return 0;
 }

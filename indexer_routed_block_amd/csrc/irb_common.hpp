@@ -36,6 +36,23 @@ IRB_DEV void split_bf16(float f, uint16_t& hi, uint16_t& lo) {
   lo = f32_to_bf16(f - bf16_to_f32(hi));
 }
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2n;
+
+// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
+IRB_DEV uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2n v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// 8 floats -> MFMA operand
+IRB_DEV bf16x8 pack_bf16x8(const float* f) {
+  const uint4 u = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                             pack_bf16x2(f[6], f[7]));
+  return __builtin_bit_cast(bf16x8, u);
+}
+// 2^x on the hardware exp unit (results below the normal range flush to 0,
+// which is harmless for softmax weights)
+IRB_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <typename T> IRB_DEV float load_as_f32(const T* p);
 template <> IRB_DEV float load_as_f32<float>(const float* p) { return *p; }
 template <> IRB_DEV float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
