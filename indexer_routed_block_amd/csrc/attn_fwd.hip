@@ -223,8 +223,7 @@ IRB_DEV void fwd_item(const AttnArgs& a, T* __restrict__ out, float* __restrict_
         x[ti][i] = (e < n) ? st[ti][i] * sc2 : -INFINITY;
         cmax = fmaxf(cmax, x[ti][i]);
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    cmax = row4_max(cmax);
     const float mnew = fmaxf(m2, cmax);
     const float mref = (mnew == -INFINITY) ? 0.f : mnew;   // nothing visible yet: every p is 0
     float p[2][4];
@@ -272,8 +271,7 @@ IRB_DEV void fwd_item(const AttnArgs& a, T* __restrict__ out, float* __restrict_
     }
   }
 
-  float ltot = lsum + __shfl_xor(lsum, 16, 64);
-  ltot += __shfl_xor(ltot, 32, 64);
+  float ltot = row4_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (kDelta) {
     float part = 0.f;
@@ -284,8 +282,7 @@ IRB_DEV void fwd_item(const AttnArgs& a, T* __restrict__ out, float* __restrict_
 #pragma unroll
         for (int i = 0; i < 4; ++i) part += oacc[dt][i] * inv * load_as_f32(dp + dt * 16 + i);
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = row4_sum(part);
     if (l16 < nh && g16 == 0) delta[(static_cast<int64_t>(b) * a.Hq + h0 + l16) * a.S_q + t] = part;
     return;
   }
@@ -403,9 +400,13 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g16 = lane >> 4, l16 = lane & 15;
+  // consecutive workgroups take the KV heads of one query tile (one head per
+  // XCD when 8 is a multiple of Hkv, keeping that head's K/V in its L2), and
+  // query tiles run last-first: causal tiles late in the sequence span the
+  // most keys, so the heavy ones start early and the grid ends on light ones
   const int bid = blockIdx.x;
   const int kvh = bid % a.Hkv;
-  const int qt = (bid / a.Hkv) % n_qt;
+  const int qt = n_qt - 1 - (bid / a.Hkv) % n_qt;
   const int b = bid / (a.Hkv * n_qt);
   const int qa = qt * BQ;
   const TileStats ts = tile_stats_wave(a, b, qa, BQ, thr_milli);
@@ -437,28 +438,35 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   const float sc2 = a.scale * kLog2e;
 
   // tile loader: 32 keys of K (16-byte chunks per thread) and V (one thread =
-  // two adjacent keys x 8 dims, so V^T can be written as dword pairs)
+  // two adjacent keys x 8 dims, so V^T can be written as dword pairs).  Row
+  // pointers are formed once; a key tile only adds a scalar offset.
   constexpr int KC = D / 8, VG = DV / 8;
   constexpr int KPER = (32 * KC + 255) / 256;
   uint4 kreg[KPER], vreg[2];
   const int vkp = tid % 16, vdg = tid / 16;           // key pair, dim group
   const bool vown = vdg < VG;
+  const T* kptr[KPER];
+  int krow[KPER];
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int chunk = tid + 256 * u;
+    krow[u] = (chunk < 32 * KC) ? chunk / KC : 1 << 20;
+    kptr[u] = kbase + static_cast<int64_t>(chunk < 32 * KC ? chunk / KC : 0) * a.sk_t + 8 * (chunk % KC);
+  }
+  const T* vptr0 = vbase + static_cast<int64_t>(2 * vkp) * a.sv_t + 8 * (vown ? vdg : 0);
+  const T* vptr1 = vptr0 + a.sv_t;
+  const int64_t kstep = 32 * a.sk_t, vstep = 32 * a.sv_t;
   auto gload = [&](int kt) {
+    const int rows = a.S_k - kt * 32;                  // keys of this tile that exist
 #pragma unroll
     for (int u = 0; u < KPER; ++u) {
-      const int chunk = tid + 256 * u;
-      const int key = kt * 32 + chunk / KC;
       kreg[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (chunk < 32 * KC && key < a.S_k)
-        kreg[u] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(key) * a.sk_t + 8 * (chunk % KC));
+      if (krow[u] < rows) kreg[u] = *reinterpret_cast<const uint4*>(kptr[u] + kt * kstep);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = kt * 32 + 2 * vkp + h;
-      vreg[h] = make_uint4(0u, 0u, 0u, 0u);
-      if (vown && key < a.S_k)
-        vreg[h] = *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(key) * a.sv_t + 8 * vdg);
-    }
+    vreg[0] = make_uint4(0u, 0u, 0u, 0u);
+    vreg[1] = vreg[0];
+    if (vown && 2 * vkp < rows) vreg[0] = *reinterpret_cast<const uint4*>(vptr0 + kt * vstep);
+    if (vown && 2 * vkp + 1 < rows) vreg[1] = *reinterpret_cast<const uint4*>(vptr1 + kt * vstep);
   };
   auto lstore = [&](int buf) {
     T* kb = reinterpret_cast<T*>(raw + buf * BUF);
@@ -569,36 +577,48 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
             st[kk][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ct][s2], st[kk][ct], 0, 0, 0);
         }
       }
+      // online softmax per column.  The reference max m2 only moves when a
+      // score exceeds it by more than kLazy (log2 units), so weights stay
+      // <= 2^kLazy and the rescale of the accumulators is rare; the result is
+      // exact after normalisation by lsum.
+      constexpr float kLazy = 8.f;
       bf16x8 pop[2];
+      float alpha[2];
+      bool rescale = false;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const uint32_t mw = mask[colq[ct]][ktl] >> (4 * g16);
-        float x[8];
-        float cmax = -INFINITY;
+        float xr[8];
+        float cm = -INFINITY;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            x[4 * kk + i] = ((mw >> (16 * kk + i)) & 1u) ? st[kk][ct][i] * sc2 : -INFINITY;
-            cmax = fmaxf(cmax, x[4 * kk + i]);
+            xr[4 * kk + i] = ((mw >> (16 * kk + i)) & 1u) ? st[kk][ct][i] : -INFINITY;
+            cm = fmaxf(cm, xr[4 * kk + i]);
           }
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-        const float mnew = fmaxf(m2[ct], cmax);
+        cm = row4_max(cm);
+        const float cmax = cm * sc2;
+        alpha[ct] = 1.f;
+        if (cmax > m2[ct] + kLazy) {
+          alpha[ct] = fast_exp2(m2[ct] - cmax);
+          m2[ct] = cmax;
+          rescale = true;
+        }
+        const float nm = (m2[ct] == -INFINITY) ? 0.f : -m2[ct];
         float p[8], ps = 0.f;
-        const float mref = (mnew == -INFINITY) ? 0.f : mnew;   // all masked so far: every p is 0
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { p[i] = fast_exp2(x[i] - mref); ps += p[i]; }
-        const float alpha = fast_exp2(m2[ct] - mref);
-        m2[ct] = mnew;
-        lsum[ct] = lsum[ct] * alpha + ps;
-        if (__ballot(alpha != 1.f)) {          // rescale only when some column's max moved
+        for (int i = 0; i < 8; ++i) { p[i] = fast_exp2(fmaf(xr[i], sc2, nm)); ps += p[i]; }
+        lsum[ct] = lsum[ct] * alpha[ct] + ps;
+        pop[ct] = pack_bf16x8(p);
+      }
+      if (__ballot(rescale)) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) oacc[dt][ct][i] *= alpha;
-        }
-        pop[ct] = pack_bf16x8(p);
+            for (int i = 0; i < 4; ++i) oacc[dt][ct][i] *= alpha[ct];
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -622,8 +642,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     const int c = 32 * wid + 16 * ct + l16;
     const int qi = c / G, h = c % G;
     const int t = qa + qi;
-    float ltot = lsum[ct] + __shfl_xor(lsum[ct], 16, 64);
-    ltot += __shfl_xor(ltot, 32, 64);
+    float ltot = row4_sum(lsum[ct]);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (kDelta) {
       float part = 0.f;
@@ -634,8 +653,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
 #pragma unroll
           for (int i = 0; i < 4; ++i) part += oacc[dt][ct][i] * inv * bf16_to_f32(dp[dt * 16 + i]);
       }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
+      part = row4_sum(part);
       if (t < a.S_q && g16 == 0) delta[(static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + t] = part;
     } else if (t < a.S_q) {
       const int64_t row = static_cast<int64_t>(b) * a.S_q + t;

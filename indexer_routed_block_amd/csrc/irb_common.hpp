@@ -93,6 +93,33 @@ IRB_DEV void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Reductions over the four 16-lane rows of a wavefront (lanes l, l^16, l^32,
+// l^48) on the VALU: with both operands equal, v_permlane16_swap /
+// v_permlane32_swap return {x[l], x[l^16]} / {x[l], x[l^32]} in some order,
+// so combining the pair gives the butterfly step without an LDS round trip.
+IRB_DEV float row4_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+IRB_DEV float row4_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// sum of lanes l and l^16 only
+IRB_DEV float row_pair_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
 // ---------------------------------------------------------------- layout
 struct Layout {
   int B, S;

@@ -162,8 +162,8 @@ score_kernel(Layout L, const QT* __restrict__ q, int H, const float* __restrict_
     }
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      if (gpq >= 2) part[ct] += __shfl_xor(part[ct], 16, 64);
-      if (gpq >= 4) part[ct] += __shfl_xor(part[ct], 32, 64);
+      if (gpq >= 4) part[ct] = row4_sum(part[ct]);
+      else if (gpq == 2) part[ct] = row_pair_sum(part[ct]);
     }
     if ((g % gpq) == 0) {
       const int qw = qa + u * qpu + g / gpq;
