@@ -173,8 +173,8 @@ def indexer_scores(qI, w, kc, c, scale=None, cu_seqlens=None, row_lens=None, q0=
     ``indexer_score_tile``: signed FP32 head weights).  ``scale`` defaults
     to 1/sqrt(D_idx).  Padding queries score -inf everywhere.
     """
-    qI = np.asarray(qI, dtype=np.float64)
-    w = np.asarray(w, dtype=np.float64)
+    qI = np.asarray(qI)
+    w = np.asarray(w)
     kc = np.asarray(kc, dtype=np.float64)
     B, S, H, D = qI.shape
     q1 = S if q1 is None else q1
@@ -186,8 +186,10 @@ def indexer_scores(qI, w, kc, c, scale=None, cu_seqlens=None, row_lens=None, q0=
     for b in range(B):
         for r0 in range(q0, q1, row_chunk):
             r1 = min(q1, r0 + row_chunk)
-            dots = np.einsum("thd,jd->thj", qI[b, r0:r1], kc[b])
-            s = scale * np.einsum("th,thj->tj", w[b, r0:r1], np.maximum(dots, 0.0))
+            qs = qI[b, r0:r1].astype(np.float64)                     # [t, H, D]
+            ws = w[b, r0:r1].astype(np.float64)                      # [t, H]
+            dots = qs @ kc[b].T                                      # [t, H, NB]
+            s = scale * (ws[:, None, :] @ np.maximum(dots, 0.0))[:, 0, :]
             j = np.arange(NB)[None, :]
             lo = base[b, r0:r1, None]
             vis = valid[b, r0:r1, None] & (j >= lo) & (j < lo + nb[b, r0:r1, None])
@@ -335,7 +337,7 @@ def compact_routes(ids, key_count):
 # a5: forward / reverse block lists
 # ---------------------------------------------------------------------------
 
-def block_lists(routes, lens, S_k, block_q, block_k, reverse=False):
+def block_lists(routes, lens, S_k, block_q, block_k, reverse=False, rows=None):
     """Block-sparse lists from token routes.
 
     Forward (FA4 page, ``_selected_block_lists``, ``_block_lists``): for
@@ -344,16 +346,38 @@ def block_lists(routes, lens, S_k, block_q, block_k, reverse=False):
     Reverse (``reverse=True``, used by backward): for every key tile, the
     ascending query tiles that reach it.  Returns counts [B, rows] and
     indices [B, rows, width] with -1 after the count; width is the number of
-    tiles on the other axis.
+    tiles on the other axis.  ``rows`` (list of (b, row)) restricts which
+    list rows are evaluated; the others keep count 0.
     """
     routes = np.asarray(routes)
     lens = np.asarray(lens)
     B, S_q, _ = routes.shape
     nqt = -(-S_q // block_q)
     nkt = -(-S_k // block_k)
-    rows, width = (nkt, nqt) if reverse else (nqt, nkt)
-    counts = np.zeros((B, rows), dtype=np.int32)
-    indices = np.full((B, rows, width), -1, dtype=np.int32)
+    n_rows, width = (nkt, nqt) if reverse else (nqt, nkt)
+    counts = np.zeros((B, n_rows), dtype=np.int32)
+    indices = np.full((B, n_rows, width), -1, dtype=np.int32)
+    if rows is not None:
+        # one list row at a time, straight from its definition
+        L = routes.shape[2]
+        pos = np.arange(L)[None, :]
+        for b, r in rows:
+            if reverse:
+                lo, hi = r * block_k, min((r + 1) * block_k, S_k)
+                hit = np.zeros(S_q, dtype=bool)
+                for t0 in range(0, S_q, 2048):        # row chunks keep temporaries small
+                    rr = routes[b, t0:t0 + 2048]
+                    live = pos < np.minimum(lens[b, t0:t0 + 2048], L)[:, None]
+                    hit[t0:t0 + 2048] = np.any(live & (rr >= lo) & (rr < hi), axis=1)
+                nz = np.unique(np.nonzero(hit)[0] // block_q)
+            else:
+                t0, t1 = r * block_q, min((r + 1) * block_q, S_q)
+                live = pos < np.minimum(lens[b, t0:t1], L)[:, None]
+                ids = routes[b, t0:t1][live]
+                nz = np.unique(ids[(ids >= 0) & (ids < S_k)] // block_k)
+            counts[b, r] = len(nz)
+            indices[b, r, :len(nz)] = nz
+        return counts, indices
     for b in range(B):
         grid = np.zeros((nqt, nkt), dtype=bool)
         for t in range(S_q):
@@ -362,7 +386,7 @@ def block_lists(routes, lens, S_k, block_q, block_k, reverse=False):
                 grid[t // block_q, routes[b, t, :n] // block_k] = True
         if reverse:
             grid = grid.T
-        for r in range(rows):
+        for r in range(n_rows):
             nz = np.nonzero(grid[r])[0]
             counts[b, r] = len(nz)
             indices[b, r, :len(nz)] = nz
@@ -389,9 +413,8 @@ def attention_fwd(q, k, v, routes, scale=None, rows=None):
     A query with an empty route gets o = 0 and lse = -inf.  ``rows``
     optionally restricts the evaluation to a list of (b, t) pairs.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    # inputs stay in their own dtype; each gathered piece is widened to float64
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     B, S_q, Hq, D = q.shape
     S_k, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
     G = Hq // Hkv
@@ -403,19 +426,19 @@ def attention_fwd(q, k, v, routes, scale=None, rows=None):
         ids = _route_set(routes[b, t], S_k)
         if len(ids) == 0:
             continue
-        kg = k[b, ids]                                  # [n, Hkv, D]
-        vg = v[b, ids]                                  # [n, Hkv, Dv]
-        qg = q[b, t].reshape(Hkv, G, D)
-        x = scale * np.einsum("agd,nad->agn", qg, kg)  # [Hkv, G, n]
+        kg = k[b, ids].astype(np.float64).transpose(1, 0, 2)    # [Hkv, n, D]
+        vg = v[b, ids].astype(np.float64).transpose(1, 0, 2)    # [Hkv, n, Dv]
+        qg = q[b, t].astype(np.float64).reshape(Hkv, G, D)
+        x = scale * (qg @ kg.transpose(0, 2, 1))                # [Hkv, G, n]
         m = x.max(axis=-1, keepdims=True)
         ls = m + np.log(np.exp(x - m).sum(axis=-1, keepdims=True))
         p = np.exp(x - ls)
-        o[b, t] = np.einsum("agn,nae->age", p, vg).reshape(Hq, Dv)
+        o[b, t] = (p @ vg).reshape(Hq, Dv)
         lse[b, :, t] = ls.reshape(Hq)
     return o, lse
 
 
-def attention_bwd(q, k, v, routes, dO, scale=None):
+def attention_bwd(q, k, v, routes, dO, scale=None, rows=None, keys=None):
     """Sparse GQA backward: dq, dk, dv (float64) for dO.
 
     Gradients of the forward above with respect to q, k and v (QSA page,
@@ -424,37 +447,55 @@ def attention_bwd(q, k, v, routes, dO, scale=None):
     ``P = softmax(x)``, ``dP = dO V_R^T``, ``dS = P (dP - rowsum(dO * o))``,
     ``dq = scale dS K_R``, ``dK_R += scale dS^T q``, ``dV_R += P^T dO``;
     the key/value sums run over every query that routes to that key.
+    ``rows`` (list of (b, t)) restricts the dq evaluation and ``keys`` (list
+    of (b, key)) the dk/dv evaluation; other entries are left at zero.  With
+    either given, only the queries they need are evaluated.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    dO = np.asarray(dO, dtype=np.float64)
+    # inputs stay in their own dtype; each gathered piece is widened to float64
+    q, k, v, dO = np.asarray(q), np.asarray(k), np.asarray(v), np.asarray(dO)
     B, S_q, Hq, D = q.shape
     S_k, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    restricted = rows is not None or keys is not None
+    want_rows = set(map(tuple, rows)) if rows is not None else set()
+    key_sets = {}
+    if keys is not None:
+        for b_, kk in keys:
+            key_sets.setdefault(int(b_), set()).add(int(kk))
     for b in range(B):
+        ks = np.array(sorted(key_sets.get(b, ())), dtype=np.int64)
         for t in range(S_q):
             ids = _route_set(routes[b, t], S_k)
             if len(ids) == 0:
                 continue
-            kg, vg = k[b, ids], v[b, ids]
-            qg = q[b, t].reshape(Hkv, G, D)
-            dog = dO[b, t].reshape(Hkv, G, Dv)
-            x = scale * np.einsum("agd,nad->agn", qg, kg)
+            need_q = (not restricted) or (b, t) in want_rows
+            hit = np.isin(ids, ks) if keys is not None else None
+            need_k = (not restricted) or (hit is not None and hit.any())
+            if not (need_q or need_k):
+                continue
+            kg = k[b, ids].astype(np.float64).transpose(1, 0, 2)    # [Hkv, n, D]
+            vg = v[b, ids].astype(np.float64).transpose(1, 0, 2)    # [Hkv, n, Dv]
+            qg = q[b, t].astype(np.float64).reshape(Hkv, G, D)
+            dog = dO[b, t].astype(np.float64).reshape(Hkv, G, Dv)
+            x = scale * (qg @ kg.transpose(0, 2, 1))    # [Hkv, G, n]
             m = x.max(axis=-1, keepdims=True)
             p = np.exp(x - m)
             p /= p.sum(axis=-1, keepdims=True)
-            og = np.einsum("agn,nae->age", p, vg)
+            og = p @ vg                                 # [Hkv, G, Dv]
             delta = np.sum(dog * og, axis=-1, keepdims=True)
-            dp = np.einsum("age,nae->agn", dog, vg)
+            dp = dog @ vg.transpose(0, 2, 1)            # [Hkv, G, n]
             ds = p * (dp - delta)
-            dq[b, t] = (scale * np.einsum("agn,nad->agd", ds, kg)).reshape(Hq, D)
-            dk[b, ids] += scale * np.einsum("agn,agd->nad", ds, qg)
-            dv[b, ids] += np.einsum("agn,age->nae", p, dog)
+            if need_q:
+                dq[b, t] = (scale * (ds @ kg)).reshape(Hq, D)
+            if need_k:
+                sel = slice(None) if hit is None else hit
+                # ids are unique, so the fancy-indexed += adds each key once
+                dk[b, ids[sel]] += scale * (ds[:, :, sel].transpose(0, 2, 1) @ qg).transpose(1, 0, 2)
+                dv[b, ids[sel]] += (p[:, :, sel].transpose(0, 2, 1) @ dog).transpose(1, 0, 2)
     return dq, dk, dv
 
 
@@ -465,20 +506,24 @@ def latent_attention_fwd(q, kv, idx, scale, dv=512):
     (-1 invalid); keys are the full latent rows, values their first ``dv``
     channels.  Returns o [T, H, dv] and lse [H, T].
     """
-    k = np.asarray(kv, dtype=np.float64)[None]
+    k = np.asarray(kv)[None]
     o, lse = attention_fwd(np.asarray(q)[None], k, k[..., :dv], np.asarray(idx)[None, :, 0, :], scale)
     return o[0], lse[0]
 
 
-def latent_attention_bwd(q, kv, idx, dO, scale, dv=512):
+def latent_attention_bwd(q, kv, idx, dO, scale, dv=512, rows=None, keys=None):
     """Latent backward: dq [T, H, Dqk] and the merged latent gradient dkv [T, 1, Dqk].
 
     Keys and values are views of one latent tensor, so its gradient is
     ``dK + [dV, 0]`` (the value part covers the first ``dv`` channels).
+    ``rows`` / ``keys`` (lists of token indices) restrict the evaluation as
+    in ``attention_bwd``.
     """
-    k = np.asarray(kv, dtype=np.float64)[None]
+    k = np.asarray(kv)[None]
+    rows = None if rows is None else [(0, int(t)) for t in rows]
+    keys = None if keys is None else [(0, int(j)) for j in keys]
     dq, dk, dvv = attention_bwd(np.asarray(q)[None], k, k[..., :dv], np.asarray(idx)[None, :, 0, :],
-                                np.asarray(dO)[None], scale)
+                                np.asarray(dO)[None], scale, rows=rows, keys=keys)
     dkv = dk[0].copy()
     dkv[..., :dv] += dvv[0]
     return dq[0], dkv

@@ -21,13 +21,15 @@ Conventions
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
 
-TENSOR_ORDER = ("layout", "kI", "qI", "w", "gamma", "q", "k", "v", "dO", "idx")
+TENSOR_ORDER = ("layout", "kI", "qI", "w", "gamma", "q", "k", "v", "dO", "idx", "draws")
 
 
 def _children(base_seed: int) -> dict:
@@ -37,24 +39,59 @@ def _children(base_seed: int) -> dict:
 
 def to_bf16_values(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); return float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    _round_bf16_inplace(x)
+    return x
+
+
+def _round_bf16_inplace(x: np.ndarray) -> None:
     bits = x.view(np.uint32)
     lsb = (bits >> np.uint32(16)) & np.uint32(1)
-    rounded = (bits + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
-    return rounded.view(np.float32)
+    bits += np.uint32(0x7FFF)
+    bits += lsb
+    bits &= np.uint32(0xFFFF0000)
+
+
+_CHUNK = 1 << 21            # elements per independently seeded piece of a tensor
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 def _normal(rng, shape, dtype: str, rms_rows: bool = False, scale: float = 1.0) -> np.ndarray:
-    x = rng.standard_normal(shape, dtype=np.float32)
-    if rms_rows:
-        # per-head RMS normalisation of the last axis: x / sqrt(mean(x^2))
-        ms = np.mean(np.square(x, dtype=np.float32), axis=-1, keepdims=True, dtype=np.float32)
-        x /= np.sqrt(ms)
-    if scale != 1.0:
-        x *= np.float32(scale)
-    if dtype == "bf16":
-        x = to_bf16_values(x)
-    return x
+    """N(0,1) float32 tensor drawn in row-aligned pieces, each from its own PCG64 seeded by ``rng``.
+
+    The pieces are filled by a thread pool (NumPy's generators and ufuncs run
+    without the GIL), so drawing a 10^9-element tensor takes seconds.  The
+    values depend only on ``rng``'s state and ``shape``.
+    """
+    shape = tuple(int(s) for s in shape)
+    out = np.empty(shape, dtype=np.float32)
+    n = out.size
+    if n == 0:
+        return out
+    row = shape[-1] if shape else 1
+    flat = out.reshape(-1, row)
+    rows_per = max(1, _CHUNK // row)
+    starts = list(range(0, flat.shape[0], rows_per))
+    seeds = rng.integers(0, 2 ** 63, size=len(starts), dtype=np.int64)
+
+    def fill(i):
+        piece = flat[starts[i]:starts[i] + rows_per]
+        np.random.Generator(np.random.PCG64(int(seeds[i]))).standard_normal(piece.shape, dtype=np.float32, out=piece)
+        if rms_rows:
+            # per-head RMS normalisation of the last axis: x / sqrt(mean(x^2))
+            ms = np.mean(np.square(piece, dtype=np.float32), axis=-1, keepdims=True, dtype=np.float32)
+            piece /= np.sqrt(ms)
+        if scale != 1.0:
+            piece *= np.float32(scale)
+        if dtype == "bf16":
+            _round_bf16_inplace(piece)
+
+    if len(starts) == 1:
+        fill(0)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, range(len(starts))))
+    return out
 
 
 def rope_table(doc_pos: np.ndarray, d_rope: int, theta: float = 10000.0) -> np.ndarray:
@@ -186,7 +223,8 @@ def make_inputs(wl: Workload, parts=("route", "attn"), S: Optional[int] = None,
     """Draw the inputs of a workload.
 
     ``parts`` selects "route" (indexer states, weights, rotary table), "attn"
-    (q, k, v), "bwd" (dO) and, for the latent workload, "idx".  ``S``, ``B``,
+    (q, k, v), "bwd" (dO), "draws" (uniform numbers, one per row and
+    selection slot) and, for the latent workload, "idx".  ``S``, ``B``,
     ``cu_seqlens``, ``row_lens`` and ``seed`` override the workload's own
     values so that tests can draw the same recipe at smaller sizes.
     """
@@ -221,6 +259,10 @@ def make_inputs(wl: Workload, parts=("route", "attn"), S: Optional[int] = None,
             out["dO"] = _normal(rngs["dO"], (B, S, wl.Hq, wl.Dv), dt)
     if "idx" in parts and wl.latent:
         out["idx"] = latent_indices(rngs["idx"], S, wl.latent_width)
+    if "draws" in parts and not wl.latent:
+        # uniform [0, 1) per (row, selection slot): a stand-in for block choices when a
+        # test needs routes at full size without scoring every block
+        out["draws"] = rngs["draws"].random((B, S, wl.topk), dtype=np.float32)
     return out
 
 

@@ -8,12 +8,13 @@ DEV = "cuda"
 
 
 def to_dev(x, dtype=None):
+    """Upload a NumPy array, converting on the device (bf16 inputs are exactly representable)."""
     if x is None:
         return None
-    t = torch.from_numpy(np.ascontiguousarray(x))
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     if dtype is not None:
         t = t.to(dtype)
-    return t.to(DEV)
+    return t
 
 
 def act_dtype(wl_dtype):
@@ -56,3 +57,16 @@ def attn_tol_check(got, want, dtype, what):
     print(f"  {what}: max-abs {mx:.3e} mean-abs {mean:.3e} max|ref| {scale:.3f}")
     assert ok, f"{what}: max-abs {mx:.3e} (beyond 2^-7|ref| {excess:.3e}) mean-abs {mean:.3e} (max |ref| {scale:.3f})"
     return mx, mean
+
+
+def score_bound(qI, w, kc, scale):
+    """M[b, t, j] = scale * sum_h |w[t,h]| * sum_d |q[t,h,d] k[j,d]|.
+
+    The "1e-3 relative" score tolerance is taken against this magnitude: it
+    bounds the cancellation inside each dot product as well as across the
+    signed head weights, so it is the scale FP32-class rounding error lives
+    on.  (relu(q.k) alone is not: a dot product that cancels to ~0 still
+    carries rounding error of order sum_d |q_d k_d| * 2^-17.)
+    """
+    dots = np.abs(qI.astype(np.float64)) @ np.abs(np.asarray(kc, dtype=np.float64)).swapaxes(-1, -2)[:, None]
+    return scale * (np.abs(w.astype(np.float64))[..., None, :] @ dots)[..., 0, :]

@@ -9,7 +9,7 @@ import torch
 import indexer_routed_block_amd as irb
 import oracle
 import synth
-from gpu_util import DEV, act_dtype, banner, host, to_dev
+from gpu_util import DEV, act_dtype, banner, host, score_bound as _score_bound, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -57,26 +57,15 @@ def test_compress_keys(wl_name, S, layout):
         np.testing.assert_array_equal(host(cu_blocks), ref_cub)
 
 
-def _score_bound(qI, w, kc, scale):
-    """M[t, j] = scale * sum_h |w[t,h]| * sum_d |q[t,h,d] k[j,d]|.
-
-    The "1e-3 relative" score tolerance is taken against this magnitude: it
-    bounds the cancellation inside each dot product as well as across the
-    signed head weights, so it is the scale FP32-class rounding error lives
-    on.  (relu(q.k) alone is not: a dot product that cancels to ~0 still
-    carries rounding error of order sum_d |q_d k_d| * 2^-17.)
-    """
-    dots = np.einsum("bthd,bjd->bthj", np.abs(qI.astype(np.float64)), np.abs(kc))
-    return scale * np.einsum("bth,bthj->btj", np.abs(w.astype(np.float64)), dots)
-
-
 @pytest.mark.parametrize("wl_name,S,layout", CASES)
 def test_indexer_score_tile(wl_name, S, layout):
     banner(f"score {wl_name} S={S} {layout}")
     wl, x = _inputs(wl_name, S, layout)
     d = _dev_inputs(wl, x)
-    kc, cu_blocks = irb.compress_keys(d["kI"], d["gamma"], d["freqs"], wl.c, 1e-5, d["cu"], d["rl"])
-    kc_h = host(kc).astype(np.float64)
+    # the oracle's compressed keys feed both sides (FP32 copy for the GPU)
+    kc_h, ref_cub = oracle.compress_keys(x["kI"], x["gamma"], 1e-5, x["freqs"], wl.c, x["cu_seqlens"], x["row_lens"])
+    kc = to_dev(kc_h.astype(np.float32))
+    cu_blocks = to_dev(ref_cub)
     scale = 1.0 / math.sqrt(wl.D_idx)
     nb = S // wl.c
     # full tile plus an unaligned sub-tile
@@ -211,3 +200,17 @@ def test_block_lists_bit_exact(bq, bk, reverse):
     rc, ri = oracle.block_lists(routes, lens, S, bq, bk, reverse)
     np.testing.assert_array_equal(host(counts), rc)
     np.testing.assert_array_equal(host(indices), ri)
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_select_rows_longer_than_lds(ties):
+    """Rows with more visible blocks than the select kernel keeps in LDS (40000 > 32768)."""
+    S, c, topk, rows = 160000, 4, 300, 16
+    banner(f"select global-memory rows S={S} ties={ties}")
+    rng = np.random.default_rng(7 + ties)
+    q0 = S - rows
+    scores = _quantised_scores(rng, 1, rows, S // c, ties)
+    sel, cnt = irb.select_topk_regions(to_dev(scores), c, topk, S, q0=q0)
+    rsel, rcnt = oracle.select_topk(scores.astype(np.float64), c, topk, q0=q0, S=S)
+    np.testing.assert_array_equal(host(cnt)[:, q0:], rcnt)
+    np.testing.assert_array_equal(host(sel)[:, q0:], rsel)

@@ -178,3 +178,20 @@ def test_duplicates_and_invalid_ids_collapse():
     ob, lb = oracle.attention_fwd(q, k, v, b)
     np.testing.assert_array_equal(oa, ob)
     np.testing.assert_array_equal(la, lb)
+
+
+def test_restricted_backward_matches_full():
+    rng = np.random.default_rng(38)
+    B, S, Hq, Hkv, D, Dv = 2, 31, 4, 2, 8, 6
+    q = rng.standard_normal((B, S, Hq, D)); k = rng.standard_normal((B, S, Hkv, D)); v = rng.standard_normal((B, S, Hkv, Dv))
+    dO = rng.standard_normal((B, S, Hq, Dv))
+    routes, lens = _routes(rng, B, S, 9)
+    full = oracle.attention_bwd(q, k, v, routes, dO, 0.4)
+    rows = [(0, 3), (1, 30), (1, 0)]
+    keys = [(0, 0), (0, 17), (1, 29)]
+    part = oracle.attention_bwd(q, k, v, routes, dO, 0.4, rows=rows, keys=keys)
+    for (b, t) in rows:
+        np.testing.assert_array_equal(part[0][b, t], full[0][b, t])
+    for (b, kk) in keys:
+        np.testing.assert_allclose(part[1][b, kk], full[1][b, kk], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(part[2][b, kk], full[2][b, kk], rtol=1e-12, atol=1e-14)

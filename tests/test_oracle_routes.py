@@ -115,3 +115,17 @@ def test_block_lists_brute_force_and_transpose(bq, bk):
             assert rc[b, j] == len(want) and ri[b, j, :len(want)].tolist() == want
         # reverse lists are the transpose of forward lists
         assert sum(fc[b]) == sum(rc[b]) == len(pairs)
+
+
+@pytest.mark.parametrize("bq,bk,reverse", [(1, 16, True), (4, 8, False), (3, 5, True), (16, 64, False)])
+def test_block_lists_row_subset_matches_full(bq, bk, reverse):
+    rng = np.random.default_rng(91)
+    ids = synth.random_routes(rng, 2, 70, 23, causal=True, frac_invalid=0.3)
+    routes, lens, _ = oracle.compact_routes(ids, 70)
+    full_c, full_i = oracle.block_lists(routes, lens, 70, bq, bk, reverse)
+    n_rows = full_c.shape[1]
+    want = [(b, r) for b in range(2) for r in range(n_rows) if (b + r) % 3 != 1]
+    part_c, part_i = oracle.block_lists(routes, lens, 70, bq, bk, reverse, rows=want)
+    for b, r in want:
+        assert part_c[b, r] == full_c[b, r]
+        np.testing.assert_array_equal(part_i[b, r], full_i[b, r])
