@@ -1,21 +1,29 @@
 """Benchmark: learned-indexer routed sparse attention on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input already
-resident in HBM: key compression -> block scoring + top-k selection -> route
-expansion -> sparse GQA attention forward (the S=8192 workload is forward
-only).  Prints one JSON line.
+resident in HBM, every stage a call of the C ABI on one stream:
 
-    python bench.py [--steps K] [--warmup W] [--workload s8192] [--no-cpu-baseline]
+* routed workloads: key compression -> block scoring + top-k selection
+  (fused, bounded score chunks) -> route expansion -> sparse GQA attention
+  forward, and, where the workload trains (packed 32768, 131072), reverse
+  block lists -> attention backward;
+* latent workload: index compaction -> attention forward -> reverse lists
+  -> backward.
 
-``value`` is the forward attention throughput in TFLOP/s counted on
-selected (query, key) pairs only: 2*(Dqk+Dv)*Hq per pair, pairs = sum of the
-produced route lengths, divided by the forward kernel's time inside the
-timed steps.  ``routed_queries_per_s`` is valid queries / route-pipeline
-time.  Both are measured with HIP events on the stream every kernel runs on.
+Prints one JSON line.  ``value`` is the forward attention throughput in
+TFLOP/s counted on selected (query, key) pairs only: 2*(Dqk+Dv)*Hq per pair,
+pairs = sum of the produced route lengths, divided by the forward call's
+time.  ``routed_queries_per_s`` is valid queries / route-pipeline time.
+``stages`` gives every call's mean time and its roofline fraction.  All
+times come from HIP events recorded on the stream the kernels run on.
+
+    python bench.py [--steps K] [--warmup W] [--workload s8192|varlen|long|latent|tiny]
+                    [--no-cpu-baseline] [--copy-probe-mib N]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -26,7 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+FP32_VALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector (published)
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_s8192_hbm_traffic.json")
+FWD_SOURCE = os.path.join(ROOT, "indexer_routed_block_amd", "csrc", "attn_fwd.hip")
 
 
 def parse():
@@ -36,8 +47,44 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="s8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=256)
+    ap.add_argument("--cpu-sample-rows", type=int, default=3072)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before warm-up, copy a buffer of this many MiB once (HBM counter calibration)")
     return ap.parse_args()
+
+
+def _layout_counts(wl, S, cu):
+    """Host metadata: per-token visible complete blocks nb(t) and validity (doc-local positions)."""
+    import numpy as np
+    pos = np.zeros(S, dtype=np.int64)
+    valid = np.zeros(S, dtype=bool)
+    if cu is None:
+        pos[:] = np.arange(S)
+        valid[:] = True
+    else:
+        for d in range(len(cu) - 1):
+            a, e = int(cu[d]), int(cu[d + 1])
+            pos[a:e] = np.arange(e - a)
+            valid[a:e] = True
+    nb = np.where(valid, (pos + 1) // max(wl.c, 1), 0)
+    return nb, valid
+
+
+def _fwd_source_hash():
+    with open(FWD_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic():
+    """HBM bytes per forward call from the committed PMC summary, or None if the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attn_fwd_source_sha256_16") != _fwd_source_hash():
+        return None
+    return t
 
 
 def main():
@@ -54,89 +101,192 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
-    if wl.latent:
-        raise SystemExit("the benchmark step runs the route pipeline; pick a routed workload")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    lib = irb.load_library()
+    sptr = irb._stream(dev)
+    stream = torch.cuda.current_stream(dev)
+    P = irb._ptr
+    C = irb._check
+
     t0 = time.time()
-    x = synth.make_inputs(wl, parts=("route", "attn"))
+    parts = ("attn", "bwd", "idx") if wl.latent else (("route", "attn", "bwd") if wl.backward else ("route", "attn"))
+    x = synth.make_inputs(wl, parts=parts)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    d = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(dev, dt if k in ("kI", "qI", "q", "k", "v") else None)
-         for k in ("kI", "qI", "w", "gamma", "freqs", "q", "k", "v")}
+    act = ("kI", "qI", "q", "k", "v", "kv", "dO")
+    d = {k: (torch.from_numpy(np.ascontiguousarray(v)).to(dev).to(dt if k in act else torch.from_numpy(v).dtype))
+         for k, v in x.items() if isinstance(v, np.ndarray) and k != "cu_seqlens"}
     cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).to(dev)
     gen_s = time.time() - t0
     S, B = wl.S, wl.B
-    c, topk, window = wl.c, wl.topk, wl.window
-    scale = 1.0 / math.sqrt(wl.D)
+    stages = {}          # name -> list of (start, end) events per timed step
 
-    # persistent buffers: the step allocates nothing
-    L = irb.route_width(topk, c, window)
-    nb = S // c
-    ws_rows = S
-    fused_ws = torch.empty(B * ws_rows * nb * 4, dtype=torch.uint8, device=dev)
-    sel = torch.empty((B, S, topk), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, S), dtype=torch.int32, device=dev)
-    dummy = torch.empty((B, 1, 1), dtype=torch.float32, device=dev)
-    routes = torch.empty((B, S, L), dtype=torch.int32, device=dev)
-    lens = torch.empty((B, S), dtype=torch.int32, device=dev)
-    out = torch.empty((B, S, wl.Hq, wl.Dv), dtype=dt, device=dev)
-    lse = torch.empty((B, wl.Hq, S), dtype=torch.float32, device=dev)
-    kc = torch.empty((B, nb, wl.D_idx), dtype=torch.float32, device=dev)
-    cu_blocks = None if cu is None else torch.empty(cu.numel(), dtype=torch.int32, device=dev)
-    lib = irb.load_library()
-    stream = torch.cuda.current_stream(dev)
-    sptr = irb._stream(dev)
-    lay = irb.make_layout(B, S, cu, None)
-    q0 = 0 if cu is not None else min(irb.first_sparse_query(c, topk), S - 1)
-    strides = irb._strides9(d["q"], d["k"], d["v"])
-    P = irb._ptr
+    # ---------------------------------------------------------------- buffers (the step allocates nothing)
+    if wl.latent:
+        Hkv, Dqk, Dv = 1, wl.D, wl.Dv
+        W = wl.latent_width
+        L = W
+        scale = wl.softmax_scale
+        idx = d["idx"].reshape(S, W)
+        routes = torch.empty((1, S, W), dtype=torch.int32, device=dev)
+        lens = torch.empty((1, S), dtype=torch.int32, device=dev)
+        bad = torch.zeros(1, dtype=torch.int32, device=dev)
+        q = d["q"][None]
+        k = d["kv"][None]
+        v = k[..., :Dv]
+        dO = d["dO"][None]
+    else:
+        Hkv, Dqk, Dv = wl.Hkv, wl.D, wl.Dv
+        scale = 1.0 / math.sqrt(wl.D)
+        c, topk, window = wl.c, wl.topk, wl.window
+        L = irb.route_width(topk, c, window)
+        nb_blocks = S // c
+        q0 = 0 if cu is not None else min(irb.first_sparse_query(c, topk), S - 1)
+        fused_ws = torch.empty(max(int(lib.irb_route_topk_fused_workspace_size(B, S, c, topk, q0, S)), 4),
+                               dtype=torch.uint8, device=dev)
+        sel = torch.empty((B, S, topk), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, S), dtype=torch.int32, device=dev)
+        dummy = torch.empty((B, 1, 1), dtype=torch.float32, device=dev)
+        routes = torch.empty((B, S, L), dtype=torch.int32, device=dev)
+        lens = torch.empty((B, S), dtype=torch.int32, device=dev)
+        kc = torch.empty((B, nb_blocks, wl.D_idx), dtype=torch.float32, device=dev)
+        cu_blocks = None if cu is None else torch.empty(cu.numel(), dtype=torch.int32, device=dev)
+        lay = irb.make_layout(B, S, cu, None)
+        q, k, v = d["q"], d["k"], d["v"]
+        dO = d.get("dO")
+    Hq = wl.Hq
+    out = torch.empty((B, S, Hq, Dv), dtype=dt, device=dev)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    strides = irb._strides9(q, k, v)
+    backward = wl.backward
+    if backward:
+        rbq, rbk = 1, 16
+        nkt, nqt = -(-S // rbk), -(-S // rbq)
+        rev_counts = torch.empty((B, nkt), dtype=torch.int32, device=dev)
+        rev_idx = torch.empty((B, nkt, nqt), dtype=torch.int32, device=dev)
+        lists_ws = torch.empty(max(int(lib.irb_build_block_lists_workspace_size(B, S, S, rbq, rbk)), 4),
+                               dtype=torch.uint8, device=dev)
+        dq = torch.empty((B, S, Hq, Dqk), dtype=dt, device=dev)
+        dk = torch.empty((B, S, Hkv, Dqk), dtype=dt, device=dev)
+        dv = dk if wl.latent else torch.empty((B, S, Hkv, Dv), dtype=dt, device=dev)
+        bwd_ws = torch.empty(max(int(lib.irb_sparse_gqa_attention_bwd_workspace_size(B, S, Hq, Hkv, Dqk, Dv)), 4),
+                             dtype=torch.uint8, device=dev)
 
-    def route_step():
-        irb._check(lib.irb_compress_keys(irb.ctypes.byref(lay), c, P(d["kI"]), irb._dtype_code(d["kI"]),
-                                         d["kI"].stride(0), d["kI"].stride(1), wl.D_idx, P(d["gamma"]), 1e-5,
-                                         P(d["freqs"]), d["freqs"].shape[-1], P(kc), P(cu_blocks), sptr))
+    def timed(name, fn, record):
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            stages.setdefault(name, []).append((e0, e1))
+        else:
+            fn()
+
+    # ---------------------------------------------------------------- the step
+    def route_step(rec):
+        if wl.latent:
+            timed("compact", lambda: C(lib.irb_compact_routes(P(idx), S, W, S, P(routes), P(lens), P(bad), sptr)), rec)
+            return
+        timed("compress", lambda: C(lib.irb_compress_keys(
+            irb.ctypes.byref(lay), c, P(d["kI"]), irb._dtype_code(d["kI"]), d["kI"].stride(0), d["kI"].stride(1),
+            wl.D_idx, P(d["gamma"]), 1e-5, P(d["freqs"]), d["freqs"].shape[-1], P(kc), P(cu_blocks), sptr)), rec)
         if q0 > 0:
-            irb._check(lib.irb_select_topk_regions(irb.ctypes.byref(lay), P(dummy), 1, 0, q0, P(cu_blocks), c, topk,
-                                                   P(sel), P(cnt), sptr))
-        irb._check(lib.irb_route_topk_fused(irb.ctypes.byref(lay), P(d["qI"]), irb._dtype_code(d["qI"]), wl.H_idx,
-                                            wl.D_idx, P(d["w"]), P(kc), P(cu_blocks), c, 1.0 / math.sqrt(wl.D_idx),
-                                            topk, q0, S, P(sel), P(cnt), P(fused_ws), fused_ws.numel(), sptr))
-        irb._check(lib.irb_expand_and_compact_routes(irb.ctypes.byref(lay), P(sel), P(cnt), topk, c, window,
-                                                     P(cu_blocks), L, P(routes), P(lens), sptr))
+            timed("select_dense_rows", lambda: C(lib.irb_select_topk_regions(
+                irb.ctypes.byref(lay), P(dummy), 1, 0, q0, P(cu_blocks), c, topk, P(sel), P(cnt), sptr)), rec)
+        timed("score_select", lambda: C(lib.irb_route_topk_fused(
+            irb.ctypes.byref(lay), P(d["qI"]), irb._dtype_code(d["qI"]), wl.H_idx, wl.D_idx, P(d["w"]), P(kc),
+            P(cu_blocks), c, 1.0 / math.sqrt(wl.D_idx), topk, q0, S, P(sel), P(cnt), P(fused_ws),
+            fused_ws.numel(), sptr)), rec)
+        timed("expand", lambda: C(lib.irb_expand_and_compact_routes(
+            irb.ctypes.byref(lay), P(sel), P(cnt), topk, c, window, P(cu_blocks), L, P(routes), P(lens), sptr)), rec)
 
-    def attn_step():
-        irb._check(lib.irb_sparse_gqa_attention_fwd(P(d["q"]), P(d["k"]), P(d["v"]), irb._dtype_code(d["q"]), strides,
-                                                    P(routes), P(lens), B, S, S, L, wl.Hq, wl.Hkv, wl.D, wl.Dv, scale,
-                                                    P(out), P(lse), sptr))
+    def attn_step(rec):
+        timed("attn_fwd", lambda: C(lib.irb_sparse_gqa_attention_fwd(
+            P(q), P(k), P(v), irb._dtype_code(q), strides, P(routes), P(lens), B, S, S, L, Hq, Hkv, Dqk, Dv,
+            scale, P(out), P(lse), sptr)), rec)
+        if backward:
+            timed("reverse_lists", lambda: C(lib.irb_build_block_lists(
+                P(routes), P(lens), B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(lists_ws),
+                lists_ws.numel(), sptr)), rec)
+            timed("attn_bwd", lambda: C(lib.irb_sparse_gqa_attention_bwd(
+                P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens),
+                P(rev_counts), P(rev_idx), rbq, rbk, nqt, B, S, S, L, Hq, Hkv, Dqk, Dv, scale, P(dq), P(dk), P(dv),
+                P(bwd_ws), bwd_ws.numel(), sptr)), rec)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
-        route_step()
-        attn_step()
+        route_step(False)
+        attn_step(False)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    step_ev = []
     t_start = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        route_step()
-        ev[i][1].record(stream)
-        attn_step()
-        ev[i][2].record(stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        route_step(True)
+        attn_step(True)
+        e1.record(stream)
+        step_ev.append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    route_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
-    attn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
-    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in evs])) for name, evs in stages.items()}
+    step_ms = float(np.mean([a.elapsed_time(b) for a, b in step_ev]))
 
+    # ---------------------------------------------------------------- algorithmic work per call
     lens_h = lens.cpu().numpy().astype(np.int64)
     pairs = int(lens_h.sum())
     valid_q = int((lens_h > 0).sum())
-    fwd_flop = 2.0 * (wl.D + wl.Dv) * wl.Hq * pairs
-    attn_avg_s = float(np.mean(attn_ms)) / 1e3
-    route_avg_s = float(np.mean(route_ms)) / 1e3
-    tflops = fwd_flop / attn_avg_s / 1e12
-    qps = valid_q / route_avg_s
+    fwd_flop = 2.0 * (Dqk + Dv) * Hq * pairs
+    gathered = 2.0 * (Dqk + Dv) * Hkv * pairs if not wl.latent else 2.0 * Dqk * pairs
+    work = {"attn_fwd": ("mfma", fwd_flop)}
+    if backward:
+        work["attn_bwd"] = ("mfma", 2.0 * (3 * Dqk + 2 * Dv) * Hq * pairs)
+        # routes read + counts and listed entries written (the -1 padding of the fixed width is not counted)
+        work["reverse_lists"] = ("hbm", 4.0 * L * B * S + 4.0 * rev_counts.numel()
+                                 + 4.0 * float(rev_counts.sum().item()))
+    if wl.latent:
+        work["compact"] = ("hbm", (8.0 * W + 4.0) * S)
+        route_ms = ms["compact"]
+    else:
+        nb_t, valid_t = _layout_counts(wl, S, x["cu_seqlens"])
+        sparse_pairs = float(np.sum(np.where(nb_t > topk, nb_t, 0)))
+        work["compress"] = ("hbm", B * S * wl.D_idx * (2 if dt == torch.bfloat16 else 4)
+                            + B * nb_blocks * (4 * wl.D_idx + 4 * d["freqs"].shape[-1]))
+        work["score_select"] = ("mfma", 2.0 * wl.H_idx * wl.D_idx * sparse_pairs)
+        work["expand"] = ("hbm", float(np.sum(valid_t)) * (4 * topk + 4 * L + 4))
+        if q0 > 0:
+            work["select_dense_rows"] = ("hbm", 4.0 * topk * q0 * B)
+        route_ms = sum(ms[n] for n in ("compress", "select_dense_rows", "score_select", "expand") if n in ms)
+    stage_out = {}
+    for name, t in ms.items():
+        bound, amount = work[name]
+        if bound == "mfma":
+            ach = amount / (t / 1e3) / 1e12
+            stage_out[name] = {"ms": round(t, 4), "bound": "mfma", "achieved": round(ach, 3), "unit": "TFLOP/s",
+                               "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 5),
+                               "work": amount}
+        else:
+            ach = amount / (t / 1e3) / 1e9
+            stage_out[name] = {"ms": round(t, 4), "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
+                               "peak": HBM_PEAK_GBS, "frac": round(ach / HBM_PEAK_GBS, 5), "work": amount}
+    fwd_s = ms["attn_fwd"] / 1e3
+    tflops = fwd_flop / fwd_s / 1e12
+    qps = valid_q / (route_ms / 1e3)
+
+    traffic = None
+    tr = _traffic() if wl.name == "s8192" else None
+    if tr is not None:
+        traffic = tr["hbm_bytes_per_call"]
 
     result = {
         "metric": "sparse-attn fwd TFLOP/s (selected pairs) + routed queries/s, S=8192",
@@ -146,9 +296,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(float(np.mean(step_ms)), 4),
-        "ms_route": round(float(np.mean(route_ms)), 4),
-        "ms_attn_fwd": round(float(np.mean(attn_ms)), 4),
+        "ms_per_step": round(step_ms, 4),
+        "ms_route": round(route_ms, 4),
+        "ms_attn_fwd": round(ms["attn_fwd"], 4),
         "wall_s_timed": round(wall, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -156,25 +306,28 @@ def main():
         "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {
-            "workload": wl.name, "B": B, "S": S, "H_idx": wl.H_idx, "D_idx": wl.D_idx, "c": c, "topk": topk,
-            "window": window, "route_width": L, "Hq": wl.Hq, "Hkv": wl.Hkv, "Dqk": wl.D, "Dv": wl.Dv,
-            "selected_pairs": pairs, "valid_queries": valid_q,
+            "workload": wl.name, "description": wl.description, "B": B, "S": S, "Hq": Hq, "Hkv": Hkv,
+            "Dqk": Dqk, "Dv": Dv, "route_width": L, "selected_pairs": pairs, "valid_queries": valid_q,
+            "backward_in_step": backward,
+            **({} if wl.latent else {"H_idx": wl.H_idx, "D_idx": wl.D_idx, "c": wl.c, "topk": wl.topk,
+                                     "window": wl.window}),
         },
         "roofline": {
-            "kernel": "attn_fwd_kernel (gather, G<=16)",
+            "kernel": "sparse_gqa_attention_fwd (attn_fwd_tile_kernel + attn_fwd_kernel)",
             "bound": "mfma",
             "achieved": round(tflops, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 5),
-            "traffic": None,
+            "traffic": traffic,
             "algorithmic_flop_per_launch": fwd_flop,
-            "avg_launch_ms": round(attn_avg_s * 1e3, 5),
-            "gathered_GBps": round(2.0 * (wl.D + wl.Dv) * wl.Hkv * pairs / attn_avg_s / 1e9, 1),
+            "avg_launch_ms": round(ms["attn_fwd"], 5),
+            "gathered_GBps": round(gathered / fwd_s / 1e9, 1),
         },
+        "stages": stage_out,
         "input_gen_s": round(gen_s, 2),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.name == "s8192":
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_sample_rows)
     print(json.dumps(result), flush=True)
 
