@@ -169,8 +169,8 @@ def main():
         dq = torch.empty((B, S, Hq, Dqk), dtype=dt, device=dev)
         dk = torch.empty((B, S, Hkv, Dqk), dtype=dt, device=dev)
         dv = dk if wl.latent else torch.empty((B, S, Hkv, Dv), dtype=dt, device=dev)
-        bwd_ws = torch.empty(max(int(lib.irb_sparse_gqa_attention_bwd_workspace_size(B, S, Hq, Hkv, Dqk, Dv)), 4),
-                             dtype=torch.uint8, device=dev)
+        bwd_ws = torch.empty(max(int(lib.irb_sparse_gqa_attention_bwd_workspace_size(
+            B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q))), 4), dtype=torch.uint8, device=dev)
 
     def timed(name, fn, record):
         if record:

@@ -264,10 +264,16 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
  *   dk OUT [B, S_k, Hkv, Dqk] dtype contiguous, dv OUT [B, S_k, Hkv, Dv]
  *     dtype contiguous.  dk == dv (latent: v aliases k) writes the merged
  *     gradient dK + [dV, 0] into dk.
- *   workspace: irb_sparse_gqa_attention_bwd_workspace_size() bytes of device scratch
- * Requirements as for the forward, plus rev_block_k in {16, 32, 64}.
+ *   workspace: irb_sparse_gqa_attention_bwd_workspace_size() bytes of device
+ *     scratch (same B, S_q, S_k, L, heads, dims and dtype as the call).  For
+ *     bf16 with Dqk = Dv in {64, 128} it holds, per 16-key tile, the listed
+ *     queries whose routes reach the tile with their 16-bit key masks (at
+ *     most B * S_q * min(L, ceil(S_k / 16)) entries; lists that repeat a
+ *     query tile can overflow it, and entries past it are dropped).
+ * Requirements as for the forward, plus rev_block_k = 16.
  */
-size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int Hq, int Hkv, int Dqk, int Dv);
+size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk,
+                                                   int Dv, int dtype);
 int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, int dtype,
                                  const int64_t* strides, const void* out, const void* dout,
                                  const float* lse, const int32_t* routes, const int32_t* lens,

@@ -50,7 +50,7 @@ _SIGS = {
     "irb_build_block_lists_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
     "irb_build_block_lists": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _SZ, _P], _I),
     "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
-    "irb_sparse_gqa_attention_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _SZ),
+    "irb_sparse_gqa_attention_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_sparse_gqa_attention_bwd": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                       _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
 }
@@ -295,7 +295,8 @@ def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, 
     dk = torch.empty((B, S_k, Hkv, Dqk), dtype=q.dtype, device=dev)
     dv = dk if merged_kv else torch.empty((B, S_k, Hkv, Dv), dtype=q.dtype, device=dev)
     if workspace is None:
-        n = lib.irb_sparse_gqa_attention_bwd_workspace_size(B, S_q, Hq, Hkv, Dqk, Dv)
+        n = lib.irb_sparse_gqa_attention_bwd_workspace_size(B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv,
+                                                            _dtype_code(q))
         workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
     _check(lib.irb_sparse_gqa_attention_bwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v), _ptr(out), _ptr(dout), _ptr(lse),

@@ -275,9 +275,11 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
   return launched(fn, irb::launch_attn_fwd(a, out, lse, static_cast<hipStream_t>(stream)));
 }
 
-size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int Hq, int Hkv, int Dqk, int Dv) {
-  if (B < 1 || S_q < 1 || Hq < 1 || Hkv < 1) return 0;
-  return irb::attn_bwd_workspace_bytes(B, S_q, Hq, Hkv, Dqk, Dv);
+size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
+                                                    int dtype) {
+  if (B < 1 || S_q < 1 || S_k < 1 || L < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return 0;
+  if (dtype != IRB_F32 && dtype != IRB_BF16) return 0;
+  return irb::attn_bwd_workspace_bytes(B, S_q, S_k, L, Hq, Hkv, Dqk, Dv, dtype);
 }
 
 int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
@@ -295,7 +297,8 @@ int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, in
   if (rev_block_q < 1) return fail(IRB_ERR_INVALID, "%s: rev_block_q must be >= 1", fn);
   if (rev_width < (S_q + rev_block_q - 1) / rev_block_q) return fail(IRB_ERR_INVALID, "%s: rev_width below the query tile count", fn);
   if (dk == dv && Dv > Dqk) return fail(IRB_ERR_INVALID, "%s: merged dk/dv needs Dv <= Dqk", fn);
-  if (ws_bytes < irb::attn_bwd_workspace_bytes(B, S_q, Hq, Hkv, Dqk, Dv)) return fail(IRB_ERR_INVALID, "%s: workspace too small", fn);
+  if (ws_bytes < irb::attn_bwd_workspace_bytes(B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv, dtype))
+    return fail(IRB_ERR_INVALID, "%s: workspace too small", fn);
   if (!workspace) return fail(IRB_ERR_INVALID, "%s: NULL workspace", fn);
   a.out = out; a.dout = dout; a.lse = lse;
   a.rev_counts = rev_counts; a.rev_indices = rev_indices;

@@ -7,24 +7,36 @@
 // _BackwardBlockPartition).  Latent shared KV (common.cudnn_sparse_attention):
 // the merged gradient dK + [dV, 0] lands in one buffer.
 //
-// Four launches, no atomics (deterministic):
-//  prep  copies of q and dO with the heads of a KV group innermost
-//        ([b, t, kvh, dim, Gp]) so that the key-side MFMAs can read
-//        (rows x dims)^T operands with 8/16-byte loads.
+// No atomics (deterministic).  Launches:
 //  delta Delta[b,h,t] = rowsum(dO * o) from the forward kernel run again with
 //        o kept in FP32 (the stored bf16 output would put its rounding into
 //        every dS of the row, and dK sums those coherently).
 //  dq    per (query, KV head): like the forward, S^T = K Q^T and
 //        dP^T = V dO^T on gathered rows, dS^T = P^T (dP^T - Delta),
 //        dQ^T += K^T dS^T with K^T read transposed from LDS.
-//  dkdv  per (16-key tile, KV head), one wavefront: walks the reverse list,
-//        finds each listed query's keys inside the tile by binary search in
-//        its ascending route, packs hitting queries 32 (query, head) rows at
-//        a time and accumulates dV^T += dO^T P and dK^T += q^T dS in
-//        registers.  The P and dS accumulators are already laid out as the B
-//        operand of those products, so nothing moves between lanes; they
-//        enter as bf16 high + low halves so the long key-side sums keep FP32
-//        accuracy.
+//  dK/dV, bf16 with D = Dv in {64, 128} (the GQA configurations):
+//   hits  per 16-key tile, the reverse list's queries whose routes hold one of
+//         its keys, ascending, each with its 16-bit key mask (a counting pass,
+//         a prefix sum, a filling pass), so the MFMA kernel never searches.
+//   dkdv  per (16-key tile, KV head), one wavefront: K and V of the tile stay
+//         in registers as B operands; 32 (query, head) rows at a time are
+//         loaded straight into the A layout for S = Q K^T and dP = dO V^T and
+//         copied row-major to a per-wave LDS slab; dV^T += dO^T P and
+//         dK^T += Q^T dS then take their A operands from the slab with LDS
+//         transpose reads, and P, dS straight from the accumulators as B
+//         operands (bf16 high + low halves, so the long key-side sums keep
+//         FP32 accuracy).
+//  dK/dV otherwise (fp32 inputs, latent 576/512):
+//   prep  copies of q and dO with the heads of a KV group innermost
+//         ([b, t, kvh, dim, Gp]) so that the key-side MFMAs can read
+//         (rows x dims)^T operands with 8/16-byte loads.
+//   dkdv  per (16-key tile, KV head), one wavefront: walks the reverse list,
+//         finds each listed query's keys inside the tile by binary search in
+//         its ascending route, packs hitting queries 32 (query, head) rows at
+//         a time and accumulates dV^T += dO^T P and dK^T += q^T dS in
+//         registers.
+#include <algorithm>
+
 #include "irb_internal.hpp"
 
 namespace irb {
@@ -128,33 +140,66 @@ static int padded_group(int G) {
   return (G + 31) / 32 * 32;
 }
 
+// bf16 GQA shapes take the hit-list path; the rest the transposed-copy path
+static bool uses_hits(int dtype, int Dqk, int Dv) {
+  return dtype == IRB_BF16 && Dqk == Dv && (Dqk == 64 || Dqk == 128);
+}
+
 struct BwdWs {
-  float* delta;   // [B, Hq, S_q]
-  void* qt;       // [B, S_q, Hkv, Dqk, Gp]
-  void* dot;      // [B, S_q, Hkv, Dv, Gp]
+  float* delta;       // [B, Hq, S_q]
+  void* qt;           // transposed path: [B, S_q, Hkv, Dqk, Gp]
+  void* dot;          //                  [B, S_q, Hkv, Dv, Gp]
+  int64_t* hit_off;   // hit path: [B * nkt + 1] counts, then exclusive offsets
+  int32_t* hit_t;     //           [cap] query of each hit
+  uint32_t* hit_m;    //           [cap] its 16-bit key mask
+  int64_t cap;        // every (key tile, query) pair with a routed key: <= B * S_q * min(L, nkt)
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-size_t attn_bwd_workspace_bytes(int B, int S_q, int Hq, int Hkv, int Dqk, int Dv) {
+static int64_t hit_capacity(int B, int S_q, int S_k, int L) {
+  const int64_t nkt = (static_cast<int64_t>(S_k) + 15) / 16;
+  return static_cast<int64_t>(B) * S_q * std::min<int64_t>(L, nkt);
+}
+
+size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype) {
   const int G = Hq / (Hkv > 0 ? Hkv : 1);
   const size_t Gp = static_cast<size_t>(padded_group(G));
   const size_t rows = static_cast<size_t>(B) * S_q;
-  const size_t esz = 4;   // sized for the widest dtype
-  return align256(rows * Hq * 4) + align256(rows * Hkv * Dqk * Gp * esz) + align256(rows * Hkv * Dv * Gp * esz);
+  size_t n = align256(rows * Hq * 4);
+  if (uses_hits(dtype, Dqk, Dv)) {
+    const size_t nkt = (static_cast<size_t>(S_k) + 15) / 16;
+    const size_t cap = static_cast<size_t>(hit_capacity(B, S_q, S_k, L));
+    n += align256((static_cast<size_t>(B) * nkt + 1) * 8) + 2 * align256(cap * 4);
+  } else {
+    const size_t esz = dtype == IRB_BF16 ? 2 : 4;
+    n += align256(rows * Hkv * Dqk * Gp * esz) + align256(rows * Hkv * Dv * Gp * esz);
+  }
+  return n;
 }
 
-static BwdWs carve(void* ws, int B, int S_q, int Hq, int Hkv, int Dqk, int Dv) {
+static BwdWs carve(void* ws, int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype) {
   const int G = Hq / Hkv;
   const size_t Gp = static_cast<size_t>(padded_group(G));
   const size_t rows = static_cast<size_t>(B) * S_q;
   char* p = static_cast<char*>(ws);
-  BwdWs w;
+  BwdWs w{};
   w.delta = reinterpret_cast<float*>(p);
   p += align256(rows * Hq * 4);
-  w.qt = p;
-  p += align256(rows * Hkv * Dqk * Gp * 4);
-  w.dot = p;
+  if (uses_hits(dtype, Dqk, Dv)) {
+    const size_t nkt = (static_cast<size_t>(S_k) + 15) / 16;
+    w.cap = hit_capacity(B, S_q, S_k, L);
+    w.hit_off = reinterpret_cast<int64_t*>(p);
+    p += align256((static_cast<size_t>(B) * nkt + 1) * 8);
+    w.hit_t = reinterpret_cast<int32_t*>(p);
+    p += align256(static_cast<size_t>(w.cap) * 4);
+    w.hit_m = reinterpret_cast<uint32_t*>(p);
+  } else {
+    const size_t esz = dtype == IRB_BF16 ? 2 : 4;
+    w.qt = p;
+    p += align256(rows * Hkv * Dqk * Gp * esz);
+    w.dot = p;
+  }
   return w;
 }
 
@@ -544,16 +589,308 @@ bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __re
   }
 }
 
+// ---------------------------------------------------------------- hit lists
+// 16-bit mask of the keys [k0, k0 + 16) in query t's ascending route
+IRB_DEV uint32_t route_tile_mask(const AttnArgs& a, int b, int t, int k0) {
+  const int64_t qrow = static_cast<int64_t>(b) * a.S_q + t;
+  const int n = max(0, min(a.lens[qrow], a.L));
+  const int32_t* r = a.routes + qrow * a.L;
+  int lo = 0, hi = n;                 // first entry >= k0
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (r[mid] < k0) lo = mid + 1; else hi = mid;
+  }
+  uint32_t m = 0u;
+  for (int e = lo; e < n; ++e) {
+    const int id = r[e];
+    if (id >= k0 + 16) break;
+    m |= 1u << (id - k0);
+  }
+  return m;
+}
+
+// One workgroup per (b, key tile).  pass 0 counts the reverse-list queries
+// whose route holds a key of the tile; pass 1 writes them, ascending, with
+// their key masks from hit_off[tile] on (never past cap).
+__global__ void __launch_bounds__(256)
+bwd_hits_kernel(AttnBwdArgs args, int nkt, int pass, int64_t* __restrict__ hit_off, int32_t* __restrict__ hit_t,
+                uint32_t* __restrict__ hit_m, int64_t cap) {
+  __shared__ int wsum[4];
+  const AttnArgs& a = args.f;
+  const int64_t lrow = blockIdx.x;
+  const int b = static_cast<int>(lrow / nkt), j = static_cast<int>(lrow % nkt);
+  const int k0 = 16 * j;
+  const int cnt = min(max(args.rev_counts[lrow], 0), args.rev_width);
+  const int32_t* qtiles = args.rev_indices + lrow * args.rev_width;
+  const int bq = args.rev_bq;
+  const int64_t ncand = static_cast<int64_t>(cnt) * bq;
+  const int64_t base = pass ? hit_off[lrow] : 0;
+  const int64_t end = pass ? min(hit_off[lrow + 1], cap) : 0;
+  int64_t done = 0;
+  for (int64_t c0 = 0; c0 < ncand; c0 += 256) {
+    const int64_t c = c0 + threadIdx.x;
+    int t = -1;
+    uint32_t m = 0u;
+    if (c < ncand) {
+      const int qt = qtiles[c / bq];
+      const int64_t tt = static_cast<int64_t>(qt) * bq + c % bq;
+      if (qt >= 0 && tt < a.S_q) {
+        t = static_cast<int>(tt);
+        m = route_tile_mask(a, b, t, k0);
+      }
+    }
+    int tot;
+    const int incl = block_scan256(m != 0u ? 1 : 0, wsum, &tot);
+    if (pass && m != 0u) {
+      const int64_t pos = base + done + incl - 1;
+      if (pos < end) {
+        hit_t[pos] = t;
+        hit_m[pos] = m;
+      }
+    }
+    done += tot;
+  }
+  if (!pass && threadIdx.x == 0) hit_off[lrow] = done;
+}
+
+// in-place exclusive prefix sum of v[0, n); v[n] receives the total
+__global__ void __launch_bounds__(256)
+bwd_scan_kernel(int64_t* __restrict__ v, int64_t n) {
+  __shared__ int64_t part[256];
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 255) / 256;
+  const int64_t lo = min(n, static_cast<int64_t>(tid) * per), hi = min(n, lo + per);
+  int64_t s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += v[i];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int64_t x = part[i];
+      part[i] = run;
+      run += x;
+    }
+    v[n] = run;
+  }
+  __syncthreads();
+  int64_t run = part[tid];
+  for (int64_t i = lo; i < hi; ++i) {
+    const int64_t x = v[i];
+    v[i] = run;
+    run += x;
+  }
+}
+
+// ---------------------------------------------------------------- dk / dv over hit lists
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16): inside each 16-lane row of
+// the wavefront, lane 4a + b receives element b of the 8-byte words that
+// lanes a, 4 + a, 8 + a and 12 + a address, in that order.  So if lane s of
+// a row addresses row (r0 + s / 4), columns c0 + 4 (s % 4) .. + 3 of a
+// row-major bf16 matrix, lane s receives column c0 + s of rows r0 .. r0 + 3:
+// four consecutive k of an MFMA A operand whose m is the column.
+IRB_DEV v4s lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+}
+
+template <int D, int DV>
+__global__ void __launch_bounds__(256, 2)
+bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
+                     const int32_t* __restrict__ hit_t, const uint32_t* __restrict__ hit_m, int64_t cap, int G,
+                     int Gp, int nkt, int n_items, int merged) {
+  constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
+  // row pitches of the slabs: 8 dwords apart modulo 64 banks, so the 8-byte
+  // words of 8 consecutive rows land in distinct banks
+  constexpr int LQ = D + 16, LO = DV + 16;
+  __shared__ __align__(16) uint16_t s_q[4][32 * LQ];
+  __shared__ __align__(16) uint16_t s_o[4][32 * LO];
+  const AttnArgs& a = args.f;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int item = blockIdx.x * 4 + wid;
+  if (item >= n_items) return;
+  const int kvh = item % a.Hkv;
+  const int jt = (item / a.Hkv) % nkt;
+  const int b = item / (a.Hkv * nkt);
+  const int k0 = 16 * jt;
+  const int kid = k0 + l16;
+  const bool kok = kid < a.S_k;
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* og = static_cast<const uint16_t*>(args.dout);
+
+  // the tile's keys and values as B operands: key l16, dims 8 g16 + 32 s
+  bf16x8 kb[KS], vb[VS];
+  {
+    const uint16_t* kr = static_cast<const uint16_t*>(a.k) + b * a.sk_b + static_cast<int64_t>(kok ? kid : 0) * a.sk_t +
+                         kvh * a.sk_h + 8 * g16;
+    const uint16_t* vr = static_cast<const uint16_t*>(a.v) + b * a.sv_b + static_cast<int64_t>(kok ? kid : 0) * a.sv_t +
+                         kvh * a.sv_h + 8 * g16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kb[s] = *reinterpret_cast<const bf16x8*>(kr + 32 * s);
+      if (!kok) bzero8(kb[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < VS; ++s) {
+      vb[s] = *reinterpret_cast<const bf16x8*>(vr + 32 * s);
+      if (!kok) bzero8(vb[s]);
+    }
+  }
+  f32x4 adk[NDK], adv[NDV];
+#pragma unroll
+  for (int i = 0; i < NDK; ++i) adk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NDV; ++i) adv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sc2 = a.scale * kLog2eB;
+  const int qpb = Gp <= 32 ? 32 / Gp : 1;       // queries per 32-row batch
+  const int bpq = Gp <= 32 ? 1 : Gp / 32;       // batches per query
+  const int64_t lrow = static_cast<int64_t>(b) * nkt + jt;
+  const int64_t h0 = min(hit_off[lrow], cap), h1 = min(hit_off[lrow + 1], cap);
+  uint16_t* sq = s_q[wid];
+  uint16_t* so = s_o[wid];
+  // this lane's word for the transpose reads: row 4 g16 + l16 / 4, column 4 (l16 % 4)
+  const int tr_off_q = (4 * g16 + (l16 >> 2)) * LQ + 4 * (l16 & 3);
+  const int tr_off_o = (4 * g16 + (l16 >> 2)) * LO + 4 * (l16 & 3);
+
+  for (int64_t e0 = h0; e0 < h1; e0 += qpb) {
+    for (int hb = 0; hb < bpq; ++hb) {
+      // rows r = 16 rt + l16 of S and dP: Q and dO rows in the A layout
+      bf16x8 qa[2][KS], oa[2][VS];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int r = 16 * rt + l16;
+        const int slot = Gp <= 32 ? r / Gp : 0;
+        const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
+        const int64_t e = e0 + slot;
+        int t = (e < h1 && h < G) ? hit_t[e] : -1;
+        if (t >= a.S_q) t = -1;
+        const int hh = kvh * G + (h < G ? h : 0);
+        const int tt = t >= 0 ? t : 0;
+        const uint16_t* qp = qg + b * a.sq_b + static_cast<int64_t>(tt) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
+        const uint16_t* op = og + ((static_cast<int64_t>(b) * a.S_q + tt) * a.Hq + hh) * DV + 8 * g16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          qa[rt][s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+          if (t < 0) bzero8(qa[rt][s]);
+        }
+#pragma unroll
+        for (int s = 0; s < VS; ++s) {
+          oa[rt][s] = *reinterpret_cast<const bf16x8*>(op + 32 * s);
+          if (t < 0) bzero8(oa[rt][s]);
+        }
+      }
+      // row-major copies for the transposed operands
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          *reinterpret_cast<bf16x8*>(sq + (16 * rt + l16) * LQ + 8 * g16 + 32 * s) = qa[rt][s];
+#pragma unroll
+        for (int s = 0; s < VS; ++s)
+          *reinterpret_cast<bf16x8*>(so + (16 * rt + l16) * LO + 8 * g16 + 32 * s) = oa[rt][s];
+      }
+      f32x4 sacc[2], pacc[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][s], kb[s], sacc[rt], 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < VS; ++s) pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[rt][s], vb[s], pacc[rt], 0, 0, 0);
+      }
+      // P and dS at rows 16 rt + 4 g16 + i, key l16; zero off the key mask
+      float p[2][4], ds[2][4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g16 + i;
+          const int slot = Gp <= 32 ? r / Gp : 0;
+          const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
+          const int64_t e = e0 + slot;
+          float pv = 0.f, dv = 0.f;
+          const int te = (e < h1 && h < G) ? hit_t[e] : -1;
+          if (te >= 0 && te < a.S_q && ((hit_m[e] >> l16) & 1u)) {
+            const int64_t li = (static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + te;
+            pv = exp2f(sacc[rt][i] * sc2 - args.lse[li] * kLog2eB);
+            dv = pv * (pacc[rt][i] - delta[li]);
+          }
+          p[rt][i] = pv;
+          ds[rt][i] = dv;
+        }
+      bf16x8 ph, pl, sh, sl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bput_f(ph, pl, j, p[0][j], true);
+        bput_f(ph, pl, 4 + j, p[1][j], true);
+        bput_f(sh, sl, j, ds[0][j], true);
+        bput_f(sh, sl, 4 + j, ds[1][j], true);
+      }
+      wave_lds_sync();
+      // dV^T += dO^T P and dK^T += Q^T dS; k-slot j of the A operands is row
+      // 4 g16 + j (j < 4) or 16 + 4 g16 + (j - 4), matching P / dS above
+#pragma unroll
+      for (int dt = 0; dt < NDV; ++dt) {
+        const uint16_t* w = so + tr_off_o + 16 * dt;
+        const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * LO);
+        const bf16x8 xa = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        adv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ph, adv[dt], 0, 0, 0);
+        adv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pl, adv[dt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDK; ++dt) {
+        const uint16_t* w = sq + tr_off_q + 16 * dt;
+        const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * LQ);
+        const bf16x8 xa = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        adk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sh, adk[dt], 0, 0, 0);
+        adk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sl, adk[dt], 0, 0, 0);
+      }
+      wave_lds_sync();   // the slabs are rewritten by the next batch
+    }
+  }
+
+  if (!kok) return;
+  uint16_t* dkp = static_cast<uint16_t*>(args.dk) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * D + 4 * g16;
+  if (merged) {
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = adk[dt][i] * a.scale + (dt < NDV ? adv[dt < NDV ? dt : 0][i] : 0.f);
+      bstore4(dkp + dt * 16, v);
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+      const float v[4] = {adk[dt][0] * a.scale, adk[dt][1] * a.scale, adk[dt][2] * a.scale, adk[dt][3] * a.scale};
+      bstore4(dkp + dt * 16, v);
+    }
+    uint16_t* dvp = static_cast<uint16_t*>(args.dv) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * DV + 4 * g16;
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt) {
+      const float v[4] = {adv[dt][0], adv[dt][1], adv[dt][2], adv[dt][3]};
+      bstore4(dvp + dt * 16, v);
+    }
+  }
+}
+
 template <typename T, int D, int DV>
 static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
   const AttnArgs& a = args.f;
   const int G = a.Hq / a.Hkv;
   const int Gp = padded_group(G);
-  BwdWs ws = carve(args.ws, a.B, a.S_q, a.Hq, a.Hkv, a.Dqk, a.Dv);
+  constexpr bool kHits = sizeof(T) == 2 && D == DV && (D == 64 || D == 128);
+  BwdWs ws = carve(args.ws, a.B, a.S_q, a.S_k, a.L, a.Hq, a.Hkv, a.Dqk, a.Dv, a.dtype);
   const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
   const int64_t rows = static_cast<int64_t>(a.B) * a.S_q;
-  hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, a,
-                     static_cast<const T*>(args.dout), static_cast<T*>(ws.qt), static_cast<T*>(ws.dot), G, Gp);
+  if (!kHits) {
+    hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, a,
+                       static_cast<const T*>(args.dout), static_cast<T*>(ws.qt), static_cast<T*>(ws.dot), G, Gp);
+  }
   if (int rc = launch_attn_delta(a, args.dout, ws.delta, stream)) return rc;
   const int PAD = sizeof(T) == 2 ? 8 : 4;
   const int64_t items = rows * a.Hkv;
@@ -584,9 +921,21 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
   const int nkt = (a.S_k + 15) / 16;
   const int64_t kitems = static_cast<int64_t>(a.B) * nkt * a.Hkv;
   const int merged = args.dk == args.dv ? 1 : 0;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0, stream, args,
-                     ws.delta, static_cast<const T*>(ws.qt), static_cast<const T*>(ws.dot), G, Gp, nkt,
-                     static_cast<int>(kitems), merged);
+  if constexpr (kHits) {
+    const int64_t ltiles = static_cast<int64_t>(a.B) * nkt;
+    hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 0,
+                       ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(256), 0, stream, ws.hit_off, ltiles);
+    hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 1,
+                       ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
+    hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0,
+                       stream, args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt,
+                       static_cast<int>(kitems), merged);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0, stream,
+                       args, ws.delta, static_cast<const T*>(ws.qt), static_cast<const T*>(ws.dot), G, Gp, nkt,
+                       static_cast<int>(kitems), merged);
+  }
   return 0;
 }
 

@@ -84,6 +84,26 @@ IRB_DEV int wave_incl_scan(int v) {
   return v;
 }
 
+// Inclusive prefix sum over a 256-thread workgroup; *total receives the
+// workgroup's sum.  wsum is 4 ints of LDS; every thread must call it (two
+// barriers, the second one keeps wsum alive until everyone has read it).
+IRB_DEV int block_scan256(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int x = wsum[w];
+    if (w < wid) off += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return incl + off;
+}
+
 // Order LDS traffic between the lanes of ONE wavefront (no cross-wave barrier):
 // wait until this wave's LDS operations have completed and stop the compiler
 // from moving memory accesses across this point.

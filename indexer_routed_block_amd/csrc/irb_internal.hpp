@@ -51,7 +51,7 @@ struct AttnBwdArgs {
   void* ws; size_t ws_bytes;
 };
 
-size_t attn_bwd_workspace_bytes(int B, int S_q, int Hq, int Hkv, int Dqk, int Dv);
+size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype);
 int launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 
 // fill a device int32 range with a value (a kernel, so callers may capture it in graphs)

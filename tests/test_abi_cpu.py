@@ -120,11 +120,20 @@ def test_attention_validation():
     odd = (ctypes.c_int64 * 9)(*list(st)[:8], 129)
     assert _err(call(strides=odd))[0] == 3
     # backward: key tile must be 16, merged dk/dv needs Dv <= Dqk
-    bwd = lambda bk=16, width=64: lib.irb_sparse_gqa_attention_bwd(
+    bwd = lambda bk=16, width=64, ws=1 << 30: lib.irb_sparse_gqa_attention_bwd(
         FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, bk, width, 1, 64, 64, 16, 4, 1, 128, 128,
-        0.1, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+        0.1, FAKE, FAKE, FAKE, FAKE, ws, None)
     assert _err(bwd(bk=32))[0] == 3
     assert _err(bwd(width=63))[0] == 3
+    need = lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 4, 1, 128, 128, 1)
+    assert need > 0
+    code, msg = _err(bwd(ws=need - 1))
+    assert code == 3 and "workspace" in msg
+    assert lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 6, 4, 128, 128, 1) == 0
+    # the hit lists of the bf16 GQA path grow with the route width; fp32 keeps the transposed copies
+    ws_size = lib.irb_sparse_gqa_attention_bwd_workspace_size
+    assert ws_size(1, 256, 256, 16, 4, 1, 128, 128, 1) > ws_size(1, 256, 256, 8, 4, 1, 128, 128, 1)
+    assert lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 4, 1, 128, 128, 0) != need
 
 
 def test_python_binding_has_no_cpu_path():
