@@ -140,9 +140,12 @@ static int padded_group(int G) {
   return (G + 31) / 32 * 32;
 }
 
-// bf16 GQA shapes take the hit-list path; the rest the transposed-copy path
-static bool uses_hits(int dtype, int Dqk, int Dv) {
-  return dtype == IRB_BF16 && Dqk == Dv && (Dqk == 64 || Dqk == 128);
+// bf16 GQA shapes and the bf16 latent shape with whole 32-head batches take
+// the hit-list path; the rest the transposed-copy path
+static bool uses_hits(int dtype, int Dqk, int Dv, int G) {
+  if (dtype != IRB_BF16) return false;
+  if (Dqk == Dv && (Dqk == 64 || Dqk == 128)) return true;
+  return Dqk == 576 && Dv == 512 && G % 32 == 0;
 }
 
 struct BwdWs {
@@ -167,7 +170,7 @@ size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv,
   const size_t Gp = static_cast<size_t>(padded_group(G));
   const size_t rows = static_cast<size_t>(B) * S_q;
   size_t n = align256(rows * Hq * 4);
-  if (uses_hits(dtype, Dqk, Dv)) {
+  if (uses_hits(dtype, Dqk, Dv, G)) {
     const size_t nkt = (static_cast<size_t>(S_k) + 15) / 16;
     const size_t cap = static_cast<size_t>(hit_capacity(B, S_q, S_k, L));
     n += align256((static_cast<size_t>(B) * nkt + 1) * 8) + 2 * align256(cap * 4);
@@ -186,7 +189,7 @@ static BwdWs carve(void* ws, int B, int S_q, int S_k, int L, int Hq, int Hkv, in
   BwdWs w{};
   w.delta = reinterpret_cast<float*>(p);
   p += align256(rows * Hq * 4);
-  if (uses_hits(dtype, Dqk, Dv)) {
+  if (uses_hits(dtype, Dqk, Dv, G)) {
     const size_t nkt = (static_cast<size_t>(S_k) + 15) / 16;
     w.cap = hit_capacity(B, S_q, S_k, L);
     w.hit_off = reinterpret_cast<int64_t*>(p);
@@ -878,16 +881,187 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   }
 }
 
+// ---------------------------------------------------------------- dk / dv, latent width
+// D = 576, Dv = 512, heads in whole 32-row batches.  One 256-thread workgroup
+// per (16-key tile, KV head), one listed query at a time: waves 0 and 1 load
+// the batch's 32 q rows (16 each) into the A layout, keep the tile's keys as
+// B operands and form S; waves 2 and 3 do the same with dO rows, values and
+// dP.  Both row sets also go row-major into LDS slabs, S and dP through a
+// small LDS exchange; then every wave forms P and dS for all 32 rows and owns
+// every fourth 16-dim tile of dK^T += q^T dS and dV^T += dO^T P, reading the
+// transposed A operands from the slabs.
+template <int D, int DV>
+__global__ void __launch_bounds__(256, 2)
+bwd_dkdv_wide_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
+                     const int32_t* __restrict__ hit_t, const uint32_t* __restrict__ hit_m, int64_t cap, int G,
+                     int nkt, int merged) {
+  constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
+  constexpr int MK = (NDK + 3) / 4, MV = (NDV + 3) / 4;   // dim tiles per wave
+  // slab pitches: rows 40 (q, 296 dwords) and 8 (dO, 264 dwords) banks apart, so
+  // the 8-byte words of 8 consecutive rows never share a bank
+  constexpr int LQ = D + 16, LO = DV + 16;
+  static_assert(KS >= VS, "key width below value width");
+  __shared__ __align__(16) uint16_t s_q[32 * LQ];
+  __shared__ __align__(16) uint16_t s_o[32 * LO];
+  __shared__ f32x4 s_x[4][64];          // S rows 0-15, S rows 16-31, dP rows 0-15, dP rows 16-31
+  const AttnArgs& a = args.f;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int item = blockIdx.x;
+  const int kvh = item % a.Hkv;
+  const int jt = (item / a.Hkv) % nkt;
+  const int b = item / (a.Hkv * nkt);
+  const int k0 = 16 * jt;
+  const int kid = k0 + l16;
+  const bool kok = kid < a.S_k;
+  const bool is_s = wid < 2;            // waves 0, 1: S from q and K; waves 2, 3: dP from dO and V
+  const int rt = wid & 1;               // this wave's 16 of the batch's 32 rows
+
+  bf16x8 kb[KS];
+  {
+    const uint16_t* src = is_s
+        ? static_cast<const uint16_t*>(a.k) + b * a.sk_b + static_cast<int64_t>(kok ? kid : 0) * a.sk_t + kvh * a.sk_h
+        : static_cast<const uint16_t*>(a.v) + b * a.sv_b + static_cast<int64_t>(kok ? kid : 0) * a.sv_t + kvh * a.sv_h;
+    const int ns = is_s ? KS : VS;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s < ns && kok) kb[s] = *reinterpret_cast<const bf16x8*>(src + 8 * g16 + 32 * s);
+      else bzero8(kb[s]);
+    }
+  }
+  f32x4 adk[MK], adv[MV];
+#pragma unroll
+  for (int i = 0; i < MK; ++i) adk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < MV; ++i) adv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sc2 = a.scale * kLog2eB;
+  const int bpq = G / 32;
+  const int64_t lrow = static_cast<int64_t>(b) * nkt + jt;
+  const int64_t h0 = min(hit_off[lrow], cap), h1 = min(hit_off[lrow + 1], cap);
+  const int tr_row = 4 * g16 + (l16 >> 2), tr_col = 4 * (l16 & 3);
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* og = static_cast<const uint16_t*>(args.dout);
+
+  for (int64_t e = h0; e < h1; ++e) {
+    const int t = hit_t[e];
+    const uint32_t m = hit_m[e];
+    if (t < 0 || t >= a.S_q) continue;          // uniform over the workgroup
+    const bool kin = (m >> l16) & 1u;
+    for (int hb = 0; hb < bpq; ++hb) {
+      {
+        const int hh = kvh * G + hb * 32 + 16 * rt + l16;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (is_s) {
+          const uint16_t* src = qg + b * a.sq_b + static_cast<int64_t>(t) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
+          bf16x8 xa[KS];
+#pragma unroll
+          for (int s = 0; s < KS; ++s) xa[s] = *reinterpret_cast<const bf16x8*>(src + 32 * s);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            *reinterpret_cast<bf16x8*>(s_q + (16 * rt + l16) * LQ + 8 * g16 + 32 * s) = xa[s];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[s], kb[s], acc, 0, 0, 0);
+          }
+        } else {
+          const uint16_t* src = og + ((static_cast<int64_t>(b) * a.S_q + t) * a.Hq + hh) * DV + 8 * g16;
+          bf16x8 xa[VS];
+#pragma unroll
+          for (int s = 0; s < VS; ++s) xa[s] = *reinterpret_cast<const bf16x8*>(src + 32 * s);
+#pragma unroll
+          for (int s = 0; s < VS; ++s) {
+            *reinterpret_cast<bf16x8*>(s_o + (16 * rt + l16) * LO + 8 * g16 + 32 * s) = xa[s];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[s], kb[s], acc, 0, 0, 0);
+          }
+        }
+        s_x[wid][lane] = acc;
+      }
+      __syncthreads();
+      // P and dS at rows 16 r2 + 4 g16 + i, key l16
+      float p[2][4], ds[2][4];
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const f32x4 sv = s_x[r2][lane], pv = s_x[2 + r2][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t li = (static_cast<int64_t>(b) * a.Hq + kvh * G + hb * 32 + 16 * r2 + 4 * g16 + i) * a.S_q + t;
+          const float pp = kin ? exp2f(sv[i] * sc2 - args.lse[li] * kLog2eB) : 0.f;
+          p[r2][i] = pp;
+          ds[r2][i] = kin ? pp * (pv[i] - delta[li]) : 0.f;
+        }
+      }
+      bf16x8 ph, pl, sh, sl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bput_f(ph, pl, j, p[0][j], true);
+        bput_f(ph, pl, 4 + j, p[1][j], true);
+        bput_f(sh, sl, j, ds[0][j], true);
+        bput_f(sh, sl, 4 + j, ds[1][j], true);
+      }
+#pragma unroll
+      for (int i = 0; i < MK; ++i) {
+        const int dt = wid + 4 * i;
+        if (dt < NDK) {
+          const uint16_t* w = s_q + tr_row * LQ + tr_col + 16 * dt;
+          const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * LQ);
+          const bf16x8 xa = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          adk[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sh, adk[i], 0, 0, 0);
+          adk[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sl, adk[i], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < MV; ++i) {
+        const int dt = wid + 4 * i;
+        if (dt < NDV) {
+          const uint16_t* w = s_o + tr_row * LO + tr_col + 16 * dt;
+          const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * LO);
+          const bf16x8 xa = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          adv[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ph, adv[i], 0, 0, 0);
+          adv[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pl, adv[i], 0, 0, 0);
+        }
+      }
+      __syncthreads();   // slabs and the exchange are rewritten by the next batch
+    }
+  }
+
+  if (!kok) return;
+  uint16_t* dkp = static_cast<uint16_t*>(args.dk) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * D + 4 * g16;
+#pragma unroll
+  for (int i = 0; i < MK; ++i) {
+    const int dt = wid + 4 * i;
+    if (dt >= NDK) continue;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = adk[i][r] * a.scale;
+    // wave w's i-th value tile is tile w + 4 i too, so the merged sum stays in-lane
+    if (merged && i < MV && dt < NDV) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += adv[i][r];
+    }
+    bstore4(dkp + dt * 16, v);
+  }
+  if (!merged) {
+    uint16_t* dvp = static_cast<uint16_t*>(args.dv) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * DV + 4 * g16;
+#pragma unroll
+    for (int i = 0; i < MV; ++i) {
+      const int dt = wid + 4 * i;
+      if (dt >= NDV) continue;
+      const float v[4] = {adv[i][0], adv[i][1], adv[i][2], adv[i][3]};
+      bstore4(dvp + dt * 16, v);
+    }
+  }
+}
+
 template <typename T, int D, int DV>
 static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
   const AttnArgs& a = args.f;
   const int G = a.Hq / a.Hkv;
   const int Gp = padded_group(G);
-  constexpr bool kHits = sizeof(T) == 2 && D == DV && (D == 64 || D == 128);
+  constexpr bool kGqaHits = sizeof(T) == 2 && D == DV && (D == 64 || D == 128);
+  constexpr bool kWide = sizeof(T) == 2 && D == 576 && DV == 512;
+  const bool hits = kGqaHits || (kWide && G % 32 == 0);
   BwdWs ws = carve(args.ws, a.B, a.S_q, a.S_k, a.L, a.Hq, a.Hkv, a.Dqk, a.Dv, a.dtype);
   const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
   const int64_t rows = static_cast<int64_t>(a.B) * a.S_q;
-  if (!kHits) {
+  if (!hits) {
     hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, a,
                        static_cast<const T*>(args.dout), static_cast<T*>(ws.qt), static_cast<T*>(ws.dot), G, Gp);
   }
@@ -921,16 +1095,21 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
   const int nkt = (a.S_k + 15) / 16;
   const int64_t kitems = static_cast<int64_t>(a.B) * nkt * a.Hkv;
   const int merged = args.dk == args.dv ? 1 : 0;
-  if constexpr (kHits) {
+  if (hits) {
     const int64_t ltiles = static_cast<int64_t>(a.B) * nkt;
     hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 0,
                        ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(256), 0, stream, ws.hit_off, ltiles);
     hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 1,
                        ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
-    hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0,
-                       stream, args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt,
-                       static_cast<int>(kitems), merged);
+    if constexpr (kGqaHits) {
+      hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0,
+                         stream, args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt,
+                         static_cast<int>(kitems), merged);
+    } else if constexpr (kWide) {
+      hipLaunchKernelGGL((bwd_dkdv_wide_kernel<D, DV>), dim3(static_cast<unsigned>(kitems)), dim3(256), 0, stream,
+                         args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, nkt, merged);
+    }
   } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0, stream,
                        args, ws.delta, static_cast<const T*>(ws.qt), static_cast<const T*>(ws.dot), G, Gp, nkt,
