@@ -387,8 +387,12 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   constexpr int BQ = 128 / G;
   constexpr int KS = D / 32, NDT = DV / 16;
   constexpr int LDK = D + 8;      // K tile row: one key, D dims (+pad)
-  constexpr int LDT = 32 + 4;     // V^T tile row: one dim, 32 keys (+pad): 18 dwords, so the
-                                  // dword-pair stores of a wave hit 64 distinct banks
+  // V^T tile row: one dim, 32 keys (+pad to 20 dwords: the 16-byte operand
+  // reads of 16 lanes cover the 64 banks once).  Keys sit in MFMA k-slot
+  // order: position 8 g + 4 h + i holds key 16 h + 4 g + i, so a lane's eight
+  // operand keys {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3} are one 16-byte
+  // word.
+  constexpr int LDT = 32 + 8;
   constexpr int KBYTES = 32 * LDK * 2, VBYTES = DV * LDT * 2;
   constexpr int BUF = KBYTES + VBYTES;
   __shared__ __align__(16) char raw[2 * BUF];
@@ -442,7 +446,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   // pointers are formed once; a key tile only adds a scalar offset.
   constexpr int KC = D / 8, VG = DV / 8;
   constexpr int KPER = (32 * KC + 255) / 256;
-  uint4 kreg[KPER], vreg[2];
+  struct Stage { uint4 k[KPER]; uint4 v[2]; };        // one key tile in flight
   const int vkp = tid % 16, vdg = tid / 16;           // key pair, dim group
   const bool vown = vdg < VG;
   const T* kptr[KPER];
@@ -456,34 +460,49 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   const T* vptr0 = vbase + static_cast<int64_t>(2 * vkp) * a.sv_t + 8 * (vown ? vdg : 0);
   const T* vptr1 = vptr0 + a.sv_t;
   const int64_t kstep = 32 * a.sk_t, vstep = 32 * a.sv_t;
-  auto gload = [&](int kt) {
+  // kt is uniform; tiles wholly inside S_k load without per-row checks
+  auto gload = [&](int kt, Stage& r) {
+    kt = __builtin_amdgcn_readfirstlane(kt);
     const int rows = a.S_k - kt * 32;                  // keys of this tile that exist
+    const int64_t ko = kt * kstep, vo = kt * vstep;
+    if (rows >= 32) {
 #pragma unroll
-    for (int u = 0; u < KPER; ++u) {
-      kreg[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (krow[u] < rows) kreg[u] = *reinterpret_cast<const uint4*>(kptr[u] + kt * kstep);
+      for (int u = 0; u < KPER; ++u)
+        if (KPER * 256 == 32 * KC || krow[u] < 32) r.k[u] = *reinterpret_cast<const uint4*>(kptr[u] + ko);
+      if (vown) {
+        r.v[0] = *reinterpret_cast<const uint4*>(vptr0 + vo);
+        r.v[1] = *reinterpret_cast<const uint4*>(vptr1 + vo);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < KPER; ++u) {
+        r.k[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (krow[u] < rows) r.k[u] = *reinterpret_cast<const uint4*>(kptr[u] + ko);
+      }
+      r.v[0] = make_uint4(0u, 0u, 0u, 0u);
+      r.v[1] = r.v[0];
+      if (vown && 2 * vkp < rows) r.v[0] = *reinterpret_cast<const uint4*>(vptr0 + vo);
+      if (vown && 2 * vkp + 1 < rows) r.v[1] = *reinterpret_cast<const uint4*>(vptr1 + vo);
     }
-    vreg[0] = make_uint4(0u, 0u, 0u, 0u);
-    vreg[1] = vreg[0];
-    if (vown && 2 * vkp < rows) vreg[0] = *reinterpret_cast<const uint4*>(vptr0 + kt * vstep);
-    if (vown && 2 * vkp + 1 < rows) vreg[1] = *reinterpret_cast<const uint4*>(vptr1 + kt * vstep);
   };
-  auto lstore = [&](int buf) {
+  // dword position of the key pair (2 vkp, 2 vkp + 1) in a V^T row
+  const int vpos = 4 * ((vkp & 7) >> 1) + 2 * (vkp >> 3) + (vkp & 1);
+  auto lstore = [&](int buf, const Stage& r) {
     T* kb = reinterpret_cast<T*>(raw + buf * BUF);
     uint32_t* vt32 = reinterpret_cast<uint32_t*>(raw + buf * BUF + KBYTES);
 #pragma unroll
     for (int u = 0; u < KPER; ++u) {
       const int chunk = tid + 256 * u;
-      if (chunk < 32 * KC) *reinterpret_cast<uint4*>(kb + (chunk / KC) * LDK + 8 * (chunk % KC)) = kreg[u];
+      if (chunk < 32 * KC) *reinterpret_cast<uint4*>(kb + (chunk / KC) * LDK + 8 * (chunk % KC)) = r.k[u];
     }
     if (vown) {
-      const uint32_t a0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t a1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+      const uint32_t a0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+      const uint32_t a1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // dims 8*vdg + 2e and + 2e + 1; each dword = (key 2*vkp, key 2*vkp + 1)
-        vt32[(8 * vdg + 2 * e) * (LDT / 2) + vkp] = (a0[e] & 0xffffu) | (a1[e] << 16);
-        vt32[(8 * vdg + 2 * e + 1) * (LDT / 2) + vkp] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+        vt32[(8 * vdg + 2 * e) * (LDT / 2) + vpos] = (a0[e] & 0xffffu) | (a1[e] << 16);
+        vt32[(8 * vdg + 2 * e + 1) * (LDT / 2) + vpos] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
       }
     }
   };
@@ -517,26 +536,36 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       cursor[lane] = hi;
     }
     __syncthreads();
-    for (int qi = 0; qi < BQ; ++qi) {
+    // wave w takes queries w, w + 4, ...; 8 independent loads per lane are in
+    // flight before the runs are combined, so the route reads overlap
+    constexpr int U = 8;
+    for (int qi = wid; qi < BQ; qi += 4) {
       const int lo = s_lo[qi], hi = s_hi[qi];
       const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + qi) * a.L;
-      for (int e0 = lo; e0 < hi; e0 += 256) {
-        const int e = e0 + tid;
-        const int id = (e < hi) ? r[e] : -1;
-        const bool ok = id >= key0 && id < key1 && id < a.S_k;
-        const int word = ok ? ((id - key0) >> 5) : -1 - lane;   // unique dummy keys for idle lanes
-        uint32_t bits = ok ? (1u << ((id - key0) & 31)) : 0u;
+      for (int e0 = lo; e0 < hi; e0 += 64 * U) {
+        int ids[U];
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t ob = __shfl_down(bits, o, 64);
-          const int ow = __shfl_down(word, o, 64);
-          if (lane + o < 64 && ow == word) bits |= ob;
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + 64 * u + lane;
+          ids[u] = (e < hi) ? r[e] : -1;
         }
-        const int prev = __shfl_up(word, 1, 64);
-        if (ok && (lane == 0 || prev != word)) atomicOr(&mask[qi][word], bits);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int id = ids[u];
+          const bool ok = id >= key0 && id < key1 && id < a.S_k;
+          const int word = ok ? ((id - key0) >> 5) : -1 - lane;   // unique dummy keys for idle lanes
+          uint32_t bits = ok ? (1u << ((id - key0) & 31)) : 0u;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t ob = __shfl_down(bits, o, 64);
+            const int ow = __shfl_down(word, o, 64);
+            if (lane + o < 64 && ow == word) bits |= ob;
+          }
+          const int prev = __shfl_up(word, 1, 64);
+          if (ok && (lane == 0 || prev != word)) atomicOr(&mask[qi][word], bits);
+        }
       }
     }
-    __syncthreads();
     // compact list of the key tiles any query routes to
     if (wid == 0) {
       int base = 0;
@@ -554,14 +583,15 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     __syncthreads();
     const int ntiles = s_ntiles;
     if (ntiles == 0) continue;
-    gload(seg0 + tiles[0]);
-    lstore(0);
+    // key tile it is in LDS buffer it % 2; the stage registers carry tile it + 1
+    Stage stg;
+    gload(seg0 + tiles[0], stg);
+    lstore(0, stg);
     __syncthreads();
-    int buf = 0;
     for (int it = 0; it < ntiles; ++it) {
+      const int buf = it & 1;
       const int ktl = tiles[it];
-      const bool more = it + 1 < ntiles;
-      if (more) gload(seg0 + tiles[it + 1]);
+      if (it + 1 < ntiles) gload(seg0 + tiles[it + 1], stg);
       const T* kb = reinterpret_cast<const T*>(raw + buf * BUF);
       const T* vt = reinterpret_cast<const T*>(raw + buf * BUF + KBYTES);
       f32x4 st[2][2];
@@ -622,17 +652,13 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const T* vr = vt + (dt * 16 + l16) * LDT + 4 * g16;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vt + (dt * 16 + l16) * LDT + 8 * g16);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
           oacc[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], oacc[dt][ct], 0, 0, 0);
       }
-      if (more) lstore(buf ^ 1);
+      if (it + 1 < ntiles) lstore(buf ^ 1, stg);
       __syncthreads();
-      buf ^= 1;
     }
   }
 
@@ -642,7 +668,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     const int c = 32 * wid + 16 * ct + l16;
     const int qi = c / G, h = c % G;
     const int t = qa + qi;
-    float ltot = row4_sum(lsum[ct]);
+    const float ltot = row4_sum(lsum[ct]);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (kDelta) {
       float part = 0.f;
