@@ -536,34 +536,34 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       cursor[lane] = hi;
     }
     __syncthreads();
-    // wave w takes queries w, w + 4, ...; 8 independent loads per lane are in
-    // flight before the runs are combined, so the route reads overlap
-    constexpr int U = 8;
+    // wave w takes queries w, w + 4, ...; each lane ORs 8 consecutive entries
+    // of a 512-entry chunk into a word locally (entries are sorted, so equal
+    // words are adjacent) and issues an LDS atomic OR only when the word
+    // changes; the 8 loads of a lane are in flight together
     for (int qi = wid; qi < BQ; qi += 4) {
       const int lo = s_lo[qi], hi = s_hi[qi];
       const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + qi) * a.L;
-      for (int e0 = lo; e0 < hi; e0 += 64 * U) {
-        int ids[U];
+      for (int e0 = lo; e0 < hi; e0 += 512) {
+        const int eb = e0 + 8 * lane;
+        int ids[8];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int e = e0 + 64 * u + lane;
-          ids[u] = (e < hi) ? r[e] : -1;
-        }
+        for (int j = 0; j < 8; ++j) ids[j] = (eb + j < hi) ? r[eb + j] : -1;
+        int word = -1;
+        uint32_t bits = 0u;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int id = ids[u];
-          const bool ok = id >= key0 && id < key1 && id < a.S_k;
-          const int word = ok ? ((id - key0) >> 5) : -1 - lane;   // unique dummy keys for idle lanes
-          uint32_t bits = ok ? (1u << ((id - key0) & 31)) : 0u;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t ob = __shfl_down(bits, o, 64);
-            const int ow = __shfl_down(word, o, 64);
-            if (lane + o < 64 && ow == word) bits |= ob;
+        for (int j = 0; j < 8; ++j) {
+          const int id = ids[j];
+          if (id >= key0 && id < key1 && id < a.S_k) {
+            const int w = (id - key0) >> 5;
+            if (w != word) {
+              if (word >= 0) atomicOr(&mask[qi][word], bits);
+              word = w;
+              bits = 0u;
+            }
+            bits |= 1u << ((id - key0) & 31);
           }
-          const int prev = __shfl_up(word, 1, 64);
-          if (ok && (lane == 0 || prev != word)) atomicOr(&mask[qi][word], bits);
         }
+        if (word >= 0) atomicOr(&mask[qi][word], bits);
       }
     }
     // compact list of the key tiles any query routes to
