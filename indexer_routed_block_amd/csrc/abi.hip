@@ -119,7 +119,7 @@ int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtyp
   if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
   IRB_REQUIRE_DEVICE();
   return launched(fn, irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, cu_blocks, c, score_scale, q0, q1, j0, j1,
-                                             out, out_row_stride, static_cast<hipStream_t>(stream)));
+                                             out, out_row_stride, 1, -1, static_cast<hipStream_t>(stream)));
 }
 
 int irb_select_topk_regions(const irb_layout* layout, const float* scores, int64_t score_row_stride, int q0, int q1,
@@ -171,7 +171,8 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
   float* scores = static_cast<float*>(workspace);
   for (int a = q0; a < q1; a += static_cast<int>(std::min<int64_t>(rows, q1 - a))) {
     const int e = a + static_cast<int>(std::min<int64_t>(rows, q1 - a));
-    int rc = irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, cu_blocks, c, score_scale, a, e, 0, nb, scores, nb, st);
+    int rc = irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, cu_blocks, c, score_scale, a, e, 0, nb, scores, nb,
+                                    0, topk, st);
     if (!rc) rc = irb::launch_select(L, scores, nb, a, e, cu_blocks, c, topk, sel, cnt, st);
     if (rc) return launched(fn, rc);
   }

@@ -27,6 +27,42 @@ namespace irb {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// s_waitcnt immediate that waits until at most N vector-memory loads of this
+// wave are outstanding (expcnt and lgkmcnt left unconstrained)
+template <int N>
+constexpr int kVmWaitTile() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  return N | (7 << 4) | (15 << 8);
+}
+
+// Direct 16-byte global-to-LDS load (global_load_lds_dwordx4): lane i writes
+// LDS bytes [lds_base + 16 i, + 16) of the wave-uniform lds_base.  Written as
+// inline assembly so that the compiler does not wait for these loads before
+// every LDS read; the kernel orders them itself with s_waitcnt vmcnt and a
+// barrier (only vector-memory loads are outstanding when it waits).
+IRB_DEV void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
+}
+IRB_DEV uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+// workgroup barrier that only orders: waits happen where the kernel puts them
+IRB_DEV void bare_barrier() {
+  asm volatile("" : : : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" : : : "memory");
+}
+
+// LDS transpose read (ds_read_b64_tr_b16): inside each 16-lane row of the
+// wavefront, lane 4 a + b receives element b of the 8-byte words that lanes
+// a, 4 + a, 8 + a and 12 + a address, in that order.
+IRB_DEV v4s lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+}
+
 IRB_DEV void ld8(const uint16_t* p, bf16x8& hi, bf16x8& lo) {
   hi = *reinterpret_cast<const bf16x8*>(p);
   (void)lo;
@@ -386,16 +422,18 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   using T = uint16_t;
   constexpr int BQ = 128 / G;
   constexpr int KS = D / 32, NDT = DV / 16;
-  constexpr int LDK = D + 8;      // K tile row: one key, D dims (+pad)
-  // V^T tile row: one dim, 32 keys (+pad to 20 dwords: the 16-byte operand
-  // reads of 16 lanes cover the 64 banks once).  Keys sit in MFMA k-slot
-  // order: position 8 g + 4 h + i holds key 16 h + 4 g + i, so a lane's eight
-  // operand keys {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3} are one 16-byte
-  // word.
-  constexpr int LDT = 32 + 8;
-  constexpr int KBYTES = 32 * LDK * 2, VBYTES = DV * LDT * 2;
+  // K and V tiles are row-major (one key per row, no padding), filled by
+  // direct global-to-LDS loads (lane i of a load writes 16-byte slot i).  The
+  // 16-byte chunks of row r sit XOR-swizzled: chunk c of a K row at slot
+  // c ^ (r mod NCK), of a V row at slot c ^ (2 r mod NCV), so the K operand
+  // reads of 16 rows and the V^T transpose reads of 4 rows hit distinct banks.
+  // Three buffers: the tile in use plus two in flight.
+  constexpr int NCK = D / 8, NCV = DV / 8;            // 16-byte chunks per row
+  constexpr int KBYTES = 32 * D * 2, VBYTES = 32 * DV * 2;
   constexpr int BUF = KBYTES + VBYTES;
-  __shared__ __align__(16) char raw[2 * BUF];
+  constexpr int NIK = 32 * NCK / 256, NIV = 32 * NCV / 256;   // loads per wave per tile
+  static_assert(NIK >= 1 && NIV >= 1, "tile loads");
+  __shared__ __align__(16) char raw[3 * BUF];
   __shared__ uint32_t mask[BQ][kSegTiles];
   __shared__ int tiles[kSegTiles];
   __shared__ int s_ntiles;
@@ -441,71 +479,31 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
   const float sc2 = a.scale * kLog2e;
 
-  // tile loader: 32 keys of K (16-byte chunks per thread) and V (one thread =
-  // two adjacent keys x 8 dims, so V^T can be written as dword pairs).  Row
-  // pointers are formed once; a key tile only adds a scalar offset.
-  constexpr int KC = D / 8, VG = DV / 8;
-  constexpr int KPER = (32 * KC + 255) / 256;
-  struct Stage { uint4 k[KPER]; uint4 v[2]; };        // one key tile in flight
-  const int vkp = tid % 16, vdg = tid / 16;           // key pair, dim group
-  const bool vown = vdg < VG;
-  const T* kptr[KPER];
-  int krow[KPER];
-#pragma unroll
-  for (int u = 0; u < KPER; ++u) {
-    const int chunk = tid + 256 * u;
-    krow[u] = (chunk < 32 * KC) ? chunk / KC : 1 << 20;
-    kptr[u] = kbase + static_cast<int64_t>(chunk < 32 * KC ? chunk / KC : 0) * a.sk_t + 8 * (chunk % KC);
-  }
-  const T* vptr0 = vbase + static_cast<int64_t>(2 * vkp) * a.sv_t + 8 * (vown ? vdg : 0);
-  const T* vptr1 = vptr0 + a.sv_t;
-  const int64_t kstep = 32 * a.sk_t, vstep = 32 * a.sv_t;
-  // kt is uniform; tiles wholly inside S_k load without per-row checks
-  auto gload = [&](int kt, Stage& r) {
+  // tile loader: wave w issues NIK + NIV direct loads per tile; lane i of
+  // load n fills slot (w NIK + n) 64 + i of the K tile (same for V)
+  auto issue = [&](int kt, int buf) {
     kt = __builtin_amdgcn_readfirstlane(kt);
-    const int rows = a.S_k - kt * 32;                  // keys of this tile that exist
-    const int64_t ko = kt * kstep, vo = kt * vstep;
-    if (rows >= 32) {
+    char* base = raw + buf * BUF;
 #pragma unroll
-      for (int u = 0; u < KPER; ++u)
-        if (KPER * 256 == 32 * KC || krow[u] < 32) r.k[u] = *reinterpret_cast<const uint4*>(kptr[u] + ko);
-      if (vown) {
-        r.v[0] = *reinterpret_cast<const uint4*>(vptr0 + vo);
-        r.v[1] = *reinterpret_cast<const uint4*>(vptr1 + vo);
-      }
-    } else {
+    for (int n = 0; n < NIK; ++n) {
+      const int slot = (wid * NIK + n) * 64 + lane;
+      const int r = slot / NCK, sc = slot % NCK;
+      const int key = min(kt * 32 + r, a.S_k - 1);
+      const T* src = kbase + static_cast<int64_t>(key) * a.sk_t + 8 * (sc ^ (r & (NCK - 1)));
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(base + (wid * NIK + n) * 1024)));
+    }
 #pragma unroll
-      for (int u = 0; u < KPER; ++u) {
-        r.k[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (krow[u] < rows) r.k[u] = *reinterpret_cast<const uint4*>(kptr[u] + ko);
-      }
-      r.v[0] = make_uint4(0u, 0u, 0u, 0u);
-      r.v[1] = r.v[0];
-      if (vown && 2 * vkp < rows) r.v[0] = *reinterpret_cast<const uint4*>(vptr0 + vo);
-      if (vown && 2 * vkp + 1 < rows) r.v[1] = *reinterpret_cast<const uint4*>(vptr1 + vo);
+    for (int n = 0; n < NIV; ++n) {
+      const int slot = (wid * NIV + n) * 64 + lane;
+      const int r = slot / NCV, sc = slot % NCV;
+      const int key = min(kt * 32 + r, a.S_k - 1);
+      const T* src = vbase + static_cast<int64_t>(key) * a.sv_t + 8 * (sc ^ ((2 * r) & (NCV - 1)));
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(base + KBYTES + (wid * NIV + n) * 1024)));
     }
   };
-  // dword position of the key pair (2 vkp, 2 vkp + 1) in a V^T row
-  const int vpos = 4 * ((vkp & 7) >> 1) + 2 * (vkp >> 3) + (vkp & 1);
-  auto lstore = [&](int buf, const Stage& r) {
-    T* kb = reinterpret_cast<T*>(raw + buf * BUF);
-    uint32_t* vt32 = reinterpret_cast<uint32_t*>(raw + buf * BUF + KBYTES);
-#pragma unroll
-    for (int u = 0; u < KPER; ++u) {
-      const int chunk = tid + 256 * u;
-      if (chunk < 32 * KC) *reinterpret_cast<uint4*>(kb + (chunk / KC) * LDK + 8 * (chunk % KC)) = r.k[u];
-    }
-    if (vown) {
-      const uint32_t a0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-      const uint32_t a1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // dims 8*vdg + 2e and + 2e + 1; each dword = (key 2*vkp, key 2*vkp + 1)
-        vt32[(8 * vdg + 2 * e) * (LDT / 2) + vpos] = (a0[e] & 0xffffu) | (a1[e] << 16);
-        vt32[(8 * vdg + 2 * e + 1) * (LDT / 2) + vpos] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-      }
-    }
-  };
+  // per-lane LDS offsets (halfwords) of the K operand (row 16 kk + l16, chunk 4 s2 + g16)
+  // and of the V^T transpose reads (key 4 g16 + l16 / 4 [+ 16], dims 16 dt + 4 (l16 % 4))
+  const int vk0 = 4 * g16 + (l16 >> 2);
 
   if (tid < BQ) cursor[tid] = 0;
   const int kt_first = ts.kmin >> 5, kt_last = ts.kmax >> 5;
@@ -583,15 +581,18 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     __syncthreads();
     const int ntiles = s_ntiles;
     if (ntiles == 0) continue;
-    // key tile it is in LDS buffer it % 2; the stage registers carry tile it + 1
-    Stage stg;
-    gload(seg0 + tiles[0], stg);
-    lstore(0, stg);
-    __syncthreads();
+    // key tile it sits in buffer it % 3; tiles it + 1 and it + 2 are in flight
+    issue(seg0 + tiles[0], 0);
+    if (ntiles > 1) issue(seg0 + tiles[1], 1);
     for (int it = 0; it < ntiles; ++it) {
-      const int buf = it & 1;
+      const int buf = it % 3;
       const int ktl = tiles[it];
-      if (it + 1 < ntiles) gload(seg0 + tiles[it + 1], stg);
+      // this wave's loads of tile it are done (those of tile it + 1 may not be);
+      // the barrier makes every wave's part visible and frees buffer (it + 2) % 3
+      if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIK + NIV>());
+      else __builtin_amdgcn_s_waitcnt(kVmWaitTile<0>());
+      bare_barrier();
+      if (it + 2 < ntiles) issue(seg0 + tiles[it + 2], (it + 2) % 3);
       const T* kb = reinterpret_cast<const T*>(raw + buf * BUF);
       const T* vt = reinterpret_cast<const T*>(raw + buf * BUF + KBYTES);
       f32x4 st[2][2];
@@ -601,7 +602,8 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       for (int s2 = 0; s2 < KS; ++s2) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + (16 * kk + l16) * LDK + 32 * s2 + 8 * g16);
+          const int kr = 16 * kk + l16;
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + kr * D + 8 * ((4 * s2 + g16) ^ (kr & (NCK - 1))));
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct)
             st[kk][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ct][s2], st[kk][ct], 0, 0, 0);
@@ -652,13 +654,14 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vt + (dt * 16 + l16) * LDT + 8 * g16);
+        const int vc = 2 * dt + ((l16 & 3) >> 1), vw = 4 * (l16 & 1);
+        const v4s v0 = lds_read_tr(vt + vk0 * DV + 8 * (vc ^ ((2 * vk0) & (NCV - 1))) + vw);
+        const v4s v1 = lds_read_tr(vt + (vk0 + 16) * DV + 8 * (vc ^ ((2 * (vk0 + 16)) & (NCV - 1))) + vw);
+        const bf16x8 vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
           oacc[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], oacc[dt][ct], 0, 0, 0);
       }
-      if (it + 1 < ntiles) lstore(buf ^ 1, stg);
-      __syncthreads();
     }
   }
 

@@ -11,9 +11,13 @@ int launch_compress(const Layout& L, int c, const void* k, int dtype, int64_t sb
                     const float* gamma, float eps, const float* freqs, int R, float* kc,
                     int32_t* cu_blocks, hipStream_t stream);
 
+// write_invisible: also write -inf at the tile's invisible entries (the fused
+// route path skips them: selection never reads them); queries with at most
+// skip_nb visible blocks are not scored (-1: score every query)
 int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
                       const float* kc, const int32_t* cu_blocks, int c, float scale, int q0, int q1,
-                      int j0, int j1, float* out, int64_t out_stride, hipStream_t stream);
+                      int j0, int j1, float* out, int64_t out_stride, int write_invisible, int skip_nb,
+                      hipStream_t stream);
 
 int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, int q1,
                   const int32_t* cu_blocks, int c, int topk, int32_t* sel, int32_t* cnt,

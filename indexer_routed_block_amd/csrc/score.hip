@@ -4,20 +4,23 @@
 // FP32 tile of scores sum_h w[t,h] * relu(q[t,h] . k[j]) with signed FP32
 // head weights; visibility and scale per the QSA page, select_qsa_token_ids.
 //
-// Tiling.  A workgroup (4 waves) owns 512/H queries x 64 blocks.  Rows of the
-// MFMA A operand are (query, head) pairs, columns are blocks, K is the index
-// dimension.  The FP32 compressed keys of the tile are split once into bf16
-// high and low halves in LDS; each wave keeps the operands of its 32 blocks
-// in registers and streams its queries' rows from global memory, issuing
-// q*hi + q*lo (plus q_lo*hi for FP32 queries) per 16x16x32 step.  The
-// accumulator layout puts 4 heads of one query in each lane, so the head
-// reduction is 4 in-lane FMAs plus at most two cross-lane adds.
+// Tiling.  Rows of the MFMA A operand are (query, head) pairs, columns are
+// blocks, K is the index dimension.  A workgroup (4 waves) owns the rows of
+// 4 * 16 RT / H queries -- each wave keeps RT row tiles (whole queries) of q in
+// registers for the whole launch -- and one segment of blocks.  It streams
+// the segment in chunks of 64 blocks: the FP32 compressed keys are split into
+// bf16 high and low halves on the way into a double-buffered LDS tile, and
+// every wave reads each 16-block operand once for all of its row tiles
+// (q*hi + q*lo, plus q_lo*hi for FP32 queries).  The accumulator layout puts
+// 4 heads of one query in each lane, so the weighted head reduction is in-lane
+// FMAs plus at most two cross-lane adds.
+#include <algorithm>
+
 #include "irb_internal.hpp"
 
 namespace irb {
 
-constexpr int kScoreBN = 64;   // blocks per workgroup
-constexpr int kScoreRows = 512; // (query, head) rows per workgroup
+constexpr int kScoreChunk = 64;   // blocks per LDS chunk
 
 template <typename QT>
 IRB_DEV void load_q_operand(const QT* p, bf16x8& hi, bf16x8& lo);
@@ -42,179 +45,252 @@ IRB_DEV void load_q_operand<float>(const float* p, bf16x8& hi, bf16x8& lo) {
   }
 }
 
-template <typename QT, int D>
-__global__ void __launch_bounds__(256)
-score_kernel(Layout L, const QT* __restrict__ q, int H, const float* __restrict__ w,
-             const float* __restrict__ kc, const int32_t* __restrict__ cu_blocks, int c, float scale,
-             int q0, int q1, int j0, int j1, float* __restrict__ out, int64_t ostride, int n_jt) {
+// Visible block range of query t: [base, base + nb) (nb = 0 when not valid)
+IRB_DEV void visible_blocks(const Layout& L, const int32_t* cu_blocks, int c, int b, int t, int& base, int& nb) {
+  const Doc d = doc_of(L, b, t);
+  base = d.valid ? block_base(L, cu_blocks, d) : 0;
+  nb = d.valid ? (t - d.start + 1) / c : 0;
+}
+
+template <typename QT, int D, int H>
+__global__ void __launch_bounds__(256, 2)
+score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kc,
+             const int32_t* __restrict__ cu_blocks, int c, float scale, int q0, int q1, int j0, int j1,
+             float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg, int write_invisible, int skip_nb) {
   constexpr int KS = D / 32;
-  constexpr int LDK = D + 8;                 // padded LDS row (bf16 elements)
   constexpr bool kSplitQ = sizeof(QT) == 4;
-  __shared__ uint16_t khi[kScoreBN * LDK];
-  __shared__ uint16_t klo[kScoreBN * LDK];
-  __shared__ int s_any;
+  // row tiles per wave (whole queries); FP32 queries at D = 128 keep half as many
+  // so that their hi/lo operands fit in registers
+  constexpr int RT = (kSplitQ && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
+  constexpr int QW = 16 * RT / H;                   // queries per wave (>= 1)
+  constexpr int QG = 4 * QW;                        // queries per workgroup
+  constexpr int LDK = D + 8;                        // padded LDS row (bf16 elements)
+  constexpr int GROUPS = kScoreChunk * D / 8;       // 8-dim groups per chunk
+  constexpr int GPT = GROUPS / 256;                 // per thread
+  static_assert(GROUPS % 256 == 0, "chunk staging");
+  __shared__ __align__(16) uint16_t kbuf[2][2][kScoreChunk * LDK];   // [buffer][hi, lo]
+  __shared__ int s_range[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g16 = lane >> 4, l16 = lane & 15;
   const int b = blockIdx.y;
-  const int BQ = kScoreRows / H;
-  const int qt = blockIdx.x / n_jt, jt = blockIdx.x % n_jt;
-  const int qa = q0 + qt * BQ, qe = min(q1, qa + BQ);
-  const int jb = j0 + jt * kScoreBN, je = min(j1, jb + kScoreBN);
+  const int qg = blockIdx.x / n_seg, sg = blockIdx.x % n_seg;
+  const int qa = q0 + qg * QG, qe = min(q1, qa + QG);
   const int nb_max = L.S / c;
 
-  if (tid == 0) s_any = 0;
-  __syncthreads();
-  for (int t = qa + tid; t < qe; t += 256) {
-    const Doc d = doc_of(L, b, t);
-    if (d.valid) {
-      const int base = block_base(L, cu_blocks, d);
-      const int nb = (t - d.start + 1) / c;
-      if (max(base, jb) < min(base + nb, je)) s_any = 1;
+  // visible block range of the workgroup's queries, clipped to [j0, j1) and the segment
+  if (tid < 64) {
+    int lo = 0x7fffffff, hi = -1;
+    if (tid < QG && qa + tid < qe) {
+      int base, nb;
+      visible_blocks(L, cu_blocks, c, b, qa + tid, base, nb);
+      if (nb > skip_nb && nb > 0) { lo = base; hi = base + nb; }
     }
-  }
-  __syncthreads();
-  float* otile = out + (static_cast<int64_t>(b) * (q1 - q0) + (qa - q0)) * ostride + (jb - j0);
-  const int ncol = je - jb;
-  if (!s_any) {
-    for (int i = tid; i < (qe - qa) * kScoreBN; i += 256) {
-      const int r = i / kScoreBN, cc = i % kScoreBN;
-      if (cc < ncol) otile[static_cast<int64_t>(r) * ostride + cc] = -INFINITY;
-    }
-    return;
-  }
-
-  // stage the tile's compressed keys as bf16 hi/lo
-  const float* kcb = kc + (static_cast<int64_t>(b) * nb_max) * D;
-  for (int i = tid; i < kScoreBN * D / 4; i += 256) {
-    const int r = i / (D / 4), c4 = (i % (D / 4)) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (jb + r < je) v = *reinterpret_cast<const float4*>(kcb + static_cast<int64_t>(jb + r) * D + c4);
-    const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint16_t h, l;
-      split_bf16(f[e], h, l);
-      khi[r * LDK + c4 + e] = h;
-      klo[r * LDK + c4 + e] = l;
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo = min(lo, __shfl_xor(lo, o, 64));
+      hi = max(hi, __shfl_xor(hi, o, 64));
     }
+    if (tid == 0) { s_range[0] = lo; s_range[1] = hi; }
   }
   __syncthreads();
+  const int sb = j0 + sg * seg_blocks, se = min(j1, sb + seg_blocks);   // this segment
+  const int cb = max(sb, s_range[0]), ce = min(se, s_range[1]);        // computed blocks
+  float* otile = out + (static_cast<int64_t>(b) * (q1 - q0) + (qa - q0)) * ostride;
+  if (write_invisible) {
+    // -inf for the segment's blocks outside [cb, ce) (the computed ones are written below)
+    for (int i = tid; i < (qe - qa) * (se - sb); i += 256) {
+      const int r = i / (se - sb), j = sb + i % (se - sb);
+      if (j < cb || j >= ce) otile[static_cast<int64_t>(r) * ostride + (j - j0)] = -INFINITY;
+    }
+  }
+  if (cb >= ce) return;
 
-  const int rh = wid >> 1, ch = wid & 1;
-  const int g = lane >> 4, l16 = lane & 15;
-  bf16x8 kh[2][KS], kl[2][KS];
+  // q rows of this wave in the A layout: row 16 rt + l16 -> query rr / H, head rr % H
+  bf16x8 qh[RT][KS], ql[RT][KS];
+  float wv[RT][4];
+  const int64_t qrow = static_cast<int64_t>(H) * D;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int col = (2 * ch + ct) * 16 + l16;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rr = 16 * rt + l16;
+    const int qi = qa + wid * QW + rr / H, hd = rr % H;
+    const bool ok = qi < qe;
+    const QT* qp = q + (static_cast<int64_t>(b) * L.S + (ok ? qi : qa)) * qrow + static_cast<int64_t>(hd) * D + 8 * g16;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kh[ct][s] = *reinterpret_cast<const bf16x8*>(&khi[col * LDK + 32 * s + 8 * g]);
-      kl[ct][s] = *reinterpret_cast<const bf16x8*>(&klo[col * LDK + 32 * s + 8 * g]);
+      load_q_operand<QT>(qp + 32 * s, qh[rt][s], ql[rt][s]);
+      if (!ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { qh[rt][s][e] = 0; if (kSplitQ) ql[rt][s][e] = 0; }
+      }
+    }
+    // head weights of this lane's accumulator rows 16 rt + 4 g16 + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r2 = 16 * rt + 4 * g16 + i;
+      const int qw = qa + wid * QW + r2 / H;
+      wv[rt][i] = qw < qe ? w[(static_cast<int64_t>(b) * L.S + qw) * H + r2 % H] : 0.f;
     }
   }
+  // visibility of this lane's write queries
+  int vbase[QW], vnb[QW];
+#pragma unroll
+  for (int k = 0; k < QW; ++k) {
+    const int qw = qa + wid * QW + k;
+    vbase[k] = 0;
+    vnb[k] = 0;
+    if (qw < qe) visible_blocks(L, cu_blocks, c, b, qw, vbase[k], vnb[k]);
+  }
 
-  // units: one query when H >= 16 (H/16 row tiles), else one row tile of 16/H queries
-  const bool wide = H >= 16;
-  const int tpu = wide ? H / 16 : 1;
-  const int qpu = wide ? 1 : 16 / H;
-  const int gpq = wide ? 4 : H / 4;          // lane groups per query inside a tile
-  const int n_units = (qe - qa + qpu - 1) / qpu;
-  const int64_t qrow = static_cast<int64_t>(H) * D;   // q elements per token
+  // chunk staging: thread owns GPT groups of 8 dims (block = grp / (D/8))
+  const float* kcb = kc + static_cast<int64_t>(b) * nb_max * D;
+  float4 stg[GPT][2];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int grp = tid + 256 * u;
+      const int r = grp / (D / 8), c8 = grp % (D / 8);
+      const int jj = min(j + r, nb_max - 1);
+      const float* src = kcb + static_cast<int64_t>(jj) * D + 8 * c8;
+      stg[u][0] = *reinterpret_cast<const float4*>(src);
+      stg[u][1] = *reinterpret_cast<const float4*>(src + 4);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int grp = tid + 256 * u;
+      const int r = grp / (D / 8), c8 = grp % (D / 8);
+      const float f[8] = {stg[u][0].x, stg[u][0].y, stg[u][0].z, stg[u][0].w,
+                          stg[u][1].x, stg[u][1].y, stg[u][1].z, stg[u][1].w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t h, l;
+        split_bf16(f[e], h, l);
+        hi[e] = static_cast<short>(h);
+        lo[e] = static_cast<short>(l);
+      }
+      *reinterpret_cast<bf16x8*>(&kbuf[buf][0][r * LDK + 8 * c8]) = hi;
+      *reinterpret_cast<bf16x8*>(&kbuf[buf][1][r * LDK + 8 * c8]) = lo;
+    }
+  };
 
-  for (int u = rh; u < n_units; u += 2) {
-    float part[2] = {0.f, 0.f};
-    for (int tq = 0; tq < tpu; ++tq) {
-      // this lane's A row
-      const int qi = qa + u * qpu + (wide ? 0 : l16 / H);
-      const int hd = wide ? 16 * tq + l16 : l16 % H;
-      bf16x8 qh[KS], ql[KS];
-      const bool qok = qi < qe;
-      const QT* qp = q + (static_cast<int64_t>(b) * L.S + (qok ? qi : qa)) * qrow + static_cast<int64_t>(hd) * D + 8 * g;
+  gload(cb);
+  lstore(0);
+  __syncthreads();
+  int buf = 0;
+  for (int j = cb; j < ce; j += kScoreChunk) {
+    const bool more = j + kScoreChunk < ce;
+    if (more) gload(j + kScoreChunk);
+#pragma unroll
+    for (int ct = 0; ct < kScoreChunk / 16; ++ct) {
+      const int jc = j + 16 * ct;                  // first block of this column tile
+      if (jc >= ce) break;
+      f32x4 acc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        load_q_operand<QT>(qp + 32 * s, qh[s], ql[s]);
-        if (!qok) {
+        const int off = (16 * ct + l16) * LDK + 32 * s + 8 * g16;
+        const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&kbuf[buf][0][off]);
+        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&kbuf[buf][1][off]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) { qh[s][e] = 0; if (kSplitQ) ql[s][e] = 0; }
+        for (int rt = 0; rt < RT; ++rt) {
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rt][s], kh, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rt][s], kl, acc[rt], 0, 0, 0);
+          if (kSplitQ) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[rt][s], kh, acc[rt], 0, 0, 0);
         }
       }
-      f32x4 acc[2];
+      // weighted ReLU summed over each query's heads
+      float part[QW];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < QW; ++k) part[k] = 0.f;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[s], kh[ct][s], acc[ct], 0, 0, 0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[s], kl[ct][s], acc[ct], 0, 0, 0);
-          if (kSplitQ) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[s], kh[ct][s], acc[ct], 0, 0, 0);
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = (16 * rt + 4 * g16 + i) / H;      // compile-time except for g16
+#pragma unroll
+          for (int kk = 0; kk < QW; ++kk)
+            if (kk == k) part[kk] = fmaf(wv[rt][i], fmaxf(acc[rt][i], 0.f), part[kk]);
         }
+      // lanes l, l^16, l^32, l^48 hold the same block: combine the head groups
+#pragma unroll
+      for (int k = 0; k < QW; ++k) {
+        if (H >= 16) part[k] = row4_sum(part[k]);
+        else if (H == 8) part[k] = row_pair_sum(part[k]);
       }
-      // weighted relu over this lane's 4 rows (rows 4g..4g+3 of the tile)
+      const int jb = jc + l16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        const int qr = qa + u * qpu + (wide ? 0 : r / H);
-        const int hr = wide ? 16 * tq + r : r % H;
-        const float wv = (qr < qe) ? w[(static_cast<int64_t>(b) * L.S + qr) * H + hr] : 0.f;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) part[ct] += wv * fmaxf(acc[ct][i], 0.f);
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      if (gpq >= 4) part[ct] = row4_sum(part[ct]);
-      else if (gpq == 2) part[ct] = row_pair_sum(part[ct]);
-    }
-    if ((g % gpq) == 0) {
-      const int qw = qa + u * qpu + g / gpq;
-      if (qw < qe) {
-        const Doc d = doc_of(L, b, qw);
-        const int base = d.valid ? block_base(L, cu_blocks, d) : 0;
-        const int nb = d.valid ? (qw - d.start + 1) / c : 0;
-        float* orow = otile + static_cast<int64_t>(qw - qa) * ostride;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int cc = (2 * ch + ct) * 16 + l16;
-          const int j = jb + cc;
-          if (cc < ncol) orow[cc] = (j >= base && j < base + nb) ? scale * part[ct] : -INFINITY;
+      for (int k = 0; k < QW; ++k) {
+        // the lane group that owns query k's sum writes it
+        const bool writer = H >= 16 ? (g16 == 0) : (H == 8 ? (g16 == 2 * (k % 2)) : (g16 == k % 4));
+        const int qw = qa + wid * QW + k;
+        if (writer && qw < qe && jb < ce) {
+          const bool vis = jb >= vbase[k] && jb < vbase[k] + vnb[k];
+          if (vis || write_invisible)
+            otile[static_cast<int64_t>(qw - qa) * ostride + (jb - j0)] = vis ? scale * part[k] : -INFINITY;
         }
       }
     }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
+}
+
+template <typename QT, int D>
+static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const int32_t* cu_blocks,
+                          int c, float scale, int q0, int q1, int j0, int j1, float* out, int64_t ostride,
+                          int write_invisible, int skip_nb, hipStream_t stream) {
+  const int RT = (sizeof(QT) == 4 && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
+  const int QG = 4 * (16 * RT / H);
+  const int n_qg = (q1 - q0 + QG - 1) / QG;
+  // block segments: about a quarter of the widest visible range, 256..2048 blocks
+  const int span = j1 - j0;
+  int seg = std::min(2048, std::max(256, (L.S / c) / 4));
+  seg = (seg + kScoreChunk - 1) / kScoreChunk * kScoreChunk;
+  const int n_seg = (span + seg - 1) / seg;
+  const dim3 grid(static_cast<unsigned>(n_qg * n_seg), static_cast<unsigned>(L.B));
+#define IRB_SCORE_CASE(HH)                                                                                   \
+  case HH:                                                                                                   \
+    hipLaunchKernelGGL((score_kernel<QT, D, HH>), grid, dim3(256), 0, stream, L, q, w, kc, cu_blocks, c,   \
+                       scale, q0, q1, j0, j1, out, ostride, seg, n_seg, write_invisible, skip_nb);          \
+    return 0;
+  switch (H) {
+    IRB_SCORE_CASE(4)
+    IRB_SCORE_CASE(8)
+    IRB_SCORE_CASE(16)
+    IRB_SCORE_CASE(32)
+    IRB_SCORE_CASE(48)
+    IRB_SCORE_CASE(64)
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+#undef IRB_SCORE_CASE
 }
 
 template <typename QT>
 static int launch_score_t(const Layout& L, const QT* q, int H, int D, const float* w, const float* kc,
                           const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1,
-                          float* out, int64_t ostride, hipStream_t stream) {
-  const int BQ = kScoreRows / H;
-  const int n_qt = (q1 - q0 + BQ - 1) / BQ;
-  const int n_jt = (j1 - j0 + kScoreBN - 1) / kScoreBN;
-  const dim3 grid(static_cast<unsigned>(n_qt * n_jt), static_cast<unsigned>(L.B));
-  const dim3 block(256);
-#define IRB_SCORE_CASE(DD)                                                                              \
-  case DD:                                                                                              \
-    hipLaunchKernelGGL((score_kernel<QT, DD>), grid, block, 0, stream, L, q, H, w, kc, cu_blocks, c, scale, \
-                       q0, q1, j0, j1, out, ostride, n_jt);                                            \
-    break;
+                          float* out, int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
   switch (D) {
-    IRB_SCORE_CASE(32)
-    IRB_SCORE_CASE(64)
-    IRB_SCORE_CASE(128)
+    case 32: return launch_score_d<QT, 32>(L, q, H, w, kc, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
+    case 64: return launch_score_d<QT, 64>(L, q, H, w, kc, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
+    case 128: return launch_score_d<QT, 128>(L, q, H, w, kc, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
-#undef IRB_SCORE_CASE
-  return 0;
 }
 
 int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
                       const float* kc, const int32_t* cu_blocks, int c, float scale, int q0, int q1,
-                      int j0, int j1, float* out, int64_t out_stride, hipStream_t stream) {
+                      int j0, int j1, float* out, int64_t out_stride, int write_invisible, int skip_nb,
+                      hipStream_t stream) {
   if (dtype == IRB_BF16)
     return launch_score_t(L, static_cast<const uint16_t*>(q), H, D, w, kc, cu_blocks, c, scale, q0, q1, j0, j1,
-                          out, out_stride, stream);
+                          out, out_stride, write_invisible, skip_nb, stream);
   return launch_score_t(L, static_cast<const float*>(q), H, D, w, kc, cu_blocks, c, scale, q0, q1, j0, j1, out,
-                        out_stride, stream);
+                        out_stride, write_invisible, skip_nb, stream);
 }
 
 }  // namespace irb
