@@ -416,7 +416,7 @@ bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __re
 
   // one 32-row batch over list slots [s0, s0 + qpb) of this wave's LDS list
   // (slots at or past nv are empty), head block hb when a query spans batches
-  auto batch = [&](int s0, int nv, int hb) {
+  auto batch = [&](int s0, int nv, int hb) __attribute__((always_inline)) {
     auto tq = [&](int slot) -> int { return slot < nv ? s_t[wid][s0 + slot] : -1; };
     auto mq = [&](int slot) -> uint32_t { return slot < nv ? s_m[wid][s0 + slot] : 0u; };
     f32x4 sacc[2], pacc[2];

@@ -481,7 +481,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
 
   // tile loader: wave w issues NIK + NIV direct loads per tile; lane i of
   // load n fills slot (w NIK + n) 64 + i of the K tile (same for V)
-  auto issue = [&](int kt, int buf) {
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
     kt = __builtin_amdgcn_readfirstlane(kt);
     char* base = raw + buf * BUF;
 #pragma unroll

@@ -59,9 +59,9 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
              float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg, int write_invisible, int skip_nb) {
   constexpr int KS = D / 32;
   constexpr bool kSplitQ = sizeof(QT) == 4;
-  // row tiles per wave (whole queries); FP32 queries at D = 128 keep half as many
-  // so that their hi/lo operands fit in registers
-  constexpr int RT = (kSplitQ && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
+  // row tiles per wave (whole queries); FP32 queries (hi/lo operands) and
+  // 4-head queries (16 per wave) keep half as many at D = 128 to stay in registers
+  constexpr int RT = ((kSplitQ || H <= 4) && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
   constexpr int QW = 16 * RT / H;                   // queries per wave (>= 1)
   constexpr int QG = 4 * QW;                        // queries per workgroup
   constexpr int LDK = D + 8;                        // padded LDS row (bf16 elements)
@@ -145,7 +145,7 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   // chunk staging: thread owns GPT groups of 8 dims (block = grp / (D/8))
   const float* kcb = kc + static_cast<int64_t>(b) * nb_max * D;
   float4 stg[GPT][2];
-  auto gload = [&](int j) {
+  auto gload = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
       const int grp = tid + 256 * u;
@@ -156,7 +156,7 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
       stg[u][1] = *reinterpret_cast<const float4*>(src + 4);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
       const int grp = tid + 256 * u;
@@ -244,7 +244,7 @@ template <typename QT, int D>
 static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const int32_t* cu_blocks,
                           int c, float scale, int q0, int q1, int j0, int j1, float* out, int64_t ostride,
                           int write_invisible, int skip_nb, hipStream_t stream) {
-  const int RT = (sizeof(QT) == 4 && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
+  const int RT = ((sizeof(QT) == 4 || H <= 4) && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
   const int QG = 4 * (16 * RT / H);
   const int n_qg = (q1 - q0 + QG - 1) / QG;
   // block segments: about a quarter of the widest visible range, 256..2048 blocks
