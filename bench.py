@@ -142,7 +142,7 @@ def main():
         L = irb.route_width(topk, c, window)
         nb_blocks = S // c
         q0 = 0 if cu is not None else min(irb.first_sparse_query(c, topk), S - 1)
-        fused_ws = torch.empty(max(int(lib.irb_route_topk_fused_workspace_size(B, S, c, topk, q0, S)), 4),
+        fused_ws = torch.empty(max(int(lib.irb_route_topk_fused_workspace_size(B, S, c, wl.D_idx, topk, q0, S)), 4),
                                dtype=torch.uint8, device=dev)
         sel = torch.empty((B, S, topk), dtype=torch.int32, device=dev)
         cnt = torch.empty((B, S), dtype=torch.int32, device=dev)

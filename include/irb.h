@@ -162,11 +162,13 @@ int irb_select_topk_regions(const irb_layout* layout, const float* scores, int64
  * irb_select_topk_regions over [q0, q1), with the FP32 scores of at most a
  * bounded number of query rows alive at a time ([QSA] select_qsa_token_ids:
  * chunking bounds the score temporary without changing top-k semantics).
- * workspace: device scratch; irb_route_topk_fused_workspace_size() gives a
- * 256 MiB-budget size, any size holding at least one score row works (rows
- * per chunk = ws_bytes / (B * (S/c) * 4)).
+ * workspace: device scratch; irb_route_topk_fused_workspace_size() gives the
+ * compressed keys split into bf16 high/low rows (B * (S/c) * D_idx * 4 bytes,
+ * rounded up to 256) plus a 256 MiB-budget of score rows; any size holding
+ * the split keys and at least one score row works (rows per chunk = the rest
+ * / (B * (S/c) * 4)).
  */
-size_t irb_route_topk_fused_workspace_size(int B, int S, int c, int topk, int q0, int q1);
+size_t irb_route_topk_fused_workspace_size(int B, int S, int c, int D_idx, int topk, int q0, int q1);
 int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype, int H_idx,
                          int D_idx, const float* w, const float* kc, const int32_t* cu_blocks,
                          int c, float score_scale, int topk, int q0, int q1, int32_t* sel,

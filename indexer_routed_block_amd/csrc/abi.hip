@@ -118,7 +118,7 @@ int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtyp
   if (!q_idx || !w || !kc || !out) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
   if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
   IRB_REQUIRE_DEVICE();
-  return launched(fn, irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, cu_blocks, c, score_scale, q0, q1, j0, j1,
+  return launched(fn, irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, nullptr, cu_blocks, c, score_scale, q0, q1, j0, j1,
                                              out, out_row_stride, 1, -1, static_cast<hipStream_t>(stream)));
 }
 
@@ -138,13 +138,19 @@ int irb_select_topk_regions(const irb_layout* layout, const float* scores, int64
                                          static_cast<hipStream_t>(stream)));
 }
 
-size_t irb_route_topk_fused_workspace_size(int B, int S, int c, int topk, int q0, int q1) {
+// fused-route workspace: the keys split into bf16 high/low rows, then score rows
+static size_t split_keys_bytes(int B, int nb, int D_idx) {
+  return (static_cast<size_t>(B) * std::max(nb, 0) * D_idx * 4 + 255) / 256 * 256;
+}
+
+size_t irb_route_topk_fused_workspace_size(int B, int S, int c, int D_idx, int topk, int q0, int q1) {
   (void)topk;
   if (B < 1 || S < 1 || c < 1 || q1 <= q0) return 0;
+  if (D_idx != 32 && D_idx != 64 && D_idx != 128) return 0;
   const int64_t nb = S / c;
   const int64_t rows_budget = nb > 0 ? ((static_cast<int64_t>(256) << 20) / (4 * nb)) : 1;
   const int64_t rows = std::min<int64_t>(std::max<int64_t>(rows_budget / B, 512), q1 - q0);
-  return static_cast<size_t>(rows * B * std::max<int64_t>(nb, 1) * 4);
+  return split_keys_bytes(B, static_cast<int>(nb), D_idx) + static_cast<size_t>(rows * B * std::max<int64_t>(nb, 1) * 4);
 }
 
 int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx, const float* w,
@@ -164,15 +170,18 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
   const int nb = L.S / c;
   if (nb < 1) return fail(IRB_ERR_INVALID, "%s: S/c must be >= 1", fn);
   const int64_t per_row = static_cast<int64_t>(L.B) * nb * 4;
-  const int64_t rows = static_cast<int64_t>(ws_bytes) / per_row;
+  const size_t kbytes = split_keys_bytes(L.B, nb, D_idx);
+  const int64_t rows = ws_bytes > kbytes ? static_cast<int64_t>(ws_bytes - kbytes) / per_row : 0;
   if (rows < 1) return fail(IRB_ERR_INVALID, "%s: workspace too small (%zu bytes)", fn, ws_bytes);
   IRB_REQUIRE_DEVICE();
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* scores = static_cast<float*>(workspace);
+  uint16_t* kcs = static_cast<uint16_t*>(workspace);
+  float* scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + kbytes);
+  if (int rc = irb::launch_split_keys(kc, kcs, static_cast<int64_t>(L.B) * nb, D_idx, st)) return launched(fn, rc);
   for (int a = q0; a < q1; a += static_cast<int>(std::min<int64_t>(rows, q1 - a))) {
     const int e = a + static_cast<int>(std::min<int64_t>(rows, q1 - a));
-    int rc = irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, cu_blocks, c, score_scale, a, e, 0, nb, scores, nb,
-                                    0, topk, st);
+    int rc = irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, kcs, cu_blocks, c, score_scale, a, e, 0, nb,
+                                    scores, nb, 0, topk, st);
     if (!rc) rc = irb::launch_select(L, scores, nb, a, e, cu_blocks, c, topk, sel, cnt, st);
     if (rc) return launched(fn, rc);
   }

@@ -686,19 +686,6 @@ bwd_scan_kernel(int64_t* __restrict__ v, int64_t n) {
 }
 
 // ---------------------------------------------------------------- dk / dv over hit lists
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-
-// LDS transpose read (gfx950 ds_read_b64_tr_b16): inside each 16-lane row of
-// the wavefront, lane 4a + b receives element b of the 8-byte words that
-// lanes a, 4 + a, 8 + a and 12 + a address, in that order.  So if lane s of
-// a row addresses row (r0 + s / 4), columns c0 + 4 (s % 4) .. + 3 of a
-// row-major bf16 matrix, lane s receives column c0 + s of rows r0 .. r0 + 3:
-// four consecutive k of an MFMA A operand whose m is the column.
-IRB_DEV v4s lds_read_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
-}
-
 template <int D, int DV>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,

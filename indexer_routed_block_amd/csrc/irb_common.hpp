@@ -113,6 +113,48 @@ IRB_DEV void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// ---------------------------------------------------------------- LDS data movement
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained).  Vector
+// memory operations complete in issue order, so this means "everything but
+// the last N issued is done".
+template <int N>
+constexpr int kVmWaitTile() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  return N | (7 << 4) | (15 << 8);
+}
+
+// Direct 16-byte global-to-LDS load (global_load_lds_dwordx4): lane i writes
+// LDS bytes [lds_base + 16 i, + 16) of the wave-uniform lds_base.  Written as
+// inline assembly so that the compiler does not wait for these loads before
+// every LDS read; the kernel orders them itself with s_waitcnt vmcnt and a
+// barrier.
+IRB_DEV void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
+}
+IRB_DEV uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+// workgroup barrier that only orders: waits happen where the kernel puts them
+IRB_DEV void bare_barrier() {
+  asm volatile("" : : : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" : : : "memory");
+}
+
+// LDS transpose read (ds_read_b64_tr_b16): inside each 16-lane row of the
+// wavefront, lane 4 a + b receives element b of the 8-byte words that lanes
+// a, 4 + a, 8 + a and 12 + a address, in that order.  So if lane s of a row
+// addresses row (r0 + s / 4), columns c0 + 4 (s % 4) .. + 3 of a row-major
+// bf16 matrix, lane s receives column c0 + s of rows r0 .. r0 + 3: four
+// consecutive k of an MFMA A operand whose m is the column.
+IRB_DEV v4s lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+}
+
 // Reductions over the four 16-lane rows of a wavefront (lanes l, l^16, l^32,
 // l^48) on the VALU: with both operands equal, v_permlane16_swap /
 // v_permlane32_swap return {x[l], x[l^16]} / {x[l], x[l^32]} in some order,

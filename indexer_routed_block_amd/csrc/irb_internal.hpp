@@ -14,10 +14,14 @@ int launch_compress(const Layout& L, int c, const void* k, int dtype, int64_t sb
 // write_invisible: also write -inf at the tile's invisible entries (the fused
 // route path skips them: selection never reads them); queries with at most
 // skip_nb visible blocks are not scored (-1: score every query)
+// kc_split (optional): the keys pre-split by launch_split_keys, streamed by
+// direct global-to-LDS loads instead of being split while staging
 int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
-                      const float* kc, const int32_t* cu_blocks, int c, float scale, int q0, int q1,
-                      int j0, int j1, float* out, int64_t out_stride, int write_invisible, int skip_nb,
-                      hipStream_t stream);
+                      const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,
+                      int q0, int q1, int j0, int j1, float* out, int64_t out_stride, int write_invisible,
+                      int skip_nb, hipStream_t stream);
+// kcs[2 blk] = bf16 high halves of kc[blk], kcs[2 blk + 1] = low halves (rows of D)
+int launch_split_keys(const float* kc, uint16_t* kcs, int64_t n_blocks, int D, hipStream_t stream);
 
 int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, int q1,
                   const int32_t* cu_blocks, int c, int topk, int32_t* sel, int32_t* cnt,

@@ -52,11 +52,16 @@ IRB_DEV void visible_blocks(const Layout& L, const int32_t* cu_blocks, int c, in
   nb = d.valid ? (t - d.start + 1) / c : 0;
 }
 
-template <typename QT, int D, int H>
+// kPre: the keys come pre-split (kcs, per block a row of bf16 high halves then
+// a row of low halves) and stream through four LDS buffers by direct
+// global-to-LDS loads, three chunks in flight; otherwise the FP32 keys are
+// split while staging through two buffers.
+template <typename QT, int D, int H, bool kPre>
 __global__ void __launch_bounds__(256, 2)
 score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kc,
-             const int32_t* __restrict__ cu_blocks, int c, float scale, int q0, int q1, int j0, int j1,
-             float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg, int write_invisible, int skip_nb) {
+             const uint16_t* __restrict__ kcs, const int32_t* __restrict__ cu_blocks, int c, float scale, int q0,
+             int q1, int j0, int j1, float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg,
+             int write_invisible, int skip_nb) {
   constexpr int KS = D / 32;
   constexpr bool kSplitQ = sizeof(QT) == 4;
   // row tiles per wave (whole queries); FP32 queries (hi/lo operands) and
@@ -65,10 +70,17 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   constexpr int QW = 16 * RT / H;                   // queries per wave (>= 1)
   constexpr int QG = 4 * QW;                        // queries per workgroup
   constexpr int LDK = D + 8;                        // padded LDS row (bf16 elements)
-  constexpr int GROUPS = kScoreChunk * D / 8;       // 8-dim groups per chunk
+  constexpr int CH = kPre ? 32 : kScoreChunk;       // blocks per chunk
+  constexpr int NBUF = kPre ? 4 : 2;
+  constexpr int GROUPS = kScoreChunk * D / 8;       // 8-dim groups per chunk (split staging)
   constexpr int GPT = GROUPS / 256;                 // per thread
   static_assert(GROUPS % 256 == 0, "chunk staging");
-  __shared__ __align__(16) uint16_t kbuf[2][2][kScoreChunk * LDK];   // [buffer][hi, lo]
+  constexpr int NC = D / 8;                         // 16-byte chunks per bf16 row
+  constexpr int PBUF = CH * 2 * D * 2;              // bytes per pre-split buffer
+  constexpr int NI = CH * 2 * NC / 256;             // direct loads per wave per chunk
+  static_assert(!kPre || NI >= 1, "pre-split staging");
+  constexpr int RAW = kPre ? NBUF * PBUF : 2 * 2 * kScoreChunk * LDK * 2;
+  __shared__ __align__(16) char kraw[RAW];
   __shared__ int s_range[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -171,20 +183,51 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
         hi[e] = static_cast<short>(h);
         lo[e] = static_cast<short>(l);
       }
-      *reinterpret_cast<bf16x8*>(&kbuf[buf][0][r * LDK + 8 * c8]) = hi;
-      *reinterpret_cast<bf16x8*>(&kbuf[buf][1][r * LDK + 8 * c8]) = lo;
+      uint16_t* kb = reinterpret_cast<uint16_t*>(kraw) + buf * 2 * kScoreChunk * LDK;
+      *reinterpret_cast<bf16x8*>(&kb[r * LDK + 8 * c8]) = hi;
+      *reinterpret_cast<bf16x8*>(&kb[kScoreChunk * LDK + r * LDK + 8 * c8]) = lo;
     }
   };
 
-  gload(cb);
-  lstore(0);
-  __syncthreads();
-  int buf = 0;
-  for (int j = cb; j < ce; j += kScoreChunk) {
-    const bool more = j + kScoreChunk < ce;
-    if (more) gload(j + kScoreChunk);
+  // pre-split chunk loader: lane i of load n fills 16-byte slot (w NI + n) 64 + i;
+  // row R = 2 block + (0 hi | 1 lo), chunk slot sc holds chunk sc ^ ((R / 2) mod NC)
+  auto issue = [&](int j, int pbuf) __attribute__((always_inline)) {
+    char* base = kraw + pbuf * PBUF;
 #pragma unroll
-    for (int ct = 0; ct < kScoreChunk / 16; ++ct) {
+    for (int n = 0; n < NI; ++n) {
+      const int slot = (wid * NI + n) * 64 + lane;
+      const int R = slot / NC, sc = slot % NC;
+      const int blk = min(j + (R >> 1), nb_max - 1);
+      const uint16_t* src = kcs + ((static_cast<int64_t>(b) * nb_max + blk) * 2 + (R & 1)) * D +
+                            8 * (sc ^ ((R >> 1) & (NC - 1)));
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(base + (wid * NI + n) * 1024)));
+    }
+  };
+  const int nch = (ce - cb + CH - 1) / CH;
+  if constexpr (kPre) {
+    for (int p = 0; p < NBUF - 1 && p < nch; ++p) issue(cb + p * CH, p);
+  } else {
+    gload(cb);
+    lstore(0);
+    __syncthreads();
+  }
+  for (int it = 0; it < nch; ++it) {
+    const int j = cb + it * CH;
+    const int buf = it % NBUF;
+    if constexpr (kPre) {
+      // this wave's loads of chunk it are done once at most the later chunks'
+      // loads (and any score stores issued after them) are outstanding
+      const int ahead = min(NBUF - 2, nch - 1 - it);
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(kVmWaitTile<2 * NI>());
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(kVmWaitTile<NI>());
+      else __builtin_amdgcn_s_waitcnt(kVmWaitTile<0>());
+      bare_barrier();
+      if (it + NBUF - 1 < nch) issue(cb + (it + NBUF - 1) * CH, (it + NBUF - 1) % NBUF);
+    } else {
+      if (it + 1 < nch) gload(j + CH);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CH / 16; ++ct) {
       const int jc = j + 16 * ct;                  // first block of this column tile
       if (jc >= ce) break;
       f32x4 acc[RT];
@@ -192,9 +235,19 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
       for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int off = (16 * ct + l16) * LDK + 32 * s + 8 * g16;
-        const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&kbuf[buf][0][off]);
-        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&kbuf[buf][1][off]);
+        bf16x8 kh, kl;
+        if constexpr (kPre) {
+          const int R = 2 * (16 * ct + l16);
+          const int sl = (4 * s + g16) ^ ((R >> 1) & (NC - 1));
+          const char* base = kraw + buf * PBUF;
+          kh = *reinterpret_cast<const bf16x8*>(base + (R * NC + sl) * 16);
+          kl = *reinterpret_cast<const bf16x8*>(base + ((R + 1) * NC + sl) * 16);
+        } else {
+          const uint16_t* kb = reinterpret_cast<const uint16_t*>(kraw) + buf * 2 * kScoreChunk * LDK;
+          const int off = (16 * ct + l16) * LDK + 32 * s + 8 * g16;
+          kh = *reinterpret_cast<const bf16x8*>(&kb[off]);
+          kl = *reinterpret_cast<const bf16x8*>(&kb[kScoreChunk * LDK + off]);
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rt][s], kh, acc[rt], 0, 0, 0);
@@ -234,16 +287,41 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
         }
       }
     }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    if constexpr (!kPre) {
+      if (it + 1 < nch) lstore(buf ^ 1);
+      __syncthreads();
+    }
   }
 }
 
+// pre-split of the compressed keys for the streaming score path: per block a
+// row of bf16 high halves, then a row of low halves
+template <int D>
+__global__ void __launch_bounds__(256)
+split_keys_kernel(const float* __restrict__ kc, uint16_t* __restrict__ kcs, int64_t n_groups) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= n_groups) return;
+  const int64_t blk = g / (D / 8);
+  const int c8 = static_cast<int>(g % (D / 8));
+  const float4 a = *reinterpret_cast<const float4*>(kc + blk * D + 8 * c8);
+  const float4 b = *reinterpret_cast<const float4*>(kc + blk * D + 8 * c8 + 4);
+  const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  bf16x8 hi, lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint16_t h, l;
+    split_bf16(f[e], h, l);
+    hi[e] = static_cast<short>(h);
+    lo[e] = static_cast<short>(l);
+  }
+  *reinterpret_cast<bf16x8*>(kcs + (blk * 2) * D + 8 * c8) = hi;
+  *reinterpret_cast<bf16x8*>(kcs + (blk * 2 + 1) * D + 8 * c8) = lo;
+}
+
 template <typename QT, int D>
-static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const int32_t* cu_blocks,
-                          int c, float scale, int q0, int q1, int j0, int j1, float* out, int64_t ostride,
-                          int write_invisible, int skip_nb, hipStream_t stream) {
+static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const uint16_t* kcs,
+                          const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1, float* out,
+                          int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
   const int RT = ((sizeof(QT) == 4 || H <= 4) && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
   const int QG = 4 * (16 * RT / H);
   const int n_qg = (q1 - q0 + QG - 1) / QG;
@@ -255,8 +333,14 @@ static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, c
   const dim3 grid(static_cast<unsigned>(n_qg * n_seg), static_cast<unsigned>(L.B));
 #define IRB_SCORE_CASE(HH)                                                                                   \
   case HH:                                                                                                   \
-    hipLaunchKernelGGL((score_kernel<QT, D, HH>), grid, dim3(256), 0, stream, L, q, w, kc, cu_blocks, c,   \
-                       scale, q0, q1, j0, j1, out, ostride, seg, n_seg, write_invisible, skip_nb);          \
+    if (kcs)                                                                                                 \
+      hipLaunchKernelGGL((score_kernel<QT, D, HH, true>), grid, dim3(256), 0, stream, L, q, w, kc, kcs,    \
+                         cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, seg, n_seg, write_invisible,     \
+                         skip_nb);                                                                           \
+    else                                                                                                     \
+      hipLaunchKernelGGL((score_kernel<QT, D, HH, false>), grid, dim3(256), 0, stream, L, q, w, kc, kcs,   \
+                         cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, seg, n_seg, write_invisible,     \
+                         skip_nb);                                                                           \
     return 0;
   switch (H) {
     IRB_SCORE_CASE(4)
@@ -272,25 +356,37 @@ static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, c
 
 template <typename QT>
 static int launch_score_t(const Layout& L, const QT* q, int H, int D, const float* w, const float* kc,
-                          const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1,
-                          float* out, int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
+                          const uint16_t* kcs, const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0,
+                          int j1, float* out, int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
   switch (D) {
-    case 32: return launch_score_d<QT, 32>(L, q, H, w, kc, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
-    case 64: return launch_score_d<QT, 64>(L, q, H, w, kc, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
-    case 128: return launch_score_d<QT, 128>(L, q, H, w, kc, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
+    case 32: return launch_score_d<QT, 32>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
+    case 64: return launch_score_d<QT, 64>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
+    case 128: return launch_score_d<QT, 128>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+int launch_split_keys(const float* kc, uint16_t* kcs, int64_t n_blocks, int D, hipStream_t stream) {
+  const int64_t groups = n_blocks * (D / 8);
+  const unsigned grid = static_cast<unsigned>((groups + 255) / 256);
+  if (groups == 0) return 0;
+  switch (D) {
+    case 32: hipLaunchKernelGGL(split_keys_kernel<32>, dim3(grid), dim3(256), 0, stream, kc, kcs, groups); return 0;
+    case 64: hipLaunchKernelGGL(split_keys_kernel<64>, dim3(grid), dim3(256), 0, stream, kc, kcs, groups); return 0;
+    case 128: hipLaunchKernelGGL(split_keys_kernel<128>, dim3(grid), dim3(256), 0, stream, kc, kcs, groups); return 0;
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
 
 int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
-                      const float* kc, const int32_t* cu_blocks, int c, float scale, int q0, int q1,
-                      int j0, int j1, float* out, int64_t out_stride, int write_invisible, int skip_nb,
-                      hipStream_t stream) {
+                      const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,
+                      int q0, int q1, int j0, int j1, float* out, int64_t out_stride, int write_invisible,
+                      int skip_nb, hipStream_t stream) {
   if (dtype == IRB_BF16)
-    return launch_score_t(L, static_cast<const uint16_t*>(q), H, D, w, kc, cu_blocks, c, scale, q0, q1, j0, j1,
-                          out, out_stride, write_invisible, skip_nb, stream);
-  return launch_score_t(L, static_cast<const float*>(q), H, D, w, kc, cu_blocks, c, scale, q0, q1, j0, j1, out,
-                        out_stride, write_invisible, skip_nb, stream);
+    return launch_score_t(L, static_cast<const uint16_t*>(q), H, D, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0,
+                          j1, out, out_stride, write_invisible, skip_nb, stream);
+  return launch_score_t(L, static_cast<const float*>(q), H, D, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1,
+                        out, out_stride, write_invisible, skip_nb, stream);
 }
 
 }  // namespace irb
