@@ -300,6 +300,161 @@ IRB_DEV void fwd_item(const AttnArgs& a, T* __restrict__ out, float* __restrict_
   }
 }
 
+// bf16, one wavefront per (batch, query, KV head) with G <= 16 heads as the
+// MFMA columns.  The next chunk's K rows (A-layout registers) and V rows
+// (registers, then the wave's LDS slab) are loaded while the current chunk is
+// computed; V^T operands come from the slab by LDS transpose reads.
+template <int D, int DV, bool kDelta>
+IRB_DEV void fwd_item_gather(const AttnArgs& a, uint16_t* __restrict__ out, float* __restrict__ lse, int G,
+                             const uint16_t* __restrict__ dout, float* __restrict__ delta, int b, int t, int kvh,
+                             char* smem) {
+  using T = uint16_t;
+  constexpr int KS = D / 32;
+  constexpr int NDT = DV / 16;
+  constexpr int LDV = DV + 8;
+  constexpr int VU = DV / 16;                 // 16-byte V chunks per lane (two lanes per row)
+  const int lane = threadIdx.x & 63;
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int h0 = kvh * G;
+  const int nh = min(16, G);
+  const T* qbase = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(t) * a.sq_t;
+  const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
+  const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
+  const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
+  const int n = max(0, min(a.lens[row], a.L));
+  const int32_t* route = a.routes + row * a.L;
+
+  bf16x8 qh[KS];
+  {
+    const bool ok = l16 < nh;
+    const T* qp = qbase + static_cast<int64_t>(h0 + (ok ? l16 : 0)) * a.sq_h + 8 * g16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qh[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+      if (!ok) zero8(qh[s]);
+    }
+  }
+  f32x4 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m2 = -INFINITY, lsum = 0.f;
+  const float sc2 = a.scale * kLog2e;
+  T* vl = reinterpret_cast<T*>(smem);
+  const int vkk = lane >> 1, vhf = lane & 1;         // V staging: row, half
+  const int vk0 = 4 * g16 + (l16 >> 2);              // V^T transpose reads: first key row
+
+  struct Pre { bf16x8 k[2][KS]; uint4 v[VU]; };
+  auto load = [&](int e0, Pre& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int e = e0 + 16 * ti + l16;
+      const int id = e < n ? route[e] : -1;
+      const bool ok = id >= 0 && id < a.S_k;
+      const T* kr = kbase + static_cast<int64_t>(ok ? id : 0) * a.sk_t + 8 * g16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        r.k[ti][s] = *reinterpret_cast<const bf16x8*>(kr + 32 * s);
+        if (!ok) zero8(r.k[ti][s]);
+      }
+    }
+    const int e = e0 + vkk;
+    const int id = e < n ? route[e] : -1;
+    const bool ok = id >= 0 && id < a.S_k;
+    const T* vr = vbase + static_cast<int64_t>(ok ? id : 0) * a.sv_t;
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      r.v[u] = ok ? *reinterpret_cast<const uint4*>(vr + 8 * (vhf + 2 * u)) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  // one register set: the chunk's V rows go to the slab and its K rows into
+  // the S MFMAs, then the set is refilled with the next chunk, whose loads
+  // overlap this chunk's softmax and PV work
+  auto step = [&](int e0, Pre& pf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < VU; ++u) *reinterpret_cast<uint4*>(vl + vkk * LDV + 8 * (vhf + 2 * u)) = pf.v[u];
+    // ---- S^T = K Q^T for two tiles of 16 keys
+    f32x4 st[2];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      st[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) st[ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf.k[ti][s], qh[s], st[ti], 0, 0, 0);
+    }
+    wave_lds_sync();
+    if (e0 + 32 < n) load(e0 + 32, pf);
+    // ---- online softmax over this chunk; column = head l16
+    float x[2][4];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + 16 * ti + 4 * g16 + i;
+        x[ti][i] = (e < n) ? st[ti][i] * sc2 : -INFINITY;
+        cmax = fmaxf(cmax, x[ti][i]);
+      }
+    cmax = row4_max(cmax);
+    const float mnew = fmaxf(m2, cmax);
+    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { p[4 * ti + i] = fast_exp2(x[ti][i] - mref); ps += p[4 * ti + i]; }
+    const float alpha = fast_exp2(m2 - mref);
+    m2 = mnew;
+    lsum = lsum * alpha + ps;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha;
+    }
+    const bf16x8 pop = pack_bf16x8(p);
+    // ---- O^T += V^T P^T; k-slot j is key 4 g16 + j (j < 4) or 16 + 4 g16 + (j - 4)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const T* w = vl + vk0 * LDV + 16 * dt + 4 * (l16 & 3);
+      const v4s v0 = lds_read_tr(w), v1 = lds_read_tr(w + 16 * LDV);
+      const bf16x8 vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, oacc[dt], 0, 0, 0);
+    }
+    wave_lds_sync();   // the slab is rewritten by the next chunk
+  };
+  if (n > 0) {
+    Pre pf;
+    load(0, pf);
+    for (int e0 = 0; e0 < n; e0 += 32) step(e0, pf);
+  }
+
+  float ltot = row4_sum(lsum);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (kDelta) {
+    float part = 0.f;
+    if (l16 < nh) {
+      const T* dp = dout + (row * a.Hq + h0 + l16) * DV + 4 * g16;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += oacc[dt][i] * inv * bf16_to_f32(dp[dt * 16 + i]);
+    }
+    part = row4_sum(part);
+    if (l16 < nh && g16 == 0) delta[(static_cast<int64_t>(b) * a.Hq + h0 + l16) * a.S_q + t] = part;
+    return;
+  }
+  if (l16 < nh) {
+    T* op = out + (row * a.Hq + h0 + l16) * DV + 4 * g16;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const float v[4] = {oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv};
+      store4(op + dt * 16, v);
+    }
+    if (g16 == 0)
+      lse[(static_cast<int64_t>(b) * a.Hq + h0 + l16) * a.S_q + t] = ltot > 0.f ? (m2 + log2f(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Query-tile kernel for dense-ish routes (G <= 16, bf16).
 //
@@ -357,7 +512,7 @@ IRB_DEV TileStats tile_stats_wave(const AttnArgs& a, int b, int qa, int BQ, int 
 }
 
 template <typename T, int D, int DV, bool kShared, bool kDelta>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, (kShared || D > 128 || sizeof(T) == 4) ? 1 : 3)
 attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G, int n_items, int latent,
                 const T* __restrict__ dout, float* __restrict__ delta, int tile_bq, int thr_milli) {
   constexpr int PAD = sizeof(T) == 2 ? 8 : 4;
@@ -378,7 +533,10 @@ attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G,
   const int t = (item / a.Hkv) % a.S_q;
   const int b = item / (a.Hkv * a.S_q);
   if (!kShared && tile_bq > 0 && tile_stats_wave(a, b, (t / tile_bq) * tile_bq, tile_bq, thr_milli).dense) return;
-  fwd_item<T, D, DV, kShared, kDelta>(a, out, lse, G, latent, dout, delta, b, t, kvh, slice, slab);
+  if constexpr (!kShared && sizeof(T) == 2 && D <= 128)
+    fwd_item_gather<D, DV, kDelta>(a, out, lse, G, dout, delta, b, t, kvh, slab);
+  else
+    fwd_item<T, D, DV, kShared, kDelta>(a, out, lse, G, latent, dout, delta, b, t, kvh, slice, slab);
 }
 
 template <int D, int DV, int G, bool kDelta>
