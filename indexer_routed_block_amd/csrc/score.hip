@@ -45,6 +45,16 @@ IRB_DEV void load_q_operand<float>(const float* p, bf16x8& hi, bf16x8& lo) {
   }
 }
 
+// Row tiles (16 rows each) of q held per wave, always whole queries.  FP32
+// queries (hi/lo operands) and 4-head queries keep two at D = 128 so that
+// their operands fit in registers.  (Eight row tiles halve the LDS key reads
+// per MFMA but halve the number of workgroups, which measured slower.)
+template <typename QT, int D, int H, bool kPre>
+constexpr int score_rt() {
+  if (sizeof(QT) == 4 || H <= 4) return (D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
+  return (64 % H == 0) ? 4 : 3;
+}
+
 // Visible block range of query t: [base, base + nb) (nb = 0 when not valid)
 IRB_DEV void visible_blocks(const Layout& L, const int32_t* cu_blocks, int c, int b, int t, int& base, int& nb) {
   const Doc d = doc_of(L, b, t);
@@ -66,7 +76,7 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   constexpr bool kSplitQ = sizeof(QT) == 4;
   // row tiles per wave (whole queries); FP32 queries (hi/lo operands) and
   // 4-head queries (16 per wave) keep half as many at D = 128 to stay in registers
-  constexpr int RT = ((kSplitQ || H <= 4) && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
+  constexpr int RT = score_rt<QT, D, H, kPre>();
   constexpr int QW = 16 * RT / H;                   // queries per wave (>= 1)
   constexpr int QG = 4 * QW;                        // queries per workgroup
   constexpr int LDK = D + 8;                        // padded LDS row (bf16 elements)
@@ -82,6 +92,7 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   constexpr int RAW = kPre ? NBUF * PBUF : 2 * 2 * kScoreChunk * LDK * 2;
   __shared__ __align__(16) char kraw[RAW];
   __shared__ int s_range[2];
+  __shared__ int s_vis[2][64];          // visible block range (base, nb) of each query
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g16 = lane >> 4, l16 = lane & 15;
@@ -93,11 +104,12 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   // visible block range of the workgroup's queries, clipped to [j0, j1) and the segment
   if (tid < 64) {
     int lo = 0x7fffffff, hi = -1;
+    int base = 0, nb = 0;
     if (tid < QG && qa + tid < qe) {
-      int base, nb;
       visible_blocks(L, cu_blocks, c, b, qa + tid, base, nb);
       if (nb > skip_nb && nb > 0) { lo = base; hi = base + nb; }
     }
+    if (tid < QG) { s_vis[0][tid] = base; s_vis[1][tid] = nb; }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       lo = min(lo, __shfl_xor(lo, o, 64));
@@ -143,15 +155,6 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
       const int qw = qa + wid * QW + r2 / H;
       wv[rt][i] = qw < qe ? w[(static_cast<int64_t>(b) * L.S + qw) * H + r2 % H] : 0.f;
     }
-  }
-  // visibility of this lane's write queries
-  int vbase[QW], vnb[QW];
-#pragma unroll
-  for (int k = 0; k < QW; ++k) {
-    const int qw = qa + wid * QW + k;
-    vbase[k] = 0;
-    vnb[k] = 0;
-    if (qw < qe) visible_blocks(L, cu_blocks, c, b, qw, vbase[k], vnb[k]);
   }
 
   // chunk staging: thread owns GPT groups of 8 dims (block = grp / (D/8))
@@ -281,7 +284,8 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
         const bool writer = H >= 16 ? (g16 == 0) : (H == 8 ? (g16 == 2 * (k % 2)) : (g16 == k % 4));
         const int qw = qa + wid * QW + k;
         if (writer && qw < qe && jb < ce) {
-          const bool vis = jb >= vbase[k] && jb < vbase[k] + vnb[k];
+          const int vb = s_vis[0][wid * QW + k], vn = s_vis[1][wid * QW + k];
+          const bool vis = jb >= vb && jb < vb + vn;
           if (vis || write_invisible)
             otile[static_cast<int64_t>(qw - qa) * ostride + (jb - j0)] = vis ? scale * part[k] : -INFINITY;
         }
@@ -322,25 +326,26 @@ template <typename QT, int D>
 static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const uint16_t* kcs,
                           const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1, float* out,
                           int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
-  const int RT = ((sizeof(QT) == 4 || H <= 4) && D == 128 && H <= 32) ? 2 : ((64 % H == 0) ? 4 : 3);
-  const int QG = 4 * (16 * RT / H);
-  const int n_qg = (q1 - q0 + QG - 1) / QG;
   // block segments: about a quarter of the widest visible range, 256..2048 blocks
   const int span = j1 - j0;
   int seg = std::min(2048, std::max(256, (L.S / c) / 4));
   seg = (seg + kScoreChunk - 1) / kScoreChunk * kScoreChunk;
   const int n_seg = (span + seg - 1) / seg;
-  const dim3 grid(static_cast<unsigned>(n_qg * n_seg), static_cast<unsigned>(L.B));
+  // queries per workgroup: 4 waves x 16 RT / H
+  auto grid_for = [&](int rt, int h) {
+    const int qg = 4 * (16 * rt / h);
+    return dim3(static_cast<unsigned>(((q1 - q0 + qg - 1) / qg) * n_seg), static_cast<unsigned>(L.B));
+  };
 #define IRB_SCORE_CASE(HH)                                                                                   \
   case HH:                                                                                                   \
     if (kcs)                                                                                                 \
-      hipLaunchKernelGGL((score_kernel<QT, D, HH, true>), grid, dim3(256), 0, stream, L, q, w, kc, kcs,    \
-                         cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, seg, n_seg, write_invisible,     \
-                         skip_nb);                                                                           \
+      hipLaunchKernelGGL((score_kernel<QT, D, HH, true>), grid_for(score_rt<QT, D, HH, true>(), HH), dim3(256), \
+                         0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, seg,  \
+                         n_seg, write_invisible, skip_nb);                                                   \
     else                                                                                                     \
-      hipLaunchKernelGGL((score_kernel<QT, D, HH, false>), grid, dim3(256), 0, stream, L, q, w, kc, kcs,   \
-                         cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, seg, n_seg, write_invisible,     \
-                         skip_nb);                                                                           \
+      hipLaunchKernelGGL((score_kernel<QT, D, HH, false>), grid_for(score_rt<QT, D, HH, false>(), HH),      \
+                         dim3(256), 0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out,    \
+                         ostride, seg, n_seg, write_invisible, skip_nb);                                     \
     return 0;
   switch (H) {
     IRB_SCORE_CASE(4)
