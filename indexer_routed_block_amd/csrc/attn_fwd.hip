@@ -665,11 +665,26 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     for (int qi = wid; qi < BQ; qi += 4) {
       const int lo = s_lo[qi], hi = s_hi[qi];
       const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + qi) * a.L;
-      for (int e0 = lo; e0 < hi; e0 += 512) {
+      // with L a multiple of 4 the rows are 16-byte aligned: start at the aligned
+      // entry below lo and read two 16-byte words per lane (entries below lo are
+      // dropped by the range test)
+      const bool vec = (a.L & 3) == 0 && (reinterpret_cast<uintptr_t>(a.routes) & 15) == 0;
+      const int lo0 = vec ? (lo & ~3) : lo;
+      for (int e0 = lo0; e0 < hi; e0 += 512) {
         const int eb = e0 + 8 * lane;
         int ids[8];
+        if (vec && eb + 8 <= hi) {
+          const int4 u0 = *reinterpret_cast<const int4*>(r + eb);
+          const int4 u1 = *reinterpret_cast<const int4*>(r + eb + 4);
+          ids[0] = u0.x; ids[1] = u0.y; ids[2] = u0.z; ids[3] = u0.w;
+          ids[4] = u1.x; ids[5] = u1.y; ids[6] = u1.z; ids[7] = u1.w;
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ids[j] = (eb + j < hi) ? r[eb + j] : -1;
+          for (int j = 0; j < 8; ++j) ids[j] = (eb + j < hi) ? r[eb + j] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (eb + j < lo) ids[j] = -1;
         int word = -1;
         uint32_t bits = 0u;
 #pragma unroll
