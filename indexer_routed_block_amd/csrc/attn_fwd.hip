@@ -545,13 +545,16 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
                      float* __restrict__ delta, int n_qt, int thr_milli) {
   using T = uint16_t;
   constexpr int BQ = 128 / G;
-  constexpr int KS = D / 32, NDT = DV / 16;
+  constexpr int KS = D / 16;          // 16-dim k-steps of S^T = K Q^T
+  constexpr int NDT = DV / 32;        // 32-dim row tiles of O^T
+  constexpr int NG = KS;              // MFMA groups per step (one S and one O MFMA each)
+  static_assert(D == DV && 2 * NDT == NG, "one S and one O MFMA per group");
   // K and V tiles are row-major (one key per row, no padding), filled by
   // direct global-to-LDS loads (lane i of a load writes 16-byte slot i).  The
   // 16-byte chunks of row r sit XOR-swizzled: chunk c of a K row at slot
   // c ^ (r mod NCK), of a V row at slot c ^ (2 r mod NCV), so the K operand
   // reads of 16 rows and the V^T transpose reads of 4 rows hit distinct banks.
-  // Three buffers: the tile in use plus two in flight.
+  // Three slots, each holding one tile's K and V.
   constexpr int NCK = D / 8, NCV = DV / 8;            // 16-byte chunks per row
   constexpr int KBYTES = 32 * D * 2, VBYTES = 32 * DV * 2;
   constexpr int BUF = KBYTES + VBYTES;
@@ -565,7 +568,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   __shared__ int s_lo[BQ], s_hi[BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int g16 = lane >> 4, l16 = lane & 15;
+  const int h32 = lane >> 5, l32 = lane & 31;
   // consecutive workgroups take the KV heads of one query tile (one head per
   // XCD when 8 is a multiple of Hkv, keeping that head's K/V in its L2), and
   // query tiles run last-first: causal tiles late in the sequence span the
@@ -580,54 +583,229 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
 
   const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
   const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
-  bf16x8 qop[2][KS];
-  int colq[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int c = 32 * wid + 16 * ct + l16;
-    const int qi = c / G, h = c % G;
-    const int t = qa + qi;
-    colq[ct] = qi;
+  // this lane's column: (query, head) pair 32 wid + l32; MFMA layout
+  // (v_mfma_f32_32x32x16_bf16): A lane l = row l % 32, k 8 (l / 32) .. + 8;
+  // B lane l = column l % 32, same k; accumulator element i of lane l =
+  // row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32
+  const int col = 32 * wid + l32;
+  const int colq = col / G, colh = col % G;
+  bf16x8 qop[KS];
+  {
+    const int t = qa + colq;
     const bool ok = t < a.S_q;
     const T* qp = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(ok ? t : 0) * a.sq_t +
-                  static_cast<int64_t>(kvh * G + h) * a.sq_h + 8 * g16;
+                  static_cast<int64_t>(kvh * G + colh) * a.sq_h + 8 * h32;
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      qop[ct][s2] = *reinterpret_cast<const bf16x8*>(qp + 32 * s2);
-      if (!ok) zero8(qop[ct][s2]);
+      qop[s2] = *reinterpret_cast<const bf16x8*>(qp + 16 * s2);
+      if (!ok) zero8(qop[s2]);
     }
   }
-  f32x4 oacc[NDT][2];
+  f32x16 oacc[NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) { oacc[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f}; oacc[dt][1] = oacc[dt][0]; }
-  float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float m2 = -INFINITY, lsum = 0.f;
   const float sc2 = a.scale * kLog2e;
 
-  // tile loader: wave w issues NIK + NIV direct loads per tile; lane i of
-  // load n fills slot (w NIK + n) 64 + i of the K tile (same for V)
-  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+  // tile loader: wave w issues NIK (K) or NIV (V) direct loads per tile;
+  // lane i of load n fills slot (w NI + n) 64 + i.  The global address is the
+  // tile's first row (wave-uniform, scalar registers) plus a per-lane 32-bit
+  // byte offset fixed for the whole kernel; only a tile reaching past the
+  // last key recomputes it with clamped rows.
+  const int wv = __builtin_amdgcn_readfirstlane(wid);
+  uint32_t koff[NIK], voff[NIV];
+#pragma unroll
+  for (int n = 0; n < NIK; ++n) {
+    const int slot = (wv * NIK + n) * 64 + lane;
+    const int r = slot / NCK, sc = slot % NCK;
+    koff[n] = static_cast<uint32_t>(r * a.sk_t + 8 * (sc ^ (r & (NCK - 1)))) * 2u;
+  }
+#pragma unroll
+  for (int n = 0; n < NIV; ++n) {
+    const int slot = (wv * NIV + n) * 64 + lane;
+    const int r = slot / NCV, sc = slot % NCV;
+    voff[n] = static_cast<uint32_t>(r * a.sv_t + 8 * (sc ^ ((2 * r) & (NCV - 1)))) * 2u;
+  }
+  const uint32_t lds0 = lds_addr(raw);
+  // K rows of key tile kt into slot `buf` (kV = false) or its V rows (kV = true)
+  auto issue = [&](int kt, auto bufc, auto vc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    constexpr bool kV = decltype(vc)::value;
+    constexpr int NI = kV ? NIV : NIK, NC = kV ? NCV : NCK;
     kt = __builtin_amdgcn_readfirstlane(kt);
-    char* base = raw + buf * BUF;
+    const int key0 = kt * 32;
+    const T* src = kV ? vbase + static_cast<int64_t>(key0) * a.sv_t : kbase + static_cast<int64_t>(key0) * a.sk_t;
+    const int stride = kV ? a.sv_t : a.sk_t;
+    const int lim = a.S_k - 1 - key0;
+    const uint32_t ld = lds0 + buf * BUF + (kV ? KBYTES : 0) + wv * NI * 1024;
+    if (lim >= 31) {
 #pragma unroll
-    for (int n = 0; n < NIK; ++n) {
-      const int slot = (wid * NIK + n) * 64 + lane;
-      const int r = slot / NCK, sc = slot % NCK;
-      const int key = min(kt * 32 + r, a.S_k - 1);
-      const T* src = kbase + static_cast<int64_t>(key) * a.sk_t + 8 * (sc ^ (r & (NCK - 1)));
-      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(base + (wid * NIK + n) * 1024)));
-    }
+      for (int n = 0; n < NI; ++n) lds_dma16_s(src, kV ? voff[n] : koff[n], ld + n * 1024);
+    } else {
 #pragma unroll
-    for (int n = 0; n < NIV; ++n) {
-      const int slot = (wid * NIV + n) * 64 + lane;
-      const int r = slot / NCV, sc = slot % NCV;
-      const int key = min(kt * 32 + r, a.S_k - 1);
-      const T* src = vbase + static_cast<int64_t>(key) * a.sv_t + 8 * (sc ^ ((2 * r) & (NCV - 1)));
-      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(base + KBYTES + (wid * NIV + n) * 1024)));
+      for (int n = 0; n < NI; ++n) {
+        const int slot = (wv * NI + n) * 64 + lane;
+        const int r = slot / NC, sc = slot % NC;
+        const int sw = kV ? (sc ^ ((2 * r) & (NC - 1))) : (sc ^ (r & (NC - 1)));
+        lds_dma16_s(src, static_cast<uint32_t>(min(r, lim) * stride + 8 * sw) * 2u, ld + n * 1024);
+      }
     }
   };
-  // per-lane LDS offsets (halfwords) of the K operand (row 16 kk + l16, chunk 4 s2 + g16)
-  // and of the V^T transpose reads (key 4 g16 + l16 / 4 [+ 16], dims 16 dt + 4 (l16 % 4))
-  const int vk0 = 4 * g16 + (l16 >> 2);
+  using KSide = std::integral_constant<bool, false>;
+  using VSide = std::integral_constant<bool, true>;
+  // per-lane LDS byte offsets inside a slot.  K operand of k-step s2: row
+  // l32, chunk 2 s2 + h32.  V^T operand of dim tile dt: lanes of a 16-lane
+  // row address keys r0 + (lane % 16) / 4 and dims 32 dt + 16 ((lane / 16) % 2)
+  // + 4 (lane % 4), r0 = 4 h32 (+ 8 for the upper four k of a step, + 16
+  // for the second step: whole rows, same swizzle, so immediate offsets)
+  uint32_t kofs[KS], vofs[NDT];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) kofs[s2] = static_cast<uint32_t>(l32 * D + 8 * ((2 * s2 + h32) ^ (l32 & (NCK - 1)))) * 2u;
+  {
+    const int s16 = lane & 15, g2 = (lane >> 4) & 1;
+    const int vr = 4 * h32 + (s16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int vc = 4 * dt + 2 * g2 + ((s16 & 3) >> 1);
+      vofs[dt] = static_cast<uint32_t>(vr * DV + 8 * (vc ^ ((2 * vr) & (NCV - 1))) + 4 * (s16 & 1)) * 2u;
+    }
+  }
+  // S^T of the key tile in the slot at byte offset kslot
+  auto scores = [&](f32x16& st, uint32_t kslot) __attribute__((always_inline)) {
+    const char* kb = raw + kslot;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kb + kofs[s2]), qop[s2], st, 0, 0, 0);
+  };
+  // V^T operand of dim tile dt, k-step t2 (keys 16 t2 + 4 h32 + {0..3, 8..11}),
+  // from the V rows of the slot at byte offset vslot
+  auto vread = [&](int dt, int t2, uint32_t vslot) __attribute__((always_inline)) {
+    const char* vt = raw + vslot + KBYTES + vofs[dt] + t2 * 16 * DV * 2;
+    const v4s v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vt));
+    const v4s v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vt + 8 * DV * 2));
+    return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  };
+  // O^T += V^T P^T for the V rows in slot vslot (both k-steps of every dim tile)
+  auto accumulate = [&](const bf16x8 (&pp)[2], uint32_t vslot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(dt, t2, vslot), pp[t2], oacc[dt], 0, 0, 0);
+  };
+
+  // Software pipeline over the key tiles of a segment (n of them): step i
+  // forms S^T of tile i + 1, the softmax of tile i and O^T += V^T P^T of
+  // tile i - 1, three independent streams interleaved group by group (one S
+  // MFMA, one O MFMA and a slice of the softmax arithmetic per group), so the
+  // MFMAs of a wavefront run under its own VALU work.  Tile t's K rows sit in
+  // slot t % 3 and its V rows in the V half of slot t % 3.  Step i first
+  // waits for K(i + 1) and V(i - 1), then the barrier frees K slot i % 3
+  // (read by S(i) in step i - 1) and V slot (i + 1) % 3 (read by step i - 1),
+  // which receive K(i + 3) and V(i + 1).  Loads are issued in the order
+  // K(0) K(1) K(2) V(0) | K(3) V(1) | K(4) V(2) | ..., so "everything but
+  // the batch of step i - 1" is one vmcnt.
+  f32x16 scur;
+  bf16x8 pprev[2];
+  auto step = [&](auto cc, auto pvc, int i, int ntiles, int seg0) __attribute__((always_inline)) {
+    constexpr int C = decltype(cc)::value;      // i % 3
+    constexpr bool kPV = decltype(pvc)::value;  // i > 0
+    if (i + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIK + NIV>());
+    else __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIV>());
+    bare_barrier();
+    if (i + 3 < ntiles) issue(seg0 + tiles[i + 3], std::integral_constant<int, C>{}, KSide{});
+    if (i + 1 < ntiles) issue(seg0 + tiles[i + 1], std::integral_constant<int, (C + 1) % 3>{}, VSide{});
+    const int ktl = tiles[i];
+    constexpr uint32_t kslot = ((C + 1) % 3) * BUF, vslot = ((C + 2) % 3) * BUF;
+    const char* kb = raw + kslot;
+    const uint32_t mw = mask[colq][ktl] >> (4 * h32);
+    // Masked online softmax of tile i in this lane's column, in eight pieces
+    // spread over the MFMA groups: 0/1 mask select of elements 0-7 / 8-15
+    // (an entry whose mask bit is clear becomes -inf by a bit select with the
+    // sign-extended bit), 2 the in-lane max, 3 the max across the two lane
+    // halves and the update of the reference max, 4-7 the exponentials.  The
+    // reference max m2 only moves when a score exceeds it by more than kLazy
+    // (log2 units), so weights stay <= 2^kLazy and the rescale of the
+    // accumulators is rare; the result is exact after normalisation by lsum.
+    // All branch-free, so the step is one scheduling region.
+    constexpr float kLazy = 8.f;
+    float xr[16], p[16];
+    float cm = -INFINITY, alpha = 1.f, nm = 0.f;
+    bool rescale = false;
+    auto piece = [&](int pc) __attribute__((always_inline)) {
+      if (pc < 2) {
+#pragma unroll
+        for (int i = 8 * pc; i < 8 * pc + 8; ++i) {
+          const int bit = 8 * (i >> 2) + (i & 3);
+          const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(mw << (31 - bit)) >> 31);
+          xr[i] = __uint_as_float((__float_as_uint(scur[i]) & m) | (~m & 0xff800000u));
+        }
+      } else if (pc == 2) {
+        const float x0 = max3_raw(xr[0], xr[1], xr[2]), x1 = max3_raw(xr[3], xr[4], xr[5]);
+        const float x2 = max3_raw(xr[6], xr[7], xr[8]), x3 = max3_raw(xr[9], xr[10], xr[11]);
+        const float x4 = max3_raw(xr[12], xr[13], xr[14]);
+        cm = max_raw(max3_raw(x0, x1, x2), max3_raw(x3, x4, xr[15]));
+      } else if (pc == 3) {
+        const uint32_t u = __float_as_uint(cm);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        const float cmax = max_raw(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc2;
+        const bool up = cmax > m2 + kLazy;
+        const float ea = fast_exp2(m2 - cmax);
+        alpha = up ? ea : 1.f;
+        m2 = up ? cmax : m2;
+        rescale = up;
+        nm = (m2 == -INFINITY) ? 0.f : -m2;
+      } else {
+#pragma unroll
+        for (int i = 4 * (pc - 4); i < 4 * (pc - 4) + 4; ++i) p[i] = fast_exp2(fmaf(xr[i], sc2, nm));
+      }
+    };
+    // group g: S MFMA of k-step g for tile i + 1 (past the last tile: a stale
+    // slot, result unused), O MFMA (dim tile g / 2, k-step g % 2) for tile
+    // i - 1, softmax pieces; LDS operands are read one group ahead
+    f32x16 snext;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) snext[e] = 0.f;
+    bf16x8 kop[2], vop[2];
+    kop[0] = *reinterpret_cast<const bf16x8*>(kb + kofs[0]);
+    if constexpr (kPV) vop[0] = vread(0, 0, vslot);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) {
+        kop[(g + 1) & 1] = *reinterpret_cast<const bf16x8*>(kb + kofs[g + 1]);
+        if constexpr (kPV) vop[(g + 1) & 1] = vread((g + 1) >> 1, (g + 1) & 1, vslot);
+      }
+      snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[g & 1], qop[g], snext, 0, 0, 0);
+      if constexpr (kPV) oacc[g >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[g & 1], pprev[g & 1], oacc[g >> 1], 0, 0, 0);
+#pragma unroll
+      for (int pc = g * 8 / NG; pc < (g + 1) * 8 / NG; ++pc) piece(pc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float ps = 0.f;
+    {
+      float s0 = (p[0] + p[1]) + (p[2] + p[3]), s1 = (p[4] + p[5]) + (p[6] + p[7]);
+      float s2v = (p[8] + p[9]) + (p[10] + p[11]), s3 = (p[12] + p[13]) + (p[14] + p[15]);
+      ps = (s0 + s1) + (s2v + s3);
+    }
+    lsum = lsum * alpha + ps;
+    bf16x8 pcur[2];
+    pcur[0] = pack_bf16x8(p);
+    pcur[1] = pack_bf16x8(p + 8);
+    // the rescale by alpha(i) follows the accumulation of tile i - 1
+    if (__ballot(rescale)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+    }
+    scur = snext;
+    pprev[0] = pcur[0];
+    pprev[1] = pcur[1];
+  };
 
   if (tid < BQ) cursor[tid] = 0;
   const int kt_first = ts.kmin >> 5, kt_last = ts.kmax >> 5;
@@ -720,119 +898,64 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     __syncthreads();
     const int ntiles = s_ntiles;
     if (ntiles == 0) continue;
-    // key tile it sits in buffer it % 3; tiles it + 1 and it + 2 are in flight
-    issue(seg0 + tiles[0], 0);
-    if (ntiles > 1) issue(seg0 + tiles[1], 1);
-    for (int it = 0; it < ntiles; ++it) {
-      const int buf = it % 3;
-      const int ktl = tiles[it];
-      // this wave's loads of tile it are done (those of tile it + 1 may not be);
-      // the barrier makes every wave's part visible and frees buffer (it + 2) % 3
-      if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIK + NIV>());
-      else __builtin_amdgcn_s_waitcnt(kVmWaitTile<0>());
-      bare_barrier();
-      if (it + 2 < ntiles) issue(seg0 + tiles[it + 2], (it + 2) % 3);
-      const T* kb = reinterpret_cast<const T*>(raw + buf * BUF);
-      const T* vt = reinterpret_cast<const T*>(raw + buf * BUF + KBYTES);
-      f32x4 st[2][2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) { st[kk][0] = f32x4{0.f, 0.f, 0.f, 0.f}; st[kk][1] = st[kk][0]; }
-#pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int kr = 16 * kk + l16;
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + kr * D + 8 * ((4 * s2 + g16) ^ (kr & (NCK - 1))));
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-            st[kk][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ct][s2], st[kk][ct], 0, 0, 0);
-        }
-      }
-      // online softmax per column.  The reference max m2 only moves when a
-      // score exceeds it by more than kLazy (log2 units), so weights stay
-      // <= 2^kLazy and the rescale of the accumulators is rare; the result is
-      // exact after normalisation by lsum.
-      constexpr float kLazy = 8.f;
-      bf16x8 pop[2];
-      float alpha[2];
-      bool rescale = false;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const uint32_t mw = mask[colq[ct]][ktl] >> (4 * g16);
-        float xr[8];
-        float cm = -INFINITY;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            xr[4 * kk + i] = ((mw >> (16 * kk + i)) & 1u) ? st[kk][ct][i] : -INFINITY;
-            cm = fmaxf(cm, xr[4 * kk + i]);
-          }
-        cm = row4_max(cm);
-        const float cmax = cm * sc2;
-        alpha[ct] = 1.f;
-        if (cmax > m2[ct] + kLazy) {
-          alpha[ct] = fast_exp2(m2[ct] - cmax);
-          m2[ct] = cmax;
-          rescale = true;
-        }
-        const float nm = (m2[ct] == -INFINITY) ? 0.f : -m2[ct];
-        float p[8], ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { p[i] = fast_exp2(fmaf(xr[i], sc2, nm)); ps += p[i]; }
-        lsum[ct] = lsum[ct] * alpha[ct] + ps;
-        pop[ct] = pack_bf16x8(p);
-      }
-      if (__ballot(rescale)) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) oacc[dt][ct][i] *= alpha[ct];
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int vc = 2 * dt + ((l16 & 3) >> 1), vw = 4 * (l16 & 1);
-        const v4s v0 = lds_read_tr(vt + vk0 * DV + 8 * (vc ^ ((2 * vk0) & (NCV - 1))) + vw);
-        const v4s v1 = lds_read_tr(vt + (vk0 + 16) * DV + 8 * (vc ^ ((2 * (vk0 + 16)) & (NCV - 1))) + vw);
-        const bf16x8 vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          oacc[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], oacc[dt][ct], 0, 0, 0);
-      }
+    // prologue: K(0) K(1) K(2) V(0), then S(0)
+    issue(seg0 + tiles[0], std::integral_constant<int, 0>{}, KSide{});
+    if (ntiles > 1) issue(seg0 + tiles[1], std::integral_constant<int, 1>{}, KSide{});
+    if (ntiles > 2) issue(seg0 + tiles[2], std::integral_constant<int, 2>{}, KSide{});
+    issue(seg0 + tiles[0], std::integral_constant<int, 0>{}, VSide{});
+    if (ntiles > 2) __builtin_amdgcn_s_waitcnt(kVmWaitTile<2 * NIK + NIV>());
+    else if (ntiles > 1) __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIK + NIV>());
+    else __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIV>());
+    bare_barrier();
+    scores(scur, 0);
+    step(std::integral_constant<int, 0>{}, std::false_type{}, 0, ntiles, seg0);
+    // steps 1 .. n - 1, unrolled by three so that every slot offset is a constant
+    for (int i = 1; i < ntiles; i += 3) {
+      step(std::integral_constant<int, 1>{}, std::true_type{}, i, ntiles, seg0);
+      if (i + 1 < ntiles) step(std::integral_constant<int, 2>{}, std::true_type{}, i + 1, ntiles, seg0);
+      if (i + 2 < ntiles) step(std::integral_constant<int, 0>{}, std::true_type{}, i + 2, ntiles, seg0);
     }
+    // drain: O^T += V^T P^T of the last tile
+    __builtin_amdgcn_s_waitcnt(kVmWaitTile<0>());
+    bare_barrier();
+    accumulate(pprev, static_cast<uint32_t>((ntiles - 1) % 3) * BUF);
   }
 
-  // ---- epilogue
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int c = 32 * wid + 16 * ct + l16;
-    const int qi = c / G, h = c % G;
-    const int t = qa + qi;
-    const float ltot = row4_sum(lsum[ct]);
+  // ---- epilogue: this lane holds dims 32 dt + 8 j + 4 h32 + {0..3} of its
+  // column; the two lane halves together hold the column's row sum
+  {
+    const int t = qa + colq;
+    const uint32_t u = __float_as_uint(lsum);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (kDelta) {
       float part = 0.f;
       if (t < a.S_q) {
-        const T* dp = dout + ((static_cast<int64_t>(b) * a.S_q + t) * a.Hq + kvh * G + h) * DV + 4 * g16;
+        const T* dp = dout + ((static_cast<int64_t>(b) * a.S_q + t) * a.Hq + kvh * G + colh) * DV + 4 * h32;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part += oacc[dt][ct][i] * inv * bf16_to_f32(dp[dt * 16 + i]);
+          for (int e = 0; e < 16; ++e)
+            part += oacc[dt][e] * inv * bf16_to_f32(dp[32 * dt + 8 * (e >> 2) + (e & 3)]);
       }
-      part = row4_sum(part);
-      if (t < a.S_q && g16 == 0) delta[(static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + t] = part;
+      const uint32_t pu = __float_as_uint(part);
+      const auto ps = __builtin_amdgcn_permlane32_swap(pu, pu, false, false);
+      part = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
+      if (t < a.S_q && h32 == 0) delta[(static_cast<int64_t>(b) * a.Hq + kvh * G + colh) * a.S_q + t] = part;
     } else if (t < a.S_q) {
       const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
-      T* op = out + (row * a.Hq + kvh * G + h) * DV + 4 * g16;
+      T* op = out + (row * a.Hq + kvh * G + colh) * DV + 4 * h32;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const float v[4] = {oacc[dt][ct][0] * inv, oacc[dt][ct][1] * inv, oacc[dt][ct][2] * inv, oacc[dt][ct][3] * inv};
-        store4(op + dt * 16, v);
-      }
-      if (g16 == 0)
-        lse[(static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + t] = ltot > 0.f ? (m2[ct] + log2f(ltot)) * kLn2 : -INFINITY;
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v[4] = {oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv, oacc[dt][4 * j + 2] * inv,
+                              oacc[dt][4 * j + 3] * inv};
+          store4(op + 32 * dt + 8 * j, v);
+        }
+      if (h32 == 0)
+        lse[(static_cast<int64_t>(b) * a.Hq + kvh * G + colh) * a.S_q + t] = ltot > 0.f ? (m2 + log2f(ltot)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -865,7 +988,9 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
   const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
   int tile_bq = 0;    // > 0: the gather kernel skips the query tiles the tile kernel takes
   if constexpr (sizeof(T) == 2 && (D == 64 || D == 128) && D == DV) {
-    if (tile_thr_milli() <= 1000 && (G == 4 || G == 8 || G == 16)) {
+    // the tile kernel addresses a 32-key tile by 32-bit byte offsets from its first row
+    const bool small_strides = static_cast<int64_t>(a.sk_t > a.sv_t ? a.sk_t : a.sv_t) * 64 < (int64_t{1} << 31);
+    if (tile_thr_milli() <= 1000 && small_strides && (G == 4 || G == 8 || G == 16)) {
       if (G == 4) launch_tile<D, DV, 4, kDelta>(a, out, lse, dout, delta, stream);
       if (G == 8) launch_tile<D, DV, 8, kDelta>(a, out, lse, dout, delta, stream);
       if (G == 16) launch_tile<D, DV, 16, kDelta>(a, out, lse, dout, delta, stream);

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <limits>
+#include <type_traits>
 
 #define IRB_DEV __device__ __forceinline__
 
@@ -16,6 +17,7 @@ constexpr int kWave = 64;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;   // MFMA A/B operand
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;    // 16x16 accumulator
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;  // 32x32 accumulator
 
 // ---------------------------------------------------------------- bf16 <-> f32
 IRB_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
@@ -38,10 +40,12 @@ IRB_DEV void split_bf16(float f, uint16_t& hi, uint16_t& lo) {
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2n;
 
-// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
+// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest
+// even; written out so the pair is never split into two conversions)
 IRB_DEV uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2n v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-  return __builtin_bit_cast(uint32_t, v);
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 // 8 floats -> MFMA operand
 IRB_DEV bf16x8 pack_bf16x8(const float* f) {
@@ -135,6 +139,12 @@ constexpr int kVmWaitTile() {
 IRB_DEV void lds_dma16(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
 }
+// Same with a wave-uniform base address in scalar registers plus a per-lane
+// 32-bit unsigned byte offset (the global "saddr" form): the base changes per
+// tile in scalar registers while the lane offsets stay in place.
+IRB_DEV void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+}
 IRB_DEV uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
@@ -159,13 +169,26 @@ IRB_DEV v4s lds_read_tr(const uint16_t* p) {
 // l^48) on the VALU: with both operands equal, v_permlane16_swap /
 // v_permlane32_swap return {x[l], x[l^16]} / {x[l], x[l^32]} in some order,
 // so combining the pair gives the butterfly step without an LDS round trip.
+// v_max_f32 without the quieting of its inputs that fmaxf adds for values the
+// compiler cannot prove canonical (lane-permute results); NaN inputs are not
+// expected here
+IRB_DEV float max_raw(float x, float y) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+IRB_DEV float max3_raw(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
 IRB_DEV float row4_max(float v) {
   const uint32_t u = __float_as_uint(v);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t w = __float_as_uint(v);
   const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 IRB_DEV float row4_sum(float v) {
   const uint32_t u = __float_as_uint(v);

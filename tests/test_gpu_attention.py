@@ -5,6 +5,7 @@ Tolerances: bf16 outputs and gradients mean-abs <= 5e-3 and per element
 fp32 inputs max-abs <= 1e-4; lse within 1e-3 (bf16) / 1e-4 (fp32) absolute.
 """
 import math
+import types
 
 import numpy as np
 import pytest
@@ -102,6 +103,21 @@ def test_gqa_bf16_batched_and_strided_q():
     qv = big[:, :, 1:1 + wl.Hq]
     assert not qv.is_contiguous()
     _run_fwd_bwd(wl, x, routes, lens, 0.11, True, q_view=qv)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 4, 64), (16, 1, 64), (16, 2, 64), (8, 2, 128), (32, 2, 128)])
+def test_gqa_bf16_head_groups_and_widths_fwd_bwd(Hq, Hkv, D):
+    """Every (group size, head width) the query-tile and key-tile kernels are built for (G = 4, 8, 16; D = 64, 128)."""
+    banner(f"attn bf16 Hq={Hq} Hkv={Hkv} D={D} S=300")
+    rng = np.random.default_rng(1000 + 7 * Hq + 3 * Hkv + D)
+    S = 300
+
+    def nrm(*shape):
+        return synth.to_bf16_values(rng.standard_normal(shape).astype(np.float32))
+
+    x = {"q": nrm(1, S, Hq, D), "k": nrm(1, S, Hkv, D), "v": nrm(1, S, Hkv, D), "dO": nrm(1, S, Hq, D)}
+    routes, lens = _random_routes(S + D + Hq, 1, S, 96, empty_rows=[(0, 7)])
+    _run_fwd_bwd(types.SimpleNamespace(dtype="bf16"), x, routes, lens, 1.0 / math.sqrt(D), True)
 
 
 @pytest.mark.parametrize("T,width", [(512, 256), (300, 64)])
