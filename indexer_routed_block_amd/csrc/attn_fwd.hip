@@ -478,6 +478,7 @@ constexpr int kSegTiles = 256;   // 32-key tiles per mask segment (8192 keys)
 struct TileStats {
   bool dense;
   int kmin, kmax;
+  int n_lane, last_lane;   // lane q < BQ: route length of query qa + q and its last entry
 };
 
 // Evaluated by a whole wavefront (uniform result).  BQ <= 64.
@@ -496,6 +497,7 @@ IRB_DEV TileStats tile_stats_wave(const AttnArgs& a, int b, int qa, int BQ, int 
       total = n;
     }
   }
+  const int lane_n = total, lane_last = kmax;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     kmin = min(kmin, __shfl_xor(kmin, o, 64));
@@ -508,6 +510,8 @@ IRB_DEV TileStats tile_stats_wave(const AttnArgs& a, int b, int qa, int BQ, int 
   st.kmax = min(kmax, a.S_k - 1);
   const int64_t span = st.kmax >= st.kmin ? static_cast<int64_t>(st.kmax - st.kmin + 1) : 0;
   st.dense = total > 0 && span > 0 && static_cast<int64_t>(total) * 1000 >= static_cast<int64_t>(thr_milli) * valid * span;
+  st.n_lane = lane_n;
+  st.last_lane = lane_last;
   return st;
 }
 
@@ -815,70 +819,100 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     __syncthreads();
     for (int i = tid; i < BQ * kSegTiles; i += 256) (&mask[0][0])[i] = 0u;
     __syncthreads();
-    // route masks of this segment.  Entry ranges [lo, hi) per query: lo is the
-    // cursor left by the previous segment, hi a binary search (one lane per
-    // query, in parallel); then all 256 threads read consecutive entries with
-    // independent loads, each wavefront OR-combines runs of equal mask words
-    // (entries are sorted) and one lane per run does the LDS atomic.
+    // route masks of this segment.  Entry ranges [lo, hi) per query (one lane
+    // per query, in parallel): lo is the cursor left by the previous segment,
+    // hi the row end when the row's last entry falls in this segment, else a
+    // binary search.
     if (wid == 0 && lane < BQ) {
       const int t = qa + lane;
       int lo = cursor[lane], hi = lo;
       if (t < a.S_q) {
         const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
-        const int n = max(0, min(a.lens[row], a.L));
+        const int n = ts.n_lane;             // min(lens, L) (0 past S_q)
         const int32_t* r = a.routes + row * a.L;
-        int l1 = lo, h1 = n;
-        while (l1 < h1) { const int m = (l1 + h1) >> 1; if (r[m] < key1) l1 = m + 1; else h1 = m; }
-        hi = l1;
+        // a row's last segment holds all its remaining entries (its last
+        // entry, known from the tile statistics, decides), otherwise a
+        // binary search
+        if (n <= lo || ts.last_lane < key1) {
+          hi = max(n, lo);
+        } else {
+          int l1 = lo, h1 = n;
+          while (l1 < h1) { const int m = (l1 + h1) >> 1; if (r[m] < key1) l1 = m + 1; else h1 = m; }
+          hi = l1;
+        }
       }
       s_lo[lane] = lo;
       s_hi[lane] = hi;
       cursor[lane] = hi;
     }
     __syncthreads();
-    // wave w takes queries w, w + 4, ...; each lane ORs 8 consecutive entries
-    // of a 512-entry chunk into a word locally (entries are sorted, so equal
-    // words are adjacent) and issues an LDS atomic OR only when the word
-    // changes; the 8 loads of a lane are in flight together
-    for (int qi = wid; qi < BQ; qi += 4) {
-      const int lo = s_lo[qi], hi = s_hi[qi];
-      const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + qi) * a.L;
-      // with L a multiple of 4 the rows are 16-byte aligned: start at the aligned
-      // entry below lo and read two 16-byte words per lane (entries below lo are
-      // dropped by the range test)
-      const bool vec = (a.L & 3) == 0 && (reinterpret_cast<uintptr_t>(a.routes) & 15) == 0;
-      const int lo0 = vec ? (lo & ~3) : lo;
-      for (int e0 = lo0; e0 < hi; e0 += 512) {
-        const int eb = e0 + 8 * lane;
-        int ids[8];
-        if (vec && eb + 8 <= hi) {
-          const int4 u0 = *reinterpret_cast<const int4*>(r + eb);
-          const int4 u1 = *reinterpret_cast<const int4*>(r + eb + 4);
-          ids[0] = u0.x; ids[1] = u0.y; ids[2] = u0.z; ids[3] = u0.w;
-          ids[4] = u1.x; ids[5] = u1.y; ids[6] = u1.z; ids[7] = u1.w;
-        } else {
+    // wave w takes queries w, w + 4, ...; each lane takes 8 consecutive
+    // entries of a 512-entry chunk and ORs each entry's bit into its mask
+    // word with an LDS atomic, branch-free (an entry outside [lo, hi) or the
+    // segment ORs 0 into word 0)
+    auto or_entries = [&](int qi, int eb, int lo, int hi, const int (&ids)[8]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) ids[j] = (eb + j < hi) ? r[eb + j] : -1;
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int id = ids[j];
+        const bool ok = eb + j >= lo && eb + j < hi && id >= key0 && id < key1 && id < a.S_k;
+        const int rel = ok ? id - key0 : 0;
+        atomicOr(&mask[qi][rel >> 5], ok ? 1u << (rel & 31) : 0u);
+      }
+    };
+    if ((a.L & 3) == 0 && a.L >= 4 && (reinterpret_cast<uintptr_t>(a.routes) & 15) == 0) {
+      // rows 16-byte aligned: the wave's (query, chunk) items are staged NI at
+      // a time in its quarter of the (idle) K/V slots by direct global-to-LDS
+      // loads, so their latencies overlap; a chunk starts at the aligned entry
+      // below lo, and 16-byte groups past the row end are clamped to its last
+      // group (those entries lie beyond hi and are dropped)
+      constexpr int QB = 3 * BUF / 4, NI = QB / 2048;
+      static_assert(NI >= 1, "route staging");
+      const uint32_t wl = lds0 + wv * QB;
+      const char* wb = raw + wid * QB;
+      int cq = wv, ce = 0;
+      if (cq < BQ) ce = __builtin_amdgcn_readfirstlane(s_lo[cq] & ~3);
+      while (cq < BQ) {
+        int bq[NI], be[NI];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (eb + j < lo) ids[j] = -1;
-        int word = -1;
-        uint32_t bits = 0u;
+        for (int j = 0; j < NI; ++j) {
+          while (cq < BQ && ce >= s_hi[cq]) {
+            cq += 4;
+            if (cq < BQ) ce = __builtin_amdgcn_readfirstlane(s_lo[cq] & ~3);
+          }
+          bq[j] = cq;
+          be[j] = ce;
+          if (cq < BQ) {
+            const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + cq) * a.L;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int id = ids[j];
-          if (id >= key0 && id < key1 && id < a.S_k) {
-            const int w = (id - key0) >> 5;
-            if (w != word) {
-              if (word >= 0) atomicOr(&mask[qi][word], bits);
-              word = w;
-              bits = 0u;
-            }
-            bits |= 1u << ((id - key0) & 31);
+            for (int h = 0; h < 2; ++h)
+              lds_dma16(r + min(ce + 256 * h + 4 * lane, a.L - 4), wl + j * 2048 + h * 1024);
+            ce += 512;
           }
         }
-        if (word >= 0) atomicOr(&mask[qi][word], bits);
+        __builtin_amdgcn_s_waitcnt(kVmWaitTile<0>());
+        asm volatile("" : : : "memory");
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          if (bq[j] >= BQ) continue;
+          const int4 u0 = *reinterpret_cast<const int4*>(wb + j * 2048 + 32 * lane);
+          const int4 u1 = *reinterpret_cast<const int4*>(wb + j * 2048 + 32 * lane + 16);
+          const int ids[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+          or_entries(bq[j], be[j] + 8 * lane, s_lo[bq[j]], s_hi[bq[j]], ids);
+        }
+        // the next round overwrites this wave's staging area
+        wave_lds_sync();
+      }
+    } else {
+      for (int qi = wid; qi < BQ; qi += 4) {
+        const int lo = s_lo[qi], hi = s_hi[qi];
+        const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + qi) * a.L;
+        for (int e0 = lo; e0 < hi; e0 += 512) {
+          const int eb = e0 + 8 * lane;
+          int ids[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ids[j] = (eb + j < hi) ? r[eb + j] : -1;
+          or_entries(qi, eb, lo, hi, ids);
+        }
       }
     }
     // compact list of the key tiles any query routes to
