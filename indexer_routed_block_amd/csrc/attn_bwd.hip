@@ -745,6 +745,34 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   const int tr_off_q = (4 * g16 + (l16 >> 2)) * LQ + 4 * (l16 & 3);
   const int tr_off_o = (4 * g16 + (l16 >> 2)) * LO + 4 * (l16 & 3);
 
+  // Hit ids of a batch (hb-th 32-row part of the hits from e0 on): hit_t of
+  // this lane's two A rows (16 rt + l16), and for each row tile rt hit_t /
+  // hit_m of the query holding the lane's softmax rows 16 rt + 4 g16 .. + 3
+  // (with Gp >= 4 those four rows belong to one query).  They are loaded one
+  // batch ahead, so a batch waits for one round of loads: its q / dO rows
+  // together with its lse and Delta values.
+  struct Ids {
+    int ta[2], ts[2];
+    uint32_t tm[2];
+  };
+  auto fetch = [&](int64_t e0_, int hb_, Ids& d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r = 16 * rt + l16;
+      const int slot = Gp <= 32 ? r / Gp : 0;
+      const int h = Gp <= 32 ? r % Gp : hb_ * 32 + r;
+      const int64_t e = e0_ + slot;
+      int t = (e < h1 && h < G) ? hit_t[e] : -1;
+      d.ta[rt] = t < a.S_q ? t : -1;
+      const int rs = 16 * rt + 4 * g16;
+      const int64_t es = e0_ + (Gp <= 32 ? rs / Gp : 0);
+      int ts = es < h1 ? hit_t[es] : -1;
+      d.ts[rt] = ts < a.S_q ? ts : -1;
+      d.tm[rt] = es < h1 ? hit_m[es] : 0u;
+    }
+  };
+  Ids cur;
+  if (h0 < h1) fetch(h0, 0, cur);
   for (int64_t e0 = h0; e0 < h1; e0 += qpb) {
     for (int hb = 0; hb < bpq; ++hb) {
       // rows r = 16 rt + l16 of S and dP: Q and dO rows in the A layout
@@ -752,11 +780,8 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int r = 16 * rt + l16;
-        const int slot = Gp <= 32 ? r / Gp : 0;
         const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
-        const int64_t e = e0 + slot;
-        int t = (e < h1 && h < G) ? hit_t[e] : -1;
-        if (t >= a.S_q) t = -1;
+        const int t = cur.ta[rt];
         const int hh = kvh * G + (h < G ? h : 0);
         const int tt = t >= 0 ? t : 0;
         const uint16_t* qp = qg + b * a.sq_b + static_cast<int64_t>(tt) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
@@ -771,6 +796,29 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
           oa[rt][s] = *reinterpret_cast<const bf16x8*>(op + 32 * s);
           if (t < 0) bzero8(oa[rt][s]);
         }
+      }
+      // lse and Delta of the softmax rows 16 rt + 4 g16 + i (index 0 stands
+      // in for rows without a query; their weights are zeroed below)
+      float lsv[2][4], dlv[2][4];
+      bool rok[2][4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g16 + i;
+          const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
+          const int te = cur.ts[rt];
+          rok[rt][i] = te >= 0 && h < G && ((cur.tm[rt] >> l16) & 1u);
+          const int64_t li = rok[rt][i] ? (static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + te : 0;
+          lsv[rt][i] = args.lse[li];
+          dlv[rt][i] = delta[li];
+        }
+      // the next batch's ids
+      Ids nxt;
+      {
+        const int64_t ne0 = hb + 1 < bpq ? e0 : e0 + qpb;
+        const int nhb = hb + 1 < bpq ? hb + 1 : 0;
+        if (ne0 < h1) fetch(ne0, nhb, nxt);
       }
       // row-major copies for the transposed operands
 #pragma unroll
@@ -798,19 +846,9 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g16 + i;
-          const int slot = Gp <= 32 ? r / Gp : 0;
-          const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
-          const int64_t e = e0 + slot;
-          float pv = 0.f, dv = 0.f;
-          const int te = (e < h1 && h < G) ? hit_t[e] : -1;
-          if (te >= 0 && te < a.S_q && ((hit_m[e] >> l16) & 1u)) {
-            const int64_t li = (static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + te;
-            pv = exp2f(sacc[rt][i] * sc2 - args.lse[li] * kLog2eB);
-            dv = pv * (pacc[rt][i] - delta[li]);
-          }
+          const float pv = rok[rt][i] ? exp2f(sacc[rt][i] * sc2 - lsv[rt][i] * kLog2eB) : 0.f;
           p[rt][i] = pv;
-          ds[rt][i] = dv;
+          ds[rt][i] = pv * (pacc[rt][i] - dlv[rt][i]);
         }
       bf16x8 ph, pl, sh, sl;
 #pragma unroll
@@ -840,6 +878,7 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
         adk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sl, adk[dt], 0, 0, 0);
       }
       wave_lds_sync();   // the slabs are rewritten by the next batch
+      cur = nxt;
     }
   }
 
