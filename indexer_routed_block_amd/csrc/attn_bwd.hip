@@ -229,6 +229,130 @@ bwd_prep_kernel(AttnArgs a, const T* __restrict__ dout, T* __restrict__ qt, T* _
 }
 
 // ---------------------------------------------------------------- dq
+// bf16, one wavefront per (batch, query, KV head) with G <= 16 heads as the
+// MFMA columns.  Per 32-key chunk: S^T = K Q^T and dP^T = V dO^T with the
+// gathered K and V rows as A operands, dS = P (dP - Delta), and
+// dQ^T += K^T dS^T with K^T from the wave's LDS slab (row-major copy of the
+// chunk's K rows) by transpose reads.  The next chunk's K and V rows load
+// while the current chunk's softmax and dQ work runs.
+template <int D, int DV>
+IRB_DEV void dq_item_gather(const AttnArgs& a, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+                            const float* __restrict__ delta, uint16_t* __restrict__ dq, int G, int b, int t, int kvh,
+                            uint16_t* kl) {
+  using T = uint16_t;
+  constexpr int KS = D / 32, VS = DV / 32, NDQ = D / 16;
+  constexpr int LDK = D + 8;
+  const int lane = threadIdx.x & 63;
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int h0 = kvh * G;
+  const int nh = min(16, G);
+  const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
+  const int n = max(0, min(a.lens[row], a.L));
+  const int32_t* route = a.routes + row * a.L;
+  const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
+  const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
+  const bool hok = l16 < nh;
+  const int hh = h0 + (hok ? l16 : 0);
+  bf16x8 qh[KS], dh[VS];
+  {
+    const T* qp = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(t) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qh[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+      if (!hok) bzero8(qh[s]);
+    }
+    const T* dp = dout + (row * a.Hq + hh) * DV + 8 * g16;
+#pragma unroll
+    for (int s = 0; s < VS; ++s) {
+      dh[s] = *reinterpret_cast<const bf16x8*>(dp + 32 * s);
+      if (!hok) bzero8(dh[s]);
+    }
+  }
+  const float lse2 = hok ? lse[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] * kLog2eB : 0.f;
+  const float dlt = hok ? delta[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] : 0.f;
+  const float sc2 = a.scale * kLog2eB;
+  f32x4 acc[NDQ];
+#pragma unroll
+  for (int i = 0; i < NDQ; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int vk0 = 4 * g16 + (l16 >> 2);   // K^T transpose reads: first key row
+
+  struct Pre { bf16x8 k[2][KS], v[2][VS]; };
+  auto load = [&](int e0, Pre& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int e = e0 + 16 * ti + l16;
+      const int id = e < n ? route[e] : -1;
+      const bool ok = id >= 0 && id < a.S_k;
+      const T* kr = kbase + static_cast<int64_t>(ok ? id : 0) * a.sk_t + 8 * g16;
+      const T* vr = vbase + static_cast<int64_t>(ok ? id : 0) * a.sv_t + 8 * g16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        r.k[ti][s] = *reinterpret_cast<const bf16x8*>(kr + 32 * s);
+        if (!ok) bzero8(r.k[ti][s]);
+      }
+#pragma unroll
+      for (int s = 0; s < VS; ++s) {
+        r.v[ti][s] = *reinterpret_cast<const bf16x8*>(vr + 32 * s);
+        if (!ok) bzero8(r.v[ti][s]);
+      }
+    }
+  };
+  auto step = [&](int e0, Pre& pf) __attribute__((always_inline)) {
+    // row-major copy of the chunk's K rows for the transposed operand
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        *reinterpret_cast<bf16x8*>(kl + (16 * ti + l16) * LDK + 8 * g16 + 32 * s) = pf.k[ti][s];
+    f32x4 st[2], dpt[2];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      st[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dpt[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) st[ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf.k[ti][s], qh[s], st[ti], 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < VS; ++s) dpt[ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf.v[ti][s], dh[s], dpt[ti], 0, 0, 0);
+    }
+    wave_lds_sync();
+    if (e0 + 32 < n) load(e0 + 32, pf);
+    // dS at keys 16 ti + 4 g16 + i, column = head l16
+    float ds[2][4];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + 16 * ti + 4 * g16 + i;
+        const float p = (e < n && hok) ? exp2f(st[ti][i] * sc2 - lse2) : 0.f;
+        ds[ti][i] = p * (dpt[ti][i] - dlt);
+      }
+    const float dsf[8] = {ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]};
+    const bf16x8 sop = pack_bf16x8(dsf);
+    // dQ^T += K^T dS^T; k-slot j is key 4 g16 + j (j < 4) or 16 + 4 g16 + (j - 4)
+#pragma unroll
+    for (int dt = 0; dt < NDQ; ++dt) {
+      const T* w = kl + vk0 * LDK + 16 * dt + 4 * (l16 & 3);
+      const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * LDK);
+      const bf16x8 xa = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sop, acc[dt], 0, 0, 0);
+    }
+    wave_lds_sync();   // the slab is rewritten by the next chunk
+  };
+  if (n > 0) {
+    Pre pf;
+    load(0, pf);
+    for (int e0 = 0; e0 < n; e0 += 32) step(e0, pf);
+  }
+  if (hok) {
+    T* op = dq + (row * a.Hq + h0 + l16) * D + 4 * g16;
+#pragma unroll
+    for (int dt = 0; dt < NDQ; ++dt) {
+      const float v[4] = {acc[dt][0] * a.scale, acc[dt][1] * a.scale, acc[dt][2] * a.scale, acc[dt][3] * a.scale};
+      bstore4(op + dt * 16, v);
+    }
+  }
+}
+
 template <typename T, int D, int DV, bool kShared>
 __global__ void __launch_bounds__(256)
 bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -246,6 +370,11 @@ bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ 
   const int kvh = item % a.Hkv;
   const int t = (item / a.Hkv) % a.S_q;
   const int b = item / (a.Hkv * a.S_q);
+  if constexpr (!kShared && sizeof(T) == 2 && D <= 128) {
+    dq_item_gather<D, DV>(a, dout, lse, delta, dq, G, b, t, kvh,
+                          reinterpret_cast<uint16_t*>(smem) + wid * 32 * (D + 8));
+    return;
+  }
   const int h0 = kvh * G + 16 * slice;
   const int nh = min(16, G - 16 * slice);
   const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
