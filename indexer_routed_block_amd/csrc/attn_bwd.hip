@@ -230,14 +230,19 @@ bwd_prep_kernel(AttnArgs a, const T* __restrict__ dout, T* __restrict__ qt, T* _
 
 // ---------------------------------------------------------------- dq
 // bf16, one wavefront per (batch, query, KV head) with G <= 16 heads as the
-// MFMA columns.  Per 32-key chunk: S^T = K Q^T and dP^T = V dO^T with the
-// gathered K and V rows as A operands, dS = P (dP - Delta), and
-// dQ^T += K^T dS^T with K^T from the wave's LDS slab (row-major copy of the
-// chunk's K rows) by transpose reads.  The next chunk's K and V rows load
-// while the current chunk's softmax and dQ work runs.
+// MFMA columns; this pass also forms the row statistic Delta.  Per 32-key
+// chunk: S^T = K Q^T and dP^T = V dO^T with the gathered K and V rows as A
+// operands, P = exp(S - lse), and, with K^T from the wave's LDS slab
+// (row-major copy of the chunk's K rows) by transpose reads,
+//   A^T += K^T (P dP)^T,   B^T += K^T P^T,   Delta += sum_k P dP,
+// so that dQ = scale (A - Delta B) = scale sum_k P (dP - Delta) k without a
+// separate pass for Delta.  P dP and P enter as bf16 high + low parts, so A
+// and B carry ~16 significant bits and their difference stays accurate.
+// Delta = sum_k P dP equals rowsum(dO o) for the FP32 o.  The next chunk's K
+// and V rows load while the current chunk's softmax and dQ work runs.
 template <int D, int DV>
 IRB_DEV void dq_item_gather(const AttnArgs& a, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-                            const float* __restrict__ delta, uint16_t* __restrict__ dq, int G, int b, int t, int kvh,
+                            float* __restrict__ delta, uint16_t* __restrict__ dq, int G, int b, int t, int kvh,
                             uint16_t* kl) {
   using T = uint16_t;
   constexpr int KS = D / 32, VS = DV / 32, NDQ = D / 16;
@@ -269,11 +274,11 @@ IRB_DEV void dq_item_gather(const AttnArgs& a, const uint16_t* __restrict__ dout
     }
   }
   const float lse2 = hok ? lse[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] * kLog2eB : 0.f;
-  const float dlt = hok ? delta[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] : 0.f;
   const float sc2 = a.scale * kLog2eB;
-  f32x4 acc[NDQ];
+  f32x4 acc[NDQ], accb[NDQ];
 #pragma unroll
-  for (int i = 0; i < NDQ; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NDQ; ++i) { acc[i] = f32x4{0.f, 0.f, 0.f, 0.f}; accb[i] = acc[i]; }
+  float dsum = 0.f;
   const int vk0 = 4 * g16 + (l16 >> 2);   // K^T transpose reads: first key row
 
   struct Pre { bf16x8 k[2][KS], v[2][VS]; };
@@ -316,25 +321,30 @@ IRB_DEV void dq_item_gather(const AttnArgs& a, const uint16_t* __restrict__ dout
     }
     wave_lds_sync();
     if (e0 + 32 < n) load(e0 + 32, pf);
-    // dS at keys 16 ti + 4 g16 + i, column = head l16
-    float ds[2][4];
+    // P and P dP at keys 16 ti + 4 g16 + i, column = head l16
+    bf16x8 ph, pl, qh2, ql2;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = e0 + 16 * ti + 4 * g16 + i;
         const float p = (e < n && hok) ? exp2f(st[ti][i] * sc2 - lse2) : 0.f;
-        ds[ti][i] = p * (dpt[ti][i] - dlt);
+        const float pd = p * dpt[ti][i];
+        dsum += pd;
+        bput_f(ph, pl, 4 * ti + i, p, true);
+        bput_f(qh2, ql2, 4 * ti + i, pd, true);
       }
-    const float dsf[8] = {ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]};
-    const bf16x8 sop = pack_bf16x8(dsf);
-    // dQ^T += K^T dS^T; k-slot j is key 4 g16 + j (j < 4) or 16 + 4 g16 + (j - 4)
+    // A^T += K^T (P dP)^T and B^T += K^T P^T; k-slot j is key 4 g16 + j
+    // (j < 4) or 16 + 4 g16 + (j - 4)
 #pragma unroll
     for (int dt = 0; dt < NDQ; ++dt) {
       const T* w = kl + vk0 * LDK + 16 * dt + 4 * (l16 & 3);
       const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * LDK);
       const bf16x8 xa = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sop, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, qh2, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ql2, acc[dt], 0, 0, 0);
+      accb[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ph, accb[dt], 0, 0, 0);
+      accb[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pl, accb[dt], 0, 0, 0);
     }
     wave_lds_sync();   // the slab is rewritten by the next chunk
   };
@@ -343,19 +353,27 @@ IRB_DEV void dq_item_gather(const AttnArgs& a, const uint16_t* __restrict__ dout
     load(0, pf);
     for (int e0 = 0; e0 < n; e0 += 32) step(e0, pf);
   }
+  const float dlt = row4_sum(dsum);
   if (hok) {
+    if (g16 == 0) delta[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] = dlt;
     T* op = dq + (row * a.Hq + h0 + l16) * D + 4 * g16;
 #pragma unroll
     for (int dt = 0; dt < NDQ; ++dt) {
-      const float v[4] = {acc[dt][0] * a.scale, acc[dt][1] * a.scale, acc[dt][2] * a.scale, acc[dt][3] * a.scale};
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (acc[dt][i] - dlt * accb[dt][i]) * a.scale;
       bstore4(op + dt * 16, v);
     }
   }
 }
 
+// whether the query side forms Delta itself (dq_item_gather)
+template <typename T, int D>
+constexpr bool dq_fuses_delta() { return sizeof(T) == 2 && D <= 128; }
+
 template <typename T, int D, int DV, bool kShared>
-__global__ void __launch_bounds__(256)
-bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+__global__ void __launch_bounds__(256, (!kShared && dq_fuses_delta<T, D>()) ? 2 : 1)
+bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta,
               T* __restrict__ dq, int G, int n_items, int latent) {
   constexpr bool kSplit = sizeof(T) == 4;
   constexpr int KS = D / 32, VS = DV / 32, NDQ = D / 16;
@@ -370,7 +388,7 @@ bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ 
   const int kvh = item % a.Hkv;
   const int t = (item / a.Hkv) % a.S_q;
   const int b = item / (a.Hkv * a.S_q);
-  if constexpr (!kShared && sizeof(T) == 2 && D <= 128) {
+  if constexpr (!kShared && dq_fuses_delta<T, D>()) {
     dq_item_gather<D, DV>(a, dout, lse, delta, dq, G, b, t, kvh,
                           reinterpret_cast<uint16_t*>(smem) + wid * 32 * (D + 8));
     return;
@@ -1220,7 +1238,11 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, a,
                        static_cast<const T*>(args.dout), static_cast<T*>(ws.qt), static_cast<T*>(ws.dot), G, Gp);
   }
-  if (int rc = launch_attn_delta(a, args.dout, ws.delta, stream)) return rc;
+  // Delta = rowsum(dO o) with o in FP32: the bf16 query side with G <= 16
+  // forms it in its own pass (and writes it before the key side reads it);
+  // otherwise a forward pass in Delta mode recomputes o
+  if (!(G <= 16 && dq_fuses_delta<T, D>()))
+    if (int rc = launch_attn_delta(a, args.dout, ws.delta, stream)) return rc;
   const int PAD = sizeof(T) == 2 ? 8 : 4;
   const int64_t items = rows * a.Hkv;
   if (G <= 16) {
