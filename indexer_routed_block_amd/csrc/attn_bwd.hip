@@ -1115,9 +1115,16 @@ bwd_dkdv_wide_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
   const uint16_t* og = static_cast<const uint16_t*>(args.dout);
 
+  // the next hit's query and key mask are read one hit ahead
+  int nt = h0 < h1 ? hit_t[h0] : -1;
+  uint32_t nm = h0 < h1 ? hit_m[h0] : 0u;
   for (int64_t e = h0; e < h1; ++e) {
-    const int t = hit_t[e];
-    const uint32_t m = hit_m[e];
+    const int t = nt;
+    const uint32_t m = nm;
+    if (e + 1 < h1) {
+      nt = hit_t[e + 1];
+      nm = hit_m[e + 1];
+    }
     if (t < 0 || t >= a.S_q) continue;          // uniform over the workgroup
     const bool kin = (m >> l16) & 1u;
     for (int hb = 0; hb < bpq; ++hb) {
@@ -1147,6 +1154,16 @@ bwd_dkdv_wide_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
         }
         s_x[wid][lane] = acc;
       }
+      // lse and Delta of rows 16 r2 + 4 g16 + i, loaded before the exchange
+      float lsv[2][4], dlv[2][4];
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t li = (static_cast<int64_t>(b) * a.Hq + kvh * G + hb * 32 + 16 * r2 + 4 * g16 + i) * a.S_q + t;
+          lsv[r2][i] = args.lse[li];
+          dlv[r2][i] = delta[li];
+        }
       __syncthreads();
       // P and dS at rows 16 r2 + 4 g16 + i, key l16
       float p[2][4], ds[2][4];
@@ -1155,10 +1172,9 @@ bwd_dkdv_wide_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
         const f32x4 sv = s_x[r2][lane], pv = s_x[2 + r2][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t li = (static_cast<int64_t>(b) * a.Hq + kvh * G + hb * 32 + 16 * r2 + 4 * g16 + i) * a.S_q + t;
-          const float pp = kin ? exp2f(sv[i] * sc2 - args.lse[li] * kLog2eB) : 0.f;
+          const float pp = kin ? exp2f(sv[i] * sc2 - lsv[r2][i] * kLog2eB) : 0.f;
           p[r2][i] = pp;
-          ds[r2][i] = kin ? pp * (pv[i] - delta[li]) : 0.f;
+          ds[r2][i] = kin ? pp * (pv[i] - dlv[r2][i]) : 0.f;
         }
       }
       bf16x8 ph, pl, sh, sl;
