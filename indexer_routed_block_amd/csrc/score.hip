@@ -193,17 +193,39 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   };
 
   // pre-split chunk loader: lane i of load n fills 16-byte slot (w NI + n) 64 + i;
-  // row R = 2 block + (0 hi | 1 lo), chunk slot sc holds chunk sc ^ ((R / 2) mod NC)
-  auto issue = [&](int j, int pbuf) __attribute__((always_inline)) {
-    char* base = kraw + pbuf * PBUF;
+  // row R = 2 block + (0 hi | 1 lo), chunk slot sc holds chunk sc ^ ((R / 2) mod NC).
+  // The chunk's first block gives a wave-uniform base address (scalar
+  // registers); the per-lane byte offsets from it are fixed for the whole
+  // launch, and only a chunk reaching past the last block clamps its rows.
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  uint32_t poff[kPre ? NI : 1];
+  if constexpr (kPre) {
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      const int slot = (wid * NI + n) * 64 + lane;
+      const int slot = (wu * NI + n) * 64 + lane;
       const int R = slot / NC, sc = slot % NC;
-      const int blk = min(j + (R >> 1), nb_max - 1);
-      const uint16_t* src = kcs + ((static_cast<int64_t>(b) * nb_max + blk) * 2 + (R & 1)) * D +
-                            8 * (sc ^ ((R >> 1) & (NC - 1)));
-      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(base + (wid * NI + n) * 1024)));
+      poff[n] = static_cast<uint32_t>(R * D + 8 * (sc ^ ((R >> 1) & (NC - 1)))) * 2u;
+    }
+  }
+  const uint32_t klds = lds_addr(kraw);
+  auto issue = [&](int j, int pbuf) __attribute__((always_inline)) {
+    j = __builtin_amdgcn_readfirstlane(j);
+    pbuf = __builtin_amdgcn_readfirstlane(pbuf);
+    const uint32_t lb = klds + pbuf * PBUF + wu * NI * 1024;
+    if (j + CH <= nb_max) {
+      const uint16_t* sb = kcs + (static_cast<int64_t>(b) * nb_max + j) * 2 * D;
+#pragma unroll
+      for (int n = 0; n < NI; ++n) lds_dma16_s(sb, poff[n], lb + n * 1024);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int slot = (wu * NI + n) * 64 + lane;
+        const int R = slot / NC, sc = slot % NC;
+        const int blk = min(j + (R >> 1), nb_max - 1);
+        const uint16_t* src = kcs + ((static_cast<int64_t>(b) * nb_max + blk) * 2 + (R & 1)) * D +
+                              8 * (sc ^ ((R >> 1) & (NC - 1)));
+        lds_dma16(src, lb + n * 1024);
+      }
     }
   };
   const int nch = (ce - cb + CH - 1) / CH;
