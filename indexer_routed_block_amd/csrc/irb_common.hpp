@@ -41,7 +41,8 @@ IRB_DEV void split_bf16(float f, uint16_t& hi, uint16_t& lo) {
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2n;
 
 // two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest
-// even; written out so the pair is never split into two conversions)
+// even; written out so the pair is never split into two conversions).  The
+// inputs must not come straight from an MFMA (see max_raw).
 IRB_DEV uint32_t pack_bf16x2(float a, float b) {
   uint32_t r;
   asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -171,7 +172,9 @@ IRB_DEV v4s lds_read_tr(const uint16_t* p) {
 // so combining the pair gives the butterfly step without an LDS round trip.
 // v_max_f32 without the quieting of its inputs that fmaxf adds for values the
 // compiler cannot prove canonical (lane-permute results); NaN inputs are not
-// expected here
+// expected here.  Like every inline-assembly helper in this file it must not
+// read an MFMA accumulator directly: the compiler does not insert the wait
+// states between an MFMA and an inline-assembly reader of its result.
 IRB_DEV float max_raw(float x, float y) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
