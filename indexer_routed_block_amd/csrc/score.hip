@@ -228,6 +228,24 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
       }
     }
   };
+  // visible ranges of the wave's queries in registers (the stores test them every tile)
+  int my_vb = 0, my_vn = 0;
+  bool my_q = false;
+  int64_t my_off = 0;
+  int vbk[H >= 16 ? 1 : QW], vnk[H >= 16 ? 1 : QW];
+  if constexpr (H >= 16) {
+    const int k = g16 < QW ? g16 : 0;
+    my_vb = s_vis[0][wid * QW + k];
+    my_vn = s_vis[1][wid * QW + k];
+    my_q = g16 < QW && qa + wid * QW + g16 < qe;
+    my_off = static_cast<int64_t>(wid * QW + k) * ostride;
+  } else {
+#pragma unroll
+    for (int k = 0; k < QW; ++k) {
+      vbk[k] = __builtin_amdgcn_readfirstlane(s_vis[0][wid * QW + k]);
+      vnk[k] = __builtin_amdgcn_readfirstlane(s_vis[1][wid * QW + k]);
+    }
+  }
   const int nch = (ce - cb + CH - 1) / CH;
   if constexpr (kPre) {
     for (int p = 0; p < NBUF - 1 && p < nch; ++p) issue(cb + p * CH, p);
@@ -251,28 +269,39 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
     } else {
       if (it + 1 < nch) gload(j + CH);
     }
+    // key operands of column tile ct (16 blocks) from the chunk buffer into slot ct % 2
+    bf16x8 okh[2][KS], okl[2][KS];
+    auto ld_ops = [&](int ct) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (kPre) {
+          const int R = 2 * (16 * ct + l16);
+          const int sl = (4 * s + g16) ^ ((R >> 1) & (NC - 1));
+          const char* base = kraw + buf * PBUF;
+          okh[ct & 1][s] = *reinterpret_cast<const bf16x8*>(base + (R * NC + sl) * 16);
+          okl[ct & 1][s] = *reinterpret_cast<const bf16x8*>(base + ((R + 1) * NC + sl) * 16);
+        } else {
+          const uint16_t* kb = reinterpret_cast<const uint16_t*>(kraw) + buf * 2 * kScoreChunk * LDK;
+          const int off = (16 * ct + l16) * LDK + 32 * s + 8 * g16;
+          okh[ct & 1][s] = *reinterpret_cast<const bf16x8*>(&kb[off]);
+          okl[ct & 1][s] = *reinterpret_cast<const bf16x8*>(&kb[kScoreChunk * LDK + off]);
+        }
+      }
+    };
+    ld_ops(0);
 #pragma unroll
     for (int ct = 0; ct < CH / 16; ++ct) {
       const int jc = j + 16 * ct;                  // first block of this column tile
       if (jc >= ce) break;
+      // the next tile's operands load while this tile's MFMAs and epilogue run
+      // (rows of the chunk buffer past ce hold stale keys and are never used)
+      if (ct + 1 < CH / 16) ld_ops(ct + 1);
       f32x4 acc[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        bf16x8 kh, kl;
-        if constexpr (kPre) {
-          const int R = 2 * (16 * ct + l16);
-          const int sl = (4 * s + g16) ^ ((R >> 1) & (NC - 1));
-          const char* base = kraw + buf * PBUF;
-          kh = *reinterpret_cast<const bf16x8*>(base + (R * NC + sl) * 16);
-          kl = *reinterpret_cast<const bf16x8*>(base + ((R + 1) * NC + sl) * 16);
-        } else {
-          const uint16_t* kb = reinterpret_cast<const uint16_t*>(kraw) + buf * 2 * kScoreChunk * LDK;
-          const int off = (16 * ct + l16) * LDK + 32 * s + 8 * g16;
-          kh = *reinterpret_cast<const bf16x8*>(&kb[off]);
-          kl = *reinterpret_cast<const bf16x8*>(&kb[kScoreChunk * LDK + off]);
-        }
+        const bf16x8 kh = okh[ct & 1][s], kl = okl[ct & 1][s];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rt][s], kh, acc[rt], 0, 0, 0);
@@ -300,16 +329,26 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
         else if (H == 8) part[k] = row_pair_sum(part[k]);
       }
       const int jb = jc + l16;
+      if constexpr (H >= 16) {
+        // every lane holds the sums of all QW (<= 4) queries: lane group g16
+        // writes query g16, one store for the whole tile
+        float v = part[0];
 #pragma unroll
-      for (int k = 0; k < QW; ++k) {
-        // the lane group that owns query k's sum writes it
-        const bool writer = H >= 16 ? (g16 == 0) : (H == 8 ? (g16 == 2 * (k % 2)) : (g16 == k % 4));
-        const int qw = qa + wid * QW + k;
-        if (writer && qw < qe && jb < ce) {
-          const int vb = s_vis[0][wid * QW + k], vn = s_vis[1][wid * QW + k];
-          const bool vis = jb >= vb && jb < vb + vn;
-          if (vis || write_invisible)
-            otile[static_cast<int64_t>(qw - qa) * ostride + (jb - j0)] = vis ? scale * part[k] : -INFINITY;
+        for (int k = 1; k < QW; ++k) v = g16 == k ? part[k] : v;
+        const bool vis = jb >= my_vb && jb < my_vb + my_vn;
+        if (my_q && jb < ce && (vis || write_invisible))
+          otile[my_off + (jb - j0)] = vis ? scale * v : -INFINITY;
+      } else {
+#pragma unroll
+        for (int k = 0; k < QW; ++k) {
+          // the lane group that owns query k's sum writes it
+          const bool writer = H == 8 ? (g16 == 2 * (k % 2)) : (g16 == k % 4);
+          const int qw = qa + wid * QW + k;
+          if (writer && qw < qe && jb < ce) {
+            const bool vis = jb >= vbk[k] && jb < vbk[k] + vnk[k];
+            if (vis || write_invisible)
+              otile[static_cast<int64_t>(qw - qa) * ostride + (jb - j0)] = vis ? scale * part[k] : -INFINITY;
+          }
         }
       }
     }
