@@ -214,3 +214,26 @@ def test_select_rows_longer_than_lds(ties):
     rsel, rcnt = oracle.select_topk(scores.astype(np.float64), c, topk, q0=q0, S=S)
     np.testing.assert_array_equal(host(cnt)[:, q0:], rcnt)
     np.testing.assert_array_equal(host(sel)[:, q0:], rsel)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("S,c,topk", [(16384, 4, 512), (32768, 4, 256), (131072, 8, 256), (65536, 4, 300)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_select_long_rows(S, c, topk, ties):
+    """Rows of 4096, 8192, 16384 and 16384 visible blocks (every register-resident
+    width of the select kernel), with the last rows made constant, two-valued
+    and of one repeated value above a sea of ties."""
+    rows = 12
+    banner(f"select long rows S={S} c={c} topk={topk} ties={ties}")
+    rng = np.random.default_rng(S + topk + ties)
+    q0 = S - rows
+    nb = S // c
+    scores = _quantised_scores(rng, 1, rows, nb, ties)
+    scores[0, -1, :] = 0.25                                   # constant row: lowest IDs win
+    scores[0, -2, :] = np.where(rng.random(nb) < 0.5, 1.0, -1.0).astype(np.float32)
+    scores[0, -3, :] = -0.0
+    scores[0, -3, rng.choice(nb, topk // 2, replace=False)] = 3.0
+    sel, cnt = irb.select_topk_regions(to_dev(scores), c, topk, S, q0=q0)
+    rsel, rcnt = oracle.select_topk(scores.astype(np.float64), c, topk, q0=q0, S=S)
+    np.testing.assert_array_equal(host(cnt)[:, q0:], rcnt)
+    np.testing.assert_array_equal(host(sel)[:, q0:], rsel)
