@@ -7,8 +7,8 @@
 // Tiling.  Rows of the MFMA A operand are (query, head) pairs, columns are
 // blocks, K is the index dimension.  A workgroup (4 waves) owns the rows of
 // 4 * 16 RT / H queries -- each wave keeps RT row tiles (whole queries) of q in
-// registers for the whole launch -- and one segment of blocks.  It streams
-// the segment in chunks of 64 blocks: the FP32 compressed keys are split into
+// registers for the whole launch -- and the whole visible block range of those
+// queries.  It streams the range in chunks of blocks: the FP32 compressed keys are split into
 // bf16 high and low halves on the way into a double-buffered LDS tile, and
 // every wave reads each 16-block operand once for all of its row tiles
 // (q*hi + q*lo, plus q_lo*hi for FP32 queries).  The accumulator layout puts
@@ -63,11 +63,17 @@ IRB_DEV void visible_blocks(const Layout& L, const int32_t* cu_blocks, int c, in
 }
 
 // kPre: the keys come pre-split (kcs, per block a row of bf16 high halves then
-// a row of low halves) and stream through four LDS buffers by direct
-// global-to-LDS loads, three chunks in flight; otherwise the FP32 keys are
+// a row of low halves) and stream through three LDS buffers by direct
+// global-to-LDS loads, two chunks in flight; otherwise the FP32 keys are
 // split while staging through two buffers.
+// Resident workgroups per CU: three for the bf16 streaming path with whole
+// 16-head row tiles (measured faster), two elsewhere (FP32 queries and narrow
+// heads need the registers).
+template <typename QT, int H, bool kPre>
+constexpr int score_occupancy() { return (kPre && sizeof(QT) == 2 && H >= 16) ? 3 : 2; }
+
 template <typename QT, int D, int H, bool kPre>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, (score_occupancy<QT, H, kPre>()))
 score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kc,
              const uint16_t* __restrict__ kcs, const int32_t* __restrict__ cu_blocks, int c, float scale, int q0,
              int q1, int j0, int j1, float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg,
@@ -81,7 +87,7 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   constexpr int QG = 4 * QW;                        // queries per workgroup
   constexpr int LDK = D + 8;                        // padded LDS row (bf16 elements)
   constexpr int CH = kPre ? 32 : kScoreChunk;       // blocks per chunk
-  constexpr int NBUF = kPre ? 4 : 2;
+  constexpr int NBUF = kPre ? 3 : 2;
   constexpr int GROUPS = kScoreChunk * D / 8;       // 8-dim groups per chunk (split staging)
   constexpr int GPT = GROUPS / 256;                 // per thread
   static_assert(GROUPS % 256 == 0, "chunk staging");
@@ -97,7 +103,8 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g16 = lane >> 4, l16 = lane & 15;
   const int b = blockIdx.y;
-  const int qg = blockIdx.x / n_seg, sg = blockIdx.x % n_seg;
+  // query groups run latest (longest visible range) first
+  const int qg = (gridDim.x / n_seg - 1) - blockIdx.x / n_seg, sg = blockIdx.x % n_seg;
   const int qa = q0 + qg * QG, qe = min(q1, qa + QG);
   const int nb_max = L.S / c;
 
@@ -387,9 +394,12 @@ template <typename QT, int D>
 static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const uint16_t* kcs,
                           const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1, float* out,
                           int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
-  // block segments: about a quarter of the widest visible range, 256..2048 blocks
+  // one segment per row: measured on MI355X, splitting rows into segments of
+  // 256..4096 blocks was slower at every size (each segment repeats the q-row
+  // loads and the pipeline fill), and latest-first order plus three resident
+  // workgroups per CU cover the causal imbalance
   const int span = j1 - j0;
-  int seg = std::min(2048, std::max(256, (L.S / c) / 4));
+  int seg = std::max(1, span);
   seg = (seg + kScoreChunk - 1) / kScoreChunk * kScoreChunk;
   const int n_seg = (span + seg - 1) / seg;
   // queries per workgroup: 4 waves x 16 RT / H
