@@ -185,7 +185,8 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
  *   sel, cnt  [B, S, topk] / [B, S] as written by irb_select_topk_regions
  *   routes    OUT [B, S, L] int32;  lens OUT [B, S] int32
  * Requires L >= topk*c + max(window, c-1) (the [QSA] width budget + c - 1 when
- * window == 0), window >= 0.
+ * window == 0), window >= 0, 0 <= topk <= 4096 (sel and cnt may be NULL when
+ * topk == 0).
  */
 int irb_expand_and_compact_routes(const irb_layout* layout, const int32_t* sel, const int32_t* cnt,
                                   int topk, int c, int window, const int32_t* cu_blocks, int L,

@@ -195,6 +195,7 @@ int irb_expand_and_compact_routes(const irb_layout* layout, const int32_t* sel, 
   irb::Layout L;
   if (int r = check_layout(fn, layout, L)) return r;
   if (c < 1 || topk < 0 || window < 0) return fail(IRB_ERR_INVALID, "%s: need c >= 1, topk >= 0, window >= 0", fn);
+  if (topk > 4096) return fail(IRB_ERR_INVALID, "%s: topk must be <= 4096 (got %d)", fn, topk);
   const int64_t need = static_cast<int64_t>(topk) * c + std::max(window, c - 1);
   if (L_width < need) return fail(IRB_ERR_INVALID, "%s: width %d < topk*c + max(window, c-1) = %lld", fn, L_width, (long long)need);
   if ((topk > 0 && (!sel || !cnt)) || !routes || !lens) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);

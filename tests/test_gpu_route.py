@@ -138,7 +138,9 @@ def test_route_pipeline_matches_oracle(wl_name, S, layout):
 
 @pytest.mark.parametrize("c,topk,window,layout,S", [(4, 16, 0, "single", 512), (4, 512, 128, "single", 8192),
                                                    (4, 8, 5, "packed", 3000), (8, 256, 512, "single", 8192),
-                                                   (3, 5, 7, "rows", 400), (1, 6, 0, "rows", 300)])
+                                                   (3, 5, 7, "rows", 400), (1, 6, 0, "rows", 300),
+                                                   (3, 20, 8, "packed", 3000), (5, 40, 0, "single", 2048),
+                                                   (16, 300, 64, "single", 8192)])
 def test_expand_bit_exact_on_fixed_selection(c, topk, window, layout, S):
     banner(f"expand c={c} topk={topk} W={window} {layout} S={S}")
     rng = np.random.default_rng(S + c)
@@ -161,7 +163,8 @@ def test_expand_bit_exact_on_fixed_selection(c, topk, window, layout, S):
     np.testing.assert_array_equal(host(routes), rr)
 
 
-@pytest.mark.parametrize("rows,width,key_count", [(300, 67, 300), (64, 2048, 5000), (17, 1, 3), (40, 1000, 10)])
+@pytest.mark.parametrize("rows,width,key_count", [(300, 67, 300), (64, 2048, 5000), (17, 1, 3), (40, 1000, 10),
+                                                  (50, 500, 1000000), (30, 3000, 70000)])
 def test_compact_bit_exact(rows, width, key_count):
     banner(f"compact rows={rows} width={width} keys={key_count}")
     rng = np.random.default_rng(rows * width)
@@ -175,6 +178,26 @@ def test_compact_bit_exact(rows, width, key_count):
     t = to_dev(ids)
     irb.compact_routes(t, key_count, out=t)
     np.testing.assert_array_equal(host(t), ro)
+
+
+def test_compact_bitmap_capacity_edge():
+    """Rows whose valid IDs span exactly the LDS bitmap's capacity (65536 values)
+    and one more, with duplicates, invalid IDs and an all-invalid row."""
+    banner("compact bitmap capacity edge")
+    rng = np.random.default_rng(11)
+    width, key_count = 700, 200000
+    ids = rng.integers(1000, 1000 + 65536, size=(6, width)).astype(np.int32)
+    ids[0, :2] = [1000, 1000 + 65535]          # span 65536 values
+    ids[1, :2] = [1000, 1000 + 65536]          # span 65537 values
+    ids[2, 1::3] = ids[2, ::3][: ids[2, 1::3].size]  # duplicates
+    ids[3, ::2] = -1
+    ids[4, 5] = key_count + 7                  # out of range, dropped and counted
+    ids[5, :] = -5                             # nothing valid
+    out, lens, bad = irb.compact_routes(to_dev(ids), key_count)
+    ro, rl, rbad = oracle.compact_routes(ids, key_count)
+    np.testing.assert_array_equal(host(out), ro)
+    np.testing.assert_array_equal(host(lens), rl)
+    assert int(host(bad)[0]) == rbad == 1
 
 
 def test_compact_latent_indices():
