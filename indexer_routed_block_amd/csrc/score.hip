@@ -63,17 +63,11 @@ IRB_DEV void visible_blocks(const Layout& L, const int32_t* cu_blocks, int c, in
 }
 
 // kPre: the keys come pre-split (kcs, per block a row of bf16 high halves then
-// a row of low halves) and stream through three LDS buffers by direct
-// global-to-LDS loads, two chunks in flight; otherwise the FP32 keys are
+// a row of low halves) and stream through four LDS buffers by direct
+// global-to-LDS loads, three chunks in flight; otherwise the FP32 keys are
 // split while staging through two buffers.
-// Resident workgroups per CU: three for the bf16 streaming path with whole
-// 16-head row tiles (measured faster), two elsewhere (FP32 queries and narrow
-// heads need the registers).
-template <typename QT, int H, bool kPre>
-constexpr int score_occupancy() { return (kPre && sizeof(QT) == 2 && H >= 16) ? 3 : 2; }
-
 template <typename QT, int D, int H, bool kPre>
-__global__ void __launch_bounds__(256, (score_occupancy<QT, H, kPre>()))
+__global__ void __launch_bounds__(256, 2)
 score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kc,
              const uint16_t* __restrict__ kcs, const int32_t* __restrict__ cu_blocks, int c, float scale, int q0,
              int q1, int j0, int j1, float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg,
@@ -87,7 +81,7 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   constexpr int QG = 4 * QW;                        // queries per workgroup
   constexpr int LDK = D + 8;                        // padded LDS row (bf16 elements)
   constexpr int CH = kPre ? 32 : kScoreChunk;       // blocks per chunk
-  constexpr int NBUF = kPre ? 3 : 2;
+  constexpr int NBUF = kPre ? 4 : 2;
   constexpr int GROUPS = kScoreChunk * D / 8;       // 8-dim groups per chunk (split staging)
   constexpr int GPT = GROUPS / 256;                 // per thread
   static_assert(GROUPS % 256 == 0, "chunk staging");
@@ -394,10 +388,11 @@ template <typename QT, int D>
 static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const uint16_t* kcs,
                           const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1, float* out,
                           int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
-  // one segment per row: measured on MI355X, splitting rows into segments of
-  // 256..4096 blocks was slower at every size (each segment repeats the q-row
-  // loads and the pipeline fill), and latest-first order plus three resident
-  // workgroups per CU cover the causal imbalance
+  // one segment per row: measured on MI355X with bf16 queries, splitting rows
+  // into segments of 512..1024 blocks was slower at S = 8192 and S = 131072
+  // (each segment repeats the q-row loads and the pipeline fill), and the
+  // latest-first order covers the causal imbalance; a third resident
+  // workgroup (three key buffers) was slower too
   const int span = j1 - j0;
   int seg = std::max(1, span);
   seg = (seg + kScoreChunk - 1) / kScoreChunk * kScoreChunk;

@@ -226,18 +226,125 @@ select_reg_kernel(Layout L, const float* __restrict__ scores, int64_t stride, in
   if (tid == 0) cnt[static_cast<int64_t>(b) * L.S + t] = topk;
 }
 
+// Rows of at most 64 * NPL blocks: one wavefront per row, NPL keys per lane
+// (i = 64 e + lane), 8-bit levels over the row's key range on a per-wave LDS
+// histogram and a ballot-based in-order emit; no workgroup barrier at all.
+template <int NPL>
+__global__ void __launch_bounds__(kSelThreads)
+select_wave_kernel(Layout L, const float* __restrict__ scores, int64_t stride, int q0, int q1,
+                   const int32_t* __restrict__ cu_blocks, int c, int topk, int32_t* __restrict__ sel,
+                   int32_t* __restrict__ cnt) {
+  __shared__ int hist_all[kSelThreads / 64][256];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = blockIdx.x * (kSelThreads / 64) + wid;
+  if (r >= q1 - q0) return;
+  const int t = q0 + r, b = blockIdx.y;
+  int* hist = hist_all[wid];
+  int32_t* srow = sel + (static_cast<int64_t>(b) * L.S + t) * topk;
+  const Doc d = doc_of(L, b, t);
+  const int n = d.valid ? (t - d.start + 1) / c : 0;
+  const int base = d.valid ? block_base(L, cu_blocks, d) : 0;
+  if (n <= topk) {                     // every visible block is taken
+    for (int i = lane; i < topk; i += 64) srow[i] = (i < n) ? base + i : -1;
+    if (lane == 0) cnt[static_cast<int64_t>(b) * L.S + t] = n;
+    return;
+  }
+  const float* row = scores + (static_cast<int64_t>(b) * (q1 - q0) + r) * stride + base;
+  float f[NPL];
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) f[e] = row[min(64 * e + lane, n - 1)];
+  // key + 1 for visible blocks, 0 past the row's end (excluded by every test below)
+  uint32_t key[NPL];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) {
+    key[e] = 64 * e + lane < n ? score_key(f[e]) + 1u : 0u;
+    kmin = min(kmin, key[e] ? key[e] : 0xffffffffu);
+    kmax = max(kmax, key[e]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, 64)));
+    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, 64)));
+  }
+  uint32_t lo = kmin, R = kmax - kmin;
+  int sh = R == 0u ? 0 : max(0, 32 - __clz(static_cast<int>(R)) - 8);
+  int krem = topk;
+  uint32_t T;
+  while (true) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[64 * j + lane] = 0;
+    wave_lds_sync();
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+      const uint32_t x = key[e] - lo;  // padding (key 0) wraps above R since lo >= 1
+      if (x <= R) atomicAdd(&hist[x >> sh], 1);
+    }
+    wave_lds_sync();
+    // lane owns bins 255 - 4 lane - j: a scan over lanes is a suffix sum over bins
+    int h[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { h[j] = hist[255 - 4 * lane - j]; local += h[j]; }
+    const int incl = wave_incl_scan(local);
+    int myb = 0, mya = 0;
+    const bool mine = incl >= krem && incl - local < krem;
+    if (mine) {
+      int acc = incl - local;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (acc >= 0 && acc + h[j] >= krem) { myb = 255 - 4 * lane - j; mya = acc; acc = -1; }
+        else if (acc >= 0) acc += h[j];
+      }
+    }
+    const int src = __ffsll(static_cast<unsigned long long>(__ballot(mine))) - 1;
+    const int B = __shfl(myb, src, 64);
+    krem -= __shfl(mya, src, 64);
+    lo += static_cast<uint32_t>(B) << sh;
+    if (sh == 0) { T = lo; break; }
+    R = (1u << sh) - 1u;
+    sh = max(0, sh - 8);
+    wave_lds_sync();                   // the histogram is cleared next
+  }
+  const int eq_quota = krem;
+  int gtc = 0, eqc = 0;
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) {
+    const bool gt = key[e] > T, eq = key[e] == T;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const int gt_before = gtc + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bg >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bg), 0));
+    const int eq_before = eqc + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(be >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(be), 0));
+    if (gt || (eq && eq_before < eq_quota)) srow[gt_before + min(eq_before, eq_quota)] = base + 64 * e + lane;
+    gtc += __popcll(bg);
+    eqc += __popcll(be);
+  }
+  if (lane == 0) cnt[static_cast<int64_t>(b) * L.S + t] = topk;
+}
+
 int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, int q1,
                   const int32_t* cu_blocks, int c, int topk, int32_t* sel, int32_t* cnt,
                   hipStream_t stream) {
   const int n_max = L.S / c;
   const dim3 grid(static_cast<unsigned>(q1 - q0), static_cast<unsigned>(L.B));
+#define IRB_SEL_WAVE(NPL)                                                                                  \
+  if (n_max <= 64 * NPL) {                                                                                 \
+    const dim3 gw(static_cast<unsigned>((q1 - q0 + kSelThreads / 64 - 1) / (kSelThreads / 64)),            \
+                  static_cast<unsigned>(L.B));                                                             \
+    hipLaunchKernelGGL(select_wave_kernel<NPL>, gw, dim3(kSelThreads), 0, stream, L, scores, stride, q0, q1, \
+                       cu_blocks, c, topk, sel, cnt);                                                      \
+    return 0;                                                                                              \
+  }
+  IRB_SEL_WAVE(8)
+  IRB_SEL_WAVE(16)
+  IRB_SEL_WAVE(32)
+#undef IRB_SEL_WAVE
 #define IRB_SEL_REG(NPT)                                                                                   \
   if (n_max <= kSelThreads * NPT) {                                                                        \
     hipLaunchKernelGGL(select_reg_kernel<NPT>, grid, dim3(kSelThreads), 0, stream, L, scores, stride, q0, q1, \
                        cu_blocks, c, topk, sel, cnt);                                                      \
     return 0;                                                                                              \
   }
-  IRB_SEL_REG(8)
   IRB_SEL_REG(16)
   IRB_SEL_REG(32)
   IRB_SEL_REG(64)

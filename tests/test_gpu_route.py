@@ -240,12 +240,13 @@ def test_select_rows_longer_than_lds(ties):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("S,c,topk", [(16384, 4, 512), (32768, 4, 256), (131072, 8, 256), (65536, 4, 300)])
+@pytest.mark.parametrize("S,c,topk", [(16384, 4, 512), (32768, 4, 256), (131072, 8, 256), (65536, 4, 300),
+                                    (8192, 4, 100), (2048, 4, 64), (4096, 4, 1000)])
 @pytest.mark.parametrize("ties", [False, True])
 def test_select_long_rows(S, c, topk, ties):
-    """Rows of 4096, 8192, 16384 and 16384 visible blocks (every register-resident
-    width of the select kernel), with the last rows made constant, two-valued
-    and of one repeated value above a sea of ties."""
+    """Rows of 512 to 16384 visible blocks (every one-wave-per-row and
+    register-resident width of the select kernels), with the last rows made
+    constant, two-valued and of one repeated value above a sea of ties."""
     rows = 12
     banner(f"select long rows S={S} c={c} topk={topk} ties={ties}")
     rng = np.random.default_rng(S + topk + ties)
