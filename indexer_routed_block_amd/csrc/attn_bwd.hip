@@ -374,7 +374,7 @@ constexpr bool dq_fuses_delta() { return sizeof(T) == 2 && D <= 128; }
 template <typename T, int D, int DV, bool kShared>
 __global__ void __launch_bounds__(256, (!kShared && dq_fuses_delta<T, D>()) ? 2 : 1)
 bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta,
-              T* __restrict__ dq, int G, int n_items, int latent) {
+              T* __restrict__ dq, int G, int n_items, int latent, int head_major) {
   constexpr bool kSplit = sizeof(T) == 4;
   constexpr int KS = D / 32, VS = DV / 32, NDQ = D / 16;
   constexpr int PAD = sizeof(T) == 2 ? 8 : 4;
@@ -385,9 +385,8 @@ bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ 
   int item, slice;
   if (kShared) { item = blockIdx.x; slice = wid; }
   else { item = blockIdx.x * 4 + wid; slice = 0; if (item >= n_items) return; }
-  const int kvh = item % a.Hkv;
-  const int t = (item / a.Hkv) % a.S_q;
-  const int b = item / (a.Hkv * a.S_q);
+  const QItem qi = decode_qitem(item, a.B, a.S_q, a.Hkv, kShared ? 0 : head_major);
+  const int kvh = qi.kvh, t = qi.t, b = qi.b;
   if constexpr (!kShared && dq_fuses_delta<T, D>()) {
     dq_item_gather<D, DV>(a, dout, lse, delta, dq, G, b, t, kvh,
                           reinterpret_cast<uint16_t*>(smem) + wid * 32 * (D + 8));
@@ -1271,7 +1270,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     }
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), lds, stream, a,
                        static_cast<const T*>(args.dout), args.lse, ws.delta, static_cast<T*>(args.dq), G,
-                       static_cast<int>(items), latent);
+                       static_cast<int>(items), latent, gather_head_major(a) ? 1 : 0);
   } else {
     const int slices = (G + 15) / 16;
     const size_t lds = static_cast<size_t>(32) * ((D + PAD) + (latent ? 0 : (DV + PAD))) * sizeof(T);
@@ -1283,7 +1282,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     }
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(items)), dim3(64 * slices), lds, stream, a,
                        static_cast<const T*>(args.dout), args.lse, ws.delta, static_cast<T*>(args.dq), G,
-                       static_cast<int>(items), latent);
+                       static_cast<int>(items), latent, 0);
   }
   const int nkt = (a.S_k + 15) / 16;
   const int64_t kitems = static_cast<int64_t>(a.B) * nkt * a.Hkv;

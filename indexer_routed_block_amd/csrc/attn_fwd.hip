@@ -518,7 +518,7 @@ IRB_DEV TileStats tile_stats_wave(const AttnArgs& a, int b, int qa, int BQ, int 
 template <typename T, int D, int DV, bool kShared, bool kDelta>
 __global__ void __launch_bounds__(256, (kShared || D > 128 || sizeof(T) == 4) ? 1 : 3)
 attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G, int n_items, int latent,
-                const T* __restrict__ dout, float* __restrict__ delta, int tile_bq, int thr_milli) {
+                const T* __restrict__ dout, float* __restrict__ delta, int tile_bq, int thr_milli, int head_major) {
   constexpr int PAD = sizeof(T) == 2 ? 8 : 4;
   extern __shared__ __align__(16) char smem[];
   const int wid = threadIdx.x >> 6;
@@ -533,9 +533,8 @@ attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G,
     if (item >= n_items) return;
     slab = smem + static_cast<size_t>(wid) * 32 * (DV + PAD) * sizeof(T);
   }
-  const int kvh = item % a.Hkv;
-  const int t = (item / a.Hkv) % a.S_q;
-  const int b = item / (a.Hkv * a.S_q);
+  const QItem qi = decode_qitem(item, a.B, a.S_q, a.Hkv, kShared ? 0 : head_major);
+  const int kvh = qi.kvh, t = qi.t, b = qi.b;
   if (!kShared && tile_bq > 0 && tile_stats_wave(a, b, (t / tile_bq) * tile_bq, tile_bq, thr_milli).dense) return;
   if constexpr (!kShared && sizeof(T) == 2 && D <= 128)
     fwd_item_gather<D, DV, kDelta>(a, out, lse, G, dout, delta, b, t, kvh, slab);
@@ -1041,7 +1040,7 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
     }
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), lds, stream, a,
                        static_cast<T*>(out), lse, G, static_cast<int>(items), latent, static_cast<const T*>(dout), delta,
-                       tile_bq, tile_thr_milli());
+                       tile_bq, tile_thr_milli(), gather_head_major(a) ? 1 : 0);
   } else {
     const int slices = (G + 15) / 16;
     const size_t lds = static_cast<size_t>(32) * ((D + PAD) + (latent ? 0 : (DV + PAD))) * sizeof(T);
@@ -1053,7 +1052,7 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
     }
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(items)), dim3(64 * slices), lds, stream, a,
                        static_cast<T*>(out), lse, G, static_cast<int>(items), latent, static_cast<const T*>(dout), delta,
-                       0, 0);
+                       0, 0, 0);
   }
   return 0;
 }

@@ -246,6 +246,14 @@ IRB_DEV int block_base(const Layout& L, const int32_t* cu_blocks, const Doc& d) 
   return (L.cu_seqlens && cu_blocks) ? cu_blocks[d.index] : 0;
 }
 
+// work item -> (b, t, KV head) of the per-query gather kernels: heads
+// fastest, or head-major (all queries of a head, then the next head)
+struct QItem { int b, t, kvh; };
+IRB_DEV QItem decode_qitem(int item, int B, int S_q, int Hkv, int head_major) {
+  if (head_major) return QItem{(item / S_q) % B, item % S_q, item / (B * S_q)};
+  return QItem{item / (Hkv * S_q), (item / Hkv) % S_q, item % Hkv};
+}
+
 // order-preserving uint32 key of a float: larger float -> larger key;
 // -0.0 folds onto +0.0; NaN maps below -inf.
 IRB_DEV uint32_t score_key(float f) {

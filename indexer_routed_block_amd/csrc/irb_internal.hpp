@@ -46,6 +46,18 @@ struct AttnArgs {
   int dtype;
 };
 
+// Per-query gather kernels visit work items (b, t, KV head).  When the K/V rows
+// of all heads outgrow the chip's last-level cache (256 MiB of Infinity Cache
+// on MI355X; half of it is the threshold), the items run head-major -- every
+// query of one KV head before the next head -- so the rows the running
+// wavefronts gather stay cache-resident; otherwise the heads of one query run
+// side by side (measured faster when everything fits).
+inline bool gather_head_major(const AttnArgs& a) {
+  const int64_t elem = a.dtype == IRB_BF16 ? 2 : 4;
+  const int64_t kv_bytes = static_cast<int64_t>(a.B) * a.S_k * a.Hkv * (a.Dqk + a.Dv) * elem;
+  return kv_bytes > (int64_t{128} << 20);
+}
+
 int launch_attn_fwd(const AttnArgs& a, void* out, float* lse, hipStream_t stream);
 // backward row statistic Delta[b,h,t] = rowsum(dO * o) with o recomputed in FP32
 int launch_attn_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t stream);
