@@ -749,18 +749,27 @@ IRB_DEV uint32_t route_tile_mask(const AttnArgs& a, int b, int t, int k0) {
     const int mid = (lo + hi) >> 1;
     if (r[mid] < k0) lo = mid + 1; else hi = mid;
   }
+  // the tile's keys are among the (at most 16) entries from lo on: their
+  // loads are independent and issue together
   uint32_t m = 0u;
-  for (int e = lo; e < n; ++e) {
-    const int id = r[e];
-    if (id >= k0 + 16) break;
-    m |= 1u << (id - k0);
+  const int e1 = min(n, lo + 16);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lo + i;
+    const int id = e < e1 ? r[e] : -1;
+    m |= (id >= k0 && id < k0 + 16) ? 1u << (id - k0) : 0u;
   }
   return m;
 }
 
 // One workgroup per (b, key tile).  pass 0 counts the reverse-list queries
 // whose route holds a key of the tile; pass 1 writes them, ascending, with
-// their key masks from hit_off[tile] on (never past cap).
+// their key masks from hit_off[tile] on (never past cap).  With one query per
+// reverse-list row (rev_bq = 1) every listed query is a hit by construction,
+// so pass 0 only copies the list's count and pass 1 places each query at its
+// list position with no search-dependent scan (a listed query whose route
+// misses the tile, possible only with a stale list, gets mask 0 and adds
+// nothing to dK / dV).
 __global__ void __launch_bounds__(256)
 bwd_hits_kernel(AttnBwdArgs args, int nkt, int pass, int64_t* __restrict__ hit_off, int32_t* __restrict__ hit_t,
                 uint32_t* __restrict__ hit_m, int64_t cap) {
@@ -775,6 +784,21 @@ bwd_hits_kernel(AttnBwdArgs args, int nkt, int pass, int64_t* __restrict__ hit_o
   const int64_t ncand = static_cast<int64_t>(cnt) * bq;
   const int64_t base = pass ? hit_off[lrow] : 0;
   const int64_t end = pass ? min(hit_off[lrow + 1], cap) : 0;
+  if (bq == 1) {
+    if (!pass) {
+      if (threadIdx.x == 0) hit_off[lrow] = cnt;
+      return;
+    }
+    for (int c = threadIdx.x; c < cnt; c += 256) {
+      const int64_t pos = base + c;
+      if (pos >= end) break;
+      const int qt = qtiles[c];
+      const bool ok = qt >= 0 && qt < a.S_q;
+      hit_t[pos] = ok ? qt : -1;
+      hit_m[pos] = ok ? route_tile_mask(a, b, qt, k0) : 0u;
+    }
+    return;
+  }
   int64_t done = 0;
   for (int64_t c0 = 0; c0 < ncand; c0 += 256) {
     const int64_t c = c0 + threadIdx.x;

@@ -50,7 +50,7 @@ def _check_lse(got, want, dtype):
     assert np.max(np.abs(got[fin] - want[fin]), initial=0.0) <= tol
 
 
-def _run_fwd_bwd(wl, x, routes, lens, scale, do_bwd, q_view=None):
+def _run_fwd_bwd(wl, x, routes, lens, scale, do_bwd, q_view=None, rev_bq=1):
     dt = act_dtype(wl.dtype)
     q = to_dev(x["q"], dt) if q_view is None else q_view
     k = to_dev(x["k"], dt)
@@ -63,9 +63,9 @@ def _run_fwd_bwd(wl, x, routes, lens, scale, do_bwd, q_view=None):
     if not do_bwd:
         return
     S = x["q"].shape[1]
-    rc, ri = irb.build_block_lists(r_d, l_d, S, 1, 16, reverse=True)
+    rc, ri = irb.build_block_lists(r_d, l_d, S, rev_bq, 16, reverse=True)
     dO = to_dev(x["dO"], dt)
-    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, 1, 16, scale)
+    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, rev_bq, 16, scale)
     rdq, rdk, rdv = oracle.attention_bwd(x["q"], x["k"], x["v"], routes, x["dO"], scale)
     attn_tol_check(host(dq), rdq, dt, "dq")
     attn_tol_check(host(dk), rdk, dt, "dk")
@@ -79,12 +79,14 @@ def test_tiny_fp32_pipeline_routes_fwd_bwd():
     _run_fwd_bwd(wl, x, routes, lens, 1.0 / math.sqrt(wl.D), True)
 
 
-@pytest.mark.parametrize("S,width", [(1024, 160), (333, 70)])
-def test_gqa_bf16_random_routes_fwd_bwd(S, width):
-    banner(f"attn gqa bf16 S={S} width={width}")
+@pytest.mark.parametrize("S,width,rev_bq", [(1024, 160, 1), (333, 70, 1), (1024, 160, 16), (333, 70, 3)])
+def test_gqa_bf16_random_routes_fwd_bwd(S, width, rev_bq):
+    """rev_bq > 1: reverse lists of query tiles, whose queries the backward
+    searches for hits; rev_bq = 1: every listed query is a hit."""
+    banner(f"attn gqa bf16 S={S} width={width} rev_bq={rev_bq}")
     wl, x = _qkv("varlen", S)
     routes, lens = _random_routes(S, 1, S, width, empty_rows=[(0, 5), (0, S - 1)])
-    _run_fwd_bwd(wl, x, routes, lens, 1.0 / math.sqrt(wl.D), True)
+    _run_fwd_bwd(wl, x, routes, lens, 1.0 / math.sqrt(wl.D), True, rev_bq=rev_bq)
 
 
 def test_gqa_bf16_window_routes_fwd():
