@@ -31,31 +31,65 @@ int launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream) {
 
 constexpr int kMarkWaves = 4;
 
-// one wavefront per query row (b, t)
+// id / bk by a multiply-high with m = floor((2^32 - 1) / bk) + 1, exact for
+// id * bk < 2^32 (the host checks S_k * bk); m = 0 means plain division
+IRB_DEV int div_bk(int id, int bk, uint32_t m) {
+  return m ? static_cast<int>(__umulhi(static_cast<uint32_t>(id), m)) : id / bk;
+}
+
+// One wavefront per query row (b, t).  kVec rows (width a multiple of 4,
+// 16-byte aligned) are read four entries per lane per load; a tile bit is set
+// once per run of equal tiles (the route is ascending).
+template <bool kVec>
 __global__ void __launch_bounds__(kMarkWaves * 64)
 mark_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int B, int S_q, int S_k, int Lw,
-            int bq, int bk, int reverse, int n_rows, int words, uint32_t* __restrict__ bits) {
+            int bq, int bk, uint32_t bkm, int reverse, int n_rows, int words, uint32_t* __restrict__ bits) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kMarkWaves + wid;
   if (row >= static_cast<int64_t>(B) * S_q) return;
   const int b = static_cast<int>(row / S_q), t = static_cast<int>(row % S_q);
-  const int n = min(lens[row], Lw);
+  const int n = max(0, min(lens[row], Lw));
   const int32_t* r = routes + row * Lw;
   const int qt = t / bq;
   uint32_t* mat = bits + static_cast<int64_t>(b) * n_rows * words;
+  auto mark = [&](int kt) __attribute__((always_inline)) {
+    if (reverse) atomicOr(&mat[static_cast<int64_t>(kt) * words + (qt >> 5)], 1u << (qt & 31));
+    else atomicOr(&mat[static_cast<int64_t>(qt) * words + (kt >> 5)], 1u << (kt & 31));
+  };
   int prev_last = -1;
-  for (int e0 = 0; e0 < n; e0 += 64) {
-    const int e = e0 + lane;
-    const int id = (e < n) ? r[e] : -1;
-    const bool ok = id >= 0 && id < S_k;            // out-of-range IDs are ignored
-    const int kt = ok ? id / bk : -1;
-    int before = __shfl_up(kt, 1, 64);
-    if (lane == 0) before = prev_last;
-    if (ok && kt != before) {
-      if (reverse) atomicOr(&mat[static_cast<int64_t>(kt) * words + (qt >> 5)], 1u << (qt & 31));
-      else atomicOr(&mat[static_cast<int64_t>(qt) * words + (kt >> 5)], 1u << (kt & 31));
+  if constexpr (kVec) {
+    for (int e0 = 0; e0 < n; e0 += 256) {
+      const int e = e0 + 4 * lane;
+      int4 v = make_int4(-1, -1, -1, -1);
+      if (e < n) v = *reinterpret_cast<const int4*>(r + e);
+      const int ids[4] = {v.x, v.y, v.z, v.w};
+      int kt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = e + j < n && ids[j] >= 0 && ids[j] < S_k;   // out-of-range IDs are ignored
+        kt[j] = ok ? div_bk(ids[j], bk, bkm) : -1;
+      }
+      int before = __shfl_up(kt[3], 1, 64);
+      if (lane == 0) before = prev_last;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (kt[j] >= 0 && kt[j] != before) mark(kt[j]);
+        if (kt[j] >= 0) before = kt[j];
+      }
+      // last valid tile of the chunk: lanes past n report -1, so take the max
+      prev_last = max(prev_last, wave_max_int(max(max(kt[0], kt[1]), max(kt[2], kt[3]))));
     }
-    prev_last = __shfl(kt, 63, 64);
+  } else {
+    for (int e0 = 0; e0 < n; e0 += 64) {
+      const int e = e0 + lane;
+      const int id = (e < n) ? r[e] : -1;
+      const bool ok = id >= 0 && id < S_k;            // out-of-range IDs are ignored
+      const int kt = ok ? div_bk(id, bk, bkm) : -1;
+      int before = __shfl_up(kt, 1, 64);
+      if (lane == 0) before = prev_last;
+      if (ok && kt != before) mark(kt);
+      prev_last = max(prev_last, wave_max_int(kt));
+    }
   }
 }
 
@@ -103,10 +137,18 @@ int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_
   int rc = launch_fill_i32(reinterpret_cast<int32_t*>(bitmap), static_cast<int64_t>(B) * n_rows * words, 0, stream);
   if (rc) return rc;
   const int64_t qrows = static_cast<int64_t>(B) * S_q;
-  if (qrows > 0)
-    hipLaunchKernelGGL(mark_kernel, dim3(static_cast<unsigned>((qrows + kMarkWaves - 1) / kMarkWaves)),
-                       dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw, bq, bk, reverse, n_rows, words,
-                       bitmap);
+  if (qrows > 0) {
+    const uint32_t bkm = (bk >= 2 && static_cast<uint64_t>(S_k) * static_cast<uint64_t>(bk) < (1ull << 32))
+                             ? 0xFFFFFFFFu / static_cast<uint32_t>(bk) + 1u
+                             : 0u;
+    const dim3 grid(static_cast<unsigned>((qrows + kMarkWaves - 1) / kMarkWaves));
+    if ((Lw % 4) == 0 && (reinterpret_cast<uintptr_t>(routes) & 15) == 0)
+      hipLaunchKernelGGL(mark_kernel<true>, grid, dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw, bq,
+                         bk, bkm, reverse, n_rows, words, bitmap);
+    else
+      hipLaunchKernelGGL(mark_kernel<false>, grid, dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw, bq,
+                         bk, bkm, reverse, n_rows, words, bitmap);
+  }
   if (n_rows > 0 && B > 0)
     hipLaunchKernelGGL(emit_kernel, dim3(static_cast<unsigned>(n_rows), static_cast<unsigned>(B)), dim3(256), 0,
                        stream, bitmap, n_rows, words, n_other, counts, indices, width);

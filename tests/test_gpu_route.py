@@ -211,13 +211,17 @@ def test_compact_latent_indices():
     assert rbad == 0 and int(host(bad)[0]) == 0
 
 
-@pytest.mark.parametrize("bq,bk,reverse", [(1, 16, True), (16, 64, False), (16, 64, True), (3, 5, False),
-                                           (3, 5, True), (128, 16, True), (1, 1, False)])
-def test_block_lists_bit_exact(bq, bk, reverse):
-    banner(f"lists bq={bq} bk={bk} reverse={reverse}")
-    rng = np.random.default_rng(bq * 100 + bk)
+@pytest.mark.parametrize("bq,bk,reverse,width", [(1, 16, True, 40), (16, 64, False, 40), (16, 64, True, 40),
+                                                 (3, 5, False, 40), (3, 5, True, 40), (128, 16, True, 40),
+                                                 (1, 1, False, 40), (1, 16, True, 37), (3, 5, False, 301),
+                                                 (1, 16, True, 600), (16, 64, False, 600)])
+def test_block_lists_bit_exact(bq, bk, reverse, width):
+    """Route widths that are a multiple of 4 take the 16-byte-load path, others
+    the per-entry path; widths above 256 span several loads per lane."""
+    banner(f"lists bq={bq} bk={bk} reverse={reverse} width={width}")
+    rng = np.random.default_rng(bq * 100 + bk + width)
     B, S = 2, 700
-    ids = synth.random_routes(rng, B, S, 40, causal=True, frac_invalid=0.2)
+    ids = synth.random_routes(rng, B, S, width, causal=True, frac_invalid=0.2)
     routes, lens, _ = oracle.compact_routes(ids, S)
     counts, indices = irb.build_block_lists(to_dev(routes), to_dev(lens), S, bq, bk, reverse)
     rc, ri = oracle.block_lists(routes, lens, S, bq, bk, reverse)
