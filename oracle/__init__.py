@@ -158,6 +158,34 @@ def compress_keys(kI, gamma, eps, freqs, c, cu_seqlens=None, row_lens=None, d_ro
     return kc, cu_blocks
 
 
+def prepare_index_queries(q_raw, gamma, freqs, eps=1e-5, d_rope=None):
+    """Normalised, rotated index queries [..., S, H, D] (float64, not rounded).
+
+    QSA page: the indexer's ``q_layernorm`` (RMSNorm over the head dimension,
+    gain ``gamma``, variance epsilon ``eps``) normalises every (token, head)
+    row of the raw index queries, and ``apply_qsa_rope`` rotates it with the
+    rotary row of the query's own token (``cat(cos, sin)`` of width
+    ``D_rope``; dimension ``i < D_rope/2`` pairs with ``i + D_rope/2``;
+    dimensions from ``D_rope`` on pass through).  ``q_raw`` is [B, S, H, D],
+    ``freqs`` [B, S, D_rope].
+    """
+    q = np.asarray(q_raw, dtype=np.float64)
+    freqs = np.asarray(freqs, dtype=np.float64)
+    R = freqs.shape[-1] if d_rope is None else d_rope
+    half = R // 2
+    g = np.asarray(gamma, dtype=np.float64)
+    u = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps) * g
+    out = u.copy()
+    if half:
+        cos = freqs[..., :half][:, :, None, :]
+        sin = freqs[..., half:2 * half][:, :, None, :]
+        x1 = u[..., :half]
+        x2 = u[..., half:2 * half]
+        out[..., :half] = x1 * cos - x2 * sin
+        out[..., half:2 * half] = x2 * cos + x1 * sin
+    return out
+
+
 # ---------------------------------------------------------------------------
 # a2: indexer scores
 # ---------------------------------------------------------------------------
