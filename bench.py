@@ -3,7 +3,9 @@
 One step = the whole hot path over one batch of synthetic input already
 resident in HBM, every stage a call of the C ABI on one stream:
 
-* routed workloads: key compression -> block scoring + top-k selection
+* routed workloads: index-query preparation (RMSNorm + RoPE; timed beside
+  the route pipeline, whose index queries the workload already gives
+  normalised) -> key compression -> block scoring + top-k selection
   (fused, bounded score chunks) -> route expansion -> sparse GQA attention
   forward, and, where the workload trains (packed 32768, 131072), reverse
   block lists -> attention backward;
@@ -152,6 +154,7 @@ def main():
         kc = torch.empty((B, nb_blocks, wl.D_idx), dtype=torch.float32, device=dev)
         cu_blocks = None if cu is None else torch.empty(cu.numel(), dtype=torch.int32, device=dev)
         lay = irb.make_layout(B, S, cu, None)
+        qprep = torch.empty_like(d["qI"])
         q, k, v = d["q"], d["k"], d["v"]
         dO = d.get("dO")
     Hq = wl.Hq
@@ -188,6 +191,12 @@ def main():
         if wl.latent:
             timed("compact", lambda: C(lib.irb_compact_routes(P(idx), S, W, S, P(routes), P(lens), P(bad), sptr)), rec)
             return
+        # index-query preparation (RMSNorm + RoPE at each query's token), timed
+        # beside the route pipeline: the workload's index queries are already
+        # normalised, so scoring keeps them and qprep is not read afterwards
+        timed("prepare_queries", lambda: C(lib.irb_prepare_index_queries(
+            P(d["qI"]), irb._dtype_code(d["qI"]), B * S, wl.H_idx, wl.D_idx, P(d["gamma"]), 1e-5, P(d["freqs"]),
+            d["freqs"].shape[-1], P(qprep), sptr)), rec)
         timed("compress", lambda: C(lib.irb_compress_keys(
             irb.ctypes.byref(lay), c, P(d["kI"]), irb._dtype_code(d["kI"]), d["kI"].stride(0), d["kI"].stride(1),
             wl.D_idx, P(d["gamma"]), 1e-5, P(d["freqs"]), d["freqs"].shape[-1], P(kc), P(cu_blocks), sptr)), rec)
@@ -260,6 +269,8 @@ def main():
     else:
         nb_t, valid_t = _layout_counts(wl, S, x["cu_seqlens"])
         sparse_pairs = float(np.sum(np.where(nb_t > topk, nb_t, 0)))
+        work["prepare_queries"] = ("hbm", 2.0 * B * S * wl.H_idx * wl.D_idx * d["qI"].element_size()
+                                   + 4.0 * B * S * d["freqs"].shape[-1])
         work["compress"] = ("hbm", B * S * wl.D_idx * (2 if dt == torch.bfloat16 else 4)
                             + B * nb_blocks * (4 * wl.D_idx + 4 * d["freqs"].shape[-1]))
         work["score_select"] = ("mfma", 2.0 * wl.H_idx * wl.D_idx * sparse_pairs)

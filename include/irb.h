@@ -4,6 +4,7 @@
  *
  * Pipeline (one call per step):
  *   irb_compress_keys            raw index keys -> compressed block keys
+ *   irb_prepare_index_queries    raw index queries -> normalised, rotated queries
  *   irb_indexer_score_tile       weighted-ReLU block scores for a query x block tile
  *   irb_select_topk_regions      top-k blocks per query (ascending, -1 suffix)
  *   irb_route_topk_fused         the two above without materialising scores
@@ -114,6 +115,28 @@ int irb_compress_keys(const irb_layout* layout, int c, const void* k_idx, int dt
                       int64_t stride_b, int64_t stride_t, int D_idx, const float* gamma,
                       float eps, const float* freqs, int D_rope, float* kc, int32_t* cu_blocks,
                       void* stream);
+
+/*
+ * Index-query preparation (ahead of a2) -- [QSA] Qwen3_8_FlashNextQSAIndexer:
+ * q_layernorm normalises every (token, head) row of the raw index queries
+ * over the head dimension (u = x * rsqrt(mean(x^2) + eps) * gamma), and
+ * apply_qsa_rope rotates it with the rotary row of the row's own token
+ * (row = cat(cos[D_rope/2], sin[D_rope/2]); dimension i < D_rope/2 pairs with
+ * i + D_rope/2; dimensions >= D_rope pass through).  Both steps run in FP32
+ * and the result is rounded once (round-to-nearest-even) to the input dtype:
+ * the normalised, rotated index queries select_qsa_token_ids expects.
+ *
+ *   q_raw   [n_tokens, H_idx, D_idx] dtype, contiguous, 16-byte aligned
+ *   gamma   [D_idx] fp32 gain
+ *   rope    [n_tokens, D_rope] fp32 contiguous rotary rows, built at each token's
+ *           document-relative position (may be NULL when D_rope == 0)
+ *   q_out   OUT [n_tokens, H_idx, D_idx] dtype, 16-byte aligned; may alias q_raw
+ * Requires D_idx in {32, 64, 128, 256, 512}, D_rope even, 0 <= D_rope <= D_idx,
+ * eps >= 0.  A batch [B, S, ...] is n_tokens = B * S.  n_tokens == 0 is a no-op.
+ */
+int irb_prepare_index_queries(const void* q_raw, int dtype, int64_t n_tokens, int H_idx, int D_idx,
+                              const float* gamma, float eps, const float* rope, int D_rope, void* q_out,
+                              void* stream);
 
 /*
  * a2 -- [CSA] indexer_score_tile (weighted-ReLU scoring into one bounded FP32

@@ -41,6 +41,7 @@ _SIGS = {
     "irb_last_error": ([], ctypes.c_char_p),
     "irb_version": ([], ctypes.c_char_p),
     "irb_compress_keys": ([_P, _I, _P, _I, _I64, _I64, _I, _P, _F, _P, _I, _P, _P, _P], _I),
+    "irb_prepare_index_queries": ([_P, _I, _I64, _I, _I, _P, _F, _P, _I, _P, _P], _I),
     "irb_indexer_score_tile": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _I, _P, _I64, _P], _I),
     "irb_select_topk_regions": ([_P, _P, _I64, _I, _I, _P, _I, _I, _P, _P, _P], _I),
     "irb_route_topk_fused_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
@@ -150,6 +151,23 @@ def compress_keys(k_idx, gamma, freqs, c, eps=1e-5, cu_seqlens=None, row_lens=No
                                  k_idx.stride(1), D, _ptr(gamma), eps, _ptr(freqs), freqs.shape[-1], _ptr(kc),
                                  _ptr(cu_blocks), _stream(dev)))
     return kc, cu_blocks
+
+
+def prepare_index_queries(q_raw, gamma, freqs=None, eps=1e-5, out=None):
+    """irb_prepare_index_queries: RMSNorm over the head dimension, then RoPE at each
+    token's rotary row; q_raw [B, S, H, D] contiguous, freqs [B, S, D_rope] fp32
+    (None: no rotation).  Returns [B, S, H, D] in q_raw's dtype (``out`` may be q_raw)."""
+    _gpu(q_raw, gamma, freqs, out)
+    lib = load_library()
+    if not q_raw.is_contiguous() or (freqs is not None and not freqs.is_contiguous()):
+        raise ValueError("prepare_index_queries: q_raw and freqs must be contiguous")
+    B, S, H, D = q_raw.shape
+    if out is None:
+        out = torch.empty_like(q_raw)
+    d_rope = 0 if freqs is None else freqs.shape[-1]
+    _check(lib.irb_prepare_index_queries(_ptr(q_raw), _dtype_code(q_raw), B * S, H, D, _ptr(gamma), eps, _ptr(freqs),
+                                         d_rope, _ptr(out), _stream(q_raw.device)))
+    return out
 
 
 def indexer_score_tile(q_idx, w, kc, c, q0=0, q1=None, j0=0, j1=None, score_scale=None, cu_blocks=None,

@@ -101,6 +101,26 @@ int irb_compress_keys(const irb_layout* layout, int c, const void* k_idx, int dt
                                            cu_blocks, static_cast<hipStream_t>(stream)));
 }
 
+int irb_prepare_index_queries(const void* q_raw, int dtype, int64_t n_tokens, int H_idx, int D_idx,
+                              const float* gamma, float eps, const float* rope, int D_rope, void* q_out,
+                              void* stream) {
+  const char* fn = "irb_prepare_index_queries";
+  if (int r = check_dtype(fn, dtype)) return r;
+  if (n_tokens < 0 || H_idx < 1 || n_tokens > (int64_t{1} << 40) / H_idx)
+    return fail(IRB_ERR_INVALID, "%s: need n_tokens >= 0 and H_idx >= 1", fn);
+  if (D_idx != 32 && D_idx != 64 && D_idx != 128 && D_idx != 256 && D_idx != 512)
+    return fail(IRB_ERR_INVALID, "%s: D_idx must be 32, 64, 128, 256 or 512 (got %d)", fn, D_idx);
+  if (D_rope < 0 || D_rope > D_idx || D_rope % 2) return fail(IRB_ERR_INVALID, "%s: D_rope must be even and <= D_idx", fn);
+  if (!q_raw || !gamma || !q_out || (D_rope > 0 && !rope)) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if ((reinterpret_cast<uintptr_t>(q_raw) | reinterpret_cast<uintptr_t>(q_out)) & 15)
+    return fail(IRB_ERR_INVALID, "%s: q_raw and q_out must be 16-byte aligned", fn);
+  if (!(eps >= 0.f)) return fail(IRB_ERR_INVALID, "%s: eps must be >= 0", fn);
+  if (n_tokens == 0) return 0;
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_prep_queries(q_raw, dtype, n_tokens * H_idx, H_idx, D_idx, gamma, eps, rope, D_rope,
+                                               q_out, static_cast<hipStream_t>(stream)));
+}
+
 int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx,
                            const float* w, const float* kc, const int32_t* cu_blocks, int c, float score_scale,
                            int q0, int q1, int j0, int j1, float* out, int64_t out_row_stride, void* stream) {

@@ -11,6 +11,11 @@ int launch_compress(const Layout& L, int c, const void* k, int dtype, int64_t sb
                     const float* gamma, float eps, const float* freqs, int R, float* kc,
                     int32_t* cu_blocks, hipStream_t stream);
 
+// normalised, rotated index queries: n_rows = tokens * H rows of D contiguous
+// elements; rope rows [tokens, R]; out may alias q
+int launch_prep_queries(const void* q, int dtype, int64_t n_rows, int H, int D, const float* gamma, float eps,
+                        const float* rope, int R, void* out, hipStream_t stream);
+
 // write_invisible: also write -inf at the tile's invisible entries (the fused
 // route path skips them: selection never reads them); queries with at most
 // skip_nb visible blocks are not scored (-1: score every query)

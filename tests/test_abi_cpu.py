@@ -145,3 +145,28 @@ def test_python_binding_has_no_cpu_path():
     r = torch.zeros(1, 8, 4, dtype=torch.int32)
     with pytest.raises(RuntimeError, match="GPU only"):
         irb.sparse_gqa_attention_fwd(q, q[:, :, :1], q[:, :, :1], r, r[..., 0])
+
+
+def test_prepare_index_queries_validation():
+    lib = irb.load_library()
+    call = lambda q=FAKE, dt=1, n=10, H=4, D=128, g=FAKE, eps=1e-5, r=FAKE, R=128, o=FAKE: _err(
+        lib.irb_prepare_index_queries(q, dt, n, H, D, g, eps, r, R, o, None))
+    s, m = call(dt=7)
+    assert s == 2
+    s, m = call(D=48)
+    assert s == 3 and "D_idx" in m
+    s, m = call(R=7)
+    assert s == 3 and "D_rope" in m
+    s, m = call(R=256)
+    assert s == 3 and "D_rope" in m
+    s, m = call(q=None)
+    assert s == 3 and "NULL" in m
+    s, m = call(r=None)
+    assert s == 3 and "NULL" in m
+    s, m = call(o=ctypes.c_void_p(0x1008))
+    assert s == 3 and "aligned" in m
+    s, m = call(eps=-1.0)
+    assert s == 3 and "eps" in m
+    s, m = call(H=0)
+    assert s == 3
+    assert call(n=0)[0] == 0          # nothing to do: no device call
