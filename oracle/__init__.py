@@ -186,6 +186,28 @@ def prepare_index_queries(q_raw, gamma, freqs, eps=1e-5, d_rope=None):
     return out
 
 
+def pack_region_bitmap(ids, regions):
+    """Membership words [..., ceil(regions / 32)] int32 of every id row.
+
+    CSA page, ``pack_region_bitmap``: bit ``r % 32`` of word ``r // 32`` is set
+    exactly when region ``r`` occurs in the row; ids at or above ``regions``
+    are padding and repeated ids are allowed.  Negative ids are padding too
+    (the route lists here pad with -1).  Words are returned as int32 bit
+    patterns (bit 31 is the sign bit).
+    """
+    ids = np.asarray(ids)
+    lead = ids.shape[:-1]
+    words = (regions + 31) // 32
+    flat = ids.reshape(-1, ids.shape[-1])
+    out = np.zeros((flat.shape[0], words), dtype=np.uint32)
+    for r in range(flat.shape[0]):
+        for x in flat[r]:
+            x = int(x)
+            if 0 <= x < regions:
+                out[r, x // 32] |= np.uint32(1) << np.uint32(x % 32)
+    return out.view(np.int32).reshape(lead + (words,))
+
+
 # ---------------------------------------------------------------------------
 # a2: indexer scores
 # ---------------------------------------------------------------------------
