@@ -5,7 +5,8 @@ resident in HBM, every stage a call of the C ABI on one stream:
 
 * routed workloads: index-query preparation (RMSNorm + RoPE; timed beside
   the route pipeline, whose index queries the workload already gives
-  normalised) -> key compression -> block scoring + top-k selection
+  normalised) -> key compression -> block scoring + top-k selection ->
+  (the selection's region bitmap, also timed beside the pipeline)
   (fused, bounded score chunks) -> route expansion -> sparse GQA attention
   forward, and, where the workload trains (packed 32768, 131072), reverse
   block lists -> attention backward;
@@ -155,6 +156,7 @@ def main():
         cu_blocks = None if cu is None else torch.empty(cu.numel(), dtype=torch.int32, device=dev)
         lay = irb.make_layout(B, S, cu, None)
         qprep = torch.empty_like(d["qI"])
+        sel_bitmap = torch.empty((B, S, (nb_blocks + 31) // 32), dtype=torch.int32, device=dev)
         q, k, v = d["q"], d["k"], d["v"]
         dO = d.get("dO")
     Hq = wl.Hq
@@ -207,6 +209,10 @@ def main():
             irb.ctypes.byref(lay), P(d["qI"]), irb._dtype_code(d["qI"]), wl.H_idx, wl.D_idx, P(d["w"]), P(kc),
             P(cu_blocks), c, 1.0 / math.sqrt(wl.D_idx), topk, q0, S, P(sel), P(cnt), P(fused_ws),
             fused_ws.numel(), sptr)), rec)
+        # route bitmap of the selection (membership words per query), timed
+        # beside the route pipeline; nothing downstream reads it
+        timed("region_bitmap", lambda: C(lib.irb_pack_region_bitmap(
+            P(sel), B * S, topk, nb_blocks, P(sel_bitmap), sptr)), rec)
         timed("expand", lambda: C(lib.irb_expand_and_compact_routes(
             irb.ctypes.byref(lay), P(sel), P(cnt), topk, c, window, P(cu_blocks), L, P(routes), P(lens), sptr)), rec)
 
@@ -273,6 +279,7 @@ def main():
                                    + 4.0 * B * S * d["freqs"].shape[-1])
         work["compress"] = ("hbm", B * S * wl.D_idx * (2 if dt == torch.bfloat16 else 4)
                             + B * nb_blocks * (4 * wl.D_idx + 4 * d["freqs"].shape[-1]))
+        work["region_bitmap"] = ("hbm", B * S * (4.0 * topk + 4.0 * ((nb_blocks + 31) // 32)))
         work["score_select"] = ("mfma", 2.0 * wl.H_idx * wl.D_idx * sparse_pairs)
         work["expand"] = ("hbm", float(np.sum(valid_t)) * (4 * topk + 4 * L + 4))
         if q0 > 0:

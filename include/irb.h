@@ -11,6 +11,7 @@
  *   irb_expand_and_compact_routes blocks + tail + window -> ascending token routes
  *   irb_compact_routes           arbitrary signed ID lists -> ascending valid prefix
  *   irb_build_block_lists        forward (query->key) / reverse (key->query) tile lists
+ *   irb_pack_region_bitmap       id rows -> region membership words
  *   irb_sparse_gqa_attention_fwd GQA attention over the routed keys only
  *   irb_sparse_gqa_attention_bwd its gradients; key/value side over reverse lists
  *
@@ -227,6 +228,21 @@ int irb_expand_and_compact_routes(const irb_layout* layout, const int32_t* sel, 
  */
 int irb_compact_routes(const int32_t* ids_in, int64_t n_rows, int width, int64_t key_count,
                        int32_t* ids_out, int32_t* lens, int32_t* out_of_range, void* stream);
+
+/*
+ * Route bitmap -- [CSA] pack_region_bitmap: each row of int32 region ids
+ * becomes ceil(regions / 32) membership words, bit r % 32 of word r / 32 set
+ * exactly when region r occurs in the row, packed without any scatter
+ * workspace.  Ids at or above `regions` are padding, as on the page; negative
+ * ids are padding too (this library pads route lists with -1).  Repeats are
+ * allowed and the rows need not be sorted.  Words hold the bit pattern as int32.
+ *
+ *   ids     [rows, slots] int32 (any leading shape flattened to rows)
+ *   bitmap  OUT [rows, ceil(regions / 32)] int32; every word is written
+ * Requires slots >= 1, 1 <= regions <= 131072.  rows == 0 is a no-op.
+ */
+int irb_pack_region_bitmap(const int32_t* ids, int64_t rows, int slots, int regions, int32_t* bitmap,
+                           void* stream);
 
 /*
  * a5 -- [FA4] _block_lists / _selected_block_lists / _BackwardBlockPartition:

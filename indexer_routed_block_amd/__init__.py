@@ -48,6 +48,7 @@ _SIGS = {
     "irb_route_topk_fused": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "irb_expand_and_compact_routes": ([_P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P], _I),
     "irb_compact_routes": ([_P, _I64, _I, _I64, _P, _P, _P, _P], _I),
+    "irb_pack_region_bitmap": ([_P, _I64, _I, _I, _P, _P], _I),
     "irb_build_block_lists_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
     "irb_build_block_lists": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _SZ, _P], _I),
     "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
@@ -226,6 +227,21 @@ def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_
                                     _ptr(cu_blocks), c, scale, topk, q0, q1, _ptr(sel), _ptr(cnt), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(dev)))
     return sel, cnt
+
+
+def pack_region_bitmap(ids, regions, out=None):
+    """irb_pack_region_bitmap: int32 membership words [..., ceil(regions / 32)] of int32 id rows [..., slots]."""
+    _gpu(ids, out)
+    lib = load_library()
+    if ids.dtype != torch.int32 or not ids.is_contiguous():
+        raise ValueError("pack_region_bitmap: ids must be contiguous int32")
+    slots = ids.shape[-1]
+    rows = ids.numel() // max(slots, 1)
+    words = (regions + 31) // 32
+    if out is None:
+        out = torch.empty(ids.shape[:-1] + (words,), dtype=torch.int32, device=ids.device)
+    _check(lib.irb_pack_region_bitmap(_ptr(ids), rows, slots, regions, _ptr(out), _stream(ids.device)))
+    return out
 
 
 def expand_and_compact_routes(sel, cnt, c, window, topk, L=None, cu_blocks=None, cu_seqlens=None, row_lens=None):

@@ -237,6 +237,17 @@ int irb_compact_routes(const int32_t* ids_in, int64_t n_rows, int width, int64_t
                                           static_cast<hipStream_t>(stream)));
 }
 
+int irb_pack_region_bitmap(const int32_t* ids, int64_t rows, int slots, int regions, int32_t* bitmap, void* stream) {
+  const char* fn = "irb_pack_region_bitmap";
+  if (rows < 0 || rows > 0x7fffffffLL * 4) return fail(IRB_ERR_INVALID, "%s: rows out of range", fn);
+  if (slots < 1) return fail(IRB_ERR_INVALID, "%s: slots must be >= 1", fn);
+  if (regions < 1 || regions > 131072) return fail(IRB_ERR_INVALID, "%s: regions must be in 1..131072 (got %d)", fn, regions);
+  if (rows == 0) return 0;
+  if (!ids || !bitmap) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_bitmap(ids, rows, slots, regions, bitmap, static_cast<hipStream_t>(stream)));
+}
+
 size_t irb_build_block_lists_workspace_size(int B, int S_q, int S_k, int block_q, int block_k) {
   if (B < 1 || S_q < 1 || S_k < 1 || block_q < 1 || block_k < 1) return 0;
   const int64_t nqt = (S_q + block_q - 1) / block_q, nkt = (S_k + block_k - 1) / block_k;

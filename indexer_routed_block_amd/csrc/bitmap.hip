@@ -1,0 +1,56 @@
+// Region membership bitmaps of id rows.
+//
+// CSA page (nemo_automodel...step5.sparse), pack_region_bitmap: each row of
+// sorted int32 region ids becomes ceil(regions / 32) membership words (bit
+// r % 32 of word r / 32 set when region r occurs in the row), packed directly
+// without an int64 scatter workspace; ids at or above `regions` are padding
+// and repeats are allowed.  Negative ids are padding here as well (the route
+// lists of this library pad with -1), and the rows need not be sorted.
+//
+// One wavefront per row: the row's words live in the wave's LDS slice, every
+// valid id ORs its bit in with an LDS atomic, and the words are then written
+// out in one coalesced pass (zeros included), so no output clearing pass is
+// needed.
+#include "irb_internal.hpp"
+
+namespace irb {
+
+constexpr int kBmWaves = 4;
+
+__global__ void __launch_bounds__(kBmWaves * 64)
+bitmap_kernel(const int32_t* __restrict__ ids, int64_t rows, int slots, int regions, int words,
+              uint32_t* __restrict__ out) {
+  extern __shared__ uint32_t bm_all[];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kBmWaves + wid;
+  if (row >= rows) return;                       // whole wavefront; no workgroup barrier below
+  uint32_t* bm = bm_all + wid * words;
+  for (int w = lane; w < words; w += 64) bm[w] = 0u;
+  wave_lds_sync();
+  const int32_t* r = ids + row * slots;
+#pragma unroll 4
+  for (int e = lane; e < slots; e += 64) {
+    const int x = r[e];
+    if (x >= 0 && x < regions) atomicOr(&bm[x >> 5], 1u << (x & 31));
+  }
+  wave_lds_sync();
+  uint32_t* o = out + row * words;
+  for (int w = lane; w < words; w += 64) o[w] = bm[w];
+}
+
+int launch_bitmap(const int32_t* ids, int64_t rows, int slots, int regions, int32_t* bitmap, hipStream_t stream) {
+  if (rows == 0) return 0;
+  const int words = (regions + 31) / 32;
+  const size_t lds = static_cast<size_t>(kBmWaves) * words * sizeof(uint32_t);
+  if (lds > 48 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bitmap_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return static_cast<int>(e);
+  }
+  hipLaunchKernelGGL(bitmap_kernel, dim3(static_cast<unsigned>((rows + kBmWaves - 1) / kBmWaves)),
+                     dim3(kBmWaves * 64), lds, stream, ids, rows, slots, regions, words,
+                     reinterpret_cast<uint32_t*>(bitmap));
+  return 0;
+}
+
+}  // namespace irb

@@ -38,6 +38,9 @@ int launch_expand(const Layout& L, const int32_t* sel, const int32_t* cnt, int t
 int launch_compact(const int32_t* in, int64_t rows, int width, int64_t key_count, int32_t* out,
                    int32_t* lens, int32_t* bad, hipStream_t stream);
 
+// membership words [rows, ceil(regions / 32)] of id rows [rows, slots]; regions <= 131072
+int launch_bitmap(const int32_t* ids, int64_t rows, int slots, int regions, int32_t* bitmap, hipStream_t stream);
+
 int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int Lw,
                        int bq, int bk, int reverse, int32_t* counts, int32_t* indices, int width,
                        uint32_t* bitmap, hipStream_t stream);

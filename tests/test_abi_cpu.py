@@ -170,3 +170,20 @@ def test_prepare_index_queries_validation():
     s, m = call(H=0)
     assert s == 3
     assert call(n=0)[0] == 0          # nothing to do: no device call
+
+
+def test_pack_region_bitmap_validation():
+    lib = irb.load_library()
+    call = lambda ids=FAKE, rows=4, slots=8, regions=100, out=FAKE: _err(
+        lib.irb_pack_region_bitmap(ids, rows, slots, regions, out, None))
+    s, m = call(slots=0)
+    assert s == 3 and "slots" in m
+    s, m = call(regions=0)
+    assert s == 3 and "regions" in m
+    s, m = call(regions=131073)
+    assert s == 3 and "regions" in m
+    s, m = call(ids=None)
+    assert s == 3 and "NULL" in m
+    s, m = call(rows=-1)
+    assert s == 3
+    assert call(rows=0, ids=None, out=None)[0] == 0      # nothing to do: no device call

@@ -265,3 +265,32 @@ def test_select_long_rows(S, c, topk, ties):
     rsel, rcnt = oracle.select_topk(scores.astype(np.float64), c, topk, q0=q0, S=S)
     np.testing.assert_array_equal(host(cnt)[:, q0:], rcnt)
     np.testing.assert_array_equal(host(sel)[:, q0:], rsel)
+
+
+@pytest.mark.parametrize("rows,slots,regions,sort", [(300, 67, 70, True), (64, 512, 2048, True), (17, 1, 1, False),
+                                                     (40, 1000, 33, False), (9, 300, 131072, True), (5, 64, 4097, False)])
+def test_pack_region_bitmap_bit_exact(rows, slots, regions, sort):
+    """Sorted and unsorted rows with repeats, -1 and at-or-above-regions padding;
+    word counts from 1 to 4096 (the LDS limit)."""
+    banner(f"bitmap rows={rows} slots={slots} regions={regions} sort={sort}")
+    rng = np.random.default_rng(rows + slots + regions)
+    ids = rng.integers(-2, regions + 3, size=(rows, slots)).astype(np.int32)
+    if sort:
+        ids.sort(axis=-1)
+    got = irb.pack_region_bitmap(to_dev(ids), regions)
+    np.testing.assert_array_equal(host(got), oracle.pack_region_bitmap(ids, regions))
+
+
+def test_pack_region_bitmap_of_selected_blocks():
+    """The S=8192 selection layout ([1, 8192, 512] ascending block ids, -1 padded) over 2048 regions."""
+    wl = synth.WORKLOADS["s8192"]
+    banner("bitmap of s8192-shaped selections")
+    rng = np.random.default_rng(77)
+    S, topk, nb = 8192, wl.topk, 8192 // wl.c
+    sel = np.full((1, S, topk), -1, dtype=np.int32)
+    for t in range(0, S, 97):
+        n = (t + 1) // wl.c
+        k = min(topk, n)
+        sel[0, t, :k] = np.sort(rng.choice(n, k, replace=False)) if k else []
+    got = irb.pack_region_bitmap(to_dev(sel), nb)
+    np.testing.assert_array_equal(host(got), oracle.pack_region_bitmap(sel, nb))
