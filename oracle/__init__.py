@@ -28,7 +28,10 @@ its reason in the design notes):
 * padding queries get all -1 routes and zero attention output, lse = -inf;
   a query with an empty route likewise;
 * latent attention uses the first ``Dv`` channels of the shared latent row
-  as the value, and its key/value gradients land in the same buffer.
+  as the value, and its key/value gradients land in the same buffer;
+* per-KV-group routes are laid out group-major, [R, B, S, L] with R = 1
+  (one route shared by every head) or R = Hkv (one per KV group); for B = 1
+  this is the CSA page's [batch, groups, queries, slots].
 
 Parity status: every function here is pinned by the CPU tests (hand-derived
 fixtures, brute force, library special cases, invariants); none is
@@ -577,6 +580,95 @@ def latent_attention_bwd(q, kv, idx, dO, scale, dv=512, rows=None, keys=None):
     dkv = dk[0].copy()
     dkv[..., :dv] += dvv[0]
     return dq[0], dkv
+
+
+# ---------------------------------------------------------------------------
+# per-KV-group routes (CSA page: scores and selections [batch, groups, ...])
+# ---------------------------------------------------------------------------
+
+def indexer_scores_grouped(qI, w, kc, c, scale=None, cu_seqlens=None, row_lens=None, q0=0, q1=None):
+    """Scores of every KV group [R, B, q1-q0, NB] (float64); invisible entries are -inf.
+
+    CSA page, ``indexer_score_tile``: the index queries carry a group axis
+    ([batch, queries, groups, heads, dim], signed weights [batch, queries,
+    groups, heads]) and every group gets its own score row over the shared
+    region summaries:
+    ``s[g, b, t, j] = scale * sum_h w[b,t,g,h] * max(0, qI[b,t,g,h] . kc[b,j])``,
+    with the visibility of ``indexer_scores``.  ``scale`` defaults to
+    1/sqrt(D_idx).  The group axis leads the result so that each group's
+    scores are one contiguous [B, rows, NB] block.
+    """
+    qI = np.asarray(qI)
+    w = np.asarray(w)
+    R = qI.shape[2]
+    return np.stack([indexer_scores(qI[:, :, g], w[:, :, g], kc, c, scale, cu_seqlens, row_lens, q0, q1)
+                     for g in range(R)])
+
+
+def _group_of_heads(Hq, Hkv, R):
+    """Route group of every query head: head h reads KV head h // (Hq/Hkv);
+    with R == Hkv route groups that KV head's group, with R == 1 the shared one."""
+    if R not in (1, Hkv):
+        raise ValueError("route groups must be 1 or the number of KV heads")
+    G = Hq // Hkv
+    return [(h // G) if R > 1 else 0 for h in range(Hq)]
+
+
+def attention_fwd_grouped(q, k, v, routes, scale=None, rows=None):
+    """Sparse GQA forward with per-KV-group routes [R, B, S_q, L] (R = 1 or Hkv).
+
+    CSA page, ``pack_region_bitmap`` / ``indexer_score_tile``: selections
+    carry a groups axis, one route per (batch, KV group, query); FA4 page,
+    ``_provider_heads``: a group's route serves the consecutive query heads
+    sharing that KV head.  Every KV group is the forward of ``attention_fwd``
+    over its own heads and its own route; R == 1 is ``attention_fwd``.
+    Output [B, S_q, Hq, Dv] and lse [B, Hq, S_q] (float64).
+    """
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    routes = np.asarray(routes)
+    R = routes.shape[0]
+    Hq, Hkv = q.shape[2], k.shape[2]
+    _group_of_heads(Hq, Hkv, R)
+    if R == 1:
+        return attention_fwd(q, k, v, routes[0], scale, rows)
+    G = Hq // Hkv
+    o = np.zeros(q.shape[:3] + (v.shape[3],), dtype=np.float64)
+    lse = np.full((q.shape[0], Hq, q.shape[1]), NEG_INF, dtype=np.float64)
+    for g in range(R):
+        hs = slice(g * G, (g + 1) * G)
+        og, lg = attention_fwd(q[:, :, hs], k[:, :, g:g + 1], v[:, :, g:g + 1], routes[g], scale, rows)
+        o[:, :, hs] = og
+        lse[:, hs] = lg
+    return o, lse
+
+
+def attention_bwd_grouped(q, k, v, routes, dO, scale=None, rows=None, keys=None):
+    """Gradients dq, dk, dv (float64) of ``attention_fwd_grouped`` for dO.
+
+    Per KV group the gradient of ``attention_bwd`` over that group's heads
+    and route (a key's dk/dv in group g sums over the queries whose group-g
+    route holds it); R == 1 is ``attention_bwd``.  ``rows`` / ``keys``
+    restrict the evaluation as there.
+    """
+    q, k, v, dO = np.asarray(q), np.asarray(k), np.asarray(v), np.asarray(dO)
+    routes = np.asarray(routes)
+    R = routes.shape[0]
+    Hq, Hkv = q.shape[2], k.shape[2]
+    _group_of_heads(Hq, Hkv, R)
+    if R == 1:
+        return attention_bwd(q, k, v, routes[0], dO, scale, rows, keys)
+    G = Hq // Hkv
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for g in range(R):
+        hs = slice(g * G, (g + 1) * G)
+        a, b_, c_ = attention_bwd(q[:, :, hs], k[:, :, g:g + 1], v[:, :, g:g + 1], routes[g], dO[:, :, hs],
+                                  scale, rows, keys)
+        dq[:, :, hs] = a
+        dk[:, :, g:g + 1] = b_
+        dv[:, :, g:g + 1] = c_
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------
