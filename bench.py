@@ -175,7 +175,7 @@ def main():
         dk = torch.empty((B, S, Hkv, Dqk), dtype=dt, device=dev)
         dv = dk if wl.latent else torch.empty((B, S, Hkv, Dv), dtype=dt, device=dev)
         bwd_ws = torch.empty(max(int(lib.irb_sparse_gqa_attention_bwd_workspace_size(
-            B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q))), 4), dtype=torch.uint8, device=dev)
+            B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q), 1)), 4), dtype=torch.uint8, device=dev)
 
     def timed(name, fn, record):
         if record:
@@ -218,14 +218,14 @@ def main():
 
     def attn_step(rec):
         timed("attn_fwd", lambda: C(lib.irb_sparse_gqa_attention_fwd(
-            P(q), P(k), P(v), irb._dtype_code(q), strides, P(routes), P(lens), B, S, S, L, Hq, Hkv, Dqk, Dv,
+            P(q), P(k), P(v), irb._dtype_code(q), strides, P(routes), P(lens), 1, B, S, S, L, Hq, Hkv, Dqk, Dv,
             scale, P(out), P(lse), sptr)), rec)
         if backward:
             timed("reverse_lists", lambda: C(lib.irb_build_block_lists(
                 P(routes), P(lens), B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(lists_ws),
                 lists_ws.numel(), sptr)), rec)
             timed("attn_bwd", lambda: C(lib.irb_sparse_gqa_attention_bwd(
-                P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens),
+                P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens), 1,
                 P(rev_counts), P(rev_idx), rbq, rbk, nqt, B, S, S, L, Hq, Hkv, Dqk, Dv, scale, P(dq), P(dk), P(dv),
                 P(bwd_ws), bwd_ws.numel(), sptr)), rec)
 

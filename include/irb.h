@@ -199,6 +199,37 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
                          int32_t* cnt, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * a2 / a2+a3 with one score row and one selection per KV group -- [CSA]
+ * indexer_score_tile: index queries [batch, queries, groups, heads, dim] and
+ * signed weights [batch, queries, groups, heads] score the shared region
+ * summaries into FP32 tiles [batch, groups, queries, regions]; selections
+ * and bitmaps carry the same groups axis (pack_region_bitmap).  Group g's
+ * score is the ungrouped score over its own H_idx heads:
+ *     out[g, b, t-q0, j-j0] = score_scale * sum_h w[b,t,g,h] * max(0, q[b,t,g,h,:] . kc[b,j,:])
+ *
+ *   q_idx  [B, S, groups, H_idx, D_idx] dtype contiguous
+ *   w      [B, S, groups, H_idx] fp32 contiguous
+ *   out    OUT group g's tile at out + g * B * (q1-q0) * out_row_stride, laid
+ *          out as irb_indexer_score_tile's
+ *   sel    OUT [groups, B, S, topk] int32, cnt OUT [groups, B, S] int32
+ *          (group-major: each group's selection is one [B, S, topk] block,
+ *          which irb_expand_and_compact_routes expands into that group's
+ *          [B, S, L] routes; for B = 1 the CSA page's [batch, groups, ...])
+ *   workspace: irb_route_topk_fused_workspace_size() bytes serve all groups
+ *          (the groups run one after another on the stream).
+ * Requires 1 <= groups <= 64; everything else as for the ungrouped calls.
+ */
+int irb_indexer_score_tile_groups(const irb_layout* layout, const void* q_idx, int dtype, int groups,
+                                  int H_idx, int D_idx, const float* w, const float* kc,
+                                  const int32_t* cu_blocks, int c, float score_scale, int q0, int q1,
+                                  int j0, int j1, float* out, int64_t out_row_stride, void* stream);
+int irb_route_topk_fused_groups(const irb_layout* layout, const void* q_idx, int dtype, int groups,
+                                int H_idx, int D_idx, const float* w, const float* kc,
+                                const int32_t* cu_blocks, int c, float score_scale, int topk, int q0,
+                                int q1, int32_t* sel, int32_t* cnt, void* workspace, size_t ws_bytes,
+                                void* stream);
+
+/*
  * a4 -- [QSA] select_qsa_token_ids: selected blocks expand to their c token
  * IDs, then the tokens of the current incomplete group [doc_start + nb*c, t]
  * are appended; plus the window [max(doc_start, t-window+1), t] ([CSA]
@@ -276,16 +307,25 @@ int irb_build_block_lists(const int32_t* routes, const int32_t* lens, int B, int
  *     element strides strides[0..2] = q (batch, token, head), [3..5] = k,
  *     [6..8] = v; the last dimension is contiguous.  A latent layout passes
  *     v = k (the value is the first Dv channels of each key row).
- *   routes [B, S_q, L] int32: routes[b,t,0:lens] ascending, unique, in [0, S_k)
+ *   routes [RG, B, S_q, L] int32, lens [RG, B, S_q] int32 with RG =
+ *     route_groups: routes[g,b,t,0:lens] ascending, unique, in [0, S_k).
+ *     RG = 1: one route per query, read by every head.  RG = Hkv: one route
+ *     per KV group and query ([CSA] indexer_score_tile / pack_region_bitmap:
+ *     scores and selections carry a groups axis; [FA4] _provider_heads: a
+ *     group's metadata serves the consecutive query heads sharing its KV
+ *     head), read by the heads h with h / (Hq/Hkv) = g.  Group-major, so each
+ *     group's routes are one [B, S_q, L] block (for B = 1 the CSA page's
+ *     [batch, groups, queries, slots]).
  *   out OUT [B, S_q, Hq, Dv] dtype contiguous; lse OUT [B, Hq, S_q] fp32
  * Requires Hq % Hkv == 0, Hq/Hkv <= 64, (Dqk, Dv) in {(64,64), (128,128)} or,
  * for bf16, (576,512); strides and q/k/v addresses 16-byte aligned;
- * softmax_scale > 0.
+ * softmax_scale > 0; route_groups = 1 or Hkv.
  */
 int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype,
                                  const int64_t* strides, const int32_t* routes, const int32_t* lens,
-                                 int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
-                                 float softmax_scale, void* out, float* lse, void* stream);
+                                 int route_groups, int B, int S_q, int S_k, int L, int Hq, int Hkv,
+                                 int Dqk, int Dv, float softmax_scale, void* out, float* lse,
+                                 void* stream);
 
 /*
  * a7 -- gradients of irb_sparse_gqa_attention_fwd ([QSA]
@@ -297,6 +337,10 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
  * reverse lists ([FA4] _selected_block_lists, reverse): rev_counts /
  * rev_indices from irb_build_block_lists(reverse=1) with the same
  * rev_block_q, rev_block_k.  No atomics: results are deterministic.
+ * With route_groups = Hkv the reverse lists are those of the grouped routes
+ * viewed as RG * B rows (irb_build_block_lists with B' = RG * B): counts
+ * [RG, B, key tiles], indices [RG, B, key tiles, rev_width]; KV head g reads
+ * group g's lists and routes.
  *
  *   out        the forward's output (accepted for interface symmetry, not read:
  *              Delta is recomputed with o in FP32 so that the rounding of the
@@ -307,19 +351,20 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
  *     dtype contiguous.  dk == dv (latent: v aliases k) writes the merged
  *     gradient dK + [dV, 0] into dk.
  *   workspace: irb_sparse_gqa_attention_bwd_workspace_size() bytes of device
- *     scratch (same B, S_q, S_k, L, heads, dims and dtype as the call).  For
- *     bf16 with Dqk = Dv in {64, 128} it holds, per 16-key tile, the listed
- *     queries whose routes reach the tile with their 16-bit key masks (at
- *     most B * S_q * min(L, ceil(S_k / 16)) entries; lists that repeat a
- *     query tile can overflow it, and entries past it are dropped).
+ *     scratch (same B, S_q, S_k, L, heads, dims, dtype and route_groups as
+ *     the call).  For bf16 with Dqk = Dv in {64, 128} it holds, per route
+ *     group and 16-key tile, the listed queries whose routes reach the tile
+ *     with their 16-bit key masks (at most RG * B * S_q * min(L, ceil(S_k /
+ *     16)) entries; lists that repeat a query tile can overflow it, and
+ *     entries past it are dropped).
  * Requirements as for the forward, plus rev_block_k = 16.
  */
 size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk,
-                                                   int Dv, int dtype);
+                                                   int Dv, int dtype, int route_groups);
 int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, int dtype,
                                  const int64_t* strides, const void* out, const void* dout,
                                  const float* lse, const int32_t* routes, const int32_t* lens,
-                                 const int32_t* rev_counts, const int32_t* rev_indices,
+                                 int route_groups, const int32_t* rev_counts, const int32_t* rev_indices,
                                  int rev_block_q, int rev_block_k, int rev_width, int B, int S_q,
                                  int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
                                  float softmax_scale, void* dq, void* dk, void* dv, void* workspace,

@@ -46,15 +46,19 @@ _SIGS = {
     "irb_select_topk_regions": ([_P, _P, _I64, _I, _I, _P, _I, _I, _P, _P, _P], _I),
     "irb_route_topk_fused_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_route_topk_fused": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "irb_indexer_score_tile_groups": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _I, _P, _I64, _P], _I),
+    "irb_route_topk_fused_groups": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P],
+                                    _I),
     "irb_expand_and_compact_routes": ([_P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P], _I),
     "irb_compact_routes": ([_P, _I64, _I, _I64, _P, _P, _P, _P], _I),
     "irb_pack_region_bitmap": ([_P, _I64, _I, _I, _P, _P], _I),
     "irb_build_block_lists_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
     "irb_build_block_lists": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _SZ, _P], _I),
-    "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
-    "irb_sparse_gqa_attention_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I], _SZ),
-    "irb_sparse_gqa_attention_bwd": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
-                                      _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
+    "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P,
+                                      _P], _I),
+    "irb_sparse_gqa_attention_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _I], _SZ),
+    "irb_sparse_gqa_attention_bwd": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
+                                      _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -173,19 +177,29 @@ def prepare_index_queries(q_raw, gamma, freqs=None, eps=1e-5, out=None):
 
 def indexer_score_tile(q_idx, w, kc, c, q0=0, q1=None, j0=0, j1=None, score_scale=None, cu_blocks=None,
                        cu_seqlens=None, row_lens=None, out=None):
-    """irb_indexer_score_tile: FP32 scores [B, q1-q0, j1-j0] (-inf where not visible)."""
+    """irb_indexer_score_tile: FP32 scores [B, q1-q0, j1-j0] (-inf where not visible).
+
+    Index queries with a group axis, q_idx [B, S, R, H, D] and w [B, S, R, H],
+    go to irb_indexer_score_tile_groups: scores [R, B, q1-q0, j1-j0]."""
     _gpu(q_idx, w, kc, cu_blocks, cu_seqlens, row_lens, out)
     lib = load_library()
-    B, S, H, D = q_idx.shape
+    grouped = q_idx.dim() == 5
+    B, S, R, H, D = q_idx.shape if grouped else (q_idx.shape[0], q_idx.shape[1], 1, q_idx.shape[2], q_idx.shape[3])
     q1 = S if q1 is None else q1
     j1 = S // c if j1 is None else j1
     scale = 1.0 / math.sqrt(D) if score_scale is None else score_scale
     if out is None:
-        out = torch.empty((B, q1 - q0, j1 - j0), dtype=torch.float32, device=q_idx.device)
+        shape = (R, B, q1 - q0, j1 - j0) if grouped else (B, q1 - q0, j1 - j0)
+        out = torch.empty(shape, dtype=torch.float32, device=q_idx.device)
     lay = make_layout(B, S, cu_seqlens, row_lens)
-    _check(lib.irb_indexer_score_tile(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), H, D, _ptr(w), _ptr(kc),
-                                      _ptr(cu_blocks), c, scale, q0, q1, j0, j1, _ptr(out), out.stride(1),
-                                      _stream(q_idx.device)))
+    if grouped:
+        _check(lib.irb_indexer_score_tile_groups(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), R, H, D, _ptr(w),
+                                                 _ptr(kc), _ptr(cu_blocks), c, scale, q0, q1, j0, j1, _ptr(out),
+                                                 out.stride(-2), _stream(q_idx.device)))
+    else:
+        _check(lib.irb_indexer_score_tile(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), H, D, _ptr(w), _ptr(kc),
+                                          _ptr(cu_blocks), c, scale, q0, q1, j0, j1, _ptr(out), out.stride(1),
+                                          _stream(q_idx.device)))
     return out
 
 
@@ -208,10 +222,15 @@ def select_topk_regions(scores, c, topk, S, q0=0, cu_blocks=None, cu_seqlens=Non
 
 def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_blocks=None, cu_seqlens=None,
                      row_lens=None, workspace=None, sel=None, cnt=None):
-    """irb_route_topk_fused: scores and selection over bounded score chunks."""
+    """irb_route_topk_fused: scores and selection over bounded score chunks.
+
+    Index queries with a group axis, q_idx [B, S, R, H, D] and w [B, S, R, H],
+    go to irb_route_topk_fused_groups: sel [R, B, S, topk], cnt [R, B, S]."""
     _gpu(q_idx, w, kc, cu_blocks, cu_seqlens, row_lens, workspace, sel, cnt)
     lib = load_library()
-    B, S, H, D = q_idx.shape
+    grouped = q_idx.dim() == 5
+    B, S, R, H, D = q_idx.shape if grouped else (q_idx.shape[0], q_idx.shape[1], 1, q_idx.shape[2], q_idx.shape[3])
+    lead = (R,) if grouped else ()
     dev = q_idx.device
     q1 = S if q1 is None else q1
     scale = 1.0 / math.sqrt(D) if score_scale is None else score_scale
@@ -219,10 +238,16 @@ def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_
         n = lib.irb_route_topk_fused_workspace_size(B, S, c, D, topk, q0, q1)
         workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
     if sel is None:
-        sel = torch.full((B, S, topk), -1, dtype=torch.int32, device=dev)
+        sel = torch.full(lead + (B, S, topk), -1, dtype=torch.int32, device=dev)
     if cnt is None:
-        cnt = torch.zeros((B, S), dtype=torch.int32, device=dev)
+        cnt = torch.zeros(lead + (B, S), dtype=torch.int32, device=dev)
     lay = make_layout(B, S, cu_seqlens, row_lens)
+    if grouped:
+        _check(lib.irb_route_topk_fused_groups(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), R, H, D, _ptr(w),
+                                               _ptr(kc), _ptr(cu_blocks), c, scale, topk, q0, q1, _ptr(sel), _ptr(cnt),
+                                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                               _stream(dev)))
+        return sel, cnt
     _check(lib.irb_route_topk_fused(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), H, D, _ptr(w), _ptr(kc),
                                     _ptr(cu_blocks), c, scale, topk, q0, q1, _ptr(sel), _ptr(cnt), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(dev)))
@@ -245,17 +270,27 @@ def pack_region_bitmap(ids, regions, out=None):
 
 
 def expand_and_compact_routes(sel, cnt, c, window, topk, L=None, cu_blocks=None, cu_seqlens=None, row_lens=None):
-    """irb_expand_and_compact_routes: (routes [B,S,L] int32, lens [B,S] int32)."""
+    """irb_expand_and_compact_routes: (routes [B,S,L] int32, lens [B,S] int32).
+
+    Per-group selections sel [R, B, S, topk], cnt [R, B, S] expand group by
+    group into routes [R, B, S, L], lens [R, B, S] (one call per group on
+    its contiguous block)."""
     _gpu(sel, cnt, cu_blocks, cu_seqlens, row_lens)
     lib = load_library()
-    B, S = cnt.shape
+    lead = tuple(cnt.shape[:-2])
+    B, S = cnt.shape[-2:]
     dev = cnt.device
     L = route_width(topk, c, window) if L is None else L
-    routes = torch.empty((B, S, L), dtype=torch.int32, device=dev)
-    lens = torch.empty((B, S), dtype=torch.int32, device=dev)
+    routes = torch.empty(lead + (B, S, L), dtype=torch.int32, device=dev)
+    lens = torch.empty(lead + (B, S), dtype=torch.int32, device=dev)
     lay = make_layout(B, S, cu_seqlens, row_lens)
-    _check(lib.irb_expand_and_compact_routes(ctypes.byref(lay), _ptr(sel), _ptr(cnt), topk, c, window,
-                                             _ptr(cu_blocks), L, _ptr(routes), _ptr(lens), _stream(dev)))
+    R = lead[0] if lead else 1
+    sel_g = sel.reshape(R, B, S, topk)
+    cnt_g = cnt.reshape(R, B, S)
+    r_g, l_g = routes.view(R, B, S, L), lens.view(R, B, S)
+    for g in range(R):
+        _check(lib.irb_expand_and_compact_routes(ctypes.byref(lay), _ptr(sel_g[g]), _ptr(cnt_g[g]), topk, c, window,
+                                                 _ptr(cu_blocks), L, _ptr(r_g[g]), _ptr(l_g[g]), _stream(dev)))
     return routes, lens
 
 
@@ -274,20 +309,25 @@ def compact_routes(ids, key_count, out=None, count_out_of_range=True):
 
 
 def build_block_lists(routes, lens, S_k, block_q, block_k, reverse, width=None, workspace=None):
-    """irb_build_block_lists: (counts [B, rows], indices [B, rows, width])."""
+    """irb_build_block_lists: (counts [B, rows], indices [B, rows, width]).
+
+    Per-group routes [R, B, S_q, L] are R * B route rows: counts [R, B, rows],
+    indices [R, B, rows, width]."""
     _gpu(routes, lens, workspace)
     lib = load_library()
-    B, S_q, L = routes.shape
+    lead = tuple(routes.shape[:-3])
+    B, S_q, L = routes.shape[-3:]
+    B_all = B * (lead[0] if lead else 1)
     dev = routes.device
     nqt, nkt = -(-S_q // block_q), -(-S_k // block_k)
     rows, other = (nkt, nqt) if reverse else (nqt, nkt)
     width = other if width is None else width
     if workspace is None:
-        n = lib.irb_build_block_lists_workspace_size(B, S_q, S_k, block_q, block_k)
+        n = lib.irb_build_block_lists_workspace_size(B_all, S_q, S_k, block_q, block_k)
         workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
-    counts = torch.empty((B, rows), dtype=torch.int32, device=dev)
-    indices = torch.empty((B, rows, width), dtype=torch.int32, device=dev)
-    _check(lib.irb_build_block_lists(_ptr(routes), _ptr(lens), B, S_q, S_k, L, block_q, block_k, int(bool(reverse)),
+    counts = torch.empty(lead + (B, rows), dtype=torch.int32, device=dev)
+    indices = torch.empty(lead + (B, rows, width), dtype=torch.int32, device=dev)
+    _check(lib.irb_build_block_lists(_ptr(routes), _ptr(lens), B_all, S_q, S_k, L, block_q, block_k, int(bool(reverse)),
                                      _ptr(counts), _ptr(indices), width, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(dev)))
     return counts, indices
@@ -298,8 +338,20 @@ def _strides9(q, k, v):
                                 v.stride(0), v.stride(1), v.stride(2))
 
 
+def _route_groups(routes, lens):
+    """Route groups of a routes tensor: [B, S, L] -> 1, [RG, B, S, L] (per KV group) -> RG."""
+    if routes.dim() == 4:
+        if lens.dim() != 3 or tuple(lens.shape) != tuple(routes.shape[:3]):
+            raise ValueError("grouped routes [RG, B, S, L] need lens [RG, B, S]")
+        return routes.shape[0]
+    return 1
+
+
 def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None, lse=None):
-    """irb_sparse_gqa_attention_fwd: (o [B,S_q,Hq,Dv] in q's dtype, lse [B,Hq,S_q] fp32)."""
+    """irb_sparse_gqa_attention_fwd: (o [B,S_q,Hq,Dv] in q's dtype, lse [B,Hq,S_q] fp32).
+
+    routes [B, S_q, L] are shared by every head; routes [Hkv, B, S_q, L]
+    (lens [Hkv, B, S_q]) give every KV group its own routes."""
     _gpu(q, k, v, routes, lens, out, lse)
     lib = load_library()
     B, S_q, Hq, Dqk = q.shape
@@ -311,14 +363,18 @@ def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None
     if lse is None:
         lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev)
     _check(lib.irb_sparse_gqa_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v),
-                                            _ptr(routes), _ptr(lens), B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv,
-                                            scale, _ptr(out), _ptr(lse), _stream(dev)))
+                                            _ptr(routes), _ptr(lens), _route_groups(routes, lens), B, S_q, S_k,
+                                            routes.shape[-1], Hq, Hkv, Dqk, Dv, scale, _ptr(out), _ptr(lse),
+                                            _stream(dev)))
     return out, lse
 
 
 def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, rev_indices, rev_block_q,
                              rev_block_k=16, softmax_scale=None, merged_kv=False, workspace=None):
-    """irb_sparse_gqa_attention_bwd: (dq, dk, dv); with merged_kv (v aliases k) dk holds dK + [dV, 0], dv is dk."""
+    """irb_sparse_gqa_attention_bwd: (dq, dk, dv); with merged_kv (v aliases k) dk holds dK + [dV, 0], dv is dk.
+
+    Grouped routes [Hkv, B, S_q, L] take the reverse lists of the routes
+    viewed as Hkv * B rows."""
     _gpu(q, k, v, out, dout, lse, routes, lens, rev_counts, rev_indices, workspace)
     lib = load_library()
     B, S_q, Hq, Dqk = q.shape
@@ -328,13 +384,20 @@ def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, 
     dq = torch.empty((B, S_q, Hq, Dqk), dtype=q.dtype, device=dev)
     dk = torch.empty((B, S_k, Hkv, Dqk), dtype=q.dtype, device=dev)
     dv = dk if merged_kv else torch.empty((B, S_k, Hkv, Dv), dtype=q.dtype, device=dev)
+    rg = _route_groups(routes, lens)
+    if rg not in (1, Hkv):
+        raise ValueError(f"sparse_gqa_attention_bwd: {rg} route groups for {Hkv} KV heads")
+    nkt = -(-S_k // rev_block_k)
+    if rev_counts.numel() != rg * B * nkt or rev_indices.numel() != rg * B * nkt * rev_indices.shape[-1]:
+        raise ValueError("sparse_gqa_attention_bwd: reverse lists do not match the routes "
+                         f"({rg} groups x {B} rows x {nkt} key tiles)")
     if workspace is None:
         n = lib.irb_sparse_gqa_attention_bwd_workspace_size(B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv,
-                                                            _dtype_code(q))
+                                                            _dtype_code(q), rg)
         workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
     _check(lib.irb_sparse_gqa_attention_bwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v), _ptr(out), _ptr(dout), _ptr(lse),
-        _ptr(routes), _ptr(lens), _ptr(rev_counts), _ptr(rev_indices), rev_block_q, rev_block_k,
+        _ptr(routes), _ptr(lens), rg, _ptr(rev_counts), _ptr(rev_indices), rev_block_q, rev_block_k,
         rev_indices.shape[-1], B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv, scale, _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
     return dq, dk, dv
@@ -355,18 +418,24 @@ def route(k_idx, q_idx, w, gamma, freqs, c, topk, window, eps=1e-5, score_scale=
 
     Returns dict(kc, cu_blocks, sel, cnt, routes, lens).  With a single
     document per row, query rows before the first sparse position take every
-    visible block and are not scored.
+    visible block and are not scored.  Index queries with a group axis
+    (q_idx [B, S, R, H, D], w [B, S, R, H]) give every group its own
+    selection and routes: sel [R, B, S, topk], routes [R, B, S, L].
     """
     B, S = q_idx.shape[:2]
+    grouped = q_idx.dim() == 5
+    R = q_idx.shape[2] if grouped else 1
+    lead = (R,) if grouped else ()
     kc, cu_blocks = compress_keys(k_idx, gamma, freqs, c, eps, cu_seqlens, row_lens)
     q0 = 0 if cu_seqlens is not None else min(first_sparse_query(c, topk), S - 1)
-    sel = torch.empty((B, S, topk), dtype=torch.int32, device=q_idx.device)
-    cnt = torch.empty((B, S), dtype=torch.int32, device=q_idx.device)
+    sel = torch.empty(lead + (B, S, topk), dtype=torch.int32, device=q_idx.device)
+    cnt = torch.empty(lead + (B, S), dtype=torch.int32, device=q_idx.device)
     if q0 > 0:
-        # rows that see at most topk blocks: selection needs no scores
+        # rows that see at most topk blocks: selection needs no scores (the same for every group)
         dummy = torch.empty((B, q0, 1), dtype=torch.float32, device=q_idx.device)
-        select_topk_regions(dummy, c, topk, S, q0=0, cu_blocks=cu_blocks, cu_seqlens=cu_seqlens,
-                            row_lens=row_lens, sel=sel, cnt=cnt)
+        for g in range(R):
+            select_topk_regions(dummy, c, topk, S, q0=0, cu_blocks=cu_blocks, cu_seqlens=cu_seqlens,
+                                row_lens=row_lens, sel=sel[g] if grouped else sel, cnt=cnt[g] if grouped else cnt)
     route_topk_fused(q_idx, w, kc, c, topk, q0=q0, q1=S, score_scale=score_scale, cu_blocks=cu_blocks,
                      cu_seqlens=cu_seqlens, row_lens=row_lens, workspace=workspace, sel=sel, cnt=cnt)
     routes, lens = expand_and_compact_routes(sel, cnt, c, window, topk, cu_blocks=cu_blocks, cu_seqlens=cu_seqlens,

@@ -121,10 +121,12 @@ int irb_prepare_index_queries(const void* q_raw, int dtype, int64_t n_tokens, in
                                                q_out, static_cast<hipStream_t>(stream)));
 }
 
-int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx,
-                           const float* w, const float* kc, const int32_t* cu_blocks, int c, float score_scale,
-                           int q0, int q1, int j0, int j1, float* out, int64_t out_row_stride, void* stream) {
-  const char* fn = "irb_indexer_score_tile";
+// groups >= 1 index-query groups per token; group g's tile lands at
+// out + g * B * (q1 - q0) * out_row_stride
+static int score_tile_impl(const char* fn, const irb_layout* layout, const void* q_idx, int dtype, int groups,
+                           int H_idx, int D_idx, const float* w, const float* kc, const int32_t* cu_blocks, int c,
+                           float score_scale, int q0, int q1, int j0, int j1, float* out, int64_t out_row_stride,
+                           void* stream) {
   irb::Layout L;
   if (int r = check_layout(fn, layout, L)) return r;
   if (int r = check_dtype(fn, dtype)) return r;
@@ -137,9 +139,33 @@ int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtyp
   if (out_row_stride < j1 - j0) return fail(IRB_ERR_INVALID, "%s: out_row_stride < j1 - j0", fn);
   if (!q_idx || !w || !kc || !out) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
   if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
+  if (groups < 1 || groups > 64) return fail(IRB_ERR_INVALID, "%s: groups must be in 1..64 (got %d)", fn, groups);
   IRB_REQUIRE_DEVICE();
-  return launched(fn, irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, nullptr, cu_blocks, c, score_scale, q0, q1, j0, j1,
-                                             out, out_row_stride, 1, -1, static_cast<hipStream_t>(stream)));
+  const int esz = dtype == IRB_BF16 ? 2 : 4;
+  const int64_t tile = static_cast<int64_t>(L.B) * (q1 - q0) * out_row_stride;
+  for (int g = 0; g < groups; ++g) {
+    const void* qg = static_cast<const char*>(q_idx) + static_cast<int64_t>(g) * H_idx * D_idx * esz;
+    const int rc = irb::launch_score_tile(L, qg, dtype, H_idx, D_idx, w + static_cast<int64_t>(g) * H_idx, kc, nullptr,
+                                          cu_blocks, c, score_scale, q0, q1, j0, j1, out + g * tile, out_row_stride, 1,
+                                          -1, groups, static_cast<hipStream_t>(stream));
+    if (rc) return launched(fn, rc);
+  }
+  return launched(fn, 0);
+}
+
+int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx,
+                           const float* w, const float* kc, const int32_t* cu_blocks, int c, float score_scale,
+                           int q0, int q1, int j0, int j1, float* out, int64_t out_row_stride, void* stream) {
+  return score_tile_impl("irb_indexer_score_tile", layout, q_idx, dtype, 1, H_idx, D_idx, w, kc, cu_blocks, c,
+                         score_scale, q0, q1, j0, j1, out, out_row_stride, stream);
+}
+
+int irb_indexer_score_tile_groups(const irb_layout* layout, const void* q_idx, int dtype, int groups, int H_idx,
+                                  int D_idx, const float* w, const float* kc, const int32_t* cu_blocks, int c,
+                                  float score_scale, int q0, int q1, int j0, int j1, float* out,
+                                  int64_t out_row_stride, void* stream) {
+  return score_tile_impl("irb_indexer_score_tile_groups", layout, q_idx, dtype, groups, H_idx, D_idx, w, kc,
+                         cu_blocks, c, score_scale, q0, q1, j0, j1, out, out_row_stride, stream);
 }
 
 int irb_select_topk_regions(const irb_layout* layout, const float* scores, int64_t score_row_stride, int q0, int q1,
@@ -173,10 +199,12 @@ size_t irb_route_topk_fused_workspace_size(int B, int S, int c, int D_idx, int t
   return split_keys_bytes(B, static_cast<int>(nb), D_idx) + static_cast<size_t>(rows * B * std::max<int64_t>(nb, 1) * 4);
 }
 
-int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx, const float* w,
-                         const float* kc, const int32_t* cu_blocks, int c, float score_scale, int topk, int q0, int q1,
-                         int32_t* sel, int32_t* cnt, void* workspace, size_t ws_bytes, void* stream) {
-  const char* fn = "irb_route_topk_fused";
+// groups >= 1 index-query groups per token: group g selects into
+// sel + g * B * S * topk and cnt + g * B * S; the split keys serve every group
+static int route_fused_impl(const char* fn, const irb_layout* layout, const void* q_idx, int dtype, int groups,
+                            int H_idx, int D_idx, const float* w, const float* kc, const int32_t* cu_blocks, int c,
+                            float score_scale, int topk, int q0, int q1, int32_t* sel, int32_t* cnt, void* workspace,
+                            size_t ws_bytes, void* stream) {
   irb::Layout L;
   if (int r = check_layout(fn, layout, L)) return r;
   if (int r = check_dtype(fn, dtype)) return r;
@@ -193,19 +221,43 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
   const size_t kbytes = split_keys_bytes(L.B, nb, D_idx);
   const int64_t rows = ws_bytes > kbytes ? static_cast<int64_t>(ws_bytes - kbytes) / per_row : 0;
   if (rows < 1) return fail(IRB_ERR_INVALID, "%s: workspace too small (%zu bytes)", fn, ws_bytes);
+  if (groups < 1 || groups > 64) return fail(IRB_ERR_INVALID, "%s: groups must be in 1..64 (got %d)", fn, groups);
   IRB_REQUIRE_DEVICE();
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t* kcs = static_cast<uint16_t*>(workspace);
   float* scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + kbytes);
   if (int rc = irb::launch_split_keys(kc, kcs, static_cast<int64_t>(L.B) * nb, D_idx, st)) return launched(fn, rc);
-  for (int a = q0; a < q1; a += static_cast<int>(std::min<int64_t>(rows, q1 - a))) {
-    const int e = a + static_cast<int>(std::min<int64_t>(rows, q1 - a));
-    int rc = irb::launch_score_tile(L, q_idx, dtype, H_idx, D_idx, w, kc, kcs, cu_blocks, c, score_scale, a, e, 0, nb,
-                                    scores, nb, 0, topk, st);
-    if (!rc) rc = irb::launch_select(L, scores, nb, a, e, cu_blocks, c, topk, sel, cnt, st);
-    if (rc) return launched(fn, rc);
+  const int esz = dtype == IRB_BF16 ? 2 : 4;
+  const int64_t sel_group = static_cast<int64_t>(L.B) * L.S;
+  for (int g = 0; g < groups; ++g) {
+    const void* qg = static_cast<const char*>(q_idx) + static_cast<int64_t>(g) * H_idx * D_idx * esz;
+    const float* wg = w + static_cast<int64_t>(g) * H_idx;
+    for (int a = q0; a < q1; a += static_cast<int>(std::min<int64_t>(rows, q1 - a))) {
+      const int e = a + static_cast<int>(std::min<int64_t>(rows, q1 - a));
+      int rc = irb::launch_score_tile(L, qg, dtype, H_idx, D_idx, wg, kc, kcs, cu_blocks, c, score_scale, a, e, 0, nb,
+                                      scores, nb, 0, topk, groups, st);
+      if (!rc)
+        rc = irb::launch_select(L, scores, nb, a, e, cu_blocks, c, topk, sel + g * sel_group * topk,
+                                cnt + g * sel_group, st);
+      if (rc) return launched(fn, rc);
+    }
   }
   return launched(fn, 0);
+}
+
+int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx, const float* w,
+                         const float* kc, const int32_t* cu_blocks, int c, float score_scale, int topk, int q0, int q1,
+                         int32_t* sel, int32_t* cnt, void* workspace, size_t ws_bytes, void* stream) {
+  return route_fused_impl("irb_route_topk_fused", layout, q_idx, dtype, 1, H_idx, D_idx, w, kc, cu_blocks, c,
+                          score_scale, topk, q0, q1, sel, cnt, workspace, ws_bytes, stream);
+}
+
+int irb_route_topk_fused_groups(const irb_layout* layout, const void* q_idx, int dtype, int groups, int H_idx,
+                                int D_idx, const float* w, const float* kc, const int32_t* cu_blocks, int c,
+                                float score_scale, int topk, int q0, int q1, int32_t* sel, int32_t* cnt,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  return route_fused_impl("irb_route_topk_fused_groups", layout, q_idx, dtype, groups, H_idx, D_idx, w, kc, cu_blocks,
+                          c, score_scale, topk, q0, q1, sel, cnt, workspace, ws_bytes, stream);
 }
 
 int irb_expand_and_compact_routes(const irb_layout* layout, const int32_t* sel, const int32_t* cnt, int topk, int c,
@@ -274,12 +326,14 @@ int irb_build_block_lists(const int32_t* routes, const int32_t* lens, int B, int
 }
 
 static int check_attn(const char* fn, const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
-                      const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L_width, int Hq,
-                      int Hkv, int Dqk, int Dv, float scale, irb::AttnArgs& a) {
+                      const int32_t* routes, const int32_t* lens, int route_groups, int B, int S_q, int S_k,
+                      int L_width, int Hq, int Hkv, int Dqk, int Dv, float scale, irb::AttnArgs& a) {
   if (int r = check_dtype(fn, dtype)) return r;
   if (B < 1 || S_q < 1 || S_k < 1 || L_width < 1) return fail(IRB_ERR_INVALID, "%s: sizes must be >= 1", fn);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(IRB_ERR_INVALID, "%s: Hq must be a multiple of Hkv", fn);
   if (Hq / Hkv > 64) return fail(IRB_ERR_INVALID, "%s: Hq/Hkv must be <= 64", fn);
+  if (route_groups != 1 && route_groups != Hkv)
+    return fail(IRB_ERR_INVALID, "%s: route_groups must be 1 or Hkv (got %d)", fn, route_groups);
   const bool dims_ok = dtype == IRB_BF16 ? ((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128) || (Dqk == 576 && Dv == 512))
                                          : ((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128));
   if (!dims_ok) return fail(IRB_ERR_INVALID, "%s: unsupported head dims (%d, %d)", fn, Dqk, Dv);
@@ -300,17 +354,18 @@ static int check_attn(const char* fn, const void* q, const void* k, const void* 
   a.sv_b = strides[6]; a.sv_t = strides[7]; a.sv_h = strides[8];
   a.routes = routes; a.lens = lens;
   a.B = B; a.S_q = S_q; a.S_k = S_k; a.L = L_width; a.Hq = Hq; a.Hkv = Hkv; a.Dqk = Dqk; a.Dv = Dv;
-  a.scale = scale; a.dtype = dtype;
+  a.scale = scale; a.dtype = dtype; a.RG = route_groups;
   return 0;
 }
 
 int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
-                                 const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L_width,
-                                 int Hq, int Hkv, int Dqk, int Dv, float softmax_scale, void* out, float* lse,
-                                 void* stream) {
+                                 const int32_t* routes, const int32_t* lens, int route_groups, int B, int S_q,
+                                 int S_k, int L_width, int Hq, int Hkv, int Dqk, int Dv, float softmax_scale,
+                                 void* out, float* lse, void* stream) {
   const char* fn = "irb_sparse_gqa_attention_fwd";
   irb::AttnArgs a;
-  if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv, softmax_scale, a))
+  if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, route_groups, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv,
+                     softmax_scale, a))
     return r;
   if (!out || !lse) return fail(IRB_ERR_INVALID, "%s: NULL output", fn);
   IRB_REQUIRE_DEVICE();
@@ -318,28 +373,31 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
 }
 
 size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
-                                                    int dtype) {
+                                                    int dtype, int route_groups) {
   if (B < 1 || S_q < 1 || S_k < 1 || L < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return 0;
   if (dtype != IRB_F32 && dtype != IRB_BF16) return 0;
-  return irb::attn_bwd_workspace_bytes(B, S_q, S_k, L, Hq, Hkv, Dqk, Dv, dtype);
+  if (route_groups != 1 && route_groups != Hkv) return 0;
+  return irb::attn_bwd_workspace_bytes(B, S_q, S_k, L, Hq, Hkv, Dqk, Dv, dtype, route_groups);
 }
 
 int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
                                  const void* out, const void* dout, const float* lse, const int32_t* routes,
-                                 const int32_t* lens, const int32_t* rev_counts, const int32_t* rev_indices,
+                                 const int32_t* lens, int route_groups, const int32_t* rev_counts,
+                                 const int32_t* rev_indices,
                                  int rev_block_q, int rev_block_k, int rev_width, int B, int S_q, int S_k, int L_width,
                                  int Hq, int Hkv, int Dqk, int Dv, float softmax_scale, void* dq, void* dk, void* dv,
                                  void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "irb_sparse_gqa_attention_bwd";
   irb::AttnBwdArgs a;
-  if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv, softmax_scale, a.f))
+  if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, route_groups, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv,
+                     softmax_scale, a.f))
     return r;
   if (!out || !dout || !lse || !rev_counts || !rev_indices || !dq || !dk || !dv) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
   if (rev_block_k != 16) return fail(IRB_ERR_INVALID, "%s: rev_block_k must be 16 (got %d)", fn, rev_block_k);
   if (rev_block_q < 1) return fail(IRB_ERR_INVALID, "%s: rev_block_q must be >= 1", fn);
   if (rev_width < (S_q + rev_block_q - 1) / rev_block_q) return fail(IRB_ERR_INVALID, "%s: rev_width below the query tile count", fn);
   if (dk == dv && Dv > Dqk) return fail(IRB_ERR_INVALID, "%s: merged dk/dv needs Dv <= Dqk", fn);
-  if (ws_bytes < irb::attn_bwd_workspace_bytes(B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv, dtype))
+  if (ws_bytes < irb::attn_bwd_workspace_bytes(B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv, dtype, route_groups))
     return fail(IRB_ERR_INVALID, "%s: workspace too small", fn);
   if (!workspace) return fail(IRB_ERR_INVALID, "%s: NULL workspace", fn);
   a.out = out; a.dout = dout; a.lse = lse;

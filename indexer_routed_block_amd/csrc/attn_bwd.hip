@@ -152,28 +152,29 @@ struct BwdWs {
   float* delta;       // [B, Hq, S_q]
   void* qt;           // transposed path: [B, S_q, Hkv, Dqk, Gp]
   void* dot;          //                  [B, S_q, Hkv, Dv, Gp]
-  int64_t* hit_off;   // hit path: [B * nkt + 1] counts, then exclusive offsets
+  int64_t* hit_off;   // hit path: [RG * B * nkt + 1] counts, then exclusive offsets
   int32_t* hit_t;     //           [cap] query of each hit
   uint32_t* hit_m;    //           [cap] its 16-bit key mask
-  int64_t cap;        // every (key tile, query) pair with a routed key: <= B * S_q * min(L, nkt)
+  int64_t cap;        // every (group, key tile, query) with a routed key: <= RG * B * S_q * min(L, nkt)
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-static int64_t hit_capacity(int B, int S_q, int S_k, int L) {
+static int64_t hit_capacity(int B, int S_q, int S_k, int L, int RG) {
   const int64_t nkt = (static_cast<int64_t>(S_k) + 15) / 16;
-  return static_cast<int64_t>(B) * S_q * std::min<int64_t>(L, nkt);
+  return static_cast<int64_t>(RG) * B * S_q * std::min<int64_t>(L, nkt);
 }
 
-size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype) {
+size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype,
+                                int RG) {
   const int G = Hq / (Hkv > 0 ? Hkv : 1);
   const size_t Gp = static_cast<size_t>(padded_group(G));
   const size_t rows = static_cast<size_t>(B) * S_q;
   size_t n = align256(rows * Hq * 4);
   if (uses_hits(dtype, Dqk, Dv, G)) {
     const size_t nkt = (static_cast<size_t>(S_k) + 15) / 16;
-    const size_t cap = static_cast<size_t>(hit_capacity(B, S_q, S_k, L));
-    n += align256((static_cast<size_t>(B) * nkt + 1) * 8) + 2 * align256(cap * 4);
+    const size_t cap = static_cast<size_t>(hit_capacity(B, S_q, S_k, L, RG));
+    n += align256((static_cast<size_t>(RG) * B * nkt + 1) * 8) + 2 * align256(cap * 4);
   } else {
     const size_t esz = dtype == IRB_BF16 ? 2 : 4;
     n += align256(rows * Hkv * Dqk * Gp * esz) + align256(rows * Hkv * Dv * Gp * esz);
@@ -181,7 +182,7 @@ size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv,
   return n;
 }
 
-static BwdWs carve(void* ws, int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype) {
+static BwdWs carve(void* ws, int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype, int RG) {
   const int G = Hq / Hkv;
   const size_t Gp = static_cast<size_t>(padded_group(G));
   const size_t rows = static_cast<size_t>(B) * S_q;
@@ -191,9 +192,9 @@ static BwdWs carve(void* ws, int B, int S_q, int S_k, int L, int Hq, int Hkv, in
   p += align256(rows * Hq * 4);
   if (uses_hits(dtype, Dqk, Dv, G)) {
     const size_t nkt = (static_cast<size_t>(S_k) + 15) / 16;
-    w.cap = hit_capacity(B, S_q, S_k, L);
+    w.cap = hit_capacity(B, S_q, S_k, L, RG);
     w.hit_off = reinterpret_cast<int64_t*>(p);
-    p += align256((static_cast<size_t>(B) * nkt + 1) * 8);
+    p += align256((static_cast<size_t>(RG) * B * nkt + 1) * 8);
     w.hit_t = reinterpret_cast<int32_t*>(p);
     p += align256(static_cast<size_t>(w.cap) * 4);
     w.hit_m = reinterpret_cast<uint32_t*>(p);
@@ -252,8 +253,9 @@ IRB_DEV void dq_item_gather(const AttnArgs& a, const uint16_t* __restrict__ dout
   const int h0 = kvh * G;
   const int nh = min(16, G);
   const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
-  const int n = max(0, min(a.lens[row], a.L));
-  const int32_t* route = a.routes + row * a.L;
+  const int64_t rrow = route_row(a, b, t, kvh);
+  const int n = max(0, min(a.lens[rrow], a.L));
+  const int32_t* route = a.routes + rrow * a.L;
   const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
   const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
   const bool hok = l16 < nh;
@@ -395,8 +397,9 @@ bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ 
   const int h0 = kvh * G + 16 * slice;
   const int nh = min(16, G - 16 * slice);
   const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
-  const int n = max(0, min(a.lens[row], a.L));
-  const int32_t* route = a.routes + row * a.L;
+  const int64_t rrow = route_row(a, b, t, kvh);
+  const int n = max(0, min(a.lens[rrow], a.L));
+  const int32_t* route = a.routes + rrow * a.L;
   const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
   const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
   const bool hok = l16 < nh;
@@ -653,8 +656,9 @@ bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __re
     }
   };
 
-  // walk the reverse list: listed query tiles, every query inside them
-  const int64_t lrow = static_cast<int64_t>(b) * nkt + jt;
+  // walk the reverse list: listed query tiles, every query inside them (lists
+  // of the route group read by this KV head: [RG, B, key tiles, width])
+  const int64_t lrow = (static_cast<int64_t>(a.RG > 1 ? kvh : 0) * a.B + b) * nkt + jt;
   const int cnt = args.rev_counts[lrow];
   const int32_t* qtiles = args.rev_indices + lrow * args.rev_width;
   const int bq = args.rev_bq;
@@ -670,7 +674,7 @@ bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __re
       if (qtile < 0 || t >= a.S_q) t = -1;
     }
     if (t >= 0) {
-      const int64_t qrow = static_cast<int64_t>(b) * a.S_q + t;
+      const int64_t qrow = route_row(a, b, t, kvh);
       const int n = max(0, min(a.lens[qrow], a.L));
       const int32_t* r = a.routes + qrow * a.L;
       int lo = 0, hi = n;                 // first entry >= k0
@@ -739,9 +743,10 @@ bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __re
 }
 
 // ---------------------------------------------------------------- hit lists
-// 16-bit mask of the keys [k0, k0 + 16) in query t's ascending route
-IRB_DEV uint32_t route_tile_mask(const AttnArgs& a, int b, int t, int k0) {
-  const int64_t qrow = static_cast<int64_t>(b) * a.S_q + t;
+// 16-bit mask of the keys [k0, k0 + 16) in query t's ascending route; gb =
+// g * B + b picks batch row b of route group g
+IRB_DEV uint32_t route_tile_mask(const AttnArgs& a, int gb, int t, int k0) {
+  const int64_t qrow = static_cast<int64_t>(gb) * a.S_q + t;
   const int n = max(0, min(a.lens[qrow], a.L));
   const int32_t* r = a.routes + qrow * a.L;
   int lo = 0, hi = n;                 // first entry >= k0
@@ -762,7 +767,7 @@ IRB_DEV uint32_t route_tile_mask(const AttnArgs& a, int b, int t, int k0) {
   return m;
 }
 
-// One workgroup per (b, key tile).  pass 0 counts the reverse-list queries
+// One workgroup per (route group, b, key tile).  pass 0 counts the reverse-list queries
 // whose route holds a key of the tile; pass 1 writes them, ascending, with
 // their key masks from hit_off[tile] on (never past cap).  With one query per
 // reverse-list row (rev_bq = 1) every listed query is a hit by construction,
@@ -776,7 +781,7 @@ bwd_hits_kernel(AttnBwdArgs args, int nkt, int pass, int64_t* __restrict__ hit_o
   __shared__ int wsum[4];
   const AttnArgs& a = args.f;
   const int64_t lrow = blockIdx.x;
-  const int b = static_cast<int>(lrow / nkt), j = static_cast<int>(lrow % nkt);
+  const int gb = static_cast<int>(lrow / nkt), j = static_cast<int>(lrow % nkt);
   const int k0 = 16 * j;
   const int cnt = min(max(args.rev_counts[lrow], 0), args.rev_width);
   const int32_t* qtiles = args.rev_indices + lrow * args.rev_width;
@@ -795,7 +800,7 @@ bwd_hits_kernel(AttnBwdArgs args, int nkt, int pass, int64_t* __restrict__ hit_o
       const int qt = qtiles[c];
       const bool ok = qt >= 0 && qt < a.S_q;
       hit_t[pos] = ok ? qt : -1;
-      hit_m[pos] = ok ? route_tile_mask(a, b, qt, k0) : 0u;
+      hit_m[pos] = ok ? route_tile_mask(a, gb, qt, k0) : 0u;
     }
     return;
   }
@@ -809,7 +814,7 @@ bwd_hits_kernel(AttnBwdArgs args, int nkt, int pass, int64_t* __restrict__ hit_o
       const int64_t tt = static_cast<int64_t>(qt) * bq + c % bq;
       if (qt >= 0 && tt < a.S_q) {
         t = static_cast<int>(tt);
-        m = route_tile_mask(a, b, t, k0);
+        m = route_tile_mask(a, gb, t, k0);
       }
     }
     int tot;
@@ -907,7 +912,7 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   const float sc2 = a.scale * kLog2eB;
   const int qpb = Gp <= 32 ? 32 / Gp : 1;       // queries per 32-row batch
   const int bpq = Gp <= 32 ? 1 : Gp / 32;       // batches per query
-  const int64_t lrow = static_cast<int64_t>(b) * nkt + jt;
+  const int64_t lrow = (static_cast<int64_t>(a.RG > 1 ? kvh : 0) * a.B + b) * nkt + jt;
   const int64_t h0 = min(hit_off[lrow], cap), h1 = min(hit_off[lrow + 1], cap);
   uint16_t* sq = s_q[wid];
   uint16_t* so = s_o[wid];
@@ -1132,7 +1137,7 @@ bwd_dkdv_wide_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   for (int i = 0; i < MV; ++i) adv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sc2 = a.scale * kLog2eB;
   const int bpq = G / 32;
-  const int64_t lrow = static_cast<int64_t>(b) * nkt + jt;
+  const int64_t lrow = (static_cast<int64_t>(a.RG > 1 ? kvh : 0) * a.B + b) * nkt + jt;
   const int64_t h0 = min(hit_off[lrow], cap), h1 = min(hit_off[lrow + 1], cap);
   const int tr_row = 4 * g16 + (l16 >> 2), tr_col = 4 * (l16 & 3);
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
@@ -1270,7 +1275,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
   constexpr bool kGqaHits = sizeof(T) == 2 && D == DV && (D == 64 || D == 128);
   constexpr bool kWide = sizeof(T) == 2 && D == 576 && DV == 512;
   const bool hits = kGqaHits || (kWide && G % 32 == 0);
-  BwdWs ws = carve(args.ws, a.B, a.S_q, a.S_k, a.L, a.Hq, a.Hkv, a.Dqk, a.Dv, a.dtype);
+  BwdWs ws = carve(args.ws, a.B, a.S_q, a.S_k, a.L, a.Hq, a.Hkv, a.Dqk, a.Dv, a.dtype, a.RG);
   const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
   const int64_t rows = static_cast<int64_t>(a.B) * a.S_q;
   if (!hits) {
@@ -1312,7 +1317,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
   const int64_t kitems = static_cast<int64_t>(a.B) * nkt * a.Hkv;
   const int merged = args.dk == args.dv ? 1 : 0;
   if (hits) {
-    const int64_t ltiles = static_cast<int64_t>(a.B) * nkt;
+    const int64_t ltiles = static_cast<int64_t>(a.RG) * a.B * nkt;
     hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 0,
                        ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(256), 0, stream, ws.hit_off, ltiles);

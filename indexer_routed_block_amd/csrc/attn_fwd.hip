@@ -119,8 +119,9 @@ IRB_DEV void fwd_item(const AttnArgs& a, T* __restrict__ out, float* __restrict_
   const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
   const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
   const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
-  const int n = max(0, min(a.lens[row], a.L));
-  const int32_t* route = a.routes + row * a.L;
+  const int64_t rrow = route_row(a, b, t, kvh);
+  const int n = max(0, min(a.lens[rrow], a.L));
+  const int32_t* route = a.routes + rrow * a.L;
 
   bf16x8 qh[KS], ql[KS];
   {
@@ -321,8 +322,9 @@ IRB_DEV void fwd_item_gather(const AttnArgs& a, uint16_t* __restrict__ out, floa
   const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
   const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
   const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
-  const int n = max(0, min(a.lens[row], a.L));
-  const int32_t* route = a.routes + row * a.L;
+  const int64_t rrow = route_row(a, b, t, kvh);
+  const int n = max(0, min(a.lens[rrow], a.L));
+  const int32_t* route = a.routes + rrow * a.L;
 
   bf16x8 qh[KS];
   {
@@ -482,16 +484,16 @@ struct TileStats {
 };
 
 // Evaluated by a whole wavefront (uniform result).  BQ <= 64.
-IRB_DEV TileStats tile_stats_wave(const AttnArgs& a, int b, int qa, int BQ, int thr_milli) {
+IRB_DEV TileStats tile_stats_wave(const AttnArgs& a, int b, int kvh, int qa, int BQ, int thr_milli) {
   const int lane = threadIdx.x & 63;
   int kmin = 0x7fffffff, kmax = -1, total = 0, valid = 0;
   const int t = qa + lane;
   if (lane < BQ && t < a.S_q) {
-    const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
-    const int n = max(0, min(a.lens[row], a.L));
+    const int64_t rrow = route_row(a, b, t, kvh);
+    const int n = max(0, min(a.lens[rrow], a.L));
     valid = 1;
     if (n > 0) {
-      const int32_t* r = a.routes + row * a.L;
+      const int32_t* r = a.routes + rrow * a.L;
       kmin = r[0];
       kmax = r[n - 1];
       total = n;
@@ -535,7 +537,7 @@ attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G,
   }
   const QItem qi = decode_qitem(item, a.B, a.S_q, a.Hkv, kShared ? 0 : head_major);
   const int kvh = qi.kvh, t = qi.t, b = qi.b;
-  if (!kShared && tile_bq > 0 && tile_stats_wave(a, b, (t / tile_bq) * tile_bq, tile_bq, thr_milli).dense) return;
+  if (!kShared && tile_bq > 0 && tile_stats_wave(a, b, kvh, (t / tile_bq) * tile_bq, tile_bq, thr_milli).dense) return;
   if constexpr (!kShared && sizeof(T) == 2 && D <= 128)
     fwd_item_gather<D, DV, kDelta>(a, out, lse, G, dout, delta, b, t, kvh, slab);
   else
@@ -581,7 +583,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   const int qt = n_qt - 1 - (bid / a.Hkv) % n_qt;
   const int b = bid / (a.Hkv * n_qt);
   const int qa = qt * BQ;
-  const TileStats ts = tile_stats_wave(a, b, qa, BQ, thr_milli);
+  const TileStats ts = tile_stats_wave(a, b, kvh, qa, BQ, thr_milli);
   if (!ts.dense) return;
 
   const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
@@ -826,9 +828,8 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       const int t = qa + lane;
       int lo = cursor[lane], hi = lo;
       if (t < a.S_q) {
-        const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
         const int n = ts.n_lane;             // min(lens, L) (0 past S_q)
-        const int32_t* r = a.routes + row * a.L;
+        const int32_t* r = a.routes + route_row(a, b, t, kvh) * a.L;
         // a row's last segment holds all its remaining entries (its last
         // entry, known from the tile statistics, decides), otherwise a
         // binary search
@@ -881,7 +882,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
           bq[j] = cq;
           be[j] = ce;
           if (cq < BQ) {
-            const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + cq) * a.L;
+            const int32_t* r = a.routes + route_row(a, b, qa + cq, kvh) * a.L;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
               lds_dma16(r + min(ce + 256 * h + 4 * lane, a.L - 4), wl + j * 2048 + h * 1024);
@@ -904,7 +905,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     } else {
       for (int qi = wid; qi < BQ; qi += 4) {
         const int lo = s_lo[qi], hi = s_hi[qi];
-        const int32_t* r = a.routes + (static_cast<int64_t>(b) * a.S_q + qa + qi) * a.L;
+        const int32_t* r = a.routes + route_row(a, b, qa + qi, kvh) * a.L;
         for (int e0 = lo; e0 < hi; e0 += 512) {
           const int eb = e0 + 8 * lane;
           int ids[8];

@@ -20,11 +20,13 @@ int launch_prep_queries(const void* q, int dtype, int64_t n_rows, int H, int D, 
 // route path skips them: selection never reads them); queries with at most
 // skip_nb visible blocks are not scored (-1: score every query)
 // kc_split (optional): the keys pre-split by launch_split_keys, streamed by
-// direct global-to-LDS loads instead of being split while staging
+// direct global-to-LDS loads instead of being split while staging.
+// n_grp: index queries [B, S, n_grp, H, D] and weights [B, S, n_grp, H] with
+// q and w pointing at one group's heads (1: [B, S, H, D] and [B, S, H])
 int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
                       const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,
                       int q0, int q1, int j0, int j1, float* out, int64_t out_stride, int write_invisible,
-                      int skip_nb, hipStream_t stream);
+                      int skip_nb, int n_grp, hipStream_t stream);
 // kcs[2 blk] = bf16 high halves of kc[blk], kcs[2 blk + 1] = low halves (rows of D)
 int launch_split_keys(const float* kc, uint16_t* kcs, int64_t n_blocks, int D, hipStream_t stream);
 
@@ -52,7 +54,16 @@ struct AttnArgs {
   int B, S_q, S_k, L, Hq, Hkv, Dqk, Dv;
   float scale;
   int dtype;
+  int RG;   // route groups: 1 (one route per query, every head) or Hkv (one per KV group)
 };
+
+// Row of (batch b, query t) in the routes / lens read by KV head kvh.  Routes
+// are laid out group-major, [RG, B, S_q, L]: with RG = Hkv each KV group has
+// its own route per query (the CSA page's per-group selections), with RG = 1
+// all heads share it.
+__device__ __forceinline__ int64_t route_row(const AttnArgs& a, int b, int t, int kvh) {
+  return (static_cast<int64_t>(a.RG > 1 ? kvh : 0) * a.B + b) * a.S_q + t;
+}
 
 // Per-query gather kernels visit work items (b, t, KV head).  When the K/V rows
 // of all heads outgrow the chip's last-level cache (256 MiB of Infinity Cache
@@ -79,7 +90,8 @@ struct AttnBwdArgs {
   void* ws; size_t ws_bytes;
 };
 
-size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype);
+size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype,
+                                int RG);
 int launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 
 // fill a device int32 range with a value (a kernel, so callers may capture it in graphs)

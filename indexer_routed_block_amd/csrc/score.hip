@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(256, 2)
 score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kc,
              const uint16_t* __restrict__ kcs, const int32_t* __restrict__ cu_blocks, int c, float scale, int q0,
              int q1, int j0, int j1, float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg,
-             int write_invisible, int skip_nb) {
+             int write_invisible, int skip_nb, int n_grp) {
   constexpr int KS = D / 32;
   constexpr bool kSplitQ = sizeof(QT) == 4;
   // row tiles per wave (whole queries); FP32 queries (hi/lo operands) and
@@ -134,7 +134,9 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   // q rows of this wave in the A layout: row 16 rt + l16 -> query rr / H, head rr % H
   bf16x8 qh[RT][KS], ql[RT][KS];
   float wv[RT][4];
-  const int64_t qrow = static_cast<int64_t>(H) * D;
+  // q rows and weights are [.., S, n_grp, H, ..]: q and w point at this
+  // call's group, one token holds n_grp groups of H heads (1: no group axis)
+  const int64_t qrow = static_cast<int64_t>(n_grp) * H * D;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int rr = 16 * rt + l16;
@@ -154,7 +156,7 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
     for (int i = 0; i < 4; ++i) {
       const int r2 = 16 * rt + 4 * g16 + i;
       const int qw = qa + wid * QW + r2 / H;
-      wv[rt][i] = qw < qe ? w[(static_cast<int64_t>(b) * L.S + qw) * H + r2 % H] : 0.f;
+      wv[rt][i] = qw < qe ? w[(static_cast<int64_t>(b) * L.S + qw) * (n_grp * H) + r2 % H] : 0.f;
     }
   }
 
@@ -387,7 +389,7 @@ split_keys_kernel(const float* __restrict__ kc, uint16_t* __restrict__ kcs, int6
 template <typename QT, int D>
 static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const uint16_t* kcs,
                           const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1, float* out,
-                          int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
+                          int64_t ostride, int write_invisible, int skip_nb, int n_grp, hipStream_t stream) {
   // one segment per row: measured on MI355X with bf16 queries, splitting rows
   // into segments of 512..1024 blocks was slower at S = 8192 and S = 131072
   // (each segment repeats the q-row loads and the pipeline fill), and the
@@ -407,11 +409,11 @@ static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, c
     if (kcs)                                                                                                 \
       hipLaunchKernelGGL((score_kernel<QT, D, HH, true>), grid_for(score_rt<QT, D, HH, true>(), HH), dim3(256), \
                          0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, seg,  \
-                         n_seg, write_invisible, skip_nb);                                                   \
+                         n_seg, write_invisible, skip_nb, n_grp);                                               \
     else                                                                                                     \
       hipLaunchKernelGGL((score_kernel<QT, D, HH, false>), grid_for(score_rt<QT, D, HH, false>(), HH),      \
                          dim3(256), 0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out,    \
-                         ostride, seg, n_seg, write_invisible, skip_nb);                                     \
+                         ostride, seg, n_seg, write_invisible, skip_nb, n_grp);                                 \
     return 0;
   switch (H) {
     IRB_SCORE_CASE(4)
@@ -428,11 +430,12 @@ static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, c
 template <typename QT>
 static int launch_score_t(const Layout& L, const QT* q, int H, int D, const float* w, const float* kc,
                           const uint16_t* kcs, const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0,
-                          int j1, float* out, int64_t ostride, int write_invisible, int skip_nb, hipStream_t stream) {
+                          int j1, float* out, int64_t ostride, int write_invisible, int skip_nb, int n_grp,
+                          hipStream_t stream) {
   switch (D) {
-    case 32: return launch_score_d<QT, 32>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
-    case 64: return launch_score_d<QT, 64>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
-    case 128: return launch_score_d<QT, 128>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, stream);
+    case 32: return launch_score_d<QT, 32>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream);
+    case 64: return launch_score_d<QT, 64>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream);
+    case 128: return launch_score_d<QT, 128>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
@@ -452,12 +455,12 @@ int launch_split_keys(const float* kc, uint16_t* kcs, int64_t n_blocks, int D, h
 int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
                       const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,
                       int q0, int q1, int j0, int j1, float* out, int64_t out_stride, int write_invisible,
-                      int skip_nb, hipStream_t stream) {
+                      int skip_nb, int n_grp, hipStream_t stream) {
   if (dtype == IRB_BF16)
     return launch_score_t(L, static_cast<const uint16_t*>(q), H, D, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0,
-                          j1, out, out_stride, write_invisible, skip_nb, stream);
+                          j1, out, out_stride, write_invisible, skip_nb, n_grp, stream);
   return launch_score_t(L, static_cast<const float*>(q), H, D, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1,
-                        out, out_stride, write_invisible, skip_nb, stream);
+                        out, out_stride, write_invisible, skip_nb, n_grp, stream);
 }
 
 }  // namespace irb

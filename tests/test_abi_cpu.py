@@ -109,8 +109,8 @@ def test_routes_lists_validation():
 def test_attention_validation():
     lib = irb.load_library()
     st = (ctypes.c_int64 * 9)(64 * 4 * 128, 4 * 128, 128, 64 * 128, 128, 128, 64 * 128, 128, 128)
-    call = lambda Hq=4, Hkv=1, D=128, Dv=128, sc=0.1, dt=1, strides=st: lib.irb_sparse_gqa_attention_fwd(
-        FAKE, FAKE, FAKE, dt, strides, FAKE, FAKE, 1, 64, 64, 16, Hq, Hkv, D, Dv, sc, FAKE, FAKE, None)
+    call = lambda Hq=4, Hkv=1, D=128, Dv=128, sc=0.1, dt=1, strides=st, rg=1: lib.irb_sparse_gqa_attention_fwd(
+        FAKE, FAKE, FAKE, dt, strides, FAKE, FAKE, rg, 1, 64, 64, 16, Hq, Hkv, D, Dv, sc, FAKE, FAKE, None)
     assert _err(call(Hq=6, Hkv=4))[0] == 3
     assert _err(call(Hq=128, Hkv=1))[0] == 3
     assert _err(call(D=96, Dv=96))[0] == 3
@@ -119,21 +119,29 @@ def test_attention_validation():
     assert _err(call(dt=5))[0] == 2
     odd = (ctypes.c_int64 * 9)(*list(st)[:8], 129)
     assert _err(call(strides=odd))[0] == 3
+    # route groups: 1 (shared) or one per KV head
+    code, msg = _err(call(Hq=8, Hkv=4, rg=2))
+    assert code == 3 and "route_groups" in msg
+    assert _err(call(Hq=8, Hkv=4, rg=0))[0] == 3
     # backward: key tile must be 16, merged dk/dv needs Dv <= Dqk
-    bwd = lambda bk=16, width=64, ws=1 << 30: lib.irb_sparse_gqa_attention_bwd(
-        FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, bk, width, 1, 64, 64, 16, 4, 1, 128, 128,
-        0.1, FAKE, FAKE, FAKE, FAKE, ws, None)
+    bwd = lambda bk=16, width=64, ws=1 << 30, rg=1: lib.irb_sparse_gqa_attention_bwd(
+        FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, FAKE, FAKE, FAKE, rg, FAKE, FAKE, 1, bk, width, 1, 64, 64, 16, 4, 1, 128,
+        128, 0.1, FAKE, FAKE, FAKE, FAKE, ws, None)
     assert _err(bwd(bk=32))[0] == 3
     assert _err(bwd(width=63))[0] == 3
-    need = lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 4, 1, 128, 128, 1)
+    assert _err(bwd(rg=2))[0] == 3
+    need = lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 4, 1, 128, 128, 1, 1)
     assert need > 0
     code, msg = _err(bwd(ws=need - 1))
     assert code == 3 and "workspace" in msg
-    assert lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 6, 4, 128, 128, 1) == 0
-    # the hit lists of the bf16 GQA path grow with the route width; fp32 keeps the transposed copies
+    assert lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 6, 4, 128, 128, 1, 1) == 0
+    # the hit lists of the bf16 GQA path grow with the route width and the route groups; fp32 keeps the
+    # transposed copies
     ws_size = lib.irb_sparse_gqa_attention_bwd_workspace_size
-    assert ws_size(1, 256, 256, 16, 4, 1, 128, 128, 1) > ws_size(1, 256, 256, 8, 4, 1, 128, 128, 1)
-    assert lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 4, 1, 128, 128, 0) != need
+    assert ws_size(1, 256, 256, 16, 4, 1, 128, 128, 1, 1) > ws_size(1, 256, 256, 8, 4, 1, 128, 128, 1, 1)
+    assert ws_size(1, 256, 256, 16, 8, 4, 128, 128, 1, 4) > ws_size(1, 256, 256, 16, 8, 4, 128, 128, 1, 1)
+    assert ws_size(1, 256, 256, 16, 8, 4, 128, 128, 1, 3) == 0
+    assert lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 4, 1, 128, 128, 0, 1) != need
 
 
 def test_python_binding_has_no_cpu_path():
