@@ -21,7 +21,12 @@ time.  ``routed_queries_per_s`` is valid queries / route-pipeline time.
 times come from HIP events recorded on the stream the kernels run on.
 
     python bench.py [--steps K] [--warmup W] [--workload s8192|varlen|long|latent|tiny]
-                    [--no-cpu-baseline] [--copy-probe-mib N]
+                    [--no-cpu-baseline] [--copy-probe-mib N] [--route-groups R]
+
+``--route-groups R`` (R = the workload's KV head count) runs the same step
+with one selection and one route per KV group: the workload's index heads
+split into R groups of H_idx / R, grouped fused scoring / selection, routes
+[R, B, S, L] read per KV head by the attention calls.
 """
 from __future__ import annotations
 
@@ -51,6 +56,8 @@ def parse():
     ap.add_argument("--workload", default="s8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=3072)
+    ap.add_argument("--route-groups", type=int, default=1,
+                    help="1: one route per query for all heads; Hkv: one selection and route per KV group")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (HBM counter calibration)")
     return ap.parse_args()
@@ -122,6 +129,11 @@ def main():
     cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).to(dev)
     gen_s = time.time() - t0
     S, B = wl.S, wl.B
+    R = args.route_groups
+    if R != 1 and (wl.latent or R != wl.Hkv or wl.H_idx % R):
+        print(f"--route-groups must be 1 or the KV head count ({wl.Hkv}), dividing the index heads", file=sys.stderr)
+        sys.exit(2)
+    G_lead = (R,) if R > 1 else ()
     stages = {}          # name -> list of (start, end) events per timed step
 
     # ---------------------------------------------------------------- buffers (the step allocates nothing)
@@ -145,18 +157,20 @@ def main():
         L = irb.route_width(topk, c, window)
         nb_blocks = S // c
         q0 = 0 if cu is not None else min(irb.first_sparse_query(c, topk), S - 1)
-        fused_ws = torch.empty(max(int(lib.irb_route_topk_fused_workspace_size(B, S, c, wl.D_idx, topk, q0, S)), 4),
-                               dtype=torch.uint8, device=dev)
-        sel = torch.empty((B, S, topk), dtype=torch.int32, device=dev)
-        cnt = torch.empty((B, S), dtype=torch.int32, device=dev)
+        fused_ws = torch.empty(max(int(lib.irb_route_topk_fused_groups_workspace_size(
+            B, S, c, wl.D_idx, topk, q0, S, R)), 4), dtype=torch.uint8, device=dev)
+        sel = torch.empty(G_lead + (B, S, topk), dtype=torch.int32, device=dev)
+        cnt = torch.empty(G_lead + (B, S), dtype=torch.int32, device=dev)
         dummy = torch.empty((B, 1, 1), dtype=torch.float32, device=dev)
-        routes = torch.empty((B, S, L), dtype=torch.int32, device=dev)
-        lens = torch.empty((B, S), dtype=torch.int32, device=dev)
+        routes = torch.empty(G_lead + (B, S, L), dtype=torch.int32, device=dev)
+        lens = torch.empty(G_lead + (B, S), dtype=torch.int32, device=dev)
+        sel_g, cnt_g = sel.view(R, B, S, topk), cnt.view(R, B, S)
+        routes_g, lens_g = routes.view(R, B, S, L), lens.view(R, B, S)
         kc = torch.empty((B, nb_blocks, wl.D_idx), dtype=torch.float32, device=dev)
         cu_blocks = None if cu is None else torch.empty(cu.numel(), dtype=torch.int32, device=dev)
         lay = irb.make_layout(B, S, cu, None)
         qprep = torch.empty_like(d["qI"])
-        sel_bitmap = torch.empty((B, S, (nb_blocks + 31) // 32), dtype=torch.int32, device=dev)
+        sel_bitmap = torch.empty(G_lead + (B, S, (nb_blocks + 31) // 32), dtype=torch.int32, device=dev)
         q, k, v = d["q"], d["k"], d["v"]
         dO = d.get("dO")
     Hq = wl.Hq
@@ -167,15 +181,16 @@ def main():
     if backward:
         rbq, rbk = 1, 16
         nkt, nqt = -(-S // rbk), -(-S // rbq)
-        rev_counts = torch.empty((B, nkt), dtype=torch.int32, device=dev)
-        rev_idx = torch.empty((B, nkt, nqt), dtype=torch.int32, device=dev)
-        lists_ws = torch.empty(max(int(lib.irb_build_block_lists_workspace_size(B, S, S, rbq, rbk)), 4),
+        # grouped routes: R * B route rows, one reverse list per (group, row, key tile)
+        rev_counts = torch.empty((R * B, nkt), dtype=torch.int32, device=dev)
+        rev_idx = torch.empty((R * B, nkt, nqt), dtype=torch.int32, device=dev)
+        lists_ws = torch.empty(max(int(lib.irb_build_block_lists_workspace_size(R * B, S, S, rbq, rbk)), 4),
                                dtype=torch.uint8, device=dev)
         dq = torch.empty((B, S, Hq, Dqk), dtype=dt, device=dev)
         dk = torch.empty((B, S, Hkv, Dqk), dtype=dt, device=dev)
         dv = dk if wl.latent else torch.empty((B, S, Hkv, Dv), dtype=dt, device=dev)
         bwd_ws = torch.empty(max(int(lib.irb_sparse_gqa_attention_bwd_workspace_size(
-            B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q), 1)), 4), dtype=torch.uint8, device=dev)
+            B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q), R)), 4), dtype=torch.uint8, device=dev)
 
     def timed(name, fn, record):
         if record:
@@ -203,29 +218,38 @@ def main():
             irb.ctypes.byref(lay), c, P(d["kI"]), irb._dtype_code(d["kI"]), d["kI"].stride(0), d["kI"].stride(1),
             wl.D_idx, P(d["gamma"]), 1e-5, P(d["freqs"]), d["freqs"].shape[-1], P(kc), P(cu_blocks), sptr)), rec)
         if q0 > 0:
-            timed("select_dense_rows", lambda: C(lib.irb_select_topk_regions(
-                irb.ctypes.byref(lay), P(dummy), 1, 0, q0, P(cu_blocks), c, topk, P(sel), P(cnt), sptr)), rec)
-        timed("score_select", lambda: C(lib.irb_route_topk_fused(
-            irb.ctypes.byref(lay), P(d["qI"]), irb._dtype_code(d["qI"]), wl.H_idx, wl.D_idx, P(d["w"]), P(kc),
-            P(cu_blocks), c, 1.0 / math.sqrt(wl.D_idx), topk, q0, S, P(sel), P(cnt), P(fused_ws),
-            fused_ws.numel(), sptr)), rec)
+            timed("select_dense_rows", lambda: [C(lib.irb_select_topk_regions(
+                irb.ctypes.byref(lay), P(dummy), 1, 0, q0, P(cu_blocks), c, topk, P(sel_g[g]), P(cnt_g[g]), sptr))
+                for g in range(R)], rec)
+        if R == 1:
+            timed("score_select", lambda: C(lib.irb_route_topk_fused(
+                irb.ctypes.byref(lay), P(d["qI"]), irb._dtype_code(d["qI"]), wl.H_idx, wl.D_idx, P(d["w"]), P(kc),
+                P(cu_blocks), c, 1.0 / math.sqrt(wl.D_idx), topk, q0, S, P(sel), P(cnt), P(fused_ws),
+                fused_ws.numel(), sptr)), rec)
+        else:
+            # index heads [H_idx] read as [R, H_idx / R]: one score row and selection per KV group
+            timed("score_select", lambda: C(lib.irb_route_topk_fused_groups(
+                irb.ctypes.byref(lay), P(d["qI"]), irb._dtype_code(d["qI"]), R, wl.H_idx // R, wl.D_idx, P(d["w"]),
+                P(kc), P(cu_blocks), c, 1.0 / math.sqrt(wl.D_idx), topk, q0, S, P(sel), P(cnt), P(fused_ws),
+                fused_ws.numel(), sptr)), rec)
         # route bitmap of the selection (membership words per query), timed
         # beside the route pipeline; nothing downstream reads it
         timed("region_bitmap", lambda: C(lib.irb_pack_region_bitmap(
-            P(sel), B * S, topk, nb_blocks, P(sel_bitmap), sptr)), rec)
-        timed("expand", lambda: C(lib.irb_expand_and_compact_routes(
-            irb.ctypes.byref(lay), P(sel), P(cnt), topk, c, window, P(cu_blocks), L, P(routes), P(lens), sptr)), rec)
+            P(sel), R * B * S, topk, nb_blocks, P(sel_bitmap), sptr)), rec)
+        timed("expand", lambda: [C(lib.irb_expand_and_compact_routes(
+            irb.ctypes.byref(lay), P(sel_g[g]), P(cnt_g[g]), topk, c, window, P(cu_blocks), L, P(routes_g[g]),
+            P(lens_g[g]), sptr)) for g in range(R)], rec)
 
     def attn_step(rec):
         timed("attn_fwd", lambda: C(lib.irb_sparse_gqa_attention_fwd(
-            P(q), P(k), P(v), irb._dtype_code(q), strides, P(routes), P(lens), 1, B, S, S, L, Hq, Hkv, Dqk, Dv,
+            P(q), P(k), P(v), irb._dtype_code(q), strides, P(routes), P(lens), R, B, S, S, L, Hq, Hkv, Dqk, Dv,
             scale, P(out), P(lse), sptr)), rec)
         if backward:
             timed("reverse_lists", lambda: C(lib.irb_build_block_lists(
-                P(routes), P(lens), B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(lists_ws),
+                P(routes), P(lens), R * B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(lists_ws),
                 lists_ws.numel(), sptr)), rec)
             timed("attn_bwd", lambda: C(lib.irb_sparse_gqa_attention_bwd(
-                P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens), 1,
+                P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens), R,
                 P(rev_counts), P(rev_idx), rbq, rbk, nqt, B, S, S, L, Hq, Hkv, Dqk, Dv, scale, P(dq), P(dk), P(dv),
                 P(bwd_ws), bwd_ws.numel(), sptr)), rec)
 
@@ -258,16 +282,18 @@ def main():
     step_ms = float(np.mean([a.elapsed_time(b) for a, b in step_ev]))
 
     # ---------------------------------------------------------------- algorithmic work per call
-    lens_h = lens.cpu().numpy().astype(np.int64)
+    # selected pairs: (route group, query, key) entries; each serves the
+    # Hq / R query heads (and Hkv / R KV heads) that read that group's routes
+    lens_h = lens.cpu().numpy().astype(np.int64).reshape(R, -1)
     pairs = int(lens_h.sum())
-    valid_q = int((lens_h > 0).sum())
-    fwd_flop = 2.0 * (Dqk + Dv) * Hq * pairs
-    gathered = 2.0 * (Dqk + Dv) * Hkv * pairs if not wl.latent else 2.0 * Dqk * pairs
+    valid_q = int((lens_h > 0).any(axis=0).sum())
+    fwd_flop = 2.0 * (Dqk + Dv) * (Hq // R) * pairs
+    gathered = 2.0 * (Dqk + Dv) * (Hkv // R) * pairs if not wl.latent else 2.0 * Dqk * pairs
     work = {"attn_fwd": ("mfma", fwd_flop)}
     if backward:
-        work["attn_bwd"] = ("mfma", 2.0 * (3 * Dqk + 2 * Dv) * Hq * pairs)
+        work["attn_bwd"] = ("mfma", 2.0 * (3 * Dqk + 2 * Dv) * (Hq // R) * pairs)
         # routes read + counts and listed entries written (the -1 padding of the fixed width is not counted)
-        work["reverse_lists"] = ("hbm", 4.0 * L * B * S + 4.0 * rev_counts.numel()
+        work["reverse_lists"] = ("hbm", 4.0 * L * R * B * S + 4.0 * rev_counts.numel()
                                  + 4.0 * float(rev_counts.sum().item()))
     if wl.latent:
         work["compact"] = ("hbm", (8.0 * W + 4.0) * S)
@@ -279,11 +305,13 @@ def main():
                                    + 4.0 * B * S * d["freqs"].shape[-1])
         work["compress"] = ("hbm", B * S * wl.D_idx * (2 if dt == torch.bfloat16 else 4)
                             + B * nb_blocks * (4 * wl.D_idx + 4 * d["freqs"].shape[-1]))
-        work["region_bitmap"] = ("hbm", B * S * (4.0 * topk + 4.0 * ((nb_blocks + 31) // 32)))
+        # per route group: its own bitmap, selection and expansion; the
+        # scoring work is the same in total (each group scores H_idx / R heads)
+        work["region_bitmap"] = ("hbm", R * B * S * (4.0 * topk + 4.0 * ((nb_blocks + 31) // 32)))
         work["score_select"] = ("mfma", 2.0 * wl.H_idx * wl.D_idx * sparse_pairs)
-        work["expand"] = ("hbm", float(np.sum(valid_t)) * (4 * topk + 4 * L + 4))
+        work["expand"] = ("hbm", R * float(np.sum(valid_t)) * (4 * topk + 4 * L + 4))
         if q0 > 0:
-            work["select_dense_rows"] = ("hbm", 4.0 * topk * q0 * B)
+            work["select_dense_rows"] = ("hbm", 4.0 * topk * q0 * B * R)
         route_ms = sum(ms[n] for n in ("compress", "select_dense_rows", "score_select", "expand") if n in ms)
     stage_out = {}
     for name, t in ms.items():
@@ -302,7 +330,7 @@ def main():
     qps = valid_q / (route_ms / 1e3)
 
     traffic = None
-    tr = _traffic() if wl.name == "s8192" else None
+    tr = _traffic() if wl.name == "s8192" and R == 1 else None
     if tr is not None:
         traffic = tr["hbm_bytes_per_call"]
 
@@ -326,7 +354,7 @@ def main():
         "config": {
             "workload": wl.name, "description": wl.description, "B": B, "S": S, "Hq": Hq, "Hkv": Hkv,
             "Dqk": Dqk, "Dv": Dv, "route_width": L, "selected_pairs": pairs, "valid_queries": valid_q,
-            "backward_in_step": backward,
+            "backward_in_step": backward, "route_groups": R,
             **({} if wl.latent else {"H_idx": wl.H_idx, "D_idx": wl.D_idx, "c": wl.c, "topk": wl.topk,
                                      "window": wl.window}),
         },
@@ -345,7 +373,7 @@ def main():
         "stages": stage_out,
         "input_gen_s": round(gen_s, 2),
     }
-    if not args.no_cpu_baseline and wl.name == "s8192":
+    if not args.no_cpu_baseline and wl.name == "s8192" and R == 1:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_sample_rows)
     print(json.dumps(result), flush=True)
 

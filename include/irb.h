@@ -215,10 +215,17 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
  *          (group-major: each group's selection is one [B, S, topk] block,
  *          which irb_expand_and_compact_routes expands into that group's
  *          [B, S, L] routes; for B = 1 the CSA page's [batch, groups, ...])
- *   workspace: irb_route_topk_fused_workspace_size() bytes serve all groups
- *          (the groups run one after another on the stream).
+ *   workspace: irb_route_topk_fused_groups_workspace_size() bytes (the split
+ *          keys once, score rows of every group); any size holding the split
+ *          keys and one score row per group works.
+ * bf16 queries with 4 heads per group, groups * 4 in {16, 32} and D_idx in
+ * {64, 128} score every group in one launch (each lane's four accumulator
+ * rows are one group's heads); other shapes score the groups one after
+ * another with the ungrouped kernels.
  * Requires 1 <= groups <= 64; everything else as for the ungrouped calls.
  */
+size_t irb_route_topk_fused_groups_workspace_size(int B, int S, int c, int D_idx, int topk, int q0, int q1,
+                                                  int groups);
 int irb_indexer_score_tile_groups(const irb_layout* layout, const void* q_idx, int dtype, int groups,
                                   int H_idx, int D_idx, const float* w, const float* kc,
                                   const int32_t* cu_blocks, int c, float score_scale, int q0, int q1,

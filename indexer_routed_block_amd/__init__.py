@@ -47,6 +47,7 @@ _SIGS = {
     "irb_route_topk_fused_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_route_topk_fused": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "irb_indexer_score_tile_groups": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _I, _P, _I64, _P], _I),
+    "irb_route_topk_fused_groups_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_route_topk_fused_groups": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P],
                                     _I),
     "irb_expand_and_compact_routes": ([_P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P], _I),
@@ -235,7 +236,8 @@ def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_
     q1 = S if q1 is None else q1
     scale = 1.0 / math.sqrt(D) if score_scale is None else score_scale
     if workspace is None:
-        n = lib.irb_route_topk_fused_workspace_size(B, S, c, D, topk, q0, q1)
+        n = (lib.irb_route_topk_fused_groups_workspace_size(B, S, c, D, topk, q0, q1, R) if grouped
+             else lib.irb_route_topk_fused_workspace_size(B, S, c, D, topk, q0, q1))
         workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
     if sel is None:
         sel = torch.full(lead + (B, S, topk), -1, dtype=torch.int32, device=dev)

@@ -143,6 +143,10 @@ static int score_tile_impl(const char* fn, const irb_layout* layout, const void*
   IRB_REQUIRE_DEVICE();
   const int esz = dtype == IRB_BF16 ? 2 : 4;
   const int64_t tile = static_cast<int64_t>(L.B) * (q1 - q0) * out_row_stride;
+  if (groups > 1 && irb::score_grouped_ok(dtype, groups, H_idx, D_idx))
+    return launched(fn, irb::launch_score_grouped(L, q_idx, dtype, groups, H_idx, D_idx, w, kc, nullptr, cu_blocks, c,
+                                                  score_scale, q0, q1, j0, j1, out, out_row_stride, tile, 1, -1,
+                                                  static_cast<hipStream_t>(stream)));
   for (int g = 0; g < groups; ++g) {
     const void* qg = static_cast<const char*>(q_idx) + static_cast<int64_t>(g) * H_idx * D_idx * esz;
     const int rc = irb::launch_score_tile(L, qg, dtype, H_idx, D_idx, w + static_cast<int64_t>(g) * H_idx, kc, nullptr,
@@ -199,6 +203,16 @@ size_t irb_route_topk_fused_workspace_size(int B, int S, int c, int D_idx, int t
   return split_keys_bytes(B, static_cast<int>(nb), D_idx) + static_cast<size_t>(rows * B * std::max<int64_t>(nb, 1) * 4);
 }
 
+size_t irb_route_topk_fused_groups_workspace_size(int B, int S, int c, int D_idx, int topk, int q0, int q1,
+                                                  int groups) {
+  if (groups < 1 || groups > 64) return 0;
+  const size_t one = irb_route_topk_fused_workspace_size(B, S, c, D_idx, topk, q0, q1);
+  if (one == 0) return 0;
+  const int nb = S / c;
+  const size_t kbytes = split_keys_bytes(B, nb, D_idx);
+  return kbytes + static_cast<size_t>(groups) * (one - kbytes);
+}
+
 // groups >= 1 index-query groups per token: group g selects into
 // sel + g * B * S * topk and cnt + g * B * S; the split keys serve every group
 static int route_fused_impl(const char* fn, const irb_layout* layout, const void* q_idx, int dtype, int groups,
@@ -217,11 +231,13 @@ static int route_fused_impl(const char* fn, const irb_layout* layout, const void
   if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
   const int nb = L.S / c;
   if (nb < 1) return fail(IRB_ERR_INVALID, "%s: S/c must be >= 1", fn);
-  const int64_t per_row = static_cast<int64_t>(L.B) * nb * 4;
+  if (groups < 1 || groups > 64) return fail(IRB_ERR_INVALID, "%s: groups must be in 1..64 (got %d)", fn, groups);
+  // all groups scored by one launch (score tiles of every group alive at once), else group by group
+  const bool one_launch = groups > 1 && irb::score_grouped_ok(dtype, groups, H_idx, D_idx);
+  const int64_t per_row = static_cast<int64_t>(L.B) * nb * 4 * (one_launch ? groups : 1);
   const size_t kbytes = split_keys_bytes(L.B, nb, D_idx);
   const int64_t rows = ws_bytes > kbytes ? static_cast<int64_t>(ws_bytes - kbytes) / per_row : 0;
   if (rows < 1) return fail(IRB_ERR_INVALID, "%s: workspace too small (%zu bytes)", fn, ws_bytes);
-  if (groups < 1 || groups > 64) return fail(IRB_ERR_INVALID, "%s: groups must be in 1..64 (got %d)", fn, groups);
   IRB_REQUIRE_DEVICE();
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t* kcs = static_cast<uint16_t*>(workspace);
@@ -229,6 +245,19 @@ static int route_fused_impl(const char* fn, const irb_layout* layout, const void
   if (int rc = irb::launch_split_keys(kc, kcs, static_cast<int64_t>(L.B) * nb, D_idx, st)) return launched(fn, rc);
   const int esz = dtype == IRB_BF16 ? 2 : 4;
   const int64_t sel_group = static_cast<int64_t>(L.B) * L.S;
+  if (one_launch) {
+    for (int a = q0; a < q1; a += static_cast<int>(std::min<int64_t>(rows, q1 - a))) {
+      const int e = a + static_cast<int>(std::min<int64_t>(rows, q1 - a));
+      const int64_t gstride = static_cast<int64_t>(L.B) * (e - a) * nb;
+      int rc = irb::launch_score_grouped(L, q_idx, dtype, groups, H_idx, D_idx, w, kc, kcs, cu_blocks, c, score_scale,
+                                         a, e, 0, nb, scores, nb, gstride, 0, topk, st);
+      for (int g = 0; g < groups && !rc; ++g)
+        rc = irb::launch_select(L, scores + g * gstride, nb, a, e, cu_blocks, c, topk, sel + g * sel_group * topk,
+                                cnt + g * sel_group, st);
+      if (rc) return launched(fn, rc);
+    }
+    return launched(fn, 0);
+  }
   for (int g = 0; g < groups; ++g) {
     const void* qg = static_cast<const char*>(q_idx) + static_cast<int64_t>(g) * H_idx * D_idx * esz;
     const float* wg = w + static_cast<int64_t>(g) * H_idx;

@@ -66,12 +66,21 @@ IRB_DEV void visible_blocks(const Layout& L, const int32_t* cu_blocks, int c, in
 // a row of low halves) and stream through four LDS buffers by direct
 // global-to-LDS loads, three chunks in flight; otherwise the FP32 keys are
 // split while staging through two buffers.
-template <typename QT, int D, int H, bool kPre>
+// GS = 4 (with H a multiple of 16): the H heads are H / 4 groups of 4 heads
+// with one score each ([CSA] indexer_score_tile, scores per KV group), all
+// groups in one launch: the four accumulator rows a lane holds are exactly
+// one group's heads, so each lane's weighted sum is that group's score and
+// no cross-lane reduction is needed; group gi's tile starts gi * gstride
+// floats after out.  GS = 0: one score per query over all H heads.
+template <typename QT, int D, int H, bool kPre, int GS>
 __global__ void __launch_bounds__(256, 2)
 score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kc,
              const uint16_t* __restrict__ kcs, const int32_t* __restrict__ cu_blocks, int c, float scale, int q0,
              int q1, int j0, int j1, float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg,
-             int write_invisible, int skip_nb, int n_grp) {
+             int write_invisible, int skip_nb, int n_grp, int64_t gstride) {
+  static_assert(GS == 0 || (GS == 4 && H % 16 == 0), "grouped scores: groups of 4 heads, H a multiple of 16");
+  constexpr int NGRP = GS ? H / GS : 1;             // score tiles written
+  constexpr bool kPerQ = H < 16 || GS > 0;          // visible ranges kept per query (wave-uniform)
   constexpr int KS = D / 32;
   constexpr bool kSplitQ = sizeof(QT) == 4;
   // row tiles per wave (whole queries); FP32 queries (hi/lo operands) and
@@ -124,10 +133,11 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   float* otile = out + (static_cast<int64_t>(b) * (q1 - q0) + (qa - q0)) * ostride;
   if (write_invisible) {
     // -inf for the segment's blocks outside [cb, ce) (the computed ones are written below)
-    for (int i = tid; i < (qe - qa) * (se - sb); i += 256) {
-      const int r = i / (se - sb), j = sb + i % (se - sb);
-      if (j < cb || j >= ce) otile[static_cast<int64_t>(r) * ostride + (j - j0)] = -INFINITY;
-    }
+    for (int gi = 0; gi < NGRP; ++gi)
+      for (int i = tid; i < (qe - qa) * (se - sb); i += 256) {
+        const int r = i / (se - sb), j = sb + i % (se - sb);
+        if (j < cb || j >= ce) otile[gi * gstride + static_cast<int64_t>(r) * ostride + (j - j0)] = -INFINITY;
+      }
   }
   if (cb >= ce) return;
 
@@ -235,8 +245,8 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   int my_vb = 0, my_vn = 0;
   bool my_q = false;
   int64_t my_off = 0;
-  int vbk[H >= 16 ? 1 : QW], vnk[H >= 16 ? 1 : QW];
-  if constexpr (H >= 16) {
+  int vbk[kPerQ ? QW : 1], vnk[kPerQ ? QW : 1];
+  if constexpr (!kPerQ) {
     const int k = g16 < QW ? g16 : 0;
     my_vb = s_vis[0][wid * QW + k];
     my_vn = s_vis[1][wid * QW + k];
@@ -312,6 +322,25 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
           if (kSplitQ) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[rt][s], kh, acc[rt], 0, 0, 0);
         }
       }
+      const int jb = jc + l16;
+      if constexpr (GS == 4) {
+        // row tile rt: query 16 rt / H, heads 16 rt % H + 4 g16 + i = group (16 rt % H) / 4 + g16
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float p = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p = fmaf(wv[rt][i], fmaxf(acc[rt][i], 0.f), p);
+          const int k = (16 * rt) / H;
+          const int gi = ((16 * rt) % H) / 4 + g16;
+          const int qw = qa + wid * QW + k;
+          if (qw < qe && jb < ce) {
+            const bool vis = jb >= vbk[k] && jb < vbk[k] + vnk[k];
+            if (vis || write_invisible)
+              otile[gi * gstride + static_cast<int64_t>(qw - qa) * ostride + (jb - j0)] = vis ? scale * p : -INFINITY;
+          }
+        }
+        continue;
+      }
       // weighted ReLU summed over each query's heads
       float part[QW];
 #pragma unroll
@@ -331,7 +360,6 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
         if (H >= 16) part[k] = row4_sum(part[k]);
         else if (H == 8) part[k] = row_pair_sum(part[k]);
       }
-      const int jb = jc + l16;
       if constexpr (H >= 16) {
         // every lane holds the sums of all QW (<= 4) queries: lane group g16
         // writes query g16, one store for the whole tile
@@ -386,10 +414,11 @@ split_keys_kernel(const float* __restrict__ kc, uint16_t* __restrict__ kcs, int6
   *reinterpret_cast<bf16x8*>(kcs + (blk * 2 + 1) * D + 8 * c8) = lo;
 }
 
-template <typename QT, int D>
+template <typename QT, int D, int GS = 0>
 static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const uint16_t* kcs,
                           const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1, float* out,
-                          int64_t ostride, int write_invisible, int skip_nb, int n_grp, hipStream_t stream) {
+                          int64_t ostride, int write_invisible, int skip_nb, int n_grp, hipStream_t stream,
+                          int64_t gstride = 0) {
   // one segment per row: measured on MI355X with bf16 queries, splitting rows
   // into segments of 512..1024 blocks was slower at S = 8192 and S = 131072
   // (each segment repeats the q-row loads and the pipeline fill), and the
@@ -407,22 +436,30 @@ static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, c
 #define IRB_SCORE_CASE(HH)                                                                                   \
   case HH:                                                                                                   \
     if (kcs)                                                                                                 \
-      hipLaunchKernelGGL((score_kernel<QT, D, HH, true>), grid_for(score_rt<QT, D, HH, true>(), HH), dim3(256), \
-                         0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, seg,  \
-                         n_seg, write_invisible, skip_nb, n_grp);                                               \
-    else                                                                                                     \
-      hipLaunchKernelGGL((score_kernel<QT, D, HH, false>), grid_for(score_rt<QT, D, HH, false>(), HH),      \
+      hipLaunchKernelGGL((score_kernel<QT, D, HH, true, GS>), grid_for(score_rt<QT, D, HH, true>(), HH),    \
                          dim3(256), 0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out,    \
-                         ostride, seg, n_seg, write_invisible, skip_nb, n_grp);                                 \
+                         ostride, seg, n_seg, write_invisible, skip_nb, n_grp, gstride);                      \
+    else                                                                                                     \
+      hipLaunchKernelGGL((score_kernel<QT, D, HH, false, GS>), grid_for(score_rt<QT, D, HH, false>(), HH),  \
+                         dim3(256), 0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out,    \
+                         ostride, seg, n_seg, write_invisible, skip_nb, n_grp, gstride);                      \
     return 0;
-  switch (H) {
-    IRB_SCORE_CASE(4)
-    IRB_SCORE_CASE(8)
-    IRB_SCORE_CASE(16)
-    IRB_SCORE_CASE(32)
-    IRB_SCORE_CASE(48)
-    IRB_SCORE_CASE(64)
-    default: return static_cast<int>(hipErrorInvalidValue);
+  if constexpr (GS == 4) {
+    switch (H) {
+      IRB_SCORE_CASE(16)
+      IRB_SCORE_CASE(32)
+      default: return static_cast<int>(hipErrorInvalidValue);
+    }
+  } else {
+    switch (H) {
+      IRB_SCORE_CASE(4)
+      IRB_SCORE_CASE(8)
+      IRB_SCORE_CASE(16)
+      IRB_SCORE_CASE(32)
+      IRB_SCORE_CASE(48)
+      IRB_SCORE_CASE(64)
+      default: return static_cast<int>(hipErrorInvalidValue);
+    }
   }
 #undef IRB_SCORE_CASE
 }
@@ -461,6 +498,25 @@ int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, c
                           j1, out, out_stride, write_invisible, skip_nb, n_grp, stream);
   return launch_score_t(L, static_cast<const float*>(q), H, D, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1,
                         out, out_stride, write_invisible, skip_nb, n_grp, stream);
+}
+
+bool score_grouped_ok(int dtype, int groups, int H_group, int D) {
+  return dtype == IRB_BF16 && H_group == 4 && (groups * H_group == 16 || groups * H_group == 32) &&
+         (D == 64 || D == 128);
+}
+
+int launch_score_grouped(const Layout& L, const void* q, int dtype, int groups, int H_group, int D, const float* w,
+                         const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,
+                         int q0, int q1, int j0, int j1, float* out, int64_t out_stride, int64_t group_stride,
+                         int write_invisible, int skip_nb, hipStream_t stream) {
+  if (!score_grouped_ok(dtype, groups, H_group, D)) return static_cast<int>(hipErrorInvalidValue);
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const int H = groups * H_group;
+  if (D == 64)
+    return launch_score_d<uint16_t, 64, 4>(L, qb, H, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1, out,
+                                           out_stride, write_invisible, skip_nb, 1, stream, group_stride);
+  return launch_score_d<uint16_t, 128, 4>(L, qb, H, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1, out,
+                                          out_stride, write_invisible, skip_nb, 1, stream, group_stride);
 }
 
 }  // namespace irb

@@ -106,6 +106,17 @@ def test_routes_lists_validation():
     assert s == 3 and "workspace" in m
 
 
+def test_grouped_route_workspace_size():
+    lib = irb.load_library()
+    one = lib.irb_route_topk_fused_workspace_size(1, 8192, 4, 128, 512, 2044, 8192)
+    four = lib.irb_route_topk_fused_groups_workspace_size(1, 8192, 4, 128, 512, 2044, 8192, 4)
+    split = 8192 // 4 * 128 * 4          # the split keys, held once
+    assert four - split == 4 * (one - split)
+    assert lib.irb_route_topk_fused_groups_workspace_size(1, 8192, 4, 128, 512, 2044, 8192, 1) == one
+    assert lib.irb_route_topk_fused_groups_workspace_size(1, 8192, 4, 128, 512, 2044, 8192, 0) == 0
+    assert lib.irb_route_topk_fused_groups_workspace_size(1, 8192, 4, 128, 512, 2044, 8192, 65) == 0
+
+
 def test_attention_validation():
     lib = irb.load_library()
     st = (ctypes.c_int64 * 9)(64 * 4 * 128, 4 * 128, 128, 64 * 128, 128, 128, 64 * 128, 128, 128)
