@@ -446,6 +446,49 @@ def block_lists(routes, lens, S_k, block_q, block_k, reverse=False, rows=None):
     return counts, indices
 
 
+def split_full_blocks(routes, lens, S_k, block_q, block_k, counts, indices, reverse=False):
+    """Split block lists into full and partial blocks.
+
+    FA4 page, ``_split_forward_full_blocks`` / ``_split_backward_full_blocks``
+    (with ``_BackwardBlockPartition``): the blocks of a forward list (key
+    tiles per query tile) or a reverse list (query tiles per key tile) are
+    separated into "full" blocks, which need no mask, and "partial" ones,
+    keeping each list's order.  A block (query tile i, key tile j) is full
+    when every pair of its rectangle ``[i*block_q, min((i+1)*block_q, S_q))
+    x [j*block_k, min((j+1)*block_k, S_k))`` is routed (the key lies in the
+    query's route); the page establishes this for complete causal
+    rectangles of an all-selected query prefix, which is one case of it.
+    Returns (full_counts, full_indices, part_counts, part_indices) in the
+    layout of ``counts`` / ``indices`` (-1 after each count).
+    """
+    routes = np.asarray(routes)
+    lens = np.asarray(lens)
+    counts = np.asarray(counts)
+    indices = np.asarray(indices)
+    B, S_q, _ = routes.shape
+    full_c = np.zeros_like(counts)
+    part_c = np.zeros_like(counts)
+    full_i = np.full_like(indices, -1)
+    part_i = np.full_like(indices, -1)
+    for b in range(B):
+        routed = np.zeros((S_q, S_k), dtype=bool)       # the dense (query, key) mask of the routes
+        for t in range(S_q):
+            ids = routes[b, t, :max(0, int(lens[b, t]))]
+            routed[t, ids[(ids >= 0) & (ids < S_k)]] = True
+        for r in range(counts.shape[1]):
+            for e in range(int(counts[b, r])):
+                o = int(indices[b, r, e])
+                i, j = (o, r) if reverse else (r, o)
+                rect = routed[i * block_q:min((i + 1) * block_q, S_q), j * block_k:min((j + 1) * block_k, S_k)]
+                if rect.size and rect.all():
+                    full_i[b, r, full_c[b, r]] = o
+                    full_c[b, r] += 1
+                else:
+                    part_i[b, r, part_c[b, r]] = o
+                    part_c[b, r] += 1
+    return full_c, full_i, part_c, part_i
+
+
 # ---------------------------------------------------------------------------
 # a6 / a7: sparse GQA attention over gathered keys
 # ---------------------------------------------------------------------------
