@@ -302,6 +302,33 @@ int irb_build_block_lists(const int32_t* routes, const int32_t* lens, int B, int
                           int width, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Full/partial block split -- [FA4] _split_forward_full_blocks and
+ * _split_backward_full_blocks (_BackwardBlockPartition: independent partial
+ * and full counts and index lists in the input layouts): the entries of a
+ * forward or reverse block list from irb_build_block_lists (same routes,
+ * block sizes and direction) are separated, each list's order kept, into
+ * full blocks -- every (query, key) pair of the block's rectangle
+ * [i*block_q, min((i+1)*block_q, S_q)) x [j*block_k, min((j+1)*block_k, S_k))
+ * is routed, so the block needs no mask -- and partial ones.  The page proves
+ * fullness for the complete causal rectangles of an all-selected query
+ * prefix; this call tests the routes themselves, which covers that case and
+ * any other fully routed block (a window, a dense selection).
+ *
+ *   routes [B, S_q, L], lens [B, S_q] (ascending unique valid prefixes)
+ *   counts [B, rows], indices [B, rows, width] as irb_build_block_lists wrote them
+ *   full_counts, part_counts OUT [B, rows]; full_indices, part_indices OUT
+ *     [B, rows, width] int32; entries past each count are not written (as
+ *     for the page's lists, readers ignore them).  Outputs must not alias
+ *     the inputs or each other.
+ * Per-KV-group routes [RG, B, S_q, L] are RG * B route rows.
+ * Requires block_q, block_k, width >= 1.
+ */
+int irb_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L,
+                          int block_q, int block_k, int reverse, const int32_t* counts,
+                          const int32_t* indices, int width, int32_t* full_counts, int32_t* full_indices,
+                          int32_t* part_counts, int32_t* part_indices, void* stream);
+
+/*
  * a6 -- [QSA] gathered_qsa_gqa_attention / qsa_gqa_attention and [LATENT]
  * cudnn_sparse_attention: every valid query attends only to the keys at
  * routes[b, t, 0:lens[b,t]]; query head h uses KV head h / (Hq/Hkv)

@@ -54,6 +54,7 @@ _SIGS = {
     "irb_compact_routes": ([_P, _I64, _I, _I64, _P, _P, _P, _P], _I),
     "irb_pack_region_bitmap": ([_P, _I64, _I, _I, _P, _P], _I),
     "irb_build_block_lists_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
+    "irb_split_full_blocks": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P], _I),
     "irb_build_block_lists": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _SZ, _P], _I),
     "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P,
                                       _P], _I),
@@ -333,6 +334,24 @@ def build_block_lists(routes, lens, S_k, block_q, block_k, reverse, width=None, 
                                      _ptr(counts), _ptr(indices), width, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(dev)))
     return counts, indices
+
+
+def split_full_blocks(routes, lens, S_k, block_q, block_k, reverse, counts, indices):
+    """irb_split_full_blocks: (full_counts, full_indices, part_counts, part_indices) in the lists' layout.
+
+    Index entries past each count are left unwritten (uninitialised memory)."""
+    _gpu(routes, lens, counts, indices)
+    lib = load_library()
+    lead = tuple(routes.shape[:-3])
+    B, S_q, L = routes.shape[-3:]
+    B_all = B * (lead[0] if lead else 1)
+    width = indices.shape[-1]
+    fc, pc = torch.empty_like(counts), torch.empty_like(counts)
+    fi, pi = torch.empty_like(indices), torch.empty_like(indices)
+    _check(lib.irb_split_full_blocks(_ptr(routes), _ptr(lens), B_all, S_q, S_k, L, block_q, block_k, int(bool(reverse)),
+                                     _ptr(counts), _ptr(indices), width, _ptr(fc), _ptr(fi), _ptr(pc), _ptr(pi),
+                                     _stream(routes.device)))
+    return fc, fi, pc, pi
 
 
 def _strides9(q, k, v):

@@ -155,4 +155,97 @@ int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_
   return 0;
 }
 
+// Full/partial split of block lists ([FA4] _split_forward_full_blocks,
+// _split_backward_full_blocks, _BackwardBlockPartition).  One workgroup per
+// list row, its entries in chunks of 256.  Entry o of row r is the block
+// (i, j) = (r, o) for forward lists, (o, r) for reverse lists; it is full
+// when every query t of tile i routes to every key of tile j.  A route is
+// ascending and unique, so query t covers tile j exactly when the entry at
+// the first position holding a key >= j*bk (binary search) is j*bk and the
+// entry ts - 1 later is the tile's last key (ts = keys in the tile).  The
+// (entry, query) tests are spread over the threads; a failing one clears the
+// entry's LDS flag, and the flags are compacted in list order into the two
+// outputs.  Reads the listed entries once and writes each once.
+__global__ void __launch_bounds__(256)
+split_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int S_q, int S_k, int Lw, int bq,
+             int bk, int reverse, int n_rows, const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
+             int width, int32_t* __restrict__ fc, int32_t* __restrict__ fi, int32_t* __restrict__ pc,
+             int32_t* __restrict__ pi) {
+  __shared__ int flag[256];
+  __shared__ int ent[256];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y, row = blockIdx.x;
+  const int64_t lrow = static_cast<int64_t>(b) * n_rows + row;
+  const int cnt = min(max(counts[lrow], 0), width);
+  const int32_t* in = indices + lrow * width;
+  int32_t* fo = fi + lrow * width;
+  int32_t* po = pi + lrow * width;
+  int nfull = 0;
+  for (int e0 = 0; e0 < cnt; e0 += 256) {
+    const int ne = min(256, cnt - e0);
+    if (tid < ne) {
+      const int o = in[e0 + tid];
+      const int i = reverse ? o : row, j = reverse ? row : o;
+      ent[tid] = o;
+      flag[tid] = (o >= 0 && static_cast<int64_t>(i) * bq < S_q && static_cast<int64_t>(j) * bk < S_k) ? 1 : 0;
+    }
+    __syncthreads();
+    const int64_t npairs = static_cast<int64_t>(ne) * bq;
+    for (int64_t p = tid; p < npairs; p += 256) {
+      const int e = static_cast<int>(p / bq), qi = static_cast<int>(p % bq);
+      const int o = ent[e];
+      const int i = reverse ? o : row, j = reverse ? row : o;
+      if (o < 0) continue;
+      const int64_t tt = static_cast<int64_t>(i) * bq + qi;
+      const int64_t k0l = static_cast<int64_t>(j) * bk;
+      if (tt >= S_q || k0l >= S_k) continue;
+      const int t = static_cast<int>(tt), k0 = static_cast<int>(k0l);
+      const int ts = min(bk, S_k - k0);
+      const int64_t qrow = static_cast<int64_t>(b) * S_q + t;
+      const int n = max(0, min(lens[qrow], Lw));
+      const int32_t* r = routes + qrow * Lw;
+      int lo = 0, hi = n;
+      while (lo < hi) {
+        const int m = (lo + hi) >> 1;
+        if (r[m] < k0) lo = m + 1; else hi = m;
+      }
+      const int last = lo + ts - 1;
+      const bool cov = last < n && r[lo] == k0 && r[last] == k0 + ts - 1;
+      if (!cov) atomicAnd(&flag[e], 0);
+    }
+    __syncthreads();
+    const int f = tid < ne ? flag[tid] : 0;
+    int tot;
+    const int incl = block_scan256(f, wsum, &tot);
+    if (tid < ne) {
+      const int before_full = incl - f;
+      if (f) fo[nfull + before_full] = ent[tid];
+      else po[(e0 - nfull) + (tid - before_full)] = ent[tid];
+    }
+    nfull += tot;
+    __syncthreads();
+  }
+  // entries past each count are not written (the lists' readers ignore them):
+  // a reverse list of one-query tiles is as wide as the sequence, and filling
+  // two such outputs would cost more HBM traffic than the split itself
+  if (tid == 0) {
+    fc[lrow] = nfull;
+    pc[lrow] = cnt - nfull;
+  }
+}
+
+int launch_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int Lw, int bq,
+                             int bk, int reverse, const int32_t* counts, const int32_t* indices, int width,
+                             int32_t* full_counts, int32_t* full_indices, int32_t* part_counts,
+                             int32_t* part_indices, hipStream_t stream) {
+  const int nqt = (S_q + bq - 1) / bq, nkt = (S_k + bk - 1) / bk;
+  const int n_rows = reverse ? nkt : nqt;
+  if (n_rows <= 0 || B <= 0) return 0;
+  hipLaunchKernelGGL(split_kernel, dim3(static_cast<unsigned>(n_rows), static_cast<unsigned>(B)), dim3(256), 0, stream,
+                     routes, lens, S_q, S_k, Lw, bq, bk, reverse, n_rows, counts, indices, width, full_counts,
+                     full_indices, part_counts, part_indices);
+  return 0;
+}
+
 }  // namespace irb

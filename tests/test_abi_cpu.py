@@ -106,6 +106,19 @@ def test_routes_lists_validation():
     assert s == 3 and "workspace" in m
 
 
+def test_split_full_blocks_validation():
+    lib = irb.load_library()
+    A, B_, C_, D_, E_ = (ctypes.c_void_p(0x1000 * k) for k in range(1, 6))
+    call = lambda bq=16, bk=16, width=8, fi=C_, pi=D_, fc=E_, pc=ctypes.c_void_p(0x7000): lib.irb_split_full_blocks(
+        A, B_, 1, 64, 64, 8, bq, bk, 0, ctypes.c_void_p(0x9000), ctypes.c_void_p(0xA000), width, fc, fi, pc, pi, None)
+    assert _err(call(bq=0))[0] == 3
+    assert _err(call(width=0))[0] == 3
+    code, msg = _err(call(fi=ctypes.c_void_p(0xA000)))
+    assert code == 3 and "alias" in msg
+    assert _err(call(fi=D_))[0] == 3
+    assert _err(call(pc=E_))[0] == 3
+
+
 def test_grouped_route_workspace_size():
     lib = irb.load_library()
     one = lib.irb_route_topk_fused_workspace_size(1, 8192, 4, 128, 512, 2044, 8192)

@@ -294,3 +294,75 @@ def test_pack_region_bitmap_of_selected_blocks():
         sel[0, t, :k] = np.sort(rng.choice(n, k, replace=False)) if k else []
     got = irb.pack_region_bitmap(to_dev(sel), nb)
     np.testing.assert_array_equal(host(got), oracle.pack_region_bitmap(sel, nb))
+
+
+def _split_check(routes, lens, S, bq, bk, reverse):
+    r_d, l_d = to_dev(routes), to_dev(lens)
+    counts, indices = irb.build_block_lists(r_d, l_d, S, bq, bk, reverse)
+    rc, ri = oracle.block_lists(routes.reshape(-1, *routes.shape[-2:]), lens.reshape(-1, lens.shape[-1]), S, bq, bk,
+                                reverse)
+    np.testing.assert_array_equal(host(counts).reshape(rc.shape), rc)
+    got = [host(x) for x in irb.split_full_blocks(r_d, l_d, S, bq, bk, reverse, counts, indices)]
+    want = oracle.split_full_blocks(routes.reshape(-1, *routes.shape[-2:]), lens.reshape(-1, lens.shape[-1]), S, bq,
+                                    bk, rc, ri, reverse)
+    fc, fi, pc, pi = (g.reshape(w.shape) for g, w in zip(got, want))
+    np.testing.assert_array_equal(fc, want[0], err_msg="full_counts")
+    np.testing.assert_array_equal(pc, want[2], err_msg="part_counts")
+    # entries past each count are not written: compare the listed prefixes
+    valid_f = np.arange(fi.shape[-1]) < want[0][..., None]
+    valid_p = np.arange(pi.shape[-1]) < want[2][..., None]
+    np.testing.assert_array_equal(fi[valid_f], want[1][valid_f], err_msg="full_indices")
+    np.testing.assert_array_equal(pi[valid_p], want[3][valid_p], err_msg="part_indices")
+    print(f"  {int(want[0].sum())} full / {int(want[2].sum())} partial blocks")
+    return int(want[0].sum())
+
+
+@pytest.mark.parametrize("bq,bk", [(64, 64), (128, 128), (16, 16), (1, 16), (5, 3)])
+def test_split_full_blocks_pipeline_routes(bq, bk):
+    """S=8192 recipe at S=2048 (all-selected prefix, then top-k blocks + 128-token
+    window): full blocks in the prefix and along the window."""
+    banner(f"split full blocks s8192 recipe S=2048 bq={bq} bk={bk}")
+    wl = synth.WORKLOADS["s8192"]
+    x = synth.make_inputs(wl, parts=("route",), S=2048)
+    r = oracle.route_pipeline(x["kI"], x["qI"], x["w"], x["gamma"], x["freqs"], wl.c, 128, wl.window)
+    nfull = 0
+    for reverse in (False, True):
+        nfull += _split_check(r["routes"], r["lens"], 2048, bq, bk, reverse)
+    assert nfull > 0
+
+
+@pytest.mark.parametrize("width,bq,bk", [(40, 3, 5), (300, 16, 16), (37, 1, 16), (64, 8, 1)])
+def test_split_full_blocks_random_routes(width, bq, bk):
+    """B=2 random causal routes with a dense causal prefix in row 0, an empty row and a ragged tail."""
+    banner(f"split full blocks random width={width} bq={bq} bk={bk}")
+    rng = np.random.default_rng(width + bq)
+    B, S = 2, 333
+    ids = synth.random_routes(rng, B, S, width, causal=True, frac_invalid=0.2)
+    routes, lens, _ = oracle.compact_routes(ids, S)
+    for t in range(min(width, S)):
+        routes[0, t] = -1
+        routes[0, t, :t + 1] = np.arange(t + 1)
+        lens[0, t] = t + 1
+    routes[1, 7] = -1
+    lens[1, 7] = 0
+    for reverse in (False, True):
+        _split_check(routes, lens, S, bq, bk, reverse)
+
+
+def test_split_full_blocks_grouped_routes():
+    """Per-KV-group routes [R, B, S, L] split as R * B route rows."""
+    banner("split full blocks grouped routes")
+    rng = np.random.default_rng(5)
+    R, S, width = 4, 256, 128
+    rs, ls = [], []
+    for g in range(R):
+        ids = synth.random_routes(rng, 1, S, width, causal=True, frac_invalid=0.1)
+        r, n, _ = oracle.compact_routes(ids, S)
+        for t in range(16 * g, min(S, 16 * g + 64)):
+            r[0, t] = -1
+            r[0, t, :t + 1] = np.arange(t + 1)
+            n[0, t] = t + 1
+        rs.append(r)
+        ls.append(n)
+    for reverse in (False, True):
+        _split_check(np.stack(rs), np.stack(ls), S, 8, 8, reverse)
