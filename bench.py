@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=3072)
     ap.add_argument("--route-groups", type=int, default=1,
                     help="1: one route per query for all heads; Hkv: one selection and route per KV group")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: HBM rate of the token-streaming kernels (key compression, "
+                         "index-query preparation) over sequence lengths 8K..2M")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (HBM counter calibration)")
     return ap.parse_args()
@@ -110,6 +113,9 @@ def main():
     import indexer_routed_block_amd as irb
     import synth
 
+    if args.sweep:
+        sweep(args)
+        return
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -386,6 +392,70 @@ def main():
     if not args.no_cpu_baseline and wl.name == "s8192" and R == 1:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_sample_rows)
     print(json.dumps(result), flush=True)
+
+
+def sweep(args):
+    """HBM rate of key compression and index-query preparation against sequence length.
+
+    Synthetic bf16 inputs of the S=8192 workload's shapes (D_idx = 128, c = 4,
+    16 index heads, full-width rotary table), drawn by a seeded torch
+    generator on the device; each size is timed with HIP events on the
+    kernels' stream (5 warm-ups, median of 20).  Bytes are the algorithmic
+    ones of the step's stages.
+    """
+    import numpy as np
+    import torch
+
+    import indexer_routed_block_amd as irb
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = irb.load_library()
+    sptr = irb._stream(dev)
+    stream = torch.cuda.current_stream(dev)
+    P, C = irb._ptr, irb._check
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    D, c, H = 128, 4, 16
+    rows = []
+    for S in (8192, 32768, 131072, 524288, 2097152):
+        kI = torch.randn((1, S, D), generator=gen, device=dev).to(torch.bfloat16)
+        qI = torch.randn((1, S, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        freqs = torch.rand((1, S, D), generator=gen, device=dev)
+        gamma = torch.ones(D, dtype=torch.float32, device=dev)
+        kc = torch.empty((1, S // c, D), dtype=torch.float32, device=dev)
+        qout = torch.empty_like(qI)
+        lay = irb.make_layout(1, S, None, None)
+        calls = {
+            "compress": (lambda: C(lib.irb_compress_keys(irb.ctypes.byref(lay), c, P(kI), 1, kI.stride(0), kI.stride(1), D,
+                                                         P(gamma), 1e-5, P(freqs), D, P(kc), None, sptr)),
+                         S * D * 2 + (S // c) * (4 * D + 4 * D)),
+            "prepare_queries": (lambda: C(lib.irb_prepare_index_queries(P(qI), 1, S, H, D, P(gamma), 1e-5, P(freqs), D,
+                                                                        P(qout), sptr)),
+                                2 * S * H * D * 2 + 4 * S * D),
+        }
+        entry = {"S": S}
+        for name, (fn, nbytes) in calls.items():
+            for _ in range(5):
+                fn()
+            ts = []
+            for _ in range(20):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+            gbs = nbytes / (ms / 1e3) / 1e9
+            entry[name] = {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(gbs, 1),
+                           "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        rows.append(entry)
+        del kI, qI, freqs, kc, qout
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "token-streaming kernels vs sequence length", "peak_GBps": HBM_PEAK_GBS,
+                      "rows": rows}), flush=True)
 
 
 def cpu_baseline(wl, x, n_rows):
