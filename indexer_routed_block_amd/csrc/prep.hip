@@ -60,7 +60,7 @@ constexpr int kPrepGroups = 4;
 template <typename T, int D>
 __global__ void __launch_bounds__(kPrepWaves * 64)
 prep_queries_kernel(const T* q, int64_t n_rows, int H, const float* __restrict__ gamma, float eps,
-                    const float* __restrict__ rope, int R, int vec_tab, T* out) {
+                    const float* __restrict__ rope, int R, int vec_tab, int xor_partner, T* out) {
   constexpr int VE = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte access
   constexpr int EPL = VE > D / 64 ? VE : D / 64;          // elements per lane
   constexpr int NV = EPL / VE;                             // 16-byte accesses per lane
@@ -77,12 +77,23 @@ prep_queries_kernel(const T* q, int64_t n_rows, int H, const float* __restrict__
   float x[U][EPL], cs[U][EPL], sn[U][EPL], gm[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) gm[e] = gamma[li * EPL + e];
+  // every row of this wave belongs to one token when H is a multiple of the
+  // wave's U * RPW rows: the rotary factors are then loaded once
+  const bool one_tok = H % (U * RPW) == 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t row = row0 + u * RPW;
     const int64_t rr = row < n_rows ? row : 0;
 #pragma unroll
     for (int v = 0; v < NV; ++v) load16<T>(q + rr * D + li * EPL + v * VE, x[u] + v * VE);
+    if (u > 0 && one_tok) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        cs[u][e] = cs[0][e];
+        sn[u][e] = sn[0][e];
+      }
+      continue;
+    }
     // rotary factors: dimension d < R uses table entry j = d mod (R / 2),
     // rotated as x_d cos_j - x_{d + R/2} sin_j (first half) or
     // x_d cos_j + x_{d - R/2} sin_j (second half)
@@ -123,20 +134,26 @@ prep_queries_kernel(const T* q, int64_t n_rows, int H, const float* __restrict__
     for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      x[u][e] = x[u][e] * inv * gm[e];
-      stage[wid][lane * EPL + e] = x[u][e];
-    }
-    wave_lds_sync();
-    const float* mine = &stage[wid][sub * D];   // this row's normalised values
+    for (int e = 0; e < EPL; ++e) x[u][e] = x[u][e] * inv * gm[e];
     float y[EPL];
+    if (xor_partner) {
+      // D_rope = D and D_rope / 2 a power-of-two multiple of EPL: the partner
+      // of dim d (d +- D/2) is element e of lane lane ^ xor_partner
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int d = li * EPL + e;
-      const int pd = d < half ? d + half : (d < R ? d - half : d);   // rotation partner (itself past R)
-      y[e] = x[u][e] * cs[u][e] + mine[pd] * sn[u][e];
+      for (int e = 0; e < EPL; ++e) y[e] = x[u][e] * cs[u][e] + __shfl_xor(x[u][e], xor_partner, 64) * sn[u][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) stage[wid][lane * EPL + e] = x[u][e];
+      wave_lds_sync();
+      const float* mine = &stage[wid][sub * D];   // this row's normalised values
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int d = li * EPL + e;
+        const int pd = d < half ? d + half : (d < R ? d - half : d);   // rotation partner (itself past R)
+        y[e] = x[u][e] * cs[u][e] + mine[pd] * sn[u][e];
+      }
+      wave_lds_sync();                            // the stage is rewritten by the next group
     }
-    wave_lds_sync();                            // the stage is rewritten by the next group
     if (row < n_rows) {
 #pragma unroll
       for (int v = 0; v < NV; ++v) store16<T>(out + row * D + li * EPL + v * VE, y + v * VE);
@@ -151,6 +168,10 @@ int launch_prep_queries(const void* q, int dtype, int64_t n_rows, int H, int D, 
   // count (8 for bf16; max(4, D / 64) for FP32) and 16-byte aligned rows
   const int epl = dtype == IRB_BF16 ? (D / 64 > 8 ? D / 64 : 8) : (D / 64 > 4 ? D / 64 : 4);
   const int vec_tab = (R > 0 && (R / 2) % epl == 0 && (reinterpret_cast<uintptr_t>(rope) & 15) == 0) ? 1 : 0;
+  // full-width rotation with the half width a power-of-two number of lanes:
+  // the partner is a lane exchange (lane ^ (R / 2 / epl)) instead of LDS
+  const int hl = R > 0 ? (R / 2) / epl : 0;
+  const int xor_partner = (vec_tab && R == D && hl > 0 && (hl & (hl - 1)) == 0) ? hl : 0;
 #define IRB_PREP_CASE(T, DD)                                                                                \
   case DD: {                                                                                                \
     constexpr int VE = 16 / static_cast<int>(sizeof(T));                                                    \
@@ -159,7 +180,7 @@ int launch_prep_queries(const void* q, int dtype, int64_t n_rows, int H, int D, 
     const int64_t per_block = static_cast<int64_t>(kPrepWaves) * kPrepGroups * RPW;                         \
     hipLaunchKernelGGL((prep_queries_kernel<T, DD>), dim3(static_cast<unsigned>((n_rows + per_block - 1) / per_block)), \
                        dim3(kPrepWaves * 64), 0, stream, static_cast<const T*>(q), n_rows, H, gamma, eps, rope, R, \
-                       vec_tab, static_cast<T*>(out));                                                      \
+                       vec_tab, xor_partner, static_cast<T*>(out));                                         \
     return 0;                                                                                               \
   }
   if (dtype == IRB_BF16) {
