@@ -194,6 +194,8 @@ def main():
                                dtype=torch.uint8, device=dev)
         full_counts, part_counts = torch.empty_like(rev_counts), torch.empty_like(rev_counts)
         full_idx, part_idx = torch.empty_like(rev_idx), torch.empty_like(rev_idx)
+        split_ws = torch.empty(max(int(lib.irb_split_full_blocks_workspace_size(R * B, S, S, rbq, rbk)), 4),
+                               dtype=torch.uint8, device=dev)
         dq = torch.empty((B, S, Hq, Dqk), dtype=dt, device=dev)
         dk = torch.empty((B, S, Hkv, Dqk), dtype=dt, device=dev)
         dv = dk if wl.latent else torch.empty((B, S, Hkv, Dv), dtype=dt, device=dev)
@@ -259,7 +261,7 @@ def main():
             # full/partial split of the reverse lists, timed beside the backward (which does not read it)
             timed("split_full_blocks", lambda: C(lib.irb_split_full_blocks(
                 P(routes), P(lens), R * B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(full_counts),
-                P(full_idx), P(part_counts), P(part_idx), sptr)), rec)
+                P(full_idx), P(part_counts), P(part_idx), P(split_ws), split_ws.numel(), sptr)), rec)
             timed("attn_bwd", lambda: C(lib.irb_sparse_gqa_attention_bwd(
                 P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens), R,
                 P(rev_counts), P(rev_idx), rbq, rbk, nqt, B, S, S, L, Hq, Hkv, Dqk, Dv, scale, P(dq), P(dk), P(dv),
@@ -307,10 +309,11 @@ def main():
         # routes read + counts and listed entries written (the -1 padding of the fixed width is not counted)
         work["reverse_lists"] = ("hbm", 4.0 * L * R * B * S + 4.0 * rev_counts.numel()
                                  + 4.0 * float(rev_counts.sum().item()))
-        # listed entries read and written once (plus counts); the route probes of each
-        # (entry, query) pair are binary searches over rows the lists were built from
+        # listed entries read and written once (plus counts), and (one-query tiles) every
+        # route read once to mark the key tiles it holds completely, one bit each
         entries = float(rev_counts.sum().item())
-        work["split_full_blocks"] = ("hbm", 8.0 * entries + 12.0 * rev_counts.numel())
+        work["split_full_blocks"] = ("hbm", 8.0 * entries + 12.0 * rev_counts.numel()
+                                     + 4.0 * float(lens.sum().item()) + float(split_ws.numel()))
     if wl.latent:
         work["compact"] = ("hbm", (8.0 * W + 4.0) * S)
         route_ms = ms["compact"]

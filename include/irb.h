@@ -320,13 +320,21 @@ int irb_build_block_lists(const int32_t* routes, const int32_t* lens, int B, int
  *     [B, rows, width] int32; entries past each count are not written (as
  *     for the page's lists, readers ignore them).  Outputs must not alias
  *     the inputs or each other.
+ *   workspace: optional device scratch.  With block_q = 1 and at least
+ *     irb_split_full_blocks_workspace_size() bytes (one bit per (query, key
+ *     tile)), every route is read once and marks the key tiles it holds
+ *     completely, and each listed block tests one bit; otherwise (NULL, too
+ *     small, or block_q > 1) every (block, query) pair binary-searches the
+ *     query's route.  Results are the same.
  * Per-KV-group routes [RG, B, S_q, L] are RG * B route rows.
  * Requires block_q, block_k, width >= 1.
  */
+size_t irb_split_full_blocks_workspace_size(int B, int S_q, int S_k, int block_q, int block_k);
 int irb_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L,
                           int block_q, int block_k, int reverse, const int32_t* counts,
                           const int32_t* indices, int width, int32_t* full_counts, int32_t* full_indices,
-                          int32_t* part_counts, int32_t* part_indices, void* stream);
+                          int32_t* part_counts, int32_t* part_indices, void* workspace, size_t ws_bytes,
+                          void* stream);
 
 /*
  * a6 -- [QSA] gathered_qsa_gqa_attention / qsa_gqa_attention and [LATENT]

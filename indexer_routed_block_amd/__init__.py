@@ -54,7 +54,8 @@ _SIGS = {
     "irb_compact_routes": ([_P, _I64, _I, _I64, _P, _P, _P, _P], _I),
     "irb_pack_region_bitmap": ([_P, _I64, _I, _I, _P, _P], _I),
     "irb_build_block_lists_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
-    "irb_split_full_blocks": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P], _I),
+    "irb_split_full_blocks_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
+    "irb_split_full_blocks": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "irb_build_block_lists": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _SZ, _P], _I),
     "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P,
                                       _P], _I),
@@ -336,10 +337,13 @@ def build_block_lists(routes, lens, S_k, block_q, block_k, reverse, width=None, 
     return counts, indices
 
 
-def split_full_blocks(routes, lens, S_k, block_q, block_k, reverse, counts, indices):
+def split_full_blocks(routes, lens, S_k, block_q, block_k, reverse, counts, indices, workspace=None,
+                      use_workspace=True):
     """irb_split_full_blocks: (full_counts, full_indices, part_counts, part_indices) in the lists' layout.
 
-    Index entries past each count are left unwritten (uninitialised memory)."""
+    Index entries past each count are left unwritten (uninitialised memory).
+    With one-query tiles a coverage-bit workspace is allocated unless
+    ``use_workspace`` is False (then every pair searches its route)."""
     _gpu(routes, lens, counts, indices)
     lib = load_library()
     lead = tuple(routes.shape[:-3])
@@ -348,9 +352,13 @@ def split_full_blocks(routes, lens, S_k, block_q, block_k, reverse, counts, indi
     width = indices.shape[-1]
     fc, pc = torch.empty_like(counts), torch.empty_like(counts)
     fi, pi = torch.empty_like(indices), torch.empty_like(indices)
+    if workspace is None and use_workspace:
+        n = lib.irb_split_full_blocks_workspace_size(B_all, S_q, S_k, block_q, block_k)
+        workspace = torch.empty(int(n), dtype=torch.uint8, device=routes.device) if n > 0 else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.irb_split_full_blocks(_ptr(routes), _ptr(lens), B_all, S_q, S_k, L, block_q, block_k, int(bool(reverse)),
                                      _ptr(counts), _ptr(indices), width, _ptr(fc), _ptr(fi), _ptr(pc), _ptr(pi),
-                                     _stream(routes.device)))
+                                     _ptr(workspace), ws_bytes, _stream(routes.device)))
     return fc, fi, pc, pi
 
 

@@ -354,10 +354,14 @@ int irb_build_block_lists(const int32_t* routes, const int32_t* lens, int B, int
                                               static_cast<hipStream_t>(stream)));
 }
 
+size_t irb_split_full_blocks_workspace_size(int B, int S_q, int S_k, int block_q, int block_k) {
+  return irb::split_cover_bytes(B, S_q, S_k, block_q, block_k);
+}
+
 int irb_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int L_width,
                           int block_q, int block_k, int reverse, const int32_t* counts, const int32_t* indices,
                           int width, int32_t* full_counts, int32_t* full_indices, int32_t* part_counts,
-                          int32_t* part_indices, void* stream) {
+                          int32_t* part_indices, void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "irb_split_full_blocks";
   if (B < 1 || S_q < 1 || S_k < 1 || L_width < 1) return fail(IRB_ERR_INVALID, "%s: sizes must be >= 1", fn);
   if (block_q < 1 || block_k < 1) return fail(IRB_ERR_INVALID, "%s: block sizes must be >= 1", fn);
@@ -367,10 +371,12 @@ int irb_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int
   if (full_indices == indices || part_indices == indices || full_indices == part_indices ||
       full_counts == counts || part_counts == counts || full_counts == part_counts)
     return fail(IRB_ERR_INVALID, "%s: outputs must not alias the input lists or each other", fn);
+  const size_t need = irb::split_cover_bytes(B, S_q, S_k, block_q, block_k);
+  uint32_t* cover = (need > 0 && workspace && ws_bytes >= need) ? static_cast<uint32_t*>(workspace) : nullptr;
   IRB_REQUIRE_DEVICE();
   return launched(fn, irb::launch_split_full_blocks(routes, lens, B, S_q, S_k, L_width, block_q, block_k, reverse ? 1 : 0,
                                                     counts, indices, width, full_counts, full_indices, part_counts,
-                                                    part_indices, static_cast<hipStream_t>(stream)));
+                                                    part_indices, cover, static_cast<hipStream_t>(stream)));
 }
 
 static int check_attn(const char* fn, const void* q, const void* k, const void* v, int dtype, const int64_t* strides,

@@ -51,11 +51,14 @@ int launch_compact(const int32_t* in, int64_t rows, int width, int64_t key_count
 // membership words [rows, ceil(regions / 32)] of id rows [rows, slots]; regions <= 131072
 int launch_bitmap(const int32_t* ids, int64_t rows, int slots, int regions, int32_t* bitmap, hipStream_t stream);
 
-// full/partial split of a block list (lists as written by launch_block_lists)
+// full/partial split of a block list (lists as written by launch_block_lists);
+// cover (split_cover_bytes, one-query tiles only, else nullptr): scratch for
+// the per-(query, key tile) coverage bits
+size_t split_cover_bytes(int B, int S_q, int S_k, int bq, int bk);
 int launch_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int Lw, int bq,
                              int bk, int reverse, const int32_t* counts, const int32_t* indices, int width,
                              int32_t* full_counts, int32_t* full_indices, int32_t* part_counts,
-                             int32_t* part_indices, hipStream_t stream);
+                             int32_t* part_indices, uint32_t* cover, hipStream_t stream);
 int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int Lw,
                        int bq, int bk, int reverse, int32_t* counts, int32_t* indices, int width,
                        uint32_t* bitmap, hipStream_t stream);

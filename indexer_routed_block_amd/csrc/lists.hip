@@ -166,11 +166,38 @@ int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_
 // (entry, query) tests are spread over the threads; a failing one clears the
 // entry's LDS flag, and the flags are compacted in list order into the two
 // outputs.  Reads the listed entries once and writes each once.
+// One-query tiles: each query's route is read once (one wavefront per query,
+// 64 consecutive entries per step) and every key tile it holds completely --
+// an entry at a tile's first key whose entry ts - 1 later is the tile's last
+// key -- sets bit (t, j) of a [B * S_q, ceil(nkt / 32)] word matrix.
+__global__ void __launch_bounds__(kMarkWaves * 64)
+cover_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int B, int S_q, int S_k, int Lw,
+             int bk, int words, uint32_t* __restrict__ cover) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kMarkWaves + wid;
+  if (row >= static_cast<int64_t>(B) * S_q) return;
+  const int n = max(0, min(lens[row], Lw));
+  const int32_t* r = routes + row * Lw;
+  uint32_t* mrow = cover + row * words;
+  for (int e = lane; e < n; e += 64) {
+    const int id = r[e];
+    if (id < 0 || id >= S_k || id % bk != 0) continue;
+    const int ts = min(bk, S_k - id);
+    const int last = e + ts - 1;
+    if (last < n && r[last] == id + ts - 1) {
+      const int j = id / bk;
+      atomicOr(&mrow[j >> 5], 1u << (j & 31));
+    }
+  }
+}
+
+// cover != nullptr: one-query tiles (bq = 1) with the coverage bits of
+// cover_kernel; otherwise each (entry, query) pair searches the route.
 __global__ void __launch_bounds__(256)
 split_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int S_q, int S_k, int Lw, int bq,
              int bk, int reverse, int n_rows, const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
              int width, int32_t* __restrict__ fc, int32_t* __restrict__ fi, int32_t* __restrict__ pc,
-             int32_t* __restrict__ pi) {
+             int32_t* __restrict__ pi, const uint32_t* __restrict__ cover, int words) {
   __shared__ int flag[256];
   __shared__ int ent[256];
   __shared__ int wsum[4];
@@ -203,6 +230,10 @@ split_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ len
       const int t = static_cast<int>(tt), k0 = static_cast<int>(k0l);
       const int ts = min(bk, S_k - k0);
       const int64_t qrow = static_cast<int64_t>(b) * S_q + t;
+      if (cover) {
+        if (!((cover[qrow * words + (j >> 5)] >> (j & 31)) & 1u)) atomicAnd(&flag[e], 0);
+        continue;
+      }
       const int n = max(0, min(lens[qrow], Lw));
       const int32_t* r = routes + qrow * Lw;
       int lo = 0, hi = n;
@@ -235,16 +266,30 @@ split_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ len
   }
 }
 
+size_t split_cover_bytes(int B, int S_q, int S_k, int bq, int bk) {
+  if (bq != 1 || B < 1 || S_q < 1 || S_k < 1 || bk < 1) return 0;
+  const size_t nkt = (static_cast<size_t>(S_k) + bk - 1) / bk;
+  return static_cast<size_t>(B) * S_q * ((nkt + 31) / 32) * 4;
+}
+
 int launch_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int Lw, int bq,
                              int bk, int reverse, const int32_t* counts, const int32_t* indices, int width,
                              int32_t* full_counts, int32_t* full_indices, int32_t* part_counts,
-                             int32_t* part_indices, hipStream_t stream) {
+                             int32_t* part_indices, uint32_t* cover, hipStream_t stream) {
   const int nqt = (S_q + bq - 1) / bq, nkt = (S_k + bk - 1) / bk;
   const int n_rows = reverse ? nkt : nqt;
   if (n_rows <= 0 || B <= 0) return 0;
+  const int words = (nkt + 31) / 32;
+  if (cover) {
+    const int64_t qrows = static_cast<int64_t>(B) * S_q;
+    int rc = launch_fill_i32(reinterpret_cast<int32_t*>(cover), qrows * words, 0, stream);
+    if (rc) return rc;
+    hipLaunchKernelGGL(cover_kernel, dim3(static_cast<unsigned>((qrows + kMarkWaves - 1) / kMarkWaves)),
+                       dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw, bk, words, cover);
+  }
   hipLaunchKernelGGL(split_kernel, dim3(static_cast<unsigned>(n_rows), static_cast<unsigned>(B)), dim3(256), 0, stream,
                      routes, lens, S_q, S_k, Lw, bq, bk, reverse, n_rows, counts, indices, width, full_counts,
-                     full_indices, part_counts, part_indices);
+                     full_indices, part_counts, part_indices, cover, words);
   return 0;
 }
 

@@ -110,13 +110,17 @@ def test_split_full_blocks_validation():
     lib = irb.load_library()
     A, B_, C_, D_, E_ = (ctypes.c_void_p(0x1000 * k) for k in range(1, 6))
     call = lambda bq=16, bk=16, width=8, fi=C_, pi=D_, fc=E_, pc=ctypes.c_void_p(0x7000): lib.irb_split_full_blocks(
-        A, B_, 1, 64, 64, 8, bq, bk, 0, ctypes.c_void_p(0x9000), ctypes.c_void_p(0xA000), width, fc, fi, pc, pi, None)
+        A, B_, 1, 64, 64, 8, bq, bk, 0, ctypes.c_void_p(0x9000), ctypes.c_void_p(0xA000), width, fc, fi, pc, pi, None,
+        0, None)
     assert _err(call(bq=0))[0] == 3
     assert _err(call(width=0))[0] == 3
     code, msg = _err(call(fi=ctypes.c_void_p(0xA000)))
     assert code == 3 and "alias" in msg
     assert _err(call(fi=D_))[0] == 3
     assert _err(call(pc=E_))[0] == 3
+    # coverage bits: one-query tiles only, one bit per (query, key tile), rows of 32-bit words
+    assert lib.irb_split_full_blocks_workspace_size(2, 100, 1000, 1, 16) == 2 * 100 * 2 * 4
+    assert lib.irb_split_full_blocks_workspace_size(2, 100, 1000, 4, 16) == 0
 
 
 def test_grouped_route_workspace_size():

@@ -313,6 +313,15 @@ def _split_check(routes, lens, S, bq, bk, reverse):
     valid_p = np.arange(pi.shape[-1]) < want[2][..., None]
     np.testing.assert_array_equal(fi[valid_f], want[1][valid_f], err_msg="full_indices")
     np.testing.assert_array_equal(pi[valid_p], want[3][valid_p], err_msg="part_indices")
+    if bq == 1:
+        # one-query tiles: the coverage-bit path (above) and the route-search path agree
+        other = [host(x) for x in irb.split_full_blocks(r_d, l_d, S, bq, bk, reverse, counts, indices,
+                                                         use_workspace=False)]
+        np.testing.assert_array_equal(other[0], got[0])
+        np.testing.assert_array_equal(other[2], got[2])
+        o1, o3 = other[1].reshape(fi.shape), other[3].reshape(pi.shape)
+        np.testing.assert_array_equal(o1[valid_f], want[1][valid_f])
+        np.testing.assert_array_equal(o3[valid_p], want[3][valid_p])
     print(f"  {int(want[0].sum())} full / {int(want[2].sum())} partial blocks")
     return int(want[0].sum())
 
