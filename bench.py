@@ -162,12 +162,13 @@ def main():
         c, topk, window = wl.c, wl.topk, wl.window
         L = irb.route_width(topk, c, window)
         nb_blocks = S // c
-        q0 = 0 if cu is not None else min(irb.first_sparse_query(c, topk), S - 1)
+        # the fused call covers every row: the score kernel skips rows that see at most topk
+        # blocks and the selection takes all their visible blocks without reading scores
+        q0 = 0
         fused_ws = torch.empty(max(int(lib.irb_route_topk_fused_groups_workspace_size(
             B, S, c, wl.D_idx, topk, q0, S, R)), 4), dtype=torch.uint8, device=dev)
         sel = torch.empty(G_lead + (B, S, topk), dtype=torch.int32, device=dev)
         cnt = torch.empty(G_lead + (B, S), dtype=torch.int32, device=dev)
-        dummy = torch.empty((B, 1, 1), dtype=torch.float32, device=dev)
         routes = torch.empty(G_lead + (B, S, L), dtype=torch.int32, device=dev)
         lens = torch.empty(G_lead + (B, S), dtype=torch.int32, device=dev)
         sel_g, cnt_g = sel.view(R, B, S, topk), cnt.view(R, B, S)
@@ -227,10 +228,6 @@ def main():
         timed("compress", lambda: C(lib.irb_compress_keys(
             irb.ctypes.byref(lay), c, P(d["kI"]), irb._dtype_code(d["kI"]), d["kI"].stride(0), d["kI"].stride(1),
             wl.D_idx, P(d["gamma"]), 1e-5, P(d["freqs"]), d["freqs"].shape[-1], P(kc), P(cu_blocks), sptr)), rec)
-        if q0 > 0:
-            timed("select_dense_rows", lambda: [C(lib.irb_select_topk_regions(
-                irb.ctypes.byref(lay), P(dummy), 1, 0, q0, P(cu_blocks), c, topk, P(sel_g[g]), P(cnt_g[g]), sptr))
-                for g in range(R)], rec)
         if R == 1:
             timed("score_select", lambda: C(lib.irb_route_topk_fused(
                 irb.ctypes.byref(lay), P(d["qI"]), irb._dtype_code(d["qI"]), wl.H_idx, wl.D_idx, P(d["w"]), P(kc),
@@ -329,9 +326,7 @@ def main():
         work["region_bitmap"] = ("hbm", R * B * S * (4.0 * topk + 4.0 * ((nb_blocks + 31) // 32)))
         work["score_select"] = ("mfma", 2.0 * wl.H_idx * wl.D_idx * sparse_pairs)
         work["expand"] = ("hbm", R * float(np.sum(valid_t)) * (4 * topk + 4 * L + 4))
-        if q0 > 0:
-            work["select_dense_rows"] = ("hbm", 4.0 * topk * q0 * B * R)
-        route_ms = sum(ms[n] for n in ("compress", "select_dense_rows", "score_select", "expand") if n in ms)
+        route_ms = sum(ms[n] for n in ("compress", "score_select", "expand") if n in ms)
     stage_out = {}
     for name, t in ms.items():
         bound, amount = work[name]

@@ -445,9 +445,9 @@ def route(k_idx, q_idx, w, gamma, freqs, c, topk, window, eps=1e-5, score_scale=
           row_lens=None, workspace=None):
     """compress -> fused score/select -> expand, all in the library.
 
-    Returns dict(kc, cu_blocks, sel, cnt, routes, lens).  With a single
-    document per row, query rows before the first sparse position take every
-    visible block and are not scored.  Index queries with a group axis
+    Returns dict(kc, cu_blocks, sel, cnt, routes, lens).  Query rows that see
+    at most topk blocks take every visible block: the fused call does not
+    score them and its selection takes them without scores.  Index queries with a group axis
     (q_idx [B, S, R, H, D], w [B, S, R, H]) give every group its own
     selection and routes: sel [R, B, S, topk], routes [R, B, S, L].
     """
@@ -456,16 +456,9 @@ def route(k_idx, q_idx, w, gamma, freqs, c, topk, window, eps=1e-5, score_scale=
     R = q_idx.shape[2] if grouped else 1
     lead = (R,) if grouped else ()
     kc, cu_blocks = compress_keys(k_idx, gamma, freqs, c, eps, cu_seqlens, row_lens)
-    q0 = 0 if cu_seqlens is not None else min(first_sparse_query(c, topk), S - 1)
     sel = torch.empty(lead + (B, S, topk), dtype=torch.int32, device=q_idx.device)
     cnt = torch.empty(lead + (B, S), dtype=torch.int32, device=q_idx.device)
-    if q0 > 0:
-        # rows that see at most topk blocks: selection needs no scores (the same for every group)
-        dummy = torch.empty((B, q0, 1), dtype=torch.float32, device=q_idx.device)
-        for g in range(R):
-            select_topk_regions(dummy, c, topk, S, q0=0, cu_blocks=cu_blocks, cu_seqlens=cu_seqlens,
-                                row_lens=row_lens, sel=sel[g] if grouped else sel, cnt=cnt[g] if grouped else cnt)
-    route_topk_fused(q_idx, w, kc, c, topk, q0=q0, q1=S, score_scale=score_scale, cu_blocks=cu_blocks,
+    route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=S, score_scale=score_scale, cu_blocks=cu_blocks,
                      cu_seqlens=cu_seqlens, row_lens=row_lens, workspace=workspace, sel=sel, cnt=cnt)
     routes, lens = expand_and_compact_routes(sel, cnt, c, window, topk, cu_blocks=cu_blocks, cu_seqlens=cu_seqlens,
                                              row_lens=row_lens)
