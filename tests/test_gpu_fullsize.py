@@ -396,3 +396,79 @@ def _sample_rows_plain(T, seed, n):
     rows = {0, 1, 7, T // 2, T - 2, T - 1}
     rows |= set(int(t) for t in rng.integers(0, T, n - len(rows)))
     return sorted(rows)
+
+
+def _group_routes(name, R):
+    """One route per KV group: the shared-route recipe with each group's own
+    uniform block draws (seeded per group)."""
+    wl = synth.WORKLOADS[name]
+    cu, (valid, start, base, nb) = _info(name)
+    slot = np.arange(wl.topk)
+    nb3 = nb[..., None].astype(np.int64)
+    keff = np.minimum(wl.topk, nb)
+    cnt = np.where(valid, keff, 0).astype(np.int32)
+    rs, ls = [], []
+    for g in range(R):
+        u = synth.make_inputs(wl, parts=("draws",), seed=wl.seed + 100 + g)["draws"]
+        pick = np.minimum((u.astype(np.float64) * nb3).astype(np.int64), np.maximum(nb3 - 1, 0))
+        local = np.where(nb3 <= wl.topk, slot, pick)
+        sel = np.where(slot < keff[..., None], base[..., None] + local, -1).astype(np.int32)
+        r, n = oracle.expand_routes(sel, cnt, wl.c, wl.window, wl.topk, cu_seqlens=cu)
+        rs.append(r)
+        ls.append(n)
+    return np.stack(rs), np.stack(ls)
+
+
+def test_grouped_attention_full_size_varlen():
+    """Packed T=32768 training step with one route per KV group (4 groups):
+    forward and dq on sampled rows of every head, dK/dV on sampled key tiles of
+    every group, and per-group exact identities over every key."""
+    name = "varlen"
+    wl = synth.WORKLOADS[name]
+    R, S, G = wl.Hkv, wl.S, wl.Hq // wl.Hkv
+    banner(f"full-size grouped attention fwd+bwd {name} S={S} groups={R}")
+    t0 = time.time()
+    routes, lens = _group_routes(name, R)
+    x = _inputs(name, ("attn",))
+    xb = _inputs(name, ("bwd",))
+    scale = 1.0 / math.sqrt(wl.D)
+    _log("routes + inputs", t0)
+    q, k, v = (to_dev(x[n], BF16) for n in ("q", "k", "v"))
+    r_d, l_d = to_dev(routes), to_dev(lens)
+    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, scale)
+    rc, ri = irb.build_block_lists(r_d, l_d, S, 1, 16, reverse=True)
+    dO = to_dev(xb["dO"], BF16)
+    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, 1, 16, scale)
+    torch.cuda.synchronize()
+    _log("gpu fwd + lists + bwd", t0)
+    rows = _sample_rows(name, 16)
+    ro, rlse = oracle.attention_fwd_grouped(x["q"], x["k"], x["v"], routes, scale, rows=[(0, t) for t in rows])
+    attn_tol_check(host(o)[0, rows], ro[0, rows], BF16, f"o ({len(rows)} rows)")
+    got_l, want_l = host(lse)[0][:, rows], rlse[0][:, rows]
+    fin = np.isfinite(want_l)
+    assert np.array_equal(np.isneginf(got_l), ~fin)
+    assert np.max(np.abs(got_l[fin] - want_l[fin]), initial=0.0) <= 1e-3
+    tiles = [S // 16 - 1, (S // 2) // 16]
+    keys = [(0, 16 * j + i) for j in tiles for i in range(16) if 16 * j + i < S]
+    rdq, rdk, rdv = oracle.attention_bwd_grouped(x["q"], x["k"], x["v"], routes, xb["dO"], scale,
+                                                 rows=[(0, t) for t in rows], keys=keys)
+    kid = [kk for _, kk in keys]
+    attn_tol_check(host(dq)[0, rows], rdq[0, rows], BF16, f"dq ({len(rows)} rows)")
+    attn_tol_check(host(dk)[0, kid], rdk[0, kid], BF16, f"dk ({len(kid)} keys)")
+    attn_tol_check(host(dv)[0, kid], rdv[0, kid], BF16, f"dv ({len(kid)} keys)")
+    _log("sampled rows and keys", t0)
+    # per KV head g (its own route's non-empty queries): sum_k dV = sum of dO over the group's heads,
+    # sum_k dK = 0, and sum_t q.dq = sum_k dK.k
+    f64 = torch.float64
+    for g in range(R):
+        live = to_dev(lens[g, 0] > 0)
+        hs = slice(g * G, (g + 1) * G)
+        want = (dO[0, :, hs].to(f64) * live[:, None, None]).sum((0, 1))
+        dvg, dkg = dv[0, :, g].to(f64), dk[0, :, g].to(f64)
+        assert bool(((dvg.sum(0) - want).abs() <= ID_TOL * dvg.abs().sum(0) + 1e-6).all()), f"sum dV, group {g}"
+        assert bool((dkg.sum(0).abs() <= ID_TOL * dkg.abs().sum(0) + 1e-6).all()), f"sum dK, group {g}"
+        qq = (q[0, :, hs].to(f64) * dq[0, :, hs].to(f64)).sum()
+        kk = (dkg * k[0, :, g].to(f64)).sum()
+        mag = (q[0, :, hs].to(f64) * dq[0, :, hs].to(f64)).abs().sum() + (dkg * k[0, :, g].to(f64)).abs().sum()
+        assert bool((qq - kk).abs() <= ID_TOL * mag), f"trace identity, group {g}"
+    _log("identities", t0)
