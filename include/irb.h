@@ -218,10 +218,10 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
  *   workspace: irb_route_topk_fused_groups_workspace_size() bytes (the split
  *          keys once, score rows of every group); any size holding the split
  *          keys and one score row per group works.
- * bf16 queries with 4 heads per group, groups * 4 in {16, 32} and D_idx in
- * {64, 128} score every group in one launch (each lane's four accumulator
- * rows are one group's heads); other shapes score the groups one after
- * another with the ungrouped kernels.
+ * bf16 queries with 4 or 8 heads per group, groups * heads in {16, 32} and
+ * D_idx in {64, 128} score every group in one launch (a lane's four
+ * accumulator rows are one group's heads, or half of them); other shapes
+ * score the groups one after another with the ungrouped kernels.
  * Requires 1 <= groups <= 64; everything else as for the ungrouped calls.
  */
 size_t irb_route_topk_fused_groups_workspace_size(int B, int S, int c, int D_idx, int topk, int q0, int q1,

@@ -27,9 +27,10 @@ int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, c
                       const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,
                       int q0, int q1, int j0, int j1, float* out, int64_t out_stride, int write_invisible,
                       int skip_nb, int n_grp, hipStream_t stream);
-// All groups of 4 heads in one launch (bf16 queries [B, S, groups, 4, D],
-// weights [B, S, groups, 4], groups * 4 in {16, 32}, D in {64, 128}): group
-// g's tile at out + g * group_stride, each laid out as launch_score_tile's.
+// All groups of 4 or 8 heads in one launch (bf16 queries [B, S, groups,
+// H_group, D], weights [B, S, groups, H_group], groups * H_group in {16, 32},
+// D in {64, 128}): group g's tile at out + g * group_stride, each laid out as
+// launch_score_tile's.
 bool score_grouped_ok(int dtype, int groups, int H_group, int D);
 int launch_score_grouped(const Layout& L, const void* q, int dtype, int groups, int H_group, int D, const float* w,
                          const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,

@@ -66,19 +66,21 @@ IRB_DEV void visible_blocks(const Layout& L, const int32_t* cu_blocks, int c, in
 // a row of low halves) and stream through four LDS buffers by direct
 // global-to-LDS loads, three chunks in flight; otherwise the FP32 keys are
 // split while staging through two buffers.
-// GS = 4 (with H a multiple of 16): the H heads are H / 4 groups of 4 heads
-// with one score each ([CSA] indexer_score_tile, scores per KV group), all
-// groups in one launch: the four accumulator rows a lane holds are exactly
-// one group's heads, so each lane's weighted sum is that group's score and
-// no cross-lane reduction is needed; group gi's tile starts gi * gstride
-// floats after out.  GS = 0: one score per query over all H heads.
+// GS = 4 or 8 (with H a multiple of 16): the H heads are H / GS groups of GS
+// heads with one score each ([CSA] indexer_score_tile, scores per KV group),
+// all groups in one launch.  The four accumulator rows a lane holds are
+// heads 4 g16 .. 4 g16 + 3 of its row tile: for GS = 4 exactly one group,
+// so each lane's weighted sum is that group's score; for GS = 8 one pair
+// exchange between lane groups (g16, g16 ^ 1) completes it.  Group gi's
+// tile starts gi * gstride floats after out.  GS = 0: one score per query
+// over all H heads.
 template <typename QT, int D, int H, bool kPre, int GS>
 __global__ void __launch_bounds__(256, 2)
 score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kc,
              const uint16_t* __restrict__ kcs, const int32_t* __restrict__ cu_blocks, int c, float scale, int q0,
              int q1, int j0, int j1, float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg,
              int write_invisible, int skip_nb, int n_grp, int64_t gstride) {
-  static_assert(GS == 0 || (GS == 4 && H % 16 == 0), "grouped scores: groups of 4 heads, H a multiple of 16");
+  static_assert(GS == 0 || ((GS == 4 || GS == 8) && H % 16 == 0), "grouped scores: groups of 4 or 8 heads, H a multiple of 16");
   constexpr int NGRP = GS ? H / GS : 1;             // score tiles written
   constexpr bool kPerQ = H < 16 || GS > 0;          // visible ranges kept per query (wave-uniform)
   constexpr int KS = D / 32;
@@ -323,17 +325,18 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
         }
       }
       const int jb = jc + l16;
-      if constexpr (GS == 4) {
-        // row tile rt: query 16 rt / H, heads 16 rt % H + 4 g16 + i = group (16 rt % H) / 4 + g16
+      if constexpr (GS > 0) {
+        // row tile rt: query 16 rt / H, heads 16 rt % H + 4 g16 + i, group (16 rt % H + 4 g16) / GS
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           float p = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) p = fmaf(wv[rt][i], fmaxf(acc[rt][i], 0.f), p);
+          if constexpr (GS == 8) p = row_pair_sum(p);     // lane groups 2m, 2m + 1 hold the pair's sum
           const int k = (16 * rt) / H;
-          const int gi = ((16 * rt) % H) / 4 + g16;
+          const int gi = ((16 * rt) % H + 4 * g16) / GS;
           const int qw = qa + wid * QW + k;
-          if (qw < qe && jb < ce) {
+          if ((GS == 4 || (g16 & 1) == 0) && qw < qe && jb < ce) {
             const bool vis = jb >= vbk[k] && jb < vbk[k] + vnk[k];
             if (vis || write_invisible)
               otile[gi * gstride + static_cast<int64_t>(qw - qa) * ostride + (jb - j0)] = vis ? scale * p : -INFINITY;
@@ -444,7 +447,7 @@ static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, c
                          dim3(256), 0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out,    \
                          ostride, seg, n_seg, write_invisible, skip_nb, n_grp, gstride);                      \
     return 0;
-  if constexpr (GS == 4) {
+  if constexpr (GS > 0) {
     switch (H) {
       IRB_SCORE_CASE(16)
       IRB_SCORE_CASE(32)
@@ -501,8 +504,8 @@ int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, c
 }
 
 bool score_grouped_ok(int dtype, int groups, int H_group, int D) {
-  return dtype == IRB_BF16 && H_group == 4 && (groups * H_group == 16 || groups * H_group == 32) &&
-         (D == 64 || D == 128);
+  return dtype == IRB_BF16 && (H_group == 4 || H_group == 8) && groups > 1 &&
+         (groups * H_group == 16 || groups * H_group == 32) && (D == 64 || D == 128);
 }
 
 int launch_score_grouped(const Layout& L, const void* q, int dtype, int groups, int H_group, int D, const float* w,
@@ -512,11 +515,16 @@ int launch_score_grouped(const Layout& L, const void* q, int dtype, int groups, 
   if (!score_grouped_ok(dtype, groups, H_group, D)) return static_cast<int>(hipErrorInvalidValue);
   const uint16_t* qb = static_cast<const uint16_t*>(q);
   const int H = groups * H_group;
-  if (D == 64)
-    return launch_score_d<uint16_t, 64, 4>(L, qb, H, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1, out,
-                                           out_stride, write_invisible, skip_nb, 1, stream, group_stride);
-  return launch_score_d<uint16_t, 128, 4>(L, qb, H, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1, out,
+#define IRB_SCORE_GROUPED(DD, GG)                                                                           \
+  return launch_score_d<uint16_t, DD, GG>(L, qb, H, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1, out, \
                                           out_stride, write_invisible, skip_nb, 1, stream, group_stride);
+  if (D == 64) {
+    if (H_group == 4) { IRB_SCORE_GROUPED(64, 4) }
+    IRB_SCORE_GROUPED(64, 8)
+  }
+  if (H_group == 4) { IRB_SCORE_GROUPED(128, 4) }
+  IRB_SCORE_GROUPED(128, 8)
+#undef IRB_SCORE_GROUPED
 }
 
 }  // namespace irb

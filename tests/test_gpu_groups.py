@@ -49,8 +49,12 @@ def _grouped_inputs(wl_name, S, layout, R):
 
 @pytest.mark.parametrize("wl_name,S,layout,R", [("s8192", 2048, "single", 4), ("varlen", 4096, "packed", 4),
                                                 ("long", 2048, "single", 8), ("s8192", 1500, "rows", 2),
+                                                ("long", 2048, "single", 4), ("long", 1024, "single", 2),
                                                 ("tiny", 512, "single", 1)])
 def test_grouped_score_tile(wl_name, S, layout, R):
+    """Groups of 4 and 8 heads over 16 or 32 index heads run in one launch
+    (s8192: 4x4, 2x8; long: 8x4, 4x8); long with 2 groups of 16 heads and
+    the tiny workload take the per-group loop."""
     banner(f"grouped score {wl_name} S={S} {layout} groups={R}")
     wl, x, d = _grouped_inputs(wl_name, S, layout, R)
     kc_h, cub = oracle.compress_keys(x["kI"], x["gamma"], 1e-5, x["freqs"], wl.c, x["cu_seqlens"], x["row_lens"])
@@ -134,7 +138,8 @@ def _check_grouped_selection(wl, x, topk, r, ref):
 
 
 @pytest.mark.parametrize("wl_name,S,layout,R", [("s8192", 2048, "single", 4), ("varlen", 4096, "packed", 4),
-                                                ("long", 4096, "single", 8), ("s8192", 1500, "rows", 2)])
+                                                ("long", 4096, "single", 8), ("s8192", 1500, "rows", 2),
+                                                ("long", 4096, "single", 4)])
 def test_grouped_route_pipeline(wl_name, S, layout, R):
     """compress -> grouped fused score/select -> per-group expand (+ bitmaps); bit-exact outside near ties."""
     banner(f"grouped pipeline {wl_name} S={S} {layout} groups={R}")
