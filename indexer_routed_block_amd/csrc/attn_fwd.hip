@@ -849,13 +849,14 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     // wave w takes queries w, w + 4, ...; each lane takes 8 consecutive
     // entries of a 512-entry chunk and ORs each entry's bit into its mask
     // word with an LDS atomic, branch-free (an entry outside [lo, hi) or the
-    // segment ORs 0 into word 0)
+    // segment ORs 0 into word `lane` of the row: a different word, and bank,
+    // for every such lane, so they do not serialise on one LDS address)
     auto or_entries = [&](int qi, int eb, int lo, int hi, const int (&ids)[8]) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int id = ids[j];
         const bool ok = eb + j >= lo && eb + j < hi && id >= key0 && id < key1 && id < a.S_k;
-        const int rel = ok ? id - key0 : 0;
+        const int rel = ok ? id - key0 : 32 * lane;
         atomicOr(&mask[qi][rel >> 5], ok ? 1u << (rel & 31) : 0u);
       }
     };
