@@ -847,17 +847,30 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     }
     __syncthreads();
     // wave w takes queries w, w + 4, ...; each lane takes 8 consecutive
-    // entries of a 512-entry chunk and ORs each entry's bit into its mask
-    // word with an LDS atomic, branch-free (an entry outside [lo, hi) or the
-    // segment ORs 0 into word `lane` of the row: a different word, and bank,
-    // for every such lane, so they do not serialise on one LDS address)
+    // entries of a 512-entry chunk.  The route is ascending, so the lane's
+    // entries that fall in one mask word are consecutive: their bits are
+    // ORed together in registers and the word takes one LDS atomic at the
+    // end of the run.  Branch-free: every step issues one atomic, and a step
+    // that ends no run (or an entry outside [lo, hi) or the segment) ORs 0
+    // into word `lane` of the row -- a different word, and bank, per lane.
     auto or_entries = [&](int qi, int eb, int lo, int hi, const int (&ids)[8]) __attribute__((always_inline)) {
+      int wd[8];
+      uint32_t bit[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int id = ids[j];
         const bool ok = eb + j >= lo && eb + j < hi && id >= key0 && id < key1 && id < a.S_k;
-        const int rel = ok ? id - key0 : 32 * lane;
-        atomicOr(&mask[qi][rel >> 5], ok ? 1u << (rel & 31) : 0u);
+        const int rel = id - key0;
+        wd[j] = ok ? rel >> 5 : -1;
+        bit[j] = ok ? 1u << (rel & 31) : 0u;
+      }
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc |= bit[j];
+        const bool flush = wd[j] >= 0 && (j == 7 || wd[j + 1] != wd[j]);
+        atomicOr(&mask[qi][flush ? wd[j] : lane], flush ? acc : 0u);
+        acc = (j < 7 && wd[j + 1] == wd[j]) ? acc : 0u;
       }
     };
     if ((a.L & 3) == 0 && a.L >= 4 && (reinterpret_cast<uintptr_t>(a.routes) & 15) == 0) {
