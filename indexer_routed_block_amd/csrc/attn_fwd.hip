@@ -566,7 +566,9 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   constexpr int NIK = 32 * NCK / 256, NIV = 32 * NCV / 256;   // loads per wave per tile
   static_assert(NIK >= 1 && NIV >= 1, "tile loads");
   __shared__ __align__(16) char raw[3 * BUF];
-  __shared__ uint32_t mask[BQ][kSegTiles];
+  // one padding word per row: the softmax reads the words of a wave's four
+  // queries at once, and rows a multiple of 256 words apart share a bank
+  __shared__ uint32_t mask[BQ][kSegTiles + 1];
   __shared__ int tiles[kSegTiles];
   __shared__ int s_ntiles;
   __shared__ int cursor[BQ];
@@ -818,7 +820,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     const int nseg = min(kSegTiles, kt_last - seg0 + 1);
     const int key0 = seg0 * 32, key1 = key0 + kSegTiles * 32;
     __syncthreads();
-    for (int i = tid; i < BQ * kSegTiles; i += 256) (&mask[0][0])[i] = 0u;
+    for (int i = tid; i < BQ * (kSegTiles + 1); i += 256) (&mask[0][0])[i] = 0u;
     __syncthreads();
     // route masks of this segment.  Entry ranges [lo, hi) per query (one lane
     // per query, in parallel): lo is the cursor left by the previous segment,
