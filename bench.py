@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: HBM rate of the token-streaming kernels (key compression, "
                          "index-query preparation) over sequence lengths 8K..2M")
+    ap.add_argument("--peaks", action="store_true",
+                    help="instead of the step: achievable bf16 GEMM rate (vendor library) and device copy bandwidth")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (HBM counter calibration)")
     return ap.parse_args()
@@ -115,6 +117,9 @@ def main():
 
     if args.sweep:
         sweep(args)
+        return
+    if args.peaks:
+        peaks()
         return
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
@@ -390,6 +395,50 @@ def main():
     if not args.no_cpu_baseline and wl.name == "s8192" and R == 1:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_sample_rows)
     print(json.dumps(result), flush=True)
+
+
+def peaks():
+    """Achievable ceilings beside the published peaks: a bf16 GEMM through the
+    vendor BLAS (torch.matmul, 8192^3, FP32 accumulate) and a 4 GiB device copy,
+    each the median of 10 HIP-event timings after 3 warm-ups."""
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(99)
+
+    def med(fn, n=10):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts]))
+
+    N = 8192
+    a = torch.randn((N, N), generator=gen, device=dev).to(torch.bfloat16)
+    b = torch.randn((N, N), generator=gen, device=dev).to(torch.bfloat16)
+    c = torch.empty((N, N), dtype=torch.bfloat16, device=dev)
+    ms_gemm = med(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    n = (4 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ms_copy = med(lambda: dst.copy_(src))
+    gemm_tflops = 2.0 * N ** 3 / (ms_gemm / 1e3) / 1e12
+    copy_gbs = 2.0 * n * 4 / (ms_copy / 1e3) / 1e9
+    print(json.dumps({"peaks": "achievable ceilings", "bf16_gemm_8192": {"ms": round(ms_gemm, 4),
+                      "TFLOPs": round(gemm_tflops, 1), "frac_of_published": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+                      "device_copy_4GiB": {"ms": round(ms_copy, 4), "GBps_read_plus_write": round(copy_gbs, 1),
+                                           "frac_of_published": round(copy_gbs / HBM_PEAK_GBS, 4)}}), flush=True)
 
 
 def sweep(args):
