@@ -205,6 +205,7 @@ def main():
         dq = torch.empty((B, S, Hq, Dqk), dtype=dt, device=dev)
         dk = torch.empty((B, S, Hkv, Dqk), dtype=dt, device=dev)
         dv = dk if wl.latent else torch.empty((B, S, Hkv, Dv), dtype=dt, device=dev)
+        dropped = torch.zeros(1, dtype=torch.int64, device=dev)
         bwd_ws = torch.empty(max(int(lib.irb_sparse_gqa_attention_bwd_workspace_size(
             B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q), R)), 4), dtype=torch.uint8, device=dev)
 
@@ -267,7 +268,7 @@ def main():
             timed("attn_bwd", lambda: C(lib.irb_sparse_gqa_attention_bwd(
                 P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens), R,
                 P(rev_counts), P(rev_idx), rbq, rbk, nqt, B, S, S, L, Hq, Hkv, Dqk, Dv, scale, P(dq), P(dk), P(dv),
-                P(bwd_ws), bwd_ws.numel(), sptr)), rec)
+                P(bwd_ws), bwd_ws.numel(), P(dropped), sptr)), rec)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -392,8 +393,12 @@ def main():
         "stages": stage_out,
         "input_gen_s": round(gen_s, 2),
     }
+    if backward:
+        result["bwd_dropped_hits"] = int(dropped.item())
     if not args.no_cpu_baseline and wl.name == "s8192" and R == 1:
-        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_sample_rows)
+        result["cpu_baseline"], check = cpu_baseline(wl, x, args.cpu_sample_rows, sel.cpu().numpy())
+        result["near_tie_rows"] = check["near_tie_rows"]
+        result["route_check"] = check
     print(json.dumps(result), flush=True)
 
 
@@ -505,12 +510,17 @@ def sweep(args):
                       "rows": rows}), flush=True)
 
 
-def cpu_baseline(wl, x, n_rows):
+def cpu_baseline(wl, x, n_rows, gpu_sel):
     """The FP64 oracle on a bounded sample: n_rows query rows spread over the sequence.
 
     Route pipeline (compress all blocks, then score / select / expand the
     sampled rows) and the attention forward of the same rows, each timed
     with perf_counter on this host's cores.
+
+    Also returns, untimed, the selection check of every query row: the
+    oracle's scores and top-k for all rows against the selection the timed
+    GPU steps produced (``gpu_sel`` [B, S, topk]); rows whose k-th and
+    (k+1)-th oracle scores lie within 1e-4 relative are counted as near ties.
     """
     import numpy as np
 
@@ -537,10 +547,18 @@ def cpu_baseline(wl, x, n_rows):
     attn_s = time.perf_counter() - t1
     pairs = int((routes[0, rows] >= 0).sum())
     flop = 2.0 * (wl.D + wl.Dv) * wl.Hq * pairs
+    t2 = time.perf_counter()
+    s_all = oracle.indexer_scores(x["qI"], x["w"], kc, wl.c)
+    sel_all, _ = oracle.select_topk(s_all, wl.c, wl.topk)
+    ties = oracle.near_tie_rows(s_all, wl.c, wl.topk)
+    differ = ~np.all(np.asarray(gpu_sel) == sel_all, axis=-1)
+    check = {"rows": int(ties.size), "near_tie_rows": int(ties.sum()), "rows_differing": int(differ.sum()),
+             "non_tie_rows_differing": int((differ & ~ties).sum()),
+             "oracle_s": round(time.perf_counter() - t2, 2)}
     return {"value": round(flop / attn_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n_rows} query rows (evenly spaced from S/4 to S-1) of the {wl.name} workload; FP64 NumPy; "
                       f"attention fwd {attn_s:.2f} s, route pipeline {route_s:.2f} s "
-                      f"({n_rows / route_s:.1f} routed queries/s incl. full key compression)"}
+                      f"({n_rows / route_s:.1f} routed queries/s incl. full key compression)"}, check
 
 
 if __name__ == "__main__":

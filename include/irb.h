@@ -147,7 +147,9 @@ int irb_prepare_index_queries(const void* q_raw, int dtype, int64_t n_tokens, in
  *     out[b, t-q0, j-j0] = score_scale * sum_h w[b,t,h] * max(0, q[b,t,h,:] . kc[b,j,:])
  * for visible j, and -inf otherwise (padding queries: all -inf).
  * The products use bf16 MFMA with kc split into bf16 high+low parts and FP32
- * accumulation (fp32 queries are split the same way).
+ * accumulation (fp32 queries are split the same way).  score_scale = 0
+ * selects the default 1/sqrt(D_idx) ([QSA] select_qsa_token_ids); otherwise
+ * it must be finite and > 0.
  *
  *   q_idx  [B, S, H_idx, D_idx] dtype contiguous
  *   w      [B, S, H_idx] fp32 contiguous
@@ -155,7 +157,7 @@ int irb_prepare_index_queries(const void* q_raw, int dtype, int64_t n_tokens, in
  *   cu_blocks as written by irb_compress_keys (packed layouts), else NULL
  *   out    OUT fp32, element (b, t-q0, j-j0) at out[(b*(q1-q0) + t-q0)*out_row_stride + j-j0]
  * Requires 0 <= q0 < q1 <= S, 0 <= j0 < j1 <= S/c, out_row_stride >= j1-j0,
- * H_idx in {4, 8, 16, 32, 48, 64}, D_idx in {32, 64, 128}, score_scale > 0.
+ * H_idx in {4, 8, 16, 32, 48, 64}, D_idx in {32, 64, 128}.
  */
 int irb_indexer_score_tile(const irb_layout* layout, const void* q_idx, int dtype, int H_idx,
                            int D_idx, const float* w, const float* kc, const int32_t* cu_blocks,
@@ -344,6 +346,8 @@ int irb_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int
  *     o = softmax(softmax_scale * q K_R^T) V_R,  lse = logsumexp(scale * q K_R^T)
  * A query with lens = 0 gets o = 0 and lse = -inf.  Softmax and both
  * products accumulate in FP32; o is rounded once to the input dtype.
+ * softmax_scale = 0 selects the default 1/sqrt(Dqk); otherwise it must be
+ * finite and > 0.
  *
  *   q [B, S_q, Hq, Dqk], k [B, S_k, Hkv, Dqk], v [B, S_k, Hkv, Dv]: dtype,
  *     element strides strides[0..2] = q (batch, token, head), [3..5] = k,
@@ -361,7 +365,7 @@ int irb_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int
  *   out OUT [B, S_q, Hq, Dv] dtype contiguous; lse OUT [B, Hq, S_q] fp32
  * Requires Hq % Hkv == 0, Hq/Hkv <= 64, (Dqk, Dv) in {(64,64), (128,128)} or,
  * for bf16, (576,512); strides and q/k/v addresses 16-byte aligned;
- * softmax_scale > 0; route_groups = 1 or Hkv.
+ * route_groups = 1 or Hkv.
  */
 int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype,
                                  const int64_t* strides, const int32_t* routes, const int32_t* lens,
@@ -397,8 +401,12 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
  *     the call).  For bf16 with Dqk = Dv in {64, 128} it holds, per route
  *     group and 16-key tile, the listed queries whose routes reach the tile
  *     with their 16-bit key masks (at most RG * B * S_q * min(L, ceil(S_k /
- *     16)) entries; lists that repeat a query tile can overflow it, and
- *     entries past it are dropped).
+ *     16)) entries; lists that repeat a query tile, or stale lists, can
+ *     overflow it: entries past it are dropped and counted).
+ *   dropped_hits OUT device int64 scalar, nullable: written with the number
+ *     of hit entries that did not fit the workspace (0 for consistent
+ *     routes and reverse lists; a non-zero value means dk / dv miss those
+ *     contributions).  Always written when given.
  * Requirements as for the forward, plus rev_block_k = 16.
  */
 size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk,
@@ -410,7 +418,7 @@ int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, in
                                  int rev_block_q, int rev_block_k, int rev_width, int B, int S_q,
                                  int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
                                  float softmax_scale, void* dq, void* dk, void* dv, void* workspace,
-                                 size_t ws_bytes, void* stream);
+                                 size_t ws_bytes, int64_t* dropped_hits, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,9 +1,9 @@
 """Python binding of libirb (learned-indexer routed sparse attention, MI355X).
 
-Argument marshalling only: every function below checks nothing that the C
-library does not check itself, allocates its outputs with torch on the
-tensors' device, and calls the same-named ``irb_*`` entry point on the
-current HIP stream.  All arithmetic runs in the library's HIP kernels.
+Argument marshalling only: every function below checks what the C library
+cannot see through bare pointers (dtype, contiguity, shapes), allocates its
+outputs with torch on the tensors' device, and calls the same-named
+``irb_*`` entry point on the current HIP stream.  All arithmetic runs in the library's HIP kernels.
 There is no fallback: if ``libirb.so`` is missing or no gfx950 device is
 current, calls raise ``RuntimeError``.
 
@@ -14,7 +14,6 @@ invalid argument -> ValueError, HIP failure -> RuntimeError.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -61,7 +60,7 @@ _SIGS = {
                                       _P], _I),
     "irb_sparse_gqa_attention_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_sparse_gqa_attention_bwd": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
-                                      _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
+                                      _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P, _P], _I),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -129,9 +128,33 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _req(t, name, dtype=None, contiguous=True, unit_last=False, shape=None):
+    """Raise unless ``t`` (None passes) has the dtype, contiguity, last-axis
+    stride and shape the C ABI assumes: the library receives bare pointers
+    (and at most three strides), so it cannot check these itself."""
+    if t is None:
+        return
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if unit_last and t.dim() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous (stride 1)")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+_ACT = (torch.bfloat16, torch.float32)
+I32 = torch.int32
+
+
 def make_layout(B: int, S: int, cu_seqlens: Optional[torch.Tensor] = None,
                 row_lens: Optional[torch.Tensor] = None) -> IrbLayout:
     """Layout struct; ``num_docs`` comes from the host-side shape of cu_seqlens."""
+    _req(cu_seqlens, "cu_seqlens", I32)
+    _req(row_lens, "row_lens", I32, shape=None if row_lens is None else (B,))
     nd = 0 if cu_seqlens is None else int(cu_seqlens.numel()) - 1
     return IrbLayout(B, S, None if cu_seqlens is None else cu_seqlens.data_ptr(), nd,
                      None if row_lens is None else row_lens.data_ptr())
@@ -150,6 +173,9 @@ def compress_keys(k_idx, gamma, freqs, c, eps=1e-5, cu_seqlens=None, row_lens=No
     """irb_compress_keys: returns (kc [B, S//c, D] fp32, cu_blocks or None)."""
     _gpu(k_idx, gamma, freqs, cu_seqlens, row_lens)
     lib = load_library()
+    _req(k_idx, "k_idx", _ACT, contiguous=False, unit_last=True)
+    _req(gamma, "gamma", torch.float32)
+    _req(freqs, "freqs", torch.float32)
     B, S, D = k_idx.shape
     dev = k_idx.device
     kc = torch.empty((B, S // c, D), dtype=torch.float32, device=dev)
@@ -167,8 +193,10 @@ def prepare_index_queries(q_raw, gamma, freqs=None, eps=1e-5, out=None):
     (None: no rotation).  Returns [B, S, H, D] in q_raw's dtype (``out`` may be q_raw)."""
     _gpu(q_raw, gamma, freqs, out)
     lib = load_library()
-    if not q_raw.is_contiguous() or (freqs is not None and not freqs.is_contiguous()):
-        raise ValueError("prepare_index_queries: q_raw and freqs must be contiguous")
+    _req(q_raw, "q_raw", _ACT)
+    _req(gamma, "gamma", torch.float32)
+    _req(freqs, "freqs", torch.float32)
+    _req(out, "out", q_raw.dtype, shape=q_raw.shape)
     B, S, H, D = q_raw.shape
     if out is None:
         out = torch.empty_like(q_raw)
@@ -186,11 +214,16 @@ def indexer_score_tile(q_idx, w, kc, c, q0=0, q1=None, j0=0, j1=None, score_scal
     go to irb_indexer_score_tile_groups: scores [R, B, q1-q0, j1-j0]."""
     _gpu(q_idx, w, kc, cu_blocks, cu_seqlens, row_lens, out)
     lib = load_library()
+    _req(q_idx, "q_idx", _ACT)
+    _req(w, "w", torch.float32, shape=q_idx.shape[:-1])
+    _req(kc, "kc", torch.float32)
+    _req(cu_blocks, "cu_blocks", I32)
+    _req(out, "out", torch.float32, contiguous=False, unit_last=True)
     grouped = q_idx.dim() == 5
     B, S, R, H, D = q_idx.shape if grouped else (q_idx.shape[0], q_idx.shape[1], 1, q_idx.shape[2], q_idx.shape[3])
     q1 = S if q1 is None else q1
     j1 = S // c if j1 is None else j1
-    scale = 1.0 / math.sqrt(D) if score_scale is None else score_scale
+    scale = 0.0 if score_scale is None else score_scale     # 0: the library's default 1/sqrt(D)
     if out is None:
         shape = (R, B, q1 - q0, j1 - j0) if grouped else (B, q1 - q0, j1 - j0)
         out = torch.empty(shape, dtype=torch.float32, device=q_idx.device)
@@ -211,7 +244,11 @@ def select_topk_regions(scores, c, topk, S, q0=0, cu_blocks=None, cu_seqlens=Non
     """irb_select_topk_regions over score rows q0..q0+rows: (sel [B,S,topk], cnt [B,S])."""
     _gpu(scores, cu_blocks, cu_seqlens, row_lens, sel, cnt)
     lib = load_library()
+    _req(scores, "scores", torch.float32, contiguous=False, unit_last=True)
+    _req(cu_blocks, "cu_blocks", I32)
     B, rows, _ = scores.shape
+    _req(sel, "sel", I32, shape=(B, S, topk))
+    _req(cnt, "cnt", I32, shape=(B, S))
     dev = scores.device
     if sel is None:
         sel = torch.full((B, S, topk), -1, dtype=torch.int32, device=dev)
@@ -231,12 +268,17 @@ def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_
     go to irb_route_topk_fused_groups: sel [R, B, S, topk], cnt [R, B, S]."""
     _gpu(q_idx, w, kc, cu_blocks, cu_seqlens, row_lens, workspace, sel, cnt)
     lib = load_library()
+    _req(q_idx, "q_idx", _ACT)
+    _req(w, "w", torch.float32, shape=q_idx.shape[:-1])
+    _req(kc, "kc", torch.float32)
+    _req(cu_blocks, "cu_blocks", I32)
+    _req(workspace, "workspace")
     grouped = q_idx.dim() == 5
     B, S, R, H, D = q_idx.shape if grouped else (q_idx.shape[0], q_idx.shape[1], 1, q_idx.shape[2], q_idx.shape[3])
     lead = (R,) if grouped else ()
     dev = q_idx.device
     q1 = S if q1 is None else q1
-    scale = 1.0 / math.sqrt(D) if score_scale is None else score_scale
+    scale = 0.0 if score_scale is None else score_scale     # 0: the library's default 1/sqrt(D)
     if workspace is None:
         n = (lib.irb_route_topk_fused_groups_workspace_size(B, S, c, D, topk, q0, q1, R) if grouped
              else lib.irb_route_topk_fused_workspace_size(B, S, c, D, topk, q0, q1))
@@ -245,6 +287,8 @@ def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_
         sel = torch.full(lead + (B, S, topk), -1, dtype=torch.int32, device=dev)
     if cnt is None:
         cnt = torch.zeros(lead + (B, S), dtype=torch.int32, device=dev)
+    _req(sel, "sel", I32, shape=lead + (B, S, topk))
+    _req(cnt, "cnt", I32, shape=lead + (B, S))
     lay = make_layout(B, S, cu_seqlens, row_lens)
     if grouped:
         _check(lib.irb_route_topk_fused_groups(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), R, H, D, _ptr(w),
@@ -262,13 +306,13 @@ def pack_region_bitmap(ids, regions, out=None):
     """irb_pack_region_bitmap: int32 membership words [..., ceil(regions / 32)] of int32 id rows [..., slots]."""
     _gpu(ids, out)
     lib = load_library()
-    if ids.dtype != torch.int32 or not ids.is_contiguous():
-        raise ValueError("pack_region_bitmap: ids must be contiguous int32")
+    _req(ids, "ids", I32)
     slots = ids.shape[-1]
     rows = ids.numel() // max(slots, 1)
     words = (regions + 31) // 32
     if out is None:
         out = torch.empty(ids.shape[:-1] + (words,), dtype=torch.int32, device=ids.device)
+    _req(out, "out", I32, shape=ids.shape[:-1] + (words,))
     _check(lib.irb_pack_region_bitmap(_ptr(ids), rows, slots, regions, _ptr(out), _stream(ids.device)))
     return out
 
@@ -281,6 +325,9 @@ def expand_and_compact_routes(sel, cnt, c, window, topk, L=None, cu_blocks=None,
     its contiguous block)."""
     _gpu(sel, cnt, cu_blocks, cu_seqlens, row_lens)
     lib = load_library()
+    _req(cnt, "cnt", I32)
+    _req(sel, "sel", I32, shape=tuple(cnt.shape) + (topk,))
+    _req(cu_blocks, "cu_blocks", I32)
     lead = tuple(cnt.shape[:-2])
     B, S = cnt.shape[-2:]
     dev = cnt.device
@@ -302,6 +349,8 @@ def compact_routes(ids, key_count, out=None, count_out_of_range=True):
     """irb_compact_routes over the last axis: (ids_out, lens, out_of_range counter or None)."""
     _gpu(ids, out)
     lib = load_library()
+    _req(ids, "ids", I32)
+    _req(out, "out", I32, shape=ids.shape)
     width = ids.shape[-1]
     rows = ids.numel() // width
     dev = ids.device
@@ -319,6 +368,9 @@ def build_block_lists(routes, lens, S_k, block_q, block_k, reverse, width=None, 
     indices [R, B, rows, width]."""
     _gpu(routes, lens, workspace)
     lib = load_library()
+    _req(routes, "routes", I32)
+    _req(lens, "lens", I32, shape=routes.shape[:-1])
+    _req(workspace, "workspace")
     lead = tuple(routes.shape[:-3])
     B, S_q, L = routes.shape[-3:]
     B_all = B * (lead[0] if lead else 1)
@@ -346,6 +398,10 @@ def split_full_blocks(routes, lens, S_k, block_q, block_k, reverse, counts, indi
     ``use_workspace`` is False (then every pair searches its route)."""
     _gpu(routes, lens, counts, indices)
     lib = load_library()
+    _req(routes, "routes", I32)
+    _req(lens, "lens", I32, shape=routes.shape[:-1])
+    _req(counts, "counts", I32)
+    _req(indices, "indices", I32)
     lead = tuple(routes.shape[:-3])
     B, S_q, L = routes.shape[-3:]
     B_all = B * (lead[0] if lead else 1)
@@ -367,6 +423,21 @@ def _strides9(q, k, v):
                                 v.stride(0), v.stride(1), v.stride(2))
 
 
+def _check_qkv(q, k, v, routes, lens):
+    """q / k / v: one activation dtype, 4-D, last dimension contiguous (other
+    strides are passed); routes / lens: contiguous int32 of matching shapes."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _req(t, n, q.dtype if n != "q" else _ACT, contiguous=False, unit_last=True)
+        if t.dim() != 4:
+            raise ValueError(f"{n}: expected [B, S, H, D], got shape {tuple(t.shape)}")
+    if k.shape[:3] != v.shape[:3] or k.shape[0] != q.shape[0]:
+        raise ValueError("k and v must share [B, S_k, Hkv], and B must match q")
+    _req(routes, "routes", I32)
+    _req(lens, "lens", I32, shape=routes.shape[:-1])
+    if routes.shape[-2] != q.shape[1] or routes.shape[-3] != q.shape[0]:
+        raise ValueError(f"routes {tuple(routes.shape)} do not match q's [B, S_q] {tuple(q.shape[:2])}")
+
+
 def _route_groups(routes, lens):
     """Route groups of a routes tensor: [B, S, L] -> 1, [RG, B, S, L] (per KV group) -> RG."""
     if routes.dim() == 4:
@@ -383,14 +454,17 @@ def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None
     (lens [Hkv, B, S_q]) give every KV group its own routes."""
     _gpu(q, k, v, routes, lens, out, lse)
     lib = load_library()
+    _check_qkv(q, k, v, routes, lens)
     B, S_q, Hq, Dqk = q.shape
     S_k, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
     dev = q.device
-    scale = 1.0 / math.sqrt(Dqk) if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale     # 0: the library's default 1/sqrt(Dqk)
     if out is None:
         out = torch.empty((B, S_q, Hq, Dv), dtype=q.dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev)
+    _req(out, "out", q.dtype, shape=(B, S_q, Hq, Dv))
+    _req(lse, "lse", torch.float32, shape=(B, Hq, S_q))
     _check(lib.irb_sparse_gqa_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v),
                                             _ptr(routes), _ptr(lens), _route_groups(routes, lens), B, S_q, S_k,
                                             routes.shape[-1], Hq, Hkv, Dqk, Dv, scale, _ptr(out), _ptr(lse),
@@ -399,17 +473,28 @@ def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None
 
 
 def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, rev_indices, rev_block_q,
-                             rev_block_k=16, softmax_scale=None, merged_kv=False, workspace=None):
+                             rev_block_k=16, softmax_scale=None, merged_kv=False, workspace=None, dropped_hits=None):
     """irb_sparse_gqa_attention_bwd: (dq, dk, dv); with merged_kv (v aliases k) dk holds dK + [dV, 0], dv is dk.
+
+    ``dropped_hits`` (int64 [1] on the device, optional) receives the number of
+    key-side hit entries that did not fit the workspace (0 for reverse lists
+    built from the same routes).
 
     Grouped routes [Hkv, B, S_q, L] take the reverse lists of the routes
     viewed as Hkv * B rows."""
-    _gpu(q, k, v, out, dout, lse, routes, lens, rev_counts, rev_indices, workspace)
+    _gpu(q, k, v, out, dout, lse, routes, lens, rev_counts, rev_indices, workspace, dropped_hits)
     lib = load_library()
+    _check_qkv(q, k, v, routes, lens)
     B, S_q, Hq, Dqk = q.shape
     S_k, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
     dev = q.device
-    scale = 1.0 / math.sqrt(Dqk) if softmax_scale is None else softmax_scale
+    _req(dout, "dout", q.dtype, shape=(B, S_q, Hq, Dv))
+    _req(lse, "lse", torch.float32, shape=(B, Hq, S_q))
+    _req(rev_counts, "rev_counts", I32)
+    _req(rev_indices, "rev_indices", I32)
+    _req(workspace, "workspace")
+    _req(dropped_hits, "dropped_hits", torch.int64, shape=(1,))
+    scale = 0.0 if softmax_scale is None else softmax_scale     # 0: the library's default 1/sqrt(Dqk)
     dq = torch.empty((B, S_q, Hq, Dqk), dtype=q.dtype, device=dev)
     dk = torch.empty((B, S_k, Hkv, Dqk), dtype=q.dtype, device=dev)
     dv = dk if merged_kv else torch.empty((B, S_k, Hkv, Dv), dtype=q.dtype, device=dev)
@@ -428,7 +513,7 @@ def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, 
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v), _ptr(out), _ptr(dout), _ptr(lse),
         _ptr(routes), _ptr(lens), rg, _ptr(rev_counts), _ptr(rev_indices), rev_block_q, rev_block_k,
         rev_indices.shape[-1], B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv, scale, _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(dropped_hits), _stream(dev)))
     return dq, dk, dv
 
 

@@ -1,6 +1,7 @@
 // C ABI of libirb: argument validation, error reporting and dispatch.
 // Every entry point validates on the host, enqueues on the caller's stream and
 // returns without synchronising.  See include/irb.h for the contract.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -133,7 +134,9 @@ static int score_tile_impl(const char* fn, const irb_layout* layout, const void*
   if (!score_heads_ok(H_idx)) return fail(IRB_ERR_INVALID, "%s: H_idx must be 4, 8, 16 or a multiple of 16 up to 64 (got %d)", fn, H_idx);
   if (D_idx != 32 && D_idx != 64 && D_idx != 128) return fail(IRB_ERR_INVALID, "%s: D_idx must be 32, 64 or 128 (got %d)", fn, D_idx);
   if (c < 1) return fail(IRB_ERR_INVALID, "%s: c must be >= 1", fn);
-  if (!(score_scale > 0.f)) return fail(IRB_ERR_INVALID, "%s: score_scale must be > 0", fn);
+  if (score_scale == 0.f) score_scale = 1.f / std::sqrt(static_cast<float>(D_idx));
+  if (!(score_scale > 0.f) || !std::isfinite(score_scale))
+    return fail(IRB_ERR_INVALID, "%s: score_scale must be finite and > 0 (0 = 1/sqrt(D_idx))", fn);
   if (q0 < 0 || q1 <= q0 || q1 > L.S) return fail(IRB_ERR_INVALID, "%s: need 0 <= q0 < q1 <= S", fn);
   if (j0 < 0 || j1 <= j0 || j1 > L.S / c) return fail(IRB_ERR_INVALID, "%s: need 0 <= j0 < j1 <= S/c", fn);
   if (out_row_stride < j1 - j0) return fail(IRB_ERR_INVALID, "%s: out_row_stride < j1 - j0", fn);
@@ -225,7 +228,9 @@ static int route_fused_impl(const char* fn, const irb_layout* layout, const void
   if (!score_heads_ok(H_idx)) return fail(IRB_ERR_INVALID, "%s: unsupported H_idx %d", fn, H_idx);
   if (D_idx != 32 && D_idx != 64 && D_idx != 128) return fail(IRB_ERR_INVALID, "%s: D_idx must be 32, 64 or 128", fn);
   if (c < 1 || topk < 1 || topk > 4096) return fail(IRB_ERR_INVALID, "%s: bad c or topk", fn);
-  if (!(score_scale > 0.f)) return fail(IRB_ERR_INVALID, "%s: score_scale must be > 0", fn);
+  if (score_scale == 0.f) score_scale = 1.f / std::sqrt(static_cast<float>(D_idx));
+  if (!(score_scale > 0.f) || !std::isfinite(score_scale))
+    return fail(IRB_ERR_INVALID, "%s: score_scale must be finite and > 0 (0 = 1/sqrt(D_idx))", fn);
   if (q0 < 0 || q1 <= q0 || q1 > L.S) return fail(IRB_ERR_INVALID, "%s: need 0 <= q0 < q1 <= S", fn);
   if (!q_idx || !w || !kc || !sel || !cnt || !workspace) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
   if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
@@ -391,7 +396,10 @@ static int check_attn(const char* fn, const void* q, const void* k, const void* 
   const bool dims_ok = dtype == IRB_BF16 ? ((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128) || (Dqk == 576 && Dv == 512))
                                          : ((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128));
   if (!dims_ok) return fail(IRB_ERR_INVALID, "%s: unsupported head dims (%d, %d)", fn, Dqk, Dv);
-  if (!(scale > 0.f)) return fail(IRB_ERR_INVALID, "%s: softmax_scale must be > 0", fn);
+  // 0 selects the method's default 1/sqrt(Dqk) ([QSA] gathered_qsa_gqa_attention)
+  if (scale == 0.f) scale = 1.f / std::sqrt(static_cast<float>(Dqk));
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(IRB_ERR_INVALID, "%s: softmax_scale must be finite and > 0 (0 = 1/sqrt(Dqk))", fn);
   if (!q || !k || !v || !strides || !routes || !lens) return fail(IRB_ERR_INVALID, "%s: NULL argument", fn);
   for (int i = 0; i < 9; ++i)
     if (strides[i] < 0) return fail(IRB_ERR_INVALID, "%s: negative stride", fn);
@@ -440,7 +448,7 @@ int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, in
                                  const int32_t* rev_indices,
                                  int rev_block_q, int rev_block_k, int rev_width, int B, int S_q, int S_k, int L_width,
                                  int Hq, int Hkv, int Dqk, int Dv, float softmax_scale, void* dq, void* dk, void* dv,
-                                 void* workspace, size_t ws_bytes, void* stream) {
+                                 void* workspace, size_t ws_bytes, int64_t* dropped_hits, void* stream) {
   const char* fn = "irb_sparse_gqa_attention_bwd";
   irb::AttnBwdArgs a;
   if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, route_groups, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv,
@@ -457,7 +465,7 @@ int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, in
   a.out = out; a.dout = dout; a.lse = lse;
   a.rev_counts = rev_counts; a.rev_indices = rev_indices;
   a.rev_bq = rev_block_q; a.rev_bk = rev_block_k; a.rev_width = rev_width;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.ws = workspace; a.ws_bytes = ws_bytes;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.ws = workspace; a.ws_bytes = ws_bytes; a.dropped = dropped_hits;
   IRB_REQUIRE_DEVICE();
   return launched(fn, irb::launch_attn_bwd(a, static_cast<hipStream_t>(stream)));
 }

@@ -831,9 +831,11 @@ bwd_hits_kernel(AttnBwdArgs args, int nkt, int pass, int64_t* __restrict__ hit_o
   if (!pass && threadIdx.x == 0) hit_off[lrow] = done;
 }
 
-// in-place exclusive prefix sum of v[0, n); v[n] receives the total
+// in-place exclusive prefix sum of v[0, n); v[n] receives the total and
+// *dropped (when given) the hits beyond the capacity, which the filling pass
+// cannot store
 __global__ void __launch_bounds__(256)
-bwd_scan_kernel(int64_t* __restrict__ v, int64_t n) {
+bwd_scan_kernel(int64_t* __restrict__ v, int64_t n, int64_t cap, int64_t* __restrict__ dropped) {
   __shared__ int64_t part[256];
   const int tid = threadIdx.x;
   const int64_t per = (n + 255) / 256;
@@ -850,6 +852,7 @@ bwd_scan_kernel(int64_t* __restrict__ v, int64_t n) {
       run += x;
     }
     v[n] = run;
+    if (dropped) *dropped = run > cap ? run - cap : 0;
   }
   __syncthreads();
   int64_t run = part[tid];
@@ -1320,7 +1323,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     const int64_t ltiles = static_cast<int64_t>(a.RG) * a.B * nkt;
     hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 0,
                        ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
-    hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(256), 0, stream, ws.hit_off, ltiles);
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(256), 0, stream, ws.hit_off, ltiles, ws.cap, args.dropped);
     hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 1,
                        ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
     if constexpr (kGqaHits) {
@@ -1332,6 +1335,9 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
                          args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, nkt, merged);
     }
   } else {
+    // no hit lists on this path: nothing can be dropped
+    if (args.dropped)
+      if (int rc = launch_fill_i32(reinterpret_cast<int32_t*>(args.dropped), 2, 0, stream)) return rc;
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0, stream,
                        args, ws.delta, static_cast<const T*>(ws.qt), static_cast<const T*>(ws.dot), G, Gp, nkt,
                        static_cast<int>(kitems), merged);

@@ -931,6 +931,8 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
         }
       }
     }
+    // every wave's mask words are complete before wave 0 reads them all
+    __syncthreads();
     // compact list of the key tiles any query routes to
     if (wid == 0) {
       int base = 0;

@@ -105,6 +105,7 @@ struct AttnBwdArgs {
   int rev_bq, rev_bk, rev_width;
   void* dq; void* dk; void* dv;
   void* ws; size_t ws_bytes;
+  int64_t* dropped;   // device, nullable: receives the hits past the workspace's capacity
 };
 
 size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype,

@@ -55,7 +55,7 @@ expand_kernel(Layout L, const int32_t* __restrict__ sel, const int32_t* __restri
   const int tail0 = d.start + nb * c;                       // first token of the incomplete group
   const int a = window > 0 ? min(tail0, max(d.start, t - window + 1)) : tail0;
   const int base = block_base(L, cu_blocks, d);
-  const int k = topk > 0 ? cnt[row] : 0;
+  const int k = topk > 0 ? min(max(cnt[row], 0), topk) : 0;   // a caller-supplied count past topk is clamped
   // first token of each selected block, staged in this wave's LDS slice
   int32_t* sb = sblk_all + wid * topk;
   const int32_t* srow = sel + row * topk;

@@ -78,7 +78,9 @@ def test_score_and_select_validation():
         ctypes.byref(lay), FAKE, 1, H, D, FAKE, FAKE, None, 4, sc, q0, q1, j0, j1, FAKE, st, None)
     assert _err(args(H=12))[0] == 3
     assert _err(args(D=96))[0] == 3
-    assert _err(args(sc=0.0))[0] == 3
+    assert _err(args(sc=-0.5))[0] == 3
+    assert _err(args(sc=float("nan")))[0] == 3
+    assert _err(args(sc=0.0))[0] == 1      # 0 = default 1/sqrt(D_idx): valid; no GPU here
     assert _err(args(q0=10, q1=10))[0] == 3
     assert _err(args(j1=17))[0] == 3
     assert _err(args(st=8))[0] == 3
@@ -144,6 +146,10 @@ def test_attention_validation():
     assert _err(call(D=96, Dv=96))[0] == 3
     assert _err(call(D=576, Dv=512, dt=0))[0] == 3      # latent dims are bf16 only
     assert _err(call(sc=-1.0))[0] == 3
+    assert _err(call(sc=float("nan")))[0] == 3
+    assert _err(call(sc=float("inf")))[0] == 3
+    # 0 selects the default 1/sqrt(Dqk): validation passes, and with no GPU here the call stops at the device check
+    assert _err(call(sc=0.0))[0] == 1
     assert _err(call(dt=5))[0] == 2
     odd = (ctypes.c_int64 * 9)(*list(st)[:8], 129)
     assert _err(call(strides=odd))[0] == 3
@@ -154,7 +160,7 @@ def test_attention_validation():
     # backward: key tile must be 16, merged dk/dv needs Dv <= Dqk
     bwd = lambda bk=16, width=64, ws=1 << 30, rg=1: lib.irb_sparse_gqa_attention_bwd(
         FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, FAKE, FAKE, FAKE, rg, FAKE, FAKE, 1, bk, width, 1, 64, 64, 16, 4, 1, 128,
-        128, 0.1, FAKE, FAKE, FAKE, FAKE, ws, None)
+        128, 0.1, FAKE, FAKE, FAKE, FAKE, ws, None, None)
     assert _err(bwd(bk=32))[0] == 3
     assert _err(bwd(width=63))[0] == 3
     assert _err(bwd(rg=2))[0] == 3
@@ -223,3 +229,32 @@ def test_pack_region_bitmap_validation():
     s, m = call(rows=-1)
     assert s == 3
     assert call(rows=0, ids=None, out=None)[0] == 0      # nothing to do: no device call
+
+
+def test_binding_rejects_layouts_the_abi_cannot_see():
+    """dtype, contiguity, unit last stride and shapes are checked in the binding
+    (the C ABI receives bare pointers); CPU tensors exercise the checks alone."""
+    import torch
+    q = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    r = torch.zeros(1, 8, 16, dtype=torch.int32)
+    n = torch.zeros(1, 8, dtype=torch.int32)
+    irb._check_qkv(q, k, k, r, n)                                     # well formed
+    with pytest.raises(TypeError, match="routes"):
+        irb._check_qkv(q, k, k, r.long(), n)                          # int64 ids (torch.topk's default)
+    with pytest.raises(ValueError, match="routes"):
+        irb._check_qkv(q, k, k, r[..., ::2], n)                       # strided ids
+    with pytest.raises(ValueError, match="lens"):
+        irb._check_qkv(q, k, k, r, n[:, :4])
+    with pytest.raises(ValueError, match="last dimension"):
+        irb._check_qkv(q, k[..., ::2], k[..., ::2], r, n)
+    with pytest.raises(TypeError, match="k"):
+        irb._check_qkv(q, k.float(), k, r, n)
+    with pytest.raises(ValueError, match="do not match"):
+        irb._check_qkv(q, k, k, r[:, :4], n[:, :4])
+    # an expanded gradient (stride 0, e.g. the gradient of o.sum()) is not contiguous
+    dout = torch.zeros(1, dtype=torch.bfloat16).expand(1, 8, 4, 64)
+    with pytest.raises(ValueError, match="contiguous"):
+        irb._req(dout, "dout", torch.bfloat16, shape=(1, 8, 4, 64))
+    with pytest.raises(ValueError, match="shape"):
+        irb._req(torch.zeros(1, 4, 8), "lse", torch.float32, shape=(1, 4, 9))

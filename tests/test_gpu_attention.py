@@ -65,7 +65,10 @@ def _run_fwd_bwd(wl, x, routes, lens, scale, do_bwd, q_view=None, rev_bq=1):
     S = x["q"].shape[1]
     rc, ri = irb.build_block_lists(r_d, l_d, S, rev_bq, 16, reverse=True)
     dO = to_dev(x["dO"], dt)
-    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, rev_bq, 16, scale)
+    dropped = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, rev_bq, 16, scale,
+                                              dropped_hits=dropped)
+    assert int(dropped.item()) == 0, "reverse lists of the same routes dropped key-side hits"
     rdq, rdk, rdv = oracle.attention_bwd(x["q"], x["k"], x["v"], routes, x["dO"], scale)
     attn_tol_check(host(dq), rdq, dt, "dq")
     attn_tol_check(host(dk), rdk, dt, "dk")
@@ -162,3 +165,29 @@ def test_backward_with_coarse_reverse_tiles():
     b = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, *irb.build_block_lists(r_d, l_d, 400, 16, 16, True), 16)
     for u, w_ in zip(a, b):
         assert torch.equal(u, w_)
+
+
+def test_backward_counts_hits_past_the_workspace():
+    """Reverse lists that do not belong to the routes (every key tile listing
+    every query) give more key-side hit entries than the workspace holds: the
+    extra ones are dropped and counted, and dq (query side) is unaffected."""
+    banner("attn bwd stale reverse lists: dropped-hit counter")
+    S, width = 256, 8
+    wl, x = _qkv("varlen", S)
+    routes, lens = _random_routes(5, 1, S, width)
+    dt = torch.bfloat16
+    q, k, v = (to_dev(x[n], dt) for n in ("q", "k", "v"))
+    r_d, l_d = to_dev(routes), to_dev(lens)
+    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d)
+    dO = to_dev(x["dO"], dt)
+    nkt = S // 16
+    rc = torch.full((1, nkt), S, dtype=torch.int32, device=DEV)
+    ri = torch.arange(S, dtype=torch.int32, device=DEV).repeat(1, nkt, 1).contiguous()
+    dropped = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, 1, dropped_hits=dropped)
+    # capacity: S query rows x min(L, key tiles) entries; the lists hold S x key tiles
+    want = S * nkt - S * min(width, nkt)
+    assert int(dropped.item()) == want
+    good_rc, good_ri = irb.build_block_lists(r_d, l_d, S, 1, 16, reverse=True)
+    dq2, _, _ = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, good_rc, good_ri, 1)
+    assert torch.equal(dq, dq2)

@@ -31,7 +31,7 @@ import torch
 import indexer_routed_block_amd as irb
 import oracle
 import synth
-from gpu_util import DEV, act_dtype, attn_tol_check, banner, host, score_bound, to_dev
+from gpu_util import DEV, act_dtype, attn_tol_check, banner, check_selection, host, score_bound, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -172,15 +172,14 @@ def test_route_pipeline_full_size(name):
     kc_d = to_dev(kc_ref.astype(np.float32))
     cub_d = to_dev(cub_ref)
     got_sel, got_routes, got_lens = host(r["sel"]), host(r["routes"]), host(r["lens"])
+    got = {"sel": got_sel[None], "cnt": host(r["cnt"])[None], "routes": got_routes[None], "lens": got_lens[None]}
     if name == "s8192":
+        # every row: bit-exact outside near ties, near-tie rows a valid top-k expanded exactly
         ref = _oracle_pipeline(name)
-        ties = oracle.near_tie_rows(ref["scores"], wl.c, wl.topk)
-        same = np.all(got_sel == ref["sel"], axis=-1)
-        bad = ~same & ~ties
-        print(f"    all rows: near-tie {int(ties.sum())}, differing {int((~same).sum())} of {ties.size}")
-        assert not bad.any(), f"{int(bad.sum())} non-tie rows differ, e.g. {np.argwhere(bad)[:3].tolist()}"
-        np.testing.assert_array_equal(got_routes[~ties], ref["routes"][~ties])
-        np.testing.assert_array_equal(got_lens[~ties], ref["lens"][~ties])
+        want = {k: ref[k][None] for k in ("sel", "cnt", "routes", "lens")}
+        want["ties"] = oracle.near_tie_rows(ref["scores"], wl.c, wl.topk)[None]
+        n_ties, n_diff = check_selection(wl, x, wl.topk, got, want, kc_ref, grouped=False)
+        print(f"    all {wl.S} rows: near-tie {n_ties}, differing {n_diff}")
     sel_ref = np.full((1, wl.S, wl.topk), -1, dtype=np.int32)
     cnt_ref = np.zeros((1, wl.S), dtype=np.int32)
     rows, n_ties = [], 0
@@ -203,11 +202,14 @@ def test_route_pipeline_full_size(name):
     rows = sorted(set(rows))
     routes_ref, lens_ref = oracle.expand_routes(sel_ref, cnt_ref, wl.c, wl.window, wl.topk, cu_seqlens=cu,
                                                 rows=[(0, t) for t in rows])
-    keep = [t for t in rows if t not in tie_rows]
     print(f"    sampled rows {len(rows)}, near-tie {len(tie_rows)}")
-    np.testing.assert_array_equal(got_sel[0, keep], sel_ref[0, keep])
-    np.testing.assert_array_equal(got_routes[0, keep], routes_ref[0, keep])
-    np.testing.assert_array_equal(got_lens[0, keep], lens_ref[0, keep])
+    # the sampled rows take the every-row check; the others carry the GPU's own values (compared to themselves)
+    want = {k: v.copy() for k, v in got.items()}
+    for key, arr in (("sel", sel_ref), ("cnt", cnt_ref), ("routes", routes_ref), ("lens", lens_ref)):
+        want[key][0, 0, rows] = arr[0, rows]
+    want["ties"] = np.zeros((1, 1, wl.S), dtype=bool)
+    want["ties"][0, 0, sorted(tie_rows)] = True
+    check_selection(wl, x, wl.topk, got, want, kc_ref, grouped=False)
     _log("sampled rows", t0)
 
 
@@ -245,8 +247,10 @@ def test_attention_fwd_full_size(name):
     q, k, v, r_d, l_d, o, lse = _fwd(name, x, routes, lens)
     torch.cuda.synchronize()
     _log("gpu fwd", t0)
-    _check_fwd_rows(name, x, routes, lens, o, lse, _sample_rows(name))
-    _log("sampled rows", t0)
+    # S=8192: every query row against the oracle; the longer workloads: sampled rows
+    rows = list(range(wl.S)) if name == "s8192" else _sample_rows(name)
+    _check_fwd_rows(name, x, routes, lens, o, lse, rows)
+    _log(f"{len(rows)} rows", t0)
 
 
 def _key_tiles(name):

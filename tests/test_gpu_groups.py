@@ -19,7 +19,7 @@ import torch
 import indexer_routed_block_amd as irb
 import oracle
 import synth
-from gpu_util import act_dtype, attn_tol_check, banner, host, score_bound, to_dev
+from gpu_util import act_dtype, attn_tol_check, banner, check_selection, host, score_bound, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -88,53 +88,12 @@ def _oracle_grouped_routes(wl, x, topk):
     return out
 
 
-# FP32 scoring error bound, relative to the magnitude M = scale sum_h |w| sum_d |q k|:
-# keys carried as bf16 high + low parts (2^-16 of each key), FP32 accumulation
-# over D = 128 products (128 * 2^-24) and over the heads: < 3e-5 M.
-SCORE_ERR = 3e-5
-
-
 def _check_grouped_selection(wl, x, topk, r, ref):
-    """Rows equal to the oracle's selection are compared bit for bit (selection,
-    routes, lengths).  A row that differs must still be a correct top-k under
-    FP32 rounding: some perturbation of each score by at most SCORE_ERR * M makes
-    the GPU's set the top k (with a few signed-weight heads per group, boundary
-    scores often cancel to ~1e-3 of their magnitude, far below the scores'
-    own relative precision), and its routes must be the oracle's expansion of
-    the GPU's selection."""
-    got_sel, got_cnt, got_routes, got_lens = host(r["sel"]), host(r["cnt"]), host(r["routes"]), host(r["lens"])
-    assert got_sel.shape == ref["sel"].shape and got_routes.shape == ref["routes"].shape
-    np.testing.assert_array_equal(got_cnt, ref["cnt"])
-    same = np.all(got_sel == ref["sel"], axis=-1)
-    np.testing.assert_array_equal(got_routes[same], ref["routes"][same])
-    np.testing.assert_array_equal(got_lens[same], ref["lens"][same])
-    diff = np.argwhere(~same)
-    print(f"rows differing from the oracle: {len(diff)} of {same.size} (near-tie rows {int(ref['ties'].sum())})")
-    scale = 1.0 / math.sqrt(wl.D_idx)
-    cu, rl = x["cu_seqlens"], x["row_lens"]
-    S = got_sel.shape[2]
-    docs = oracle.documents(got_sel.shape[1], S, cu, rl)
-    valid, start, base, nb = oracle.token_info(docs, S, wl.c)
-    for g, b, t in diff:
-        s = oracle.indexer_scores_grouped(x["qI"], x["w"], ref["kc"], wl.c, scale, cu, rl, q0=t, q1=t + 1)[g, b, 0]
-        M = score_bound(x["qI"][b:b + 1, t:t + 1, g], x["w"][b:b + 1, t:t + 1, g], ref["kc"][b:b + 1], scale)[0, 0]
-        lo, n = int(base[b, t]), int(nb[b, t])
-        k = int(got_cnt[g, b, t])
-        chosen = got_sel[g, b, t, :k] - lo
-        assert k == min(topk, n) and len(set(chosen.tolist())) == k and np.all((chosen >= 0) & (chosen < n))
-        inside = np.zeros(n, dtype=bool)
-        inside[chosen] = True
-        vs, vm = s[lo:lo + n], M[lo:lo + n]
-        if k < n:
-            low = np.min(vs[inside] + SCORE_ERR * vm[inside])
-            high = np.max(vs[~inside] - SCORE_ERR * vm[~inside])
-            assert low >= high, f"group {g} row {t}: not a top-{k} within the FP32 bound ({low:.3e} < {high:.3e})"
-        sel1 = got_sel[g, b:b + 1].copy()
-        cnt1 = got_cnt[g, b:b + 1].copy()
-        rr, ll = oracle.expand_routes(sel1, cnt1, wl.c, wl.window, topk, cu,
-                                      None if rl is None else rl[b:b + 1], rows=[(0, int(t))])
-        np.testing.assert_array_equal(got_routes[g, b, t], rr[0, t])
-        assert got_lens[g, b, t] == ll[0, t]
+    """Every row of every group: bit-exact where the selection equals the
+    oracle's, else a correct top-k under the FP32 scoring bound whose routes
+    expand the GPU's own selection (gpu_util.check_selection)."""
+    got = {k: host(r[k]) for k in ("sel", "cnt", "routes", "lens")}
+    check_selection(wl, x, topk, got, ref, ref["kc"], grouped=True)
 
 
 @pytest.mark.parametrize("wl_name,S,layout,R", [("s8192", 2048, "single", 4), ("varlen", 4096, "packed", 4),
