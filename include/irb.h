@@ -201,6 +201,28 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
                          int32_t* cnt, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * irb_route_topk_fused without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs and results as
+ * irb_route_topk_fused, minus the workspace: the split keys and score rows
+ * live in a static device array of IRB_NOALLOC_SCRATCH_BYTES that each GPU
+ * the library runs on holds until the process ends.  The call allocates
+ * nothing; it needs B * (S/c) * D_idx * 4 bytes (rounded up to 256) of split
+ * keys plus at least one B * (S/c) * 4-byte score row within that maximum,
+ * and returns IRB_ERR_INVALID otherwise (e.g. B * (S/c) = 16384 blocks of
+ * 128 dims use 8 MiB, leaving 56 MiB of score rows; score chunks hold as many
+ * query rows as fit).  The scratch needs no clearing between calls.  All
+ * calls on one GPU share that GPU's array: calls that overlap in time on one
+ * GPU (different streams or host threads without ordering) race and give
+ * wrong selections; calls ordered on one stream are safe.
+ */
+#define IRB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int irb_route_topk_fused_noalloc(const irb_layout* layout, const void* q_idx, int dtype, int H_idx,
+                                 int D_idx, const float* w, const float* kc, const int32_t* cu_blocks,
+                                 int c, float score_scale, int topk, int q0, int q1, int32_t* sel,
+                                 int32_t* cnt, void* stream);
+
+/*
  * a2 / a2+a3 with one score row and one selection per KV group -- [CSA]
  * indexer_score_tile: index queries [batch, queries, groups, heads, dim] and
  * signed weights [batch, queries, groups, heads] score the shared region

@@ -45,6 +45,7 @@ _SIGS = {
     "irb_select_topk_regions": ([_P, _P, _I64, _I, _I, _P, _I, _I, _P, _P, _P], _I),
     "irb_route_topk_fused_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_route_topk_fused": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "irb_route_topk_fused_noalloc": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P], _I),
     "irb_indexer_score_tile_groups": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _I, _P, _I64, _P], _I),
     "irb_route_topk_fused_groups_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_route_topk_fused_groups": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P],
@@ -299,6 +300,34 @@ def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_
     _check(lib.irb_route_topk_fused(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), H, D, _ptr(w), _ptr(kc),
                                     _ptr(cu_blocks), c, scale, topk, q0, q1, _ptr(sel), _ptr(cnt), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(dev)))
+    return sel, cnt
+
+
+def route_topk_fused_noalloc(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_blocks=None,
+                             cu_seqlens=None, row_lens=None, sel=None, cnt=None):
+    """irb_route_topk_fused_noalloc: route_topk_fused's selection with the library's
+    static per-device scratch instead of a workspace (the call allocates no device
+    memory; pass ``sel`` / ``cnt`` to allocate nothing here either)."""
+    _gpu(q_idx, w, kc, cu_blocks, cu_seqlens, row_lens, sel, cnt)
+    lib = load_library()
+    _req(q_idx, "q_idx", _ACT)
+    _req(w, "w", torch.float32, shape=q_idx.shape[:-1])
+    _req(kc, "kc", torch.float32)
+    _req(cu_blocks, "cu_blocks", I32)
+    B, S, H, D = q_idx.shape
+    dev = q_idx.device
+    q1 = S if q1 is None else q1
+    scale = 0.0 if score_scale is None else score_scale
+    if sel is None:
+        sel = torch.full((B, S, topk), -1, dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.zeros((B, S), dtype=torch.int32, device=dev)
+    _req(sel, "sel", I32, shape=(B, S, topk))
+    _req(cnt, "cnt", I32, shape=(B, S))
+    lay = make_layout(B, S, cu_seqlens, row_lens)
+    _check(lib.irb_route_topk_fused_noalloc(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), H, D, _ptr(w), _ptr(kc),
+                                            _ptr(cu_blocks), c, scale, topk, q0, q1, _ptr(sel), _ptr(cnt),
+                                            _stream(dev)))
     return sel, cnt
 
 

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "irb_internal.hpp"
@@ -72,6 +73,36 @@ int check_dtype(const char* fn, int dtype) {
 }
 
 bool score_heads_ok(int H) { return H >= 4 && H <= 64 && H % 4 == 0 && (16 % H == 0 || H % 16 == 0); }
+
+// Scratch of irb_route_topk_fused_noalloc: one copy per GPU the library runs
+// on, held until the process ends.  Host code never passes `scratch` itself
+// (in host code the name is a stand-in, not a device address): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept in g_scratch_dev.
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[IRB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// device address of this device's scratch (looked up on the first call on the device)
+int scratch_ptr(const char* fn, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(IRB_ERR_HIP, "%s: no current device", fn);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(IRB_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return 0;
+}
 
 }  // namespace
 
@@ -221,7 +252,7 @@ size_t irb_route_topk_fused_groups_workspace_size(int B, int S, int c, int D_idx
 static int route_fused_impl(const char* fn, const irb_layout* layout, const void* q_idx, int dtype, int groups,
                             int H_idx, int D_idx, const float* w, const float* kc, const int32_t* cu_blocks, int c,
                             float score_scale, int topk, int q0, int q1, int32_t* sel, int32_t* cnt, void* workspace,
-                            size_t ws_bytes, void* stream) {
+                            size_t ws_bytes, void* stream, bool static_scratch = false) {
   irb::Layout L;
   if (int r = check_layout(fn, layout, L)) return r;
   if (int r = check_dtype(fn, dtype)) return r;
@@ -232,7 +263,8 @@ static int route_fused_impl(const char* fn, const irb_layout* layout, const void
   if (!(score_scale > 0.f) || !std::isfinite(score_scale))
     return fail(IRB_ERR_INVALID, "%s: score_scale must be finite and > 0 (0 = 1/sqrt(D_idx))", fn);
   if (q0 < 0 || q1 <= q0 || q1 > L.S) return fail(IRB_ERR_INVALID, "%s: need 0 <= q0 < q1 <= S", fn);
-  if (!q_idx || !w || !kc || !sel || !cnt || !workspace) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (!q_idx || !w || !kc || !sel || !cnt || (!workspace && !static_scratch))
+    return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
   if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
   const int nb = L.S / c;
   if (nb < 1) return fail(IRB_ERR_INVALID, "%s: S/c must be >= 1", fn);
@@ -241,9 +273,19 @@ static int route_fused_impl(const char* fn, const irb_layout* layout, const void
   const bool one_launch = groups > 1 && irb::score_grouped_ok(dtype, groups, H_idx, D_idx);
   const int64_t per_row = static_cast<int64_t>(L.B) * nb * 4 * (one_launch ? groups : 1);
   const size_t kbytes = split_keys_bytes(L.B, nb, D_idx);
+  if (static_scratch) {
+    ws_bytes = IRB_NOALLOC_SCRATCH_BYTES;
+    if (kbytes + static_cast<size_t>(per_row) > ws_bytes)
+      return fail(IRB_ERR_INVALID,
+                  "%s: B * (S/c) = %lld blocks of %d dims need %zu bytes of scratch (split keys and one score row); "
+                  "the static maximum is %zu bytes",
+                  fn, static_cast<long long>(L.B) * nb, D_idx, kbytes + static_cast<size_t>(per_row), ws_bytes);
+  }
   const int64_t rows = ws_bytes > kbytes ? static_cast<int64_t>(ws_bytes - kbytes) / per_row : 0;
   if (rows < 1) return fail(IRB_ERR_INVALID, "%s: workspace too small (%zu bytes)", fn, ws_bytes);
   IRB_REQUIRE_DEVICE();
+  if (static_scratch)
+    if (int r = scratch_ptr(fn, &workspace)) return r;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t* kcs = static_cast<uint16_t*>(workspace);
   float* scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + kbytes);
@@ -284,6 +326,13 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
                          int32_t* sel, int32_t* cnt, void* workspace, size_t ws_bytes, void* stream) {
   return route_fused_impl("irb_route_topk_fused", layout, q_idx, dtype, 1, H_idx, D_idx, w, kc, cu_blocks, c,
                           score_scale, topk, q0, q1, sel, cnt, workspace, ws_bytes, stream);
+}
+
+int irb_route_topk_fused_noalloc(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx,
+                                 const float* w, const float* kc, const int32_t* cu_blocks, int c, float score_scale,
+                                 int topk, int q0, int q1, int32_t* sel, int32_t* cnt, void* stream) {
+  return route_fused_impl("irb_route_topk_fused_noalloc", layout, q_idx, dtype, 1, H_idx, D_idx, w, kc, cu_blocks, c,
+                          score_scale, topk, q0, q1, sel, cnt, nullptr, 0, stream, true);
 }
 
 int irb_route_topk_fused_groups(const irb_layout* layout, const void* q_idx, int dtype, int groups, int H_idx,

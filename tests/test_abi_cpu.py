@@ -258,3 +258,19 @@ def test_binding_rejects_layouts_the_abi_cannot_see():
         irb._req(dout, "dout", torch.bfloat16, shape=(1, 8, 4, 64))
     with pytest.raises(ValueError, match="shape"):
         irb._req(torch.zeros(1, 4, 8), "lse", torch.float32, shape=(1, 4, 9))
+
+
+def test_noalloc_route_rejects_inputs_beyond_its_scratch():
+    """The allocation-free fused route checks its static scratch bound on the host
+    (no device needed): 2^20 blocks of 128 dims need 512 MiB of split keys."""
+    lib = irb.load_library()
+    big = _layout(S=1 << 22)
+    code, msg = _err(lib.irb_route_topk_fused_noalloc(ctypes.byref(big), FAKE, 1, 16, 128, FAKE, FAKE, None, 4, 0.0,
+                                                      512, 0, 1 << 22, FAKE, FAKE, None))
+    assert code == 3 and "static maximum" in msg
+    ok = _layout(S=8192)
+    # within the bound: validation passes and the call stops at the device check (no GPU here)
+    assert _err(lib.irb_route_topk_fused_noalloc(ctypes.byref(ok), FAKE, 1, 16, 128, FAKE, FAKE, None, 4, 0.0, 512,
+                                                 0, 8192, FAKE, FAKE, None))[0] == 1
+    assert _err(lib.irb_route_topk_fused_noalloc(ctypes.byref(ok), FAKE, 1, 12, 128, FAKE, FAKE, None, 4, 0.0, 512,
+                                                 0, 8192, FAKE, FAKE, None))[0] == 3
