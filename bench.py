@@ -3,15 +3,16 @@
 One step = the whole hot path over one batch of synthetic input already
 resident in HBM, every stage a call of the C ABI on one stream:
 
-* routed workloads: index-query preparation (RMSNorm + RoPE; timed beside
-  the route pipeline, whose index queries the workload already gives
-  normalised) -> key compression -> block scoring + top-k selection ->
-  (the selection's region bitmap, also timed beside the pipeline)
+* routed workloads: key compression -> block scoring + top-k selection
   (fused, bounded score chunks) -> route expansion -> sparse GQA attention
   forward, and, where the workload trains (packed 32768, 131072), reverse
   block lists -> attention backward;
 * latent workload: index compaction -> attention forward -> reverse lists
   -> backward.
+
+Calls whose outputs the step does not read (index-query preparation, the
+selection's region bitmap, the full/partial split of the reverse lists) are
+timed after the step, outside it, under ``aux_calls_outside_step``.
 
 Prints one JSON line.  ``value`` is the forward attention throughput in
 TFLOP/s counted on selected (query, key) pairs only: 2*(Dqk+Dv)*Hq per pair,
@@ -225,12 +226,6 @@ def main():
         if wl.latent:
             timed("compact", lambda: C(lib.irb_compact_routes(P(idx), S, W, S, P(routes), P(lens), P(bad), sptr)), rec)
             return
-        # index-query preparation (RMSNorm + RoPE at each query's token), timed
-        # beside the route pipeline: the workload's index queries are already
-        # normalised, so scoring keeps them and qprep is not read afterwards
-        timed("prepare_queries", lambda: C(lib.irb_prepare_index_queries(
-            P(d["qI"]), irb._dtype_code(d["qI"]), B * S, wl.H_idx, wl.D_idx, P(d["gamma"]), 1e-5, P(d["freqs"]),
-            d["freqs"].shape[-1], P(qprep), sptr)), rec)
         timed("compress", lambda: C(lib.irb_compress_keys(
             irb.ctypes.byref(lay), c, P(d["kI"]), irb._dtype_code(d["kI"]), d["kI"].stride(0), d["kI"].stride(1),
             wl.D_idx, P(d["gamma"]), 1e-5, P(d["freqs"]), d["freqs"].shape[-1], P(kc), P(cu_blocks), sptr)), rec)
@@ -245,10 +240,6 @@ def main():
                 irb.ctypes.byref(lay), P(d["qI"]), irb._dtype_code(d["qI"]), R, wl.H_idx // R, wl.D_idx, P(d["w"]),
                 P(kc), P(cu_blocks), c, 1.0 / math.sqrt(wl.D_idx), topk, q0, S, P(sel), P(cnt), P(fused_ws),
                 fused_ws.numel(), sptr)), rec)
-        # route bitmap of the selection (membership words per query), timed
-        # beside the route pipeline; nothing downstream reads it
-        timed("region_bitmap", lambda: C(lib.irb_pack_region_bitmap(
-            P(sel), R * B * S, topk, nb_blocks, P(sel_bitmap), sptr)), rec)
         timed("expand", lambda: [C(lib.irb_expand_and_compact_routes(
             irb.ctypes.byref(lay), P(sel_g[g]), P(cnt_g[g]), topk, c, window, P(cu_blocks), L, P(routes_g[g]),
             P(lens_g[g]), sptr)) for g in range(R)], rec)
@@ -261,14 +252,28 @@ def main():
             timed("reverse_lists", lambda: C(lib.irb_build_block_lists(
                 P(routes), P(lens), R * B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(lists_ws),
                 lists_ws.numel(), sptr)), rec)
-            # full/partial split of the reverse lists, timed beside the backward (which does not read it)
-            timed("split_full_blocks", lambda: C(lib.irb_split_full_blocks(
-                P(routes), P(lens), R * B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(full_counts),
-                P(full_idx), P(part_counts), P(part_idx), P(split_ws), split_ws.numel(), sptr)), rec)
             timed("attn_bwd", lambda: C(lib.irb_sparse_gqa_attention_bwd(
                 P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens), R,
                 P(rev_counts), P(rev_idx), rbq, rbk, nqt, B, S, S, L, Hq, Hkv, Dqk, Dv, scale, P(dq), P(dk), P(dv),
                 P(bwd_ws), bwd_ws.numel(), P(dropped), sptr)), rec)
+
+    def aux_step(rec):
+        """Calls timed beside the step, outside it: nothing in the step reads their outputs."""
+        if wl.latent:
+            return
+        # index-query preparation (RMSNorm + RoPE at each query's token): the
+        # workload's index queries are already normalised, so scoring keeps them
+        timed("prepare_queries", lambda: C(lib.irb_prepare_index_queries(
+            P(d["qI"]), irb._dtype_code(d["qI"]), B * S, wl.H_idx, wl.D_idx, P(d["gamma"]), 1e-5, P(d["freqs"]),
+            d["freqs"].shape[-1], P(qprep), sptr)), rec)
+        # route bitmap of the selection (membership words per query)
+        timed("region_bitmap", lambda: C(lib.irb_pack_region_bitmap(
+            P(sel), R * B * S, topk, nb_blocks, P(sel_bitmap), sptr)), rec)
+        if backward:
+            # full/partial split of the reverse lists
+            timed("split_full_blocks", lambda: C(lib.irb_split_full_blocks(
+                P(routes), P(lens), R * B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(full_counts),
+                P(full_idx), P(part_counts), P(part_idx), P(split_ws), split_ws.numel(), sptr)), rec)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -295,6 +300,12 @@ def main():
         step_ev.append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    # the auxiliary calls, after the timed steps (same number of repetitions)
+    for _ in range(2):
+        aux_step(False)
+    for _ in range(args.steps):
+        aux_step(True)
+    torch.cuda.synchronize()
     ms = {name: float(np.mean([a.elapsed_time(b) for a, b in evs])) for name, evs in stages.items()}
     step_ms = float(np.mean([a.elapsed_time(b) for a, b in step_ev]))
 
@@ -333,17 +344,18 @@ def main():
         work["score_select"] = ("mfma", 2.0 * wl.H_idx * wl.D_idx * sparse_pairs)
         work["expand"] = ("hbm", R * float(np.sum(valid_t)) * (4 * topk + 4 * L + 4))
         route_ms = sum(ms[n] for n in ("compress", "score_select", "expand") if n in ms)
-    stage_out = {}
+    stage_out, aux_out = {}, {}
+    aux_names = ("prepare_queries", "region_bitmap", "split_full_blocks")
     for name, t in ms.items():
         bound, amount = work[name]
         if bound == "mfma":
             ach = amount / (t / 1e3) / 1e12
-            stage_out[name] = {"ms": round(t, 4), "bound": "mfma", "achieved": round(ach, 3), "unit": "TFLOP/s",
+            (aux_out if name in aux_names else stage_out)[name] = {"ms": round(t, 4), "bound": "mfma", "achieved": round(ach, 3), "unit": "TFLOP/s",
                                "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 5),
                                "work": amount}
         else:
             ach = amount / (t / 1e3) / 1e9
-            stage_out[name] = {"ms": round(t, 4), "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
+            (aux_out if name in aux_names else stage_out)[name] = {"ms": round(t, 4), "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
                                "peak": HBM_PEAK_GBS, "frac": round(ach / HBM_PEAK_GBS, 5), "work": amount}
     fwd_s = ms["attn_fwd"] / 1e3
     tflops = fwd_flop / fwd_s / 1e12
@@ -391,6 +403,7 @@ def main():
             "gathered_GBps": round(gathered / fwd_s / 1e9, 1),
         },
         "stages": stage_out,
+        "aux_calls_outside_step": aux_out,
         "input_gen_s": round(gen_s, 2),
     }
     if backward:

@@ -175,6 +175,9 @@ size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv,
     const size_t nkt = (static_cast<size_t>(S_k) + 15) / 16;
     const size_t cap = static_cast<size_t>(hit_capacity(B, S_q, S_k, L, RG));
     n += align256((static_cast<size_t>(RG) * B * nkt + 1) * 8) + 2 * align256(cap * 4);
+    // 64 heads over shared latent rows: the query-major path (used when v aliases k)
+    if (dtype == IRB_BF16 && Dqk == 576 && Dv == 512 && G == 64)
+      n = std::max(n, latent_bwd_workspace_bytes(B, S_q, S_k, L, Hq, Hkv));
   } else {
     const size_t esz = dtype == IRB_BF16 ? 2 : 4;
     n += align256(rows * Hkv * Dqk * Gp * esz) + align256(rows * Hkv * Dv * Gp * esz);
@@ -1278,6 +1281,9 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
   constexpr bool kGqaHits = sizeof(T) == 2 && D == DV && (D == 64 || D == 128);
   constexpr bool kWide = sizeof(T) == 2 && D == 576 && DV == 512;
   const bool hits = kGqaHits || (kWide && G % 32 == 0);
+  if constexpr (kWide)
+    if (latent_bwd_applies(a, args.dk, args.dv))
+      return launch_latent_bwd(a, args.dout, args.lse, args.dq, args.dk, args.ws, args.dropped, stream);
   BwdWs ws = carve(args.ws, a.B, a.S_q, a.S_k, a.L, a.Hq, a.Hkv, a.Dqk, a.Dv, a.dtype, a.RG);
   const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
   const int64_t rows = static_cast<int64_t>(a.B) * a.S_q;

@@ -1038,6 +1038,10 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
   if (items == 0) return 0;
   const int PAD = sizeof(T) == 2 ? 8 : 4;
   const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
+  if constexpr (sizeof(T) == 2 && D == 576 && DV == 512) {
+    const int rc = launch_latent_fwd(a, out, lse, dout, delta, kDelta, stream);
+    if (rc >= 0) return rc;
+  }
   int tile_bq = 0;    // > 0: the gather kernel skips the query tiles the tile kernel takes
   if constexpr (sizeof(T) == 2 && (D == 64 || D == 128) && D == DV) {
     // the tile kernel addresses a 32-key tile by 32-bit byte offsets from its first row

@@ -95,6 +95,16 @@ inline bool gather_head_major(const AttnArgs& a) {
 }
 
 int launch_attn_fwd(const AttnArgs& a, void* out, float* lse, hipStream_t stream);
+// bf16 shared latent rows (576 / 512) with 64 heads per KV head: o and lse, or
+// (delta_mode) Delta[b,h,t] = rowsum(dO * o) with o in FP32; -1 if the shape is not its own
+int launch_latent_fwd(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, bool delta_mode,
+                      hipStream_t stream);
+// query-major latent backward (bf16 576 / 512 with v aliasing k, 64 heads per
+// KV head, merged dk == dv): its workspace bytes, whether it applies, and the launch
+size_t latent_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv);
+bool latent_bwd_applies(const AttnArgs& a, const void* dk, const void* dv);
+int launch_latent_bwd(const AttnArgs& a, const void* dout, const float* lse, void* dq, void* dkv_out, void* ws,
+                      int64_t* dropped, hipStream_t stream);
 // backward row statistic Delta[b,h,t] = rowsum(dO * o) with o recomputed in FP32
 int launch_attn_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t stream);
 

@@ -73,6 +73,10 @@ def attn_tol_check(got, want, dtype, what):
         worst = mx - 1e-4
         ok = mx <= 1e-4
     print(f"  {what}: max-abs {mx:.3e} (|ref|<4: {mx_small:.3e}) mean-abs {mean:.3e} max|ref| {scale:.3f}")
+    if not ok and err.size:
+        bad = np.argwhere(err > (bf16_tolerance(want) if dtype == torch.bfloat16 else 1e-4))
+        print(f"  {what}: {len(bad)} elements beyond the bound; first {bad[:8].tolist()}; worst at "
+              f"{np.unravel_index(int(np.argmax(err)), err.shape)}")
     assert ok, (f"{what}: max-abs {mx:.3e}, |ref|<4 max-abs {mx_small:.3e}, worst excess over the bound "
                 f"{worst:.3e}, mean-abs {mean:.3e} (max |ref| {scale:.3f})")
     return mx, mean
