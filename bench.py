@@ -190,6 +190,8 @@ def main():
     out = torch.empty((B, S, Hq, Dv), dtype=dt, device=dev)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     strides = irb._strides9(q, k, v)
+    fwd_ws_n = int(lib.irb_sparse_gqa_attention_fwd_workspace_size(B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q), R))
+    fwd_ws = torch.empty(max(fwd_ws_n, 16), dtype=torch.uint8, device=dev)
     backward = wl.backward
     if backward:
         rbq, rbk = 1, 16
@@ -247,7 +249,7 @@ def main():
     def attn_step(rec):
         timed("attn_fwd", lambda: C(lib.irb_sparse_gqa_attention_fwd(
             P(q), P(k), P(v), irb._dtype_code(q), strides, P(routes), P(lens), R, B, S, S, L, Hq, Hkv, Dqk, Dv,
-            scale, P(out), P(lse), sptr)), rec)
+            scale, P(out), P(lse), P(fwd_ws) if fwd_ws_n > 0 else None, fwd_ws_n, sptr)), rec)
         if backward:
             timed("reverse_lists", lambda: C(lib.irb_build_block_lists(
                 P(routes), P(lens), R * B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(lists_ws),

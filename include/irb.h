@@ -385,15 +385,26 @@ int irb_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int
  *     group's routes are one [B, S_q, L] block (for B = 1 the CSA page's
  *     [batch, groups, queries, slots]).
  *   out OUT [B, S_q, Hq, Dv] dtype contiguous; lse OUT [B, Hq, S_q] fp32
+ *   workspace: optional device scratch (16-byte aligned, NULL allowed) of
+ *     irb_sparse_gqa_attention_fwd_workspace_size() bytes: the key-membership
+ *     words of every route row ([FA4] _block_lists builds its block masks
+ *     from the routes once; here one bit per (route row, key)), built once
+ *     per call and read by every KV head's query tiles.  The size is 0 where
+ *     the query-tile kernel does not run (fp32, head dims 576/512, group
+ *     sizes other than 4, 8, 16) or the words would exceed 256 MiB; with no
+ *     (or a smaller) workspace the tiles build their masks from the routes
+ *     in LDS.  Results are the same either way.
  * Requires Hq % Hkv == 0, Hq/Hkv <= 64, (Dqk, Dv) in {(64,64), (128,128)} or,
  * for bf16, (576,512); strides and q/k/v addresses 16-byte aligned;
  * route_groups = 1 or Hkv.
  */
+size_t irb_sparse_gqa_attention_fwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk,
+                                                   int Dv, int dtype, int route_groups);
 int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype,
                                  const int64_t* strides, const int32_t* routes, const int32_t* lens,
                                  int route_groups, int B, int S_q, int S_k, int L, int Hq, int Hkv,
                                  int Dqk, int Dv, float softmax_scale, void* out, float* lse,
-                                 void* stream);
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * a7 -- gradients of irb_sparse_gqa_attention_fwd ([QSA]

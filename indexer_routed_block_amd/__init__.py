@@ -57,8 +57,9 @@ _SIGS = {
     "irb_split_full_blocks_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
     "irb_split_full_blocks": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "irb_build_block_lists": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _SZ, _P], _I),
+    "irb_sparse_gqa_attention_fwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P,
-                                      _P], _I),
+                                      _P, _SZ, _P], _I),
     "irb_sparse_gqa_attention_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_sparse_gqa_attention_bwd": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
                                       _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P, _P], _I),
@@ -476,12 +477,15 @@ def _route_groups(routes, lens):
     return 1
 
 
-def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None, lse=None):
+def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None, lse=None, workspace=None,
+                             use_workspace=True):
     """irb_sparse_gqa_attention_fwd: (o [B,S_q,Hq,Dv] in q's dtype, lse [B,Hq,S_q] fp32).
 
     routes [B, S_q, L] are shared by every head; routes [Hkv, B, S_q, L]
-    (lens [Hkv, B, S_q]) give every KV group its own routes."""
-    _gpu(q, k, v, routes, lens, out, lse)
+    (lens [Hkv, B, S_q]) give every KV group its own routes.  The
+    key-membership workspace is allocated here unless given or
+    ``use_workspace`` is False (then the query tiles build their masks in LDS)."""
+    _gpu(q, k, v, routes, lens, out, lse, workspace)
     lib = load_library()
     _check_qkv(q, k, v, routes, lens)
     B, S_q, Hq, Dqk = q.shape
@@ -494,10 +498,17 @@ def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None
         lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev)
     _req(out, "out", q.dtype, shape=(B, S_q, Hq, Dv))
     _req(lse, "lse", torch.float32, shape=(B, Hq, S_q))
+    rg = _route_groups(routes, lens)
+    if workspace is None and use_workspace:
+        n = lib.irb_sparse_gqa_attention_fwd_workspace_size(B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv,
+                                                            _dtype_code(q), rg)
+        workspace = torch.empty(int(n), dtype=torch.uint8, device=dev) if n > 0 else None
+    _req(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.irb_sparse_gqa_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v),
-                                            _ptr(routes), _ptr(lens), _route_groups(routes, lens), B, S_q, S_k,
+                                            _ptr(routes), _ptr(lens), rg, B, S_q, S_k,
                                             routes.shape[-1], Hq, Hkv, Dqk, Dv, scale, _ptr(out), _ptr(lse),
-                                            _stream(dev)))
+                                            _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse
 
 

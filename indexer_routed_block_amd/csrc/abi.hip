@@ -469,18 +469,31 @@ static int check_attn(const char* fn, const void* q, const void* k, const void* 
   return 0;
 }
 
+size_t irb_sparse_gqa_attention_fwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
+                                                    int dtype, int route_groups) {
+  if (B < 1 || S_q < 1 || S_k < 1 || L < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return 0;
+  if (route_groups != 1 && route_groups != Hkv) return 0;
+  irb::AttnArgs a{};
+  a.B = B; a.S_q = S_q; a.S_k = S_k; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.Dqk = Dqk; a.Dv = Dv;
+  a.dtype = dtype; a.RG = route_groups;
+  return irb::attn_fwd_qbits_bytes(a);
+}
+
 int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
                                  const int32_t* routes, const int32_t* lens, int route_groups, int B, int S_q,
                                  int S_k, int L_width, int Hq, int Hkv, int Dqk, int Dv, float softmax_scale,
-                                 void* out, float* lse, void* stream) {
+                                 void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "irb_sparse_gqa_attention_fwd";
   irb::AttnArgs a;
   if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, route_groups, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv,
                      softmax_scale, a))
     return r;
   if (!out || !lse) return fail(IRB_ERR_INVALID, "%s: NULL output", fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return fail(IRB_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
   IRB_REQUIRE_DEVICE();
-  return launched(fn, irb::launch_attn_fwd(a, out, lse, static_cast<hipStream_t>(stream)));
+  return launched(fn, irb::launch_attn_fwd(a, out, lse, workspace, workspace ? ws_bytes : 0,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,

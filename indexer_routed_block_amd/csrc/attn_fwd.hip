@@ -547,7 +547,8 @@ attn_fwd_kernel(AttnArgs a, T* __restrict__ out, float* __restrict__ lse, int G,
 template <int D, int DV, int G, bool kDelta>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__ lse, const uint16_t* __restrict__ dout,
-                     float* __restrict__ delta, int n_qt, int thr_milli) {
+                     float* __restrict__ delta, int n_qt, int thr_milli, const uint32_t* __restrict__ qbits,
+                     int qwords) {
   using T = uint16_t;
   constexpr int BQ = 128 / G;
   constexpr int KS = D / 16;          // 16-dim k-steps of S^T = K Q^T
@@ -721,8 +722,8 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   auto step = [&](auto cc, auto pvc, int i, int ntiles, int seg0) __attribute__((always_inline)) {
     constexpr int C = decltype(cc)::value;      // i % 3
     constexpr bool kPV = decltype(pvc)::value;  // i > 0
-    if (i + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIK + NIV>());
-    else __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIV>());
+    if (i + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kDmaWait<NIK + NIV>());
+    else __builtin_amdgcn_s_waitcnt(kDmaWait<NIV>());
     bare_barrier();
     if (i + 3 < ntiles) issue(seg0 + tiles[i + 3], std::integral_constant<int, C>{}, KSide{});
     if (i + 1 < ntiles) issue(seg0 + tiles[i + 1], std::integral_constant<int, (C + 1) % 3>{}, VSide{});
@@ -820,6 +821,15 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     const int nseg = min(kSegTiles, kt_last - seg0 + 1);
     const int key0 = seg0 * 32, key1 = key0 + kSegTiles * 32;
     __syncthreads();
+    if (qbits) {
+      // the queries' key-membership words (one bit per key, built once per
+      // route row by the bitmap pass) are this segment's mask rows as they are
+      for (int i = tid; i < BQ * nseg; i += 256) {
+        const int qi = i / nseg, j = i - qi * nseg;
+        const int t = qa + qi;
+        mask[qi][j] = t < a.S_q ? qbits[route_row(a, b, t, kvh) * qwords + seg0 + j] : 0u;
+      }
+    } else {
     for (int i = tid; i < BQ * (kSegTiles + 1); i += 256) (&mask[0][0])[i] = 0u;
     __syncthreads();
     // route masks of this segment.  Entry ranges [lo, hi) per query (one lane
@@ -905,7 +915,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
             ce += 512;
           }
         }
-        __builtin_amdgcn_s_waitcnt(kVmWaitTile<0>());
+        __builtin_amdgcn_s_waitcnt(kDmaWait<0>());
         asm volatile("" : : : "memory");
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
@@ -931,6 +941,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
         }
       }
     }
+    }
     // every wave's mask words are complete before wave 0 reads them all
     __syncthreads();
     // compact list of the key tiles any query routes to
@@ -955,9 +966,9 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     if (ntiles > 1) issue(seg0 + tiles[1], std::integral_constant<int, 1>{}, KSide{});
     if (ntiles > 2) issue(seg0 + tiles[2], std::integral_constant<int, 2>{}, KSide{});
     issue(seg0 + tiles[0], std::integral_constant<int, 0>{}, VSide{});
-    if (ntiles > 2) __builtin_amdgcn_s_waitcnt(kVmWaitTile<2 * NIK + NIV>());
-    else if (ntiles > 1) __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIK + NIV>());
-    else __builtin_amdgcn_s_waitcnt(kVmWaitTile<NIV>());
+    if (ntiles > 2) __builtin_amdgcn_s_waitcnt(kDmaWait<2 * NIK + NIV>());
+    else if (ntiles > 1) __builtin_amdgcn_s_waitcnt(kDmaWait<NIK + NIV>());
+    else __builtin_amdgcn_s_waitcnt(kDmaWait<NIV>());
     bare_barrier();
     scores(scur, 0);
     step(std::integral_constant<int, 0>{}, std::false_type{}, 0, ntiles, seg0);
@@ -968,7 +979,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       if (i + 2 < ntiles) step(std::integral_constant<int, 0>{}, std::true_type{}, i + 2, ntiles, seg0);
     }
     // drain: O^T += V^T P^T of the last tile
-    __builtin_amdgcn_s_waitcnt(kVmWaitTile<0>());
+    __builtin_amdgcn_s_waitcnt(kDmaWait<0>());
     bare_barrier();
     accumulate(pprev, static_cast<uint32_t>((ntiles - 1) % 3) * BUF);
   }
@@ -1022,17 +1033,32 @@ static int tile_thr_milli() {
 }
 
 template <int D, int DV, int G, bool kDelta>
-static void launch_tile(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, hipStream_t stream) {
+static void launch_tile(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta,
+                        const uint32_t* qbits, int qwords, hipStream_t stream) {
   constexpr int BQ = 128 / G;
   const int n_qt = (a.S_q + BQ - 1) / BQ;
   const unsigned grid = static_cast<unsigned>(a.B) * n_qt * a.Hkv;
   hipLaunchKernelGGL((attn_fwd_tile_kernel<D, DV, G, kDelta>), dim3(grid), dim3(256), 0, stream, a,
                      static_cast<uint16_t*>(out), lse, static_cast<const uint16_t*>(dout), delta, n_qt,
-                     tile_thr_milli());
+                     tile_thr_milli(), qbits, qwords);
+}
+
+// key-membership words per route row, built in the forward's workspace when
+// the query-tile kernel can run and they fit the budget (else 0 bytes: the
+// tile kernel builds its masks from the routes in LDS)
+static constexpr size_t kQbitsBudget = size_t{256} << 20;
+size_t attn_fwd_qbits_bytes(const AttnArgs& a) {
+  const int G = a.Hq / a.Hkv;
+  if (a.dtype != IRB_BF16 || a.Dqk != a.Dv || (a.Dqk != 64 && a.Dqk != 128) || (G != 4 && G != 8 && G != 16)) return 0;
+  if (a.S_k > 131072) return 0;
+  const size_t words = (static_cast<size_t>(a.S_k) + 31) / 32;
+  const size_t bytes = static_cast<size_t>(a.RG) * a.B * a.S_q * words * 4;
+  return bytes <= kQbitsBudget ? bytes : 0;
 }
 
 template <typename T, int D, int DV, bool kDelta>
-static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, hipStream_t stream) {
+static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int64_t items = static_cast<int64_t>(a.B) * a.S_q * a.Hkv;
   if (items == 0) return 0;
@@ -1047,9 +1073,17 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
     // the tile kernel addresses a 32-key tile by 32-bit byte offsets from its first row
     const bool small_strides = static_cast<int64_t>(a.sk_t > a.sv_t ? a.sk_t : a.sv_t) * 64 < (int64_t{1} << 31);
     if (tile_thr_milli() <= 1000 && small_strides && (G == 4 || G == 8 || G == 16)) {
-      if (G == 4) launch_tile<D, DV, 4, kDelta>(a, out, lse, dout, delta, stream);
-      if (G == 8) launch_tile<D, DV, 8, kDelta>(a, out, lse, dout, delta, stream);
-      if (G == 16) launch_tile<D, DV, 16, kDelta>(a, out, lse, dout, delta, stream);
+      const size_t qb = attn_fwd_qbits_bytes(a);
+      const uint32_t* qbits = nullptr;
+      const int qwords = (a.S_k + 31) / 32;
+      if (qb > 0 && ws && ws_bytes >= qb) {
+        const int64_t rows = static_cast<int64_t>(a.RG) * a.B * a.S_q;
+        if (int rc = launch_route_bits(a.routes, a.lens, rows, a.L, a.S_k, static_cast<uint32_t*>(ws), stream)) return rc;
+        qbits = static_cast<const uint32_t*>(ws);
+      }
+      if (G == 4) launch_tile<D, DV, 4, kDelta>(a, out, lse, dout, delta, qbits, qwords, stream);
+      if (G == 8) launch_tile<D, DV, 8, kDelta>(a, out, lse, dout, delta, qbits, qwords, stream);
+      if (G == 16) launch_tile<D, DV, 16, kDelta>(a, out, lse, dout, delta, qbits, qwords, stream);
       tile_bq = 128 / G;
     }
   }
@@ -1081,24 +1115,25 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
 }
 
 template <bool kDelta>
-static int dispatch_fwd(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, hipStream_t stream) {
+static int dispatch_fwd(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   if (a.dtype == IRB_BF16) {
-    if (a.Dqk == 64 && a.Dv == 64) return launch_fwd_t<uint16_t, 64, 64, kDelta>(a, out, lse, dout, delta, stream);
-    if (a.Dqk == 128 && a.Dv == 128) return launch_fwd_t<uint16_t, 128, 128, kDelta>(a, out, lse, dout, delta, stream);
-    if (a.Dqk == 576 && a.Dv == 512) return launch_fwd_t<uint16_t, 576, 512, kDelta>(a, out, lse, dout, delta, stream);
+    if (a.Dqk == 64 && a.Dv == 64) return launch_fwd_t<uint16_t, 64, 64, kDelta>(a, out, lse, dout, delta, ws, ws_bytes, stream);
+    if (a.Dqk == 128 && a.Dv == 128) return launch_fwd_t<uint16_t, 128, 128, kDelta>(a, out, lse, dout, delta, ws, ws_bytes, stream);
+    if (a.Dqk == 576 && a.Dv == 512) return launch_fwd_t<uint16_t, 576, 512, kDelta>(a, out, lse, dout, delta, ws, ws_bytes, stream);
   } else {
-    if (a.Dqk == 64 && a.Dv == 64) return launch_fwd_t<float, 64, 64, kDelta>(a, out, lse, dout, delta, stream);
-    if (a.Dqk == 128 && a.Dv == 128) return launch_fwd_t<float, 128, 128, kDelta>(a, out, lse, dout, delta, stream);
+    if (a.Dqk == 64 && a.Dv == 64) return launch_fwd_t<float, 64, 64, kDelta>(a, out, lse, dout, delta, ws, ws_bytes, stream);
+    if (a.Dqk == 128 && a.Dv == 128) return launch_fwd_t<float, 128, 128, kDelta>(a, out, lse, dout, delta, ws, ws_bytes, stream);
   }
   return static_cast<int>(hipErrorInvalidValue);
 }
 
-int launch_attn_fwd(const AttnArgs& a, void* out, float* lse, hipStream_t stream) {
-  return dispatch_fwd<false>(a, out, lse, nullptr, nullptr, stream);
+int launch_attn_fwd(const AttnArgs& a, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return dispatch_fwd<false>(a, out, lse, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 int launch_attn_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t stream) {
-  return dispatch_fwd<true>(a, nullptr, nullptr, dout, delta, stream);
+  return dispatch_fwd<true>(a, nullptr, nullptr, dout, delta, nullptr, 0, stream);
 }
 
 }  // namespace irb

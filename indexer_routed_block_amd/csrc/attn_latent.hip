@@ -43,16 +43,6 @@ constexpr int kPSlot = kHeads * kKC * 2;  // P^T of one chunk: [head][16 keys] b
 constexpr float kLog2eL = 1.4426950408889634f;
 constexpr float kLn2L = 0.6931471805599453f;
 
-// s_waitcnt immediate for direct-to-LDS data: at most N vector-memory
-// operations of this wave outstanding AND lgkmcnt(0).  Measured on MI355X:
-// with vmcnt alone, a chunk's rows were now and then read before their LDS
-// writes had landed (one 16-key chunk of one query in roughly one call in
-// ten); draining lgkmcnt as well removed every such case over 80 calls.
-template <int N>
-constexpr int kDmaWait() {
-  return kVmWaitTile<N>() & ~(15 << 8);
-}
-
 // byte offset inside a buffer of (row r, bf16 element d) under the chunk swizzle
 IRB_DEV uint32_t swz(int r, int d) {
   return static_cast<uint32_t>(r * kRowB + 16 * ((d >> 3) ^ (r & 7)) + 2 * (d & 7));

@@ -38,6 +38,60 @@ bitmap_kernel(const int32_t* __restrict__ ids, int64_t rows, int slots, int regi
   for (int w = lane; w < words; w += 64) o[w] = bm[w];
 }
 
+// Key-membership words of ascending route rows with their lengths (the
+// forward's query-tile masks): only the first lens[row] entries count.  A
+// lane takes 8 consecutive entries; entries of one word are ORed together in
+// registers and the word takes one LDS atomic per run, so the long runs of
+// consecutive keys (selected blocks, windows) do not serialise on one word.
+__global__ void __launch_bounds__(kBmWaves * 64)
+route_bits_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int64_t rows, int L,
+                  int keys, int words, uint32_t* __restrict__ out) {
+  extern __shared__ uint32_t rb_all[];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kBmWaves + wid;
+  if (row >= rows) return;                       // whole wavefront; no workgroup barrier below
+  uint32_t* bm = rb_all + wid * words;
+  for (int w = lane; w < words; w += 64) bm[w] = 0u;
+  wave_lds_sync();
+  const int32_t* r = routes + row * L;
+  const int n = max(0, min(lens[row], L));
+  for (int e0 = 8 * lane; e0 < n; e0 += 512) {
+    int id[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) id[j] = e0 + j < n ? r[e0 + j] : -1;
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = id[j] >= 0 && id[j] < keys;
+      acc |= ok ? 1u << (id[j] & 31) : 0u;
+      const int wd = ok ? id[j] >> 5 : -1;
+      const int nx = (j < 7 && id[j + 1] >= 0 && id[j + 1] < keys) ? id[j + 1] >> 5 : -2;
+      if (wd >= 0 && nx != wd) {
+        atomicOr(&bm[wd], acc);
+        acc = 0u;
+      }
+    }
+  }
+  wave_lds_sync();
+  uint32_t* o = out + row * words;
+  for (int w = lane; w < words; w += 64) o[w] = bm[w];
+}
+
+int launch_route_bits(const int32_t* routes, const int32_t* lens, int64_t rows, int L, int keys, uint32_t* bits,
+                      hipStream_t stream) {
+  if (rows == 0) return 0;
+  const int words = (keys + 31) / 32;
+  const size_t lds = static_cast<size_t>(kBmWaves) * words * sizeof(uint32_t);
+  if (lds > 48 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_bits_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return static_cast<int>(e);
+  }
+  hipLaunchKernelGGL(route_bits_kernel, dim3(static_cast<unsigned>((rows + kBmWaves - 1) / kBmWaves)),
+                     dim3(kBmWaves * 64), lds, stream, routes, lens, rows, L, keys, words, bits);
+  return 0;
+}
+
 int launch_bitmap(const int32_t* ids, int64_t rows, int slots, int regions, int32_t* bitmap, hipStream_t stream) {
   if (rows == 0) return 0;
   const int words = (regions + 31) / 32;

@@ -132,6 +132,17 @@ constexpr int kVmWaitTile() {
   return N | (7 << 4) | (15 << 8);
 }
 
+// The same, also waiting for lgkmcnt(0): the wait to use before reading (or
+// publishing with a barrier) data that direct global-to-LDS loads wrote.
+// Measured on MI355X: after a vmcnt-only wait such data was now and then read
+// before it had landed in LDS (one 16-key chunk in roughly one latent
+// backward call in ten); with lgkmcnt drained as well no case remained, at
+// no measurable cost.
+template <int N>
+constexpr int kDmaWait() {
+  return kVmWaitTile<N>() & ~(15 << 8);
+}
+
 // Direct 16-byte global-to-LDS load (global_load_lds_dwordx4): lane i writes
 // LDS bytes [lds_base + 16 i, + 16) of the wave-uniform lds_base.  Written as
 // inline assembly so that the compiler does not wait for these loads before

@@ -49,6 +49,9 @@ int launch_expand(const Layout& L, const int32_t* sel, const int32_t* cnt, int t
 int launch_compact(const int32_t* in, int64_t rows, int width, int64_t key_count, int32_t* out,
                    int32_t* lens, int32_t* bad, hipStream_t stream);
 
+// key-membership words [rows, ceil(keys / 32)] of the first lens[row] entries of route rows [rows, L]; keys <= 131072
+int launch_route_bits(const int32_t* routes, const int32_t* lens, int64_t rows, int L, int keys, uint32_t* bits,
+                      hipStream_t stream);
 // membership words [rows, ceil(regions / 32)] of id rows [rows, slots]; regions <= 131072
 int launch_bitmap(const int32_t* ids, int64_t rows, int slots, int regions, int32_t* bitmap, hipStream_t stream);
 
@@ -94,7 +97,10 @@ inline bool gather_head_major(const AttnArgs& a) {
   return kv_bytes > (int64_t{128} << 20);
 }
 
-int launch_attn_fwd(const AttnArgs& a, void* out, float* lse, hipStream_t stream);
+// ws (nullable): at least attn_fwd_qbits_bytes(a) bytes for the per-route-row
+// key-membership words of the query-tile kernel (else its masks come from the routes)
+size_t attn_fwd_qbits_bytes(const AttnArgs& a);
+int launch_attn_fwd(const AttnArgs& a, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 // bf16 shared latent rows (576 / 512) with 64 heads per KV head: o and lse, or
 // (delta_mode) Delta[b,h,t] = rowsum(dO * o) with o in FP32; -1 if the shape is not its own
 int launch_latent_fwd(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta, bool delta_mode,

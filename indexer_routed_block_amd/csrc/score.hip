@@ -276,9 +276,9 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
       // this wave's loads of chunk it are done once at most the later chunks'
       // loads (and any score stores issued after them) are outstanding
       const int ahead = min(NBUF - 2, nch - 1 - it);
-      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(kVmWaitTile<2 * NI>());
-      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(kVmWaitTile<NI>());
-      else __builtin_amdgcn_s_waitcnt(kVmWaitTile<0>());
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(kDmaWait<2 * NI>());
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(kDmaWait<NI>());
+      else __builtin_amdgcn_s_waitcnt(kDmaWait<0>());
       bare_barrier();
       if (it + NBUF - 1 < nch) issue(cb + (it + NBUF - 1) * CH, (it + NBUF - 1) % NBUF);
     } else {

@@ -140,7 +140,7 @@ def test_attention_validation():
     lib = irb.load_library()
     st = (ctypes.c_int64 * 9)(64 * 4 * 128, 4 * 128, 128, 64 * 128, 128, 128, 64 * 128, 128, 128)
     call = lambda Hq=4, Hkv=1, D=128, Dv=128, sc=0.1, dt=1, strides=st, rg=1: lib.irb_sparse_gqa_attention_fwd(
-        FAKE, FAKE, FAKE, dt, strides, FAKE, FAKE, rg, 1, 64, 64, 16, Hq, Hkv, D, Dv, sc, FAKE, FAKE, None)
+        FAKE, FAKE, FAKE, dt, strides, FAKE, FAKE, rg, 1, 64, 64, 16, Hq, Hkv, D, Dv, sc, FAKE, FAKE, None, 0, None)
     assert _err(call(Hq=6, Hkv=4))[0] == 3
     assert _err(call(Hq=128, Hkv=1))[0] == 3
     assert _err(call(D=96, Dv=96))[0] == 3
@@ -153,6 +153,16 @@ def test_attention_validation():
     assert _err(call(dt=5))[0] == 2
     odd = (ctypes.c_int64 * 9)(*list(st)[:8], 129)
     assert _err(call(strides=odd))[0] == 3
+    # forward workspace: key-membership words of every route row where the query-tile kernel runs
+    fws = lib.irb_sparse_gqa_attention_fwd_workspace_size
+    assert fws(1, 8192, 8192, 2176, 32, 4, 128, 128, 1, 1) == 8192 * 256 * 4
+    assert fws(1, 8192, 8192, 2176, 32, 4, 128, 128, 1, 4) == 4 * 8192 * 256 * 4
+    assert fws(1, 8192, 8192, 2176, 32, 4, 128, 128, 0, 1) == 0          # fp32: no query-tile kernel
+    assert fws(1, 16384, 16384, 2048, 64, 1, 576, 512, 1, 1) == 0        # latent rows
+    assert fws(1, 131072, 131072, 2560, 64, 8, 128, 128, 1, 1) == 0      # 2 GiB of words: over the budget
+    misaligned = lambda: lib.irb_sparse_gqa_attention_fwd(FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, 1, 1, 64, 64, 16, 4, 1,
+                                                          128, 128, 0.1, FAKE, FAKE, ctypes.c_void_p(0x1004), 64, None)
+    assert _err(misaligned())[0] == 3
     # route groups: 1 (shared) or one per KV head
     code, msg = _err(call(Hq=8, Hkv=4, rg=2))
     assert code == 3 and "route_groups" in msg
