@@ -33,9 +33,21 @@ its reason in the design notes):
   (one route shared by every head) or R = Hkv (one per KV group); for B = 1
   this is the CSA page's [batch, groups, queries, slots].
 
+* CSA variant: slots of a region that are not valid hold zeros in the
+  gathered payload; a region summary is the per-dimension softmax (over the
+  region's valid slots) of the compression logits weighting the keys, in
+  float32, rounded to BF16 and then to E4M3 (E4M3 as torch's float8_e4m3fn
+  conversion: round to nearest even, NaN past 448); a query's historical
+  regions are the complete ones before the region holding it, and that
+  current region fills the extra selection slot.
+
 Parity status: every function here is pinned by the CPU tests (hand-derived
-fixtures, brute force, library special cases, invariants); none is
-"parity unpinned" with respect to these readings.
+fixtures, brute force, library special cases, invariants) with respect to
+these readings.  ``summarize_region_payload`` is "parity unpinned" with
+respect to the pages: the CSA page states its precision (FP32 arithmetic,
+BF16 then E4M3 rounding) but not its formula, so only the reading above is
+pinned (closed forms: equal logits give the mean, a lone or dominant slot
+gives its key, the BF16 rounding precedes the E4M3 one).
 """
 from __future__ import annotations
 
@@ -726,3 +738,159 @@ def route_pipeline(kI, qI, w, gamma, freqs, c, topk, window, eps=1e-5, scale=Non
     sel, cnt = select_topk(s, c, topk, cu_seqlens, row_lens)
     routes, lens = expand_routes(sel, cnt, c, window, topk, cu_seqlens, row_lens)
     return dict(kc=kc, cu_blocks=cu_blocks, scores=s, sel=sel, cnt=cnt, routes=routes, lens=lens)
+
+
+# ---------------------------------------------------------------------------
+# CSA variant: region payload gather, learned region summaries, E4M3
+# rounding, selection with the current-region slot
+# ---------------------------------------------------------------------------
+
+def _round_to_grid(x, mant_bits, min_exp):
+    """Round-to-nearest-even onto a binary floating-point grid with
+    ``mant_bits`` stored mantissa bits and smallest normal exponent ``min_exp``
+    (below it the grid is uniform: subnormals), unbounded above."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    m, e = np.frexp(np.where(fin, x, 1.0))          # |x| = m 2^e, 0.5 <= m < 1: leading bit 2^(e-1)
+    step = np.ldexp(1.0, np.maximum(e - 1, min_exp) - mant_bits)
+    out[fin] = (np.rint(x / step) * step)[fin]      # np.rint rounds halves to even
+    return out
+
+
+def round_to_bf16(x):
+    """bfloat16 round-to-nearest-even (8 significand bits, float32's exponent range), as float64."""
+    q = _round_to_grid(x, 7, -126)
+    return np.where(np.abs(q) >= 2.0 ** 128, np.copysign(np.inf, q), q)
+
+
+def round_to_e4m3(x):
+    """E4M3 (OCP FN: 4 exponent bits with bias 7, 3 mantissa bits, no infinities)
+    round-to-nearest-even, as float64 -- the CSA page's "E4M3-rounded"
+    tensors (index queries and region summaries) are BF16 tensors holding
+    such values.  The largest finite value is 448; a value that rounds past
+    it (to 480 on the grid) or is not finite becomes NaN, as torch's
+    float8_e4m3fn conversion does.  Zero keeps its sign."""
+    x = np.asarray(x, dtype=np.float64)
+    q = _round_to_grid(x, 3, -6)
+    return np.where(np.isfinite(q) & (np.abs(q) <= 448.0), q, np.nan)
+
+
+def gather_region_payload(keys, logits, sources, valid):
+    """CSA page, ``gather_region_payload`` / ``_gather_region_payload``: the
+    index keys and compression logits of every region's source tokens,
+    gathered without arithmetic into [B, R, region_size, D].
+
+    ``keys``, ``logits`` [B, T, D]; ``sources`` int32 [B, R, region_size]
+    (token index, -1 for a missing slot); ``valid`` bool of the same shape
+    (excludes padding tokens and missing slots).  Reading: slots that are not
+    valid hold zeros (the page leaves their content open; the summary
+    ignores them).
+    """
+    keys = np.asarray(keys)
+    logits = np.asarray(logits)
+    src = np.asarray(sources).astype(np.int64)
+    ok = np.asarray(valid, dtype=bool) & (src >= 0) & (src < keys.shape[1])
+    idx = np.where(ok, src, 0)
+    b = np.arange(keys.shape[0])[:, None, None]
+    pk = np.where(ok[..., None], keys[b, idx], 0).astype(keys.dtype)
+    pz = np.where(ok[..., None], logits[b, idx], 0).astype(logits.dtype)
+    return pk, pz
+
+
+def summarize_region_payload(pk, pz, valid, fp32_only=False):
+    """CSA page, ``_summarize_region_payload`` (reading; the page states FP32
+    arithmetic and two quantisation roundings, not the formula).
+
+    Per region r and dimension d, the compression logits of the region's
+    valid slots weight their keys through a softmax over the slots
+    (``Step5SparseIndexer.project_keys``: per-dimension compression logits):
+
+        s[r, d] = sum_s exp(z[r,s,d] - m[r,d]) k[r,s,d] / sum_s exp(z[r,s,d] - m[r,d]),
+        m[r, d] = max over valid slots s of z[r,s,d],
+
+    evaluated in float32, then rounded to BF16 and that value to E4M3
+    (``indexer_score_tile`` takes E4M3-rounded BF16 summaries).  A region with
+    no valid slot summarises to 0.  ``fp32_only`` returns the float32 values
+    before the two roundings (to locate rounding boundaries).
+    """
+    k = np.asarray(pk, dtype=np.float32)
+    z = np.asarray(pz, dtype=np.float32)
+    ok = np.asarray(valid, dtype=bool)[..., None]
+    zm = np.where(ok, z, np.float32(-np.inf))
+    m = np.max(zm, axis=-2, keepdims=True)
+    any_ok = np.isfinite(m)
+    m = np.where(any_ok, m, np.float32(0.0))
+    e = np.where(ok, np.exp(zm - m, dtype=np.float32), np.float32(0.0))
+    den = np.sum(e, axis=-2, dtype=np.float32)
+    num = np.sum(e * k, axis=-2, dtype=np.float32)
+    s = np.where(den > 0, num / np.where(den > 0, den, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
+    if fp32_only:
+        return s
+    return round_to_e4m3(round_to_bf16(s))
+
+
+def region_bases(docs, c: int):
+    """Global region ID of every document's first region when every token
+    belongs to a region (CSA page, ``region_metadata``: regions of
+    ``region_size`` tokens, reset at every document boundary, so a
+    document of ``len`` tokens has ``ceil(len / c)`` regions, the last one
+    possibly incomplete), and the total region count of each row."""
+    out, totals = [], []
+    for row in docs:
+        base, bases = 0, []
+        for (a, e) in row:
+            bases.append(base)
+            base += -(-(e - a) // c)
+        out.append(bases)
+        totals.append(base)
+    return out, totals
+
+
+def select_regions_csa(scores, c, topk, cu_seqlens=None, row_lens=None, q0=0, S=None):
+    """CSA page, ``RegionSelection.region_ids`` with ``RegionMetadata.current``
+    (reading): ids [B, rows, topk + 1] int32 and their counts [B, rows].
+
+    A query at document position ``pos`` lies in region ``floor(pos / c)`` of
+    its document, the current region, which it always keeps.  Its historical
+    regions are the ones before that, ``floor(pos / c)`` of them (all
+    complete); they compete for ``topk`` slots by score as in
+    ``select_topk`` (ties to the lower index; with at most ``topk`` of them
+    all are taken).  ``scores`` are the block scores of this library's
+    numbering (complete blocks only, as written by ``indexer_scores``); the
+    output uses the page's numbering, in which every document's regions
+    (incomplete last one included) are consecutive, sorted ascending, with
+    the unused slots holding the sentinel R = the row's region count.
+    Padding queries hold only sentinels (count 0).
+    """
+    scores = np.asarray(scores)
+    B, rows, NB = scores.shape
+    S = q0 + rows if S is None else S
+    docs = documents(B, S, cu_seqlens, row_lens)
+    valid, start, base, nb = token_info(docs, S, c)
+    rbases, totals = region_bases(docs, c)
+    ids = np.zeros((B, rows, topk + 1), dtype=np.int32)
+    cnt = np.zeros((B, rows), dtype=np.int32)
+    for b in range(B):
+        ids[b] = totals[b]
+        dstarts = [a for (a, e) in docs[b]]
+        for r in range(rows):
+            t = q0 + r
+            if not valid[b, t]:
+                continue
+            d = dstarts.index(int(start[b, t]))
+            pos = t - int(start[b, t])
+            h = pos // c                          # historical regions = complete blocks before the current one
+            k = min(topk, h)
+            lo = int(base[b, t])
+            if k > 0:
+                vis = scores[b, r, lo:lo + h]
+                order = np.lexsort((np.arange(h), -vis))[:k]
+                chosen = np.sort(order)
+            else:
+                chosen = np.zeros(0, dtype=np.int64)
+            rb = rbases[b][d]
+            ids[b, r, :k] = rb + chosen
+            ids[b, r, k] = rb + h
+            cnt[b, r] = k + 1
+    return ids, cnt
