@@ -261,6 +261,77 @@ int irb_route_topk_fused_groups(const irb_layout* layout, const void* q_idx, int
                                 void* stream);
 
 /*
+ * Step-5 CSA variant (next row of the hot path) -- [CSA] nemo_automodel.
+ * components.models.step5.sparse.  Regions are summarised by learned
+ * per-dimension weights instead of mean pooling, scoring takes E4M3-rounded
+ * BF16 queries and summaries (irb_indexer_score_tile accepts them as bf16
+ * tensors and reproduces their products exactly), and the selection keeps
+ * the query's current region in an extra slot.
+ *
+ * irb_round_e4m3 -- the E4M3 rounding of [CSA] indexer_score_tile's inputs:
+ *   out[i] = x[i] rounded to nearest even on the E4M3 grid (4 exponent bits,
+ *   bias 7, 3 mantissa bits, largest 448; a value rounding past it, or not
+ *   finite, gives NaN), stored as bf16 (exact).  x bf16 or fp32 [n];
+ *   out bf16 [n] (may alias a bf16 x).
+ */
+int irb_round_e4m3(const void* x, int dtype, int64_t n, uint16_t* out, void* stream);
+
+/*
+ * [CSA] gather_region_payload / _gather_region_payload: the keys and
+ * compression logits of every region's source tokens, gathered without
+ * arithmetic (bit-exact copies):
+ *   packed_keys[b, r, s, :] = keys[b, sources[b, r, s], :] where the slot is
+ *   valid, zeros otherwise; packed_logits likewise.
+ *   keys, logits [B, T, D] dtype contiguous; sources int32 [B, R, region_size]
+ *   (-1 = missing slot; ids outside [0, T) count as missing); valid uint8
+ *   [B, R, region_size] (0 excludes a padding token; NULL = every slot with
+ *   a source); outputs [B, R, region_size, D] dtype.  Requires D * element
+ *   size a multiple of 16 and 16-byte aligned keys, logits and outputs.
+ */
+int irb_gather_region_payload(const void* keys, const void* logits, int dtype, int B, int T, int D,
+                              const int32_t* sources, const uint8_t* valid, int R, int region_size,
+                              void* packed_keys, void* packed_logits, void* stream);
+
+/*
+ * [CSA] _summarize_region_payload: FP32 arithmetic and the two quantisation
+ * roundings the page requires.  The page does not print the formula; the
+ * reading taken here: per region r and dimension d,
+ *   s[b, r, d] = sum_s softmax_s(z[b, r, s, d]) k[b, r, s, d]
+ * over the region's valid slots (the softmax of the per-dimension
+ * compression logits, max-subtracted), in FP32, rounded to BF16 and then to
+ * E4M3 (irb_round_e4m3).  A region with no valid slot gives 0.
+ *   packed_keys, packed_logits [B, R, region_size, D] dtype contiguous (as
+ *   irb_gather_region_payload writes them); valid uint8 [B, R, region_size];
+ *   summary OUT bf16 [B, R, D] holding E4M3 values.
+ */
+int irb_summarize_region_payload(const void* packed_keys, const void* packed_logits, int dtype,
+                                 const uint8_t* valid, int B, int R, int region_size, int D,
+                                 uint16_t* summary, void* stream);
+
+/*
+ * [CSA] RegionSelection.region_ids with RegionMetadata.current: for each
+ * valid query t in [q0, q1) at document position pos, its historical
+ * regions -- the floor(pos / c) complete blocks of its document before the
+ * one holding it -- compete for topk slots by score exactly as in
+ * irb_select_topk_regions; the current region (floor(pos / c) of its
+ * document) is always added.  The ids are the page's region numbering, in
+ * which every token belongs to a region, so each document's regions (its
+ * incomplete last one included) are consecutive: written ascending (the
+ * current one last), then the sentinel R = the row's region count up to
+ * topk + 1 slots; cnt = used slots (0 for padding queries, which hold only
+ * sentinels).
+ *   scores   as for irb_select_topk_regions (block columns of this library's
+ *            numbering: complete blocks only, e.g. irb_indexer_score_tile)
+ *   region_ids OUT [B, S, topk + 1] int32; cnt OUT [B, S] int32 (rows q0..q1-1)
+ *   workspace irb_select_regions_csa_workspace_size() bytes of device scratch
+ * Requires 1 <= topk <= 4096, 1 <= c.
+ */
+size_t irb_select_regions_csa_workspace_size(int B, int S, int topk, int num_docs);
+int irb_select_regions_csa(const irb_layout* layout, const float* scores, int64_t score_row_stride,
+                           int q0, int q1, const int32_t* cu_blocks, int c, int topk, int32_t* region_ids,
+                           int32_t* cnt, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * a4 -- [QSA] select_qsa_token_ids: selected blocks expand to their c token
  * IDs, then the tokens of the current incomplete group [doc_start + nb*c, t]
  * are appended; plus the window [max(doc_start, t-window+1), t] ([CSA]

@@ -50,6 +50,11 @@ _SIGS = {
     "irb_route_topk_fused_groups_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_route_topk_fused_groups": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P],
                                     _I),
+    "irb_round_e4m3": ([_P, _I, _I64, _P, _P], _I),
+    "irb_gather_region_payload": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P], _I),
+    "irb_summarize_region_payload": ([_P, _P, _I, _P, _I, _I, _I, _I, _P, _P], _I),
+    "irb_select_regions_csa_workspace_size": ([_I, _I, _I, _I], _SZ),
+    "irb_select_regions_csa": ([_P, _P, _I64, _I, _I, _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "irb_expand_and_compact_routes": ([_P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P], _I),
     "irb_compact_routes": ([_P, _I64, _I, _I64, _P, _P, _P, _P], _I),
     "irb_pack_region_bitmap": ([_P, _I64, _I, _I, _P, _P], _I),
@@ -330,6 +335,70 @@ def route_topk_fused_noalloc(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=N
                                             _ptr(cu_blocks), c, scale, topk, q0, q1, _ptr(sel), _ptr(cnt),
                                             _stream(dev)))
     return sel, cnt
+
+
+def round_e4m3(x, out=None):
+    """irb_round_e4m3: x (bf16 or fp32, contiguous) rounded to E4M3, stored as bf16 (``out`` may be a bf16 x)."""
+    _gpu(x, out)
+    lib = load_library()
+    _req(x, "x", _ACT)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _req(out, "out", torch.bfloat16, shape=x.shape)
+    _check(lib.irb_round_e4m3(_ptr(x), _dtype_code(x), x.numel(), _ptr(out), _stream(x.device)))
+    return out
+
+
+def gather_region_payload(keys, logits, sources, valid=None):
+    """irb_gather_region_payload: (packed_keys, packed_logits) [B, R, region_size, D] in the keys' dtype."""
+    _gpu(keys, logits, sources, valid)
+    lib = load_library()
+    _req(keys, "keys", _ACT)
+    _req(logits, "logits", keys.dtype, shape=keys.shape)
+    _req(sources, "sources", I32)
+    if valid is not None:
+        _req(valid, "valid", (torch.bool, torch.uint8), shape=sources.shape)
+    B, T, D = keys.shape
+    R, rs = sources.shape[1], sources.shape[2]
+    pk = torch.empty((B, R, rs, D), dtype=keys.dtype, device=keys.device)
+    pz = torch.empty_like(pk)
+    _check(lib.irb_gather_region_payload(_ptr(keys), _ptr(logits), _dtype_code(keys), B, T, D, _ptr(sources),
+                                         _ptr(valid), R, rs, _ptr(pk), _ptr(pz), _stream(keys.device)))
+    return pk, pz
+
+
+def summarize_region_payload(packed_keys, packed_logits, valid):
+    """irb_summarize_region_payload: E4M3-rounded bf16 region summaries [B, R, D]."""
+    _gpu(packed_keys, packed_logits, valid)
+    lib = load_library()
+    _req(packed_keys, "packed_keys", _ACT)
+    _req(packed_logits, "packed_logits", packed_keys.dtype, shape=packed_keys.shape)
+    _req(valid, "valid", (torch.bool, torch.uint8), shape=packed_keys.shape[:-1])
+    B, R, rs, D = packed_keys.shape
+    out = torch.empty((B, R, D), dtype=torch.bfloat16, device=packed_keys.device)
+    _check(lib.irb_summarize_region_payload(_ptr(packed_keys), _ptr(packed_logits), _dtype_code(packed_keys),
+                                            _ptr(valid), B, R, rs, D, _ptr(out), _stream(packed_keys.device)))
+    return out
+
+
+def select_regions_csa(scores, c, topk, S, q0=0, cu_blocks=None, cu_seqlens=None, row_lens=None, workspace=None):
+    """irb_select_regions_csa over score rows q0..q0+rows: (region_ids [B, S, topk + 1], cnt [B, S])."""
+    _gpu(scores, cu_blocks, cu_seqlens, row_lens, workspace)
+    lib = load_library()
+    _req(scores, "scores", torch.float32, contiguous=False, unit_last=True)
+    _req(cu_blocks, "cu_blocks", I32)
+    B, rows, _ = scores.shape
+    dev = scores.device
+    lay = make_layout(B, S, cu_seqlens, row_lens)
+    if workspace is None:
+        n = lib.irb_select_regions_csa_workspace_size(B, S, topk, lay.num_docs)
+        workspace = torch.empty(max(int(n), 16), dtype=torch.uint8, device=dev)
+    ids = torch.zeros((B, S, topk + 1), dtype=torch.int32, device=dev)
+    cnt = torch.zeros((B, S), dtype=torch.int32, device=dev)
+    _check(lib.irb_select_regions_csa(ctypes.byref(lay), _ptr(scores), scores.stride(1), q0, q0 + rows,
+                                      _ptr(cu_blocks), c, topk, _ptr(ids), _ptr(cnt), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(dev)))
+    return ids, cnt
 
 
 def pack_region_bitmap(ids, regions, out=None):

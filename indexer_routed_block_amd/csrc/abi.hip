@@ -343,6 +343,70 @@ int irb_route_topk_fused_groups(const irb_layout* layout, const void* q_idx, int
                           c, score_scale, topk, q0, q1, sel, cnt, workspace, ws_bytes, stream);
 }
 
+int irb_round_e4m3(const void* x, int dtype, int64_t n, uint16_t* out, void* stream) {
+  const char* fn = "irb_round_e4m3";
+  if (int r = check_dtype(fn, dtype)) return r;
+  if (n < 0) return fail(IRB_ERR_INVALID, "%s: n must be >= 0", fn);
+  if (n == 0) return ok();
+  if (!x || !out) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_round_e4m3(x, dtype, n, out, static_cast<hipStream_t>(stream)));
+}
+
+int irb_gather_region_payload(const void* keys, const void* logits, int dtype, int B, int T, int D,
+                              const int32_t* sources, const uint8_t* valid, int R, int region_size, void* packed_keys,
+                              void* packed_logits, void* stream) {
+  const char* fn = "irb_gather_region_payload";
+  if (int r = check_dtype(fn, dtype)) return r;
+  const int esize = dtype == IRB_BF16 ? 2 : 4;
+  if (B < 1 || T < 1 || D < 1 || R < 0 || region_size < 1) return fail(IRB_ERR_INVALID, "%s: bad sizes", fn);
+  if ((D * esize) % 16) return fail(IRB_ERR_INVALID, "%s: D * element size must be a multiple of 16 bytes", fn);
+  if (!keys || !logits || !sources || !packed_keys || !packed_logits) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if ((reinterpret_cast<uintptr_t>(keys) | reinterpret_cast<uintptr_t>(logits) | reinterpret_cast<uintptr_t>(packed_keys) |
+       reinterpret_cast<uintptr_t>(packed_logits)) & 15)
+    return fail(IRB_ERR_INVALID, "%s: keys, logits and outputs must be 16-byte aligned", fn);
+  if (R == 0) return ok();
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_gather_payload(keys, logits, esize, B, T, D, sources, valid, R, region_size, packed_keys,
+                                                 packed_logits, static_cast<hipStream_t>(stream)));
+}
+
+int irb_summarize_region_payload(const void* packed_keys, const void* packed_logits, int dtype, const uint8_t* valid,
+                                 int B, int R, int region_size, int D, uint16_t* summary, void* stream) {
+  const char* fn = "irb_summarize_region_payload";
+  if (int r = check_dtype(fn, dtype)) return r;
+  if (B < 1 || R < 0 || region_size < 1 || D < 1) return fail(IRB_ERR_INVALID, "%s: bad sizes", fn);
+  if (!packed_keys || !packed_logits || !valid || !summary) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (R == 0) return ok();
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_summarize(packed_keys, packed_logits, dtype, valid, B, R, region_size, D, summary,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t irb_select_regions_csa_workspace_size(int B, int S, int topk, int num_docs) {
+  if (B < 1 || S < 1 || topk < 1 || num_docs < 0) return 0;
+  return irb::region_ids_workspace_bytes(B, S, topk, num_docs);
+}
+
+int irb_select_regions_csa(const irb_layout* layout, const float* scores, int64_t score_row_stride, int q0, int q1,
+                           const int32_t* cu_blocks, int c, int topk, int32_t* region_ids, int32_t* cnt,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "irb_select_regions_csa";
+  irb::Layout L;
+  if (int r = check_layout(fn, layout, L)) return r;
+  if (c < 1) return fail(IRB_ERR_INVALID, "%s: c must be >= 1", fn);
+  if (topk < 1 || topk > 4096) return fail(IRB_ERR_INVALID, "%s: topk must be in 1..4096 (got %d)", fn, topk);
+  if (q0 < 0 || q1 <= q0 || q1 > L.S) return fail(IRB_ERR_INVALID, "%s: need 0 <= q0 < q1 <= S", fn);
+  if (score_row_stride < 1) return fail(IRB_ERR_INVALID, "%s: score_row_stride must be >= 1", fn);
+  if (!scores || !region_ids || !cnt || !workspace) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (L.cu_seqlens && !cu_blocks) return fail(IRB_ERR_INVALID, "%s: packed layout needs cu_blocks", fn);
+  if (ws_bytes < irb::region_ids_workspace_bytes(L.B, L.S, topk, L.num_docs))
+    return fail(IRB_ERR_INVALID, "%s: workspace too small", fn);
+  IRB_REQUIRE_DEVICE();
+  return launched(fn, irb::launch_region_ids(L, scores, score_row_stride, q0, q1, cu_blocks, c, topk, region_ids, cnt,
+                                             workspace, static_cast<hipStream_t>(stream)));
+}
+
 int irb_expand_and_compact_routes(const irb_layout* layout, const int32_t* sel, const int32_t* cnt, int topk, int c,
                                   int window, const int32_t* cu_blocks, int L_width, int32_t* routes, int32_t* lens,
                                   void* stream) {

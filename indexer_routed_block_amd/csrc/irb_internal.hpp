@@ -39,9 +39,21 @@ int launch_score_grouped(const Layout& L, const void* q, int dtype, int groups, 
 // kcs[2 blk] = bf16 high halves of kc[blk], kcs[2 blk + 1] = low halves (rows of D)
 int launch_split_keys(const float* kc, uint16_t* kcs, int64_t n_blocks, int D, hipStream_t stream);
 
+// hist_only = 1: a query sees only the complete blocks before its own group's
+// block (floor(pos / c) of them: the CSA historical regions), else floor((pos + 1) / c)
 int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, int q1,
                   const int32_t* cu_blocks, int c, int topk, int32_t* sel, int32_t* cnt,
-                  hipStream_t stream);
+                  hipStream_t stream, int hist_only = 0);
+
+// CSA variant (csa.hip)
+int launch_round_e4m3(const void* x, int dtype, int64_t n, uint16_t* out, hipStream_t stream);
+int launch_gather_payload(const void* keys, const void* logits, int esize, int B, int T, int D, const int32_t* sources,
+                          const uint8_t* valid, int R, int rs, void* pk, void* pz, hipStream_t stream);
+int launch_summarize(const void* pk, const void* pz, int dtype, const uint8_t* valid, int B, int R, int rs, int D,
+                     uint16_t* summary, hipStream_t stream);
+size_t region_ids_workspace_bytes(int B, int S, int topk, int num_docs);
+int launch_region_ids(const Layout& L, const float* scores, int64_t stride, int q0, int q1, const int32_t* cu_blocks,
+                      int c, int topk, int32_t* ids, int32_t* cnt, void* ws, hipStream_t stream);
 
 int launch_expand(const Layout& L, const int32_t* sel, const int32_t* cnt, int topk, int c, int window,
                   const int32_t* cu_blocks, int Lw, int32_t* routes, int32_t* lens, hipStream_t stream);

@@ -40,7 +40,7 @@ template <bool kInLds>
 __global__ void __launch_bounds__(kSelThreads)
 select_kernel(Layout L, const float* __restrict__ scores, int64_t stride, int q0, int q1,
               const int32_t* __restrict__ cu_blocks, int c, int topk, int32_t* __restrict__ sel,
-              int32_t* __restrict__ cnt) {
+              int32_t* __restrict__ cnt, int hist_only) {
   extern __shared__ uint32_t keys[];
   __shared__ int hist[256];
   __shared__ int wsum[4];
@@ -49,7 +49,7 @@ select_kernel(Layout L, const float* __restrict__ scores, int64_t stride, int q0
   const int r = blockIdx.x, t = q0 + r, b = blockIdx.y;
   int32_t* srow = sel + (static_cast<int64_t>(b) * L.S + t) * topk;
   const Doc d = doc_of(L, b, t);
-  const int n = d.valid ? (t - d.start + 1) / c : 0;
+  const int n = d.valid ? (t - d.start + 1 - hist_only) / c : 0;   // visible blocks (hist: before the query's own)
   const int base = d.valid ? block_base(L, cu_blocks, d) : 0;
   if (n <= topk) {                     // every visible block is taken
     for (int i = tid; i < topk; i += kSelThreads) srow[i] = (i < n) ? base + i : -1;
@@ -115,7 +115,7 @@ template <int NPT>
 __global__ void __launch_bounds__(kSelThreads, (NPT >= 64 ? 2 : 4))
 select_reg_kernel(Layout L, const float* __restrict__ scores, int64_t stride, int q0, int q1,
                   const int32_t* __restrict__ cu_blocks, int c, int topk, int32_t* __restrict__ sel,
-                  int32_t* __restrict__ cnt) {
+                  int32_t* __restrict__ cnt, int hist_only) {
   static_assert(4 * NPT <= kSelThreads, "one scan entry per (round, wave)");
   __shared__ int hist[kSelBins];
   __shared__ int wsum[4];
@@ -126,7 +126,7 @@ select_reg_kernel(Layout L, const float* __restrict__ scores, int64_t stride, in
   const int r = blockIdx.x, t = q0 + r, b = blockIdx.y;
   int32_t* srow = sel + (static_cast<int64_t>(b) * L.S + t) * topk;
   const Doc d = doc_of(L, b, t);
-  const int n = d.valid ? (t - d.start + 1) / c : 0;
+  const int n = d.valid ? (t - d.start + 1 - hist_only) / c : 0;   // visible blocks (hist: before the query's own)
   const int base = d.valid ? block_base(L, cu_blocks, d) : 0;
   if (n <= topk) {                     // every visible block is taken
     for (int i = tid; i < topk; i += kSelThreads) srow[i] = (i < n) ? base + i : -1;
@@ -233,7 +233,7 @@ template <int NPL>
 __global__ void __launch_bounds__(kSelThreads)
 select_wave_kernel(Layout L, const float* __restrict__ scores, int64_t stride, int q0, int q1,
                    const int32_t* __restrict__ cu_blocks, int c, int topk, int32_t* __restrict__ sel,
-                   int32_t* __restrict__ cnt) {
+                   int32_t* __restrict__ cnt, int hist_only) {
   __shared__ int hist_all[kSelThreads / 64][256];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = blockIdx.x * (kSelThreads / 64) + wid;
@@ -242,7 +242,7 @@ select_wave_kernel(Layout L, const float* __restrict__ scores, int64_t stride, i
   int* hist = hist_all[wid];
   int32_t* srow = sel + (static_cast<int64_t>(b) * L.S + t) * topk;
   const Doc d = doc_of(L, b, t);
-  const int n = d.valid ? (t - d.start + 1) / c : 0;
+  const int n = d.valid ? (t - d.start + 1 - hist_only) / c : 0;   // visible blocks (hist: before the query's own)
   const int base = d.valid ? block_base(L, cu_blocks, d) : 0;
   if (n <= topk) {                     // every visible block is taken
     for (int i = lane; i < topk; i += 64) srow[i] = (i < n) ? base + i : -1;
@@ -324,7 +324,7 @@ select_wave_kernel(Layout L, const float* __restrict__ scores, int64_t stride, i
 
 int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, int q1,
                   const int32_t* cu_blocks, int c, int topk, int32_t* sel, int32_t* cnt,
-                  hipStream_t stream) {
+                  hipStream_t stream, int hist_only) {
   const int n_max = L.S / c;
   const dim3 grid(static_cast<unsigned>(q1 - q0), static_cast<unsigned>(L.B));
 #define IRB_SEL_WAVE(NPL)                                                                                  \
@@ -332,7 +332,7 @@ int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, 
     const dim3 gw(static_cast<unsigned>((q1 - q0 + kSelThreads / 64 - 1) / (kSelThreads / 64)),            \
                   static_cast<unsigned>(L.B));                                                             \
     hipLaunchKernelGGL(select_wave_kernel<NPL>, gw, dim3(kSelThreads), 0, stream, L, scores, stride, q0, q1, \
-                       cu_blocks, c, topk, sel, cnt);                                                      \
+                       cu_blocks, c, topk, sel, cnt, hist_only);                                                      \
     return 0;                                                                                              \
   }
   IRB_SEL_WAVE(8)
@@ -342,7 +342,7 @@ int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, 
 #define IRB_SEL_REG(NPT)                                                                                   \
   if (n_max <= kSelThreads * NPT) {                                                                        \
     hipLaunchKernelGGL(select_reg_kernel<NPT>, grid, dim3(kSelThreads), 0, stream, L, scores, stride, q0, q1, \
-                       cu_blocks, c, topk, sel, cnt);                                                      \
+                       cu_blocks, c, topk, sel, cnt, hist_only);                                                      \
     return 0;                                                                                              \
   }
   IRB_SEL_REG(16)
@@ -357,10 +357,10 @@ int launch_select(const Layout& L, const float* scores, int64_t stride, int q0, 
       if (e != hipSuccess) return static_cast<int>(e);
     }
     hipLaunchKernelGGL(select_kernel<true>, grid, dim3(kSelThreads), lds, stream, L, scores, stride, q0, q1,
-                       cu_blocks, c, topk, sel, cnt);
+                       cu_blocks, c, topk, sel, cnt, hist_only);
   } else {
     hipLaunchKernelGGL(select_kernel<false>, grid, dim3(kSelThreads), 0, stream, L, scores, stride, q0, q1,
-                       cu_blocks, c, topk, sel, cnt);
+                       cu_blocks, c, topk, sel, cnt, hist_only);
   }
   return 0;
 }

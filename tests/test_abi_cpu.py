@@ -284,3 +284,32 @@ def test_noalloc_route_rejects_inputs_beyond_its_scratch():
                                                  0, 8192, FAKE, FAKE, None))[0] == 1
     assert _err(lib.irb_route_topk_fused_noalloc(ctypes.byref(ok), FAKE, 1, 12, 128, FAKE, FAKE, None, 4, 0.0, 512,
                                                  0, 8192, FAKE, FAKE, None))[0] == 3
+
+
+def test_csa_validation():
+    lib = irb.load_library()
+    # E4M3 rounding: dtype, n
+    assert _err(lib.irb_round_e4m3(FAKE, 7, 10, FAKE, None))[0] == 2
+    assert _err(lib.irb_round_e4m3(FAKE, 1, -1, FAKE, None))[0] == 3
+    assert _err(lib.irb_round_e4m3(None, 1, 0, None, None))[0] == 0          # nothing to do
+    # payload gather: rows must be whole 16-byte pieces, pointers aligned
+    s, m = _err(lib.irb_gather_region_payload(FAKE, FAKE, 1, 1, 10, 4, FAKE, None, 3, 4, FAKE, FAKE, None))
+    assert s == 3 and "16" in m
+    s, m = _err(lib.irb_gather_region_payload(ctypes.c_void_p(0x1008), FAKE, 1, 1, 10, 8, FAKE, None, 3, 4, FAKE,
+                                              FAKE, None))
+    assert s == 3 and "aligned" in m
+    assert _err(lib.irb_gather_region_payload(FAKE, FAKE, 1, 1, 10, 8, FAKE, None, 3, 0, FAKE, FAKE, None))[0] == 3
+    # summaries need the valid mask
+    s, m = _err(lib.irb_summarize_region_payload(FAKE, FAKE, 1, None, 1, 3, 4, 8, FAKE, None))
+    assert s == 3 and "NULL" in m
+    # selection with the current-region slot: workspace holds the block selection and the region prefix
+    lay = _layout(S=64)
+    need = lib.irb_select_regions_csa_workspace_size(1, 64, 4, 0)
+    assert need >= 64 * 4 * 4
+    s, m = _err(lib.irb_select_regions_csa(ctypes.byref(lay), FAKE, 16, 0, 64, None, 4, 4, FAKE, FAKE, FAKE, need - 1,
+                                           None))
+    assert s == 3 and "workspace" in m
+    assert _err(lib.irb_select_regions_csa(ctypes.byref(lay), FAKE, 16, 0, 64, None, 4, 0, FAKE, FAKE, FAKE, need,
+                                           None))[0] == 3
+    assert _err(lib.irb_select_regions_csa(ctypes.byref(lay), FAKE, 16, 0, 64, None, 4, 4, FAKE, FAKE, FAKE, need,
+                                           None))[0] == 1                    # valid; no GPU here
