@@ -259,10 +259,42 @@ def main():
                 P(rev_counts), P(rev_idx), rbq, rbk, nqt, B, S, S, L, Hq, Hkv, Dqk, Dv, scale, P(dq), P(dk), P(dv),
                 P(bwd_ws), bwd_ws.numel(), P(dropped), sptr)), rec)
 
+    # Step-5 CSA calls (S=8192 workload only): regions = the complete groups of c
+    # tokens, compression logits drawn N(0,1) in bf16 by a seeded device
+    # generator, the fused route call's score tile materialised once (untimed)
+    csa = (not wl.latent) and wl.name == "s8192" and R == 1
+    if csa:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wl.seed + 77)
+        csa_logits = torch.randn((B, S, wl.D_idx), generator=gen, device=dev).to(torch.bfloat16)
+        csa_src = (torch.arange(nb_blocks, device=dev, dtype=torch.int32)[:, None] * c
+                   + torch.arange(c, device=dev, dtype=torch.int32)[None, :]).expand(B, nb_blocks, c).contiguous()
+        csa_valid = torch.ones((B, nb_blocks, c), dtype=torch.uint8, device=dev)
+        csa_pk = torch.empty((B, nb_blocks, c, wl.D_idx), dtype=torch.bfloat16, device=dev)
+        csa_pz = torch.empty_like(csa_pk)
+        csa_sum = torch.empty((B, nb_blocks, wl.D_idx), dtype=torch.bfloat16, device=dev)
+        csa_q = torch.empty_like(d["qI"])
+        csa_scores = torch.empty((B, S, nb_blocks), dtype=torch.float32, device=dev)
+        csa_ids = torch.empty((B, S, topk + 1), dtype=torch.int32, device=dev)
+        csa_cnt = torch.empty((B, S), dtype=torch.int32, device=dev)
+        csa_ws = torch.empty(max(int(lib.irb_select_regions_csa_workspace_size(B, S, topk, 0)), 16), dtype=torch.uint8,
+                             device=dev)
+
     def aux_step(rec):
         """Calls timed beside the step, outside it: nothing in the step reads their outputs."""
         if wl.latent:
             return
+        if csa:
+            timed("csa_gather_payload", lambda: C(lib.irb_gather_region_payload(
+                P(d["kI"]), P(csa_logits), 1, B, S, wl.D_idx, P(csa_src), P(csa_valid), nb_blocks, c, P(csa_pk),
+                P(csa_pz), sptr)), rec)
+            timed("csa_summarize", lambda: C(lib.irb_summarize_region_payload(
+                P(csa_pk), P(csa_pz), 1, P(csa_valid), B, nb_blocks, c, wl.D_idx, P(csa_sum), sptr)), rec)
+            timed("csa_round_queries", lambda: C(lib.irb_round_e4m3(
+                P(d["qI"]), 1, d["qI"].numel(), P(csa_q), sptr)), rec)
+            timed("csa_select", lambda: C(lib.irb_select_regions_csa(
+                irb.ctypes.byref(lay), P(csa_scores), nb_blocks, 0, S, None, c, topk, P(csa_ids), P(csa_cnt),
+                P(csa_ws), csa_ws.numel(), sptr)), rec)
         # index-query preparation (RMSNorm + RoPE at each query's token): the
         # workload's index queries are already normalised, so scoring keeps them
         timed("prepare_queries", lambda: C(lib.irb_prepare_index_queries(
@@ -303,6 +335,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     # the auxiliary calls, after the timed steps (same number of repetitions)
+    if csa:
+        C(lib.irb_indexer_score_tile(irb.ctypes.byref(lay), P(d["qI"]), 1, wl.H_idx, wl.D_idx, P(d["w"]), P(kc), None, c,
+                                     0.0, 0, S, 0, nb_blocks, P(csa_scores), nb_blocks, sptr))
     for _ in range(2):
         aux_step(False)
     for _ in range(args.steps):
@@ -343,11 +378,21 @@ def main():
         # per route group: its own bitmap, selection and expansion; the
         # scoring work is the same in total (each group scores H_idx / R heads)
         work["region_bitmap"] = ("hbm", R * B * S * (4.0 * topk + 4.0 * ((nb_blocks + 31) // 32)))
+        if csa:
+            slots = float(B * nb_blocks * c)
+            # gather: keys and logits rows read and written, plus the source ids and valid flags
+            work["csa_gather_payload"] = ("hbm", slots * (4 * 2 * wl.D_idx + 5))
+            work["csa_summarize"] = ("hbm", slots * (2 * 2 * wl.D_idx + 1) + 2.0 * B * nb_blocks * wl.D_idx)
+            work["csa_round_queries"] = ("hbm", 4.0 * d["qI"].numel())
+            hist = np.where(valid_t, np.arange(S) // c, 0)
+            work["csa_select"] = ("hbm", 4.0 * float(np.sum(np.where(hist > topk, hist, 0)))
+                                  + 4.0 * (topk + 1) * S * B + 4.0 * S * B)
         work["score_select"] = ("mfma", 2.0 * wl.H_idx * wl.D_idx * sparse_pairs)
         work["expand"] = ("hbm", R * float(np.sum(valid_t)) * (4 * topk + 4 * L + 4))
         route_ms = sum(ms[n] for n in ("compress", "score_select", "expand") if n in ms)
     stage_out, aux_out = {}, {}
-    aux_names = ("prepare_queries", "region_bitmap", "split_full_blocks")
+    aux_names = ("prepare_queries", "region_bitmap", "split_full_blocks", "csa_gather_payload", "csa_summarize",
+                 "csa_round_queries", "csa_select")
     for name, t in ms.items():
         bound, amount = work[name]
         if bound == "mfma":
