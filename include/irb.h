@@ -8,6 +8,7 @@
  *   irb_indexer_score_tile       weighted-ReLU block scores for a query x block tile
  *   irb_select_topk_regions      top-k blocks per query (ascending, -1 suffix)
  *   irb_route_topk_fused         the two above without materialising scores
+ *   irb_route_topk_fused_raw     the same from raw index queries (preparation fused)
  *   irb_expand_and_compact_routes blocks + tail + window -> ascending token routes
  *   irb_compact_routes           arbitrary signed ID lists -> ascending valid prefix
  *   irb_build_block_lists        forward (query->key) / reverse (key->query) tile lists
@@ -199,6 +200,30 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
                          int D_idx, const float* w, const float* kc, const int32_t* cu_blocks,
                          int c, float score_scale, int topk, int q0, int q1, int32_t* sel,
                          int32_t* cnt, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Index-query preparation fused into a2+a3 -- [QSA] Qwen3_8_FlashNextQSAIndexer
+ * (q_layernorm, apply_qsa_rope) feeding select_qsa_token_ids: the same
+ * sel/cnt as irb_prepare_index_queries(q_raw -> q) followed by
+ * irb_route_topk_fused(q), without writing or re-reading the prepared
+ * queries.  The score kernel normalises and rotates each raw query row as it
+ * loads it, with the preparation call's FP32 arithmetic in the same order
+ * and the same single rounding to the input dtype, so its operands equal the
+ * prepared queries bit for bit.
+ *   q_raw  [B, S, H_idx, D_idx] dtype contiguous, 16-byte aligned (raw index queries)
+ *   gamma  [D_idx] fp32 gain, 16-byte aligned;  eps >= 0
+ *   rope   [B, S, D_rope] fp32 rotary rows cat(cos, sin) at each token's
+ *          document position, 16-byte aligned (NULL when D_rope == 0)
+ *   everything else, the workspace included, as irb_route_topk_fused
+ *          (irb_route_topk_fused_workspace_size gives its size).
+ * Requires D_rope = 0 or a multiple of 64 up to D_idx (each lane of the score
+ * kernel then holds the rotation partners of its own dimensions); other
+ * rotary widths go through irb_prepare_index_queries + irb_route_topk_fused.
+ */
+int irb_route_topk_fused_raw(const irb_layout* layout, const void* q_raw, int dtype, int H_idx, int D_idx,
+                             const float* gamma, float eps, const float* rope, int D_rope, const float* w,
+                             const float* kc, const int32_t* cu_blocks, int c, float score_scale, int topk, int q0,
+                             int q1, int32_t* sel, int32_t* cnt, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * irb_route_topk_fused without a workspace, for callers that cannot allocate

@@ -45,6 +45,8 @@ _SIGS = {
     "irb_select_topk_regions": ([_P, _P, _I64, _I, _I, _P, _I, _I, _P, _P, _P], _I),
     "irb_route_topk_fused_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_route_topk_fused": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "irb_route_topk_fused_raw": ([_P, _P, _I, _I, _I, _P, _F, _P, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P, _SZ,
+                                  _P], _I),
     "irb_route_topk_fused_noalloc": ([_P, _P, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _P, _P, _P], _I),
     "irb_indexer_score_tile_groups": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _F, _I, _I, _I, _I, _P, _I64, _P], _I),
     "irb_route_topk_fused_groups_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
@@ -306,6 +308,42 @@ def route_topk_fused(q_idx, w, kc, c, topk, q0=0, q1=None, score_scale=None, cu_
     _check(lib.irb_route_topk_fused(ctypes.byref(lay), _ptr(q_idx), _dtype_code(q_idx), H, D, _ptr(w), _ptr(kc),
                                     _ptr(cu_blocks), c, scale, topk, q0, q1, _ptr(sel), _ptr(cnt), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(dev)))
+    return sel, cnt
+
+
+def route_topk_fused_raw(q_raw, gamma, freqs, w, kc, c, topk, eps=1e-5, q0=0, q1=None, score_scale=None,
+                         cu_blocks=None, cu_seqlens=None, row_lens=None, workspace=None, sel=None, cnt=None):
+    """irb_route_topk_fused_raw: route_topk_fused's selection from raw index queries
+    q_raw [B, S, H, D], RMSNorm (gain ``gamma``) and RoPE (rows ``freqs`` [B, S, D_rope],
+    None: no rotation) applied inside the score kernel."""
+    _gpu(q_raw, gamma, freqs, w, kc, cu_blocks, cu_seqlens, row_lens, workspace, sel, cnt)
+    lib = load_library()
+    _req(q_raw, "q_raw", _ACT)
+    _req(gamma, "gamma", torch.float32)
+    _req(freqs, "freqs", torch.float32)
+    _req(w, "w", torch.float32, shape=q_raw.shape[:-1])
+    _req(kc, "kc", torch.float32)
+    _req(cu_blocks, "cu_blocks", I32)
+    _req(workspace, "workspace")
+    B, S, H, D = q_raw.shape
+    dev = q_raw.device
+    q1 = S if q1 is None else q1
+    scale = 0.0 if score_scale is None else score_scale
+    if workspace is None:
+        n = lib.irb_route_topk_fused_workspace_size(B, S, c, D, topk, q0, q1)
+        workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
+    if sel is None:
+        sel = torch.full((B, S, topk), -1, dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.zeros((B, S), dtype=torch.int32, device=dev)
+    _req(sel, "sel", I32, shape=(B, S, topk))
+    _req(cnt, "cnt", I32, shape=(B, S))
+    d_rope = 0 if freqs is None else freqs.shape[-1]
+    lay = make_layout(B, S, cu_seqlens, row_lens)
+    _check(lib.irb_route_topk_fused_raw(ctypes.byref(lay), _ptr(q_raw), _dtype_code(q_raw), H, D, _ptr(gamma), eps,
+                                        _ptr(freqs), d_rope, _ptr(w), _ptr(kc), _ptr(cu_blocks), c, scale, topk, q0,
+                                        q1, _ptr(sel), _ptr(cnt), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(dev)))
     return sel, cnt
 
 

@@ -252,7 +252,8 @@ size_t irb_route_topk_fused_groups_workspace_size(int B, int S, int c, int D_idx
 static int route_fused_impl(const char* fn, const irb_layout* layout, const void* q_idx, int dtype, int groups,
                             int H_idx, int D_idx, const float* w, const float* kc, const int32_t* cu_blocks, int c,
                             float score_scale, int topk, int q0, int q1, int32_t* sel, int32_t* cnt, void* workspace,
-                            size_t ws_bytes, void* stream, bool static_scratch = false) {
+                            size_t ws_bytes, void* stream, bool static_scratch = false,
+                            const irb::QPrep& prep = irb::QPrep{}) {
   irb::Layout L;
   if (int r = check_layout(fn, layout, L)) return r;
   if (int r = check_dtype(fn, dtype)) return r;
@@ -311,7 +312,7 @@ static int route_fused_impl(const char* fn, const irb_layout* layout, const void
     for (int a = q0; a < q1; a += static_cast<int>(std::min<int64_t>(rows, q1 - a))) {
       const int e = a + static_cast<int>(std::min<int64_t>(rows, q1 - a));
       int rc = irb::launch_score_tile(L, qg, dtype, H_idx, D_idx, wg, kc, kcs, cu_blocks, c, score_scale, a, e, 0, nb,
-                                      scores, nb, 0, topk, groups, st);
+                                      scores, nb, 0, topk, groups, st, prep);
       if (!rc)
         rc = irb::launch_select(L, scores, nb, a, e, cu_blocks, c, topk, sel + g * sel_group * topk,
                                 cnt + g * sel_group, st);
@@ -326,6 +327,26 @@ int irb_route_topk_fused(const irb_layout* layout, const void* q_idx, int dtype,
                          int32_t* sel, int32_t* cnt, void* workspace, size_t ws_bytes, void* stream) {
   return route_fused_impl("irb_route_topk_fused", layout, q_idx, dtype, 1, H_idx, D_idx, w, kc, cu_blocks, c,
                           score_scale, topk, q0, q1, sel, cnt, workspace, ws_bytes, stream);
+}
+
+int irb_route_topk_fused_raw(const irb_layout* layout, const void* q_raw, int dtype, int H_idx, int D_idx,
+                             const float* gamma, float eps, const float* rope, int D_rope, const float* w,
+                             const float* kc, const int32_t* cu_blocks, int c, float score_scale, int topk, int q0,
+                             int q1, int32_t* sel, int32_t* cnt, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "irb_route_topk_fused_raw";
+  if (!gamma || (reinterpret_cast<uintptr_t>(gamma) & 15)) return fail(IRB_ERR_INVALID, "%s: gamma must be a 16-byte aligned fp32 [D_idx] tensor", fn);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(IRB_ERR_INVALID, "%s: eps must be finite and >= 0", fn);
+  if (!irb::score_prep_ok(D_idx, D_rope))
+    return fail(IRB_ERR_INVALID, "%s: D_rope must be 0 or a multiple of 64 up to D_idx (got %d, D_idx %d)", fn, D_rope, D_idx);
+  if (D_rope > 0 && (!rope || (reinterpret_cast<uintptr_t>(rope) & 15)))
+    return fail(IRB_ERR_INVALID, "%s: rope must be a 16-byte aligned fp32 [B, S, D_rope] tensor", fn);
+  irb::QPrep prep;
+  prep.gamma = gamma;
+  prep.rope = D_rope > 0 ? rope : nullptr;
+  prep.eps = eps;
+  prep.R = D_rope;
+  return route_fused_impl(fn, layout, q_raw, dtype, 1, H_idx, D_idx, w, kc, cu_blocks, c, score_scale, topk, q0, q1,
+                          sel, cnt, workspace, ws_bytes, stream, false, prep);
 }
 
 int irb_route_topk_fused_noalloc(const irb_layout* layout, const void* q_idx, int dtype, int H_idx, int D_idx,

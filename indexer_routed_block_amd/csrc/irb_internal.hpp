@@ -23,10 +23,22 @@ int launch_prep_queries(const void* q, int dtype, int64_t n_rows, int H, int D, 
 // direct global-to-LDS loads instead of being split while staging.
 // n_grp: index queries [B, S, n_grp, H, D] and weights [B, S, n_grp, H] with
 // q and w pointing at one group's heads (1: [B, S, H, D] and [B, S, H])
+// Index-query preparation applied by the score kernel as it loads raw
+// queries (gamma == nullptr: the queries are used as they are).  Same
+// arithmetic as launch_prep_queries, so the scores equal those of prepared
+// queries; needs R == 0 or R a multiple of 64 up to D (each lane then holds
+// the rotation partners of its own dimensions).
+struct QPrep {
+  const float* gamma = nullptr;
+  const float* rope = nullptr;   // [B * S, R] rotary rows
+  float eps = 0.f;
+  int R = 0;
+};
+bool score_prep_ok(int D, int R);
 int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
                       const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,
                       int q0, int q1, int j0, int j1, float* out, int64_t out_stride, int write_invisible,
-                      int skip_nb, int n_grp, hipStream_t stream);
+                      int skip_nb, int n_grp, hipStream_t stream, const QPrep& prep = QPrep{});
 // All groups of 4 or 8 heads in one launch (bf16 queries [B, S, groups,
 // H_group, D], weights [B, S, groups, H_group], groups * H_group in {16, 32},
 // D in {64, 128}): group g's tile at out + g * group_stride, each laid out as

@@ -127,9 +127,11 @@ prep_queries_kernel(const T* q, int64_t n_rows, int H, const float* __restrict__
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t row = row0 + u * RPW;
+    // the sum of squares and the rotation are written as explicit fmas so
+    // that the scoring kernel's fused preparation rounds identically
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) ss += x[u][e] * x[u][e];
+    for (int e = 0; e < EPL; ++e) ss = fmaf(x[u][e], x[u][e], ss);
 #pragma unroll
     for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
@@ -140,7 +142,7 @@ prep_queries_kernel(const T* q, int64_t n_rows, int H, const float* __restrict__
       // D_rope = D and D_rope / 2 a power-of-two multiple of EPL: the partner
       // of dim d (d +- D/2) is element e of lane lane ^ xor_partner
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) y[e] = x[u][e] * cs[u][e] + __shfl_xor(x[u][e], xor_partner, 64) * sn[u][e];
+      for (int e = 0; e < EPL; ++e) y[e] = fmaf(x[u][e], cs[u][e], __shfl_xor(x[u][e], xor_partner, 64) * sn[u][e]);
     } else {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) stage[wid][lane * EPL + e] = x[u][e];
@@ -150,7 +152,7 @@ prep_queries_kernel(const T* q, int64_t n_rows, int H, const float* __restrict__
       for (int e = 0; e < EPL; ++e) {
         const int d = li * EPL + e;
         const int pd = d < half ? d + half : (d < R ? d - half : d);   // rotation partner (itself past R)
-        y[e] = x[u][e] * cs[u][e] + mine[pd] * sn[u][e];
+        y[e] = fmaf(x[u][e], cs[u][e], mine[pd] * sn[u][e]);
       }
       wave_lds_sync();                            // the stage is rewritten by the next group
     }

@@ -45,6 +45,124 @@ IRB_DEV void load_q_operand<float>(const float* p, bf16x8& hi, bf16x8& lo) {
   }
 }
 
+// Index-query preparation fused into the q loads (QSA page: the indexer's
+// q_layernorm and apply_qsa_rope, consumed by select_qsa_token_ids).  This
+// lane holds dimensions 32 s + 8 g16 + e (s < D / 32, e < 8) of its row; the
+// four lanes g16 = 0..3 of a row together hold all of it.  The arithmetic
+// is that of the preparation kernel step for step, so the operands equal
+// the prepared queries exactly: per-chunk sums of squares (that kernel's
+// chunks of EPL dimensions, fmas in dimension order), the same pairwise
+// tree over chunks (a chunk pairs with chunk ^ o, o = chunks / 2 .. 1), the
+// same reciprocal square root, gain and fma rotation, one rounding to QT.
+// The rotation partner d +- R / 2 of a dimension sits in this lane's own
+// registers because R / 2 is a multiple of 32.
+template <typename QT, int D>
+IRB_DEV void prep_q_operands(const QT* qp, const float* rope_row, int g16, const QPrep& pp, const float (&gm)[D / 32][8],
+                             bf16x8 (&qh)[D / 32], bf16x8 (&ql)[D / 32]) {
+  constexpr int KS = D / 32;
+  constexpr int EPL = sizeof(QT) == 2 ? 8 : 4;   // the preparation kernel's dimensions per lane (D <= 128)
+  constexpr int HPL = 8 / EPL;                   // its chunks per run of 8 dimensions here
+  constexpr int LPR = D / EPL;                   // its chunks per row
+  const int R = pp.R, half = R / 2;
+  // every load first (raw row, rotary factors), so their latencies overlap;
+  // runs past R read the gain row instead (a valid address) and discard it
+  float x[KS][8], cs[KS][8], sn[KS][8];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if constexpr (sizeof(QT) == 2) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[s][e] = bf16_to_f32(static_cast<uint16_t>(v[e]));
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * s);
+      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * s + 4);
+      x[s][0] = a.x; x[s][1] = a.y; x[s][2] = a.z; x[s][3] = a.w;
+      x[s][4] = c.x; x[s][5] = c.y; x[s][6] = c.z; x[s][7] = c.w;
+    }
+    const int d0 = 32 * s + 8 * g16;
+    const bool rot = d0 < R;
+    const int j0 = d0 < half ? d0 : d0 - half;
+    const float* cp = rot ? rope_row + j0 : pp.gamma;
+    const float* sp = rot ? rope_row + half + j0 : pp.gamma;
+    const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
+    const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
+    const float sg = d0 < half ? -1.f : 1.f;
+    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      cs[s][e] = rot ? cv[e] : 1.f;
+      sn[s][e] = rot ? sg * sv[e] : 0.f;
+    }
+  }
+  // chunk (s, h) is the preparation kernel's chunk (4 s + g16) HPL + h
+  float p[KS][HPL];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int h = 0; h < HPL; ++h) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a = fmaf(x[s][h * EPL + e], x[s][h * EPL + e], a);
+      p[s][h] = a;
+    }
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) {
+    if (o < HPL) {                               // the other half of this lane's run
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float a = p[s][0], c = p[s][HPL - 1];
+        p[s][0] = a + c;
+        p[s][HPL - 1] = c + a;
+      }
+    } else if (o < 4 * HPL) {                    // the same run in lane group g16 ^ (o / HPL)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int h = 0; h < HPL; ++h) p[s][h] += __shfl_xor(p[s][h], 16 * (o / HPL), 64);
+    } else {                                     // run s ^ (o / (4 HPL)) of this lane
+      float n[KS][HPL];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int h = 0; h < HPL; ++h) n[s][h] = p[s][h] + p[s ^ (o / (4 * HPL))][h];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int h = 0; h < HPL; ++h) p[s][h] = n[s][h];
+    }
+  }
+  const float inv = 1.0f / sqrtf(p[0][0] / static_cast<float>(D) + pp.eps);
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[s][e] = x[s][e] * inv * gm[s][e];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int d0 = 32 * s + 8 * g16;
+    // the rotation partner run (itself past R, where the sine factor is 0)
+    const int ps = d0 < half ? s + half / 32 : (d0 < R ? s - half / 32 : s);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float pv = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) pv = s2 == ps ? x[s2][e] : pv;
+      const float y = fmaf(x[s][e], cs[s][e], pv * sn[s][e]);
+      if constexpr (sizeof(QT) == 2) {
+        qh[s][e] = static_cast<short>(f32_to_bf16(y));
+      } else {
+        uint16_t h, l;
+        split_bf16(y, h, l);
+        qh[s][e] = static_cast<short>(h);
+        ql[s][e] = static_cast<short>(l);
+      }
+    }
+  }
+}
+
+// gamma and the rotary rows are read 16 bytes at a time (16-byte aligned)
+bool score_prep_ok(int D, int R) { return R == 0 || (R > 0 && R % 64 == 0 && R <= D); }
+
 // Row tiles (16 rows each) of q held per wave, always whole queries.  FP32
 // queries (hi/lo operands) and 4-head queries keep two at D = 128 so that
 // their operands fit in registers.  (Eight row tiles halve the LDS key reads
@@ -79,7 +197,7 @@ __global__ void __launch_bounds__(256, 2)
 score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, const float* __restrict__ kc,
              const uint16_t* __restrict__ kcs, const int32_t* __restrict__ cu_blocks, int c, float scale, int q0,
              int q1, int j0, int j1, float* __restrict__ out, int64_t ostride, int seg_blocks, int n_seg,
-             int write_invisible, int skip_nb, int n_grp, int64_t gstride) {
+             int write_invisible, int skip_nb, int n_grp, int64_t gstride, QPrep prep) {
   static_assert(GS == 0 || ((GS == 4 || GS == 8) && H % 16 == 0), "grouped scores: groups of 4 or 8 heads, H a multiple of 16");
   constexpr int NGRP = GS ? H / GS : 1;             // score tiles written
   constexpr bool kPerQ = H < 16 || GS > 0;          // visible ranges kept per query (wave-uniform)
@@ -149,19 +267,35 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   // q rows and weights are [.., S, n_grp, H, ..]: q and w point at this
   // call's group, one token holds n_grp groups of H heads (1: no group axis)
   const int64_t qrow = static_cast<int64_t>(n_grp) * H * D;
+  // gain of this lane's dimensions (fused preparation only)
+  float gm[KS][8];
+  if (prep.gamma) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float4 g0 = *reinterpret_cast<const float4*>(prep.gamma + 32 * s + 8 * g16);
+      const float4 g1 = *reinterpret_cast<const float4*>(prep.gamma + 32 * s + 8 * g16 + 4);
+      gm[s][0] = g0.x; gm[s][1] = g0.y; gm[s][2] = g0.z; gm[s][3] = g0.w;
+      gm[s][4] = g1.x; gm[s][5] = g1.y; gm[s][6] = g1.z; gm[s][7] = g1.w;
+    }
+  }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int rr = 16 * rt + l16;
     const int qi = qa + wid * QW + rr / H, hd = rr % H;
     const bool ok = qi < qe;
-    const QT* qp = q + (static_cast<int64_t>(b) * L.S + (ok ? qi : qa)) * qrow + static_cast<int64_t>(hd) * D + 8 * g16;
+    const int64_t tok = static_cast<int64_t>(b) * L.S + (ok ? qi : qa);
+    const QT* qp = q + tok * qrow + static_cast<int64_t>(hd) * D + 8 * g16;
+    if (prep.gamma) {
+      prep_q_operands<QT, D>(qp, prep.rope + tok * prep.R, g16, prep, gm, qh[rt], ql[rt]);
+    } else {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      load_q_operand<QT>(qp + 32 * s, qh[rt][s], ql[rt][s]);
-      if (!ok) {
+      for (int s = 0; s < KS; ++s) load_q_operand<QT>(qp + 32 * s, qh[rt][s], ql[rt][s]);
+    }
+    if (!ok) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) { qh[rt][s][e] = 0; if (kSplitQ) ql[rt][s][e] = 0; }
-      }
     }
     // head weights of this lane's accumulator rows 16 rt + 4 g16 + i
 #pragma unroll
@@ -421,7 +555,7 @@ template <typename QT, int D, int GS = 0>
 static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, const float* kc, const uint16_t* kcs,
                           const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0, int j1, float* out,
                           int64_t ostride, int write_invisible, int skip_nb, int n_grp, hipStream_t stream,
-                          int64_t gstride = 0) {
+                          int64_t gstride = 0, const QPrep& prep = QPrep{}) {
   // one segment per row: measured on MI355X with bf16 queries, splitting rows
   // into segments of 512..1024 blocks was slower at S = 8192 and S = 131072
   // (each segment repeats the q-row loads and the pipeline fill), and the
@@ -441,11 +575,11 @@ static int launch_score_d(const Layout& L, const QT* q, int H, const float* w, c
     if (kcs)                                                                                                 \
       hipLaunchKernelGGL((score_kernel<QT, D, HH, true, GS>), grid_for(score_rt<QT, D, HH, true>(), HH),    \
                          dim3(256), 0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out,    \
-                         ostride, seg, n_seg, write_invisible, skip_nb, n_grp, gstride);                      \
+                         ostride, seg, n_seg, write_invisible, skip_nb, n_grp, gstride, prep);                \
     else                                                                                                     \
       hipLaunchKernelGGL((score_kernel<QT, D, HH, false, GS>), grid_for(score_rt<QT, D, HH, false>(), HH),  \
                          dim3(256), 0, stream, L, q, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out,    \
-                         ostride, seg, n_seg, write_invisible, skip_nb, n_grp, gstride);                      \
+                         ostride, seg, n_seg, write_invisible, skip_nb, n_grp, gstride, prep);                \
     return 0;
   if constexpr (GS > 0) {
     switch (H) {
@@ -471,11 +605,11 @@ template <typename QT>
 static int launch_score_t(const Layout& L, const QT* q, int H, int D, const float* w, const float* kc,
                           const uint16_t* kcs, const int32_t* cu_blocks, int c, float scale, int q0, int q1, int j0,
                           int j1, float* out, int64_t ostride, int write_invisible, int skip_nb, int n_grp,
-                          hipStream_t stream) {
+                          hipStream_t stream, const QPrep& prep) {
   switch (D) {
-    case 32: return launch_score_d<QT, 32>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream);
-    case 64: return launch_score_d<QT, 64>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream);
-    case 128: return launch_score_d<QT, 128>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream);
+    case 32: return launch_score_d<QT, 32>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream, 0, prep);
+    case 64: return launch_score_d<QT, 64>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream, 0, prep);
+    case 128: return launch_score_d<QT, 128>(L, q, H, w, kc, kcs, cu_blocks, c, scale, q0, q1, j0, j1, out, ostride, write_invisible, skip_nb, n_grp, stream, 0, prep);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
@@ -495,12 +629,13 @@ int launch_split_keys(const float* kc, uint16_t* kcs, int64_t n_blocks, int D, h
 int launch_score_tile(const Layout& L, const void* q, int dtype, int H, int D, const float* w,
                       const float* kc, const uint16_t* kc_split, const int32_t* cu_blocks, int c, float scale,
                       int q0, int q1, int j0, int j1, float* out, int64_t out_stride, int write_invisible,
-                      int skip_nb, int n_grp, hipStream_t stream) {
+                      int skip_nb, int n_grp, hipStream_t stream, const QPrep& prep) {
+  if (prep.gamma && !score_prep_ok(D, prep.R)) return static_cast<int>(hipErrorInvalidValue);
   if (dtype == IRB_BF16)
     return launch_score_t(L, static_cast<const uint16_t*>(q), H, D, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0,
-                          j1, out, out_stride, write_invisible, skip_nb, n_grp, stream);
+                          j1, out, out_stride, write_invisible, skip_nb, n_grp, stream, prep);
   return launch_score_t(L, static_cast<const float*>(q), H, D, w, kc, kc_split, cu_blocks, c, scale, q0, q1, j0, j1,
-                        out, out_stride, write_invisible, skip_nb, n_grp, stream);
+                        out, out_stride, write_invisible, skip_nb, n_grp, stream, prep);
 }
 
 bool score_grouped_ok(int dtype, int groups, int H_group, int D) {

@@ -224,6 +224,34 @@ def test_prepare_index_queries_validation():
     assert call(n=0)[0] == 0          # nothing to do: no device call
 
 
+def test_route_raw_validation():
+    """The fused-preparation route checks the preparation arguments on the host
+    before the route arguments; a valid call stops at the device check."""
+    lib = irb.load_library()
+    lay = _layout(S=8192)
+    call = lambda g=FAKE, eps=1e-5, r=FAKE, R=128, D=128: _err(lib.irb_route_topk_fused_raw(
+        ctypes.byref(lay), FAKE, 1, 16, D, g, eps, r, R, FAKE, FAKE, None, 4, 0.0, 512, 0, 8192, FAKE, FAKE, FAKE,
+        1 << 24, None))
+    s, m = call(g=None)
+    assert s == 3 and "gamma" in m
+    s, m = call(g=ctypes.c_void_p(0x1004))
+    assert s == 3 and "gamma" in m
+    s, m = call(eps=-1.0)
+    assert s == 3 and "eps" in m
+    for R in (32, 96, 256):              # not a multiple of 64 up to D_idx
+        s, m = call(R=R)
+        assert s == 3 and "D_rope" in m
+    s, m = call(R=128, D=64)
+    assert s == 3 and "D_rope" in m
+    s, m = call(r=None)
+    assert s == 3 and "rope" in m
+    s, m = call(r=ctypes.c_void_p(0x1008))
+    assert s == 3 and "rope" in m
+    assert call()[0] == 1                # valid: stops at the device check (no GPU here)
+    assert call(r=None, R=0)[0] == 1     # no rotation: the table is not needed
+    assert call(R=64)[0] == 1            # partial rotation
+
+
 def test_pack_region_bitmap_validation():
     lib = irb.load_library()
     call = lambda ids=FAKE, rows=4, slots=8, regions=100, out=FAKE: _err(

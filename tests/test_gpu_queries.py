@@ -16,28 +16,9 @@ import torch
 import indexer_routed_block_amd as irb
 import oracle
 import synth
-from gpu_util import banner, host, to_dev
+from gpu_util import banner, host, prep_term_bound as _term_bound, rne_bf16 as _rne_bf16, to_dev
 
 pytestmark = pytest.mark.gpu
-
-
-def _rne_bf16(y):
-    """Round float64 values to the nearest bf16 (8 significant bits), ties to even."""
-    f, e = np.frexp(y)                      # y = f 2^e, |f| in [0.5, 1)
-    return np.ldexp(np.rint(f * 256.0), e - 8)
-
-
-def _term_bound(q, gamma, freqs, d_rope):
-    """E per element: 2^-20 times the summed magnitudes of the combined terms."""
-    u = np.abs(oracle.prepare_index_queries(q, gamma, freqs, 1e-5, d_rope=0))
-    mag = u.copy()
-    h = d_rope // 2
-    if h:
-        cos = np.abs(freqs[..., :h])[:, :, None, :]
-        sin = np.abs(freqs[..., h:2 * h])[:, :, None, :]
-        mag[..., :h] = u[..., :h] * cos + u[..., h:2 * h] * sin
-        mag[..., h:2 * h] = u[..., h:2 * h] * cos + u[..., :h] * sin
-    return 2.0 ** -20 * (mag + 1e-30)
 
 
 def _check_bf16(got, ref, bound):
