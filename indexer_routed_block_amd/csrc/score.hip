@@ -64,6 +64,9 @@ IRB_DEV void prep_q_operands(const QT* qp, const float* rope_row, int g16, const
   constexpr int HPL = 8 / EPL;                   // its chunks per run of 8 dimensions here
   constexpr int LPR = D / EPL;                   // its chunks per row
   const int R = pp.R, half = R / 2;
+  // full-width rotation (the usual case): run s pairs with run s ^ (KS / 2)
+  // and both use the same table entries
+  const bool full = R == D;
   // every load first (raw row, rotary factors), so their latencies overlap;
   // runs past R read the gain row instead (a valid address) and discard it
   float x[KS][8], cs[KS][8], sn[KS][8];
@@ -79,20 +82,45 @@ IRB_DEV void prep_q_operands(const QT* qp, const float* rope_row, int g16, const
       x[s][0] = a.x; x[s][1] = a.y; x[s][2] = a.z; x[s][3] = a.w;
       x[s][4] = c.x; x[s][5] = c.y; x[s][6] = c.z; x[s][7] = c.w;
     }
-    const int d0 = 32 * s + 8 * g16;
-    const bool rot = d0 < R;
-    const int j0 = d0 < half ? d0 : d0 - half;
-    const float* cp = rot ? rope_row + j0 : pp.gamma;
-    const float* sp = rot ? rope_row + half + j0 : pp.gamma;
-    const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
-    const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
-    const float sg = d0 < half ? -1.f : 1.f;
-    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  }
+  if (full) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      cs[s][e] = rot ? cv[e] : 1.f;
-      sn[s][e] = rot ? sg * sv[e] : 0.f;
+    for (int s = 0; s < (KS > 1 ? KS / 2 : 1); ++s) {
+      const int j0 = 32 * s + 8 * g16;
+      const float4 c0 = *reinterpret_cast<const float4*>(rope_row + j0);
+      const float4 c1 = *reinterpret_cast<const float4*>(rope_row + j0 + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(rope_row + half + j0);
+      const float4 s1 = *reinterpret_cast<const float4*>(rope_row + half + j0 + 4);
+      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cs[s][e] = cv[e];
+        sn[s][e] = -sv[e];
+        if (KS > 1) {
+          cs[(s + KS / 2) % KS][e] = cv[e];
+          sn[(s + KS / 2) % KS][e] = sv[e];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int d0 = 32 * s + 8 * g16;
+      const bool rot = d0 < R;
+      const int j0 = d0 < half ? d0 : d0 - half;
+      const float* cp = rot ? rope_row + j0 : pp.gamma;
+      const float* sp = rot ? rope_row + half + j0 : pp.gamma;
+      const float4 c0 = *reinterpret_cast<const float4*>(cp), c1 = *reinterpret_cast<const float4*>(cp + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(sp), s1 = *reinterpret_cast<const float4*>(sp + 4);
+      const float sg = d0 < half ? -1.f : 1.f;
+      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cs[s][e] = rot ? cv[e] : 1.f;
+        sn[s][e] = rot ? sg * sv[e] : 0.f;
+      }
     }
   }
   // chunk (s, h) is the preparation kernel's chunk (4 s + g16) HPL + h
@@ -137,6 +165,7 @@ IRB_DEV void prep_q_operands(const QT* qp, const float* rope_row, int g16, const
   for (int s = 0; s < KS; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[s][e] = x[s][e] * inv * gm[s][e];
+  // the partner of run s: run s ^ (KS / 2) for a full-width rotation, else picked at run time
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int d0 = 32 * s + 8 * g16;
@@ -144,9 +173,11 @@ IRB_DEV void prep_q_operands(const QT* qp, const float* rope_row, int g16, const
     const int ps = d0 < half ? s + half / 32 : (d0 < R ? s - half / 32 : s);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float pv = 0.f;
+      float pv = x[KS > 1 ? s ^ (KS / 2) : s][e];
+      if (!full) {
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) pv = s2 == ps ? x[s2][e] : pv;
+        for (int s2 = 0; s2 < KS; ++s2) pv = s2 == ps ? x[s2][e] : pv;
+      }
       const float y = fmaf(x[s][e], cs[s][e], pv * sn[s][e]);
       if constexpr (sizeof(QT) == 2) {
         qh[s][e] = static_cast<short>(f32_to_bf16(y));
@@ -261,6 +292,48 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
   }
   if (cb >= ce) return;
 
+  // pre-split chunk loader: lane i of load n fills 16-byte slot (w NI + n) 64 + i;
+  // row R = 2 block + (0 hi | 1 lo), chunk slot sc holds chunk sc ^ ((R / 2) mod NC).
+  // The chunk's first block gives a wave-uniform base address (scalar
+  // registers); the per-lane byte offsets from it are fixed for the whole
+  // launch, and only a chunk reaching past the last block clamps its rows.
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  uint32_t poff[kPre ? NI : 1];
+  if constexpr (kPre) {
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int slot = (wu * NI + n) * 64 + lane;
+      const int R = slot / NC, sc = slot % NC;
+      poff[n] = static_cast<uint32_t>(R * D + 8 * (sc ^ ((R >> 1) & (NC - 1)))) * 2u;
+    }
+  }
+  const uint32_t klds = lds_addr(kraw);
+  auto issue = [&](int j, int pbuf) __attribute__((always_inline)) {
+    j = __builtin_amdgcn_readfirstlane(j);
+    pbuf = __builtin_amdgcn_readfirstlane(pbuf);
+    const uint32_t lb = klds + pbuf * PBUF + wu * NI * 1024;
+    if (j + CH <= nb_max) {
+      const uint16_t* sb = kcs + (static_cast<int64_t>(b) * nb_max + j) * 2 * D;
+#pragma unroll
+      for (int n = 0; n < NI; ++n) lds_dma16_s(sb, poff[n], lb + n * 1024);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int slot = (wu * NI + n) * 64 + lane;
+        const int R = slot / NC, sc = slot % NC;
+        const int blk = min(j + (R >> 1), nb_max - 1);
+        const uint16_t* src = kcs + ((static_cast<int64_t>(b) * nb_max + blk) * 2 + (R & 1)) * D +
+                              8 * (sc ^ ((R >> 1) & (NC - 1)));
+        lds_dma16(src, lb + n * 1024);
+      }
+    }
+  };
+  // the first chunks' loads go out before the q rows are loaded (and prepared)
+  const int nch = (ce - cb + CH - 1) / CH;
+  if constexpr (kPre) {
+    for (int p = 0; p < NBUF - 1 && p < nch; ++p) issue(cb + p * CH, p);
+  }
+
   // q rows of this wave in the A layout: row 16 rt + l16 -> query rr / H, head rr % H
   bf16x8 qh[RT][KS], ql[RT][KS];
   float wv[RT][4];
@@ -341,42 +414,6 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
     }
   };
 
-  // pre-split chunk loader: lane i of load n fills 16-byte slot (w NI + n) 64 + i;
-  // row R = 2 block + (0 hi | 1 lo), chunk slot sc holds chunk sc ^ ((R / 2) mod NC).
-  // The chunk's first block gives a wave-uniform base address (scalar
-  // registers); the per-lane byte offsets from it are fixed for the whole
-  // launch, and only a chunk reaching past the last block clamps its rows.
-  const int wu = __builtin_amdgcn_readfirstlane(wid);
-  uint32_t poff[kPre ? NI : 1];
-  if constexpr (kPre) {
-#pragma unroll
-    for (int n = 0; n < NI; ++n) {
-      const int slot = (wu * NI + n) * 64 + lane;
-      const int R = slot / NC, sc = slot % NC;
-      poff[n] = static_cast<uint32_t>(R * D + 8 * (sc ^ ((R >> 1) & (NC - 1)))) * 2u;
-    }
-  }
-  const uint32_t klds = lds_addr(kraw);
-  auto issue = [&](int j, int pbuf) __attribute__((always_inline)) {
-    j = __builtin_amdgcn_readfirstlane(j);
-    pbuf = __builtin_amdgcn_readfirstlane(pbuf);
-    const uint32_t lb = klds + pbuf * PBUF + wu * NI * 1024;
-    if (j + CH <= nb_max) {
-      const uint16_t* sb = kcs + (static_cast<int64_t>(b) * nb_max + j) * 2 * D;
-#pragma unroll
-      for (int n = 0; n < NI; ++n) lds_dma16_s(sb, poff[n], lb + n * 1024);
-    } else {
-#pragma unroll
-      for (int n = 0; n < NI; ++n) {
-        const int slot = (wu * NI + n) * 64 + lane;
-        const int R = slot / NC, sc = slot % NC;
-        const int blk = min(j + (R >> 1), nb_max - 1);
-        const uint16_t* src = kcs + ((static_cast<int64_t>(b) * nb_max + blk) * 2 + (R & 1)) * D +
-                              8 * (sc ^ ((R >> 1) & (NC - 1)));
-        lds_dma16(src, lb + n * 1024);
-      }
-    }
-  };
   // visible ranges of the wave's queries in registers (the stores test them every tile)
   int my_vb = 0, my_vn = 0;
   bool my_q = false;
@@ -395,10 +432,7 @@ score_kernel(Layout L, const QT* __restrict__ q, const float* __restrict__ w, co
       vnk[k] = __builtin_amdgcn_readfirstlane(s_vis[1][wid * QW + k]);
     }
   }
-  const int nch = (ce - cb + CH - 1) / CH;
-  if constexpr (kPre) {
-    for (int p = 0; p < NBUF - 1 && p < nch; ++p) issue(cb + p * CH, p);
-  } else {
+  if constexpr (!kPre) {
     gload(cb);
     lstore(0);
     __syncthreads();
