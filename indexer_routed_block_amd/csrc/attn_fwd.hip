@@ -548,7 +548,7 @@ template <int D, int DV, int G, bool kDelta>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__ lse, const uint16_t* __restrict__ dout,
                      float* __restrict__ delta, int n_qt, int thr_milli, const uint32_t* __restrict__ qbits,
-                     int qwords) {
+                     int qwords, int gather_rest) {
   using T = uint16_t;
   constexpr int BQ = 128 / G;
   constexpr int KS = D / 16;          // 16-dim k-steps of S^T = K Q^T
@@ -587,7 +587,17 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   const int b = bid / (a.Hkv * n_qt);
   const int qa = qt * BQ;
   const TileStats ts = tile_stats_wave(a, b, kvh, qa, BQ, thr_milli);
-  if (!ts.dense) return;
+  if (!ts.dense) {
+    // a sparse tile is the gather kernel's, or, when this launch takes every
+    // tile (gather_rest), gathered here: wave w takes queries w, w + 4, ...
+    // with its own slab of the (so far unused) K/V slots
+    if (!gather_rest) return;
+    char* slab = raw + wid * 32 * (DV + 8) * 2;
+    static_assert(4 * 32 * (DV + 8) * 2 <= 3 * BUF, "gather slabs");
+    for (int q = wid; q < BQ; q += 4)
+      if (qa + q < a.S_q) fwd_item_gather<D, DV, kDelta>(a, out, lse, G, dout, delta, b, qa + q, kvh, slab);
+    return;
+  }
 
   const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
   const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
@@ -1034,13 +1044,13 @@ static int tile_thr_milli() {
 
 template <int D, int DV, int G, bool kDelta>
 static void launch_tile(const AttnArgs& a, void* out, float* lse, const void* dout, float* delta,
-                        const uint32_t* qbits, int qwords, hipStream_t stream) {
+                        const uint32_t* qbits, int qwords, int gather_rest, hipStream_t stream) {
   constexpr int BQ = 128 / G;
   const int n_qt = (a.S_q + BQ - 1) / BQ;
   const unsigned grid = static_cast<unsigned>(a.B) * n_qt * a.Hkv;
   hipLaunchKernelGGL((attn_fwd_tile_kernel<D, DV, G, kDelta>), dim3(grid), dim3(256), 0, stream, a,
                      static_cast<uint16_t*>(out), lse, static_cast<const uint16_t*>(dout), delta, n_qt,
-                     tile_thr_milli(), qbits, qwords);
+                     tile_thr_milli(), qbits, qwords, gather_rest);
 }
 
 // key-membership words per route row, built in the forward's workspace when
@@ -1081,9 +1091,14 @@ static int launch_fwd_t(const AttnArgs& a, void* out, float* lse, const void* do
         if (int rc = launch_route_bits(a.routes, a.lens, rows, a.L, a.S_k, static_cast<uint32_t*>(ws), stream)) return rc;
         qbits = static_cast<const uint32_t*>(ws);
       }
-      if (G == 4) launch_tile<D, DV, 4, kDelta>(a, out, lse, dout, delta, qbits, qwords, stream);
-      if (G == 8) launch_tile<D, DV, 8, kDelta>(a, out, lse, dout, delta, qbits, qwords, stream);
-      if (G == 16) launch_tile<D, DV, 16, kDelta>(a, out, lse, dout, delta, qbits, qwords, stream);
+      // routes at least thr/1000 of the key range wide: nearly every tile is
+      // dense, so the tile launch also gathers the few sparse ones itself and
+      // the per-query gather launch (one wave per query just to skip it) is saved
+      const bool gather_rest = static_cast<int64_t>(a.L) * 1000 >= static_cast<int64_t>(tile_thr_milli()) * a.S_k;
+      if (G == 4) launch_tile<D, DV, 4, kDelta>(a, out, lse, dout, delta, qbits, qwords, gather_rest, stream);
+      if (G == 8) launch_tile<D, DV, 8, kDelta>(a, out, lse, dout, delta, qbits, qwords, gather_rest, stream);
+      if (G == 16) launch_tile<D, DV, 16, kDelta>(a, out, lse, dout, delta, qbits, qwords, gather_rest, stream);
+      if (gather_rest) return 0;
       tile_bq = 128 / G;
     }
   }

@@ -40,37 +40,60 @@ bitmap_kernel(const int32_t* __restrict__ ids, int64_t rows, int slots, int regi
 
 // Key-membership words of ascending route rows with their lengths (the
 // forward's query-tile masks): only the first lens[row] entries count.  A
-// lane takes 8 consecutive entries; entries of one word are ORed together in
-// registers and the word takes one LDS atomic per run, so the long runs of
-// consecutive keys (selected blocks, windows) do not serialise on one word.
+// lane takes 8 consecutive entries of each 512-entry chunk; entries of one
+// word are ORed together in registers and the word takes one LDS atomic per
+// run, so the long runs of consecutive keys (selected blocks, windows) do not
+// serialise on one word.  Rows whose entries are 16-byte aligned (vec) are
+// read as int4 pairs, and the loads of up to kRbChunks chunks are issued
+// before any of their entries is used.
+constexpr int kRbChunks = 4;
+
+IRB_DEV void or_run8(uint32_t* bm, const int (&id)[8], int keys) {
+  uint32_t acc = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool ok = id[j] >= 0 && id[j] < keys;
+    acc |= ok ? 1u << (id[j] & 31) : 0u;
+    const int wd = ok ? id[j] >> 5 : -1;
+    const int nx = (j < 7 && id[j + 1] >= 0 && id[j + 1] < keys) ? id[j + 1] >> 5 : -2;
+    if (wd >= 0 && nx != wd) {
+      atomicOr(&bm[wd], acc);
+      acc = 0u;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kBmWaves * 64)
 route_bits_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int64_t rows, int L,
-                  int keys, int words, uint32_t* __restrict__ out) {
+                  int keys, int words, int vec, uint32_t* __restrict__ out) {
   extern __shared__ uint32_t rb_all[];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kBmWaves + wid;
   if (row >= rows) return;                       // whole wavefront; no workgroup barrier below
   uint32_t* bm = rb_all + wid * words;
   for (int w = lane; w < words; w += 64) bm[w] = 0u;
-  wave_lds_sync();
   const int32_t* r = routes + row * L;
   const int n = max(0, min(lens[row], L));
-  for (int e0 = 8 * lane; e0 < n; e0 += 512) {
-    int id[8];
+  wave_lds_sync();
+  for (int c0 = 0; c0 < n; c0 += 512 * kRbChunks) {
+    int id[kRbChunks][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) id[j] = e0 + j < n ? r[e0 + j] : -1;
-    uint32_t acc = 0u;
+    for (int u = 0; u < kRbChunks; ++u) {
+      const int e0 = c0 + 512 * u + 8 * lane;
+      if (vec && e0 + 8 <= L) {
+        // the row holds L entries: reading past n stays inside it
+        const int4 a = *reinterpret_cast<const int4*>(r + e0);
+        const int4 b = *reinterpret_cast<const int4*>(r + e0 + 4);
+        const int v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = id[j] >= 0 && id[j] < keys;
-      acc |= ok ? 1u << (id[j] & 31) : 0u;
-      const int wd = ok ? id[j] >> 5 : -1;
-      const int nx = (j < 7 && id[j + 1] >= 0 && id[j + 1] < keys) ? id[j + 1] >> 5 : -2;
-      if (wd >= 0 && nx != wd) {
-        atomicOr(&bm[wd], acc);
-        acc = 0u;
+        for (int j = 0; j < 8; ++j) id[u][j] = e0 + j < n ? v[j] : -1;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) id[u][j] = e0 + j < n ? r[e0 + j] : -1;
       }
     }
+#pragma unroll
+    for (int u = 0; u < kRbChunks; ++u) or_run8(bm, id[u], keys);
   }
   wave_lds_sync();
   uint32_t* o = out + row * words;
@@ -87,8 +110,9 @@ int launch_route_bits(const int32_t* routes, const int32_t* lens, int64_t rows, 
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return static_cast<int>(e);
   }
+  const int vec = (L % 4 == 0 && (reinterpret_cast<uintptr_t>(routes) & 15) == 0) ? 1 : 0;
   hipLaunchKernelGGL(route_bits_kernel, dim3(static_cast<unsigned>((rows + kBmWaves - 1) / kBmWaves)),
-                     dim3(kBmWaves * 64), lds, stream, routes, lens, rows, L, keys, words, bits);
+                     dim3(kBmWaves * 64), lds, stream, routes, lens, rows, L, keys, words, vec, bits);
   return 0;
 }
 

@@ -82,10 +82,14 @@ def test_tiny_fp32_pipeline_routes_fwd_bwd():
     _run_fwd_bwd(wl, x, routes, lens, 1.0 / math.sqrt(wl.D), True)
 
 
-@pytest.mark.parametrize("S,width,rev_bq", [(1024, 160, 1), (333, 70, 1), (1024, 160, 16), (333, 70, 3)])
+@pytest.mark.parametrize("S,width,rev_bq", [(1024, 160, 1), (333, 70, 1), (1024, 160, 16), (333, 70, 3),
+                                            (1024, 100, 1)])
 def test_gqa_bf16_random_routes_fwd_bwd(S, width, rev_bq):
     """rev_bq > 1: reverse lists of query tiles, whose queries the backward
-    searches for hits; rev_bq = 1: every listed query is a hit."""
+    searches for hits; rev_bq = 1: every listed query is a hit.  Routes at
+    least 0.12 S wide (160 of 1024, 70 of 333) take every query tile in the
+    query-tile launch, sparse tiles gathered there; narrower ones (100 of
+    1024) leave the sparse tiles to the per-query gather launch."""
     banner(f"attn gqa bf16 S={S} width={width} rev_bq={rev_bq}")
     wl, x = _qkv("varlen", S)
     routes, lens = _random_routes(S, 1, S, width, empty_rows=[(0, 5), (0, S - 1)])
