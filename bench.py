@@ -48,7 +48,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 FP32_VALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector (published)
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_s8192_hbm_traffic.json")
-FWD_SOURCE = os.path.join(ROOT, "indexer_routed_block_amd", "csrc", "attn_fwd.hip")
+# the forward call's kernels: route-bit packing and the attention kernels
+FWD_SOURCES = [os.path.join(ROOT, "indexer_routed_block_amd", "csrc", f) for f in ("attn_fwd.hip", "bitmap.hip")]
 
 
 def parse():
@@ -89,8 +90,11 @@ def _layout_counts(wl, S, cu):
 
 
 def _fwd_source_hash():
-    with open(FWD_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in FWD_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic():
@@ -441,7 +445,7 @@ def main():
                                      "window": wl.window}),
         },
         "roofline": {
-            "kernel": "sparse_gqa_attention_fwd (attn_fwd_tile_kernel + attn_fwd_kernel)",
+            "kernel": "sparse_gqa_attention_fwd (route_bits_kernel + attn_fwd_tile_kernel)",
             "bound": "mfma",
             "achieved": round(tflops, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS,
