@@ -7,46 +7,19 @@
 // and repeats are allowed.  Negative ids are padding here as well (the route
 // lists of this library pad with -1), and the rows need not be sorted.
 //
-// One wavefront per row: the row's words live in the wave's LDS slice, every
-// valid id ORs its bit in with an LDS atomic, and the words are then written
-// out in one coalesced pass (zeros included), so no output clearing pass is
-// needed.
+// One wavefront per row: the row's words live in the wave's LDS slice; a
+// lane takes 8 consecutive ids of each 512-id chunk (16-byte loads when the
+// rows are 16-byte aligned), ORs the bits of ids that share a word in
+// registers and sets each run's word with one LDS atomic, so sorted rows
+// (consecutive ids in one or two words) need few atomics.  The words are
+// then written out in one coalesced pass (zeros included), so no output
+// clearing pass is needed.
 #include "irb_internal.hpp"
 
 namespace irb {
 
 constexpr int kBmWaves = 4;
-
-__global__ void __launch_bounds__(kBmWaves * 64)
-bitmap_kernel(const int32_t* __restrict__ ids, int64_t rows, int slots, int regions, int words,
-              uint32_t* __restrict__ out) {
-  extern __shared__ uint32_t bm_all[];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kBmWaves + wid;
-  if (row >= rows) return;                       // whole wavefront; no workgroup barrier below
-  uint32_t* bm = bm_all + wid * words;
-  for (int w = lane; w < words; w += 64) bm[w] = 0u;
-  wave_lds_sync();
-  const int32_t* r = ids + row * slots;
-#pragma unroll 4
-  for (int e = lane; e < slots; e += 64) {
-    const int x = r[e];
-    if (x >= 0 && x < regions) atomicOr(&bm[x >> 5], 1u << (x & 31));
-  }
-  wave_lds_sync();
-  uint32_t* o = out + row * words;
-  for (int w = lane; w < words; w += 64) o[w] = bm[w];
-}
-
-// Key-membership words of ascending route rows with their lengths (the
-// forward's query-tile masks): only the first lens[row] entries count.  A
-// lane takes 8 consecutive entries of each 512-entry chunk; entries of one
-// word are ORed together in registers and the word takes one LDS atomic per
-// run, so the long runs of consecutive keys (selected blocks, windows) do not
-// serialise on one word.  Rows whose entries are 16-byte aligned (vec) are
-// read as int4 pairs, and the loads of up to kRbChunks chunks are issued
-// before any of their entries is used.
-constexpr int kRbChunks = 4;
+constexpr int kRbChunks = 4;   // 512-entry chunks whose loads are issued together
 
 IRB_DEV void or_run8(uint32_t* bm, const int (&id)[8], int keys) {
   uint32_t acc = 0u;
@@ -63,6 +36,48 @@ IRB_DEV void or_run8(uint32_t* bm, const int (&id)[8], int keys) {
   }
 }
 
+__global__ void __launch_bounds__(kBmWaves * 64)
+bitmap_kernel(const int32_t* __restrict__ ids, int64_t rows, int slots, int regions, int words, int vec,
+              uint32_t* __restrict__ out) {
+  extern __shared__ uint32_t bm_all[];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kBmWaves + wid;
+  if (row >= rows) return;                       // whole wavefront; no workgroup barrier below
+  uint32_t* bm = bm_all + wid * words;
+  for (int w = lane; w < words; w += 64) bm[w] = 0u;
+  const int32_t* r = ids + row * slots;
+  wave_lds_sync();
+  for (int c0 = 0; c0 < slots; c0 += 512 * kRbChunks) {
+    int id[kRbChunks][8];
+#pragma unroll
+    for (int u = 0; u < kRbChunks; ++u) {
+      const int e0 = c0 + 512 * u + 8 * lane;
+      if (vec && e0 + 8 <= slots) {
+        const int4 a = *reinterpret_cast<const int4*>(r + e0);
+        const int4 b = *reinterpret_cast<const int4*>(r + e0 + 4);
+        id[u][0] = a.x; id[u][1] = a.y; id[u][2] = a.z; id[u][3] = a.w;
+        id[u][4] = b.x; id[u][5] = b.y; id[u][6] = b.z; id[u][7] = b.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) id[u][j] = e0 + j < slots ? r[e0 + j] : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRbChunks; ++u) or_run8(bm, id[u], regions);
+  }
+  wave_lds_sync();
+  uint32_t* o = out + row * words;
+  for (int w = lane; w < words; w += 64) o[w] = bm[w];
+}
+
+// Key-membership words of ascending route rows with their lengths (the
+// forward's query-tile masks): only the first lens[row] entries count.  A
+// lane takes 8 consecutive entries of each 512-entry chunk; entries of one
+// word are ORed together in registers and the word takes one LDS atomic per
+// run, so the long runs of consecutive keys (selected blocks, windows) do not
+// serialise on one word.  Rows whose entries are 16-byte aligned (vec) are
+// read as int4 pairs, and the loads of up to kRbChunks chunks are issued
+// before any of their entries is used.
 __global__ void __launch_bounds__(kBmWaves * 64)
 route_bits_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int64_t rows, int L,
                   int keys, int words, int vec, uint32_t* __restrict__ out) {
@@ -125,8 +140,9 @@ int launch_bitmap(const int32_t* ids, int64_t rows, int slots, int regions, int3
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return static_cast<int>(e);
   }
+  const int vec = (slots % 4 == 0 && (reinterpret_cast<uintptr_t>(ids) & 15) == 0) ? 1 : 0;
   hipLaunchKernelGGL(bitmap_kernel, dim3(static_cast<unsigned>((rows + kBmWaves - 1) / kBmWaves)),
-                     dim3(kBmWaves * 64), lds, stream, ids, rows, slots, regions, words,
+                     dim3(kBmWaves * 64), lds, stream, ids, rows, slots, regions, words, vec,
                      reinterpret_cast<uint32_t*>(bitmap));
   return 0;
 }

@@ -265,7 +265,8 @@ def test_select_long_rows(S, c, topk, ties):
 
 
 @pytest.mark.parametrize("rows,slots,regions,sort", [(300, 67, 70, True), (64, 512, 2048, True), (17, 1, 1, False),
-                                                     (40, 1000, 33, False), (9, 300, 131072, True), (5, 64, 4097, False)])
+                                                     (40, 1000, 33, False), (9, 300, 131072, True), (5, 64, 4097, False),
+                                                     (3, 4100, 5000, False), (4, 4100, 5000, True)])
 def test_pack_region_bitmap_bit_exact(rows, slots, regions, sort):
     """Sorted and unsorted rows with repeats, -1 and at-or-above-regions padding;
     word counts from 1 to 4096 (the LDS limit)."""
