@@ -867,12 +867,15 @@ bwd_scan_kernel(int64_t* __restrict__ v, int64_t n, int64_t cap, int64_t* __rest
 }
 
 // ---------------------------------------------------------------- dk / dv over hit lists
-template <int D, int DV>
+// GP > 0: the padded group size as a constant (4, 8, 16, 32: the row ->
+// (query, head) splits below become shifts and masks); 0: Gp_rt at run time
+template <int D, int DV, int GP>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
                      const int32_t* __restrict__ hit_t, const uint32_t* __restrict__ hit_m, int64_t cap, int G,
-                     int Gp, int nkt, int n_items, int merged) {
+                     int Gp_rt, int nkt, int n_items, int merged) {
   constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
+  const int Gp = GP > 0 ? GP : Gp_rt;
   // row pitches of the slabs: 8 dwords apart modulo 64 banks, so the 8-byte
   // words of 8 consecutive rows land in distinct banks
   constexpr int LQ = D + 16, LO = DV + 16;
@@ -936,6 +939,8 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
     int ta[2], ts[2];
     uint32_t tm[2];
   };
+  // (branch-free: entries past the list read its first entry, a valid
+  // address, and are then discarded)
   auto fetch = [&](int64_t e0_, int hb_, Ids& d) __attribute__((always_inline)) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -943,18 +948,23 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
       const int slot = Gp <= 32 ? r / Gp : 0;
       const int h = Gp <= 32 ? r % Gp : hb_ * 32 + r;
       const int64_t e = e0_ + slot;
-      int t = (e < h1 && h < G) ? hit_t[e] : -1;
+      const int tv = hit_t[e < h1 ? e : h0];
+      const int t = (e < h1 && h < G) ? tv : -1;
       d.ta[rt] = t < a.S_q ? t : -1;
       const int rs = 16 * rt + 4 * g16;
       const int64_t es = e0_ + (Gp <= 32 ? rs / Gp : 0);
-      int ts = es < h1 ? hit_t[es] : -1;
+      const int tsv = hit_t[es < h1 ? es : h0];
+      const uint32_t tmv = hit_m[es < h1 ? es : h0];
+      const int ts = es < h1 ? tsv : -1;
       d.ts[rt] = ts < a.S_q ? ts : -1;
-      d.tm[rt] = es < h1 ? hit_m[es] : 0u;
+      d.tm[rt] = es < h1 ? tmv : 0u;
     }
   };
   Ids cur;
   if (h0 < h1) fetch(h0, 0, cur);
   for (int64_t e0 = h0; e0 < h1; e0 += qpb) {
+    // every row of the batch a real (query, head): no row needs zeroing
+    const bool full = e0 + qpb <= h1 && G == Gp;
     for (int hb = 0; hb < bpq; ++hb) {
       // rows r = 16 rt + l16 of S and dP: Q and dO rows in the A layout
       bf16x8 qa[2][KS], oa[2][VS];
@@ -968,14 +978,14 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
         const uint16_t* qp = qg + b * a.sq_b + static_cast<int64_t>(tt) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
         const uint16_t* op = og + ((static_cast<int64_t>(b) * a.S_q + tt) * a.Hq + hh) * DV + 8 * g16;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          qa[rt][s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
-          if (t < 0) bzero8(qa[rt][s]);
-        }
+        for (int s = 0; s < KS; ++s) qa[rt][s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
 #pragma unroll
-        for (int s = 0; s < VS; ++s) {
-          oa[rt][s] = *reinterpret_cast<const bf16x8*>(op + 32 * s);
-          if (t < 0) bzero8(oa[rt][s]);
+        for (int s = 0; s < VS; ++s) oa[rt][s] = *reinterpret_cast<const bf16x8*>(op + 32 * s);
+        if (!full && t < 0) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) bzero8(qa[rt][s]);
+#pragma unroll
+          for (int s = 0; s < VS; ++s) bzero8(oa[rt][s]);
         }
       }
       // lse and Delta of the softmax rows 16 rt + 4 g16 + i (index 0 stands
@@ -1029,7 +1039,7 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
         for (int i = 0; i < 4; ++i) {
           const float pv = rok[rt][i] ? exp2f(sacc[rt][i] * sc2 - lsv[rt][i] * kLog2eB) : 0.f;
           p[rt][i] = pv;
-          ds[rt][i] = pv * (pacc[rt][i] - dlv[rt][i]);
+          ds[rt][i] = rok[rt][i] ? pv * (pacc[rt][i] - dlv[rt][i]) : 0.f;
         }
       bf16x8 ph, pl, sh, sl;
 #pragma unroll
@@ -1333,9 +1343,16 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 1,
                        ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
     if constexpr (kGqaHits) {
-      hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0,
-                         stream, args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt,
-                         static_cast<int>(kitems), merged);
+      const dim3 grid(static_cast<unsigned>((kitems + 3) / 4));
+#define IRB_DKDV_HITS(GPV)                                                                                   \
+  hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV, GPV>), grid, dim3(256), 0, stream, args, ws.delta, ws.hit_off, \
+                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, static_cast<int>(kitems), merged)
+      if (Gp == 4) IRB_DKDV_HITS(4);
+      else if (Gp == 8) IRB_DKDV_HITS(8);
+      else if (Gp == 16) IRB_DKDV_HITS(16);
+      else if (Gp == 32) IRB_DKDV_HITS(32);
+      else IRB_DKDV_HITS(0);
+#undef IRB_DKDV_HITS
     } else if constexpr (kWide) {
       hipLaunchKernelGGL((bwd_dkdv_wide_kernel<D, DV>), dim3(static_cast<unsigned>(kitems)), dim3(256), 0, stream,
                          args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, nkt, merged);

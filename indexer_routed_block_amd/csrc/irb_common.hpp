@@ -22,13 +22,9 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;  // 3
 // ---------------------------------------------------------------- bf16 <-> f32
 IRB_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
 
-// round-to-nearest-even; NaN kept quiet
-IRB_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+// round-to-nearest-even (the hardware conversion, v_cvt_pk_bf16_f32: one
+// instruction, denormals kept, NaN stays a quiet NaN)
+IRB_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 // high part = f rounded to bf16; low part = bf16 of the remainder.  hi + lo
 // carries ~16 significant bits of f, so a bf16 MFMA against both halves
