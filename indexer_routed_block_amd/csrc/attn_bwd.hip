@@ -935,9 +935,13 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   // (with Gp >= 4 those four rows belong to one query).  They are loaded one
   // batch ahead, so a batch waits for one round of loads: its q / dO rows
   // together with its lse and Delta values.
+  // The raw list entries with their validity (checked where they are used,
+  // so the loads have no consumer in the fetching iteration and stay in
+  // flight; masking them at fetch time had the compiler wait for them there)
   struct Ids {
     int ta[2], ts[2];
     uint32_t tm[2];
+    bool va[2], vs[2];
   };
   // (branch-free: entries past the list read its first entry, a valid
   // address, and are then discarded)
@@ -948,128 +952,201 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
       const int slot = Gp <= 32 ? r / Gp : 0;
       const int h = Gp <= 32 ? r % Gp : hb_ * 32 + r;
       const int64_t e = e0_ + slot;
-      const int tv = hit_t[e < h1 ? e : h0];
-      const int t = (e < h1 && h < G) ? tv : -1;
-      d.ta[rt] = t < a.S_q ? t : -1;
+      d.ta[rt] = hit_t[e < h1 ? e : h0];
+      d.va[rt] = e < h1 && h < G;
       const int rs = 16 * rt + 4 * g16;
       const int64_t es = e0_ + (Gp <= 32 ? rs / Gp : 0);
-      const int tsv = hit_t[es < h1 ? es : h0];
-      const uint32_t tmv = hit_m[es < h1 ? es : h0];
-      const int ts = es < h1 ? tsv : -1;
-      d.ts[rt] = ts < a.S_q ? ts : -1;
-      d.tm[rt] = es < h1 ? tmv : 0u;
+      d.ts[rt] = hit_t[es < h1 ? es : h0];
+      d.tm[rt] = hit_m[es < h1 ? es : h0];
+      d.vs[rt] = es < h1;
     }
   };
-  Ids cur;
-  if (h0 < h1) fetch(h0, 0, cur);
-  for (int64_t e0 = h0; e0 < h1; e0 += qpb) {
+  // Second half of a batch: P and dS at rows 16 rt + 4 g16 + i, key l16
+  // (zero off the key mask) as bf16 high/low operands (form_pds), then
+  // dV^T += dO^T P and dK^T += Q^T dS with the A operands read transposed
+  // from the slabs written by start (accumulate).  k-slot j of the A
+  // operands is row 4 g16 + j (j < 4) or 16 + 4 g16 + (j - 4), matching P / dS.
+  struct PdS {
+    bf16x8 ph, pl, sh, sl;
+  };
+  auto form_pds = [&](const f32x4 (&sacc)[2], const f32x4 (&pacc)[2], const float (&lsv)[2][4],
+                      const float (&dlv)[2][4], const bool (&rok)[2][4], PdS& o) __attribute__((always_inline)) {
+    float p[2][4], ds[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // every lane evaluates the exponential (no branch per element);
+        // masked entries are then replaced by 0 (their inputs may come
+        // from the stand-in row)
+        const float e = fast_exp2(sacc[rt][i] * sc2 - lsv[rt][i] * kLog2eB);
+        p[rt][i] = rok[rt][i] ? e : 0.f;
+        ds[rt][i] = rok[rt][i] ? e * (pacc[rt][i] - dlv[rt][i]) : 0.f;
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bput_f(o.ph, o.pl, j, p[0][j], true);
+      bput_f(o.ph, o.pl, 4 + j, p[1][j], true);
+      bput_f(o.sh, o.sl, j, ds[0][j], true);
+      bput_f(o.sh, o.sl, 4 + j, ds[1][j], true);
+    }
+  };
+  // The NDV + NDK dim tiles run as one sequence (dV tiles, then dK tiles)
+  // whose transposed A operands are read kAhead tiles ahead of their MFMAs,
+  // so several LDS reads are in flight behind each pair of MFMAs.
+  constexpr int kAhead = 3;
+  auto tile_operand = [&](int u) __attribute__((always_inline)) {
+    const uint16_t* w = u < NDV ? so + tr_off_o + 16 * u : sq + tr_off_q + 16 * (u - NDV);
+    const int pitch = u < NDV ? LO : LQ;
+    const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * pitch);
+    return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  };
+  auto accumulate = [&](const PdS& o) __attribute__((always_inline)) {
+    wave_lds_sync();
+    bf16x8 xa[kAhead + 1];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) xa[u] = tile_operand(u);
+#pragma unroll
+    for (int u = 0; u < NDV + NDK; ++u) {
+      if (u + kAhead < NDV + NDK) xa[(u + kAhead) % (kAhead + 1)] = tile_operand(u + kAhead);
+      const bf16x8 x = xa[u % (kAhead + 1)];
+      if (u < NDV) {
+        adv[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, o.ph, adv[u], 0, 0, 0);
+        adv[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, o.pl, adv[u], 0, 0, 0);
+      } else {
+        adk[u - NDV] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, o.sh, adk[u - NDV], 0, 0, 0);
+        adk[u - NDV] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, o.sl, adk[u - NDV], 0, 0, 0);
+      }
+    }
+    wave_lds_sync();   // the slabs are rewritten by the next batch
+  };
+  // First half of a batch: the rows' copies into the slabs and S = Q K^T,
+  // dP = dO V^T
+  auto start = [&](const bf16x8 (&qa)[2][KS], const bf16x8 (&oa)[2][VS], f32x4 (&sacc)[2],
+                   f32x4 (&pacc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        *reinterpret_cast<bf16x8*>(sq + (16 * rt + l16) * LQ + 8 * g16 + 32 * s) = qa[rt][s];
+#pragma unroll
+      for (int s = 0; s < VS; ++s)
+        *reinterpret_cast<bf16x8*>(so + (16 * rt + l16) * LO + 8 * g16 + 32 * s) = oa[rt][s];
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][s], kb[s], sacc[rt], 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < VS; ++s) pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[rt][s], vb[s], pacc[rt], 0, 0, 0);
+    }
+  };
+  // Rows of the batch at e0_ (ids d, 32-row part hb_) in the A layout
+  auto load_rows = [&](int64_t e0_, int hb_, const Ids& d, bf16x8 (&qa)[2][KS], bf16x8 (&oa)[2][VS])
+                       __attribute__((always_inline)) {
     // every row of the batch a real (query, head): no row needs zeroing
-    const bool full = e0 + qpb <= h1 && G == Gp;
-    for (int hb = 0; hb < bpq; ++hb) {
-      // rows r = 16 rt + l16 of S and dP: Q and dO rows in the A layout
-      bf16x8 qa[2][KS], oa[2][VS];
+    const bool full = e0_ + qpb <= h1 && G == Gp;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int r = 16 * rt + l16;
-        const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
-        const int t = cur.ta[rt];
-        const int hh = kvh * G + (h < G ? h : 0);
-        const int tt = t >= 0 ? t : 0;
-        const uint16_t* qp = qg + b * a.sq_b + static_cast<int64_t>(tt) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
-        const uint16_t* op = og + ((static_cast<int64_t>(b) * a.S_q + tt) * a.Hq + hh) * DV + 8 * g16;
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r = 16 * rt + l16;
+      const int h = Gp <= 32 ? r % Gp : hb_ * 32 + r;
+      const int t = d.va[rt] && d.ta[rt] < a.S_q ? d.ta[rt] : -1;
+      const int hh = kvh * G + (h < G ? h : 0);
+      const int tt = t >= 0 ? t : 0;
+      const uint16_t* qp = qg + b * a.sq_b + static_cast<int64_t>(tt) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * g16;
+      const uint16_t* op = og + ((static_cast<int64_t>(b) * a.S_q + tt) * a.Hq + hh) * DV + 8 * g16;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qa[rt][s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+      for (int s = 0; s < KS; ++s) qa[rt][s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
 #pragma unroll
-        for (int s = 0; s < VS; ++s) oa[rt][s] = *reinterpret_cast<const bf16x8*>(op + 32 * s);
-        if (!full && t < 0) {
+      for (int s = 0; s < VS; ++s) oa[rt][s] = *reinterpret_cast<const bf16x8*>(op + 32 * s);
+      if (!full && t < 0) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) bzero8(qa[rt][s]);
+        for (int s = 0; s < KS; ++s) bzero8(qa[rt][s]);
 #pragma unroll
-          for (int s = 0; s < VS; ++s) bzero8(oa[rt][s]);
-        }
+        for (int s = 0; s < VS; ++s) bzero8(oa[rt][s]);
       }
-      // lse and Delta of the softmax rows 16 rt + 4 g16 + i (index 0 stands
-      // in for rows without a query; their weights are zeroed below)
-      float lsv[2][4], dlv[2][4];
-      bool rok[2][4];
+    }
+  };
+  // lse / Delta / key-mask flags of the batch's softmax rows (index 0 stands
+  // in for rows without a query; their weights are zeroed in finish)
+  auto load_stats = [&](int hb_, const Ids& d, float (&lsv)[2][4], float (&dlv)[2][4], bool (&rok)[2][4])
+                        __attribute__((always_inline)) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * g16 + i;
-          const int h = Gp <= 32 ? r % Gp : hb * 32 + r;
-          const int te = cur.ts[rt];
-          rok[rt][i] = te >= 0 && h < G && ((cur.tm[rt] >> l16) & 1u);
-          const int64_t li = rok[rt][i] ? (static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + te : 0;
-          lsv[rt][i] = args.lse[li];
-          dlv[rt][i] = delta[li];
-        }
-      // the next batch's ids
-      Ids nxt;
-      {
-        const int64_t ne0 = hb + 1 < bpq ? e0 : e0 + qpb;
-        const int nhb = hb + 1 < bpq ? hb + 1 : 0;
-        if (ne0 < h1) fetch(ne0, nhb, nxt);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g16 + i;
+        const int h = Gp <= 32 ? r % Gp : hb_ * 32 + r;
+        const int te = d.vs[rt] && d.ts[rt] < a.S_q ? d.ts[rt] : -1;
+        rok[rt][i] = te >= 0 && h < G && ((d.tm[rt] >> l16) & 1u);
+        const int64_t li = rok[rt][i] ? (static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + te : 0;
+        lsv[rt][i] = args.lse[li];
+        dlv[rt][i] = delta[li];
       }
-      // row-major copies for the transposed operands
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          *reinterpret_cast<bf16x8*>(sq + (16 * rt + l16) * LQ + 8 * g16 + 32 * s) = qa[rt][s];
-#pragma unroll
-        for (int s = 0; s < VS; ++s)
-          *reinterpret_cast<bf16x8*>(so + (16 * rt + l16) * LO + 8 * g16 + 32 * s) = oa[rt][s];
-      }
+  };
+
+  if constexpr (GP > 0) {
+    // one 32-row batch per qpb listed queries (bpq = 1), software-pipelined:
+    // the rows and statistics of batch e0 + qpb load into the registers
+    // batch e0 has just released (rows after its S and dP, statistics after
+    // its P and dS) while batch e0's dK / dV work runs, and the ids of the
+    // batch after that are read meanwhile
+    bf16x8 qa[2][KS], oa[2][VS];
+    float lsv[2][4], dlv[2][4];
+    bool rok[2][4];
+    Ids nxt;
+    if (h0 < h1) {
+      Ids cur;
+      fetch(h0, 0, cur);
+      load_rows(h0, 0, cur, qa, oa);
+      load_stats(0, cur, lsv, dlv, rok);
+      if (h0 + qpb < h1) fetch(h0 + qpb, 0, nxt);
+    }
+    for (int64_t e0 = h0; e0 < h1; e0 += qpb) {
       f32x4 sacc[2], pacc[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][s], kb[s], sacc[rt], 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < VS; ++s) pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[rt][s], vb[s], pacc[rt], 0, 0, 0);
+      start(qa, oa, sacc, pacc);
+      PdS o;
+      form_pds(sacc, pacc, lsv, dlv, rok, o);
+      // The next rows are issued only after P and dS have consumed this
+      // batch's statistics: memory-operation counters complete in order, so
+      // a wait for the statistics placed after these loads would wait for
+      // them too.  The empty statement uses the operands and orders memory.
+      asm volatile("" : : "v"(o.ph), "v"(o.pl), "v"(o.sh), "v"(o.sl) : "memory");
+      const int64_t ne0 = e0 + qpb;
+      if (ne0 < h1) {
+        load_rows(ne0, 0, nxt, qa, oa);
+        load_stats(0, nxt, lsv, dlv, rok);
+        if (ne0 + qpb < h1) fetch(ne0 + qpb, 0, nxt);
       }
-      // P and dS at rows 16 rt + 4 g16 + i, key l16; zero off the key mask
-      float p[2][4], ds[2][4];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = rok[rt][i] ? exp2f(sacc[rt][i] * sc2 - lsv[rt][i] * kLog2eB) : 0.f;
-          p[rt][i] = pv;
-          ds[rt][i] = rok[rt][i] ? pv * (pacc[rt][i] - dlv[rt][i]) : 0.f;
+      accumulate(o);
+    }
+  } else {
+    // run-time group size (G > 32: several 32-row batches per query)
+    Ids cur;
+    if (h0 < h1) fetch(h0, 0, cur);
+    for (int64_t e0 = h0; e0 < h1; e0 += qpb) {
+      for (int hb = 0; hb < bpq; ++hb) {
+        bf16x8 qa[2][KS], oa[2][VS];
+        float lsv[2][4], dlv[2][4];
+        bool rok[2][4];
+        load_rows(e0, hb, cur, qa, oa);
+        load_stats(hb, cur, lsv, dlv, rok);
+        // the next batch's ids
+        Ids nxt;
+        {
+          const int64_t ne0 = hb + 1 < bpq ? e0 : e0 + qpb;
+          const int nhb = hb + 1 < bpq ? hb + 1 : 0;
+          if (ne0 < h1) fetch(ne0, nhb, nxt);
         }
-      bf16x8 ph, pl, sh, sl;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bput_f(ph, pl, j, p[0][j], true);
-        bput_f(ph, pl, 4 + j, p[1][j], true);
-        bput_f(sh, sl, j, ds[0][j], true);
-        bput_f(sh, sl, 4 + j, ds[1][j], true);
+        f32x4 sacc[2], pacc[2];
+        start(qa, oa, sacc, pacc);
+        PdS o;
+        form_pds(sacc, pacc, lsv, dlv, rok, o);
+        accumulate(o);
+        cur = nxt;
       }
-      wave_lds_sync();
-      // dV^T += dO^T P and dK^T += Q^T dS; k-slot j of the A operands is row
-      // 4 g16 + j (j < 4) or 16 + 4 g16 + (j - 4), matching P / dS above
-#pragma unroll
-      for (int dt = 0; dt < NDV; ++dt) {
-        const uint16_t* w = so + tr_off_o + 16 * dt;
-        const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * LO);
-        const bf16x8 xa = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        adv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ph, adv[dt], 0, 0, 0);
-        adv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pl, adv[dt], 0, 0, 0);
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDK; ++dt) {
-        const uint16_t* w = sq + tr_off_q + 16 * dt;
-        const v4s x0 = lds_read_tr(w), x1 = lds_read_tr(w + 16 * LQ);
-        const bf16x8 xa = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        adk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sh, adk[dt], 0, 0, 0);
-        adk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, sl, adk[dt], 0, 0, 0);
-      }
-      wave_lds_sync();   // the slabs are rewritten by the next batch
-      cur = nxt;
     }
   }
 
