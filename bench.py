@@ -364,9 +364,9 @@ def main():
     work = {"attn_fwd": ("mfma", fwd_flop)}
     if backward:
         work["attn_bwd"] = ("mfma", 2.0 * (3 * Dqk + 2 * Dv) * (Hq // R) * pairs)
-        # routes read + counts and listed entries written (the -1 padding of the fixed width is not counted)
-        work["reverse_lists"] = ("hbm", 4.0 * L * R * B * S + 4.0 * rev_counts.numel()
-                                 + 4.0 * float(rev_counts.sum().item()))
+        # routes read + counts and the index matrix written: the call's output is
+        # [rows, width] with -1 after each count, every entry of it written
+        work["reverse_lists"] = ("hbm", 4.0 * L * R * B * S + 4.0 * rev_counts.numel() + 4.0 * rev_idx.numel())
         # listed entries read and written once (plus counts), and (one-query tiles) every
         # route read once to mark the key tiles it holds completely, one bit each
         entries = float(rev_counts.sum().item())

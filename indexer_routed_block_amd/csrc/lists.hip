@@ -6,11 +6,14 @@
 // scratch), _BackwardBlockPartition (counts + ascending padded indices).
 //
 // Two passes over a bit matrix in caller-provided scratch (1 bit per
-// (row tile, other-axis tile) pair): a mark pass where each wavefront reads
-// 64 consecutive route entries of a query (coalesced) and sets the bit of
-// every new tile with one atomic OR per run of equal tiles, and an emit pass
-// where a workgroup scans one row of the matrix with popcount prefix sums
-// and writes the ascending tile list.
+// (row tile, other-axis tile) pair).  Mark: a wavefront reads a query's route
+// (coalesced, 64 or 256 entries per step) and sets the bit of every new tile
+// once per run of equal tiles -- for reverse lists into a band of the matrix
+// held in LDS by the workgroup that owns the band's query tiles, written out
+// whole afterwards; otherwise (forward lists, or key-tile counts whose band
+// would not fit in LDS) by global atomics into the zeroed matrix.  Emit: a
+// workgroup scans one row with popcount prefix sums and writes the ascending
+// tile list and its -1 padding.
 #include "irb_internal.hpp"
 
 namespace irb {
@@ -37,36 +40,27 @@ IRB_DEV int div_bk(int id, int bk, uint32_t m) {
   return m ? static_cast<int>(__umulhi(static_cast<uint32_t>(id), m)) : id / bk;
 }
 
-// One wavefront per query row (b, t).  kVec rows (width a multiple of 4,
-// 16-byte aligned) are read four entries per lane per load; a tile bit is set
-// once per run of equal tiles (the route is ascending).
-template <bool kVec>
-__global__ void __launch_bounds__(kMarkWaves * 64)
-mark_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int B, int S_q, int S_k, int Lw,
-            int bq, int bk, uint32_t bkm, int reverse, int n_rows, int words, uint32_t* __restrict__ bits) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kMarkWaves + wid;
-  if (row >= static_cast<int64_t>(B) * S_q) return;
-  const int b = static_cast<int>(row / S_q), t = static_cast<int>(row % S_q);
-  const int n = max(0, min(lens[row], Lw));
-  const int32_t* r = routes + row * Lw;
-  const int qt = t / bq;
-  uint32_t* mat = bits + static_cast<int64_t>(b) * n_rows * words;
-  auto mark = [&](int kt) __attribute__((always_inline)) {
-    if (reverse) atomicOr(&mat[static_cast<int64_t>(kt) * words + (qt >> 5)], 1u << (qt & 31));
-    else atomicOr(&mat[static_cast<int64_t>(qt) * words + (kt >> 5)], 1u << (kt & 31));
-  };
+// Walks one ascending route (n entries at r) with a whole wavefront and calls
+// mark(kt) once per run of equal key tiles kt = id / bk.  kVec rows (width a
+// multiple of 4, 16-byte aligned) are read four entries per lane per load.
+// Out-of-range IDs are ignored.
+template <bool kVec, typename Mark>
+IRB_DEV void walk_route_tiles(const int32_t* __restrict__ r, int n, int S_k, int bk, uint32_t bkm, Mark&& mark) {
+  const int lane = threadIdx.x & 63;
   int prev_last = -1;
   if constexpr (kVec) {
+    // the next chunk's load is issued before the current chunk is marked
+    int4 v = make_int4(-1, -1, -1, -1);
+    if (4 * lane < n) v = *reinterpret_cast<const int4*>(r + 4 * lane);
     for (int e0 = 0; e0 < n; e0 += 256) {
       const int e = e0 + 4 * lane;
-      int4 v = make_int4(-1, -1, -1, -1);
-      if (e < n) v = *reinterpret_cast<const int4*>(r + e);
+      int4 vn = make_int4(-1, -1, -1, -1);
+      if (e + 256 < n) vn = *reinterpret_cast<const int4*>(r + e + 256);
       const int ids[4] = {v.x, v.y, v.z, v.w};
       int kt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool ok = e + j < n && ids[j] >= 0 && ids[j] < S_k;   // out-of-range IDs are ignored
+        const bool ok = e + j < n && ids[j] >= 0 && ids[j] < S_k;
         kt[j] = ok ? div_bk(ids[j], bk, bkm) : -1;
       }
       int before = __shfl_up(kt[3], 1, 64);
@@ -76,14 +70,18 @@ mark_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens
         if (kt[j] >= 0 && kt[j] != before) mark(kt[j]);
         if (kt[j] >= 0) before = kt[j];
       }
-      // last valid tile of the chunk: lanes past n report -1, so take the max
-      prev_last = max(prev_last, wave_max_int(max(max(kt[0], kt[1]), max(kt[2], kt[3]))));
+      // a tile already marked for the next chunk's first entry: the largest
+      // of the highest lane holding a valid entry (the route is ascending)
+      const int lmax = max(max(kt[0], kt[1]), max(kt[2], kt[3]));
+      const uint64_t bal = __ballot(lmax >= 0);
+      if (bal) prev_last = max(prev_last, __builtin_amdgcn_readlane(lmax, 63 - __builtin_clzll(bal)));
+      v = vn;
     }
   } else {
     for (int e0 = 0; e0 < n; e0 += 64) {
       const int e = e0 + lane;
       const int id = (e < n) ? r[e] : -1;
-      const bool ok = id >= 0 && id < S_k;            // out-of-range IDs are ignored
+      const bool ok = id >= 0 && id < S_k;
       const int kt = ok ? div_bk(id, bk, bkm) : -1;
       int before = __shfl_up(kt, 1, 64);
       if (lane == 0) before = prev_last;
@@ -93,38 +91,131 @@ mark_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens
   }
 }
 
-// one workgroup per bit-matrix row
+// One wavefront per query row (b, t); one global atomic OR per run of equal
+// tiles into the zeroed bit matrix.
+template <bool kVec>
+__global__ void __launch_bounds__(kMarkWaves * 64)
+mark_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int B, int S_q, int S_k, int Lw,
+            int bq, int bk, uint32_t bkm, int reverse, int n_rows, int words, uint32_t* __restrict__ bits) {
+  const int wid = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kMarkWaves + wid;
+  if (row >= static_cast<int64_t>(B) * S_q) return;
+  const int b = static_cast<int>(row / S_q), t = static_cast<int>(row % S_q);
+  const int n = max(0, min(lens[row], Lw));
+  const int qt = t / bq;
+  uint32_t* mat = bits + static_cast<int64_t>(b) * n_rows * words;
+  walk_route_tiles<kVec>(routes + row * Lw, n, S_k, bk, bkm, [&](int kt) __attribute__((always_inline)) {
+    if (reverse) atomicOr(&mat[static_cast<int64_t>(kt) * words + (qt >> 5)], 1u << (qt & 31));
+    else atomicOr(&mat[static_cast<int64_t>(qt) * words + (kt >> 5)], 1u << (kt & 31));
+  });
+}
+
+// Reverse lists: one workgroup per band of qw consecutive words (32 qw query
+// tiles) of one batch row.  The band's words of every key-tile row are built
+// in LDS with LDS atomics (wave w walks the band's queries w, w + 8, ...),
+// then every word of the band is written out, zeros included, so the matrix
+// needs neither a clearing pass nor global atomics.
+constexpr int kBandWaves = 8;
+
+template <bool kVec>
+__global__ void __launch_bounds__(kBandWaves * 64)
+mark_band_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens, int S_q, int S_k, int Lw,
+                 int bq, int bk, uint32_t bkm, int n_rows, int words, int qw, uint32_t* __restrict__ bits) {
+  extern __shared__ uint32_t band[];   // [n_rows][qw]
+  const int tid = threadIdx.x, wid = tid >> 6;
+  const int b = blockIdx.y;
+  const int w0 = blockIdx.x * qw;
+  const int nw = min(qw, words - w0);
+  for (int i = tid; i < n_rows * qw; i += kBandWaves * 64) band[i] = 0u;
+  __syncthreads();
+  const int qt0 = 32 * w0;
+  const int t1 = static_cast<int>(min(static_cast<int64_t>(S_q), static_cast<int64_t>(qt0 + 32 * nw) * bq));
+  for (int t = qt0 * bq + wid; t < t1; t += kBandWaves) {
+    const int64_t row = static_cast<int64_t>(b) * S_q + t;
+    const int n = max(0, min(lens[row], Lw));
+    const int rel = t / bq - qt0;
+    uint32_t* col = band + (rel >> 5);
+    const uint32_t bit = 1u << (rel & 31);
+    walk_route_tiles<kVec>(routes + row * Lw, n, S_k, bk, bkm,
+                           [&](int kt) __attribute__((always_inline)) { atomicOr(&col[kt * qw], bit); });
+  }
+  __syncthreads();
+  uint32_t* mat = bits + static_cast<int64_t>(b) * n_rows * words + w0;
+  for (int i = tid; i < n_rows * qw; i += kBandWaves * 64) {
+    const int kt = i / qw, j = i - kt * qw;
+    if (j < nw) mat[static_cast<int64_t>(kt) * words + j] = band[i];
+  }
+}
+
+// One workgroup per bit-matrix row: popcount prefix sums over the row's
+// words (four per thread per step when vec_in), the ascending list, then -1
+// up to the row's width (16-byte stores when vec_out).
 __global__ void __launch_bounds__(256)
-emit_kernel(const uint32_t* __restrict__ bits, int n_rows, int words, int n_other, int32_t* __restrict__ counts,
-            int32_t* __restrict__ indices, int width) {
+emit_kernel(const uint32_t* __restrict__ bits, int n_rows, int words, int32_t* __restrict__ counts,
+            int32_t* __restrict__ indices, int width, int vec_in, int vec_out) {
   __shared__ int wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x;
   const int b = blockIdx.y, row = blockIdx.x;
   const uint32_t* w = bits + (static_cast<int64_t>(b) * n_rows + row) * words;
   int32_t* out = indices + (static_cast<int64_t>(b) * n_rows + row) * width;
   int base = 0;
-  for (int w0 = 0; w0 < words; w0 += 256) {
-    const int i = w0 + tid;
-    const uint32_t x = (i < words) ? w[i] : 0u;
-    const int pc = __popc(x);
-    const int incl = wave_incl_scan(pc);
-    if (lane == 63) wsum[wid] = incl;
-    __syncthreads();
-    int off = 0, tot = 0;
-    for (int k = 0; k < 4; ++k) { if (k < wid) off += wsum[k]; tot += wsum[k]; }
-    int o = base + off + incl - pc;
-    uint32_t y = x;
-    while (y) {
-      const int bit = __ffs(y) - 1;
-      y &= y - 1;
-      out[o++] = i * 32 + bit;
+  if (vec_in) {
+    for (int w0 = 0; w0 < words; w0 += 1024) {
+      const int i = w0 + 4 * tid;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (i < words) x = *reinterpret_cast<const uint4*>(w + i);
+      const int pc = __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+      int tot;
+      const int incl = block_scan256(pc, wsum, &tot);
+      int o = base + incl - pc;
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t y = xs[j];
+        while (y) {
+          const int bit = __ffs(y) - 1;
+          y &= y - 1;
+          out[o++] = (i + j) * 32 + bit;
+        }
+      }
+      base += tot;
     }
-    base += tot;
-    __syncthreads();
+  } else {
+    for (int w0 = 0; w0 < words; w0 += 256) {
+      const int i = w0 + tid;
+      const uint32_t x = (i < words) ? w[i] : 0u;
+      const int pc = __popc(x);
+      int tot;
+      const int incl = block_scan256(pc, wsum, &tot);
+      int o = base + incl - pc;
+      uint32_t y = x;
+      while (y) {
+        const int bit = __ffs(y) - 1;
+        y &= y - 1;
+        out[o++] = i * 32 + bit;
+      }
+      base += tot;
+    }
   }
-  for (int i = base + tid; i < width; i += 256) out[i] = -1;
+  if (vec_out) {
+    const int a = min(width, (base + 3) & ~3);
+    if (base + tid < a) out[base + tid] = -1;
+    for (int i = a + 4 * tid; i < width; i += 1024) *reinterpret_cast<int4*>(out + i) = make_int4(-1, -1, -1, -1);
+  } else {
+    for (int i = base + tid; i < width; i += 256) out[i] = -1;
+  }
   if (tid == 0) counts[static_cast<int64_t>(b) * n_rows + row] = base;
-  (void)n_other;
+}
+
+// words per band of the reverse-list mark (0: the atomic path).  A band's
+// LDS (n_rows x qw words) stays within 64 KiB, two workgroups per CU, and
+// qw shrinks until the grid has at least 1024 bands.
+static int band_words(int B, int n_rows, int words) {
+  int qw = 8;
+  while (qw > 1 && (static_cast<int64_t>(n_rows) * qw * 4 > 65536 ||
+                    static_cast<int64_t>(B) * ((words + qw - 1) / qw) < 1024))
+    qw >>= 1;
+  return static_cast<int64_t>(n_rows) * qw * 4 <= 65536 ? qw : 0;
 }
 
 int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_q, int S_k, int Lw, int bq, int bk,
@@ -134,24 +225,41 @@ int launch_block_lists(const int32_t* routes, const int32_t* lens, int B, int S_
   const int n_rows = reverse ? nkt : nqt;
   const int n_other = reverse ? nqt : nkt;
   const int words = (n_other + 31) / 32;
-  int rc = launch_fill_i32(reinterpret_cast<int32_t*>(bitmap), static_cast<int64_t>(B) * n_rows * words, 0, stream);
-  if (rc) return rc;
   const int64_t qrows = static_cast<int64_t>(B) * S_q;
-  if (qrows > 0) {
-    const uint32_t bkm = (bk >= 2 && static_cast<uint64_t>(S_k) * static_cast<uint64_t>(bk) < (1ull << 32))
-                             ? 0xFFFFFFFFu / static_cast<uint32_t>(bk) + 1u
-                             : 0u;
-    const dim3 grid(static_cast<unsigned>((qrows + kMarkWaves - 1) / kMarkWaves));
-    if ((Lw % 4) == 0 && (reinterpret_cast<uintptr_t>(routes) & 15) == 0)
-      hipLaunchKernelGGL(mark_kernel<true>, grid, dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw, bq,
-                         bk, bkm, reverse, n_rows, words, bitmap);
+  const uint32_t bkm = (bk >= 2 && static_cast<uint64_t>(S_k) * static_cast<uint64_t>(bk) < (1ull << 32))
+                           ? 0xFFFFFFFFu / static_cast<uint32_t>(bk) + 1u
+                           : 0u;
+  const bool vec_routes = (Lw % 4) == 0 && (reinterpret_cast<uintptr_t>(routes) & 15) == 0;
+  const int qw = reverse ? band_words(B, n_rows, words) : 0;
+  if (qw > 0) {
+    // every word of the matrix is written by exactly one band
+    const dim3 grid(static_cast<unsigned>((words + qw - 1) / qw), static_cast<unsigned>(B));
+    const size_t lds = static_cast<size_t>(n_rows) * qw * 4;
+    if (vec_routes)
+      hipLaunchKernelGGL(mark_band_kernel<true>, grid, dim3(kBandWaves * 64), lds, stream, routes, lens, S_q, S_k, Lw, bq, bk, bkm,
+                         n_rows, words, qw, bitmap);
     else
-      hipLaunchKernelGGL(mark_kernel<false>, grid, dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw, bq,
-                         bk, bkm, reverse, n_rows, words, bitmap);
+      hipLaunchKernelGGL(mark_band_kernel<false>, grid, dim3(kBandWaves * 64), lds, stream, routes, lens, S_q, S_k, Lw, bq, bk, bkm,
+                         n_rows, words, qw, bitmap);
+  } else {
+    int rc = launch_fill_i32(reinterpret_cast<int32_t*>(bitmap), static_cast<int64_t>(B) * n_rows * words, 0, stream);
+    if (rc) return rc;
+    if (qrows > 0) {
+      const dim3 grid(static_cast<unsigned>((qrows + kMarkWaves - 1) / kMarkWaves));
+      if (vec_routes)
+        hipLaunchKernelGGL(mark_kernel<true>, grid, dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw,
+                           bq, bk, bkm, reverse, n_rows, words, bitmap);
+      else
+        hipLaunchKernelGGL(mark_kernel<false>, grid, dim3(kMarkWaves * 64), 0, stream, routes, lens, B, S_q, S_k, Lw,
+                           bq, bk, bkm, reverse, n_rows, words, bitmap);
+    }
   }
-  if (n_rows > 0 && B > 0)
+  if (n_rows > 0 && B > 0) {
+    const int vec_in = (words % 4) == 0 && (reinterpret_cast<uintptr_t>(bitmap) & 15) == 0;
+    const int vec_out = (width % 4) == 0 && (reinterpret_cast<uintptr_t>(indices) & 15) == 0;
     hipLaunchKernelGGL(emit_kernel, dim3(static_cast<unsigned>(n_rows), static_cast<unsigned>(B)), dim3(256), 0,
-                       stream, bitmap, n_rows, words, n_other, counts, indices, width);
+                       stream, bitmap, n_rows, words, counts, indices, width, vec_in, vec_out);
+  }
   return 0;
 }
 

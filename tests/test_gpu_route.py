@@ -226,6 +226,22 @@ def test_block_lists_bit_exact(bq, bk, reverse, width):
     np.testing.assert_array_equal(host(indices), ri)
 
 
+@pytest.mark.parametrize("B,S_q,S_k,bq,width", [(2, 65560, 1000, 1, 24), (1, 131100, 1000, 2, 13)])
+def test_reverse_lists_banded_bit_exact(B, S_q, S_k, bq, width):
+    """Reverse lists with enough query tiles (over 65504) that the LDS band
+    of the mark pass holds several words per key-tile row, the last band
+    partial; key IDs past S_k are ignored; a 16-byte-load and a per-entry
+    route width."""
+    banner(f"banded reverse lists B={B} S_q={S_q} S_k={S_k} bq={bq} width={width}")
+    rng = np.random.default_rng(S_q + width)
+    ids = rng.integers(-1, S_k + 5, size=(B, S_q, width)).astype(np.int32)
+    routes, lens, _ = oracle.compact_routes(ids, S_k)
+    counts, indices = irb.build_block_lists(to_dev(routes), to_dev(lens), S_k, bq, 16, True)
+    rc, ri = oracle.block_lists(routes, lens, S_k, bq, 16, True)
+    np.testing.assert_array_equal(host(counts), rc)
+    np.testing.assert_array_equal(host(indices), ri)
+
+
 @pytest.mark.parametrize("ties", [False, True])
 def test_select_rows_longer_than_lds(ties):
     """Rows with more visible blocks than the select kernel keeps in LDS (40000 > 32768)."""
