@@ -379,7 +379,7 @@ constexpr bool dq_fuses_delta() { return sizeof(T) == 2 && D <= 128; }
 template <typename T, int D, int DV, bool kShared>
 __global__ void __launch_bounds__(256, (!kShared && dq_fuses_delta<T, D>()) ? 2 : 1)
 bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta,
-              T* __restrict__ dq, int G, int n_items, int latent, int head_major) {
+              T* __restrict__ dq, int G, int n_items, int latent, int head_major, int tile_bq, int thr_milli) {
   constexpr bool kSplit = sizeof(T) == 4;
   constexpr int KS = D / 32, VS = DV / 32, NDQ = D / 16;
   constexpr int PAD = sizeof(T) == 2 ? 8 : 4;
@@ -393,6 +393,8 @@ bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ 
   const QItem qi = decode_qitem(item, a.B, a.S_q, a.Hkv, kShared ? 0 : head_major);
   const int kvh = qi.kvh, t = qi.t, b = qi.b;
   if constexpr (!kShared && dq_fuses_delta<T, D>()) {
+    // the query-tile kernel's tiles (same test) are not this launch's
+    if (tile_bq > 0 && tile_stats_wave(a, b, kvh, (t / tile_bq) * tile_bq, tile_bq, thr_milli).dense) return;
     dq_item_gather<D, DV>(a, dout, lse, delta, dq, G, b, t, kvh,
                           reinterpret_cast<uint16_t*>(smem) + wid * 32 * (D + 8));
     return;
@@ -528,6 +530,261 @@ bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ 
       const float v[4] = {acc[dt][0] * a.scale, acc[dt][1] * a.scale, acc[dt][2] * a.scale, acc[dt][3] * a.scale};
       bstore4(op + dt * 16, v);
     }
+  }
+}
+
+// ---------------------------------------------------------------- dq, query tiles
+// bf16 GQA with D = Dv in {64, 128} and G in {4, 8, 16}: one workgroup per
+// (query tile of 128 / G queries, KV head), organised like the forward's
+// query-tile kernel.  The tile's 128 (query, head) pairs are the MFMA columns
+// (wave w holds pairs 32 w .. 32 w + 31); the 32-key tiles that any of its
+// queries routes to stream through LDS by direct loads (two slots: the next
+// tile loads while the current one is used); each query's key-membership
+// words (built once per call) mask them.  Two sweeps over those key tiles:
+//   1: S^T = K Q^T, dP^T = V dO^T, P = exp(S - lse) on routed keys,
+//      Delta += sum_k P dP in FP32;
+//   2: S^T, dP^T and P again, dS = P (dP - Delta) in FP32, rounded once to
+//      bf16, and dQ^T += K^T dS^T with K^T from LDS transpose reads.  dS is
+//      formed before the rounding, so each term carries only its own
+//      relative rounding (no cancellation is rounded in).
+// dQ = scale (dQ^T)^T; Delta is written for the key side.  Query tiles whose
+// routes cover too little of their key range go per query (dq_item_gather):
+// here when gather_rest, else in the per-query launch, which skips this
+// kernel's tiles by the same test.
+template <int D, int G>
+__global__ void __launch_bounds__(256, 2)
+bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+                   float* __restrict__ delta, uint16_t* __restrict__ dq, int n_qt, int thr_milli,
+                   const uint32_t* __restrict__ qbits, int qwords, int gather_rest) {
+  using T = uint16_t;
+  constexpr int BQ = 128 / G;
+  constexpr int KS = D / 16;     // 16-dim k-steps of S^T and dP^T
+  constexpr int NDT = D / 32;    // 32-dim row tiles of dQ^T
+  constexpr int NC = D / 8;      // 16-byte chunks per K or V row
+  // K and V rows of a key tile, row-major (K first), chunk c of row r at slot
+  // c ^ (2 r mod NC): the transpose reads of four rows (K^T) hit distinct banks
+  constexpr int KBYTES = 32 * D * 2;
+  constexpr int BUF = 2 * KBYTES;
+  constexpr int NI = 32 * NC / 256;        // direct loads per wave per tile side
+  constexpr int SLAB = 32 * (D + 8) * 2;   // per-wave LDS of dq_item_gather
+  constexpr int RAW = 2 * BUF > 4 * SLAB ? 2 * BUF : 4 * SLAB;
+  static_assert(NI >= 1, "tile loads");
+  __shared__ __align__(16) char raw[RAW];
+  __shared__ uint32_t mask[BQ][kSegTiles + 1];
+  __shared__ int tiles[kSegTiles];
+  __shared__ int s_ntiles;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int h32 = lane >> 5, l32 = lane & 31;
+  // grid order as the forward's tile kernel: KV heads of one query tile
+  // adjacent, query tiles last-first
+  const int bid = blockIdx.x;
+  const int kvh = bid % a.Hkv;
+  const int qt = n_qt - 1 - (bid / a.Hkv) % n_qt;
+  const int b = bid / (a.Hkv * n_qt);
+  const int qa = qt * BQ;
+  const TileStats ts = tile_stats_wave(a, b, kvh, qa, BQ, thr_milli);
+  if (!ts.dense) {
+    if (!gather_rest) return;
+    T* slab = reinterpret_cast<T*>(raw + wid * SLAB);
+    for (int q = wid; q < BQ; q += 4)
+      if (qa + q < a.S_q) dq_item_gather<D, D>(a, dout, lse, delta, dq, G, b, qa + q, kvh, slab);
+    return;
+  }
+
+  const T* kbase = static_cast<const T*>(a.k) + b * a.sk_b + kvh * a.sk_h;
+  const T* vbase = static_cast<const T*>(a.v) + b * a.sv_b + kvh * a.sv_h;
+  // this lane's column (query colq of the tile, head colh of the group); MFMA
+  // layout (v_mfma_f32_32x32x16_bf16): A lane l = row l % 32, k 8 (l / 32) ..
+  // + 8; B lane l = column l % 32, same k; accumulator element i of lane l =
+  // row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32
+  const int col = 32 * wid + l32;
+  const int colq = col / G, colh = col % G;
+  const int t = qa + colq;
+  const bool tok = t < a.S_q;
+  const int hh = kvh * G + colh;
+  bf16x8 qop[KS], dop[KS];
+  {
+    const int tt = tok ? t : 0;
+    const T* qp = static_cast<const T*>(a.q) + b * a.sq_b + static_cast<int64_t>(tt) * a.sq_t +
+                  static_cast<int64_t>(hh) * a.sq_h + 8 * h32;
+    const T* dp = dout + ((static_cast<int64_t>(b) * a.S_q + tt) * a.Hq + hh) * D + 8 * h32;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qop[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+      dop[s] = *reinterpret_cast<const bf16x8*>(dp + 16 * s);
+      if (!tok) { bzero8(qop[s]); bzero8(dop[s]); }
+    }
+  }
+  const float lse2 = tok ? lse[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] * kLog2eB : 0.f;
+  const float sc2 = a.scale * kLog2eB;
+
+  // tile loader: lane i of wave w's load n fills 16-byte slot (w NI + n) 64 + i
+  // of the K (or V) half; the global address is the tile's first row (scalar
+  // registers) plus a per-lane 32-bit byte offset fixed for the whole kernel
+  const int wv = __builtin_amdgcn_readfirstlane(wid);
+  uint32_t koff[NI], voff[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int slot = (wv * NI + n) * 64 + lane;
+    const int r = slot / NC, sw = (slot % NC) ^ ((2 * r) & (NC - 1));
+    koff[n] = static_cast<uint32_t>(r * a.sk_t + 8 * sw) * 2u;
+    voff[n] = static_cast<uint32_t>(r * a.sv_t + 8 * sw) * 2u;
+  }
+  const uint32_t lds0 = lds_addr(raw);
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    kt = __builtin_amdgcn_readfirstlane(kt);
+    buf = __builtin_amdgcn_readfirstlane(buf);
+    const int key0 = kt * 32;
+    const T* ks = kbase + static_cast<int64_t>(key0) * a.sk_t;
+    const T* vs = vbase + static_cast<int64_t>(key0) * a.sv_t;
+    const int lim = a.S_k - 1 - key0;
+    const uint32_t ld = lds0 + buf * BUF + wv * NI * 1024;
+    if (lim >= 31) {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) lds_dma16_s(ks, koff[n], ld + n * 1024);
+#pragma unroll
+      for (int n = 0; n < NI; ++n) lds_dma16_s(vs, voff[n], ld + KBYTES + n * 1024);
+    } else {
+      // the last tile: rows past the last key repeat it (their keys are never routed)
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int slot = (wv * NI + n) * 64 + lane;
+        const int r = slot / NC, sw = (slot % NC) ^ ((2 * r) & (NC - 1));
+        const int rr = min(r, lim);
+        lds_dma16_s(ks, static_cast<uint32_t>(rr * a.sk_t + 8 * sw) * 2u, ld + n * 1024);
+        lds_dma16_s(vs, static_cast<uint32_t>(rr * a.sv_t + 8 * sw) * 2u, ld + KBYTES + n * 1024);
+      }
+    }
+  };
+  // per-lane LDS byte offsets inside a slot.  Row reads (A = K or V rows, k =
+  // dims): row l32, chunk 2 s + h32.  K^T transpose reads of dim tile dt:
+  // lanes of a 16-lane row address keys 4 h32 + (lane % 16) / 4 (+ 8 for the
+  // upper four k of a step, + 16 for the second step) and dims 32 dt +
+  // 16 ((lane / 16) % 2) + 4 (lane % 4)
+  uint32_t rofs[KS], tofs[NDT];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    rofs[s] = static_cast<uint32_t>(l32 * D + 8 * ((2 * s + h32) ^ ((2 * l32) & (NC - 1)))) * 2u;
+  {
+    const int s16 = lane & 15, g2 = (lane >> 4) & 1;
+    const int vr = 4 * h32 + (s16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int vc = 4 * dt + 2 * g2 + ((s16 & 3) >> 1);
+      tofs[dt] = static_cast<uint32_t>(vr * D + 8 * (vc ^ ((2 * vr) & (NC - 1))) + 4 * (s16 & 1)) * 2u;
+    }
+  }
+  // K^T operand of dim tile dt, k-step t2: keys 16 t2 + 4 h32 + {0..3, 8..11},
+  // the order in which S^T's accumulator holds them (B operand straight from it)
+  auto kread = [&](uint32_t slot, int dt, int t2) __attribute__((always_inline)) {
+    const char* p = raw + slot + tofs[dt] + t2 * 16 * D * 2;
+    const v4s v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(p));
+    const v4s v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(p + 8 * D * 2));
+    return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  };
+
+  float dsum = 0.f, dlt = 0.f;
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  const int kt_first = ts.kmin >> 5, kt_last = ts.kmax >> 5;
+
+  auto sweep = [&](auto passc) __attribute__((always_inline)) {
+    constexpr bool kDq = decltype(passc)::value;
+    for (int seg0 = kt_first; seg0 <= kt_last; seg0 += kSegTiles) {
+      const int nseg = min(kSegTiles, kt_last - seg0 + 1);
+      // the previous segment's tiles, masks and slots are no longer read
+      __syncthreads();
+      for (int i = tid; i < BQ * nseg; i += 256) {
+        const int qi = i / nseg, j = i - qi * nseg;
+        const int tq = qa + qi;
+        mask[qi][j] = tq < a.S_q ? qbits[route_row(a, b, tq, kvh) * qwords + seg0 + j] : 0u;
+      }
+      __syncthreads();
+      // compact list of the key tiles any query routes to
+      if (wid == 0) {
+        int base = 0;
+        for (int j0 = 0; j0 < kSegTiles; j0 += 64) {
+          const int j = j0 + lane;
+          uint32_t any = 0u;
+          if (j < nseg)
+            for (int qi = 0; qi < BQ; ++qi) any |= mask[qi][j];
+          const uint64_t bal = __ballot(any != 0u);
+          if (any) tiles[base + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+          base += __popcll(bal);
+        }
+        if (lane == 0) s_ntiles = base;
+      }
+      __syncthreads();
+      const int ntiles = s_ntiles;
+      if (ntiles == 0) continue;
+      issue(seg0 + tiles[0], 0);
+      for (int i = 0; i < ntiles; ++i) {
+        const int cur = i & 1;
+        // tile i's loads (the only ones in flight) have landed; past the
+        // barrier every wave is done with tile i - 1, whose slot is refilled
+        __builtin_amdgcn_s_waitcnt(kDmaWait<0>());
+        bare_barrier();
+        if (i + 1 < ntiles) issue(seg0 + tiles[i + 1], cur ^ 1);
+        const uint32_t slot = static_cast<uint32_t>(cur) * BUF;
+        const char* kb = raw + slot;
+        const char* vb = raw + slot + KBYTES;
+        const uint32_t mw = mask[colq][tiles[i]] >> (4 * h32);
+        f32x16 st, dpt;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { st[e] = 0.f; dpt[e] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kb + rofs[s]), qop[s], st, 0, 0, 0);
+          dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vb + rofs[s]), dop[s], dpt, 0, 0, 0);
+        }
+        float p[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int bit = 8 * (e >> 2) + (e & 3);
+          p[e] = ((mw >> bit) & 1u) ? exp2f(st[e] * sc2 - lse2) : 0.f;
+        }
+        if constexpr (!kDq) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) dsum += p[e] * dpt[e];
+        } else {
+          float ds[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ds[e] = p[e] * (dpt[e] - dlt);
+          const bf16x8 dsb[2] = {pack_bf16x8(ds), pack_bf16x8(ds + 8)};
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(slot, dt, t2), dsb[t2], acc[dt], 0, 0, 0);
+        }
+      }
+    }
+  };
+  sweep(std::false_type{});
+  {
+    // the column's two lane halves hold different keys
+    const uint32_t u = __float_as_uint(dsum);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    dlt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  sweep(std::true_type{});
+
+  // ---- epilogue: this lane holds dims 32 dt + 8 j + 4 h32 + {0..3} of its column
+  if (tok) {
+    if (h32 == 0) delta[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] = dlt;
+    T* op = dq + ((static_cast<int64_t>(b) * a.S_q + t) * a.Hq + hh) * D + 4 * h32;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v[4] = {acc[dt][4 * j] * a.scale, acc[dt][4 * j + 1] * a.scale, acc[dt][4 * j + 2] * a.scale,
+                            acc[dt][4 * j + 3] * a.scale};
+        bstore4(op + 32 * dt + 8 * j, v);
+      }
   }
 }
 
@@ -1385,7 +1642,39 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     if (int rc = launch_attn_delta(a, args.dout, ws.delta, stream)) return rc;
   const int PAD = sizeof(T) == 2 ? 8 : 4;
   const int64_t items = rows * a.Hkv;
-  if (G <= 16) {
+  bool dq_done = false;
+  int tile_bq = 0;   // > 0: the per-query launch skips the query tiles the tile kernel takes
+  if constexpr (kGqaHits) {
+    // query tiles: key-membership words per route row, kept in the hit-list
+    // area of the workspace (the hit lists are built after this pass)
+    const bool small_strides = static_cast<int64_t>(a.sk_t > a.sv_t ? a.sk_t : a.sv_t) * 64 < (int64_t{1} << 31);
+    const size_t qb = attn_fwd_qbits_bytes(a);
+    const size_t room = 2 * align256(static_cast<size_t>(ws.cap) * 4);
+    if (tile_thr_milli() <= 1000 && small_strides && (G == 4 || G == 8 || G == 16) && qb > 0 && qb <= room) {
+      uint32_t* qbits = reinterpret_cast<uint32_t*>(ws.hit_t);
+      if (int rc = launch_route_bits(a.routes, a.lens, static_cast<int64_t>(a.RG) * rows, a.L, a.S_k, qbits, stream))
+        return rc;
+      const int qwords = (a.S_k + 31) / 32;
+      // routes wide against the key range: nearly every tile is dense, and the
+      // tile launch runs the few sparse ones per query itself
+      const int gather_rest = static_cast<int64_t>(a.L) * 1000 >= static_cast<int64_t>(tile_thr_milli()) * a.S_k;
+      const int BQ = 128 / G;
+      const int n_qt = (a.S_q + BQ - 1) / BQ;
+      const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * n_qt * a.Hkv));
+#define IRB_DQ_TILE(GV)                                                                                        \
+  hipLaunchKernelGGL((bwd_dq_tile_kernel<D, GV>), grid, dim3(256), 0, stream, a, static_cast<const uint16_t*>(args.dout), \
+                     args.lse, ws.delta, static_cast<uint16_t*>(args.dq), n_qt, tile_thr_milli(), qbits, qwords,   \
+                     gather_rest)
+      if (G == 4) IRB_DQ_TILE(4);
+      else if (G == 8) IRB_DQ_TILE(8);
+      else IRB_DQ_TILE(16);
+#undef IRB_DQ_TILE
+      dq_done = gather_rest != 0;
+      tile_bq = BQ;
+    }
+  }
+  if (dq_done) {
+  } else if (G <= 16) {
     const size_t lds = static_cast<size_t>(4) * 32 * (D + PAD) * sizeof(T);
     auto kern = bwd_dq_kernel<T, D, DV, false>;
     if (lds > 48 * 1024) {
@@ -1395,7 +1684,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     }
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), lds, stream, a,
                        static_cast<const T*>(args.dout), args.lse, ws.delta, static_cast<T*>(args.dq), G,
-                       static_cast<int>(items), latent, gather_head_major(a) ? 1 : 0);
+                       static_cast<int>(items), latent, gather_head_major(a) ? 1 : 0, tile_bq, tile_thr_milli());
   } else {
     const int slices = (G + 15) / 16;
     const size_t lds = static_cast<size_t>(32) * ((D + PAD) + (latent ? 0 : (DV + PAD))) * sizeof(T);
@@ -1407,7 +1696,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     }
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(items)), dim3(64 * slices), lds, stream, a,
                        static_cast<const T*>(args.dout), args.lse, ws.delta, static_cast<T*>(args.dq), G,
-                       static_cast<int>(items), latent, 0);
+                       static_cast<int>(items), latent, 0, 0, 0);
   }
   const int nkt = (a.S_k + 15) / 16;
   const int64_t kitems = static_cast<int64_t>(a.B) * nkt * a.Hkv;

@@ -475,47 +475,6 @@ IRB_DEV void fwd_item_gather(const AttnArgs& a, uint16_t* __restrict__ out, floa
 // 128 columns of MFMA work, so a tile is taken here only when its route
 // entries fill at least thr/1000 of (valid queries x key span); the gather
 // kernel handles the other tiles (both kernels evaluate the same integer test).
-constexpr int kSegTiles = 256;   // 32-key tiles per mask segment (8192 keys)
-
-struct TileStats {
-  bool dense;
-  int kmin, kmax;
-  int n_lane, last_lane;   // lane q < BQ: route length of query qa + q and its last entry
-};
-
-// Evaluated by a whole wavefront (uniform result).  BQ <= 64.
-IRB_DEV TileStats tile_stats_wave(const AttnArgs& a, int b, int kvh, int qa, int BQ, int thr_milli) {
-  const int lane = threadIdx.x & 63;
-  int kmin = 0x7fffffff, kmax = -1, total = 0, valid = 0;
-  const int t = qa + lane;
-  if (lane < BQ && t < a.S_q) {
-    const int64_t rrow = route_row(a, b, t, kvh);
-    const int n = max(0, min(a.lens[rrow], a.L));
-    valid = 1;
-    if (n > 0) {
-      const int32_t* r = a.routes + rrow * a.L;
-      kmin = r[0];
-      kmax = r[n - 1];
-      total = n;
-    }
-  }
-  const int lane_n = total, lane_last = kmax;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, __shfl_xor(kmin, o, 64));
-    kmax = max(kmax, __shfl_xor(kmax, o, 64));
-    total += __shfl_xor(total, o, 64);
-    valid += __shfl_xor(valid, o, 64);
-  }
-  TileStats st;
-  st.kmin = max(kmin, 0);
-  st.kmax = min(kmax, a.S_k - 1);
-  const int64_t span = st.kmax >= st.kmin ? static_cast<int64_t>(st.kmax - st.kmin + 1) : 0;
-  st.dense = total > 0 && span > 0 && static_cast<int64_t>(total) * 1000 >= static_cast<int64_t>(thr_milli) * valid * span;
-  st.n_lane = lane_n;
-  st.last_lane = lane_last;
-  return st;
-}
 
 template <typename T, int D, int DV, bool kShared, bool kDelta>
 __global__ void __launch_bounds__(256, (kShared || D > 128 || sizeof(T) == 4) ? 1 : 3)
@@ -1034,7 +993,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
 }
 
 // route-density threshold (per mille) above which a query tile runs on the tile kernel
-static int tile_thr_milli() {
+int tile_thr_milli() {
   static int v = [] {
     const char* e = getenv("IRB_TILE_MIN_DENSITY");
     return e ? static_cast<int>(atof(e) * 1000.0) : 120;

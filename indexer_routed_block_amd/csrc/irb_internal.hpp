@@ -109,6 +109,56 @@ __device__ __forceinline__ int64_t route_row(const AttnArgs& a, int b, int t, in
   return (static_cast<int64_t>(a.RG > 1 ? kvh : 0) * a.B + b) * a.S_q + t;
 }
 
+// ---- query tiles (forward and dq query-tile kernels)
+constexpr int kSegTiles = 256;   // 32-key tiles per mask segment (8192 keys)
+
+// route-density threshold (per mille) above which a query tile runs on the
+// query-tile kernels (IRB_TILE_MIN_DENSITY overrides it)
+int tile_thr_milli();
+
+// Statistics of the query tile [qa, qa + BQ) of batch b, KV head kvh: whether
+// its routes are dense enough in their key range for the tile kernels.
+struct TileStats {
+  bool dense;
+  int kmin, kmax;
+  int n_lane, last_lane;   // lane q < BQ: route length of query qa + q and its last entry
+};
+
+// Evaluated by a whole wavefront (uniform result).  BQ <= 64.
+__device__ __forceinline__ TileStats tile_stats_wave(const AttnArgs& a, int b, int kvh, int qa, int BQ, int thr_milli) {
+  const int lane = threadIdx.x & 63;
+  int kmin = 0x7fffffff, kmax = -1, total = 0, valid = 0;
+  const int t = qa + lane;
+  if (lane < BQ && t < a.S_q) {
+    const int64_t rrow = route_row(a, b, t, kvh);
+    const int n = max(0, min(a.lens[rrow], a.L));
+    valid = 1;
+    if (n > 0) {
+      const int32_t* r = a.routes + rrow * a.L;
+      kmin = r[0];
+      kmax = r[n - 1];
+      total = n;
+    }
+  }
+  const int lane_n = total, lane_last = kmax;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, __shfl_xor(kmin, o, 64));
+    kmax = max(kmax, __shfl_xor(kmax, o, 64));
+    total += __shfl_xor(total, o, 64);
+    valid += __shfl_xor(valid, o, 64);
+  }
+  TileStats st;
+  st.kmin = max(kmin, 0);
+  st.kmax = min(kmax, a.S_k - 1);
+  const int64_t span = st.kmax >= st.kmin ? static_cast<int64_t>(st.kmax - st.kmin + 1) : 0;
+  st.dense = total > 0 && span > 0 && static_cast<int64_t>(total) * 1000 >= static_cast<int64_t>(thr_milli) * valid * span;
+  st.n_lane = lane_n;
+  st.last_lane = lane_last;
+  return st;
+}
+
+
 // Per-query gather kernels visit work items (b, t, KV head).  When the K/V rows
 // of all heads outgrow the chip's last-level cache (256 MiB of Infinity Cache
 // on MI355X; half of it is the threshold), the items run head-major -- every
