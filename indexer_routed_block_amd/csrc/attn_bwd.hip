@@ -1130,7 +1130,7 @@ template <int D, int DV, int GP>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
                      const int32_t* __restrict__ hit_t, const uint32_t* __restrict__ hit_m, int64_t cap, int G,
-                     int Gp_rt, int nkt, int n_items, int merged) {
+                     int Gp_rt, int nkt, int merged) {
   constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
   const int Gp = GP > 0 ? GP : Gp_rt;
   // row pitches of the slabs: 8 dwords apart modulo 64 banks, so the 8-byte
@@ -1141,11 +1141,15 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   const AttnArgs& a = args.f;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g16 = lane >> 4, l16 = lane & 15;
-  const int item = blockIdx.x * 4 + wid;
-  if (item >= n_items) return;
-  const int kvh = item % a.Hkv;
-  const int jt = (item / a.Hkv) % nkt;
-  const int b = item / (a.Hkv * nkt);
+  // one workgroup per (b, four consecutive 16-key tiles, KV head), wave w on
+  // tile 4 J + w: neighbouring tiles' lists share queries (a window, dense
+  // routes), whose q / dO rows the four waves then find in the L2
+  const int ngrp = (nkt + 3) / 4;
+  const int kvh = blockIdx.x % a.Hkv;
+  const int J = (blockIdx.x / a.Hkv) % ngrp;
+  const int b = blockIdx.x / (a.Hkv * ngrp);
+  const int jt = 4 * J + wid;
+  if (jt >= nkt) return;
   const int k0 = 16 * jt;
   const int kid = k0 + l16;
   const bool kok = kid < a.S_k;
@@ -1709,10 +1713,10 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 1,
                        ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
     if constexpr (kGqaHits) {
-      const dim3 grid(static_cast<unsigned>((kitems + 3) / 4));
+      const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * ((nkt + 3) / 4) * a.Hkv));
 #define IRB_DKDV_HITS(GPV)                                                                                   \
   hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV, GPV>), grid, dim3(256), 0, stream, args, ws.delta, ws.hit_off, \
-                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, static_cast<int>(kitems), merged)
+                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, merged)
       if (Gp == 4) IRB_DKDV_HITS(4);
       else if (Gp == 8) IRB_DKDV_HITS(8);
       else if (Gp == 16) IRB_DKDV_HITS(16);
