@@ -49,7 +49,8 @@ FP32_VALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector (published)
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_s8192_hbm_traffic.json")
 # the forward call's kernels: route-bit packing and the attention kernels
-FWD_SOURCES = [os.path.join(ROOT, "indexer_routed_block_amd", "csrc", f) for f in ("attn_fwd.hip", "bitmap.hip")]
+FWD_SOURCES = [os.path.join(ROOT, "indexer_routed_block_amd", "csrc", f)
+               for f in ("attn_fwd.hip", "bitmap.hip", "irb_internal.hpp", "irb_common.hpp")]
 
 
 def parse():
