@@ -156,6 +156,11 @@ struct BwdWs {
   int32_t* hit_t;     //           [cap] query of each hit
   uint32_t* hit_m;    //           [cap] its 16-bit key mask
   int64_t cap;        // every (group, key tile, query) with a routed key: <= RG * B * S_q * min(L, nkt)
+  // union lists of 64-key groups (bf16 GQA): counts then offsets, queries, four 16-bit masks each
+  int64_t* off64;     // [RG * B * ngrp + 1]
+  int32_t* t64;       // [cap64]
+  uint16_t* m64;      // [cap64][4]
+  int64_t cap64;      // <= RG * B * S_q * min(L, ngrp)
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -163,6 +168,31 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static int64_t hit_capacity(int B, int S_q, int S_k, int L, int RG) {
   const int64_t nkt = (static_cast<int64_t>(S_k) + 15) / 16;
   return static_cast<int64_t>(RG) * B * S_q * std::min<int64_t>(L, nkt);
+}
+
+// the key side's union lists of 64-key groups: bf16 GQA shapes whose query
+// bitmap (S_q bits plus a count per word) fits 64 KiB of LDS
+static bool uses_union(int dtype, int Dqk, int Dv, int S_q) {
+  static const bool on = [] {
+    const char* e = getenv("IRB_KEY_UNION");
+    return !(e && e[0] == '0');
+  }();
+  return on && dtype == IRB_BF16 && Dqk == Dv && (Dqk == 64 || Dqk == 128) &&
+         (static_cast<int64_t>(S_q) + 31) / 32 * 8 <= 65536;
+}
+// least overlap (per mille: sum of a 64-key group's four tile-list counts
+// over its union count) for the shared-batch key side; IRB_KEY_UNION_MIN_OVERLAP
+// overrides it
+static int key_overlap_milli() {
+  static const int v = [] {
+    const char* e = getenv("IRB_KEY_UNION_MIN_OVERLAP");
+    return e ? static_cast<int>(atof(e) * 1000.0) : 2000;
+  }();
+  return v;
+}
+static int64_t union_capacity(int B, int S_q, int S_k, int L, int RG) {
+  const int64_t ngrp = (static_cast<int64_t>(S_k) + 63) / 64;
+  return static_cast<int64_t>(RG) * B * S_q * std::min<int64_t>(L, ngrp);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype,
@@ -175,6 +205,11 @@ size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv,
     const size_t nkt = (static_cast<size_t>(S_k) + 15) / 16;
     const size_t cap = static_cast<size_t>(hit_capacity(B, S_q, S_k, L, RG));
     n += align256((static_cast<size_t>(RG) * B * nkt + 1) * 8) + 2 * align256(cap * 4);
+    if (G <= 32 && uses_union(dtype, Dqk, Dv, S_q)) {
+      const size_t ngrp = (static_cast<size_t>(S_k) + 63) / 64;
+      const size_t cap64 = static_cast<size_t>(union_capacity(B, S_q, S_k, L, RG));
+      n += align256((static_cast<size_t>(RG) * B * ngrp + 1) * 8) + align256(cap64 * 4) + align256(cap64 * 8);
+    }
     // 64 heads over shared latent rows: the query-major path (used when v aliases k)
     if (dtype == IRB_BF16 && Dqk == 576 && Dv == 512 && G == 64)
       n = std::max(n, latent_bwd_workspace_bytes(B, S_q, S_k, L, Hq, Hkv));
@@ -201,6 +236,16 @@ static BwdWs carve(void* ws, int B, int S_q, int S_k, int L, int Hq, int Hkv, in
     w.hit_t = reinterpret_cast<int32_t*>(p);
     p += align256(static_cast<size_t>(w.cap) * 4);
     w.hit_m = reinterpret_cast<uint32_t*>(p);
+    p += align256(static_cast<size_t>(w.cap) * 4);
+    if (G <= 32 && uses_union(dtype, Dqk, Dv, S_q)) {
+      const size_t ngrp = (static_cast<size_t>(S_k) + 63) / 64;
+      w.cap64 = union_capacity(B, S_q, S_k, L, RG);
+      w.off64 = reinterpret_cast<int64_t*>(p);
+      p += align256((static_cast<size_t>(RG) * B * ngrp + 1) * 8);
+      w.t64 = reinterpret_cast<int32_t*>(p);
+      p += align256(static_cast<size_t>(w.cap64) * 4);
+      w.m64 = reinterpret_cast<uint16_t*>(p);
+    }
   } else {
     const size_t esz = dtype == IRB_BF16 ? 2 : 4;
     w.qt = p;
@@ -534,6 +579,20 @@ bwd_dq_kernel(AttnArgs a, const T* __restrict__ dout, const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------- dq, query tiles
+// XOR swizzle of the dq tile kernel's K and V rows (NC 16-byte chunks per
+// row): chunk c of row r at position c ^ dqt_swz<NC>(r).  NC = 16: row bits
+// 0, 1 to bits 2, 3 and bits 2, 3 to bits 0, 1 -- a permutation, so the 16
+// rows of a 16-lane row read fall on distinct banks, and four consecutive
+// rows take distinct bits 2-3, so the 32-lane transpose reads (four rows x
+// four neighbouring chunks) do too.  Row r + 8 (r < 8) is row r's pattern
+// with bit 1 flipped, row r + 16 the same pattern.  NC = 8: c ^ 2r.
+template <int NC>
+IRB_DEV int dqt_swz(int r) {
+  if constexpr (NC >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (2 * r) & 7;
+}
+
+
 // bf16 GQA with D = Dv in {64, 128} and G in {4, 8, 16}: one workgroup per
 // (query tile of 128 / G queries, KV head), organised like the forward's
 // query-tile kernel.  The tile's 128 (query, head) pairs are the MFMA columns
@@ -562,7 +621,7 @@ bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* _
   constexpr int NDT = D / 32;    // 32-dim row tiles of dQ^T
   constexpr int NC = D / 8;      // 16-byte chunks per K or V row
   // K and V rows of a key tile, row-major (K first), chunk c of row r at slot
-  // c ^ (2 r mod NC): the transpose reads of four rows (K^T) hit distinct banks
+  // c ^ dqt_swz(r)
   constexpr int KBYTES = 32 * D * 2;
   constexpr int BUF = 2 * KBYTES;
   constexpr int NI = 32 * NC / 256;        // direct loads per wave per tile side
@@ -627,7 +686,7 @@ bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* _
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
     const int slot = (wv * NI + n) * 64 + lane;
-    const int r = slot / NC, sw = (slot % NC) ^ ((2 * r) & (NC - 1));
+    const int r = slot / NC, sw = (slot % NC) ^ dqt_swz<NC>(r);
     koff[n] = static_cast<uint32_t>(r * a.sk_t + 8 * sw) * 2u;
     voff[n] = static_cast<uint32_t>(r * a.sv_t + 8 * sw) * 2u;
   }
@@ -650,7 +709,7 @@ bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* _
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
         const int slot = (wv * NI + n) * 64 + lane;
-        const int r = slot / NC, sw = (slot % NC) ^ ((2 * r) & (NC - 1));
+        const int r = slot / NC, sw = (slot % NC) ^ dqt_swz<NC>(r);
         const int rr = min(r, lim);
         lds_dma16_s(ks, static_cast<uint32_t>(rr * a.sk_t + 8 * sw) * 2u, ld + n * 1024);
         lds_dma16_s(vs, static_cast<uint32_t>(rr * a.sv_t + 8 * sw) * 2u, ld + KBYTES + n * 1024);
@@ -665,22 +724,25 @@ bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* _
   uint32_t rofs[KS], tofs[NDT];
 #pragma unroll
   for (int s = 0; s < KS; ++s)
-    rofs[s] = static_cast<uint32_t>(l32 * D + 8 * ((2 * s + h32) ^ ((2 * l32) & (NC - 1)))) * 2u;
+    rofs[s] = static_cast<uint32_t>(l32 * D + 8 * ((2 * s + h32) ^ dqt_swz<NC>(l32))) * 2u;
   {
     const int s16 = lane & 15, g2 = (lane >> 4) & 1;
     const int vr = 4 * h32 + (s16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const int vc = 4 * dt + 2 * g2 + ((s16 & 3) >> 1);
-      tofs[dt] = static_cast<uint32_t>(vr * D + 8 * (vc ^ ((2 * vr) & (NC - 1))) + 4 * (s16 & 1)) * 2u;
+      tofs[dt] = static_cast<uint32_t>(vr * D + 8 * (vc ^ dqt_swz<NC>(vr)) + 4 * (s16 & 1)) * 2u;
     }
   }
   // K^T operand of dim tile dt, k-step t2: keys 16 t2 + 4 h32 + {0..3, 8..11},
   // the order in which S^T's accumulator holds them (B operand straight from it)
+  // rows 8 further: the same positions with bit 1 flipped (NC = 16), bit 1
+  // of this lane's position being bit 1 of its chunk, (lane / 16) % 2
+  const int tdel = NC >= 16 ? (((lane >> 4) & 1) ? -32 : 32) : 0;
   auto kread = [&](uint32_t slot, int dt, int t2) __attribute__((always_inline)) {
     const char* p = raw + slot + tofs[dt] + t2 * 16 * D * 2;
     const v4s v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(p));
-    const v4s v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(p + 8 * D * 2));
+    const v4s v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(p + 8 * D * 2 + tdel));
     return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
   };
 
@@ -1123,14 +1185,109 @@ bwd_scan_kernel(int64_t* __restrict__ v, int64_t n, int64_t cap, int64_t* __rest
   }
 }
 
+// ---------------------------------------------------------------- union hit lists
+// Hit lists of 64-key groups (four consecutive 16-key tiles) for the shared-
+// batch mode of the key side.  One workgroup per (route group, b, group): the
+// queries of the group's four tile lists (entries with a non-zero key mask)
+// are marked in an LDS bitmap over the row's S_q queries; pass 0 counts
+// them, pass 1 writes them ascending from off64[group] on (never past cap64)
+// with the four tiles' 16-bit masks side by side (0 where a tile's list lacks
+// the query).  LDS: the bitmap, then (pass 1) each word's exclusive count.
+__global__ void __launch_bounds__(256)
+bwd_union_kernel(int S_q, int nkt, int ngrp, int pass, const int64_t* __restrict__ hit_off,
+                 const int32_t* __restrict__ hit_t, const uint32_t* __restrict__ hit_m, int64_t cap,
+                 int64_t* __restrict__ off64, int32_t* __restrict__ t64, uint16_t* __restrict__ m64, int64_t cap64) {
+  extern __shared__ uint32_t ub[];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x;
+  const int words = (S_q + 31) / 32;
+  uint32_t* bm = ub;
+  int* pre = reinterpret_cast<int*>(ub + words);
+  const int64_t grow = blockIdx.x;
+  const int64_t gb = grow / ngrp;
+  const int J = static_cast<int>(grow % ngrp);
+  const int64_t lrow0 = gb * nkt + 4 * J;
+  const int ntl = min(4, nkt - 4 * J);
+  for (int i = tid; i < words; i += 256) bm[i] = 0u;
+  __syncthreads();
+  for (int w = 0; w < ntl; ++w) {
+    const int64_t h0 = min(hit_off[lrow0 + w], cap), h1 = min(hit_off[lrow0 + w + 1], cap);
+    for (int64_t e = h0 + tid; e < h1; e += 256) {
+      const int t = hit_t[e];
+      if (t >= 0 && t < S_q && hit_m[e] != 0u) atomicOr(&bm[t >> 5], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  if (pass == 0) {
+    int c = 0;
+    for (int i = tid; i < words; i += 256) c += __popc(bm[i]);
+    int tot;
+    block_scan256(c, wsum, &tot);
+    if (tid == 0) off64[grow] = tot;
+    return;
+  }
+  const int64_t base = min(off64[grow], cap64), end = min(off64[grow + 1], cap64);
+  int run = 0;
+  for (int w0 = 0; w0 < words; w0 += 256) {
+    const int i = w0 + tid;
+    const uint32_t x = i < words ? bm[i] : 0u;
+    const int pc = __popc(x);
+    int tot;
+    const int incl = block_scan256(pc, wsum, &tot);
+    int o = run + incl - pc;
+    if (i < words) pre[i] = o;
+    uint32_t y = x;
+    while (y) {
+      const int bit = __ffs(y) - 1;
+      y &= y - 1;
+      const int64_t pos = base + o++;
+      if (pos < end) {
+        t64[pos] = i * 32 + bit;
+        *reinterpret_cast<uint2*>(m64 + 4 * pos) = make_uint2(0u, 0u);
+      }
+    }
+    run += tot;
+  }
+  // the zeroed masks are in place before the tiles' fields are written
+  __syncthreads();
+  for (int w = 0; w < ntl; ++w) {
+    const int64_t h0 = min(hit_off[lrow0 + w], cap), h1 = min(hit_off[lrow0 + w + 1], cap);
+    for (int64_t e = h0 + tid; e < h1; e += 256) {
+      const int t = hit_t[e];
+      const uint32_t m = hit_m[e];
+      if (t < 0 || t >= S_q || m == 0u) continue;
+      const int64_t pos = base + pre[t >> 5] + __popc(bm[t >> 5] & ((1u << (t & 31)) - 1u));
+      if (pos < end) m64[4 * pos + w] = static_cast<uint16_t>(m);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dk / dv over hit lists
+// Whether 64-key group J of (b, KV head kvh) runs in shared batches: its
+// four 16-key tile lists hold at least overlap_milli / 1000 times as many
+// entries as their union (off64 == nullptr: no union lists, never).  Every
+// wave of both key-side launches evaluates the same counts.
+IRB_DEV bool union_group(const AttnArgs& a, int b, int kvh, int J, int nkt, int ngrp,
+                         const int64_t* __restrict__ hit_off, int64_t cap, const int64_t* __restrict__ off64,
+                         int64_t cap64, int overlap_milli) {
+  if (off64 == nullptr) return false;
+  const int64_t g = static_cast<int64_t>(a.RG > 1 ? kvh : 0) * a.B + b;
+  const int64_t lrow64 = g * ngrp + J;
+  const int64_t u = min(off64[lrow64 + 1], cap64) - min(off64[lrow64], cap64);
+  const int64_t l0 = g * nkt + 4 * J, l1 = g * nkt + min(4 * J + 4, nkt);
+  const int64_t sumc = min(hit_off[l1], cap) - min(hit_off[l0], cap);
+  return u > 0 && u * overlap_milli <= sumc * 1000;
+}
+
+
 // GP > 0: the padded group size as a constant (4, 8, 16, 32: the row ->
 // (query, head) splits below become shifts and masks); 0: Gp_rt at run time
 template <int D, int DV, int GP>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
                      const int32_t* __restrict__ hit_t, const uint32_t* __restrict__ hit_m, int64_t cap, int G,
-                     int Gp_rt, int nkt, int merged) {
+                     int Gp_rt, int nkt, int merged, const int64_t* __restrict__ off64, int64_t cap64,
+                     int overlap_milli) {
   constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
   const int Gp = GP > 0 ? GP : Gp_rt;
   // row pitches of the slabs: 8 dwords apart modulo 64 banks, so the 8-byte
@@ -1149,6 +1306,8 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   const int J = (blockIdx.x / a.Hkv) % ngrp;
   const int b = blockIdx.x / (a.Hkv * ngrp);
   const int jt = 4 * J + wid;
+  // groups whose tile lists overlap enough are the shared-batch kernel's
+  if (GP > 0 && union_group(a, b, kvh, J, nkt, ngrp, hit_off, cap, off64, cap64, overlap_milli)) return;
   if (jt >= nkt) return;
   const int k0 = 16 * jt;
   const int kid = k0 + l16;
@@ -1419,6 +1578,311 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = adk[dt][i] * a.scale + (dt < NDV ? adv[dt < NDV ? dt : 0][i] : 0.f);
+      bstore4(dkp + dt * 16, v);
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+      const float v[4] = {adk[dt][0] * a.scale, adk[dt][1] * a.scale, adk[dt][2] * a.scale, adk[dt][3] * a.scale};
+      bstore4(dkp + dt * 16, v);
+    }
+    uint16_t* dvp = static_cast<uint16_t*>(args.dv) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * DV + 4 * g16;
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt) {
+      const float v[4] = {adv[dt][0], adv[dt][1], adv[dt][2], adv[dt][3]};
+      bstore4(dvp + dt * 16, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dk / dv in shared batches
+// 4-byte direct global-to-LDS load (global_load_lds_dword): lane i writes LDS
+// bytes [lds_base + 4 i, + 4); inactive lanes write nothing
+IRB_DEV void lds_dma4(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
+}
+
+// 16-byte chunk position of chunk c of row r in a shared-batch row buffer:
+// c ^ f(r & 15), f a bit permutation (row bits 0-2 to bits 1-3, bit 3 to
+// bit 0), so that the A-operand reads of 16 consecutive rows at one chunk
+// and the 32-lane transpose reads of eight consecutive rows at two
+// neighbouring chunks both hit distinct banks (rows are 256 bytes, whole
+// bank rounds, so without it they would not; 128-byte rows use three bits)
+template <int NC>
+IRB_DEV int ub_pos(int r, int c) {
+  const int f = NC > 8 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (((r & 3) << 1) | ((r >> 2) & 1));
+  return c ^ f;
+}
+
+// Groups of four 16-key tiles whose lists overlap (union_group): one
+// workgroup per (b, group, KV head), wave w on tile 4 J + w with its keys and
+// values as B operands as in bwd_dkdv_hits_kernel.  The group's union list
+// runs in batches of QPB queries (32 rows); each batch's q and dO rows, the
+// rows' lse and Delta and the queries' key masks go by direct global-to-LDS
+// loads into one of four buffers, three batches ahead of the one being
+// computed, so a workgroup keeps three batches of loads in flight; each
+// batch's loads also bring the query ids of the batch three later, which
+// address that batch's loads once this one has landed.  Every
+// wave applies its own tile to each batch (skipping batches that reach none
+// of its keys) exactly as the per-tile kernel does, so the sums differ only
+// in the order of their terms.
+template <int D, int DV, int GP>
+__global__ void __launch_bounds__(256, 2)
+bwd_dkdv_union_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
+                      int64_t cap, int G, int nkt, int merged, const int64_t* __restrict__ off64,
+                      const int32_t* __restrict__ t64, const uint16_t* __restrict__ m64, int64_t cap64,
+                      int overlap_milli) {
+  static_assert(D == DV && GP >= 4 && GP <= 32, "shared batches: one row layout, whole queries per batch");
+  constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
+  constexpr int QPB = 32 / GP;               // queries per batch
+  constexpr int NC = D / 8;                  // 16-byte chunks per row
+  constexpr int RB = D * 2;                  // bytes per row
+  constexpr int QB = 32 * RB;                // a batch's q rows (then its dO rows)
+  constexpr int SB = 2 * QB + 256 + 64 + 32; // + lse[32], Delta[32], masks (2 words per query), ids of batch + 3
+  constexpr int NBUF = 4;
+  constexpr int NRI = 2 * 32 * NC / 256;     // 16-byte row loads per wave and batch
+  static_assert(NRI >= 1 && (2 * 32 * NC) % 256 == 0, "row loads");
+  __shared__ __align__(16) char lds[NBUF * SB];
+  const AttnArgs& a = args.f;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wid);
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int ngrp = (nkt + 3) / 4;
+  const int kvh = blockIdx.x % a.Hkv;
+  const int J = (blockIdx.x / a.Hkv) % ngrp;
+  const int b = blockIdx.x / (a.Hkv * ngrp);
+  if (!union_group(a, b, kvh, J, nkt, ngrp, hit_off, cap, off64, cap64, overlap_milli)) return;
+  const int jt = 4 * J + wid;
+  const bool live = jt < nkt;
+  const int k0 = 16 * jt;
+  const int kid = k0 + l16;
+  const bool kok = kid < a.S_k;
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* og = static_cast<const uint16_t*>(args.dout);
+  const int64_t lrow64 = (static_cast<int64_t>(a.RG > 1 ? kvh : 0) * a.B + b) * ngrp + J;
+  const int64_t u0 = min(off64[lrow64], cap64), u1 = min(off64[lrow64 + 1], cap64);
+  const int nb = static_cast<int>((u1 - u0 + QPB - 1) / QPB);
+
+  bf16x8 kb[KS], vb[VS];
+  {
+    const uint16_t* kr = static_cast<const uint16_t*>(a.k) + b * a.sk_b + static_cast<int64_t>(kok ? kid : 0) * a.sk_t +
+                         kvh * a.sk_h + 8 * g16;
+    const uint16_t* vr = static_cast<const uint16_t*>(a.v) + b * a.sv_b + static_cast<int64_t>(kok ? kid : 0) * a.sv_t +
+                         kvh * a.sv_h + 8 * g16;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      kb[s2] = *reinterpret_cast<const bf16x8*>(kr + 32 * s2);
+      if (!kok) bzero8(kb[s2]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < VS; ++s2) {
+      vb[s2] = *reinterpret_cast<const bf16x8*>(vr + 32 * s2);
+      if (!kok) bzero8(vb[s2]);
+    }
+  }
+  f32x4 adk[NDK], adv[NDV];
+#pragma unroll
+  for (int i = 0; i < NDK; ++i) adk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NDV; ++i) adv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sc2 = a.scale * kLog2eB;
+
+  // row loads: load n of this wave fills 16-byte slots (wv NRI + n) 64 + lane
+  // of the buffer; slot s < 32 NC is position s % NC of q row s / NC, the
+  // rest the same of the dO rows; row r is head r % GP of the batch's query r / GP
+  int rk[NRI], rh[NRI], rc[NRI];
+#pragma unroll
+  for (int n = 0; n < NRI; ++n) {
+    const int slot = (wv * NRI + n) * 64 + lane;
+    const int rs = slot % (32 * NC);
+    const int r = rs / NC;
+    rk[n] = r / GP;
+    rh[n] = r % GP;
+    rc[n] = ub_pos<NC>(r, rs % NC);          // the global chunk stored at this position (f is an involution)
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  // a batch's query ids as one vector value (registers)
+  typedef int TQ __attribute__((ext_vector_type(8)));
+  static_assert(QPB <= 8, "ids per batch");
+  auto tpick = [&](TQ tq, int k) __attribute__((always_inline)) {
+    int t = tq[0];
+#pragma unroll
+    for (int kk = 1; kk < QPB; ++kk) t = k == kk ? tq[kk] : t;
+    return t;
+  };
+  // query ids of batch j from memory (the first batches; entries past the list repeat its last)
+  auto load_t = [&](int j) __attribute__((always_inline)) {
+    const int64_t e0 = u0 + static_cast<int64_t>(j) * QPB;
+    TQ tq = TQ{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < QPB; ++kk) {
+      const int64_t e = e0 + kk < u1 ? e0 + kk : u1 - 1;
+      tq[kk] = t64[e];
+    }
+    return tq;
+  };
+  auto issue = [&](int j, TQ tq) __attribute__((always_inline)) {
+    const int64_t e0 = u0 + static_cast<int64_t>(j) * QPB;
+    const uint32_t base = lds0 + static_cast<uint32_t>(j % NBUF) * SB;
+#pragma unroll
+    for (int n = 0; n < NRI; ++n) {
+      const bool ok = e0 + rk[n] < u1 && rh[n] < G;
+      const int t = ok ? tpick(tq, rk[n]) : 0;
+      const int hh = kvh * G + (rh[n] < G ? rh[n] : 0);
+      const bool isq = (wv * NRI + n) * 64 < 32 * NC;       // wave-uniform
+      const uint16_t* src = isq ? qg + b * a.sq_b + static_cast<int64_t>(t) * a.sq_t + static_cast<int64_t>(hh) * a.sq_h + 8 * rc[n]
+                                : og + ((static_cast<int64_t>(b) * a.S_q + t) * a.Hq + hh) * DV + 8 * rc[n];
+      lds_dma16(src, base + (wv * NRI + n) * 1024);
+    }
+    if (wv == 0) {
+      // lse (lanes 0-31) and Delta (lanes 32-63) of the batch's 32 rows
+      const int r = lane & 31, k = r / GP, h = r % GP;
+      const bool ok = e0 + k < u1 && h < G;
+      const int64_t li = ok ? (static_cast<int64_t>(b) * a.Hq + kvh * G + h) * a.S_q + tpick(tq, k) : 0;
+      lds_dma4(lane < 32 ? args.lse + li : delta + li, base + 2 * QB);
+    } else if (wv == 1) {
+      // the queries' four 16-bit tile masks (two words each)
+      if (lane < 2 * QPB) {
+        const int64_t e = e0 + (lane >> 1) < u1 ? e0 + (lane >> 1) : u1 - 1;
+        lds_dma4(m64 + 4 * e + 2 * (lane & 1), base + 2 * QB + 256);
+      }
+    } else if (wv == 2) {
+      // the query ids of batch j + NBUF - 1
+      if (lane < QPB) {
+        const int64_t en = e0 + (NBUF - 1) * QPB + lane;
+        lds_dma4(t64 + (en < u1 ? en : u1 - 1), base + 2 * QB + 320);
+      }
+    }
+  };
+
+  // P and dS of a batch as bf16 high / low operands (as in the per-tile kernel)
+  struct PdS {
+    bf16x8 ph, pl, sh, sl;
+  };
+  auto tile_operand = [&](const char* buf, int u) __attribute__((always_inline)) {
+    const bool isv = u < NDV;
+    const char* rows = isv ? buf + QB : buf;
+    const int uu = isv ? u : u - NDV;
+    const int r = 4 * g16 + (l16 >> 2);
+    const int c = 2 * uu + ((l16 & 3) >> 1);
+    const char* p = rows + r * RB + 16 * ub_pos<NC>(r, c) + 8 * (l16 & 1);
+    const v4s x0 = lds_read_tr(reinterpret_cast<const uint16_t*>(p));
+    const v4s x1 = lds_read_tr(reinterpret_cast<const uint16_t*>(p + 16 * RB));   // row r + 16: same f
+    return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  };
+  constexpr int kAhead = 3;
+
+  if (nb > 0) {
+    const int npre = nb < NBUF - 1 ? nb : NBUF - 1;
+    for (int j = 0; j < npre; ++j) issue(j, load_t(j));
+    for (int i = 0; i < nb; ++i) {
+      // batch i's loads (this wave's) have landed once only the later
+      // batches' may still be out; then the barrier publishes every wave's
+      // (waves 0-2 issue one load per batch more than wave 3)
+      const int later = min(NBUF - 2, nb - 1 - i);
+      if (later <= 0) __builtin_amdgcn_s_waitcnt(kDmaWait<0>());
+      else if (later == 1) {
+        if (wv < 3) __builtin_amdgcn_s_waitcnt(kDmaWait<NRI + 1>());
+        else __builtin_amdgcn_s_waitcnt(kDmaWait<NRI>());
+      } else {
+        if (wv < 3) __builtin_amdgcn_s_waitcnt(kDmaWait<2 * (NRI + 1)>());
+        else __builtin_amdgcn_s_waitcnt(kDmaWait<2 * NRI>());
+      }
+      bare_barrier();
+      const char* buf = lds + (i % NBUF) * SB;
+      // every wave is done with batch i - 1: its buffer takes batch i + 3,
+      // addressed by the ids that batch i brought
+      if (i + NBUF - 1 < nb) {
+        const int* tn = reinterpret_cast<const int*>(buf + 2 * QB + 320);
+        TQ tq = TQ{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < QPB; ++kk) tq[kk] = tn[kk];
+        issue(i + NBUF - 1, tq);
+      }
+      const float* st = reinterpret_cast<const float*>(buf + 2 * QB);
+      const uint32_t* mw = reinterpret_cast<const uint32_t*>(buf + 2 * QB + 256);
+      const int64_t e0 = u0 + static_cast<int64_t>(i) * QPB;
+      float lsv[2][4], dlv[2][4];
+      bool rok[2][4];
+      int any = 0;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int k = (16 * rt + 4 * g16) / GP;
+        const uint32_t m16 = (mw[2 * k + (wid >> 1)] >> (16 * (wid & 1))) & 0xffffu;
+        const bool qok = e0 + k < u1 && ((m16 >> l16) & 1u);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r = 16 * rt + 4 * g16 + i4;
+          rok[rt][i4] = qok && (r % GP) < G;
+          lsv[rt][i4] = st[r];
+          dlv[rt][i4] = st[32 + r];
+          any |= rok[rt][i4] ? 1 : 0;
+        }
+      }
+      // a wave none of whose keys the batch reaches skips it
+      if (live && __ballot(any) != 0ull) {
+        f32x4 sacc[2], pacc[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          pacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const int r = 16 * rt + l16;
+#pragma unroll
+          for (int s2 = 0; s2 < KS; ++s2)
+            sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *reinterpret_cast<const bf16x8*>(buf + r * RB + 16 * ub_pos<NC>(r, g16 + 4 * s2)), kb[s2], sacc[rt], 0, 0, 0);
+#pragma unroll
+          for (int s2 = 0; s2 < VS; ++s2)
+            pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *reinterpret_cast<const bf16x8*>(buf + QB + r * RB + 16 * ub_pos<NC>(r, g16 + 4 * s2)), vb[s2], pacc[rt], 0,
+                0, 0);
+        }
+        PdS o;
+        {
+          float p[2][4], ds[2][4];
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const float e = fast_exp2(sacc[rt][i4] * sc2 - lsv[rt][i4] * kLog2eB);
+              p[rt][i4] = rok[rt][i4] ? e : 0.f;
+              ds[rt][i4] = rok[rt][i4] ? e * (pacc[rt][i4] - dlv[rt][i4]) : 0.f;
+            }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bput_f(o.ph, o.pl, j, p[0][j], true);
+            bput_f(o.ph, o.pl, 4 + j, p[1][j], true);
+            bput_f(o.sh, o.sl, j, ds[0][j], true);
+            bput_f(o.sh, o.sl, 4 + j, ds[1][j], true);
+          }
+        }
+        bf16x8 xa[kAhead + 1];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) xa[u] = tile_operand(buf, u);
+#pragma unroll
+        for (int u = 0; u < NDV + NDK; ++u) {
+          if (u + kAhead < NDV + NDK) xa[(u + kAhead) % (kAhead + 1)] = tile_operand(buf, u + kAhead);
+          const bf16x8 x = xa[u % (kAhead + 1)];
+          if (u < NDV) {
+            adv[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, o.ph, adv[u], 0, 0, 0);
+            adv[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, o.pl, adv[u], 0, 0, 0);
+          } else {
+            adk[u - NDV] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, o.sh, adk[u - NDV], 0, 0, 0);
+            adk[u - NDV] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, o.sl, adk[u - NDV], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  if (!kok) return;
+  uint16_t* dkp = static_cast<uint16_t*>(args.dk) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * D + 4 * g16;
+  if (merged) {
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = adk[dt][r] * a.scale + (dt < NDV ? adv[dt < NDV ? dt : 0][r] : 0.f);
       bstore4(dkp + dt * 16, v);
     }
   } else {
@@ -1713,16 +2177,40 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_hits_kernel, dim3(static_cast<unsigned>(ltiles)), dim3(256), 0, stream, args, nkt, 1,
                        ws.hit_off, ws.hit_t, ws.hit_m, ws.cap);
     if constexpr (kGqaHits) {
-      const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * ((nkt + 3) / 4) * a.Hkv));
+      const int ngrp = (nkt + 3) / 4;
+      const int64_t lgroups = static_cast<int64_t>(a.RG) * a.B * ngrp;
+      if (ws.off64) {
+        // union lists of the 64-key groups (count, offsets, fill)
+        const size_t lds = static_cast<size_t>((a.S_q + 31) / 32) * 8;
+        hipLaunchKernelGGL(bwd_union_kernel, dim3(static_cast<unsigned>(lgroups)), dim3(256), lds, stream, a.S_q, nkt,
+                           ngrp, 0, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, ws.off64, ws.t64, ws.m64, ws.cap64);
+        hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(256), 0, stream, ws.off64, lgroups, ws.cap64,
+                           static_cast<int64_t*>(nullptr));
+        hipLaunchKernelGGL(bwd_union_kernel, dim3(static_cast<unsigned>(lgroups)), dim3(256), lds, stream, a.S_q, nkt,
+                           ngrp, 1, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, ws.off64, ws.t64, ws.m64, ws.cap64);
+      }
+      // per-tile groups, then (with union lists) the shared-batch groups
+      const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * ngrp * a.Hkv));
+      const int ovl = key_overlap_milli();
 #define IRB_DKDV_HITS(GPV)                                                                                   \
   hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV, GPV>), grid, dim3(256), 0, stream, args, ws.delta, ws.hit_off, \
-                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, merged)
+                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, merged, ws.off64, ws.cap64, ovl)
       if (Gp == 4) IRB_DKDV_HITS(4);
       else if (Gp == 8) IRB_DKDV_HITS(8);
       else if (Gp == 16) IRB_DKDV_HITS(16);
       else if (Gp == 32) IRB_DKDV_HITS(32);
       else IRB_DKDV_HITS(0);
 #undef IRB_DKDV_HITS
+      if (ws.off64) {
+#define IRB_DKDV_UNION(GPV)                                                                                      \
+  hipLaunchKernelGGL((bwd_dkdv_union_kernel<D, DV, GPV>), grid, dim3(256), 0, stream, args, ws.delta, ws.hit_off, \
+                     ws.cap, G, nkt, merged, ws.off64, ws.t64, ws.m64, ws.cap64, ovl)
+        if (Gp == 4) IRB_DKDV_UNION(4);
+        else if (Gp == 8) IRB_DKDV_UNION(8);
+        else if (Gp == 16) IRB_DKDV_UNION(16);
+        else if (Gp == 32) IRB_DKDV_UNION(32);
+#undef IRB_DKDV_UNION
+      }
     } else if constexpr (kWide) {
       hipLaunchKernelGGL((bwd_dkdv_wide_kernel<D, DV>), dim3(static_cast<unsigned>(kitems)), dim3(256), 0, stream,
                          args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, nkt, merged);

@@ -517,8 +517,9 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   // K and V tiles are row-major (one key per row, no padding), filled by
   // direct global-to-LDS loads (lane i of a load writes 16-byte slot i).  The
   // 16-byte chunks of row r sit XOR-swizzled: chunk c of a K row at slot
-  // c ^ (r mod NCK), of a V row at slot c ^ (2 r mod NCV), so the K operand
-  // reads of 16 rows and the V^T transpose reads of 4 rows hit distinct banks.
+  // c ^ (r mod NCK), of a V row at slot c ^ tr_swz(r), so the K operand
+  // reads of 16 rows and the 32-lane V^T transpose reads (4 rows x 4 chunks;
+  // the reads 8 and 16 rows further use the same pattern) hit distinct banks.
   // Three slots, each holding one tile's K and V.
   constexpr int NCK = D / 8, NCV = DV / 8;            // 16-byte chunks per row
   constexpr int KBYTES = 32 * D * 2, VBYTES = 32 * DV * 2;
@@ -603,7 +604,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   for (int n = 0; n < NIV; ++n) {
     const int slot = (wv * NIV + n) * 64 + lane;
     const int r = slot / NCV, sc = slot % NCV;
-    voff[n] = static_cast<uint32_t>(r * a.sv_t + 8 * (sc ^ ((2 * r) & (NCV - 1)))) * 2u;
+    voff[n] = static_cast<uint32_t>(r * a.sv_t + 8 * (sc ^ tr_swz<NCV>(r))) * 2u;
   }
   const uint32_t lds0 = lds_addr(raw);
   // K rows of key tile kt into slot `buf` (kV = false) or its V rows (kV = true)
@@ -625,7 +626,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       for (int n = 0; n < NI; ++n) {
         const int slot = (wv * NI + n) * 64 + lane;
         const int r = slot / NC, sc = slot % NC;
-        const int sw = kV ? (sc ^ ((2 * r) & (NC - 1))) : (sc ^ (r & (NC - 1)));
+        const int sw = kV ? (sc ^ tr_swz<NC>(r)) : (sc ^ (r & (NC - 1)));
         lds_dma16_s(src, static_cast<uint32_t>(min(r, lim) * stride + 8 * sw) * 2u, ld + n * 1024);
       }
     }
@@ -646,7 +647,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const int vc = 4 * dt + 2 * g2 + ((s16 & 3) >> 1);
-      vofs[dt] = static_cast<uint32_t>(vr * DV + 8 * (vc ^ ((2 * vr) & (NCV - 1))) + 4 * (s16 & 1)) * 2u;
+      vofs[dt] = static_cast<uint32_t>(vr * DV + 8 * (vc ^ tr_swz<NCV>(vr)) + 4 * (s16 & 1)) * 2u;
     }
   }
   // S^T of the key tile in the slot at byte offset kslot

@@ -163,6 +163,20 @@ IRB_DEV void bare_barrier() {
   asm volatile("" : : : "memory");
 }
 
+// XOR swizzle of the 16-byte chunks of a row-major bf16 tile in LDS whose
+// rows span whole 256-byte bank rounds: chunk c of row r sits at position
+// c ^ tr_swz<NC>(r) (NC chunks per row).  It depends on r mod 8 only, so a
+// read 8 or 16 rows further is the same pattern at a constant offset.  For
+// NC = 16 the row's two low bits go to bits 2-3 and bit 2 to bit 0: the four
+// rows x four neighbouring chunks of a 32-lane transpose read
+// (ds_read_b64_tr_b16) fall on distinct banks, and 16 consecutive rows read
+// at one chunk on pairs of banks.  NC = 8 (128-byte rows): c ^ 2r.
+template <int NC>
+IRB_DEV int tr_swz(int r) {
+  if constexpr (NC >= 16) return ((r & 3) << 2) | ((r >> 2) & 1);
+  else return (2 * r) & 7;
+}
+
 // LDS transpose read (ds_read_b64_tr_b16): inside each 16-lane row of the
 // wavefront, lane 4 a + b receives element b of the 8-byte words that lanes
 // a, 4 + a, 8 + a and 12 + a address, in that order.  So if lane s of a row
