@@ -114,9 +114,12 @@ def test_gqa_bf16_batched_and_strided_q():
     _run_fwd_bwd(wl, x, routes, lens, 0.11, True, q_view=qv)
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(16, 4, 64), (16, 1, 64), (16, 2, 64), (8, 2, 128), (32, 2, 128)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 4, 64), (16, 1, 64), (16, 2, 64), (8, 2, 128), (32, 2, 128), (32, 1, 128),
+                                     (32, 1, 64)])
 def test_gqa_bf16_head_groups_and_widths_fwd_bwd(Hq, Hkv, D):
-    """Every (group size, head width) the query-tile and key-tile kernels are built for (G = 4, 8, 16; D = 64, 128)."""
+    """Every (group size, head width) the query-tile and key-tile kernels are built for (G = 4, 8, 16; D = 64, 128),
+    and G = 32 (one query per 32-row key-side batch; per-query forward and dQ).  The routes (96 of at most 300
+    keys) overlap enough that most 64-key groups run in shared batches."""
     banner(f"attn bf16 Hq={Hq} Hkv={Hkv} D={D} S=300")
     rng = np.random.default_rng(1000 + 7 * Hq + 3 * Hkv + D)
     S = 300
