@@ -196,6 +196,11 @@ def main():
     Hq = wl.Hq
     out = torch.empty((B, S, Hq, Dv), dtype=dt, device=dev)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    # training steps keep o in FP32 as well where the backward reads its row
+    # statistic off it (the library says where; elsewhere it forms it itself)
+    keep_o32 = wl.backward and bool(lib.irb_sparse_gqa_attention_bwd_reads_out_f32(
+        B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q), R))
+    out32 = torch.empty((B, S, Hq, Dv), dtype=torch.float32, device=dev) if keep_o32 else None
     strides = irb._strides9(q, k, v)
     fwd_ws_n = int(lib.irb_sparse_gqa_attention_fwd_workspace_size(B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q), R))
     fwd_ws = torch.empty(max(fwd_ws_n, 16), dtype=torch.uint8, device=dev)
@@ -258,13 +263,14 @@ def main():
     def attn_step(rec):
         timed("attn_fwd", lambda: C(lib.irb_sparse_gqa_attention_fwd(
             P(q), P(k), P(v), irb._dtype_code(q), strides, P(routes), P(lens), R, B, S, S, L, Hq, Hkv, Dqk, Dv,
-            scale, P(out), P(lse), P(fwd_ws) if fwd_ws_n > 0 else None, fwd_ws_n, sptr)), rec)
+            scale, P(out), P(lse), P(out32) if out32 is not None else None, P(fwd_ws) if fwd_ws_n > 0 else None,
+            fwd_ws_n, sptr)), rec)
         if backward:
             timed("reverse_lists", lambda: C(lib.irb_build_block_lists(
                 P(routes), P(lens), R * B, S, S, L, rbq, rbk, 1, P(rev_counts), P(rev_idx), nqt, P(lists_ws),
                 lists_ws.numel(), sptr)), rec)
             timed("attn_bwd", lambda: C(lib.irb_sparse_gqa_attention_bwd(
-                P(q), P(k), P(v), irb._dtype_code(q), strides, P(out), P(dO), P(lse), P(routes), P(lens), R,
+                P(q), P(k), P(v), irb._dtype_code(q), strides, P(out32), P(dO), P(lse), P(routes), P(lens), R,
                 P(rev_counts), P(rev_idx), rbq, rbk, nqt, B, S, S, L, Hq, Hkv, Dqk, Dv, scale, P(dq), P(dk), P(dv),
                 P(bwd_ws), bwd_ws.numel(), P(dropped), sptr)), rec)
 

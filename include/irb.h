@@ -481,6 +481,10 @@ int irb_split_full_blocks(const int32_t* routes, const int32_t* lens, int B, int
  *     group's routes are one [B, S_q, L] block (for B = 1 the CSA page's
  *     [batch, groups, queries, slots]).
  *   out OUT [B, S_q, Hq, Dv] dtype contiguous; lse OUT [B, Hq, S_q] fp32
+ *   out_f32 OUT, nullable: [B, S_q, Hq, Dv] fp32 contiguous, 16-byte aligned:
+ *     o before its rounding to the input dtype -- what the backward's
+ *     row statistic Delta = rowsum(dO * o) is read off (irb_sparse_gqa_
+ *     attention_bwd's out_f32), saving it a pass over the routes
  *   workspace: optional device scratch (16-byte aligned, NULL allowed) of
  *     irb_sparse_gqa_attention_fwd_workspace_size() bytes: the key-membership
  *     words of every route row ([FA4] _block_lists builds its block masks
@@ -499,7 +503,7 @@ size_t irb_sparse_gqa_attention_fwd_workspace_size(int B, int S_q, int S_k, int 
 int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype,
                                  const int64_t* strides, const int32_t* routes, const int32_t* lens,
                                  int route_groups, int B, int S_q, int S_k, int L, int Hq, int Hkv,
-                                 int Dqk, int Dv, float softmax_scale, void* out, float* lse,
+                                 int Dqk, int Dv, float softmax_scale, void* out, float* lse, float* out_f32,
                                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -517,9 +521,12 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
  * [RG, B, key tiles], indices [RG, B, key tiles, rev_width]; KV head g reads
  * group g's lists and routes.
  *
- *   out        the forward's output (accepted for interface symmetry, not read:
- *              Delta is recomputed with o in FP32 so that the rounding of the
- *              stored output does not enter dS)
+ *   out_f32    nullable: the forward's FP32 output (irb_sparse_gqa_attention_fwd
+ *              out_f32).  Given, Delta = rowsum(dO * o) is read off it; NULL,
+ *              Delta is formed with o in FP32 from the routes (the query side
+ *              sums P dP, or the forward runs again in Delta mode) -- never
+ *              from the stored, rounded output, whose rounding would enter
+ *              every dS.  16-byte aligned.
  *   lse        the forward's lse; dout [B, S_q, Hq, Dv] dtype contiguous
  *   dq OUT [B, S_q, Hq, Dqk] dtype contiguous
  *   dk OUT [B, S_k, Hkv, Dqk] dtype contiguous, dv OUT [B, S_k, Hkv, Dv]
@@ -541,8 +548,17 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
  */
 size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk,
                                                    int Dv, int dtype, int route_groups);
+/*
+ * 1 when irb_sparse_gqa_attention_bwd with these sizes reads Delta off an
+ * out_f32 given to it -- a pass over the routes (or a forward in Delta mode)
+ * is then saved, so a training step should have the forward write out_f32 --
+ * and 0 where its per-query dQ pass forms Delta anyway (the FP32 output would
+ * only cost its write).  Contiguous q / k / v assumed; 0 for invalid sizes.
+ */
+int irb_sparse_gqa_attention_bwd_reads_out_f32(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
+                                               int dtype, int route_groups);
 int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, int dtype,
-                                 const int64_t* strides, const void* out, const void* dout,
+                                 const int64_t* strides, const float* out_f32, const void* dout,
                                  const float* lse, const int32_t* routes, const int32_t* lens,
                                  int route_groups, const int32_t* rev_counts, const int32_t* rev_indices,
                                  int rev_block_q, int rev_block_k, int rev_width, int B, int S_q,

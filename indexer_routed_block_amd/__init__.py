@@ -66,8 +66,9 @@ _SIGS = {
     "irb_build_block_lists": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _SZ, _P], _I),
     "irb_sparse_gqa_attention_fwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "irb_sparse_gqa_attention_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P,
-                                      _P, _SZ, _P], _I),
+                                      _P, _P, _SZ, _P], _I),
     "irb_sparse_gqa_attention_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _I], _SZ),
+    "irb_sparse_gqa_attention_bwd_reads_out_f32": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _I], _I),
     "irb_sparse_gqa_attention_bwd": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
                                       _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P, _P], _I),
 }
@@ -585,13 +586,15 @@ def _route_groups(routes, lens):
 
 
 def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None, lse=None, workspace=None,
-                             use_workspace=True):
+                             use_workspace=True, out_f32=None):
     """irb_sparse_gqa_attention_fwd: (o [B,S_q,Hq,Dv] in q's dtype, lse [B,Hq,S_q] fp32).
 
     routes [B, S_q, L] are shared by every head; routes [Hkv, B, S_q, L]
     (lens [Hkv, B, S_q]) give every KV group its own routes.  The
     key-membership workspace is allocated here unless given or
-    ``use_workspace`` is False (then the query tiles build their masks in LDS)."""
+    ``use_workspace`` is False (then the query tiles build their masks in LDS).
+    ``out_f32`` (True, or an fp32 tensor of o's shape) also writes o before
+    its rounding, the backward's Delta input; the result is then (o, lse, o32)."""
     _gpu(q, k, v, routes, lens, out, lse, workspace)
     lib = load_library()
     _check_qkv(q, k, v, routes, lens)
@@ -605,6 +608,11 @@ def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None
         lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev)
     _req(out, "out", q.dtype, shape=(B, S_q, Hq, Dv))
     _req(lse, "lse", torch.float32, shape=(B, Hq, S_q))
+    if out_f32 is True:
+        out_f32 = torch.empty((B, S_q, Hq, Dv), dtype=torch.float32, device=dev)
+    elif out_f32 is not None:
+        _gpu(out_f32)
+        _req(out_f32, "out_f32", torch.float32, shape=(B, S_q, Hq, Dv))
     rg = _route_groups(routes, lens)
     if workspace is None and use_workspace:
         n = lib.irb_sparse_gqa_attention_fwd_workspace_size(B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv,
@@ -615,13 +623,18 @@ def sparse_gqa_attention_fwd(q, k, v, routes, lens, softmax_scale=None, out=None
     _check(lib.irb_sparse_gqa_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v),
                                             _ptr(routes), _ptr(lens), rg, B, S_q, S_k,
                                             routes.shape[-1], Hq, Hkv, Dqk, Dv, scale, _ptr(out), _ptr(lse),
-                                            _ptr(workspace), ws_bytes, _stream(dev)))
-    return out, lse
+                                            _ptr(out_f32), _ptr(workspace), ws_bytes, _stream(dev)))
+    return (out, lse) if out_f32 is None else (out, lse, out_f32)
 
 
 def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, rev_indices, rev_block_q,
-                             rev_block_k=16, softmax_scale=None, merged_kv=False, workspace=None, dropped_hits=None):
+                             rev_block_k=16, softmax_scale=None, merged_kv=False, workspace=None, dropped_hits=None,
+                             out_f32=None):
     """irb_sparse_gqa_attention_bwd: (dq, dk, dv); with merged_kv (v aliases k) dk holds dK + [dV, 0], dv is dk.
+
+    ``out`` (the forward's output in q's dtype) is not read: Delta comes from
+    ``out_f32`` (the forward's FP32 output, optional) or is formed from the
+    routes.
 
     ``dropped_hits`` (int64 [1] on the device, optional) receives the number of
     key-side hit entries that did not fit the workspace (0 for reverse lists
@@ -637,6 +650,9 @@ def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, 
     dev = q.device
     _req(dout, "dout", q.dtype, shape=(B, S_q, Hq, Dv))
     _req(lse, "lse", torch.float32, shape=(B, Hq, S_q))
+    if out_f32 is not None:
+        _gpu(out_f32)
+        _req(out_f32, "out_f32", torch.float32, shape=(B, S_q, Hq, Dv))
     _req(rev_counts, "rev_counts", I32)
     _req(rev_indices, "rev_indices", I32)
     _req(workspace, "workspace")
@@ -657,7 +673,7 @@ def sparse_gqa_attention_bwd(q, k, v, out, dout, lse, routes, lens, rev_counts, 
                                                             _dtype_code(q), rg)
         workspace = torch.empty(max(int(n), 4), dtype=torch.uint8, device=dev)
     _check(lib.irb_sparse_gqa_attention_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v), _ptr(out), _ptr(dout), _ptr(lse),
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _strides9(q, k, v), _ptr(out_f32), _ptr(dout), _ptr(lse),
         _ptr(routes), _ptr(lens), rg, _ptr(rev_counts), _ptr(rev_indices), rev_block_q, rev_block_k,
         rev_indices.shape[-1], B, S_q, S_k, routes.shape[-1], Hq, Hkv, Dqk, Dv, scale, _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(dropped_hits), _stream(dev)))

@@ -551,6 +551,7 @@ static int check_attn(const char* fn, const void* q, const void* k, const void* 
   a.routes = routes; a.lens = lens;
   a.B = B; a.S_q = S_q; a.S_k = S_k; a.L = L_width; a.Hq = Hq; a.Hkv = Hkv; a.Dqk = Dqk; a.Dv = Dv;
   a.scale = scale; a.dtype = dtype; a.RG = route_groups;
+  a.o32 = nullptr;
   return 0;
 }
 
@@ -567,13 +568,17 @@ size_t irb_sparse_gqa_attention_fwd_workspace_size(int B, int S_q, int S_k, int 
 int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
                                  const int32_t* routes, const int32_t* lens, int route_groups, int B, int S_q,
                                  int S_k, int L_width, int Hq, int Hkv, int Dqk, int Dv, float softmax_scale,
-                                 void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                                 void* out, float* lse, float* out_f32, void* workspace, size_t ws_bytes,
+                                 void* stream) {
   const char* fn = "irb_sparse_gqa_attention_fwd";
   irb::AttnArgs a;
   if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, route_groups, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv,
                      softmax_scale, a))
     return r;
   if (!out || !lse) return fail(IRB_ERR_INVALID, "%s: NULL output", fn);
+  if ((reinterpret_cast<uintptr_t>(out_f32) & 15) != 0)
+    return fail(IRB_ERR_INVALID, "%s: out_f32 must be 16-byte aligned", fn);
+  a.o32 = out_f32;
   if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
     return fail(IRB_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
   IRB_REQUIRE_DEVICE();
@@ -589,8 +594,14 @@ size_t irb_sparse_gqa_attention_bwd_workspace_size(int B, int S_q, int S_k, int 
   return irb::attn_bwd_workspace_bytes(B, S_q, S_k, L, Hq, Hkv, Dqk, Dv, dtype, route_groups);
 }
 
+int irb_sparse_gqa_attention_bwd_reads_out_f32(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv,
+                                               int dtype, int route_groups) {
+  if (route_groups != 1 && route_groups != Hkv) return 0;
+  return irb::attn_bwd_reads_out32(B, S_q, S_k, L, Hq, Hkv, Dqk, Dv, dtype, route_groups) ? 1 : 0;
+}
+
 int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, int dtype, const int64_t* strides,
-                                 const void* out, const void* dout, const float* lse, const int32_t* routes,
+                                 const float* out_f32, const void* dout, const float* lse, const int32_t* routes,
                                  const int32_t* lens, int route_groups, const int32_t* rev_counts,
                                  const int32_t* rev_indices,
                                  int rev_block_q, int rev_block_k, int rev_width, int B, int S_q, int S_k, int L_width,
@@ -601,7 +612,9 @@ int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, in
   if (int r = check_attn(fn, q, k, v, dtype, strides, routes, lens, route_groups, B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv,
                      softmax_scale, a.f))
     return r;
-  if (!out || !dout || !lse || !rev_counts || !rev_indices || !dq || !dk || !dv) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if (!dout || !lse || !rev_counts || !rev_indices || !dq || !dk || !dv) return fail(IRB_ERR_INVALID, "%s: NULL tensor", fn);
+  if ((reinterpret_cast<uintptr_t>(out_f32) & 15) != 0)
+    return fail(IRB_ERR_INVALID, "%s: out_f32 must be 16-byte aligned", fn);
   if (rev_block_k != 16) return fail(IRB_ERR_INVALID, "%s: rev_block_k must be 16 (got %d)", fn, rev_block_k);
   if (rev_block_q < 1) return fail(IRB_ERR_INVALID, "%s: rev_block_q must be >= 1", fn);
   if (rev_width < (S_q + rev_block_q - 1) / rev_block_q) return fail(IRB_ERR_INVALID, "%s: rev_width below the query tile count", fn);
@@ -609,7 +622,7 @@ int irb_sparse_gqa_attention_bwd(const void* q, const void* k, const void* v, in
   if (ws_bytes < irb::attn_bwd_workspace_bytes(B, S_q, S_k, L_width, Hq, Hkv, Dqk, Dv, dtype, route_groups))
     return fail(IRB_ERR_INVALID, "%s: workspace too small", fn);
   if (!workspace) return fail(IRB_ERR_INVALID, "%s: NULL workspace", fn);
-  a.out = out; a.dout = dout; a.lse = lse;
+  a.out32 = out_f32; a.dout = dout; a.lse = lse;
   a.rev_counts = rev_counts; a.rev_indices = rev_indices;
   a.rev_bq = rev_block_q; a.rev_bk = rev_block_k; a.rev_width = rev_width;
   a.dq = dq; a.dk = dk; a.dv = dv; a.ws = workspace; a.ws_bytes = ws_bytes; a.dropped = dropped_hits;

@@ -220,6 +220,25 @@ size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv,
   return n;
 }
 
+// whether the backward reads Delta off the forward's FP32 output when given
+// one: where a pass would otherwise form it (the query-tile dQ, a forward in
+// Delta mode, the latent path), not where the per-query dQ pass forms it
+// anyway (row strides as in contiguous q / k / v assumed)
+bool attn_bwd_reads_out32(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype, int RG) {
+  if (B < 1 || S_q < 1 || S_k < 1 || L < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return false;
+  const int G = Hq / Hkv;
+  if (dtype == IRB_BF16 && Dqk == 576 && Dv == 512 && G == 64) return true;
+  const bool fused = dtype == IRB_BF16 && Dqk <= 128 && G <= 16;
+  if (!fused) return true;
+  if (!(Dqk == Dv && (Dqk == 64 || Dqk == 128)) || !(G == 4 || G == 8 || G == 16)) return false;
+  AttnArgs a{};
+  a.B = B; a.S_q = S_q; a.S_k = S_k; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.Dqk = Dqk; a.Dv = Dv;
+  a.dtype = dtype; a.RG = RG;
+  const size_t qb = attn_fwd_qbits_bytes(a);
+  const size_t room = 2 * align256(static_cast<size_t>(hit_capacity(B, S_q, S_k, L, RG)) * 4);
+  return tile_thr_milli() <= 1000 && qb > 0 && qb <= room;
+}
+
 static BwdWs carve(void* ws, int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype, int RG) {
   const int G = Hq / Hkv;
   const size_t Gp = static_cast<size_t>(padded_group(G));
@@ -275,6 +294,51 @@ bwd_prep_kernel(AttnArgs a, const T* __restrict__ dout, T* __restrict__ qt, T* _
     const int hp = i % Gp, d = (i / Gp) % a.Dv, g = i / (Gp * a.Dv);
     ddst[i] = (hp < G) ? drow[static_cast<int64_t>(g * G + hp) * a.Dv + d] : T(0);
   }
+}
+
+// ---------------------------------------------------------------- delta from the FP32 output
+// Delta[b, h, t] = sum_d dO[b, t, h, d] o[b, t, h, d] with the forward's FP32
+// o: 16 lanes per (row, head), four elements per lane and step, summed
+// across the 16 lanes
+template <typename T>
+__global__ void __launch_bounds__(256)
+delta_from_o_kernel(const T* __restrict__ dout, const float* __restrict__ o32, float* __restrict__ delta, int B,
+                    int S_q, int Hq, int Dv) {
+  const int64_t g = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 4;   // (row, head)
+  const int l = threadIdx.x & 15;
+  const int64_t n = static_cast<int64_t>(B) * S_q * Hq;
+  const bool ok = g < n;
+  float part = 0.f;
+  if (ok) {
+    const T* dp = dout + g * Dv;
+    const float* op = o32 + g * Dv;
+    for (int d = 4 * l; d < Dv; d += 64) {
+      const float4 o = *reinterpret_cast<const float4*>(op + d);
+      part += load_as_f32(dp + d) * o.x + load_as_f32(dp + d + 1) * o.y + load_as_f32(dp + d + 2) * o.z +
+              load_as_f32(dp + d + 3) * o.w;
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 16);
+  if (ok && l == 0) {
+    const int h = static_cast<int>(g % Hq);
+    const int64_t bt = g / Hq;
+    const int b = static_cast<int>(bt / S_q), t = static_cast<int>(bt % S_q);
+    delta[(static_cast<int64_t>(b) * Hq + h) * S_q + t] = part;
+  }
+}
+
+int launch_delta_from_o(const AttnArgs& a, const void* dout, const float* o32, float* delta, hipStream_t stream) {
+  const int64_t groups = static_cast<int64_t>(a.B) * a.S_q * a.Hq;
+  if (groups == 0) return 0;
+  const dim3 grid(static_cast<unsigned>((groups * 16 + 255) / 256));
+  if (a.dtype == IRB_BF16)
+    hipLaunchKernelGGL(delta_from_o_kernel<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(dout),
+                       o32, delta, a.B, a.S_q, a.Hq, a.Dv);
+  else
+    hipLaunchKernelGGL(delta_from_o_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(dout), o32,
+                       delta, a.B, a.S_q, a.Hq, a.Dv);
+  return 0;
 }
 
 // ---------------------------------------------------------------- dq
@@ -606,7 +670,8 @@ IRB_DEV int dqt_swz(int r) {
 //      bf16, and dQ^T += K^T dS^T with K^T from LDS transpose reads.  dS is
 //      formed before the rounding, so each term carries only its own
 //      relative rounding (no cancellation is rounded in).
-// dQ = scale (dQ^T)^T; Delta is written for the key side.  Query tiles whose
+// dQ = scale (dQ^T)^T; Delta is written for the key side.  With Delta given
+// (have_delta: computed from the forward's FP32 output) only sweep 2 runs.  Query tiles whose
 // routes cover too little of their key range go per query (dq_item_gather):
 // here when gather_rest, else in the per-query launch, which skips this
 // kernel's tiles by the same test.
@@ -614,7 +679,7 @@ template <int D, int G>
 __global__ void __launch_bounds__(256, 2)
 bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
                    float* __restrict__ delta, uint16_t* __restrict__ dq, int n_qt, int thr_milli,
-                   const uint32_t* __restrict__ qbits, int qwords, int gather_rest) {
+                   const uint32_t* __restrict__ qbits, int qwords, int gather_rest, int have_delta) {
   using T = uint16_t;
   constexpr int BQ = 128 / G;
   constexpr int KS = D / 16;     // 16-dim k-steps of S^T and dP^T
@@ -826,8 +891,11 @@ bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* _
       }
     }
   };
-  sweep(std::false_type{});
-  {
+  if (have_delta) {
+    // Delta given (from the forward's FP32 output): the second sweep only
+    dlt = tok ? delta[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] : 0.f;
+  } else {
+    sweep(std::false_type{});
     // the column's two lane halves hold different keys
     const uint32_t u = __float_as_uint(dsum);
     const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -837,7 +905,7 @@ bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* _
 
   // ---- epilogue: this lane holds dims 32 dt + 8 j + 4 h32 + {0..3} of its column
   if (tok) {
-    if (h32 == 0) delta[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] = dlt;
+    if (h32 == 0 && !have_delta) delta[(static_cast<int64_t>(b) * a.Hq + hh) * a.S_q + t] = dlt;
     T* op = dq + ((static_cast<int64_t>(b) * a.S_q + t) * a.Hq + hh) * D + 4 * h32;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -2095,7 +2163,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
   const bool hits = kGqaHits || (kWide && G % 32 == 0);
   if constexpr (kWide)
     if (latent_bwd_applies(a, args.dk, args.dv))
-      return launch_latent_bwd(a, args.dout, args.lse, args.dq, args.dk, args.ws, args.dropped, stream);
+      return launch_latent_bwd(a, args.dout, args.lse, args.out32, args.dq, args.dk, args.ws, args.dropped, stream);
   BwdWs ws = carve(args.ws, a.B, a.S_q, a.S_k, a.L, a.Hq, a.Hkv, a.Dqk, a.Dv, a.dtype, a.RG);
   const int latent = (a.v == a.k && a.sv_b == a.sk_b && a.sv_t == a.sk_t && a.sv_h == a.sk_h) ? 1 : 0;
   const int64_t rows = static_cast<int64_t>(a.B) * a.S_q;
@@ -2103,22 +2171,33 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, a,
                        static_cast<const T*>(args.dout), static_cast<T*>(ws.qt), static_cast<T*>(ws.dot), G, Gp);
   }
-  // Delta = rowsum(dO o) with o in FP32: the bf16 query side with G <= 16
-  // forms it in its own pass (and writes it before the key side reads it);
-  // otherwise a forward pass in Delta mode recomputes o
-  if (!(G <= 16 && dq_fuses_delta<T, D>()))
+  // query tiles for dQ: key-membership words per route row, kept in the
+  // hit-list area of the workspace (the hit lists are built after the dQ pass)
+  bool tile_dq = false;
+  if constexpr (kGqaHits) {
+    const bool small_strides = static_cast<int64_t>(a.sk_t > a.sv_t ? a.sk_t : a.sv_t) * 64 < (int64_t{1} << 31);
+    const size_t qb = attn_fwd_qbits_bytes(a);
+    const size_t room = 2 * align256(static_cast<size_t>(ws.cap) * 4);
+    tile_dq = tile_thr_milli() <= 1000 && small_strides && (G == 4 || G == 8 || G == 16) && qb > 0 && qb <= room;
+  }
+  // Delta = rowsum(dO o) with o in FP32: read off the forward's FP32 output
+  // when given and a pass would otherwise form it (the query-tile dQ, or a
+  // forward in Delta mode); else the bf16 query side with G <= 16 forms it
+  // in its own pass (written before the key side reads it), and otherwise a
+  // forward pass in Delta mode recomputes o
+  const bool fused_delta = G <= 16 && dq_fuses_delta<T, D>();
+  const bool have_delta = args.out32 != nullptr && (tile_dq || !fused_delta);
+  if (have_delta) {
+    if (int rc = launch_delta_from_o(a, args.dout, args.out32, ws.delta, stream)) return rc;
+  } else if (!fused_delta) {
     if (int rc = launch_attn_delta(a, args.dout, ws.delta, stream)) return rc;
+  }
   const int PAD = sizeof(T) == 2 ? 8 : 4;
   const int64_t items = rows * a.Hkv;
   bool dq_done = false;
   int tile_bq = 0;   // > 0: the per-query launch skips the query tiles the tile kernel takes
   if constexpr (kGqaHits) {
-    // query tiles: key-membership words per route row, kept in the hit-list
-    // area of the workspace (the hit lists are built after this pass)
-    const bool small_strides = static_cast<int64_t>(a.sk_t > a.sv_t ? a.sk_t : a.sv_t) * 64 < (int64_t{1} << 31);
-    const size_t qb = attn_fwd_qbits_bytes(a);
-    const size_t room = 2 * align256(static_cast<size_t>(ws.cap) * 4);
-    if (tile_thr_milli() <= 1000 && small_strides && (G == 4 || G == 8 || G == 16) && qb > 0 && qb <= room) {
+    if (tile_dq) {
       uint32_t* qbits = reinterpret_cast<uint32_t*>(ws.hit_t);
       if (int rc = launch_route_bits(a.routes, a.lens, static_cast<int64_t>(a.RG) * rows, a.L, a.S_k, qbits, stream))
         return rc;
@@ -2132,7 +2211,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
 #define IRB_DQ_TILE(GV)                                                                                        \
   hipLaunchKernelGGL((bwd_dq_tile_kernel<D, GV>), grid, dim3(256), 0, stream, a, static_cast<const uint16_t*>(args.dout), \
                      args.lse, ws.delta, static_cast<uint16_t*>(args.dq), n_qt, tile_thr_milli(), qbits, qwords,   \
-                     gather_rest)
+                     gather_rest, have_delta ? 1 : 0)
       if (G == 4) IRB_DQ_TILE(4);
       else if (G == 8) IRB_DQ_TILE(8);
       else IRB_DQ_TILE(16);

@@ -291,10 +291,12 @@ IRB_DEV void fwd_item(const AttnArgs& a, T* __restrict__ out, float* __restrict_
   }
   if (l16 < nh) {
     T* op = out + (row * a.Hq + h0 + l16) * DV + 4 * g16;
+    float* o32 = a.o32 ? a.o32 + (row * a.Hq + h0 + l16) * DV + 4 * g16 : nullptr;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const float v[4] = {oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv};
       store4(op + dt * 16, v);
+      if (o32) store4(o32 + dt * 16, v);
     }
     if (g16 == 0)
       lse[(static_cast<int64_t>(b) * a.Hq + h0 + l16) * a.S_q + t] = ltot > 0.f ? (m2 + log2f(ltot)) * kLn2 : -INFINITY;
@@ -447,10 +449,12 @@ IRB_DEV void fwd_item_gather(const AttnArgs& a, uint16_t* __restrict__ out, floa
   }
   if (l16 < nh) {
     T* op = out + (row * a.Hq + h0 + l16) * DV + 4 * g16;
+    float* o32 = a.o32 ? a.o32 + (row * a.Hq + h0 + l16) * DV + 4 * g16 : nullptr;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const float v[4] = {oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv};
       store4(op + dt * 16, v);
+      if (o32) store4(o32 + dt * 16, v);
     }
     if (g16 == 0)
       lse[(static_cast<int64_t>(b) * a.Hq + h0 + l16) * a.S_q + t] = ltot > 0.f ? (m2 + log2f(ltot)) * kLn2 : -INFINITY;
@@ -979,6 +983,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     } else if (t < a.S_q) {
       const int64_t row = static_cast<int64_t>(b) * a.S_q + t;
       T* op = out + (row * a.Hq + kvh * G + colh) * DV + 4 * h32;
+      float* o32 = a.o32 ? a.o32 + (row * a.Hq + kvh * G + colh) * DV + 4 * h32 : nullptr;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -986,6 +991,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
           const float v[4] = {oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv, oacc[dt][4 * j + 2] * inv,
                               oacc[dt][4 * j + 3] * inv};
           store4(op + 32 * dt + 8 * j, v);
+          if (o32) store4(o32 + 32 * dt + 8 * j, v);
         }
       if (h32 == 0)
         lse[(static_cast<int64_t>(b) * a.Hq + kvh * G + colh) * a.S_q + t] = ltot > 0.f ? (m2 + log2f(ltot)) * kLn2 : -INFINITY;

@@ -275,14 +275,18 @@ latent_fwd_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__ ls
   for (int hb = 0; hb < 2; ++hb) {
     const float inv = hb ? i1 : i0;
     uint16_t* op = out + (row * a.Hq + h0 + 32 * hb + l32) * kLDV + 128 * wid + 4 * h32;
+    float* o32 = a.o32 ? a.o32 + (row * a.Hq + h0 + 32 * hb + l32) * kLDV + 128 * wid + 4 * h32 : nullptr;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
+        const float v[4] = {oacc[dt][hb][4 * q4] * inv, oacc[dt][hb][4 * q4 + 1] * inv, oacc[dt][hb][4 * q4 + 2] * inv,
+                            oacc[dt][hb][4 * q4 + 3] * inv};
         uint2 u;
-        u.x = pack_bf16x2(oacc[dt][hb][4 * q4] * inv, oacc[dt][hb][4 * q4 + 1] * inv);
-        u.y = pack_bf16x2(oacc[dt][hb][4 * q4 + 2] * inv, oacc[dt][hb][4 * q4 + 3] * inv);
+        u.x = pack_bf16x2(v[0], v[1]);
+        u.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(op + 32 * dt + 8 * q4) = u;
+        if (o32) *reinterpret_cast<float4*>(o32 + 32 * dt + 8 * q4) = make_float4(v[0], v[1], v[2], v[3]);
       }
   }
 }
@@ -700,8 +704,8 @@ bool latent_bwd_applies(const AttnArgs& a, const void* dk, const void* dv) {
          ds_lds <= 150 * 1024;
 }
 
-int launch_latent_bwd(const AttnArgs& a, const void* dout, const float* lse, void* dq, void* dkv_out, void* ws,
-                      int64_t* dropped, hipStream_t stream) {
+int launch_latent_bwd(const AttnArgs& a, const void* dout, const float* lse, const float* out32, void* dq,
+                      void* dkv_out, void* ws, int64_t* dropped, hipStream_t stream) {
   constexpr int NB = 3;
   const size_t rows = static_cast<size_t>(a.B) * a.S_q;
   const size_t rk = rows * a.Hkv;
@@ -722,7 +726,12 @@ int launch_latent_bwd(const AttnArgs& a, const void* dout, const float* lse, voi
   if (rk == 0) return 0;
   if (rk > 0x7fffffff) return static_cast<int>(hipErrorInvalidValue);
   const int items = static_cast<int>(rk);
-  if (int rc = launch_latent_fwd(a, nullptr, nullptr, dout, delta, true, stream)) return rc;
+  // Delta from the forward's FP32 output when given, else the forward again in Delta mode
+  if (out32) {
+    if (int rc = launch_delta_from_o(a, dout, out32, delta, stream)) return rc;
+  } else if (int rc = launch_latent_fwd(a, nullptr, nullptr, dout, delta, true, stream)) {
+    return rc;
+  }
   hipLaunchKernelGGL(latent_prep_kernel, dim3(static_cast<unsigned>(rk), kLD / 64 + kLDV / 64), dim3(256), 0, stream, a,
                      static_cast<const uint16_t*>(dout), qt, dot);
   {

@@ -99,6 +99,7 @@ struct AttnArgs {
   float scale;
   int dtype;
   int RG;   // route groups: 1 (one route per query, every head) or Hkv (one per KV group)
+  float* o32;   // forward, nullable: o also in FP32, [B, S_q, Hq, Dv] (the backward's Delta input)
 };
 
 // Row of (batch b, query t) in the routes / lens read by KV head kvh.  Routes
@@ -183,14 +184,17 @@ int launch_latent_fwd(const AttnArgs& a, void* out, float* lse, const void* dout
 // KV head, merged dk == dv): its workspace bytes, whether it applies, and the launch
 size_t latent_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv);
 bool latent_bwd_applies(const AttnArgs& a, const void* dk, const void* dv);
-int launch_latent_bwd(const AttnArgs& a, const void* dout, const float* lse, void* dq, void* dkv_out, void* ws,
-                      int64_t* dropped, hipStream_t stream);
+int launch_latent_bwd(const AttnArgs& a, const void* dout, const float* lse, const float* out32, void* dq,
+                      void* dkv_out, void* ws, int64_t* dropped, hipStream_t stream);
+// Delta[b,h,t] = rowsum(dO * o) from the forward's FP32 o
+int launch_delta_from_o(const AttnArgs& a, const void* dout, const float* o32, float* delta, hipStream_t stream);
 // backward row statistic Delta[b,h,t] = rowsum(dO * o) with o recomputed in FP32
 int launch_attn_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t stream);
 
 struct AttnBwdArgs {
   AttnArgs f;
-  const void* out; const void* dout; const float* lse;
+  const float* out32;   // nullable: the forward's FP32 o; Delta = rowsum(dO * o) is then read off it
+  const void* dout; const float* lse;
   const int32_t* rev_counts; const int32_t* rev_indices;
   int rev_bq, rev_bk, rev_width;
   void* dq; void* dk; void* dv;
@@ -201,6 +205,7 @@ struct AttnBwdArgs {
 size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype,
                                 int RG);
 int launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
+bool attn_bwd_reads_out32(int B, int S_q, int S_k, int L, int Hq, int Hkv, int Dqk, int Dv, int dtype, int RG);
 
 // fill a device int32 range with a value (a kernel, so callers may capture it in graphs)
 int launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);

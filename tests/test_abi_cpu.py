@@ -140,7 +140,8 @@ def test_attention_validation():
     lib = irb.load_library()
     st = (ctypes.c_int64 * 9)(64 * 4 * 128, 4 * 128, 128, 64 * 128, 128, 128, 64 * 128, 128, 128)
     call = lambda Hq=4, Hkv=1, D=128, Dv=128, sc=0.1, dt=1, strides=st, rg=1: lib.irb_sparse_gqa_attention_fwd(
-        FAKE, FAKE, FAKE, dt, strides, FAKE, FAKE, rg, 1, 64, 64, 16, Hq, Hkv, D, Dv, sc, FAKE, FAKE, None, 0, None)
+        FAKE, FAKE, FAKE, dt, strides, FAKE, FAKE, rg, 1, 64, 64, 16, Hq, Hkv, D, Dv, sc, FAKE, FAKE, None, None, 0,
+        None)
     assert _err(call(Hq=6, Hkv=4))[0] == 3
     assert _err(call(Hq=128, Hkv=1))[0] == 3
     assert _err(call(D=96, Dv=96))[0] == 3
@@ -161,8 +162,15 @@ def test_attention_validation():
     assert fws(1, 16384, 16384, 2048, 64, 1, 576, 512, 1, 1) == 0        # latent rows
     assert fws(1, 131072, 131072, 2560, 64, 8, 128, 128, 1, 1) == 0      # 2 GiB of words: over the budget
     misaligned = lambda: lib.irb_sparse_gqa_attention_fwd(FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, 1, 1, 64, 64, 16, 4, 1,
-                                                          128, 128, 0.1, FAKE, FAKE, ctypes.c_void_p(0x1004), 64, None)
+                                                          128, 128, 0.1, FAKE, FAKE, None, ctypes.c_void_p(0x1004),
+                                                          64, None)
     assert _err(misaligned())[0] == 3
+    # the optional FP32 output must be 16-byte aligned (forward and backward)
+    o32_bad = lambda: lib.irb_sparse_gqa_attention_fwd(FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, 1, 1, 64, 64, 16, 4, 1,
+                                                       128, 128, 0.1, FAKE, FAKE, ctypes.c_void_p(0x1004), None, 0,
+                                                       None)
+    code, msg = _err(o32_bad())
+    assert code == 3 and "out_f32" in msg
     # route groups: 1 (shared) or one per KV head
     code, msg = _err(call(Hq=8, Hkv=4, rg=2))
     assert code == 3 and "route_groups" in msg
@@ -172,6 +180,10 @@ def test_attention_validation():
         FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, FAKE, FAKE, FAKE, rg, FAKE, FAKE, 1, bk, width, 1, 64, 64, 16, 4, 1, 128,
         128, 0.1, FAKE, FAKE, FAKE, FAKE, ws, None, None)
     assert _err(bwd(bk=32))[0] == 3
+    code, msg = _err(lib.irb_sparse_gqa_attention_bwd(
+        FAKE, FAKE, FAKE, 1, st, ctypes.c_void_p(0x1004), FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, 16, 64, 1, 64, 64,
+        16, 4, 1, 128, 128, 0.1, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None))
+    assert code == 3 and "out_f32" in msg
     assert _err(bwd(width=63))[0] == 3
     assert _err(bwd(rg=2))[0] == 3
     need = lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 4, 1, 128, 128, 1, 1)
@@ -186,6 +198,14 @@ def test_attention_validation():
     assert ws_size(1, 256, 256, 16, 8, 4, 128, 128, 1, 4) > ws_size(1, 256, 256, 16, 8, 4, 128, 128, 1, 1)
     assert ws_size(1, 256, 256, 16, 8, 4, 128, 128, 1, 3) == 0
     assert lib.irb_sparse_gqa_attention_bwd_workspace_size(1, 64, 64, 16, 4, 1, 128, 128, 0, 1) != need
+    # where the backward reads Delta off the forward's FP32 output
+    reads = lib.irb_sparse_gqa_attention_bwd_reads_out_f32
+    assert reads(1, 32768, 32768, 1024, 32, 4, 128, 128, 1, 1) == 1      # packed 32768: query-tile dQ
+    assert reads(1, 131072, 131072, 2560, 64, 8, 128, 128, 1, 1) == 0    # per-query dQ forms Delta itself
+    assert reads(1, 16384, 16384, 2048, 64, 1, 576, 512, 1, 1) == 1      # latent rows
+    assert reads(1, 512, 512, 64, 4, 1, 64, 64, 0, 1) == 1               # fp32: Delta-mode forward saved
+    assert reads(1, 300, 300, 96, 32, 1, 128, 128, 1, 1) == 1            # 32 heads per group: the same
+    assert reads(1, 64, 64, 16, 6, 4, 128, 128, 1, 1) == 0               # invalid head counts
 
 
 def test_python_binding_has_no_cpu_path():

@@ -56,23 +56,29 @@ def _run_fwd_bwd(wl, x, routes, lens, scale, do_bwd, q_view=None, rev_bq=1):
     k = to_dev(x["k"], dt)
     v = to_dev(x["v"], dt)
     r_d, l_d = to_dev(routes), to_dev(lens)
-    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, scale)
+    o, lse, o32 = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, scale, out_f32=True)
     ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], routes, scale)
     attn_tol_check(host(o), ro, dt, "o")
     _check_lse(host(lse), rlse, dt)
+    # the stored output is the FP32 output rounded once
+    assert torch.equal(o, o32.to(o.dtype)), "o is not the rounding of the FP32 output"
+    attn_tol_check(host(o32), ro, torch.float32 if dt == torch.float32 else dt, "o (fp32)")
     if not do_bwd:
         return
     S = x["q"].shape[1]
     rc, ri = irb.build_block_lists(r_d, l_d, S, rev_bq, 16, reverse=True)
     dO = to_dev(x["dO"], dt)
-    dropped = torch.full((1,), -1, dtype=torch.int64, device=DEV)
-    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, rev_bq, 16, scale,
-                                              dropped_hits=dropped)
-    assert int(dropped.item()) == 0, "reverse lists of the same routes dropped key-side hits"
     rdq, rdk, rdv = oracle.attention_bwd(x["q"], x["k"], x["v"], routes, x["dO"], scale)
-    attn_tol_check(host(dq), rdq, dt, "dq")
-    attn_tol_check(host(dk), rdk, dt, "dk")
-    attn_tol_check(host(dv), rdv, dt, "dv")
+    # Delta formed from the routes, then read off the forward's FP32 output
+    for fo in (None, o32):
+        dropped = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+        dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, rev_bq, 16, scale,
+                                                  dropped_hits=dropped, out_f32=fo)
+        assert int(dropped.item()) == 0, "reverse lists of the same routes dropped key-side hits"
+        tag = "" if fo is None else " (Delta from the FP32 output)"
+        attn_tol_check(host(dq), rdq, dt, "dq" + tag)
+        attn_tol_check(host(dk), rdk, dt, "dk" + tag)
+        attn_tol_check(host(dv), rdv, dt, "dv" + tag)
 
 
 def test_tiny_fp32_pipeline_routes_fwd_bwd():
@@ -144,18 +150,21 @@ def test_latent_shared_kv_fwd_bwd(T, width):
     q_d = to_dev(x["q"], torch.bfloat16)[None]
     k_d, v_d = kv_d, kv_d[..., :wl.Dv]
     r_d, l_d = to_dev(routes)[None], to_dev(lens)[None]
-    o, lse = irb.sparse_gqa_attention_fwd(q_d, k_d, v_d, r_d, l_d, wl.softmax_scale)
+    o, lse, o32 = irb.sparse_gqa_attention_fwd(q_d, k_d, v_d, r_d, l_d, wl.softmax_scale, out_f32=True)
     ro, rlse = oracle.latent_attention_fwd(x["q"], x["kv"], idx, wl.softmax_scale, dv=wl.Dv)
     attn_tol_check(host(o)[0], ro, torch.bfloat16, "latent o")
     _check_lse(host(lse)[0], rlse, torch.bfloat16)
+    assert torch.equal(o, o32.to(torch.bfloat16)), "o is not the rounding of the FP32 output"
     rc, ri = irb.build_block_lists(r_d, l_d, T, 1, 16, reverse=True)
     dO = to_dev(x["dO"], torch.bfloat16)[None]
-    dq, dkv, dv_alias = irb.sparse_gqa_attention_bwd(q_d, k_d, v_d, o, dO, lse, r_d, l_d, rc, ri, 1, 16,
-                                                     wl.softmax_scale, merged_kv=True)
-    assert dv_alias.data_ptr() == dkv.data_ptr()
     rdq, rdkv = oracle.latent_attention_bwd(x["q"], x["kv"], idx, x["dO"], wl.softmax_scale, dv=wl.Dv)
-    attn_tol_check(host(dq)[0], rdq, torch.bfloat16, "latent dq")
-    attn_tol_check(host(dkv)[0], rdkv, torch.bfloat16, "latent dkv")
+    for fo in (None, o32):
+        dq, dkv, dv_alias = irb.sparse_gqa_attention_bwd(q_d, k_d, v_d, o, dO, lse, r_d, l_d, rc, ri, 1, 16,
+                                                         wl.softmax_scale, merged_kv=True, out_f32=fo)
+        assert dv_alias.data_ptr() == dkv.data_ptr()
+        tag = "" if fo is None else " (Delta from the FP32 output)"
+        attn_tol_check(host(dq)[0], rdq, torch.bfloat16, "latent dq" + tag)
+        attn_tol_check(host(dkv)[0], rdkv, torch.bfloat16, "latent dkv" + tag)
 
 
 def test_backward_with_coarse_reverse_tiles():

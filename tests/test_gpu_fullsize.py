@@ -213,12 +213,18 @@ def test_route_pipeline_full_size(name):
     _log("sampled rows", t0)
 
 
-def _fwd(name, x, routes, lens):
+def _fwd(name, x, routes, lens, o32=False):
+    """The forward as the step runs it: training workloads also keep the FP32 output
+    (the backward's Delta input), which the stored output must round to exactly."""
     wl = synth.WORKLOADS[name]
     q, k, v = (to_dev(x[n], BF16) for n in ("q", "k", "v"))
     r_d, l_d = to_dev(routes), to_dev(lens)
-    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, 1.0 / math.sqrt(wl.D))
-    return q, k, v, r_d, l_d, o, lse
+    if not o32:
+        o, lse = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, 1.0 / math.sqrt(wl.D))
+        return q, k, v, r_d, l_d, o, lse
+    o, lse, out32 = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, 1.0 / math.sqrt(wl.D), out_f32=True)
+    assert torch.equal(o, out32.to(BF16)), "o is not the rounding of the FP32 output"
+    return q, k, v, r_d, l_d, o, lse, out32
 
 
 def _check_fwd_rows(name, x, routes, lens, o, lse, rows):
@@ -312,12 +318,12 @@ def test_attention_bwd_full_size(name):
     S, G = wl.S, wl.Hq // wl.Hkv
     scale = 1.0 / math.sqrt(wl.D)
     _log("routes + inputs", t0)
-    q, k, v, r_d, l_d, o, lse = _fwd(name, x, routes, lens)
+    q, k, v, r_d, l_d, o, lse, o32 = _fwd(name, x, routes, lens, o32=True)
     rc, ri = irb.build_block_lists(r_d, l_d, S, 1, 16, reverse=True)
     dO = to_dev(xb["dO"], BF16)
     torch.cuda.synchronize()
     g0 = time.time()
-    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, 1, 16, scale)
+    dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, 1, 16, scale, out_f32=o32)
     torch.cuda.synchronize()
     _log(f"gpu fwd + lists + bwd (bwd {time.time() - g0:.2f}s)", t0)
     tiles = _key_tiles(name)
@@ -360,13 +366,14 @@ def test_latent_full_size():
     q_d = to_dev(x["q"], BF16)[None]
     k_d, v_d = kv_d, kv_d[..., :Dv]
     r_d, l_d = to_dev(routes)[None], to_dev(lens)[None]
-    o, lse = irb.sparse_gqa_attention_fwd(q_d, k_d, v_d, r_d, l_d, wl.softmax_scale)
+    o, lse, o32 = irb.sparse_gqa_attention_fwd(q_d, k_d, v_d, r_d, l_d, wl.softmax_scale, out_f32=True)
+    assert torch.equal(o, o32.to(BF16)), "o is not the rounding of the FP32 output"
     rc, ri = irb.build_block_lists(r_d, l_d, T, 1, 16, reverse=True)
     dO = to_dev(x["dO"], BF16)[None]
     torch.cuda.synchronize()
     g0 = time.time()
     dq, dkv, _ = irb.sparse_gqa_attention_bwd(q_d, k_d, v_d, o, dO, lse, r_d, l_d, rc, ri, 1, 16,
-                                              wl.softmax_scale, merged_kv=True)
+                                              wl.softmax_scale, merged_kv=True, out_f32=o32)
     torch.cuda.synchronize()
     _log(f"compaction + fwd + lists + bwd (bwd {time.time() - g0:.2f}s)", t0)
     rows = _sample_rows_plain(T, wl.seed, 24)
