@@ -693,18 +693,28 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   // the batch of step i - 1" is one vmcnt.
   f32x16 scur;
   bf16x8 pprev[2];
+  // Values a step needs before its first MFMA, read from LDS one step ahead
+  // (so that no step starts with a chain of LDS round trips): the key tiles
+  // whose K (nk = tiles[i + 3]) and V (nv = tiles[i + 1]) rows step i
+  // loads, and this lane's mask word of tile i (nmw).  Indices past the
+  // list are clamped; their values go unused.
+  int nk = 0, nv = 0;
+  uint32_t nmw = 0u;
   auto step = [&](auto cc, auto pvc, int i, int ntiles, int seg0) __attribute__((always_inline)) {
     constexpr int C = decltype(cc)::value;      // i % 3
     constexpr bool kPV = decltype(pvc)::value;  // i > 0
     if (i + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kDmaWait<NIK + NIV>());
     else __builtin_amdgcn_s_waitcnt(kDmaWait<NIV>());
     bare_barrier();
-    if (i + 3 < ntiles) issue(seg0 + tiles[i + 3], std::integral_constant<int, C>{}, KSide{});
-    if (i + 1 < ntiles) issue(seg0 + tiles[i + 1], std::integral_constant<int, (C + 1) % 3>{}, VSide{});
-    const int ktl = tiles[i];
+    const int tk = __builtin_amdgcn_readfirstlane(nk), tv = __builtin_amdgcn_readfirstlane(nv);
+    if (i + 3 < ntiles) issue(seg0 + tk, std::integral_constant<int, C>{}, KSide{});
+    if (i + 1 < ntiles) issue(seg0 + tv, std::integral_constant<int, (C + 1) % 3>{}, VSide{});
+    const uint32_t mw = nmw >> (4 * h32);
+    nk = tiles[min(i + 4, ntiles - 1)];
+    nv = tiles[min(i + 2, ntiles - 1)];
+    nmw = mask[colq][tv];
     constexpr uint32_t kslot = ((C + 1) % 3) * BUF, vslot = ((C + 2) % 3) * BUF;
     const char* kb = raw + kslot;
-    const uint32_t mw = mask[colq][ktl] >> (4 * h32);
     // Masked online softmax of tile i in this lane's column, in eight pieces
     // spread over the MFMA groups: 0/1 mask select of elements 0-7 / 8-15
     // (an entry whose mask bit is clear becomes -inf by a bit select with the
@@ -716,7 +726,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     // All branch-free, so the step is one scheduling region.
     constexpr float kLazy = 8.f;
     float xr[16], p[16];
-    float cm = -INFINITY, alpha = 1.f, nm = 0.f;
+    float cm = -INFINITY, mprev = 0.f, nm = 0.f;
     bool rescale = false;
     auto piece = [&](int pc) __attribute__((always_inline)) {
       if (pc < 2) {
@@ -736,8 +746,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
         const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
         const float cmax = max_raw(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc2;
         const bool up = cmax > m2 + kLazy;
-        const float ea = fast_exp2(m2 - cmax);
-        alpha = up ? ea : 1.f;
+        mprev = m2;
         m2 = up ? cmax : m2;
         rescale = up;
         nm = (m2 == -INFINITY) ? 0.f : -m2;
@@ -748,42 +757,48 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     };
     // group g: S MFMA of k-step g for tile i + 1 (past the last tile: a stale
     // slot, result unused), O MFMA (dim tile g / 2, k-step g % 2) for tile
-    // i - 1, softmax pieces; LDS operands are read one group ahead
+    // i - 1, softmax pieces; LDS operands are read two groups ahead
     f32x16 snext;
 #pragma unroll
     for (int e = 0; e < 16; ++e) snext[e] = 0.f;
-    bf16x8 kop[2], vop[2];
-    kop[0] = *reinterpret_cast<const bf16x8*>(kb + kofs[0]);
-    if constexpr (kPV) vop[0] = vread(0, 0, vslot);
+    bf16x8 kop[3], vop[3];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      kop[g] = *reinterpret_cast<const bf16x8*>(kb + kofs[g]);
+      if constexpr (kPV) vop[g] = vread(g >> 1, g & 1, vslot);
+    }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      if (g + 1 < NG) {
-        kop[(g + 1) & 1] = *reinterpret_cast<const bf16x8*>(kb + kofs[g + 1]);
-        if constexpr (kPV) vop[(g + 1) & 1] = vread((g + 1) >> 1, (g + 1) & 1, vslot);
+      if (g + 2 < NG) {
+        kop[(g + 2) % 3] = *reinterpret_cast<const bf16x8*>(kb + kofs[g + 2]);
+        if constexpr (kPV) vop[(g + 2) % 3] = vread((g + 2) >> 1, (g + 2) & 1, vslot);
       }
-      snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[g & 1], qop[g], snext, 0, 0, 0);
-      if constexpr (kPV) oacc[g >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[g & 1], pprev[g & 1], oacc[g >> 1], 0, 0, 0);
+      snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[g % 3], qop[g], snext, 0, 0, 0);
+      if constexpr (kPV) oacc[g >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[g % 3], pprev[g & 1], oacc[g >> 1], 0, 0, 0);
 #pragma unroll
       for (int pc = g * 8 / NG; pc < (g + 1) * 8 / NG; ++pc) piece(pc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    float ps = 0.f;
+    float ps;
     {
-      float s0 = (p[0] + p[1]) + (p[2] + p[3]), s1 = (p[4] + p[5]) + (p[6] + p[7]);
-      float s2v = (p[8] + p[9]) + (p[10] + p[11]), s3 = (p[12] + p[13]) + (p[14] + p[15]);
+      const float s0 = (p[0] + p[1]) + (p[2] + p[3]), s1 = (p[4] + p[5]) + (p[6] + p[7]);
+      const float s2v = (p[8] + p[9]) + (p[10] + p[11]), s3 = (p[12] + p[13]) + (p[14] + p[15]);
       ps = (s0 + s1) + (s2v + s3);
     }
-    lsum = lsum * alpha + ps;
     bf16x8 pcur[2];
     pcur[0] = pack_bf16x8(p);
     pcur[1] = pack_bf16x8(p + 8);
-    // the rescale by alpha(i) follows the accumulation of tile i - 1
+    // the rescale by alpha(i) (rare: the reference max moved) follows the
+    // accumulation of tile i - 1; its exponential is only taken then
     if (__ballot(rescale)) {
+      const float alpha = rescale ? fast_exp2(mprev - m2) : 1.f;
+      lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
     }
+    lsum += ps;
     scur = snext;
     pprev[0] = pcur[0];
     pprev[1] = pcur[1];
@@ -944,6 +959,9 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     else if (ntiles > 1) __builtin_amdgcn_s_waitcnt(kDmaWait<NIK + NIV>());
     else __builtin_amdgcn_s_waitcnt(kDmaWait<NIV>());
     bare_barrier();
+    nk = tiles[min(3, ntiles - 1)];
+    nv = tiles[min(1, ntiles - 1)];
+    nmw = mask[colq][tiles[0]];
     scores(scur, 0);
     step(std::integral_constant<int, 0>{}, std::false_type{}, 0, ntiles, seg0);
     // steps 1 .. n - 1, unrolled by three so that every slot offset is a constant
