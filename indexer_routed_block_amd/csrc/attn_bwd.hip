@@ -1664,11 +1664,6 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
 }
 
 // ---------------------------------------------------------------- dk / dv in shared batches
-// 4-byte direct global-to-LDS load (global_load_lds_dword): lane i writes LDS
-// bytes [lds_base + 4 i, + 4); inactive lanes write nothing
-IRB_DEV void lds_dma4(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
-}
 
 // 16-byte chunk position of chunk c of row r in a shared-batch row buffer:
 // c ^ f(r & 15), f a bit permutation (row bits 0-2 to bits 1-3, bit 3 to

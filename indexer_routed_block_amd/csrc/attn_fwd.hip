@@ -777,6 +777,16 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       if constexpr (kPV) oacc[g >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[g % 3], pprev[g & 1], oacc[g >> 1], 0, 0, 0);
 #pragma unroll
       for (int pc = g * 8 / NG; pc < (g + 1) * 8 / NG; ++pc) piece(pc);
+      // issue order within the group: MFMA, LDS read, 3 VALU, LDS read,
+      // 3 VALU, MFMA, LDS read, the rest of the VALU work
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     float ps;
@@ -812,12 +822,21 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     __syncthreads();
     if (qbits) {
       // the queries' key-membership words (one bit per key, built once per
-      // route row by the bitmap pass) are this segment's mask rows as they are
-      for (int i = tid; i < BQ * nseg; i += 256) {
-        const int qi = i / nseg, j = i - qi * nseg;
+      // route row by the bitmap pass) are this segment's mask rows as they
+      // are: 64 words of one row per direct load, all of a wave's loads in
+      // flight together.  Words past the segment (their sources clamped to
+      // the row's last word) are never read; rows past the last query are 0.
+      const int nch = (nseg + 63) >> 6;
+      for (int c = wv; c < BQ * nch; c += 4) {
+        const int qi = c / nch, j = ((c - qi * nch) << 6) + lane;
         const int t = qa + qi;
-        mask[qi][j] = t < a.S_q ? qbits[route_row(a, b, t, kvh) * qwords + seg0 + j] : 0u;
+        if (t < a.S_q)
+          lds_dma4(qbits + route_row(a, b, t, kvh) * qwords + min(seg0 + j, qwords - 1),
+                   __builtin_amdgcn_readfirstlane(lds_addr(&mask[qi][(c - qi * nch) << 6])));
+        else
+          mask[qi][j] = 0u;
       }
+      __builtin_amdgcn_s_waitcnt(kDmaWait<0>());
     } else {
     for (int i = tid; i < BQ * (kSegTiles + 1); i += 256) (&mask[0][0])[i] = 0u;
     __syncthreads();

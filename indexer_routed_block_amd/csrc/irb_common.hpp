@@ -153,6 +153,11 @@ IRB_DEV void lds_dma16(const void* src, uint32_t lds_base) {
 IRB_DEV void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
 }
+// 4-byte direct global-to-LDS load (global_load_lds_dword): lane i writes LDS
+// bytes [lds_base + 4 i, + 4); inactive lanes write nothing
+IRB_DEV void lds_dma4(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
+}
 IRB_DEV uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
