@@ -19,7 +19,8 @@
 namespace irb {
 
 constexpr int kBmWaves = 4;
-constexpr int kRbChunks = 4;   // 512-entry chunks whose loads are issued together
+constexpr int kBmChunks = 4;   // 512-id chunks whose loads are issued together (region bitmaps)
+constexpr int kRbChunks = 5;   // the same for route rows (2560 entries: one round for routes of that width)
 
 IRB_DEV void or_run8(uint32_t* bm, const int (&id)[8], int keys) {
   uint32_t acc = 0u;
@@ -47,10 +48,10 @@ bitmap_kernel(const int32_t* __restrict__ ids, int64_t rows, int slots, int regi
   for (int w = lane; w < words; w += 64) bm[w] = 0u;
   const int32_t* r = ids + row * slots;
   wave_lds_sync();
-  for (int c0 = 0; c0 < slots; c0 += 512 * kRbChunks) {
-    int id[kRbChunks][8];
+  for (int c0 = 0; c0 < slots; c0 += 512 * kBmChunks) {
+    int id[kBmChunks][8];
 #pragma unroll
-    for (int u = 0; u < kRbChunks; ++u) {
+    for (int u = 0; u < kBmChunks; ++u) {
       const int e0 = c0 + 512 * u + 8 * lane;
       if (vec && e0 + 8 <= slots) {
         const int4 a = *reinterpret_cast<const int4*>(r + e0);
@@ -63,7 +64,7 @@ bitmap_kernel(const int32_t* __restrict__ ids, int64_t rows, int slots, int regi
       }
     }
 #pragma unroll
-    for (int u = 0; u < kRbChunks; ++u) or_run8(bm, id[u], regions);
+    for (int u = 0; u < kBmChunks; ++u) or_run8(bm, id[u], regions);
   }
   wave_lds_sync();
   uint32_t* o = out + row * words;
