@@ -70,6 +70,9 @@ def parse():
                     help="instead of the step: achievable bf16 GEMM rate (vendor library) and device copy bandwidth")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (HBM counter calibration)")
+    ap.add_argument("--cold", action="store_true",
+                    help="cold-cache timing: write a 512 MiB buffer before every timed call, so that L2 and the "
+                         "256 MiB Infinity Cache hold none of its inputs; ms_per_step is then the sum of the stages")
     return ap.parse_args()
 
 
@@ -224,8 +227,13 @@ def main():
         bwd_ws = torch.empty(max(int(lib.irb_sparse_gqa_attention_bwd_workspace_size(
             B, S, S, L, Hq, Hkv, Dqk, Dv, irb._dtype_code(q), R)), 4), dtype=torch.uint8, device=dev)
 
+    # cold-cache mode: a 512 MiB write on the same stream before each timed call
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev) if args.cold else None
+
     def timed(name, fn, record):
         if record:
+            if flush is not None:
+                flush.fill_(1.0)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -418,12 +426,16 @@ def main():
             ach = amount / (t / 1e3) / 1e9
             (aux_out if name in aux_names else stage_out)[name] = {"ms": round(t, 4), "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
                                "peak": HBM_PEAK_GBS, "frac": round(ach / HBM_PEAK_GBS, 5), "work": amount}
+    if args.cold:
+        # the flushes sit between the step's calls: the step is its calls' sum
+        step_ms = sum(v["ms"] for v in stage_out.values())
     fwd_s = ms["attn_fwd"] / 1e3
     tflops = fwd_flop / fwd_s / 1e12
     qps = valid_q / (route_ms / 1e3)
 
     traffic = None
-    tr = _traffic() if wl.name == "s8192" and R == 1 else None
+    # the counter record is of the default (warm) run
+    tr = _traffic() if wl.name == "s8192" and R == 1 and not args.cold else None
     if tr is not None:
         traffic = tr["hbm_bytes_per_call"]
 
@@ -444,6 +456,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic",
+        "cache": "cold" if args.cold else "warm",
         "config": {
             "workload": wl.name, "description": wl.description, "B": B, "S": S, "Hq": Hq, "Hkv": Hkv,
             "Dqk": Dqk, "Dv": Dv, "route_width": L, "selected_pairs": pairs, "valid_queries": valid_q,
