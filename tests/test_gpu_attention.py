@@ -138,6 +138,32 @@ def test_gqa_bf16_head_groups_and_widths_fwd_bwd(Hq, Hkv, D):
     _run_fwd_bwd(types.SimpleNamespace(dtype="bf16"), x, routes, lens, 1.0 / math.sqrt(D), True)
 
 
+@pytest.mark.parametrize("use_ws", [True, False])
+def test_gqa_bf16_long_routes_fwd(use_ws):
+    """Route rows past one round of the key-membership pass's loads (up to 3055
+    entries against 2560) and past several 512-entry staging chunks of the
+    query-tile kernel's own mask building (without the workspace)."""
+    banner(f"attn bf16 long routes S=4096 workspace={use_ws}")
+    rng = np.random.default_rng(4241)
+    S, Hq, Hkv, D = 4096, 8, 2, 64
+
+    def nrm(*shape):
+        return synth.to_bf16_values(rng.standard_normal(shape).astype(np.float32))
+
+    x = {"q": nrm(1, S, Hq, D), "k": nrm(1, S, Hkv, D), "v": nrm(1, S, Hkv, D)}
+    ids = synth.random_routes(np.random.default_rng(4243), 1, S, 4000, causal=True, frac_invalid=0.25,
+                              duplicates=False)
+    routes, lens, _ = oracle.compact_routes(ids, S)
+    assert int(lens.max()) > 2560
+    dt = torch.bfloat16
+    q, k, v = to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, to_dev(routes), to_dev(lens), scale, use_workspace=use_ws)
+    ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], routes, scale)
+    attn_tol_check(host(o), ro, dt, "o")
+    _check_lse(host(lse), rlse, dt)
+
+
 @pytest.mark.parametrize("T,width", [(512, 256), (300, 64)])
 def test_latent_shared_kv_fwd_bwd(T, width):
     banner(f"attn latent T={T} width={width}")
