@@ -40,22 +40,34 @@ IRB_DEV int div_bk(int id, int bk, uint32_t m) {
   return m ? static_cast<int>(__umulhi(static_cast<uint32_t>(id), m)) : id / bk;
 }
 
-// Walks one ascending route (n entries at r) with a whole wavefront and calls
-// mark(kt) once per run of equal key tiles kt = id / bk.  kVec rows (width a
-// multiple of 4, 16-byte aligned) are read four entries per lane per load.
-// Out-of-range IDs are ignored.
+// Walks one ascending route (n entries at r, in a row of w entries) with a
+// whole wavefront and calls mark(kt) once per run of equal key tiles
+// kt = id / bk.  kVec rows (w a multiple of 4, 16-byte aligned) are read four
+// entries per lane per load, four 256-entry chunks in flight.  Out-of-range
+// IDs are ignored.
 template <bool kVec, typename Mark>
-IRB_DEV void walk_route_tiles(const int32_t* __restrict__ r, int n, int S_k, int bk, uint32_t bkm, Mark&& mark) {
+IRB_DEV void walk_route_tiles(const int32_t* __restrict__ r, int n, int w, int S_k, int bk, uint32_t bkm, Mark&& mark) {
   const int lane = threadIdx.x & 63;
   int prev_last = -1;
   if constexpr (kVec) {
-    // the next chunk's load is issued before the current chunk is marked
-    int4 v = make_int4(-1, -1, -1, -1);
-    if (4 * lane < n) v = *reinterpret_cast<const int4*>(r + 4 * lane);
-    for (int e0 = 0; e0 < n; e0 += 256) {
+    if (n <= 0) return;
+    // chunk c + 4 is loaded when chunk c is marked: the loop is unrolled by
+    // four over fixed register slots and every load is issued (addresses past
+    // the row clamped to its last four entries), with no exit inside the
+    // unrolled body, so the waits stay counted; entries past n, including
+    // whole chunks after the last, are ignored
+    constexpr int PF = 4;
+    auto ld = [&](int e) __attribute__((always_inline)) { return *reinterpret_cast<const int4*>(r + min(e, w - 4)); };
+    int4 slot[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) slot[p] = ld(256 * p + 4 * lane);
+    for (int e00 = 0; e00 < n; e00 += 256 * PF)
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int e0 = e00 + 256 * p;
       const int e = e0 + 4 * lane;
-      int4 vn = make_int4(-1, -1, -1, -1);
-      if (e + 256 < n) vn = *reinterpret_cast<const int4*>(r + e + 256);
+      const int4 v = slot[p];
+      slot[p] = ld(e + 256 * PF);
       const int ids[4] = {v.x, v.y, v.z, v.w};
       int kt[4];
 #pragma unroll
@@ -75,7 +87,6 @@ IRB_DEV void walk_route_tiles(const int32_t* __restrict__ r, int n, int S_k, int
       const int lmax = max(max(kt[0], kt[1]), max(kt[2], kt[3]));
       const uint64_t bal = __ballot(lmax >= 0);
       if (bal) prev_last = max(prev_last, __builtin_amdgcn_readlane(lmax, 63 - __builtin_clzll(bal)));
-      v = vn;
     }
   } else {
     for (int e0 = 0; e0 < n; e0 += 64) {
@@ -104,7 +115,7 @@ mark_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__ lens
   const int n = max(0, min(lens[row], Lw));
   const int qt = t / bq;
   uint32_t* mat = bits + static_cast<int64_t>(b) * n_rows * words;
-  walk_route_tiles<kVec>(routes + row * Lw, n, S_k, bk, bkm, [&](int kt) __attribute__((always_inline)) {
+  walk_route_tiles<kVec>(routes + row * Lw, n, Lw, S_k, bk, bkm, [&](int kt) __attribute__((always_inline)) {
     if (reverse) atomicOr(&mat[static_cast<int64_t>(kt) * words + (qt >> 5)], 1u << (qt & 31));
     else atomicOr(&mat[static_cast<int64_t>(qt) * words + (kt >> 5)], 1u << (kt & 31));
   });
@@ -136,7 +147,7 @@ mark_band_kernel(const int32_t* __restrict__ routes, const int32_t* __restrict__
     const int rel = t / bq - qt0;
     uint32_t* col = band + (rel >> 5);
     const uint32_t bit = 1u << (rel & 31);
-    walk_route_tiles<kVec>(routes + row * Lw, n, S_k, bk, bkm,
+    walk_route_tiles<kVec>(routes + row * Lw, n, Lw, S_k, bk, bkm,
                            [&](int kt) __attribute__((always_inline)) { atomicOr(&col[kt * qw], bit); });
   }
   __syncthreads();
