@@ -19,7 +19,7 @@ import torch
 import indexer_routed_block_amd as irb
 import oracle
 import synth
-from gpu_util import act_dtype, attn_tol_check, banner, check_selection, host, score_bound, to_dev
+from gpu_util import SCORE_ERR, act_dtype, attn_tol_check, banner, check_selection, host, score_bound, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +71,7 @@ def test_grouped_score_tile(wl_name, S, layout, R):
             M = score_bound(x["qI"][:, q0:q1, g], x["w"][:, q0:q1, g], kc_h[:, j0:j1], scale)
             fin = np.isfinite(ref[g])
             err = np.abs(got[g][fin] - ref[g][fin])
-            assert np.all(err <= 1e-3 * M[fin] + 1e-30), f"group {g}: max rel-to-M {np.max(err / M[fin]):.2e}"
+            assert np.all(err <= SCORE_ERR * M[fin] + 1e-30), f"group {g}: max rel-to-M {np.max(err / M[fin]):.2e}"
 
 
 def _oracle_grouped_routes(wl, x, topk):

@@ -9,7 +9,7 @@ import torch
 import indexer_routed_block_amd as irb
 import oracle
 import synth
-from gpu_util import DEV, act_dtype, banner, check_selection, host, score_bound as _score_bound, to_dev
+from gpu_util import DEV, SCORE_ERR, act_dtype, banner, check_selection, host, score_bound as _score_bound, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,8 @@ def test_indexer_score_tile(wl_name, S, layout):
         M = _score_bound(x["qI"][:, q0:q1], x["w"][:, q0:q1], kc_h[:, j0:j1], scale)
         fin = np.isfinite(ref)
         err = np.abs(got[fin] - ref[fin])
-        assert np.all(err <= 1e-3 * M[fin] + 1e-30), f"max rel-to-M {np.max(err / np.maximum(M[fin], 1e-30)):.2e}"
+        # the FP32 scoring bound (well inside the stated 1e-3 relative)
+        assert np.all(err <= SCORE_ERR * M[fin] + 1e-30), f"max rel-to-M {np.max(err / np.maximum(M[fin], 1e-30)):.2e}"
 
 
 def _quantised_scores(rng, B, S, nb, ties):
