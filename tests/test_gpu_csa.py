@@ -43,9 +43,12 @@ def test_gather_region_payload_bit_exact(dtype, D):
     logits = rng.standard_normal((B, T, D)).astype(np.float32)
     src = rng.integers(-1, T + 5, (B, R, rs)).astype(np.int32)          # some ids past T count as missing
     valid = (src >= 0) & (rng.random((B, R, rs)) < 0.85)
+    if dtype == torch.bfloat16:
+        # the inputs are bf16 values on both sides (rounded on the host)
+        keys, logits = oracle.round_to_bf16(keys), oracle.round_to_bf16(logits)
     k_d, z_d = to_dev(keys, dtype), to_dev(logits, dtype)
     pk, pz = irb.gather_region_payload(k_d, z_d, to_dev(src), to_dev(valid))
-    rk, rz = oracle.gather_region_payload(host(k_d), host(z_d), src, valid & (src < T))
+    rk, rz = oracle.gather_region_payload(keys, logits, src, valid & (src < T))
     np.testing.assert_array_equal(host(pk), rk)
     np.testing.assert_array_equal(host(pz), rz)
 

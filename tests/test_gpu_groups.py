@@ -111,10 +111,11 @@ def test_grouped_route_pipeline(wl_name, S, layout, R):
     # the groups really select differently (a shared or swapped group would not)
     if R > 1:
         assert not np.array_equal(ref["sel"][0], ref["sel"][1])
-    # membership words of the GPU's grouped selection, [R, B, S, words]
+    # membership words of a grouped selection, [R, B, S, words] (the oracle's
+    # selection on both sides)
     nb = S // wl.c
-    bm = host(irb.pack_region_bitmap(r["sel"].contiguous(), nb))
-    np.testing.assert_array_equal(bm, oracle.pack_region_bitmap(host(r["sel"]), nb))
+    bm = host(irb.pack_region_bitmap(to_dev(ref["sel"].astype(np.int32)), nb))
+    np.testing.assert_array_equal(bm, oracle.pack_region_bitmap(ref["sel"], nb))
 
 
 def _group_random_routes(seed, R, B, S, width, empty=()):
