@@ -240,14 +240,15 @@ def test_grouped_full_size_s8192():
     r = irb.route(d["kI"], d["qI"], d["w"], d["gamma"], d["freqs"], wl.c, wl.topk, wl.window)
     ref = _oracle_grouped_routes(wl, x, wl.topk)
     _check_grouped_selection(wl, x, wl.topk, r, ref)
-    got_routes = host(r["routes"])
-    # forward over the GPU's own grouped routes, checked on sampled rows
+    # forward over the oracle's grouped routes (both sides), checked on sampled rows
+    ref_routes = np.ascontiguousarray(ref["routes"].astype(np.int32))
+    ref_lens = np.ascontiguousarray(ref["lens"].astype(np.int32))
     a = synth.make_inputs(wl, parts=("attn",))
     q, k, v = (to_dev(a[n], torch.bfloat16) for n in ("q", "k", "v"))
-    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, r["routes"], r["lens"])
+    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, to_dev(ref_routes), to_dev(ref_lens))
     rng = np.random.default_rng(8192)
     rows = sorted(set([0, 1, 2047, 2048, S - 1] + rng.integers(0, S, 43).tolist()))
     todo = [(0, int(t)) for t in rows]
-    ro, rlse = oracle.attention_fwd_grouped(a["q"], a["k"], a["v"], got_routes, 1.0 / math.sqrt(wl.D), rows=todo)
+    ro, rlse = oracle.attention_fwd_grouped(a["q"], a["k"], a["v"], ref_routes, 1.0 / math.sqrt(wl.D), rows=todo)
     attn_tol_check(host(o)[0, rows], ro[0, rows], torch.bfloat16, "o (sampled rows)")
     _check_lse(host(lse)[0][:, rows], rlse[0][:, rows], torch.bfloat16)
