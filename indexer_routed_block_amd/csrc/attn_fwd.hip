@@ -531,10 +531,14 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
   constexpr int NIK = 32 * NCK / 256, NIV = 32 * NCV / 256;   // loads per wave per tile
   static_assert(NIK >= 1 && NIV >= 1, "tile loads");
   __shared__ __align__(16) char raw[3 * BUF];
+  // key tiles per mask segment: halved where a full segment's mask rows
+  // would leave LDS for only one workgroup per CU (G = 4 at D = 128: 32
+  // query rows next to 48 KiB of K/V slots)
+  constexpr int SEG = 3 * BUF + BQ * (kSegTiles + 1) * 4 > 78 * 1024 ? kSegTiles / 2 : kSegTiles;
   // one padding word per row: the softmax reads the words of a wave's four
   // queries at once, and rows a multiple of 256 words apart share a bank
-  __shared__ uint32_t mask[BQ][kSegTiles + 1];
-  __shared__ int tiles[kSegTiles];
+  __shared__ uint32_t mask[BQ][SEG + 1];
+  __shared__ int tiles[SEG];
   __shared__ int s_ntiles;
   __shared__ int cursor[BQ];
   __shared__ int s_lo[BQ], s_hi[BQ];
@@ -816,9 +820,9 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
 
   if (tid < BQ) cursor[tid] = 0;
   const int kt_first = ts.kmin >> 5, kt_last = ts.kmax >> 5;
-  for (int seg0 = kt_first; seg0 <= kt_last; seg0 += kSegTiles) {
-    const int nseg = min(kSegTiles, kt_last - seg0 + 1);
-    const int key0 = seg0 * 32, key1 = key0 + kSegTiles * 32;
+  for (int seg0 = kt_first; seg0 <= kt_last; seg0 += SEG) {
+    const int nseg = min(SEG, kt_last - seg0 + 1);
+    const int key0 = seg0 * 32, key1 = key0 + SEG * 32;
     __syncthreads();
     if (qbits) {
       // the queries' key-membership words (one bit per key, built once per
@@ -838,7 +842,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
       }
       __builtin_amdgcn_s_waitcnt(kDmaWait<0>());
     } else {
-    for (int i = tid; i < BQ * (kSegTiles + 1); i += 256) (&mask[0][0])[i] = 0u;
+    for (int i = tid; i < BQ * (SEG + 1); i += 256) (&mask[0][0])[i] = 0u;
     __syncthreads();
     // route masks of this segment.  Entry ranges [lo, hi) per query (one lane
     // per query, in parallel): lo is the cursor left by the previous segment,
@@ -955,7 +959,7 @@ attn_fwd_tile_kernel(AttnArgs a, uint16_t* __restrict__ out, float* __restrict__
     // compact list of the key tiles any query routes to
     if (wid == 0) {
       int base = 0;
-      for (int j0 = 0; j0 < kSegTiles; j0 += 64) {
+      for (int j0 = 0; j0 < SEG; j0 += 64) {
         const int j = j0 + lane;
         uint32_t any = 0u;
         if (j < nseg)

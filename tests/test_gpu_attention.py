@@ -140,18 +140,19 @@ def test_gqa_bf16_head_groups_and_widths_fwd_bwd(Hq, Hkv, D):
 
 @pytest.mark.parametrize("use_ws", [True, False])
 def test_gqa_bf16_long_routes_fwd(use_ws):
-    """Route rows past one round of the key-membership pass's loads (up to 3055
-    entries against 2560) and past several 512-entry staging chunks of the
-    query-tile kernel's own mask building (without the workspace)."""
-    banner(f"attn bf16 long routes S=4096 workspace={use_ws}")
+    """Route rows past one round of the key-membership pass's loads (over 2560
+    entries) and past several 512-entry staging chunks of the query-tile
+    kernel's own mask building (without the workspace); G = 4 at D = 128 runs
+    its mask segments at 128 key tiles, so 144 key tiles make two."""
+    banner(f"attn bf16 long routes S=4608 G=4 D=128 workspace={use_ws}")
     rng = np.random.default_rng(4241)
-    S, Hq, Hkv, D = 4096, 8, 2, 64
+    S, Hq, Hkv, D = 4608, 8, 2, 128
 
     def nrm(*shape):
         return synth.to_bf16_values(rng.standard_normal(shape).astype(np.float32))
 
     x = {"q": nrm(1, S, Hq, D), "k": nrm(1, S, Hkv, D), "v": nrm(1, S, Hkv, D)}
-    ids = synth.random_routes(np.random.default_rng(4243), 1, S, 4000, causal=True, frac_invalid=0.25,
+    ids = synth.random_routes(np.random.default_rng(4243), 1, S, 4400, causal=True, frac_invalid=0.25,
                               duplicates=False)
     routes, lens, _ = oracle.compact_routes(ids, S)
     assert int(lens.max()) > 2560
