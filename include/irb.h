@@ -522,11 +522,12 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
  * group g's lists and routes.
  *
  *   out_f32    nullable: the forward's FP32 output (irb_sparse_gqa_attention_fwd
- *              out_f32).  Given, Delta = rowsum(dO * o) is read off it; NULL,
- *              Delta is formed with o in FP32 from the routes (the query side
- *              sums P dP, or the forward runs again in Delta mode) -- never
- *              from the stored, rounded output, whose rounding would enter
- *              every dS.  16-byte aligned.
+ *              out_f32).  Given, Delta = rowsum(dO * o) is read off it for the
+ *              sizes where irb_sparse_gqa_attention_bwd_reads_out_f32 is 1;
+ *              otherwise (or NULL) Delta is formed with o in FP32 from the
+ *              routes (the query side sums P dP, or the forward runs again in
+ *              Delta mode) -- never from the stored, rounded output, whose
+ *              rounding would enter every dS.  16-byte aligned.
  *   lse        the forward's lse; dout [B, S_q, Hq, Dv] dtype contiguous
  *   dq OUT [B, S_q, Hq, Dqk] dtype contiguous
  *   dk OUT [B, S_k, Hkv, Dqk] dtype contiguous, dv OUT [B, S_k, Hkv, Dv]
