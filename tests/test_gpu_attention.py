@@ -165,6 +165,35 @@ def test_gqa_bf16_long_routes_fwd(use_ws):
     _check_lse(host(lse), rlse, dt)
 
 
+@pytest.mark.parametrize("S_q,S_k,width,Hq,Hkv,D", [(300, 1000, 160, 16, 4, 128), (5, 4096, 2048, 32, 4, 128),
+                                                    (77, 600, 64, 8, 2, 64)])
+def test_gqa_bf16_fewer_queries_than_keys_fwd(S_q, S_k, width, Hq, Hkv, D):
+    """Query and key counts differ (the call takes both): routes draw distinct
+    keys from the whole key range, ascending, -1 after each row's length;
+    wide rows take the query-tile kernel with its tiles partly past S_q, the
+    narrowest the per-query gather."""
+    banner(f"attn bf16 S_q={S_q} S_k={S_k} width={width} Hq={Hq} Hkv={Hkv} D={D}")
+    rng = np.random.default_rng(S_q * 7 + S_k)
+
+    def nrm(*shape):
+        return synth.to_bf16_values(rng.standard_normal(shape).astype(np.float32))
+
+    x = {"q": nrm(1, S_q, Hq, D), "k": nrm(1, S_k, Hkv, D), "v": nrm(1, S_k, Hkv, D)}
+    routes = np.full((1, S_q, width), -1, dtype=np.int32)
+    lens = np.zeros((1, S_q), dtype=np.int32)
+    for t in range(S_q):
+        n = int(rng.integers(1, width + 1)) if t % 5 else width
+        routes[0, t, :n] = np.sort(rng.choice(S_k, n, replace=False))
+        lens[0, t] = n
+    dt = torch.bfloat16
+    q, k, v = to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, to_dev(routes), to_dev(lens), scale)
+    ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], routes, scale)
+    attn_tol_check(host(o), ro, dt, "o")
+    _check_lse(host(lse), rlse, dt)
+
+
 @pytest.mark.parametrize("T,width", [(512, 256), (300, 64)])
 def test_latent_shared_kv_fwd_bwd(T, width):
     banner(f"attn latent T={T} width={width}")
