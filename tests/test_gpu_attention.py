@@ -167,18 +167,19 @@ def test_gqa_bf16_long_routes_fwd(use_ws):
 
 @pytest.mark.parametrize("S_q,S_k,width,Hq,Hkv,D", [(300, 1000, 160, 16, 4, 128), (5, 4096, 2048, 32, 4, 128),
                                                     (77, 600, 64, 8, 2, 64)])
-def test_gqa_bf16_fewer_queries_than_keys_fwd(S_q, S_k, width, Hq, Hkv, D):
-    """Query and key counts differ (the call takes both): routes draw distinct
+def test_gqa_bf16_fewer_queries_than_keys_fwd_bwd(S_q, S_k, width, Hq, Hkv, D):
+    """Query and key counts differ (the calls take both): routes draw distinct
     keys from the whole key range, ascending, -1 after each row's length;
     wide rows take the query-tile kernel with its tiles partly past S_q, the
-    narrowest the per-query gather."""
+    narrowest the per-query gather.  The backward runs on reverse lists over
+    the S_k keys, with Delta formed from the routes and from the FP32 output."""
     banner(f"attn bf16 S_q={S_q} S_k={S_k} width={width} Hq={Hq} Hkv={Hkv} D={D}")
     rng = np.random.default_rng(S_q * 7 + S_k)
 
     def nrm(*shape):
         return synth.to_bf16_values(rng.standard_normal(shape).astype(np.float32))
 
-    x = {"q": nrm(1, S_q, Hq, D), "k": nrm(1, S_k, Hkv, D), "v": nrm(1, S_k, Hkv, D)}
+    x = {"q": nrm(1, S_q, Hq, D), "k": nrm(1, S_k, Hkv, D), "v": nrm(1, S_k, Hkv, D), "dO": nrm(1, S_q, Hq, D)}
     routes = np.full((1, S_q, width), -1, dtype=np.int32)
     lens = np.zeros((1, S_q), dtype=np.int32)
     for t in range(S_q):
@@ -188,10 +189,23 @@ def test_gqa_bf16_fewer_queries_than_keys_fwd(S_q, S_k, width, Hq, Hkv, D):
     dt = torch.bfloat16
     q, k, v = to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt)
     scale = 1.0 / math.sqrt(D)
-    o, lse = irb.sparse_gqa_attention_fwd(q, k, v, to_dev(routes), to_dev(lens), scale)
+    r_d, l_d = to_dev(routes), to_dev(lens)
+    o, lse, o32 = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, scale, out_f32=True)
     ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], routes, scale)
     attn_tol_check(host(o), ro, dt, "o")
     _check_lse(host(lse), rlse, dt)
+    rc, ri = irb.build_block_lists(r_d, l_d, S_k, 1, 16, reverse=True)
+    dO = to_dev(x["dO"], dt)
+    rdq, rdk, rdv = oracle.attention_bwd(x["q"], x["k"], x["v"], routes, x["dO"], scale)
+    for fo in (None, o32):
+        dropped = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+        dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, 1, 16, scale,
+                                                  dropped_hits=dropped, out_f32=fo)
+        assert int(dropped.item()) == 0
+        tag = "" if fo is None else " (Delta from the FP32 output)"
+        attn_tol_check(host(dq), rdq, dt, "dq" + tag)
+        attn_tol_check(host(dk), rdk, dt, "dk" + tag)
+        attn_tol_check(host(dv), rdv, dt, "dv" + tag)
 
 
 @pytest.mark.parametrize("T,width", [(512, 256), (300, 64)])
