@@ -171,6 +171,12 @@ def test_attention_validation():
                                                        None)
     code, msg = _err(o32_bad())
     assert code == 3 and "out_f32" in msg
+    # empty sizes are rejected before anything is enqueued
+    sized = lambda B=1, S_q=64, S_k=64, L=16: lib.irb_sparse_gqa_attention_fwd(
+        FAKE, FAKE, FAKE, 1, st, FAKE, FAKE, 1, B, S_q, S_k, L, 4, 1, 128, 128, 0.1, FAKE, FAKE, None, None, 0, None)
+    for kw in ({"B": 0}, {"S_q": 0}, {"S_k": 0}, {"L": 0}):
+        code, msg = _err(sized(**kw))
+        assert code == 3 and "sizes" in msg, kw
     # route groups: 1 (shared) or one per KV head
     code, msg = _err(call(Hq=8, Hkv=4, rg=2))
     assert code == 3 and "route_groups" in msg

@@ -208,6 +208,28 @@ def test_gqa_bf16_fewer_queries_than_keys_fwd_bwd(S_q, S_k, width, Hq, Hkv, D):
         attn_tol_check(host(dv), rdv, dt, "dv" + tag)
 
 
+def test_gqa_bf16_all_routes_empty_fwd_bwd():
+    """No query routes to any key: o = 0 and lse = -inf for every row, empty
+    reverse lists, and zero gradients (with and without the FP32 output)."""
+    banner("attn bf16 all routes empty S=300")
+    S, Hq, Hkv, D = 300, 32, 4, 128
+    rng = np.random.default_rng(300)
+    dt = torch.bfloat16
+    q, k, v, dO = (to_dev(synth.to_bf16_values(rng.standard_normal(sh).astype(np.float32)), dt)
+                   for sh in ((1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)))
+    r_d = to_dev(np.full((1, S, 64), -1, dtype=np.int32))
+    l_d = to_dev(np.zeros((1, S), dtype=np.int32))
+    o, lse, o32 = irb.sparse_gqa_attention_fwd(q, k, v, r_d, l_d, out_f32=True)
+    assert not torch.any(o != 0) and not torch.any(o32 != 0)
+    assert torch.all(torch.isneginf(lse))
+    rc, ri = irb.build_block_lists(r_d, l_d, S, 1, 16, reverse=True)
+    assert not torch.any(rc != 0) and torch.all(ri == -1)
+    for fo in (None, o32):
+        dq, dk, dv = irb.sparse_gqa_attention_bwd(q, k, v, o, dO, lse, r_d, l_d, rc, ri, 1, 16, out_f32=fo)
+        for g in (dq, dk, dv):
+            assert not torch.any(g != 0)
+
+
 @pytest.mark.parametrize("T,width", [(512, 256), (300, 64)])
 def test_latent_shared_kv_fwd_bwd(T, width):
     banner(f"attn latent T={T} width={width}")
