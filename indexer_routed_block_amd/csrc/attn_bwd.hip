@@ -920,7 +920,11 @@ bwd_dq_tile_kernel(AttnArgs a, const uint16_t* __restrict__ dout, const float* _
 
 // ---------------------------------------------------------------- dk / dv
 constexpr int kListCap = 128;
+constexpr int kRedChunk = 8;   // accumulator slices summed across the waves per LDS round
 
+// One workgroup per (16-key tile, KV head); its four waves take every fourth
+// 64-candidate chunk of the tile's reverse list, and their dK / dV partial
+// sums meet in LDS before wave 0 stores them.
 template <typename T, int D, int DV>
 __global__ void __launch_bounds__(256)
 bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __restrict__ qt, const T* __restrict__ dot,
@@ -929,10 +933,11 @@ bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __re
   constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
   __shared__ int s_t[4][kListCap];
   __shared__ uint32_t s_m[4][kListCap];
+  __shared__ f32x4 s_red[3][kRedChunk][64];
   const AttnArgs& a = args.f;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g16 = lane >> 4, l16 = lane & 15;
-  const int item = blockIdx.x * 4 + wid;
+  const int item = blockIdx.x;
   if (item >= n_items) return;
   const int kvh = item % a.Hkv;
   const int jt = (item / a.Hkv) % nkt;
@@ -1054,7 +1059,7 @@ bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __re
   const int bq = args.rev_bq;
   const int64_t ncand = static_cast<int64_t>(cnt) * bq;
   int listed = 0;   // entries in s_t/s_m waiting for a batch
-  for (int64_t c0 = 0; c0 < ncand; c0 += 64) {
+  for (int64_t c0 = 64 * wid; c0 < ncand; c0 += 256) {
     const int64_t cidx = c0 + lane;
     int t = -1;
     uint32_t mask = 0u;
@@ -1107,7 +1112,30 @@ bwd_dkdv_kernel(AttnBwdArgs args, const float* __restrict__ delta, const T* __re
     for (int hb = 0; hb < bpq; ++hb) batch(0, listed, hb);
   }
 
-  if (!kok) return;
+  // waves 1-3 hand their partial sums to wave 0, kRedChunk slices at a time
+  // (slice s < NDK is adk[s], the rest adv[s - NDK]); fixed summation order
+  constexpr int NS = NDK + NDV;
+#pragma unroll
+  for (int c = 0; c < NS; c += kRedChunk) {
+    if (wid > 0) {
+#pragma unroll
+      for (int j = 0; j < kRedChunk; ++j)
+        if (c + j < NS) s_red[wid - 1][j][lane] = c + j < NDK ? adk[c + j < NDK ? c + j : 0] : adv[c + j >= NDK ? c + j - NDK : 0];
+    }
+    __syncthreads();
+    if (wid == 0) {
+#pragma unroll
+      for (int j = 0; j < kRedChunk; ++j) {
+        if (c + j >= NS) continue;
+        const f32x4 w = s_red[0][j][lane] + s_red[1][j][lane] + s_red[2][j][lane];
+        if (c + j < NDK) adk[c + j < NDK ? c + j : 0] += w;
+        else adv[c + j >= NDK ? c + j - NDK : 0] += w;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (wid != 0 || !kok) return;
   T* dkp = static_cast<T*>(args.dk) + ((static_cast<int64_t>(b) * a.S_k + kid) * a.Hkv + kvh) * D + 4 * g16;
   if (merged) {
 #pragma unroll
@@ -2293,7 +2321,7 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
     // no hit lists on this path: nothing can be dropped
     if (args.dropped)
       if (int rc = launch_fill_i32(reinterpret_cast<int32_t*>(args.dropped), 2, 0, stream)) return rc;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DV>), dim3(static_cast<unsigned>((kitems + 3) / 4)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DV>), dim3(static_cast<unsigned>(kitems)), dim3(256), 0, stream,
                        args, ws.delta, static_cast<const T*>(ws.qt), static_cast<const T*>(ws.dot), G, Gp, nkt,
                        static_cast<int>(kitems), merged);
   }

@@ -138,6 +138,73 @@ def test_gqa_bf16_head_groups_and_widths_fwd_bwd(Hq, Hkv, D):
     _run_fwd_bwd(types.SimpleNamespace(dtype="bf16"), x, routes, lens, 1.0 / math.sqrt(D), True)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,S,width,rev_bq", [(8, 2, 128, 700, 200, 1), (4, 1, 64, 600, 300, 4)])
+def test_fp32_head_widths_fwd_bwd(Hq, Hkv, D, S, width, rev_bq):
+    """FP32 inputs at both head widths, routes wide enough that a key tile's
+    reverse list holds several rounds of 256 query candidates (the key side
+    splits them across a workgroup's four waves), with per-query and 4-query
+    reverse tiles."""
+    banner(f"attn fp32 Hq={Hq} Hkv={Hkv} D={D} S={S} width={width} rev_bq={rev_bq}")
+    rng = np.random.default_rng(2000 + S + D)
+
+    def nrm(*shape):
+        return rng.standard_normal(shape).astype(np.float32)
+
+    x = {"q": nrm(1, S, Hq, D), "k": nrm(1, S, Hkv, D), "v": nrm(1, S, Hkv, D), "dO": nrm(1, S, Hq, D)}
+    routes, lens = _random_routes(S + width, 1, S, width, empty_rows=[(0, 3)])
+    _run_fwd_bwd(types.SimpleNamespace(dtype="fp32"), x, routes, lens, 1.0 / math.sqrt(D), True, rev_bq=rev_bq)
+
+
+@pytest.mark.parametrize("Hq,shared", [(16, False), (32, False), (16, True)])
+def test_bf16_wide_heads_fwd_bwd(Hq, shared):
+    """D = 576 / Dv = 512 outside the latent kernels' head count: the general
+    forward; on the backward the per-tile key side (16 query heads) or the
+    wide hit-list key side (32), with separate K and V, or one shared tensor
+    (V its first 512 columns) whose merged gradient is dK + [dV, 0]."""
+    banner(f"attn bf16 D=576/512 Hq={Hq} shared={shared}")
+    rng = np.random.default_rng(576 + Hq + int(shared))
+    S, Hkv, D, DV, width = 160, 1, 576, 512, 48
+
+    def nrm(*shape):
+        return synth.to_bf16_values(rng.standard_normal(shape).astype(np.float32))
+
+    q, dO = nrm(1, S, Hq, D), nrm(1, S, Hq, DV)
+    if shared:
+        kv = nrm(1, S, Hkv, D)
+        k, v = kv, np.ascontiguousarray(kv[..., :DV])
+    else:
+        k, v = nrm(1, S, Hkv, D), nrm(1, S, Hkv, DV)
+    routes, lens = _random_routes(S + Hq, 1, S, width, empty_rows=[(0, 9)])
+    scale = 1.0 / math.sqrt(D)
+    dt = torch.bfloat16
+    q_d, dO_d = to_dev(q, dt), to_dev(dO, dt)
+    if shared:
+        kv_d = to_dev(kv, dt)
+        k_d, v_d = kv_d, kv_d[..., :DV]
+    else:
+        k_d, v_d = to_dev(k, dt), to_dev(v, dt)
+    r_d, l_d = to_dev(routes), to_dev(lens)
+    o, lse = irb.sparse_gqa_attention_fwd(q_d, k_d, v_d, r_d, l_d, scale)
+    ro, rlse = oracle.attention_fwd(q, k, v, routes, scale)
+    attn_tol_check(host(o), ro, dt, "o")
+    _check_lse(host(lse), rlse, dt)
+    rc, ri = irb.build_block_lists(r_d, l_d, S, 1, 16, reverse=True)
+    rdq, rdk, rdv = oracle.attention_bwd(q, k, v, routes, dO, scale)
+    dropped = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    dq, dk, dv = irb.sparse_gqa_attention_bwd(q_d, k_d, v_d, o, dO_d, lse, r_d, l_d, rc, ri, 1, 16, scale,
+                                              dropped_hits=dropped, merged_kv=shared)
+    assert int(dropped.item()) == 0
+    attn_tol_check(host(dq), rdq, dt, "dq")
+    if shared:
+        assert dv.data_ptr() == dk.data_ptr()
+        rdkv = rdk.copy()
+        rdkv[..., :DV] += rdv
+        attn_tol_check(host(dk), rdkv, dt, "dkv (merged)")
+    else:
+        attn_tol_check(host(dk), rdk, dt, "dk")
+        attn_tol_check(host(dv), rdv, dt, "dv")
+
+
 @pytest.mark.parametrize("use_ws", [True, False])
 def test_gqa_bf16_long_routes_fwd(use_ws):
     """Route rows past one round of the key-membership pass's loads (over 2560
