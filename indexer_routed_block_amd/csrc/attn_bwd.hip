@@ -1376,21 +1376,38 @@ IRB_DEV bool union_group(const AttnArgs& a, int b, int kvh, int J, int nkt, int 
 }
 
 
+// LDS of a shared-batch group: four batch buffers, each the batch's q and dO
+// rows (32 rows of D bf16 each) + lse, Delta, masks and the next ids
+template <int D>
+constexpr int union_lds_bytes() {
+  return 4 * (2 * 32 * D * 2 + 256 + 64 + 32);
+}
+template <int D, int DV, int GP>
+IRB_DEV void dkdv_union_group(const AttnBwdArgs& args, const float* __restrict__ delta, int G, int nkt, int merged,
+                              const int64_t* __restrict__ off64, const int32_t* __restrict__ t64,
+                              const uint16_t* __restrict__ m64, int64_t cap64, char* lds);
+
 // GP > 0: the padded group size as a constant (4, 8, 16, 32: the row ->
-// (query, head) splits below become shifts and masks); 0: Gp_rt at run time
+// (query, head) splits below become shifts and masks); 0: Gp_rt at run time.
+// With union lists (off64), a workgroup whose group passes union_group runs
+// it in shared batches (dkdv_union_group) in the same launch, so the long
+// lists of either kind overlap with the other kind's groups.
 template <int D, int DV, int GP>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
                      const int32_t* __restrict__ hit_t, const uint32_t* __restrict__ hit_m, int64_t cap, int G,
-                     int Gp_rt, int nkt, int merged, const int64_t* __restrict__ off64, int64_t cap64,
-                     int overlap_milli) {
+                     int Gp_rt, int nkt, int merged, const int64_t* __restrict__ off64, const int32_t* __restrict__ t64,
+                     const uint16_t* __restrict__ m64, int64_t cap64, int overlap_milli) {
   constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
   const int Gp = GP > 0 ? GP : Gp_rt;
   // row pitches of the slabs: 8 dwords apart modulo 64 banks, so the 8-byte
   // words of 8 consecutive rows land in distinct banks
   constexpr int LQ = D + 16, LO = DV + 16;
-  __shared__ __align__(16) uint16_t s_q[4][32 * LQ];
-  __shared__ __align__(16) uint16_t s_o[4][32 * LO];
+  constexpr int kSlabs = 4 * 32 * (LQ + LO) * 2;
+  constexpr int kLds = GP > 0 && union_lds_bytes<D>() > kSlabs ? union_lds_bytes<D>() : kSlabs;
+  __shared__ __align__(16) char lds[kLds];
+  auto s_q = reinterpret_cast<uint16_t(*)[32 * LQ]>(lds);
+  auto s_o = reinterpret_cast<uint16_t(*)[32 * LO]>(lds + 4 * 32 * LQ * 2);
   const AttnArgs& a = args.f;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g16 = lane >> 4, l16 = lane & 15;
@@ -1402,8 +1419,11 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   const int J = (blockIdx.x / a.Hkv) % ngrp;
   const int b = blockIdx.x / (a.Hkv * ngrp);
   const int jt = 4 * J + wid;
-  // groups whose tile lists overlap enough are the shared-batch kernel's
-  if (GP > 0 && union_group(a, b, kvh, J, nkt, ngrp, hit_off, cap, off64, cap64, overlap_milli)) return;
+  // groups whose tile lists overlap enough run in shared batches
+  if (GP > 0 && union_group(a, b, kvh, J, nkt, ngrp, hit_off, cap, off64, cap64, overlap_milli)) {
+    if constexpr (GP > 0) dkdv_union_group<D, DV, GP>(args, delta, G, nkt, merged, off64, t64, m64, cap64, lds);
+    return;
+  }
   if (jt >= nkt) return;
   const int k0 = 16 * jt;
   const int kid = k0 + l16;
@@ -1705,9 +1725,10 @@ IRB_DEV int ub_pos(int r, int c) {
   return c ^ f;
 }
 
-// Groups of four 16-key tiles whose lists overlap (union_group): one
-// workgroup per (b, group, KV head), wave w on tile 4 J + w with its keys and
-// values as B operands as in bwd_dkdv_hits_kernel.  The group's union list
+// Groups of four 16-key tiles whose lists overlap (union_group), run by the
+// workgroup of bwd_dkdv_hits_kernel that the group falls to (b, group, KV
+// head), wave w on tile 4 J + w with its keys and values as B operands as in
+// the per-tile path.  The group's union list
 // runs in batches of QPB queries (32 rows); each batch's q and dO rows, the
 // rows' lse and Delta and the queries' key masks go by direct global-to-LDS
 // loads into one of four buffers, three batches ahead of the one being
@@ -1718,11 +1739,9 @@ IRB_DEV int ub_pos(int r, int c) {
 // of its keys) exactly as the per-tile kernel does, so the sums differ only
 // in the order of their terms.
 template <int D, int DV, int GP>
-__global__ void __launch_bounds__(256, 2)
-bwd_dkdv_union_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
-                      int64_t cap, int G, int nkt, int merged, const int64_t* __restrict__ off64,
-                      const int32_t* __restrict__ t64, const uint16_t* __restrict__ m64, int64_t cap64,
-                      int overlap_milli) {
+IRB_DEV void dkdv_union_group(const AttnBwdArgs& args, const float* __restrict__ delta, int G, int nkt, int merged,
+                              const int64_t* __restrict__ off64, const int32_t* __restrict__ t64,
+                              const uint16_t* __restrict__ m64, int64_t cap64, char* lds) {
   static_assert(D == DV && GP >= 4 && GP <= 32, "shared batches: one row layout, whole queries per batch");
   constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
   constexpr int QPB = 32 / GP;               // queries per batch
@@ -1733,7 +1752,7 @@ bwd_dkdv_union_kernel(AttnBwdArgs args, const float* __restrict__ delta, const i
   constexpr int NBUF = 4;
   constexpr int NRI = 2 * 32 * NC / 256;     // 16-byte row loads per wave and batch
   static_assert(NRI >= 1 && (2 * 32 * NC) % 256 == 0, "row loads");
-  __shared__ __align__(16) char lds[NBUF * SB];
+  static_assert(NBUF * SB == union_lds_bytes<D>(), "buffer layout");
   const AttnArgs& a = args.f;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wid);
@@ -1742,7 +1761,6 @@ bwd_dkdv_union_kernel(AttnBwdArgs args, const float* __restrict__ delta, const i
   const int kvh = blockIdx.x % a.Hkv;
   const int J = (blockIdx.x / a.Hkv) % ngrp;
   const int b = blockIdx.x / (a.Hkv * ngrp);
-  if (!union_group(a, b, kvh, J, nkt, ngrp, hit_off, cap, off64, cap64, overlap_milli)) return;
   const int jt = 4 * J + wid;
   const bool live = jt < nkt;
   const int k0 = 16 * jt;
@@ -2291,28 +2309,18 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
         hipLaunchKernelGGL(bwd_union_kernel, dim3(static_cast<unsigned>(lgroups)), dim3(256), lds, stream, a.S_q, nkt,
                            ngrp, 1, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, ws.off64, ws.t64, ws.m64, ws.cap64);
       }
-      // per-tile groups, then (with union lists) the shared-batch groups
+      // one launch: per-tile groups, and (with union lists) the shared-batch groups
       const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * ngrp * a.Hkv));
       const int ovl = key_overlap_milli();
 #define IRB_DKDV_HITS(GPV)                                                                                   \
   hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV, GPV>), grid, dim3(256), 0, stream, args, ws.delta, ws.hit_off, \
-                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, merged, ws.off64, ws.cap64, ovl)
+                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, merged, ws.off64, ws.t64, ws.m64, ws.cap64, ovl)
       if (Gp == 4) IRB_DKDV_HITS(4);
       else if (Gp == 8) IRB_DKDV_HITS(8);
       else if (Gp == 16) IRB_DKDV_HITS(16);
       else if (Gp == 32) IRB_DKDV_HITS(32);
       else IRB_DKDV_HITS(0);
 #undef IRB_DKDV_HITS
-      if (ws.off64) {
-#define IRB_DKDV_UNION(GPV)                                                                                      \
-  hipLaunchKernelGGL((bwd_dkdv_union_kernel<D, DV, GPV>), grid, dim3(256), 0, stream, args, ws.delta, ws.hit_off, \
-                     ws.cap, G, nkt, merged, ws.off64, ws.t64, ws.m64, ws.cap64, ovl)
-        if (Gp == 4) IRB_DKDV_UNION(4);
-        else if (Gp == 8) IRB_DKDV_UNION(8);
-        else if (Gp == 16) IRB_DKDV_UNION(16);
-        else if (Gp == 32) IRB_DKDV_UNION(32);
-#undef IRB_DKDV_UNION
-      }
     } else if constexpr (kWide) {
       hipLaunchKernelGGL((bwd_dkdv_wide_kernel<D, DV>), dim3(static_cast<unsigned>(kitems)), dim3(256), 0, stream,
                          args, ws.delta, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, G, nkt, merged);
