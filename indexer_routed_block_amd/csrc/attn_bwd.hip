@@ -161,6 +161,7 @@ struct BwdWs {
   int32_t* t64;       // [cap64]
   uint16_t* m64;      // [cap64][4]
   int64_t cap64;      // <= RG * B * S_q * min(L, ngrp)
+  int32_t* ord;       // [B * ngrp * Hkv] dispatch order of the key-side workgroups
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -208,7 +209,8 @@ size_t attn_bwd_workspace_bytes(int B, int S_q, int S_k, int L, int Hq, int Hkv,
     if (G <= 32 && uses_union(dtype, Dqk, Dv, S_q)) {
       const size_t ngrp = (static_cast<size_t>(S_k) + 63) / 64;
       const size_t cap64 = static_cast<size_t>(union_capacity(B, S_q, S_k, L, RG));
-      n += align256((static_cast<size_t>(RG) * B * ngrp + 1) * 8) + align256(cap64 * 4) + align256(cap64 * 8);
+      n += align256((static_cast<size_t>(RG) * B * ngrp + 1) * 8) + align256(cap64 * 4) + align256(cap64 * 8) +
+           align256(static_cast<size_t>(B) * ngrp * Hkv * 4);
     }
     // 64 heads over shared latent rows: the query-major path (used when v aliases k)
     if (dtype == IRB_BF16 && Dqk == 576 && Dv == 512 && G == 64)
@@ -264,6 +266,8 @@ static BwdWs carve(void* ws, int B, int S_q, int S_k, int L, int Hq, int Hkv, in
       w.t64 = reinterpret_cast<int32_t*>(p);
       p += align256(static_cast<size_t>(w.cap64) * 4);
       w.m64 = reinterpret_cast<uint16_t*>(p);
+      p += align256(static_cast<size_t>(w.cap64) * 8);
+      w.ord = reinterpret_cast<int32_t*>(p);
     }
   } else {
     const size_t esz = dtype == IRB_BF16 ? 2 : 4;
@@ -1375,6 +1379,78 @@ IRB_DEV bool union_group(const AttnArgs& a, int b, int kvh, int J, int nkt, int 
   return u > 0 && u * overlap_milli <= sumc * 1000;
 }
 
+// Dispatch order of the key-side workgroups, heaviest first: item (b, group,
+// KV head) weighs its union count when it runs in shared batches, else its
+// longest tile list (the slowest of its four waves); items go out by
+// descending half-octave bucket of that weight, in their launch order inside
+// a bucket (neighbouring groups share window queries through the L2).  One
+// workgroup; every workgroup of the key side writes its own key tiles only,
+// so the order changes no result, only how the long lists spread over the chip.
+constexpr int kOrderMax = 1 << 16;   // larger grids keep the launch order
+__global__ void __launch_bounds__(1024)
+bwd_order_kernel(AttnArgs a, int nkt, const int64_t* __restrict__ hit_off, int64_t cap,
+                 const int64_t* __restrict__ off64, int64_t cap64, int overlap_milli, int32_t* __restrict__ ord) {
+  constexpr int NBK = 64, NW = 16;
+  __shared__ int cnt[NBK];
+  __shared__ int wc[NW][NBK];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int ngrp = (nkt + 3) / 4;
+  const int items = a.B * ngrp * a.Hkv;
+  if (threadIdx.x < NBK) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  auto bucket = [&](int it) -> int {
+    const int kvh = it % a.Hkv, J = (it / a.Hkv) % ngrp, b = it / (a.Hkv * ngrp);
+    const int64_t g = static_cast<int64_t>(a.RG > 1 ? kvh : 0) * a.B + b;
+    int64_t w = 0;
+    if (union_group(a, b, kvh, J, nkt, ngrp, hit_off, cap, off64, cap64, overlap_milli)) {
+      w = min(off64[g * ngrp + J + 1], cap64) - min(off64[g * ngrp + J], cap64);
+    } else {
+      for (int j = 4 * J; j < min(4 * J + 4, nkt); ++j)
+        w = max(w, min(hit_off[g * nkt + j + 1], cap) - min(hit_off[g * nkt + j], cap));
+    }
+    const uint64_t w1 = static_cast<uint64_t>(w) + 1;
+    const int lg = 63 - __clzll(w1);                                   // floor(log2(w + 1))
+    const int k = 2 * lg + (lg > 0 ? static_cast<int>((w1 >> (lg - 1)) & 1) : 0);
+    return NBK - 1 - min(k, NBK - 1);
+  };
+  for (int it = threadIdx.x; it < items; it += blockDim.x) atomicAdd(&cnt[bucket(it)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int k = 0; k < NBK; ++k) {
+      const int c = cnt[k];
+      cnt[k] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // stable scatter, 1024 items at a time: rank inside the wave by ballot,
+  // then after the same bucket's items of the lower waves
+  for (int c0 = 0; c0 < items; c0 += NW * 64) {
+    const int it = c0 + static_cast<int>(threadIdx.x);
+    const int k = it < items ? bucket(it) : -1;
+    int rank = 0;
+    for (int kk = 0; kk < NBK; ++kk) {
+      const uint64_t m = __ballot(k == kk);
+      if (k == kk) rank = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == 0) wc[wid][kk] = __popcll(m);
+    }
+    __syncthreads();
+    if (k >= 0) {
+      int pos = cnt[k] + rank;
+      for (int w = 0; w < wid; ++w) pos += wc[w][k];
+      ord[pos] = it;
+    }
+    __syncthreads();
+    if (threadIdx.x < NBK) {
+      int t = 0;
+      for (int w = 0; w < NW; ++w) t += wc[w][threadIdx.x];
+      cnt[threadIdx.x] += t;
+    }
+    __syncthreads();
+  }
+}
+
 
 // LDS of a shared-batch group: four batch buffers, each the batch's q and dO
 // rows (32 rows of D bf16 each) + lse, Delta, masks and the next ids
@@ -1385,7 +1461,7 @@ constexpr int union_lds_bytes() {
 template <int D, int DV, int GP>
 IRB_DEV void dkdv_union_group(const AttnBwdArgs& args, const float* __restrict__ delta, int G, int nkt, int merged,
                               const int64_t* __restrict__ off64, const int32_t* __restrict__ t64,
-                              const uint16_t* __restrict__ m64, int64_t cap64, char* lds);
+                              const uint16_t* __restrict__ m64, int64_t cap64, char* lds, int item);
 
 // GP > 0: the padded group size as a constant (4, 8, 16, 32: the row ->
 // (query, head) splits below become shifts and masks); 0: Gp_rt at run time.
@@ -1397,7 +1473,8 @@ __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const int64_t* __restrict__ hit_off,
                      const int32_t* __restrict__ hit_t, const uint32_t* __restrict__ hit_m, int64_t cap, int G,
                      int Gp_rt, int nkt, int merged, const int64_t* __restrict__ off64, const int32_t* __restrict__ t64,
-                     const uint16_t* __restrict__ m64, int64_t cap64, int overlap_milli) {
+                     const uint16_t* __restrict__ m64, int64_t cap64, int overlap_milli,
+                     const int32_t* __restrict__ ord) {
   constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
   const int Gp = GP > 0 ? GP : Gp_rt;
   // row pitches of the slabs: 8 dwords apart modulo 64 banks, so the 8-byte
@@ -1415,13 +1492,15 @@ bwd_dkdv_hits_kernel(AttnBwdArgs args, const float* __restrict__ delta, const in
   // tile 4 J + w: neighbouring tiles' lists share queries (a window, dense
   // routes), whose q / dO rows the four waves then find in the L2
   const int ngrp = (nkt + 3) / 4;
-  const int kvh = blockIdx.x % a.Hkv;
-  const int J = (blockIdx.x / a.Hkv) % ngrp;
-  const int b = blockIdx.x / (a.Hkv * ngrp);
+  // (b, group, KV head) of this workgroup: heaviest first when ordered
+  const int item = ord ? ord[blockIdx.x] : static_cast<int>(blockIdx.x);
+  const int kvh = item % a.Hkv;
+  const int J = (item / a.Hkv) % ngrp;
+  const int b = item / (a.Hkv * ngrp);
   const int jt = 4 * J + wid;
   // groups whose tile lists overlap enough run in shared batches
   if (GP > 0 && union_group(a, b, kvh, J, nkt, ngrp, hit_off, cap, off64, cap64, overlap_milli)) {
-    if constexpr (GP > 0) dkdv_union_group<D, DV, GP>(args, delta, G, nkt, merged, off64, t64, m64, cap64, lds);
+    if constexpr (GP > 0) dkdv_union_group<D, DV, GP>(args, delta, G, nkt, merged, off64, t64, m64, cap64, lds, item);
     return;
   }
   if (jt >= nkt) return;
@@ -1741,7 +1820,7 @@ IRB_DEV int ub_pos(int r, int c) {
 template <int D, int DV, int GP>
 IRB_DEV void dkdv_union_group(const AttnBwdArgs& args, const float* __restrict__ delta, int G, int nkt, int merged,
                               const int64_t* __restrict__ off64, const int32_t* __restrict__ t64,
-                              const uint16_t* __restrict__ m64, int64_t cap64, char* lds) {
+                              const uint16_t* __restrict__ m64, int64_t cap64, char* lds, int item) {
   static_assert(D == DV && GP >= 4 && GP <= 32, "shared batches: one row layout, whole queries per batch");
   constexpr int KS = D / 32, VS = DV / 32, NDK = D / 16, NDV = DV / 16;
   constexpr int QPB = 32 / GP;               // queries per batch
@@ -1758,9 +1837,9 @@ IRB_DEV void dkdv_union_group(const AttnBwdArgs& args, const float* __restrict__
   const int wv = __builtin_amdgcn_readfirstlane(wid);
   const int g16 = lane >> 4, l16 = lane & 15;
   const int ngrp = (nkt + 3) / 4;
-  const int kvh = blockIdx.x % a.Hkv;
-  const int J = (blockIdx.x / a.Hkv) % ngrp;
-  const int b = blockIdx.x / (a.Hkv * ngrp);
+  const int kvh = item % a.Hkv;
+  const int J = (item / a.Hkv) % ngrp;
+  const int b = item / (a.Hkv * ngrp);
   const int jt = 4 * J + wid;
   const bool live = jt < nkt;
   const int k0 = 16 * jt;
@@ -2310,11 +2389,19 @@ static int launch_bwd_t(const AttnBwdArgs& args, hipStream_t stream) {
                            ngrp, 1, ws.hit_off, ws.hit_t, ws.hit_m, ws.cap, ws.off64, ws.t64, ws.m64, ws.cap64);
       }
       // one launch: per-tile groups, and (with union lists) the shared-batch groups
-      const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * ngrp * a.Hkv));
+      const int64_t kgroups = static_cast<int64_t>(a.B) * ngrp * a.Hkv;
+      const dim3 grid(static_cast<unsigned>(kgroups));
       const int ovl = key_overlap_milli();
+      const int32_t* ord = nullptr;
+      if (ws.off64 && kgroups <= kOrderMax) {
+        hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, stream, a, nkt, ws.hit_off, ws.cap, ws.off64,
+                           ws.cap64, ovl, ws.ord);
+        ord = ws.ord;
+      }
 #define IRB_DKDV_HITS(GPV)                                                                                   \
   hipLaunchKernelGGL((bwd_dkdv_hits_kernel<D, DV, GPV>), grid, dim3(256), 0, stream, args, ws.delta, ws.hit_off, \
-                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, merged, ws.off64, ws.t64, ws.m64, ws.cap64, ovl)
+                     ws.hit_t, ws.hit_m, ws.cap, G, Gp, nkt, merged, ws.off64, ws.t64, ws.m64, ws.cap64, ovl, \
+                     ord)
       if (Gp == 4) IRB_DKDV_HITS(4);
       else if (Gp == 8) IRB_DKDV_HITS(8);
       else if (Gp == 16) IRB_DKDV_HITS(16);
