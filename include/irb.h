@@ -540,7 +540,8 @@ int irb_sparse_gqa_attention_fwd(const void* q, const void* k, const void* v, in
  *     with their 16-bit key masks (at most RG * B * S_q * min(L, ceil(S_k /
  *     16)) entries; lists that repeat a query tile, or stale lists, can
  *     overflow it: entries past it are dropped and counted), and per group
- *     of four such tiles the union of their lists (bounded by the routes).
+ *     of four such tiles the union of their lists (bounded by the routes)
+ *     and the order in which the key-side workgroups are dispatched.
  *   dropped_hits OUT device int64 scalar, nullable: written with the number
  *     of hit entries that did not fit the workspace (0 for consistent
  *     routes and reverse lists; a non-zero value means dk / dv miss those
