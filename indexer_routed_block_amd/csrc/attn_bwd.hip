@@ -182,12 +182,13 @@ static bool uses_union(int dtype, int Dqk, int Dv, int S_q) {
          (static_cast<int64_t>(S_q) + 31) / 32 * 8 <= 65536;
 }
 // least overlap (per mille: sum of a 64-key group's four tile-list counts
-// over its union count) for the shared-batch key side; IRB_KEY_UNION_MIN_OVERLAP
-// overrides it
+// over its union count) for the shared-batch key side, 1.5 (measured best of
+// 1.0-3: lower sends groups whose tiles share few queries through batches
+// that reach one tile each); IRB_KEY_UNION_MIN_OVERLAP overrides it
 static int key_overlap_milli() {
   static const int v = [] {
     const char* e = getenv("IRB_KEY_UNION_MIN_OVERLAP");
-    return e ? static_cast<int>(atof(e) * 1000.0) : 2000;
+    return e ? static_cast<int>(atof(e) * 1000.0) : 1500;
   }();
   return v;
 }
